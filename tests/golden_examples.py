@@ -1,0 +1,52 @@
+"""Parser for tests/golden/worked_examples.txt (hand-derived examples)."""
+
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.txt")
+
+
+def _pairs(text, base):
+    out = {}
+    for tok in text.split():
+        k, v = tok.split(":")
+        out[int(k, 16)] = v if base is None else int(v, base)
+    return out
+
+
+def load():
+    blocks, cur = [], {}
+    with open(GOLDEN) as f:
+        for raw in f:
+            line = raw.strip()
+            if line.startswith("#"):
+                continue
+            if not line:
+                if cur:
+                    blocks.append(cur)
+                    cur = {}
+                continue
+            key, val = line.split(":", 1)
+            cur[key.strip()] = val.strip()
+    if cur:
+        blocks.append(cur)
+    examples = []
+    for b in blocks:
+        ex = {"name": b["name"], "max_len": int(b["max_len"])}
+        freq = np.zeros(256, np.uint64)
+        for s, v in _pairs(b["freq"], 10).items():
+            freq[s] = v
+        ex["freq"] = freq
+        ln = np.zeros(256, np.uint8)
+        for s, v in _pairs(b["lengths"], 10).items():
+            ln[s] = v
+        ex["lengths"] = ln
+        ex["codes"] = _pairs(b["codes"], None)  # sym -> bit string
+        if "input" in b:
+            ex["chunk"] = int(b["chunk"])
+            ex["input"] = np.array([int(t, 16) for t in b["input"].split()], np.uint8)
+            ex["stream"] = np.array([int(t, 16) for t in b["stream"].split()], np.uint8)
+            ex["payload_bits"] = int(b["payload_bits"])
+        examples.append(ex)
+    return examples

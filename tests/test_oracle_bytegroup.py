@@ -1,0 +1,67 @@
+"""Pins of the oracle's byte grouping, container and size accounting (CPU only)."""
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+
+def test_split_matches_torch_bf16_bit_view():
+    x32 = np.random.default_rng(1).normal(0, 0.02, 10_000).astype(np.float32)
+    t = torch.from_numpy(x32).to(torch.bfloat16)
+    u16 = t.view(torch.int16).numpy().view(np.uint16)
+    hi, lo = oracle.split_bf16(u16)
+    b = u16.view(np.uint8).reshape(-1, 2)  # little-endian: byte 1 is the high byte
+    assert np.array_equal(hi, b[:, 1]) and np.array_equal(lo, b[:, 0])
+    assert np.array_equal(oracle.merge_bf16(hi, lo), u16)
+
+
+def test_generator_bf16_rounding_matches_torch():
+    x32 = np.random.default_rng(2).normal(0, 0.02, 100_000).astype(np.float32)
+    x32[::7] *= 20
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(workloads.bf16_bits(x32), ref)
+
+
+def test_bf16_container_round_trip_and_layout():
+    x = workloads.bf16_weights(70_000)
+    enc = oracle.encode_bf16(x, 16384)
+    buf = oracle.container_bytes(enc)
+    bh, bl = enc["stream_hi"].size, enc["stream_lo"].size
+    assert buf.size == 560 + bh + (-bh % 16) + bl
+    assert bytes(buf[:4]) == b"LECB"
+    back = oracle.parse_container(buf)
+    assert np.array_equal(oracle.decode_bf16(back), x)
+    # byte grouping separates a compressible high plane from a nearly random low plane
+    assert enc["bits_hi"] < 0.5 * 8 * x.size
+    assert enc["bits_lo"] > 0.95 * 8 * x.size
+
+
+def test_delta_planes():
+    d, w0, w1 = workloads.bf16_delta(1 << 16, return_snapshots=True)
+    assert np.array_equal(w0 ^ d, w1)
+    hi, lo = oracle.split_bf16(d)
+    assert (hi == 0).mean() > 0.95  # a small update rarely touches sign/exponent bits
+
+
+def test_workload_entropy_closed_forms():
+    # round(N(0, s^2)) has entropy close to the Gaussian differential entropy at these s.
+    h = oracle.histogram(workloads.int8_fixed(0))
+    assert abs(oracle.entropy_bits(h) - oracle.metrics.gaussian_entropy_bits(20.0)) < 0.01
+    h10 = oracle.histogram(workloads.int8_drift_batch(0, 1 << 20))
+    assert abs(oracle.entropy_bits(h10) - oracle.metrics.gaussian_entropy_bits(10.0)) < 0.01
+
+
+def test_payload_identity_and_optimum():
+    x = workloads.int8_fixed(0)
+    warm = [oracle.histogram(workloads.int8_fixed(r)) for r in (1, 2, 3, 4)]
+    F = oracle.codebook_frequencies(warm, 1)
+    ln = oracle.package_merge_lengths(F, 16)
+    h = oracle.histogram(x)
+    fixed_bits = oracle.payload_bits_identity(h, ln)
+    opt_bits = oracle.per_batch_optimal_bits(h, 16)
+    shannon = oracle.metrics.shannon_bits(h)
+    assert shannon <= opt_bits <= fixed_bits
+    assert fixed_bits / opt_bits - 1 < 0.005  # the page's "within 0.5 % of per-shard Huffman" holds here
+    assert fixed_bits / shannon - 1 < 0.01
