@@ -45,6 +45,9 @@ from .stream import (
     num_chunks,
     table_bytes,
     encoded_bound,
+    header_bytes,
+    gap_bytes,
+    units_per_chunk,
     encode_bitstring,
     encode,
     decode_bitwise,
@@ -58,7 +61,7 @@ from .metrics import entropy_bits, payload_bits_identity, per_batch_optimal_bits
 __all__ = [
     "histogram", "codebook_frequencies", "package_merge_lengths", "canonical_codes",
     "kraft_sum_scaled", "OracleError", "CorruptStream", "UncodedSymbol", "num_chunks",
-    "table_bytes", "encoded_bound", "encode_bitstring", "encode", "decode_bitwise", "decode",
+    "table_bytes", "header_bytes", "gap_bytes", "units_per_chunk", "encoded_bound", "encode_bitstring", "encode", "decode_bitwise", "decode",
     "chunk_word_counts", "parse_table", "split_bf16", "merge_bf16", "encode_bf16", "decode_bf16",
     "container_bytes", "parse_container", "entropy_bits", "payload_bits_identity",
     "per_batch_optimal_bits",

@@ -21,10 +21,22 @@ kernel and followed bit for bit by the library:
   significant bit first, starting at bit 31 of a fresh 32-bit word and filling
   downwards; the chunk's last word is zero-padded; words are stored
   little-endian; chunks follow each other with no gap;
+* decode units: a chunk of Wc payload words is cut at K = max(1, chunk // 256)
+  word-aligned bit positions s_j = 32 * floor(j * Wc / K), j = 0..K-1; the
+  GAP of unit j is the distance in bits from s_j to the first code-word
+  boundary at or after s_j (boundaries = code-word starts and the end of the
+  chunk's data); it is always 0..15 because no code word exceeds 16 bits.
+  The gaps let a decoder start K independent decoders per chunk at exact
+  code-word starts (the "gap array" of Yamamoto et al., 2020 -- prior art, not
+  on the pages; the pages' Key design item 3 asks for independent parallel
+  tasks);
 * stream = ``u32 end[nc]`` (end[c] = index, counted in payload words, one past
-  chunk c's last word; so chunk c spans words [end[c-1], end[c]) with
-  end[-1] = 0) || zero bytes up to a 16-byte boundary || ``u32 payload[W]``
-  with W = end[nc-1];  size = align16(4*nc) + 4*W;  n = 0 -> empty stream;
+  chunk c's last word; chunk c spans words [end[c-1], end[c]) with
+  end[-1] = 0) || zero bytes up to a 16-byte boundary || gap nibbles
+  (nibble i = c*K + j is the low half of byte i//2 when i is even, the high
+  half when odd) || zero bytes up to a 16-byte boundary || ``u32 payload[W]``
+  with W = end[nc-1];
+  size = align16(4*nc) + align16(ceil(nc*K/2)) + 4*W;  n = 0 -> empty stream;
 * nothing else is stored: chunk size, n and the codebook travel outside
   (the fixed codebook is never transmitted, per Methodology step 4).
 """
@@ -56,8 +68,21 @@ def num_chunks(n: int, chunk: int) -> int:
     return -(-int(n) // int(chunk))
 
 
+def units_per_chunk(chunk: int) -> int:
+    return max(1, int(chunk) // 256)
+
+
 def table_bytes(n: int, chunk: int) -> int:
     return _align16(4 * num_chunks(n, chunk))
+
+
+def gap_bytes(n: int, chunk: int) -> int:
+    return _align16(-(-num_chunks(n, chunk) * units_per_chunk(chunk) // 2))
+
+
+def header_bytes(n: int, chunk: int) -> int:
+    """Bytes before the payload: offset table and gap nibbles, each padded to 16 bytes."""
+    return table_bytes(n, chunk) + gap_bytes(n, chunk)
 
 
 def encoded_bound(n: int, chunk: int, max_len: int = 16) -> int:
@@ -65,7 +90,32 @@ def encoded_bound(n: int, chunk: int, max_len: int = 16) -> int:
     nc = num_chunks(n, chunk)
     if nc == 0:
         return 0
-    return table_bytes(n, chunk) + 4 * (-(-int(n) * int(max_len) // 32) + nc)
+    return header_bytes(n, chunk) + 4 * (-(-int(n) * int(max_len) // 32) + nc)
+
+
+def unit_starts(words: int, chunk: int) -> np.ndarray:
+    """Word index of each decode-unit boundary of a chunk with ``words`` payload words."""
+    K = units_per_chunk(chunk)
+    return (np.arange(K, dtype=np.int64) * int(words)) // K
+
+
+def _gap_of(boundaries, s):
+    """First element of the sorted ``boundaries`` at or after bit s, minus s."""
+    i = int(np.searchsorted(boundaries, s, side="left"))
+    return int(boundaries[i]) - s
+
+
+def _pack_nibbles(gaps: np.ndarray, nbytes: int) -> np.ndarray:
+    g = np.zeros(2 * nbytes, dtype=np.uint8)
+    g[: gaps.size] = gaps
+    return (g[0::2] | (g[1::2] << 4)).astype(np.uint8)
+
+
+def _unpack_nibbles(raw: np.ndarray) -> np.ndarray:
+    out = np.empty(2 * raw.size, dtype=np.uint8)
+    out[0::2] = raw & 0xF
+    out[1::2] = raw >> 4
+    return out
 
 
 def _check_args(sym, lengths, chunk):
@@ -82,6 +132,15 @@ def _check_args(sym, lengths, chunk):
 # encoder (i): the definition, one character per bit.  Small inputs only.
 # --------------------------------------------------------------------------
 
+def _assemble(n, chunk, ends, gaps, payload_words):
+    nc = num_chunks(n, chunk)
+    table = np.zeros(table_bytes(n, chunk) // 4, dtype="<u4")
+    table[:nc] = ends
+    gap = _pack_nibbles(np.asarray(gaps, dtype=np.uint8), gap_bytes(n, chunk))
+    payload = np.asarray(payload_words, dtype=np.uint64).astype("<u4")
+    return np.concatenate([table.view(np.uint8), gap, payload.view(np.uint8)])
+
+
 def encode_bitstring(sym, lengths, codes, chunk: int):
     """Encode by writing every code word as a '0'/'1' string (the definition).
 
@@ -93,8 +152,7 @@ def encode_bitstring(sym, lengths, codes, chunk: int):
     nc = num_chunks(n, chunk)
     if nc == 0:
         return np.zeros(0, dtype=np.uint8), 0
-    words = []
-    ends = []
+    words, ends, gaps = [], [], []
     payload_bits = 0
     for c in range(nc):
         parts = []
@@ -105,16 +163,20 @@ def encode_bitstring(sym, lengths, codes, chunk: int):
             parts.append(format(int(codes[s]), f"0{ln}b"))
         bits = "".join(parts)
         payload_bits += len(bits)
+        boundaries = [0]
+        for part in parts:
+            boundaries.append(boundaries[-1] + len(part))  # starts of the next word, then the data end
         bits += "0" * (-len(bits) % 32)
+        nwords = len(bits) // 32
+        for w in unit_starts(nwords, chunk):
+            s_j = 32 * int(w)
+            gaps.append(min(b for b in boundaries if b >= s_j) - s_j)
         for i in range(0, len(bits), 32):
             words.append(int(bits[i:i + 32], 2))
         ends.append(len(words))
     if len(words) >= 1 << 32:
         raise OverflowError("payload too large for 32-bit word offsets")
-    table = np.zeros(_align16(4 * nc) // 4, dtype="<u4")
-    table[:nc] = ends
-    payload = np.array(words, dtype="<u4")
-    return np.concatenate([table.view(np.uint8), payload.view(np.uint8)]), payload_bits
+    return _assemble(n, chunk, ends, gaps, words), payload_bits
 
 
 # --------------------------------------------------------------------------
@@ -152,6 +214,8 @@ def encode(sym, lengths, codes, chunk: int):
     bit 31-(g&31), spilling into the next word when it crosses the boundary.
     Fields of distinct symbols are disjoint, so each word is the plain SUM of
     its fields; sums stay below 2^32 and are exact in float64 bincount.
+    Gaps: for each unit boundary S (global bit), the first code-word start at
+    or after S inside the same chunk, else the chunk's data end.
     """
     sym, lengths = _check_args(sym, lengths, chunk)
     codes = np.asarray(codes, dtype=np.int64).ravel()
@@ -159,6 +223,7 @@ def encode(sym, lengths, codes, chunk: int):
     nc = num_chunks(n, chunk)
     if nc == 0:
         return np.zeros(0, dtype=np.uint8), 0
+    K = units_per_chunk(chunk)
     bits = chunk_bit_counts(sym, lengths, chunk)
     words = (bits + 31) // 32
     ends = np.cumsum(words)
@@ -166,6 +231,9 @@ def encode(sym, lengths, codes, chunk: int):
     if W >= 1 << 32:
         raise OverflowError("payload too large for 32-bit word offsets")
     starts = ends - words
+    data_end = 32 * starts + bits  # global bit just past each chunk's last code word
+    unit_bit = 32 * (starts[:, None] + (np.arange(K, dtype=np.int64)[None, :] * words[:, None]) // K)
+    gaps = np.full((nc, K), -1, dtype=np.int64)
     payload = np.zeros(W + 1, dtype=np.float64)
     block = max(1, (1 << 22) // chunk) * chunk
     for start in range(0, n, block):
@@ -186,12 +254,18 @@ def encode(sym, lengths, codes, chunk: int):
         lo = np.where(fits, 0, (cd << np.maximum(32 + shift, 0)) & 0xFFFFFFFF)
         payload += np.bincount(w, weights=hi.astype(np.float64), minlength=W + 1)
         payload += np.bincount(w + 1, weights=lo.astype(np.float64), minlength=W + 2)[: W + 1]
+        # gaps of the unit boundaries of this block's chunks
+        c0, c1 = int(cid[0]), int(cid[-1]) + 1
+        S = unit_bit[c0:c1]
+        i = np.searchsorted(g, S.ravel(), side="left").reshape(S.shape)
+        inside = (i < g.size)
+        inside[inside] &= cid[i[inside]] == np.arange(c0, c1)[:, None].repeat(K, 1)[inside]
+        nxt = np.where(inside, g[np.minimum(i, g.size - 1)], data_end[c0:c1, None])
+        gaps[c0:c1] = nxt - S
+    assert np.all((gaps >= 0) & (gaps <= 15))
     payload = payload[:W].astype(np.uint64)
     assert np.all(payload < (1 << 32))
-    table = np.zeros(_align16(4 * nc) // 4, dtype="<u4")
-    table[:nc] = ends
-    out = np.concatenate([table.view(np.uint8), payload.astype("<u4").view(np.uint8)])
-    return out, int(bits.sum())
+    return _assemble(n, chunk, ends, gaps.ravel(), payload), int(bits.sum())
 
 
 # --------------------------------------------------------------------------
@@ -199,27 +273,43 @@ def encode(sym, lengths, codes, chunk: int):
 # --------------------------------------------------------------------------
 
 def parse_table(stream, n: int, chunk: int):
-    """Validate the offset table; return (starts, ends, payload words as uint64)."""
+    """Validate the layout; return (starts, ends, gaps[nc, K], payload words as uint64)."""
     stream = np.ascontiguousarray(stream).view(np.uint8).ravel()
     nc = num_chunks(n, chunk)
+    K = units_per_chunk(chunk)
     if nc == 0:
         if stream.size != 0:
             raise CorruptStream("non-empty stream for n = 0")
-        return np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros(0, np.uint64)
-    tb = _align16(4 * nc)
-    if stream.size < tb or (stream.size - tb) % 4:
-        raise CorruptStream("stream shorter than its offset table or not whole words")
+        z = np.zeros(0, np.int64)
+        return z, z, np.zeros((0, K), np.int64), np.zeros(0, np.uint64)
+    tb = table_bytes(n, chunk)
+    hb = header_bytes(n, chunk)
+    if stream.size < hb or (stream.size - hb) % 4:
+        raise CorruptStream("stream shorter than its header or not whole words")
     ends = stream[: 4 * nc].view("<u4").astype(np.int64)
     if np.any(stream[4 * nc: tb] != 0):
         raise CorruptStream("non-zero table padding")
-    W = (stream.size - tb) // 4
+    nib = _unpack_nibbles(stream[tb:hb])
+    if np.any(nib[nc * K:] != 0):
+        raise CorruptStream("non-zero gap padding")
+    gaps = nib[: nc * K].astype(np.int64).reshape(nc, K)
+    W = (stream.size - hb) // 4
     starts = np.concatenate([[0], ends[:-1]])
     if np.any(ends <= starts):
         raise CorruptStream("offset table not strictly increasing")
     if int(ends[-1]) != W:
         raise CorruptStream("offset table disagrees with the stream size")
-    payload = stream[tb:].view("<u4").astype(np.uint64)
-    return starts, ends, payload
+    payload = stream[hb:].view("<u4").astype(np.uint64)
+    return starts, ends, gaps, payload
+
+
+def _check_gaps(starts, ends, gaps, boundary_lists, chunk):
+    """Every stored gap must equal the distance to the first boundary at or after its unit start."""
+    for c in range(starts.size):
+        b = np.asarray(boundary_lists[c], dtype=np.int64)
+        for j, w in enumerate(unit_starts(int(ends[c] - starts[c]), chunk)):
+            if _gap_of(b, 32 * int(w)) != int(gaps[c, j]):
+                raise CorruptStream("gap disagrees with the code-word boundaries")
 
 
 def _canonical_tables(lengths):
@@ -250,13 +340,15 @@ def decode_bitwise(stream, lengths, chunk: int, n: int) -> np.ndarray:
     (v - first[l])-th symbol of length l in canonical order.
     """
     lengths = np.asarray(lengths, dtype=np.int64).ravel()
-    starts, ends, payload = parse_table(stream, n, chunk)
+    starts, ends, gaps, payload = parse_table(stream, n, chunk)
     first, count, index, syms = _canonical_tables(lengths)
     out = np.zeros(n, dtype=np.uint8)
+    boundary_lists = []
     for c in range(starts.size):
         words = payload[starts[c]:ends[c]]
         bitstr = "".join(format(int(w), "032b") for w in words)
         p = 0
+        bl = [0]
         for k in range(min(chunk, n - c * chunk)):
             v = 0
             ln = 0
@@ -271,10 +363,13 @@ def decode_bitwise(stream, lengths, chunk: int, n: int) -> np.ndarray:
                 if count[ln] and first[ln] <= v < first[ln] + count[ln]:
                     out[c * chunk + k] = syms[index[ln] + v - first[ln]]
                     break
+            bl.append(p)
         if (len(bitstr) - p) >= 32:
             raise CorruptStream("chunk holds more words than its symbols need")
         if "1" in bitstr[p:]:
             raise CorruptStream("non-zero padding after the last code word")
+        boundary_lists.append(bl)
+    _check_gaps(starts, ends, gaps, boundary_lists, chunk)
     return out
 
 
@@ -297,23 +392,45 @@ def _lookup_table(lengths, codes):
 
 
 def decode(stream, lengths, chunk: int, n: int, codes=None) -> np.ndarray:
-    """Decoder (ii): all chunks advance one symbol per step through a 16-bit lookup table."""
+    """Decoder (ii): all chunks advance one symbol per step through a 16-bit lookup table.
+
+    The gaps are not needed to decode sequentially; they are checked afterwards
+    against the code-word boundaries the decode found.
+    """
     from .huffman import canonical_codes
 
     lengths = np.asarray(lengths, dtype=np.int64).ravel()
     if codes is None:
         codes = canonical_codes(lengths)
-    starts, ends, payload = parse_table(stream, n, chunk)
+    starts, ends, gaps, payload = parse_table(stream, n, chunk)
     nc = starts.size
     out = np.zeros(n, dtype=np.uint8)
     if nc == 0:
         return out
+    K = units_per_chunk(chunk)
     sym_of, len_of = _lookup_table(lengths, codes)
     words = np.concatenate([payload, np.zeros(2, dtype=np.uint64)])
     pos = starts * 32
     endbit = ends * 32
     m = np.minimum(chunk, n - np.arange(nc, dtype=np.int64) * chunk)
     base = np.arange(nc, dtype=np.int64) * chunk
+    # unit boundaries (global bits) and the first code-word boundary found at or after each
+    wc = ends - starts
+    ubit = 32 * (starts[:, None] + (np.arange(K, dtype=np.int64)[None, :] * wc[:, None]) // K)
+    found = np.full((nc, K), -1, dtype=np.int64)
+
+    def mark(act, p):
+        # a boundary at p settles every unit boundary in (previous boundary, p]
+        sub = ubit[act] if not isinstance(act, slice) else ubit
+        f = found[act] if not isinstance(act, slice) else found
+        hit = (f < 0) & (sub <= p[:, None])
+        f[hit] = np.broadcast_to(p[:, None], f.shape)[hit]
+        if isinstance(act, slice):
+            found[:] = f
+        else:
+            found[act] = f
+
+    mark(slice(None), pos.copy())
     for k in range(int(m.max())):
         act = np.nonzero(m > k)[0] if m[-1] <= k else slice(None)
         p = pos[act]
@@ -327,6 +444,7 @@ def decode(stream, lengths, chunk: int, n: int, codes=None) -> np.ndarray:
             raise CorruptStream("code word runs past the end of its chunk")
         out[base[act] + k] = sym_of[peek.astype(np.int64)]
         pos[act] = p + ln
+        mark(act, pos[act])
     if np.any(endbit - pos >= 32):
         raise CorruptStream("chunk holds more words than its symbols need")
     rest = endbit - pos
@@ -334,4 +452,6 @@ def decode(stream, lengths, chunk: int, n: int, codes=None) -> np.ndarray:
     mask = (np.uint64(1) << rest.astype(np.uint64)) - np.uint64(1)
     if np.any(last & mask):
         raise CorruptStream("non-zero padding after the last code word")
+    if np.any(found - ubit != gaps):
+        raise CorruptStream("gap disagrees with the code-word boundaries")
     return out

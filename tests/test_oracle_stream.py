@@ -39,7 +39,7 @@ def test_two_encoders_and_two_decoders_agree(name, n, chunk, gen):
     s2, b2 = encode(x, ln, cd, chunk)
     assert np.array_equal(s1, s2) and b1 == b2
     assert b1 == oracle.payload_bits_identity(oracle.histogram(x), ln)
-    assert s1.size == oracle.table_bytes(n, chunk) + 4 * int(oracle.chunk_word_counts(x, ln, chunk).sum())
+    assert s1.size == oracle.header_bytes(n, chunk) + 4 * int(oracle.chunk_word_counts(x, ln, chunk).sum())
     assert s1.size <= oracle.encoded_bound(n, chunk, 16)
     y1 = decode_bitwise(s1, ln, chunk, n)
     y2 = decode(s1, ln, chunk, n)
@@ -52,7 +52,7 @@ def test_uniform_code_closed_form_byteswap():
     x = workloads.uniform_bytes(5, 4096 * 3)
     ln = np.full(256, 8, np.uint8)
     s, bits = encode(x, ln, canonical_codes(ln), 4096)
-    tb = oracle.table_bytes(x.size, 4096)
+    tb = oracle.header_bytes(x.size, 4096)
     assert bits == 8 * x.size
     assert np.array_equal(s[tb:], x.view(">u4").astype("<u4").view(np.uint8))
     assert list(s[:12].view("<u4")) == [1024, 2048, 3072]
@@ -105,7 +105,8 @@ def _corruptions():
 def test_corrupt_streams_detected():
     x, ln, s = _corruptions()
     n, chunk = x.size, 1024
-    tb = oracle.table_bytes(n, chunk)
+    tb = oracle.header_bytes(n, chunk)
+    gb = oracle.table_bytes(n, chunk)
     bad = []
     t = s.copy(); t[0:4] = np.array([0, 0, 0, 0], np.uint8); bad.append(("zero end", t))
     t = s.copy(); e = t[:20].view("<u4").copy(); e[1], e[2] = e[2], e[1]; t[:20] = e.view(np.uint8); bad.append(("non-monotone", t))
@@ -117,6 +118,9 @@ def test_corrupt_streams_detected():
     bits0 = int(oracle.stream.chunk_bit_counts(x[:chunk], ln, chunk)[0])
     if bits0 % 32:
         t = s.copy(); off = tb + 4 * (int(ends[0]) - 1); t[off] |= 1; bad.append(("padding bit", t))
+    # gap section: chunk 0 has K = 4 units; change the gap of unit 1, then its padding nibble area
+    t = s.copy(); t[gb] ^= 0x10; bad.append(("gap value", t))
+    t = s.copy(); t[tb - 1] = 0x01; bad.append(("gap padding", t))
     for name, t in bad:
         with pytest.raises(CorruptStream):
             decode(t, ln, chunk, n)
@@ -127,9 +131,9 @@ def test_corrupt_streams_detected():
 def test_incomplete_code_rejects_unmatched_prefix():
     ln = np.zeros(256, np.uint8)
     ln[7] = 1  # only code word is "0"
-    s = np.zeros(20, np.uint8)
+    s = np.zeros(36, np.uint8)
     s[0] = 1
-    s[19] = 0x80  # first payload bit is 1: no code word matches
+    s[35] = 0x80  # first payload bit is 1: no code word matches
     with pytest.raises(CorruptStream):
         decode(s, ln, 4096, 3)
     with pytest.raises(CorruptStream):
@@ -143,9 +147,28 @@ def test_chunks_are_independent():
     ln, cd = _codebook(x)
     s, _ = encode(x, ln, cd, 512)
     nc = oracle.num_chunks(x.size, 512)
-    tb = oracle.table_bytes(x.size, 512)
+    tb = oracle.header_bytes(x.size, 512)
+    gb = oracle.table_bytes(x.size, 512)
     ends = s[:4 * nc].view("<u4").astype(np.int64)
     starts = np.concatenate([[0], ends[:-1]])
     for c in range(nc):
         one, _ = encode(x[c * 512:(c + 1) * 512], ln, cd, 512)
-        assert np.array_equal(one[16:], s[tb + 4 * starts[c]: tb + 4 * ends[c]])
+        assert np.array_equal(one[32:], s[tb + 4 * starts[c]: tb + 4 * ends[c]])
+        assert one[16] == s[gb + c]  # K = 2 nibbles per chunk = one gap byte per chunk
+
+
+def test_gaps_point_at_code_word_starts():
+    # Every nonzero gap lands on a code-word start (or the data end) that is not word-aligned.
+    x = workloads.skewed_bytes(13, 20 * 4096 + 100, sigma=25)
+    ln, cd = _codebook(x)
+    s, _ = encode(x, ln, cd, 4096)
+    starts, ends, gaps, payload = oracle.parse_table(s, x.size, 4096)
+    assert gaps.shape == (21, 16) and np.all(gaps[:, 0] == 0) and gaps.max() <= 15
+    assert (gaps > 0).mean() > 0.5  # most unit boundaries fall inside a code word
+    for c in range(starts.size):
+        lens = ln[x[c * 4096:(c + 1) * 4096]].astype(np.int64)
+        bnd = set(np.concatenate([[0], np.cumsum(lens)]).tolist())
+        for j, w in enumerate(oracle.stream.unit_starts(int(ends[c] - starts[c]), 4096)):
+            p = 32 * int(w) + int(gaps[c, j])
+            assert p in bnd
+            assert not any(q in bnd for q in range(32 * int(w), p))
