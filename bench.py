@@ -1,0 +1,422 @@
+#!/usr/bin/env python3
+"""Throughput bench of the Huffman byte codec on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+One step = one pass of the whole coding path over one synthetic tensor, with
+inputs resident in HBM:
+
+* per-tensor bf16 (default, ``bf16_weights``: 64 Mi bf16 elements, chunk
+  16384; also ``bf16_delta``): plane histograms -> read back -> two host
+  codebooks -> upload -> encode both byte planes -> read back stream sizes ->
+  decode both planes -> restore the 16-bit words;
+* fixed codebook (``int8_fixed``, ``int8_acts``, ``int8_drift``): encode +
+  decode with a codebook built once from warm-up batches (untimed, as in
+  single-stage coding).
+
+Prints ONE JSON line.  ``value`` = uncompressed bytes / wall-clock step time
+(GB/s, 1e9).  Encode and decode rates, the ratio, per-kernel timings from HIP
+events on the launch stream, the roofline of the dominant kernel and the CPU
+oracle baseline (timed on host worker processes started before the GPU is
+touched) ride along.  Parity of the timed outputs is checked before anything
+is reported.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "encode / decode GB/s of uncompressed input on 1 MI355X; % of HBM peak; ratio"
+HBM_PEAK_GBPS = 8000.0
+
+
+# ============================================================================ CPU oracle baseline
+# Runs in spawned worker processes that import numpy + the oracle only.
+
+def _cpu_worker(args):
+    import oracle
+
+    kind, data, lengths, chunk = args
+    t0 = time.perf_counter()
+    if kind == "bytes":
+        ln = lengths[0]
+        s, _ = oracle.encode(data, ln, oracle.canonical_codes(ln), chunk)
+        t1 = time.perf_counter()
+        y = oracle.decode(s, ln, chunk, data.size)
+        t2 = time.perf_counter()
+        assert np.array_equal(y, data)
+    else:
+        hi, lo = oracle.split_bf16(data)
+        ss = []
+        for plane, ln in zip((hi, lo), lengths):
+            ss.append(oracle.encode(plane, ln, oracle.canonical_codes(ln), chunk)[0])
+        t1 = time.perf_counter()
+        ys = [oracle.decode(s, ln, chunk, data.size) for s, ln in zip(ss, lengths)]
+        t2 = time.perf_counter()
+        assert np.array_equal(oracle.merge_bf16(*ys), data)
+    return t1 - t0, t2 - t1
+
+
+def cpu_baseline(cfg: dict, x: np.ndarray, lengths, sample_elems: int) -> dict:
+    """Oracle encode + decode of a bounded sample, split over chunk ranges across host cores."""
+    import oracle
+
+    chunk = cfg["chunk"]
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    sample = x[:sample_elems]
+    t0 = time.perf_counter()
+    if cfg["kind"] == "bf16":
+        # per-tensor mode: the histograms and codebooks are part of the encode
+        hi, lo = oracle.split_bf16(sample)
+        lengths = [oracle.package_merge_lengths(oracle.histogram(p), 16) for p in (hi, lo)]
+    t_build = time.perf_counter() - t0
+    per = -(-sample.size // cores)
+    per = -(-per // chunk) * chunk
+    jobs = [("bytes" if cfg["kind"] == "u8" else "bf16", sample[i:i + per], lengths, chunk)
+            for i in range(0, sample.size, per)]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(jobs)) as pool:
+        times = pool.map(_cpu_worker, jobs)
+    wall = time.perf_counter() - t0
+    enc = max(t[0] for t in times) + t_build
+    dec = max(t[1] for t in times)
+    nbytes = sample.size * sample.itemsize
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(nbytes / (enc + dec) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": f"first {sample.size} elements ({nbytes} bytes) of the same tensor, "
+                  f"{len(jobs)} worker processes over chunk ranges",
+        "encode_GBps": round(nbytes / enc / 1e9, 4),
+        "decode_GBps": round(nbytes / dec / 1e9, 4),
+        "wall_s": round(wall, 2),
+        "cpu_model": cpu_model,
+    }
+
+
+# ============================================================================ inputs
+
+def make_input(name: str, scale: float):
+    cfg = dict(workloads.CONFIGS[name])
+    n = int(cfg["n"] * scale)
+    n = max(cfg["chunk"], n // cfg["chunk"] * cfg["chunk"]) if scale < 1 else cfg["n"]
+    cfg["n"] = n
+    lengths = None
+    if name == "int8_fixed":
+        x = workloads.int8_fixed(0, n)
+        warm = [np.bincount(workloads.int8_fixed(r, n), minlength=256) for r in (1, 2, 3, 4)]
+        hist = np.sum(warm, axis=0).astype(np.uint64)
+    elif name == "int8_acts":
+        rows = n // 2048
+        x = workloads.int8_acts(0, rows)
+        warm = [np.bincount(workloads.int8_acts(r, rows), minlength=256) for r in (1, 2, 3, 4)]
+        hist = np.sum(warm, axis=0).astype(np.uint64)
+    elif name == "int8_drift":
+        batch = min(workloads.BLOCK, n)
+        x = np.concatenate([workloads.int8_drift_batch(k, batch) for k in range(n // batch)])
+        hist = np.bincount(x[:batch], minlength=256).astype(np.uint64)
+    elif name == "bf16_weights":
+        x = workloads.bf16_weights(n)
+        hist = None
+    elif name == "bf16_delta":
+        x = workloads.bf16_delta(n)
+        hist = None
+    else:
+        raise SystemExit(f"unknown config {name}")
+    return cfg, x, hist
+
+
+# ============================================================================ GPU runs
+
+class Timer:
+    """HIP events on the launch stream, one list of (start, stop) per label."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def start(self, label):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(label, []).append([e, None])
+
+    def stop(self, label):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[label][-1][1] = e
+
+    def mean_ms(self, label, skip=0):
+        ps = self.pairs.get(label, [])[skip:]
+        return float(np.mean([a.elapsed_time(b) for a, b in ps])) if ps else 0.0
+
+
+def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
+    import torch
+    import lossless_entropy_coding_byte_amd as lecb
+    import oracle
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    chunk, n = cfg["chunk"], cfg["n"]
+    T = Timer(torch)
+    info = {}
+    if cfg["kind"] == "bf16":
+        xd = torch.from_numpy(x.view(np.int16)).to(dev)
+        hist_d = torch.zeros(512, dtype=torch.int64, device=dev)
+        blob_hi, blob_lo = lecb.new_codebook_blob(dev), lecb.new_codebook_blob(dev)
+        cap = lecb.lecb_encoded_bound(n, chunk)
+        out_hi = torch.empty(cap, dtype=torch.uint8, device=dev)
+        out_lo = torch.empty(cap, dtype=torch.uint8, device=dev)
+        res = lecb.new_results(2, dev)
+        res_dec = lecb.new_results(2, dev)
+        ws = lecb.new_workspace(n, chunk, dev)
+        y = torch.empty(n, dtype=torch.int16, device=dev)
+        scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=dev)
+        state = {}
+
+        def step():
+            T.start("encode")
+            T.start("histogram")
+            lecb.lecb_histogram_bf16(xd, hist_d[:256], hist_d[256:])
+            T.stop("histogram")
+            h = hist_d.cpu().numpy().astype(np.uint64)
+            cb_hi = lecb.lecb_build_codebook(h[:256], 16, 0)
+            cb_lo = lecb.lecb_build_codebook(h[256:], 16, 0)
+            lecb.lecb_codebook_upload(cb_hi, blob_hi)
+            lecb.lecb_codebook_upload(cb_lo, blob_lo)
+            T.start("encode_hi")
+            lecb.lecb_encode_plane(xd, n, 1, blob_hi, chunk, out_hi, res[:24], ws)
+            T.stop("encode_hi")
+            T.start("encode_lo")
+            lecb.lecb_encode_plane(xd, n, 0, blob_lo, chunk, out_lo, res[24:], ws)
+            T.stop("encode_lo")
+            T.stop("encode")
+            r = lecb.results_to_numpy(res)
+            T.start("decode")
+            T.start("decode_hi")
+            lecb.lecb_decode(out_hi, int(r[0]["bytes"]), blob_hi, chunk, n, scratch, res_dec[:24], ws)
+            T.stop("decode_hi")
+            half = (n + 15) // 16 * 16
+            T.start("decode_lo")
+            lecb.lecb_decode(out_lo, int(r[1]["bytes"]), blob_lo, chunk, n, scratch[half:], res_dec[24:], ws)
+            T.stop("decode_lo")
+            T.start("merge")
+            lecb.lecb_merge_bf16(scratch[:n], scratch[half:half + n], y)
+            T.stop("merge")
+            T.stop("decode")
+            state.update(r=r, cb_hi=cb_hi, cb_lo=cb_lo)
+
+        nbytes = 2 * n
+    else:
+        xd = torch.from_numpy(x).to(dev)
+        cb = lecb.lecb_build_codebook(hist, 16, 1)
+        dcb = lecb.DeviceCodebook.upload(cb, dev)
+        cap = lecb.lecb_encoded_bound(n, chunk)
+        out = torch.empty(cap, dtype=torch.uint8, device=dev)
+        res = lecb.new_results(1, dev)
+        res_dec = lecb.new_results(1, dev)
+        ws = lecb.new_workspace(n, chunk, dev)
+        y = torch.empty(n, dtype=torch.uint8, device=dev)
+        state = {"cb": cb}
+
+        def step():
+            T.start("encode")
+            lecb.lecb_encode(xd, n, dcb.blob, chunk, out, res, ws)
+            T.stop("encode")
+            r = lecb.results_to_numpy(res)
+            T.start("decode")
+            lecb.lecb_decode(out, int(r[0]["bytes"]), dcb.blob, chunk, n, y, res_dec, ws)
+            T.stop("decode")
+            state.update(r=r)
+
+        nbytes = n
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    T.pairs.clear()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # ---------------- parity of the timed outputs
+    rd = lecb.results_to_numpy(res_dec)
+    r = state["r"]
+    parity = {"round_trip": bool(torch.equal(y.view(-1)[: n], xd.view(-1)[: n])),
+              "device_status": [int(v) for v in list(r["status"]) + list(rd["status"])]}
+    if cfg["kind"] == "bf16":
+        hi, lo = oracle.split_bf16(x)
+        ok_len = True
+        streams = [(out_hi, r[0], hi, state["cb_hi"]), (out_lo, r[1], lo, state["cb_lo"])]
+        for _, _, plane, cbx in streams:
+            ok_len &= bool(np.array_equal(cbx.lengths(), oracle.package_merge_lengths(oracle.histogram(plane), 16)))
+        parity["codebooks_match_oracle"] = ok_len
+        sizes = [int(r[0]["bytes"]), int(r[1]["bytes"])]
+        container = 560 + (sizes[0] + 15) // 16 * 16 + sizes[1]
+        lengths_out.extend([state["cb_hi"].lengths(), state["cb_lo"].lengths()])
+    else:
+        streams = [(out, r[0], x, state["cb"])]
+        sizes = [int(r[0]["bytes"])]
+        container = sizes[0]
+        lengths_out.append(state["cb"].lengths())
+    # sampled chunks, bit-exact against the oracle (chunk payloads are independent)
+    rng = np.random.default_rng(1234)
+    nc = oracle.num_chunks(n, chunk)
+    picks = sorted(set([0, nc - 1] + list(rng.integers(0, nc, 6))))
+    exact = True
+    for buf, rr, plane, cbx in streams:
+        ln = cbx.lengths()
+        cd = oracle.canonical_codes(ln)
+        tb, hb = oracle.table_bytes(n, chunk), oracle.header_bytes(n, chunk)
+        table = buf[: 4 * nc].cpu().numpy().view("<u4").astype(np.int64)
+        K = oracle.units_per_chunk(chunk)
+        gaps = buf[tb:tb + (nc * K + 1) // 2].cpu().numpy()
+        for c in picks:
+            one, _ = oracle.encode(plane[c * chunk:(c + 1) * chunk], ln, cd, chunk)
+            s0 = int(table[c - 1]) if c else 0
+            words = buf[hb + 4 * s0: hb + 4 * int(table[c])].cpu().numpy()
+            exact &= bool(np.array_equal(one[32:], words))
+            g = np.empty(2 * gaps.size, np.uint8); g[0::2] = gaps & 15; g[1::2] = gaps >> 4
+            og = one[16:16 + (K + 1) // 2]
+            go = np.empty(2 * og.size, np.uint8); go[0::2] = og & 15; go[1::2] = og >> 4
+            exact &= bool(np.array_equal(g[c * K:(c + 1) * K], go[:K]))
+        wc = oracle.chunk_word_counts(plane, ln, chunk)
+        exact &= bool(np.array_equal(table, np.cumsum(wc)))
+    parity["sampled_chunks_bit_exact"] = exact
+    parity["tables_match_oracle"] = exact
+
+    # ---------------- timings
+    ms_step = wall / steps * 1e3
+    enc_ms, dec_ms = T.mean_ms("encode"), T.mean_ms("decode")
+    kernels = {}
+    for label in T.pairs:
+        if label in ("encode", "decode"):
+            continue
+        kernels[label] = T.mean_ms(label)
+    info.update(
+        nbytes=nbytes, ms_step=ms_step, enc_ms=enc_ms, dec_ms=dec_ms, kernels=kernels,
+        sizes=sizes, container=container, parity=parity,
+        payload_bits=[int(v["payload_bits"]) for v in r],
+    )
+    return info
+
+
+def roofline(cfg, info):
+    """Dominant kernel's achieved algorithmic GB/s against the 8 TB/s HBM peak."""
+    n = cfg["n"]
+    k = info["kernels"]
+    if cfg["kind"] == "bf16":
+        s_hi, s_lo = info["sizes"]
+        algo = {
+            # plane encode reads the 16-bit words (both bytes share each word) and writes its stream
+            "encode_hi": 2 * n + s_hi, "encode_lo": 2 * n + s_lo,
+            # plane decode reads its stream and writes one byte per element
+            "decode_hi": s_hi + n, "decode_lo": s_lo + n,
+            "histogram": 2 * n, "merge": 4 * n,
+        }
+    else:
+        s = info["sizes"][0]
+        algo = {"encode": n + s, "decode": s + n}
+        k = {"encode": info["enc_ms"], "decode": info["dec_ms"]}
+    dom = max(k, key=lambda lbl: k[lbl])
+    ach = algo[dom] / (k[dom] * 1e-3) / 1e9
+    per_kernel = {lbl: {"ms": round(k[lbl], 4), "GBps": round(algo[lbl] / (k[lbl] * 1e-3) / 1e9, 1),
+                        "frac": round(algo[lbl] / (k[lbl] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                  for lbl in k if lbl in algo and k[lbl] > 0}
+    return {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": int(algo[dom])}, per_kernel
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="bf16_weights", choices=list(workloads.CONFIGS))
+    ap.add_argument("--scale", type=float, default=1.0, help="fraction of the config's size (tests)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 23, help="elements the oracle baseline codes")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the codec shards by whole chunks; see the multi-GPU notes of the design)", file=sys.stderr)
+        sys.exit(2)
+
+    cfg, x, hist = make_input(args.config, args.scale)
+
+    # CPU baseline first: the worker processes start before this process touches the GPU.
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        if cfg["kind"] == "u8":
+            lens = [oracle.package_merge_lengths(oracle.codebook_frequencies([hist], 1), 16)]
+        else:
+            lens = None
+        cpu = cpu_baseline(cfg, x, lens, min(args.cpu_sample, x.size))
+
+    lengths = []
+    info = run_gpu(cfg, x, hist, args.steps, args.warmup, lengths)
+    roof, per_kernel = roofline(cfg, info)
+    nbytes = info["nbytes"]
+    value = nbytes / (info["ms_step"] * 1e-3) / 1e9
+    enc_gbps = nbytes / (info["enc_ms"] * 1e-3) / 1e9
+    dec_gbps = nbytes / (info["dec_ms"] * 1e-3) / 1e9
+    ok = info["parity"]["round_trip"] and info["parity"]["sampled_chunks_bit_exact"] and not any(info["parity"]["device_status"])
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(info["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": args.config, "elements": cfg["n"], "element_bytes": x.itemsize,
+                   "chunk": cfg["chunk"], "mode": cfg["mode"], "max_len": 16},
+        "encode_GBps": round(enc_gbps, 2),
+        "decode_GBps": round(dec_gbps, 2),
+        "encode_ms": round(info["enc_ms"], 4),
+        "decode_ms": round(info["dec_ms"], 4),
+        "ratio": round(nbytes / info["container"], 4),
+        "bits_per_symbol": [round(b / cfg["n"], 4) for b in info["payload_bits"]],
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": info["parity"],
+        "parity_ok": bool(ok),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

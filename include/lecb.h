@@ -1,0 +1,232 @@
+/*
+ * lecb.h -- C ABI of the MI355X (gfx950) Huffman byte codec.
+ *
+ * What it computes
+ * ----------------
+ * Lossless Huffman coding of 8-bit tensor symbols, two ways:
+ *
+ *  - fixed-codebook, single-stage coding ("Single-Stage Huffman Encoder for
+ *    ML Compression", Methodology steps 1-4): symbol statistics of a few
+ *    warm-up batches are summed, one canonical codebook is built from them
+ *    once and kept on the device, and every later tensor is coded with it
+ *    directly -- no per-tensor histogram, no codebook in the stream;
+ *
+ *  - byte-grouped, per-tensor coding of bf16 tensors ("Lossless Compression
+ *    for LLM Tensor Incremental Snapshots", Technical framework steps 1-3 and
+ *    the reverse path): the 16-bit words are split into a high-byte and a
+ *    low-byte plane, each plane gets its own histogram and its own codebook,
+ *    and decoding restores the 16-bit words.
+ *
+ * Stream format v1 (identical, bit for bit, to the oracle's):
+ *   stream  = u32 end[nc] | zero pad to 16 B | gap nibbles[nc*K] | zero pad to 16 B | u32 payload[W]
+ *   nc      = ceil(n / chunk); chunk c holds symbols [c*chunk, min((c+1)*chunk, n));
+ *   end[c]  = payload word one past chunk c's last word (chunk c spans
+ *             [end[c-1], end[c]) with end[-1] = 0); W = end[nc-1];
+ *   payload = per chunk, the code words of its symbols concatenated, most
+ *             significant bit first within 32-bit words (words stored
+ *             little-endian), starting on a fresh word, last word zero-padded;
+ *   gaps    = K = chunk/256 decode units per chunk; unit j of a chunk with
+ *             Wc words starts at bit s_j = 32*floor(j*Wc/K); its gap (0..15)
+ *             is the distance from s_j to the first code-word boundary at or
+ *             after s_j (code-word starts and the chunk's data end count);
+ *             nibble i = c*K + j is the low half of byte i/2 if i is even;
+ *   size    = align16(4*nc) + align16(ceil(nc*K/2)) + 4*W  (0 when n == 0).
+ * The codebook is not in the stream.  Code words are canonical: they follow
+ * from the 256 code lengths alone (shorter codes first, ties by symbol).
+ *
+ * Conventions
+ * -----------
+ *  - Every buffer is owned by the caller.  Device pointers are HIP device
+ *    memory on the current device, 16-byte aligned.  `stream` arguments are
+ *    hipStream_t passed as void* (NULL = the null stream).
+ *  - Device entry points only enqueue work on `stream`; they never
+ *    synchronise and never allocate.  The one exception is
+ *    lecb_encode_bf16_pertensor, which must read the histograms back.
+ *  - Return values: LECB_OK or a negative lecb_status detected on the host
+ *    (bad argument, too small a buffer).  Problems only the GPU can see
+ *    (a byte with no code word, a corrupt stream, output overflow) are
+ *    written to lecb_result.status in device memory; read it after
+ *    synchronising.  On any error the output contents are undefined.
+ *  - A workspace (lecb_workspace_bytes) must be zero-filled once, e.g. with
+ *    lecb_workspace_init, before its first use.  Every call leaves it ready
+ *    for the next.  Calls that overlap in time must not share a workspace.
+ *  - chunk must be a power of two in [LECB_MIN_CHUNK, LECB_MAX_CHUNK].
+ */
+#ifndef LECB_H
+#define LECB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LECB_ABI_VERSION 1u
+#define LECB_MAX_CODE_LEN 16u
+#define LECB_UNIT_SYMBOLS 256u
+#define LECB_MIN_CHUNK 256u
+#define LECB_MAX_CHUNK 65536u
+#define LECB_CONTAINER_HEADER_BYTES 560u
+
+typedef enum {
+    LECB_OK = 0,
+    LECB_ERR_INVALID_ARG = -1,    /* null/misaligned pointer, bad chunk or max_len */
+    LECB_ERR_CAPACITY = -2,       /* output buffer too small (host or device check) */
+    LECB_ERR_TOO_LARGE = -3,      /* payload would need >= 2^32 words */
+    LECB_ERR_NO_SYMBOLS = -4,     /* histogram empty, or more coded symbols than 2^max_len */
+    LECB_ERR_HIP = -5,            /* a HIP runtime call failed */
+    LECB_ERR_WORKSPACE = -6,      /* workspace too small */
+    LECB_ERR_UNCODED_SYMBOL = -16,/* device: input holds a byte whose code length is 0 */
+    LECB_ERR_CORRUPT = -17        /* device: stream is not a valid v1 stream for these arguments */
+} lecb_status;
+
+/* Canonical codebook, host side.  Fully determined by len[]. */
+typedef struct {
+    uint32_t max_len;     /* length limit it was built with (1..16) */
+    uint32_t num_coded;   /* symbols with len > 0 */
+    uint8_t len[256];     /* code length per byte value; 0 = no code word */
+    uint16_t code[256];   /* right-aligned code word; its MSB is the first bit emitted */
+} lecb_codebook;
+
+/* Written by the device at the end of a call (read it after synchronising). */
+typedef struct {
+    uint64_t bytes;        /* encode: stream size in bytes; decode: stream bytes used */
+    uint64_t payload_bits; /* exact coded bits = sum over symbols of their code length */
+    int32_t status;        /* LECB_OK or a device-detected lecb_status */
+    uint32_t reserved;
+} lecb_result;
+
+/* ------------------------------------------------------------------ host only, pure */
+
+uint32_t lecb_abi_version(void);
+const char* lecb_status_str(int status);
+
+/* ceil(n / chunk); 0 on a bad chunk. */
+uint64_t lecb_num_chunks(uint64_t n, uint32_t chunk);
+/* Bytes before the payload: align16(4*nc) + align16(ceil(nc*K/2)). */
+uint64_t lecb_header_bytes(uint64_t n, uint32_t chunk);
+/* Largest stream any codebook with lengths <= max_len can produce:
+ * header + 4*(ceil(n*max_len/32) + nc).  0 on bad arguments. */
+uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len);
+/* Workspace bytes an encode or decode of n symbols with this chunk needs. */
+uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk);
+
+/* Build a canonical, length-limited optimal codebook from a histogram.
+ * Frequencies are first raised to at least min_freq (min_freq = 1 gives every
+ * byte value a code word, as a fixed codebook needs; 0 keeps absent symbols
+ * uncoded).  Lengths minimise sum(F*len) subject to len <= max_len
+ * (package-merge; ties: lower frequency, then lower byte value, merges first;
+ * a single coded symbol gets length 1).  Basis: "Single-Stage Huffman Encoder
+ * for ML Compression", Methodology steps 2-3; "Lossless Compression for LLM
+ * Tensor Incremental Snapshots", Technical framework step 3.
+ * Errors: INVALID_ARG (null, max_len not in 1..16), NO_SYMBOLS (all zero, or
+ * more than 2^max_len coded symbols). */
+int lecb_build_codebook(const uint64_t hist[256], uint32_t max_len, uint32_t min_freq,
+                        lecb_codebook* out);
+
+/* Canonical codes for given lengths (decoder side, or a stored container).
+ * Errors: INVALID_ARG if a length exceeds 16 or the lengths violate Kraft. */
+int lecb_codebook_from_lengths(const uint8_t len[256], lecb_codebook* out);
+
+/* Size of the device-resident codebook (encode table + decode tables). */
+uint64_t lecb_device_codebook_bytes(void);
+
+/* Bf16 container header (per-tensor mode stores its two length tables):
+ * magic "LECB", u16 version 1, u16 kind 1, u64 n, u32 chunk, u32 max_len,
+ * u8 len_hi[256], u8 len_lo[256], u64 bytes_hi, u64 bytes_lo, zero pad to
+ * 560 bytes; stream_hi follows, zero-padded to 16 bytes, then stream_lo. */
+int lecb_container_write_header(uint8_t out[LECB_CONTAINER_HEADER_BYTES], uint64_t n,
+                                uint32_t chunk, uint32_t max_len, const uint8_t len_hi[256],
+                                const uint8_t len_lo[256], uint64_t bytes_hi, uint64_t bytes_lo);
+int lecb_container_read_header(const uint8_t in[LECB_CONTAINER_HEADER_BYTES], uint64_t* n,
+                               uint32_t* chunk, uint32_t* max_len, uint8_t len_hi[256],
+                               uint8_t len_lo[256], uint64_t* bytes_hi, uint64_t* bytes_lo);
+
+/* ------------------------------------------------------------------ device, asynchronous */
+
+/* Zero-fill a workspace (a fill kernel, no memset node). */
+int lecb_workspace_init(void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* Place a codebook on the device: "stored on each accelerator" ("Single-Stage
+ * Huffman Encoder for ML Compression", Methodology step 3).  d_blob holds
+ * lecb_device_codebook_bytes() bytes; the tables are built by a kernel from
+ * the codebook passed by value, so `cb` may be reused as soon as this returns. */
+int lecb_codebook_upload(const lecb_codebook* cb, void* d_blob, void* stream);
+
+/* Byte histogram f[s] = #{i : in[i] == s} as u64[256] ("frequency analysis",
+ * "Single-Stage Huffman Encoder for ML Compression", Overview and Methodology
+ * step 1).  accumulate = 0 overwrites d_hist, 1 adds to it. */
+int lecb_histogram(const uint8_t* d_in, uint64_t n, uint64_t* d_hist, int accumulate,
+                   void* stream);
+/* Histograms of the high and low byte planes of 16-bit words in one pass
+ * ("Lossless Compression for LLM Tensor Incremental Snapshots", Technical
+ * framework steps 1-2). */
+int lecb_histogram_bf16(const uint16_t* d_in, uint64_t n, uint64_t* d_hist_hi,
+                        uint64_t* d_hist_lo, int accumulate, void* stream);
+
+/* Byte grouping: hi[i] = in[i] >> 8, lo[i] = in[i] & 0xFF, and its inverse
+ * ("Lossless Compression for LLM Tensor Incremental Snapshots", Technical
+ * framework step 1 and the byte-group restore of the reverse path). */
+int lecb_split_bf16(const uint16_t* d_in, uint64_t n, uint8_t* d_hi, uint8_t* d_lo,
+                    void* stream);
+int lecb_merge_bf16(const uint8_t* d_hi, const uint8_t* d_lo, uint64_t n, uint16_t* d_out,
+                    void* stream);
+
+/* Encode n bytes with an uploaded codebook into a v1 stream ("Single-Stage
+ * Huffman Encoder for ML Compression", Methodology step 4).  out_capacity must
+ * be at least lecb_header_bytes(n, chunk); a payload that does not fit sets
+ * status CAPACITY (lecb_encoded_bound gives a size that always fits).
+ * d_res receives bytes, payload_bits, status. */
+int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t chunk,
+                uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
+                uint64_t ws_bytes, void* stream);
+
+/* Decode a v1 stream of n symbols into d_out[n] (reverse path of "Lossless
+ * Compression for LLM Tensor Incremental Snapshots", Technical framework).
+ * stream_bytes must be the exact stream size (lecb_result.bytes of the
+ * encode); it bounds every read.  A size below the header or not a whole
+ * number of payload words returns LECB_ERR_CORRUPT at once.  A stream that is not exactly what
+ * lecb_encode produces for these arguments sets status CORRUPT (offset table
+ * not increasing or past the stream, a bit pattern with no code word, a code
+ * word crossing a unit or chunk end, a gap that is not the first boundary,
+ * non-zero padding, too many words). */
+int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_blob,
+                uint32_t chunk, uint64_t n, uint8_t* d_out, lecb_result* d_res, void* d_ws,
+                uint64_t ws_bytes, void* stream);
+
+/* Encode one byte plane of 16-bit words without materialising it:
+ * plane 1 = high bytes (in >> 8), plane 0 = low bytes (in & 0xFF). */
+int lecb_encode_plane(const uint16_t* d_in, uint64_t n, int plane, const void* d_blob,
+                      uint32_t chunk, uint8_t* d_out, uint64_t out_capacity,
+                      lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* Per-tensor bf16 encode, the classic three steps ("Single-Stage Huffman
+ * Encoder for ML Compression", Overview) on byte planes ("Lossless
+ * Compression for LLM Tensor Incremental Snapshots", Technical framework):
+ * one-pass plane histograms -> read back (synchronises `stream` once) ->
+ * host codebook per plane (no clamp, length limit max_len) -> upload ->
+ * encode each plane.  cb_hi / cb_lo (host) receive the codebooks, whose
+ * lengths a container stores.  d_hist: 512 u64 of device scratch (high
+ * plane histogram in [0, 256), low plane in [256, 512)).
+ * d_res2: two lecb_result (hi, lo).  d_blob_hi/lo: device codebooks.
+ * d_ws: lecb_workspace_bytes(n, chunk) (the two planes use it in turn). */
+int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
+                               uint32_t max_len, uint64_t* d_hist, void* d_blob_hi,
+                               void* d_blob_lo, lecb_codebook* cb_hi, lecb_codebook* cb_lo,
+                               uint8_t* d_out_hi, uint64_t cap_hi, uint8_t* d_out_lo,
+                               uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
+                               uint64_t ws_bytes, void* stream);
+
+/* Decode both planes and restore the 16-bit words.  d_scratch: 2*align16(n)
+ * bytes of device memory for the decoded planes.  d_ws: lecb_workspace_bytes(n, chunk). */
+int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
+                     uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
+                     uint32_t chunk, uint64_t n, uint16_t* d_out, uint8_t* d_scratch,
+                     lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LECB_H */

@@ -1,0 +1,252 @@
+// C ABI: argument checks, sizes, workspace, launches.  No device allocation,
+// no implicit synchronisation (lecb_encode_bf16_pertensor aside).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "lecb.h"
+#include "lecb_internal.hpp"
+
+using namespace lecb;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint64_t num_chunks_checked(uint64_t n, uint32_t chunk) {
+    return valid_chunk(chunk) ? (n + chunk - 1) / chunk : 0;
+}
+
+uint64_t header_of(uint64_t n, uint32_t chunk) {
+    const uint64_t nc = num_chunks_checked(n, chunk);
+    return nc ? table_bytes(nc) + gap_bytes(nc, chunk) : 0;
+}
+
+uint64_t ws_bytes_of(uint64_t n, uint32_t chunk) {
+    const uint64_t nc = num_chunks_checked(n, chunk);
+    return (sizeof(WsHeader) + 8 * nc + 255) & ~uint64_t(255);
+}
+
+int build_args(const lecb_codebook* cb, CodebookArgs* a) {
+    lecb_codebook canon;
+    const int rc = canonical_from_lengths(cb->len, &canon);
+    if (rc != LECB_OK) return rc;
+    std::memset(a, 0, sizeof(*a));
+    for (int s = 0; s < 256; ++s) {
+        a->enc[s] = canon.len[s] ? ((uint32_t)canon.code[s] << 5) | canon.len[s] : 0u;
+        if (canon.len[s]) ++a->count[canon.len[s]];
+    }
+    uint32_t code = 0, idx = 0;
+    for (int l = 1; l <= 16; ++l) {
+        code = (code + a->count[l - 1]) << 1;
+        a->first[l] = code;
+        a->base[l] = idx;
+        idx += a->count[l];
+    }
+    uint32_t fill[17];
+    std::memcpy(fill, a->base, sizeof(fill));
+    for (int s = 0; s < 256; ++s)
+        if (canon.len[s]) a->sorted[fill[canon.len[s]]++] = (uint8_t)s;
+    a->max_len = 0;
+    for (int s = 0; s < 256; ++s) a->max_len = std::max<uint32_t>(a->max_len, canon.len[s]);
+    a->num_coded = canon.num_coded;
+    return LECB_OK;
+}
+
+int encode_common(const void* d_in, int plane, uint64_t n, const void* d_blob, uint32_t chunk,
+                  uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
+                  uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || !d_res || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
+    if (n == 0) return launch_result(d_res, 0, 0, LECB_OK, stream);
+    if (!d_in || !d_out || !d_ws || !aligned16(d_in) || !aligned16(d_out) || !aligned16(d_ws))
+        return LECB_ERR_INVALID_ARG;
+    const uint64_t nc = num_chunks_checked(n, chunk);
+    if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
+    if (out_capacity < header_of(n, chunk)) return LECB_ERR_CAPACITY;
+    EncodeLaunch L{};
+    L.in = d_in;
+    L.plane = plane;
+    L.n = n;
+    L.chunk = chunk;
+    L.nc = nc;
+    L.cb = reinterpret_cast<const DeviceCodebook*>(d_blob);
+    L.out = d_out;
+    L.capacity = out_capacity;
+    L.res = d_res;
+    L.ws = reinterpret_cast<WsHeader*>(d_ws);
+    L.grid = (int)std::min<uint64_t>(nc, (uint64_t)device_cu_count() * 8);
+    return launch_encode(L, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t lecb_abi_version(void) { return LECB_ABI_VERSION; }
+
+const char* lecb_status_str(int status) {
+    switch (status) {
+        case LECB_OK: return "ok";
+        case LECB_ERR_INVALID_ARG: return "invalid argument";
+        case LECB_ERR_CAPACITY: return "output capacity too small";
+        case LECB_ERR_TOO_LARGE: return "payload needs 2^32 words or more";
+        case LECB_ERR_NO_SYMBOLS: return "no codebook possible for this histogram";
+        case LECB_ERR_HIP: return "HIP runtime error";
+        case LECB_ERR_WORKSPACE: return "workspace too small";
+        case LECB_ERR_UNCODED_SYMBOL: return "input holds a byte with no code word";
+        case LECB_ERR_CORRUPT: return "corrupt stream";
+        default: return "unknown status";
+    }
+}
+
+uint64_t lecb_num_chunks(uint64_t n, uint32_t chunk) { return num_chunks_checked(n, chunk); }
+
+uint64_t lecb_header_bytes(uint64_t n, uint32_t chunk) { return header_of(n, chunk); }
+
+uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16) return 0;
+    const uint64_t nc = num_chunks_checked(n, chunk);
+    if (!nc) return 0;
+    return header_of(n, chunk) + 4 * ((n * max_len + 31) / 32 + nc);
+}
+
+uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk) {
+    return valid_chunk(chunk) ? ws_bytes_of(n, chunk) : 0;
+}
+
+uint64_t lecb_device_codebook_bytes(void) { return sizeof(DeviceCodebook); }
+
+int lecb_workspace_init(void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!d_ws || !aligned16(d_ws) || ws_bytes < sizeof(WsHeader)) return LECB_ERR_INVALID_ARG;
+    return launch_fill_zero(d_ws, ws_bytes, stream);
+}
+
+int lecb_codebook_upload(const lecb_codebook* cb, void* d_blob, void* stream) {
+    if (!cb || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
+    CodebookArgs args;
+    const int rc = build_args(cb, &args);
+    if (rc != LECB_OK) return rc;
+    return launch_codebook_upload(args, reinterpret_cast<DeviceCodebook*>(d_blob), stream);
+}
+
+int lecb_histogram(const uint8_t* d_in, uint64_t n, uint64_t* d_hist, int accumulate,
+                   void* stream) {
+    if (!d_hist || !aligned16(d_hist) || (n && (!d_in || !aligned16(d_in))))
+        return LECB_ERR_INVALID_ARG;
+    return launch_histogram_u8(d_in, n, d_hist, accumulate, stream);
+}
+
+int lecb_histogram_bf16(const uint16_t* d_in, uint64_t n, uint64_t* d_hist_hi,
+                        uint64_t* d_hist_lo, int accumulate, void* stream) {
+    if (!d_hist_hi || !d_hist_lo || !aligned16(d_hist_hi) || !aligned16(d_hist_lo) ||
+        (n && (!d_in || !aligned16(d_in))))
+        return LECB_ERR_INVALID_ARG;
+    return launch_histogram_u16(d_in, n, d_hist_hi, d_hist_lo, accumulate, stream);
+}
+
+int lecb_split_bf16(const uint16_t* d_in, uint64_t n, uint8_t* d_hi, uint8_t* d_lo,
+                    void* stream) {
+    if (n && (!d_in || !d_hi || !d_lo || !aligned16(d_in) || !aligned16(d_hi) || !aligned16(d_lo)))
+        return LECB_ERR_INVALID_ARG;
+    return launch_split(d_in, n, d_hi, d_lo, stream);
+}
+
+int lecb_merge_bf16(const uint8_t* d_hi, const uint8_t* d_lo, uint64_t n, uint16_t* d_out,
+                    void* stream) {
+    if (n && (!d_out || !d_hi || !d_lo || !aligned16(d_out) || !aligned16(d_hi) || !aligned16(d_lo)))
+        return LECB_ERR_INVALID_ARG;
+    return launch_merge(d_hi, d_lo, n, d_out, stream);
+}
+
+int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t chunk,
+                uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
+                uint64_t ws_bytes, void* stream) {
+    return encode_common(d_in, -1, n, d_blob, chunk, d_out, out_capacity, d_res, d_ws, ws_bytes,
+                         stream);
+}
+
+int lecb_encode_plane(const uint16_t* d_in, uint64_t n, int plane, const void* d_blob,
+                      uint32_t chunk, uint8_t* d_out, uint64_t out_capacity,
+                      lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (plane != 0 && plane != 1) return LECB_ERR_INVALID_ARG;
+    return encode_common(d_in, plane, n, d_blob, chunk, d_out, out_capacity, d_res, d_ws,
+                         ws_bytes, stream);
+}
+
+int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_blob,
+                uint32_t chunk, uint64_t n, uint8_t* d_out, lecb_result* d_res, void* d_ws,
+                uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || !d_res || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
+    if (n == 0)
+        return launch_result(d_res, 0, 0, stream_bytes == 0 ? LECB_OK : LECB_ERR_CORRUPT, stream);
+    if (!d_stream || !d_out || !d_ws || !aligned16(d_stream) || !aligned16(d_ws))
+        return LECB_ERR_INVALID_ARG;
+    const uint64_t hb = header_of(n, chunk);
+    if (stream_bytes < hb + 4 || (stream_bytes - hb) % 4) return LECB_ERR_CORRUPT;
+    if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
+    DecodeLaunch L{};
+    L.stream_base = d_stream;
+    L.stream_bytes = stream_bytes;
+    L.cb = reinterpret_cast<const DeviceCodebook*>(d_blob);
+    L.chunk = chunk;
+    L.n = n;
+    L.nc = num_chunks_checked(n, chunk);
+    L.out = d_out;
+    L.res = d_res;
+    L.ws = reinterpret_cast<WsHeader*>(d_ws);
+    return launch_decode(L, stream);
+}
+
+int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
+                               uint32_t max_len, uint64_t* d_hist, void* d_blob_hi,
+                               void* d_blob_lo, lecb_codebook* cb_hi, lecb_codebook* cb_lo,
+                               uint8_t* d_out_hi, uint64_t cap_hi, uint8_t* d_out_lo,
+                               uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
+                               uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) ||
+        !cb_hi || !cb_lo || !d_res2)
+        return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        std::memset(cb_hi, 0, sizeof(*cb_hi));
+        std::memset(cb_lo, 0, sizeof(*cb_lo));
+        int rc = launch_result(d_res2, 0, 0, LECB_OK, stream);
+        return rc ? rc : launch_result(d_res2 + 1, 0, 0, LECB_OK, stream);
+    }
+    int rc = lecb_histogram_bf16(d_in, n, d_hist, d_hist + 256, 0, stream);
+    if (rc) return rc;
+    uint64_t h[512];
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(h, d_hist, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return LECB_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return LECB_ERR_HIP;
+    // d_hist[0:256] = high plane, d_hist[256:512] = low plane
+    rc = lecb_build_codebook(h, max_len, 0, cb_hi);
+    if (!rc) rc = lecb_build_codebook(h + 256, max_len, 0, cb_lo);
+    if (!rc) rc = lecb_codebook_upload(cb_hi, d_blob_hi, stream);
+    if (!rc) rc = lecb_codebook_upload(cb_lo, d_blob_lo, stream);
+    if (!rc)
+        rc = lecb_encode_plane(d_in, n, 1, d_blob_hi, chunk, d_out_hi, cap_hi, d_res2, d_ws,
+                               ws_bytes, stream);
+    if (!rc)
+        rc = lecb_encode_plane(d_in, n, 0, d_blob_lo, chunk, d_out_lo, cap_lo, d_res2 + 1, d_ws,
+                               ws_bytes, stream);
+    return rc;
+}
+
+int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
+                     uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
+                     uint32_t chunk, uint64_t n, uint16_t* d_out, uint8_t* d_scratch,
+                     lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!d_res2) return LECB_ERR_INVALID_ARG;
+    if (n && (!d_scratch || !aligned16(d_scratch) || !d_out || !aligned16(d_out)))
+        return LECB_ERR_INVALID_ARG;
+    uint8_t* hi = d_scratch;
+    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
+    int rc = lecb_decode(d_hi, hi_bytes, d_blob_hi, chunk, n, hi, d_res2, d_ws, ws_bytes, stream);
+    if (!rc) rc = lecb_decode(d_lo, lo_bytes, d_blob_lo, chunk, n, lo, d_res2 + 1, d_ws, ws_bytes, stream);
+    if (!rc) rc = lecb_merge_bf16(hi, lo, n, d_out, stream);
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,310 @@
+// Histogram, byte-group split/merge, device codebook construction, fill.
+//
+// Histogram: "Single-Stage Huffman Encoder for ML Compression", Overview
+// (frequency analysis) and Methodology step 1; "Lossless Compression for LLM
+// Tensor Incremental Snapshots", Technical framework step 2.  Byte grouping:
+// same page, Technical framework step 1 and the byte-group restore.
+#include <hip/hip_runtime.h>
+
+#include "lecb_internal.hpp"
+
+namespace lecb {
+
+namespace {
+
+constexpr int HIST_THREADS = 256;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+__device__ inline v4u ld_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+}
+__device__ inline void st_stream(void* p, v4u v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p));
+}
+
+// Each workgroup counts into LDS sub-histograms replicated R ways; lane l
+// uses replica l % R and bin b of replica r sits at word b*R + r, so the 32
+// lanes of a half-wave always hit 32 different banks whatever the data (a
+// skewed plane such as a snapshot delta's high bytes is ~98 % one value).
+template <int R>
+__device__ inline void hist_add(uint32_t* s, uint32_t word, int r) {
+    atomicAdd(&s[((word)&0xFFu) * R + r], 1u);
+    atomicAdd(&s[((word >> 8) & 0xFFu) * R + r], 1u);
+    atomicAdd(&s[((word >> 16) & 0xFFu) * R + r], 1u);
+    atomicAdd(&s[(word >> 24) * R + r], 1u);
+}
+
+template <int R>
+__device__ inline void hist_flush(const uint32_t* s, unsigned long long* out) {
+    const int b = threadIdx.x;  // HIST_THREADS == 256 bins
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) sum += s[b * R + ((k + b) & (R - 1))];
+    if (sum) atomicAdd(&out[b], (unsigned long long)sum);
+}
+
+__global__ __launch_bounds__(HIST_THREADS) void hist_u8_kernel(const uint8_t* __restrict__ in,
+                                                               uint64_t n,
+                                                               unsigned long long* hist) {
+    constexpr int R = 32;
+    __shared__ uint32_t s[256 * R];
+    for (int i = threadIdx.x; i < 256 * R; i += HIST_THREADS) s[i] = 0;
+    __syncthreads();
+    const int r = threadIdx.x & (R - 1);
+    const uint64_t n16 = n / 16;
+    const uint4* in4 = reinterpret_cast<const uint4*>(in);
+    const uint64_t stride = (uint64_t)gridDim.x * HIST_THREADS;
+    for (uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x; i < n16; i += stride) {
+        const v4u v = ld_stream(&in4[i]);
+        hist_add<R>(s, v.x, r);
+        hist_add<R>(s, v.y, r);
+        hist_add<R>(s, v.z, r);
+        hist_add<R>(s, v.w, r);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += HIST_THREADS)
+            atomicAdd(&s[in[i] * R + r], 1u);
+    }
+    __syncthreads();
+    hist_flush<R>(s, hist);
+}
+
+__global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* __restrict__ in,
+                                                                uint64_t n,
+                                                                unsigned long long* hist_hi,
+                                                                unsigned long long* hist_lo) {
+    constexpr int R = 16;
+    __shared__ uint32_t s_hi[256 * R];
+    __shared__ uint32_t s_lo[256 * R];
+    for (int i = threadIdx.x; i < 256 * R; i += HIST_THREADS) {
+        s_hi[i] = 0;
+        s_lo[i] = 0;
+    }
+    __syncthreads();
+    const int r = threadIdx.x & (R - 1);
+    const uint64_t n8 = n / 8;
+    const uint4* in4 = reinterpret_cast<const uint4*>(in);
+    const uint64_t stride = (uint64_t)gridDim.x * HIST_THREADS;
+    for (uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x; i < n8; i += stride) {
+        const v4u v = ld_stream(&in4[i]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            atomicAdd(&s_lo[(w[k] & 0xFFu) * R + r], 1u);
+            atomicAdd(&s_hi[((w[k] >> 8) & 0xFFu) * R + r], 1u);
+            atomicAdd(&s_lo[((w[k] >> 16) & 0xFFu) * R + r], 1u);
+            atomicAdd(&s_hi[(w[k] >> 24) * R + r], 1u);
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint64_t i = n8 * 8 + threadIdx.x; i < n; i += HIST_THREADS) {
+            atomicAdd(&s_lo[(in[i] & 0xFFu) * R + r], 1u);
+            atomicAdd(&s_hi[(in[i] >> 8) * R + r], 1u);
+        }
+    }
+    __syncthreads();
+    hist_flush<R>(s_hi, hist_hi);
+    hist_flush<R>(s_lo, hist_lo);
+}
+
+constexpr int BG_THREADS = 256;
+
+// 16 elements per thread: two 16-byte loads of u16, two 16-byte stores.
+__device__ inline uint32_t pick_lo(uint32_t a, uint32_t b) {
+    return (a & 0xFFu) | ((a >> 8) & 0xFF00u) | ((b & 0xFFu) << 16) | ((b << 8) & 0xFF000000u);
+}
+__device__ inline uint32_t pick_hi(uint32_t a, uint32_t b) {
+    return ((a >> 8) & 0xFFu) | ((a >> 16) & 0xFF00u) | ((b << 8) & 0xFF0000u) | (b & 0xFF000000u);
+}
+
+__global__ __launch_bounds__(BG_THREADS) void split_kernel(const uint16_t* __restrict__ in,
+                                                           uint64_t n, uint8_t* __restrict__ hi,
+                                                           uint8_t* __restrict__ lo) {
+    const uint64_t n16 = n / 16;
+    const uint64_t stride = (uint64_t)gridDim.x * BG_THREADS;
+    for (uint64_t i = (uint64_t)blockIdx.x * BG_THREADS + threadIdx.x; i < n16; i += stride) {
+        const v4u a = ld_stream(reinterpret_cast<const uint4*>(in) + 2 * i);
+        const v4u b = ld_stream(reinterpret_cast<const uint4*>(in) + 2 * i + 1);
+        v4u h, l;
+        l.x = pick_lo(a.x, a.y); l.y = pick_lo(a.z, a.w); l.z = pick_lo(b.x, b.y); l.w = pick_lo(b.z, b.w);
+        h.x = pick_hi(a.x, a.y); h.y = pick_hi(a.z, a.w); h.z = pick_hi(b.x, b.y); h.w = pick_hi(b.z, b.w);
+        st_stream(reinterpret_cast<uint4*>(hi) + i, h);
+        st_stream(reinterpret_cast<uint4*>(lo) + i, l);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += BG_THREADS) {
+            hi[i] = (uint8_t)(in[i] >> 8);
+            lo[i] = (uint8_t)(in[i] & 0xFF);
+        }
+    }
+}
+
+__device__ inline uint32_t join2(uint32_t h, uint32_t l, int half) {
+    // elements 2*half, 2*half+1 from byte pairs
+    const uint32_t hs = half ? (h >> 16) : h;
+    const uint32_t ls = half ? (l >> 16) : l;
+    return (ls & 0xFFu) | ((hs & 0xFFu) << 8) | ((ls & 0xFF00u) << 8) | ((hs & 0xFF00u) << 16);
+}
+
+__global__ __launch_bounds__(BG_THREADS) void merge_kernel(const uint8_t* __restrict__ hi,
+                                                           const uint8_t* __restrict__ lo,
+                                                           uint64_t n, uint16_t* __restrict__ out) {
+    const uint64_t n16 = n / 16;
+    const uint64_t stride = (uint64_t)gridDim.x * BG_THREADS;
+    for (uint64_t i = (uint64_t)blockIdx.x * BG_THREADS + threadIdx.x; i < n16; i += stride) {
+        const v4u h = ld_stream(reinterpret_cast<const uint4*>(hi) + i);
+        const v4u l = ld_stream(reinterpret_cast<const uint4*>(lo) + i);
+        v4u a, b;
+        a.x = join2(h.x, l.x, 0); a.y = join2(h.x, l.x, 1);
+        a.z = join2(h.y, l.y, 0); a.w = join2(h.y, l.y, 1);
+        b.x = join2(h.z, l.z, 0); b.y = join2(h.z, l.z, 1);
+        b.z = join2(h.w, l.w, 0); b.w = join2(h.w, l.w, 1);
+        st_stream(reinterpret_cast<uint4*>(out) + 2 * i, a);
+        st_stream(reinterpret_cast<uint4*>(out) + 2 * i + 1, b);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += BG_THREADS)
+            out[i] = (uint16_t)(((uint16_t)hi[i] << 8) | lo[i]);
+    }
+}
+
+// Device codebook: encode table and decode tables from the canonical
+// description passed by value.  Grid covers the LUT_SIZE lookup entries.
+__global__ __launch_bounds__(256) void codebook_kernel(CodebookArgs a, DeviceCodebook* cb) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < 256) {
+        cb->enc[t] = a.enc[t];
+        cb->sorted[t] = a.sorted[t];
+    }
+    if (t < 17) {
+        cb->first[t] = a.first[t];
+        cb->base[t] = a.base[t];
+        cb->limit[t] = t ? (a.first[t] + a.count[t]) << (16 - t) : 0;
+    }
+    if (t == 0) {
+        cb->max_len = a.max_len;
+        cb->num_coded = a.num_coded;
+        cb->pad[0] = cb->pad[1] = cb->pad[2] = 0;
+    }
+    if (t < LUT_SIZE) {
+        // canonical decode of the LUT_BITS-bit prefix t
+        uint16_t entry = 0;
+        for (int l = 1; l <= LUT_BITS; ++l) {
+            const uint32_t v = (uint32_t)t >> (LUT_BITS - l);
+            if (a.count[l] && v >= a.first[l] && v < a.first[l] + a.count[l]) {
+                entry = (uint16_t)((l << 8) | a.sorted[a.base[l] + v - a.first[l]]);
+                break;
+            }
+        }
+        cb->lut[t] = entry;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* p, uint64_t bytes) {
+    const uint64_t n16 = bytes / 16;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    const uint4 z = {0, 0, 0, 0};
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        reinterpret_cast<uint4*>(p)[i] = z;
+    if (blockIdx.x == 0)
+        for (uint64_t i = n16 * 16 + threadIdx.x; i < bytes; i += blockDim.x) p[i] = 0;
+}
+
+__global__ void result_kernel(lecb_result* r, uint64_t bytes, uint64_t bits, int32_t status) {
+    r->bytes = bytes;
+    r->payload_bits = bits;
+    r->status = status;
+    r->reserved = 0;
+}
+
+int grid_for(uint64_t items, int threads, int max_blocks) {
+    uint64_t g = (items + threads - 1) / threads;
+    if (g < 1) g = 1;
+    if (g > (uint64_t)max_blocks) g = max_blocks;
+    return (int)g;
+}
+
+}  // namespace
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+int launch_histogram_u8(const uint8_t* in, uint64_t n, uint64_t* hist, int accumulate,
+                        void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!accumulate) {
+        int rc = launch_fill_zero(hist, 256 * sizeof(uint64_t), stream);
+        if (rc) return rc;
+    }
+    if (n == 0) return LECB_OK;
+    const int grid = grid_for(n / 16 + 1, HIST_THREADS * 8, device_cu_count() * 4);
+    hipLaunchKernelGGL(hist_u8_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, n,
+                       reinterpret_cast<unsigned long long*>(hist));
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_histogram_u16(const uint16_t* in, uint64_t n, uint64_t* hist_hi, uint64_t* hist_lo,
+                         int accumulate, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!accumulate) {
+        int rc = launch_fill_zero(hist_hi, 256 * sizeof(uint64_t), stream);
+        if (!rc) rc = launch_fill_zero(hist_lo, 256 * sizeof(uint64_t), stream);
+        if (rc) return rc;
+    }
+    if (n == 0) return LECB_OK;
+    const int grid = grid_for(n / 8 + 1, HIST_THREADS * 8, device_cu_count() * 4);
+    hipLaunchKernelGGL(hist_u16_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, n,
+                       reinterpret_cast<unsigned long long*>(hist_hi),
+                       reinterpret_cast<unsigned long long*>(hist_lo));
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_split(const uint16_t* in, uint64_t n, uint8_t* hi, uint8_t* lo, void* stream) {
+    if (n == 0) return LECB_OK;
+    const int grid = grid_for(n / 16 + 1, BG_THREADS, device_cu_count() * 16);
+    hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(BG_THREADS), 0,
+                       reinterpret_cast<hipStream_t>(stream), in, n, hi, lo);
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_merge(const uint8_t* hi, const uint8_t* lo, uint64_t n, uint16_t* out, void* stream) {
+    if (n == 0) return LECB_OK;
+    const int grid = grid_for(n / 16 + 1, BG_THREADS, device_cu_count() * 16);
+    hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(BG_THREADS), 0,
+                       reinterpret_cast<hipStream_t>(stream), hi, lo, n, out);
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_codebook_upload(const CodebookArgs& args, DeviceCodebook* blob, void* stream) {
+    hipLaunchKernelGGL(codebook_kernel, dim3(LUT_SIZE / 256), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), args, blob);
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_result(lecb_result* r, uint64_t bytes, uint64_t bits, int32_t status, void* stream) {
+    hipLaunchKernelGGL(result_kernel, dim3(1), dim3(1), 0, reinterpret_cast<hipStream_t>(stream), r,
+                       bytes, bits, status);
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_fill_zero(void* ptr, uint64_t bytes, void* stream) {
+    if (bytes == 0) return LECB_OK;
+    const int grid = grid_for(bytes / 16 + 1, 256, device_cu_count() * 8);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<uint8_t*>(ptr),
+                       bytes);
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+}  // namespace lecb

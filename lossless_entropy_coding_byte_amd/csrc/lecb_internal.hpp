@@ -1,0 +1,115 @@
+// Internal declarations shared by the host runtime and the HIP kernels.
+#pragma once
+
+#include <cstdint>
+
+#include "lecb.h"
+
+namespace lecb {
+
+// ---------------------------------------------------------------- device codebook
+// Decode lookup covers code words of up to LUT_BITS bits in one probe; longer
+// ones go through the canonical per-length limits.
+constexpr int LUT_BITS = 12;
+constexpr int LUT_SIZE = 1 << LUT_BITS;
+
+struct DeviceCodebook {
+    uint32_t enc[256];        // (code << 5) | len ; len 0 = byte has no code word
+    uint16_t lut[LUT_SIZE];   // next LUT_BITS bits -> (len << 8) | sym, len <= LUT_BITS; 0 = longer/none
+    uint32_t limit[17];       // per length l: (first[l] + count[l]) << (16 - l); 0 if no codes
+    uint32_t first[17];       // first canonical code of length l
+    uint32_t base[17];        // index in `sorted` of the first symbol of length l
+    uint8_t sorted[256];      // coded symbols by (length, byte value)
+    uint32_t max_len;
+    uint32_t num_coded;
+    uint32_t pad[3];
+};
+static_assert(sizeof(DeviceCodebook) % 16 == 0, "device codebook must stay 16-byte sized");
+
+// Everything the upload kernel needs, passed by value as a kernel argument.
+struct CodebookArgs {
+    uint32_t enc[256];
+    uint32_t first[17];
+    uint32_t count[17];
+    uint32_t base[17];
+    uint8_t sorted[256];
+    uint32_t max_len;
+    uint32_t num_coded;
+};
+
+// ---------------------------------------------------------------- workspace
+// Encode: chunk tickets, look-back flags (epoch-tagged so they never need
+// clearing), exit counter and accumulators.  Decode: exit counter + status.
+struct WsHeader {
+    uint32_t ticket;
+    uint32_t exit_count;
+    uint32_t epoch;
+    int32_t status;
+    uint64_t bits;
+    uint64_t words;
+    uint64_t pad[4];
+};
+static_assert(sizeof(WsHeader) == 64, "workspace header is 64 bytes");
+
+inline uint64_t align16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
+inline int ilog2(uint32_t x) {
+    int l = 0;
+    while ((1u << l) < x) ++l;
+    return l;
+}
+inline bool valid_chunk(uint32_t chunk) {
+    return chunk >= LECB_MIN_CHUNK && chunk <= LECB_MAX_CHUNK && (chunk & (chunk - 1)) == 0;
+}
+inline uint32_t units_per_chunk(uint32_t chunk) { return chunk / LECB_UNIT_SYMBOLS; }
+inline uint64_t table_bytes(uint64_t nc) { return align16(4 * nc); }
+inline uint64_t gap_bytes(uint64_t nc, uint32_t chunk) {
+    return align16((nc * units_per_chunk(chunk) + 1) / 2);
+}
+
+// ---------------------------------------------------------------- host helpers
+int build_lengths(const uint64_t freq[256], uint32_t max_len, uint32_t min_freq,
+                  uint8_t len_out[256]);
+int canonical_from_lengths(const uint8_t len[256], lecb_codebook* out);
+
+// ---------------------------------------------------------------- launches (kernels_*.hip)
+struct EncodeLaunch {
+    const void* in;          // u8 symbols, or u16 words when plane >= 0
+    int plane;               // -1 = bytes; 0 = low byte of u16; 1 = high byte of u16
+    uint64_t n;
+    uint32_t chunk;
+    uint64_t nc;
+    const DeviceCodebook* cb;
+    uint8_t* out;            // stream base
+    uint64_t capacity;       // bytes
+    lecb_result* res;
+    WsHeader* ws;            // followed by nc u64 flags
+    int grid;
+};
+int launch_encode(const EncodeLaunch& a, void* stream);
+
+struct DecodeLaunch {
+    const uint8_t* stream_base;
+    uint64_t stream_bytes;
+    const DeviceCodebook* cb;
+    uint32_t chunk;
+    uint64_t n;
+    uint64_t nc;
+    uint8_t* out;
+    lecb_result* res;
+    WsHeader* ws;
+};
+int launch_decode(const DecodeLaunch& a, void* stream);
+
+int launch_histogram_u8(const uint8_t* in, uint64_t n, uint64_t* hist, int accumulate,
+                        void* stream);
+int launch_histogram_u16(const uint16_t* in, uint64_t n, uint64_t* hist_hi, uint64_t* hist_lo,
+                         int accumulate, void* stream);
+int launch_split(const uint16_t* in, uint64_t n, uint8_t* hi, uint8_t* lo, void* stream);
+int launch_merge(const uint8_t* hi, const uint8_t* lo, uint64_t n, uint16_t* out, void* stream);
+int launch_codebook_upload(const CodebookArgs& args, DeviceCodebook* blob, void* stream);
+int launch_fill_zero(void* ptr, uint64_t bytes, void* stream);
+int launch_result(lecb_result* r, uint64_t bytes, uint64_t bits, int32_t status, void* stream);
+
+int device_cu_count();
+
+}  // namespace lecb

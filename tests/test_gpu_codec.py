@@ -1,0 +1,271 @@
+"""GPU parity of every kernel against the oracle, through the C ABI.
+
+Bar: bit-exact streams, byte-exact round trips, exact histograms.  Sizes span
+several chunks, several 4096-symbol tiles and a ragged tail.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import lossless_entropy_coding_byte_amd as lecb
+from gpu_helpers import DEV, to_dev, codebook_for, gpu_encode, gpu_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------- histogram
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 4096 * 3 + 5, 1_000_003])
+def test_histogram_u8_exact(n):
+    _say(f"hist u8 n={n}")
+    x = workloads.skewed_bytes(n, n, sigma=30)
+    h = torch.zeros(256, dtype=torch.int64, device=DEV)
+    lecb.lecb_histogram(to_dev(x), h)
+    assert np.array_equal(h.cpu().numpy().astype(np.uint64), oracle.histogram(x))
+    lecb.lecb_histogram(to_dev(x), h, accumulate=True)
+    assert np.array_equal(h.cpu().numpy().astype(np.uint64), 2 * oracle.histogram(x))
+
+
+def test_histogram_single_value_plane():
+    # every byte equal: all increments land in one bin
+    x = np.full(3_000_017, 0, np.uint8)
+    h = torch.zeros(256, dtype=torch.int64, device=DEV)
+    lecb.lecb_histogram(to_dev(x), h)
+    assert int(h[0]) == x.size and int(h.sum()) == x.size
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 100_001, 1 << 20])
+def test_histogram_bf16_exact(n):
+    _say(f"hist bf16 n={n}")
+    x = workloads.bf16_weights(n)
+    hh = torch.zeros(256, dtype=torch.int64, device=DEV)
+    hl = torch.zeros(256, dtype=torch.int64, device=DEV)
+    lecb.lecb_histogram_bf16(to_dev(x.view(np.int16)), hh, hl)
+    hi, lo = oracle.split_bf16(x)
+    assert np.array_equal(hh.cpu().numpy().astype(np.uint64), oracle.histogram(hi))
+    assert np.array_equal(hl.cpu().numpy().astype(np.uint64), oracle.histogram(lo))
+
+
+# ----------------------------------------------------------------------------- byte grouping
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 99_999, 1 << 20])
+def test_split_merge_exact(n):
+    x = workloads.bf16_weights(n)
+    xd = to_dev(x.view(np.int16))
+    hi = torch.empty(n, dtype=torch.uint8, device=DEV)
+    lo = torch.empty(n, dtype=torch.uint8, device=DEV)
+    lecb.lecb_split_bf16(xd, hi, lo)
+    rh, rl = oracle.split_bf16(x)
+    assert np.array_equal(hi.cpu().numpy(), rh) and np.array_equal(lo.cpu().numpy(), rl)
+    back = torch.empty(n, dtype=torch.int16, device=DEV)
+    lecb.lecb_merge_bf16(hi, lo, back)
+    assert np.array_equal(back.cpu().numpy().view(np.uint16), x)
+
+
+# ----------------------------------------------------------------------------- encode / decode
+
+def _gauss(seed, n, sigma=20.0):
+    return workloads.q8(np.random.default_rng([7, seed]).normal(0, sigma, n))
+
+
+CASES = [
+    # name, n, chunk, input maker, clamp
+    ("one_symbol_one_chunk", 1, 4096, lambda n: np.array([77], np.uint8), True),
+    ("tiny_lt_unit", 100, 256, lambda n: _gauss(1, n), True),
+    ("ragged_256", 256 * 37 + 11, 256, lambda n: _gauss(2, n), True),
+    ("ragged_1024", 1024 * 19 + 1000, 1024, lambda n: _gauss(3, n, 5.0), False),
+    ("tiles_4096", 4096 * 25 + 4095, 4096, lambda n: _gauss(4, n), True),
+    ("tiles_16384", 16384 * 9 + 77, 16384, lambda n: _gauss(5, n, 60.0), True),
+    ("tiles_65536", 65536 * 5 + 12345, 65536, lambda n: _gauss(6, n, 2.0), False),
+    ("all_equal", 50_000, 4096, lambda n: np.full(n, 200, np.uint8), False),
+    ("two_symbols", 70_001, 1024, lambda n: workloads.uniform_bytes(9, n, 2), False),
+    ("uniform_8bit", 4096 * 8, 4096, lambda n: workloads.uniform_bytes(10, n), False),
+]
+
+
+@pytest.mark.parametrize("name,n,chunk,gen,clamp", CASES, ids=[c[0] for c in CASES])
+def test_encode_bit_exact_and_round_trip(name, n, chunk, gen, clamp):
+    _say(f"encode/decode case={name} n={n} chunk={chunk}")
+    x = gen(n)
+    ln = codebook_for(x, clamp)
+    ref, ref_bits = oracle.encode(x, ln, oracle.canonical_codes(ln), chunk)
+    got, r, dcb = gpu_encode(x, ln, chunk)
+    assert int(r["status"]) == 0, lecb.lecb_status_str(int(r["status"]))
+    assert int(r["bytes"]) == ref.size
+    assert int(r["payload_bits"]) == ref_bits
+    assert np.array_equal(got, ref)
+    y, rd = gpu_decode(ref, dcb, chunk, n)
+    assert int(rd["status"]) == 0, lecb.lecb_status_str(int(rd["status"]))
+    assert int(rd["payload_bits"]) == ref_bits
+    assert np.array_equal(y, x)
+
+
+def test_long_codes_straddle_words():
+    # geometric weights: code lengths up to 16, many code words cross word boundaries
+    f = np.array([max(1, (1 << 30) >> s) for s in range(256)], np.uint64)
+    ln = oracle.package_merge_lengths(f, 16)
+    assert int(ln.max()) == 16
+    x = workloads.uniform_bytes(11, 4096 * 6 + 333)
+    ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), 4096)
+    got, r, dcb = gpu_encode(x, ln, 4096)
+    assert np.array_equal(got, ref)
+    y, rd = gpu_decode(ref, dcb, 4096, x.size)
+    assert int(rd["status"]) == 0 and np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("max_len", [9, 11, 12, 13])
+def test_length_limits(max_len):
+    x = _gauss(12, 4096 * 4 + 1, 30.0)
+    ln = codebook_for(x, True, max_len)
+    assert int(ln.max()) == max_len
+    ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), 4096)
+    got, r, dcb = gpu_encode(x, ln, 4096)
+    assert np.array_equal(got, ref)
+    y, rd = gpu_decode(ref, dcb, 4096, x.size)
+    assert int(rd["status"]) == 0 and np.array_equal(y, x)
+
+
+def test_empty_input():
+    ln = codebook_for(np.arange(256, dtype=np.uint8), True)
+    got, r, dcb = gpu_encode(np.zeros(0, np.uint8), ln, 4096)
+    assert int(r["bytes"]) == 0 and int(r["status"]) == 0
+
+
+def test_determinism_repeat_encode():
+    x = _gauss(13, 4096 * 200 + 5)
+    ln = codebook_for(x, True)
+    a, _, _ = gpu_encode(x, ln, 4096)
+    b, _, _ = gpu_encode(x, ln, 4096)
+    assert np.array_equal(a, b)
+
+
+def test_workspace_reuse_across_calls():
+    # the epoch-tagged look-back flags must not leak between calls sharing a workspace
+    x1 = _gauss(14, 4096 * 300 + 9)
+    x2 = _gauss(15, 4096 * 120 + 1, 40.0)
+    ln = codebook_for(np.concatenate([x1, x2]), True)
+    cb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+    ws = lecb.new_workspace(x1.size, 4096, DEV)
+    for x in (x1, x2, x1, x2):
+        out, res = lecb.encode_bytes(to_dev(x), cb, 4096, ws=ws)
+        r = lecb.results_to_numpy(res)[0]
+        ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), 4096)
+        assert np.array_equal(out[: int(r["bytes"])].cpu().numpy(), ref)
+
+
+def test_cross_decode_gpu_stream_with_oracle():
+    x = _gauss(16, 16384 * 3 + 5000, 25.0)
+    ln = codebook_for(x, True)
+    got, r, _ = gpu_encode(x, ln, 16384)
+    assert np.array_equal(oracle.decode(got, ln, 16384, x.size), x)
+
+
+# ----------------------------------------------------------------------------- bf16 planes
+
+def test_plane_encode_matches_oracle():
+    x = workloads.bf16_weights(200_003)
+    hi, lo = oracle.split_bf16(x)
+    xd = to_dev(x.view(np.int16))
+    for plane, data in ((1, hi), (0, lo)):
+        ln = codebook_for(data, False)
+        ref, bits = oracle.encode(data, ln, oracle.canonical_codes(ln), 16384)
+        dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+        out = torch.empty(lecb.lecb_encoded_bound(x.size, 16384), dtype=torch.uint8, device=DEV)
+        res = lecb.new_results(1, DEV)
+        ws = lecb.new_workspace(x.size, 16384, DEV)
+        lecb.lecb_encode_plane(xd, x.size, plane, dcb.blob, 16384, out, res, ws)
+        r = lecb.results_to_numpy(res)[0]
+        assert int(r["status"]) == 0 and int(r["payload_bits"]) == bits
+        assert np.array_equal(out[: int(r["bytes"])].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), (1 << 20, 65536)])
+def test_bf16_pertensor_pipeline(n, chunk):
+    _say(f"bf16 per-tensor n={n} chunk={chunk}")
+    x = workloads.bf16_weights(n)
+    ref = oracle.encode_bf16(x, chunk)
+    xd = to_dev(x.view(np.int16))
+    hist = torch.zeros(512, dtype=torch.int64, device=DEV)
+    bh, bl = lecb.new_codebook_blob(DEV), lecb.new_codebook_blob(DEV)
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(2, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    cb_hi, cb_lo = lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
+    r = lecb.results_to_numpy(res)
+    assert np.array_equal(cb_hi.lengths(), ref["len_hi"]) and np.array_equal(cb_lo.lengths(), ref["len_lo"])
+    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), ref["stream_hi"])
+    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), ref["stream_lo"])
+    out = torch.empty(n, dtype=torch.int16, device=DEV)
+    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
+    res2 = lecb.new_results(2, DEV)
+    lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, out,
+                          scratch, res2, ws)
+    rr = lecb.results_to_numpy(res2)
+    assert int(rr[0]["status"]) == 0 and int(rr[1]["status"]) == 0
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
+
+
+# ----------------------------------------------------------------------------- device-side errors
+
+def test_uncoded_symbol_sets_status():
+    x = _gauss(17, 10_000, 3.0)
+    ln = codebook_for(x, False)
+    x2 = x.copy()
+    x2[5000] = np.uint8(np.flatnonzero(ln == 0)[0])  # a byte value with no code word
+    assert ln[x2[5000]] == 0
+    got, r, _ = gpu_encode(x2, ln, 4096)
+    assert int(r["status"]) == lecb.LECB_ERR_UNCODED_SYMBOL
+
+
+def test_capacity_overflow_sets_status():
+    x = workloads.uniform_bytes(18, 50_000)
+    ln = codebook_for(x, True)
+    dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+    small = torch.empty(lecb.lecb_header_bytes(x.size, 4096) + 64, dtype=torch.uint8, device=DEV)
+    out, res = lecb.encode_bytes(to_dev(x), dcb, 4096, out=small)
+    assert int(lecb.results_to_numpy(res)[0]["status"]) == lecb.LECB_ERR_CAPACITY
+
+
+def test_corrupt_streams_set_status():
+    x = _gauss(19, 4096 * 6 + 100, 12.0)
+    ln = codebook_for(x, True)
+    ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), 4096)
+    dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+    nc = oracle.num_chunks(x.size, 4096)
+    tb = oracle.table_bytes(x.size, 4096)
+    hb = oracle.header_bytes(x.size, 4096)
+    bad = {}
+    t = ref.copy(); t[0:4] = 0; bad["zero end"] = t
+    t = ref.copy(); e = t[:4 * nc].view("<u4").copy(); e[1], e[2] = e[2], e[1]; t[:4 * nc] = e.view(np.uint8); bad["non-monotone"] = t
+    t = ref.copy(); t[4 * nc] = 1; bad["table padding"] = t
+    t = ref.copy(); t[tb] ^= 0x10; bad["gap value"] = t
+    t = ref.copy(); t[hb - 1] = 1; bad["gap padding"] = t
+    t = ref.copy(); t[hb + 40:hb + 48] ^= 0xFF; bad["payload bits"] = t
+    for name, t in bad.items():
+        try:
+            oracle.decode(t, ln, 4096, x.size)
+            oracle_bad = False
+        except oracle.CorruptStream:
+            oracle_bad = True
+        y, r = gpu_decode(t, dcb, 4096, x.size)
+        # the two decoders accept and reject exactly the same streams
+        assert (int(r["status"]) == lecb.LECB_ERR_CORRUPT) == oracle_bad, name
+        if name != "payload bits":
+            assert oracle_bad, name
+        elif not oracle_bad:
+            assert np.array_equal(y, oracle.decode(t, ln, 4096, x.size))
+    # a size below the header is rejected on the host
+    with pytest.raises(lecb.LecbError):
+        gpu_decode(ref[: hb - 4], dcb, 4096, x.size)
