@@ -296,10 +296,11 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         K = oracle.units_per_chunk(chunk)
         gaps = buf[tb:tb + (nc * K + 1) // 2].cpu().numpy()
         for c in picks:
-            one, _ = oracle.encode(plane[c * chunk:(c + 1) * chunk], ln, cd, chunk)
+            piece = plane[c * chunk:(c + 1) * chunk]
+            one, _ = oracle.encode(piece, ln, cd, chunk)
             s0 = int(table[c - 1]) if c else 0
             words = buf[hb + 4 * s0: hb + 4 * int(table[c])].cpu().numpy()
-            exact &= bool(np.array_equal(one[32:], words))
+            exact &= bool(np.array_equal(one[oracle.header_bytes(piece.size, chunk):], words))
             g = np.empty(2 * gaps.size, np.uint8); g[0::2] = gaps & 15; g[1::2] = gaps >> 4
             og = one[16:16 + (K + 1) // 2]
             go = np.empty(2 * og.size, np.uint8); go[0::2] = og & 15; go[1::2] = og >> 4

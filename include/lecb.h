@@ -106,8 +106,9 @@ const char* lecb_status_str(int status);
 uint64_t lecb_num_chunks(uint64_t n, uint32_t chunk);
 /* Bytes before the payload: align16(4*nc) + align16(ceil(nc*K/2)). */
 uint64_t lecb_header_bytes(uint64_t n, uint32_t chunk);
-/* Largest stream any codebook with lengths <= max_len can produce:
- * header + 4*(ceil(n*max_len/32) + nc).  0 on bad arguments. */
+/* Largest stream any codebook with lengths <= max_len can produce, rounded
+ * up to 16 bytes: align16(header + 4*(ceil(n*max_len/32) + nc)).  0 on bad
+ * arguments. */
 uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len);
 /* Workspace bytes an encode or decode of n symbols with this chunk needs. */
 uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk);
@@ -185,7 +186,8 @@ int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t ch
 /* Decode a v1 stream of n symbols into d_out[n] (reverse path of "Lossless
  * Compression for LLM Tensor Incremental Snapshots", Technical framework).
  * stream_bytes must be the exact stream size (lecb_result.bytes of the
- * encode); it bounds every read.  A size below the header or not a whole
+ * encode).  The buffer must be readable up to align16(stream_bytes) (the
+ * decoder fetches whole 16-byte groups; bytes past stream_bytes are ignored).  A size below the header or not a whole
  * number of payload words returns LECB_ERR_CORRUPT at once.  A stream that is not exactly what
  * lecb_encode produces for these arguments sets status CORRUPT (offset table
  * not increasing or past the stream, a bit pattern with no code word, a code

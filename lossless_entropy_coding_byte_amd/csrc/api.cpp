@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 
 #include "lecb.h"
@@ -13,6 +14,17 @@ using namespace lecb;
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Encode workgroups launched per compute unit (persistent grid).  Tunable with
+// LECB_ENCODE_WGS_PER_CU for launch-shape sweeps; 4 by default.
+int encode_wgs_per_cu() {
+    static int v = [] {
+        const char* e = std::getenv("LECB_ENCODE_WGS_PER_CU");
+        const int x = e ? std::atoi(e) : 0;
+        return x >= 1 && x <= 64 ? x : 4;
+    }();
+    return v;
+}
 
 uint64_t num_chunks_checked(uint64_t n, uint32_t chunk) {
     return valid_chunk(chunk) ? (n + chunk - 1) / chunk : 0;
@@ -75,7 +87,7 @@ int encode_common(const void* d_in, int plane, uint64_t n, const void* d_blob, u
     L.capacity = out_capacity;
     L.res = d_res;
     L.ws = reinterpret_cast<WsHeader*>(d_ws);
-    L.grid = (int)std::min<uint64_t>(nc, (uint64_t)device_cu_count() * 8);
+    L.grid = (int)std::min<uint64_t>(nc, (uint64_t)device_cu_count() * encode_wgs_per_cu());
     return launch_encode(L, stream);
 }
 
@@ -108,7 +120,7 @@ uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len) {
     if (!valid_chunk(chunk) || max_len < 1 || max_len > 16) return 0;
     const uint64_t nc = num_chunks_checked(n, chunk);
     if (!nc) return 0;
-    return header_of(n, chunk) + 4 * ((n * max_len + 31) / 32 + nc);
+    return align16(header_of(n, chunk) + 4 * ((n * max_len + 31) / 32 + nc));
 }
 
 uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk) {
@@ -180,7 +192,8 @@ int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_bl
     if (!valid_chunk(chunk) || !d_res || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
     if (n == 0)
         return launch_result(d_res, 0, 0, stream_bytes == 0 ? LECB_OK : LECB_ERR_CORRUPT, stream);
-    if (!d_stream || !d_out || !d_ws || !aligned16(d_stream) || !aligned16(d_ws))
+    if (!d_stream || !d_out || !d_ws || !aligned16(d_stream) || !aligned16(d_out) ||
+        !aligned16(d_ws))
         return LECB_ERR_INVALID_ARG;
     const uint64_t hb = header_of(n, chunk);
     if (stream_bytes < hb + 4 || (stream_bytes - hb) % 4) return LECB_ERR_CORRUPT;

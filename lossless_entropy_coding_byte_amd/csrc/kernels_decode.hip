@@ -6,15 +6,17 @@
 // is split into K = chunk/256 units whose exact starting code-word boundary
 // is its word-aligned start plus the stored 4-bit gap.
 //
-// One lane per unit, 256 units per workgroup; K divides 256, so a chunk's
-// units never straddle workgroups.  Per lane:
+// One lane per unit, 256 units per workgroup (K divides 256, so a chunk's
+// units never straddle workgroups).  Per lane:
 //   1. count the code words between its start and the next unit's start
 //      (the chunk's last unit takes the remainder of the chunk's symbols);
 //   2. exclusive scan of the counts inside each chunk -> output offsets;
-//   3. decode again, storing the symbols.
-// A code word is looked up with the next LUT_BITS bits in an LDS table;
-// longer ones use the canonical per-length limits.  Every structural rule of
-// the format is checked; a violation sets status CORRUPT.
+//   3. decode again, storing 16 symbols per 16-byte store.
+// Each lane reads its unit's words straight from global memory, 64 bytes per
+// refill (four 16-byte loads issued together), so a lane waits on memory once
+// per 16 payload words.  A code word is looked up with the next LUT_BITS bits
+// in an LDS table; longer ones use the canonical per-length limits.  Every
+// structural rule of the format is checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
 #include "lecb_internal.hpp"
@@ -23,7 +25,8 @@ namespace lecb {
 
 namespace {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_MAX_THREADS = 256;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 struct DecArgs {
     const uint32_t* table;
@@ -52,30 +55,75 @@ struct Tables {
     uint8_t sorted[256];
 };
 
+// Bit reader over one decode unit: a 64-bit bit buffer fed from a queue of
+// 16 payload words held in registers.  An empty queue is refilled with four
+// 16-byte loads at once (the lane waits for them: one wait per 16 words).
+// Loads are at a clamped address (the caller's buffer is readable up to the
+// next 16-byte boundary); words past the payload read as zero.
 struct Reader {
     const uint32_t* p;
-    uint64_t limit;   // words readable
-    uint64_t wi;      // next word to load
+    uint64_t limit;   // payload words
+    uint64_t gmax;    // last readable 16-byte group
+    uint64_t g;       // next group to load
+    uint64_t widx;    // payload index of q0.x
+    v4u q0, q1, q2, q3;
+    int nq;           // words left in the queue
     uint64_t buf;     // pending bits, MSB first
     int nb;           // valid bits in buf
 
-    __device__ inline uint32_t ld(uint64_t i) const { return i < limit ? p[i] : 0u; }
-    __device__ inline void start(uint64_t word, uint32_t bit) {
-        buf = (((uint64_t)ld(word) << 32) | ld(word + 1)) << bit;
-        nb = 64 - (int)bit;
-        wi = word + 2;
+    __device__ inline v4u ld4(uint64_t grp) const {
+        return *reinterpret_cast<const v4u*>(p + 4 * min(grp, gmax));
     }
+    __device__ inline void fill() {
+        q0 = ld4(g);
+        q1 = ld4(g + 1);
+        q2 = ld4(g + 2);
+        q3 = ld4(g + 3);
+        g += 4;
+        nq = 16;
+    }
+    __device__ inline uint32_t pop() {
+        if (nq == 0) fill();
+        const uint32_t w = widx < limit ? q0.x : 0u;
+        ++widx;
+        q0.x = q0.y;
+        q0.y = q0.z;
+        q0.z = q0.w;
+        if ((--nq & 3) == 0) {
+            q0 = q1;
+            q1 = q2;
+            q2 = q3;
+        }
+        return w;
+    }
+    __device__ inline void start(const uint32_t* payload, uint64_t words, uint64_t word,
+                                 uint32_t bit) {
+        p = payload;
+        limit = words;
+        gmax = words ? (words - 1) >> 2 : 0;
+        g = word >> 2;
+        widx = word & ~uint64_t(3);
+        fill();
+        for (uint32_t k = 0; k < (uint32_t)(word & 3); ++k) (void)pop();
+        const uint32_t w0 = pop();
+        const uint32_t w1 = pop();
+        buf = (((uint64_t)w0 << 32) | w1) << bit;
+        nb = 64 - (int)bit;
+    }
+    // afterwards at least 32 bits are buffered: room for two code words
     __device__ inline void refill() {
         if (nb < 32) {
-            buf |= (uint64_t)ld(wi++) << (32 - nb);
+            buf |= (uint64_t)pop() << (32 - nb);
             nb += 32;
         }
     }
 };
 
 // One code word: returns its length (0 = no code word matches) and the symbol.
-__device__ inline uint32_t decode_one(const Tables& T, Reader& r, uint32_t& sym) {
-    r.refill();
+// The caller guarantees at least 16 buffered bits (refill() before every
+// second code word).
+template <class R>
+__device__ inline uint32_t decode_one(const Tables& T, R& r, uint32_t& sym) {
     const uint32_t e = T.lut[r.buf >> (64 - LUT_BITS)];
     uint32_t len;
     if (e) {
@@ -103,145 +151,202 @@ __device__ inline uint32_t gap_of(const uint8_t* gaps, uint64_t i) {
     return (i & 1) ? (b >> 4) : (b & 0xFu);
 }
 
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
-    __shared__ Tables T;
-    __shared__ uint32_t s_cnt[DEC_THREADS];
-    __shared__ uint64_t s_bits[DEC_THREADS / 64];
+// Per-unit geometry, computed by every lane for its own unit.
+struct Unit {
+    uint64_t c;          // chunk
+    uint32_t j;          // unit within the chunk
+    bool active, last, bad;
+    uint64_t sw, wc;     // chunk's first payload word and word count
+    uint32_t start_bit, end_bit, sj1, m_c;
+};
+
+// Count pass: code words in [start_bit, end_bit); validates the boundary.
+__device__ inline uint32_t count_unit(const Tables& T, const Unit& U, const uint32_t* payload,
+                                      uint64_t words, bool& bad) {
+    Reader r;
+    r.start(payload, words, U.sw + (U.start_bit >> 5), U.start_bit & 31);
+    uint32_t pos = U.start_bit, last_start = 0xFFFFFFFFu, cnt = 0;
+    while (pos < U.end_bit) {
+        uint32_t sym;
+        if (cnt & 1) r.refill();  // >= 32 bits after start; refill before every odd symbol
+        const uint32_t len = decode_one(T, r, sym);
+        if (!len) {
+            bad = true;
+            return cnt;
+        }
+        last_start = pos;
+        pos += len;
+        ++cnt;
+    }
+    if (pos != U.end_bit) bad = true;
+    // the stored gap must name the FIRST boundary at or after sj1
+    if (U.end_bit != U.sj1 && last_start != 0xFFFFFFFFu && last_start >= U.sj1) bad = true;
+    return cnt;
+}
+
+// Decode pass: cnt symbols to dst (byte stores to a 16-byte boundary, then
+// 16 symbols per 16-byte store, then the tail).  Returns the bits consumed.
+__device__ inline uint32_t decode_unit(const Tables& T, const Unit& U, const uint32_t* payload,
+                                       uint64_t words, uint32_t cnt, uint8_t* dst, bool& bad) {
+    Reader r;
+    r.start(payload, words, U.sw + (U.start_bit >> 5), U.start_bit & 31);
+    uint32_t pos = U.start_bit;
+    bool invalid = false;
+    uint32_t k = 0;
+    const uint32_t head = min(cnt, (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u));
+    for (; k < head; ++k) {
+        uint32_t sym = 0;
+        if (k & 1) r.refill();
+        const uint32_t len = decode_one(T, r, sym);
+        invalid |= len == 0;
+        pos += len;
+        dst[k] = (uint8_t)sym;
+    }
+    for (; k + 16 <= cnt; k += 16) {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t sym = 0;
+            if ((k + i) & 1) r.refill();  // parity of the symbol index within the unit
+            const uint32_t len = decode_one(T, r, sym);
+            invalid |= len == 0;
+            pos += len;
+            w[i >> 2] |= (sym & 0xFFu) << (8 * (i & 3));
+        }
+        v4u v;
+        v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+        *reinterpret_cast<v4u*>(dst + k) = v;
+    }
+    for (; k < cnt; ++k) {
+        uint32_t sym = 0;
+        if (k & 1) r.refill();
+        const uint32_t len = decode_one(T, r, sym);
+        invalid |= len == 0;
+        pos += len;
+        dst[k] = (uint8_t)sym;
+    }
+    bad |= invalid;
+    if (!bad && U.last) {
+        // data must end inside the chunk's last word, followed by zero padding
+        const uint64_t endw = (uint64_t)U.wc << 5;
+        if (pos > endw || pos + 32 <= endw) bad = true;
+        else {
+            const uint32_t rest = (uint32_t)(endw - pos);
+            r.refill();
+            if (rest && (r.buf >> (64 - rest)) != 0) bad = true;
+        }
+    }
+    return pos - U.start_bit;
+}
+
+__global__ __launch_bounds__(DEC_MAX_THREADS) void decode_kernel(DecArgs a) {
+    __shared__ __attribute__((aligned(16))) Tables T;
+    __shared__ uint32_t s_cnt[DEC_MAX_THREADS];
+    __shared__ uint64_t s_lo[DEC_MAX_THREADS / 64];
+    __shared__ uint64_t s_hi[DEC_MAX_THREADS / 64];
 
     const int tid = threadIdx.x;
-    for (int i = tid; i < LUT_SIZE; i += DEC_THREADS) T.lut[i] = a.cb->lut[i];
+    const int nthreads = blockDim.x;
+    const int nwaves = nthreads / 64;
+    {
+        // 16-byte copies of the lookup table (LUT_SIZE * 2 bytes)
+        const v4u* src = reinterpret_cast<const v4u*>(a.cb->lut);
+        v4u* dst = reinterpret_cast<v4u*>(T.lut);
+        constexpr int NV = LUT_SIZE * 2 / 16;
+        for (int i = tid; i < NV; i += nthreads) dst[i] = src[i];
+    }
     if (tid < 17) {
         T.limit[tid] = a.cb->limit[tid];
         T.first[tid] = a.cb->first[tid];
         T.base[tid] = a.cb->base[tid];
     }
-    T.sorted[tid] = a.cb->sorted[tid];
-    __syncthreads();
+    for (int i = tid; i < 256; i += nthreads) T.sorted[i] = a.cb->sorted[i];
 
+    // ---- unit geometry
     const uint32_t K = 1u << a.log2k;
-    const uint64_t u = (uint64_t)blockIdx.x * DEC_THREADS + tid;
-    const uint64_t c = u >> a.log2k;
-    const uint32_t j = (uint32_t)(u & (K - 1));
-    const bool active = c < a.nc;
-    bool bad = false;
-
-    uint64_t sw = 0, wc = 0;
-    uint32_t start_bit = 0, end_bit = 0, m_c = 0;
-    const bool last = j == K - 1;
-    if (active) {
-        sw = c ? a.table[c - 1] : 0;
-        const uint64_t ew = a.table[c];
-        if (ew <= sw || ew > a.payload_words || ew - sw > a.chunk / 2) bad = true;
-        wc = bad ? 0 : ew - sw;
-        m_c = (uint32_t)min<uint64_t>(a.chunk, a.n - c * a.chunk);
-        const uint32_t sj = (uint32_t)(((uint64_t)j * wc) >> a.log2k) << 5;
+    Unit U;
+    const uint64_t u = (uint64_t)blockIdx.x * nthreads + tid;
+    U.c = u >> a.log2k;
+    U.j = (uint32_t)(u & (K - 1));
+    U.active = U.c < a.nc;
+    U.last = U.j == K - 1;
+    U.bad = false;
+    U.sw = U.wc = 0;
+    U.start_bit = U.end_bit = U.sj1 = U.m_c = 0;
+    if (U.active) {
+        U.sw = U.c ? a.table[U.c - 1] : 0;
+        const uint64_t ew = a.table[U.c];
+        if (ew <= U.sw || ew > a.payload_words || ew - U.sw > a.chunk / 2) U.bad = true;
+        U.wc = U.bad ? 0 : ew - U.sw;
+        U.m_c = (uint32_t)min<uint64_t>(a.chunk, a.n - U.c * a.chunk);
+        const uint32_t sj = (uint32_t)(((uint64_t)U.j * U.wc) >> a.log2k) << 5;
         const uint32_t gj = gap_of(a.gaps, u);
-        if (j == 0 && gj != 0) bad = true;
-        start_bit = sj + gj;
-        if (!last) {
-            const uint32_t sj1 = (uint32_t)(((uint64_t)(j + 1) * wc) >> a.log2k) << 5;
-            end_bit = sj1 + gap_of(a.gaps, u + 1);
+        if (U.j == 0 && gj != 0) U.bad = true;
+        U.start_bit = sj + gj;
+        if (!U.last) {
+            U.sj1 = (uint32_t)(((uint64_t)(U.j + 1) * U.wc) >> a.log2k) << 5;
+            U.end_bit = U.sj1 + gap_of(a.gaps, u + 1);
+        } else {
+            U.end_bit = (uint32_t)(U.wc << 5);
         }
     }
+
+    __syncthreads();  // tables complete
 
     // ---- 1. count
     uint32_t cnt = 0;
-    if (active && !last && !bad) {
-        Reader r{a.payload, a.payload_words, 0, 0, 0};
-        r.start(sw + (start_bit >> 5), start_bit & 31);
-        uint32_t pos = start_bit, last_start = 0xFFFFFFFFu;
-        const uint32_t sj1 = end_bit - gap_of(a.gaps, u + 1);
-        while (pos < end_bit) {
-            uint32_t sym;
-            const uint32_t len = decode_one(T, r, sym);
-            if (!len) {
-                bad = true;
-                break;
-            }
-            last_start = pos;
-            pos += len;
-            ++cnt;
-        }
-        if (!bad) {
-            if (pos != end_bit) bad = true;
-            // the stored gap must name the FIRST boundary at or after sj1
-            if (end_bit != sj1 && last_start != 0xFFFFFFFFu && last_start >= sj1) bad = true;
-        }
-    }
+    bool bad = U.bad;
+    if (U.active && !U.last && !bad)
+        cnt = count_unit(T, U, a.payload, a.payload_words, bad);
 
     // ---- 2. exclusive scan of counts within each chunk (segments of K lanes)
     s_cnt[tid] = cnt;
     __syncthreads();
-    for (uint32_t o = 1; o < DEC_THREADS; o <<= 1) {
-        const uint32_t v = tid >= (int)o ? s_cnt[tid - o] : 0u;
+    for (int o = 1; o < nthreads; o <<= 1) {
+        const uint32_t v = tid >= o ? s_cnt[tid - o] : 0u;
         __syncthreads();
         s_cnt[tid] += v;
         __syncthreads();
     }
-    const int seg0 = tid - (int)j;  // lane of unit 0 of this chunk
+    const int seg0 = tid - (int)U.j;  // lane of unit 0 of this chunk
     const uint32_t before_seg = seg0 > 0 ? s_cnt[seg0 - 1] : 0u;
     const uint32_t out_off = s_cnt[tid] - cnt - before_seg;
-    if (active) {
-        if (last) {
-            if (out_off > m_c) bad = true;
-            else cnt = m_c - out_off;
-        } else if (out_off + cnt > m_c) {
+    if (U.active) {
+        if (U.last) {
+            if (out_off > U.m_c) bad = true;
+            else cnt = U.m_c - out_off;
+        } else if (out_off + cnt > U.m_c) {
             bad = true;  // never store outside this chunk's slot
         }
     }
 
     // ---- 3. decode and store
     uint64_t used_bits = 0;
-    if (active && !bad) {
-        Reader r{a.payload, a.payload_words, 0, 0, 0};
-        r.start(sw + (start_bit >> 5), start_bit & 31);
-        uint8_t* dst = a.out + c * a.chunk + out_off;
-        uint32_t pos = start_bit;
-        for (uint32_t k = 0; k < cnt; ++k) {
-            uint32_t sym;
-            const uint32_t len = decode_one(T, r, sym);
-            if (!len) {
-                bad = true;
-                break;
-            }
-            pos += len;
-            dst[k] = (uint8_t)sym;
-        }
-        if (!bad && last) {
-            // data must end inside the chunk's last word, followed by zero padding
-            const uint64_t endw = (uint64_t)wc << 5;
-            if (pos > endw || pos + 32 <= endw) bad = true;
-            else {
-                const uint32_t rest = (uint32_t)(endw - pos);
-                r.refill();
-                if (rest && (r.buf >> (64 - rest)) != 0) bad = true;
-            }
-        }
-        used_bits = pos - start_bit;
+    if (U.active && !bad) {
+        uint8_t* dst = a.out + U.c * a.chunk + out_off;
+        used_bits = decode_unit(T, U, a.payload, a.payload_words, cnt, dst, bad);
     }
 
     // padding bytes of the header are part of the format
     if (blockIdx.x == 0) {
-        for (uint64_t b = a.table_pad_from + tid; b < a.table_pad_to; b += DEC_THREADS)
+        for (uint64_t b = a.table_pad_from + tid; b < a.table_pad_to; b += nthreads)
             bad |= a.stream[b] != 0;
-        for (uint64_t b = a.gap_pad_from + tid; b < a.gap_pad_to; b += DEC_THREADS)
+        for (uint64_t b = a.gap_pad_from + tid; b < a.gap_pad_to; b += nthreads)
             bad |= a.stream[b] != 0;
         if (tid == 0 && ((a.nc << a.log2k) & 1))
             bad |= (a.stream[a.gap_pad_from - 1] >> 4) != 0;
     }
 
     // ---- status, accounting, exit
-    const uint64_t wsum = [&] {
-        uint64_t v = used_bits;
+    uint64_t v = used_bits;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-        return v;
-    }();
-    if ((tid & 63) == 0) s_bits[tid >> 6] = wsum;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();
+    if ((tid & 63) == 0) s_lo[tid >> 6] = v;
     const int any_bad = __syncthreads_or(bad);
     if (tid == 0) {
         uint64_t tot = 0;
-        for (int w = 0; w < DEC_THREADS / 64; ++w) tot += s_bits[w];
+        for (int w = 0; w < nwaves; ++w) tot += s_lo[w];
         if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(&a.ws->bits), (unsigned long long)tot);
         if (any_bad) atomicCAS(&a.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
         __threadfence();
@@ -274,21 +379,23 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
     a.payload_words = (L.stream_bytes - tb - gb) / 4;
     a.cb = L.cb;
     a.chunk = L.chunk;
-    a.log2k = (uint32_t)ilog2(units_per_chunk(L.chunk));
+    const uint32_t K = units_per_chunk(L.chunk);
+    a.log2k = (uint32_t)ilog2(K);
     a.n = L.n;
     a.nc = L.nc;
     a.header_bytes = tb + gb;
     a.stream = L.stream_base;
     a.table_pad_from = 4 * L.nc;
     a.table_pad_to = tb;
-    a.gap_pad_from = tb + (L.nc * units_per_chunk(L.chunk) + 1) / 2;
+    a.gap_pad_from = tb + (L.nc * K + 1) / 2;
     a.gap_pad_to = tb + gb;
     a.out = L.out;
     a.res = L.res;
     a.ws = L.ws;
-    const uint64_t units = L.nc * units_per_chunk(L.chunk);
-    const uint64_t grid = (units + DEC_THREADS - 1) / DEC_THREADS;
-    hipLaunchKernelGGL(decode_kernel, dim3((uint32_t)grid), dim3(DEC_THREADS), 0,
+
+    const uint64_t units = L.nc * K;
+    const uint64_t grid = (units + DEC_MAX_THREADS - 1) / DEC_MAX_THREADS;
+    hipLaunchKernelGGL(decode_kernel, dim3((uint32_t)grid), dim3(DEC_MAX_THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }

@@ -138,44 +138,62 @@ __device__ inline uint64_t make_flag(uint32_t tag, uint32_t state, uint64_t valu
 // the call gives up with status WORKSPACE instead of waiting forever.
 constexpr uint32_t SPIN_LIMIT = 1u << 24;
 
+constexpr int LB_SLOTS = 4;  // flags each lane examines per round: 256 predecessors per round
+
 // Exclusive prefix (in payload words) of chunk c; run by all 64 lanes of wave 0.
-// *timed_out is set when SPIN_LIMIT was reached.
+// Each round covers the 256 chunks below `end`: slot i of lane l holds chunk
+// end-1-(64*i+l), so a smaller (64*i+l) is a nearer predecessor.  The round
+// waits until every flag in it is published, then adds up everything from the
+// nearest inclusive prefix (state PREFIX) upwards; with no prefix in the
+// window it adds all 256 aggregates and moves down.  *timed_out is set when
+// SPIN_LIMIT was reached.
 __device__ uint64_t look_back(uint64_t* flags, int64_t c, uint32_t tag, bool* timed_out) {
     const int lane = threadIdx.x & 63;
     uint64_t excl = 0;
     int64_t end = c;
     uint32_t spins = 0;
     while (end > 0) {
-        const int64_t idx = end - 64 + lane;
-        uint64_t f = 0;
-        bool ok = false;
-        for (;;) {
+        uint64_t f[LB_SLOTS];
+        uint32_t pending = 0;  // bit i: slot i not yet valid
+#pragma unroll
+        for (int i = 0; i < LB_SLOTS; ++i) {
+            const int64_t idx = end - 1 - (64 * i + lane);
             if (idx >= 0) {
-                if (!ok) {
-                    f = __hip_atomic_load(&flags[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok = (uint32_t)(f >> 36) == tag && ((f >> 34) & 3u) != 0;
-                }
+                pending |= 1u << i;
             } else {
-                f = make_flag(tag, ST_PREFIX, 0);
-                ok = true;
+                f[i] = make_flag(tag, ST_PREFIX, 0);  // before chunk 0: prefix 0
             }
-            if (__all(ok)) break;
+        }
+        for (;;) {
+#pragma unroll
+            for (int i = 0; i < LB_SLOTS; ++i) {
+                if (pending & (1u << i)) {
+                    const int64_t idx = end - 1 - (64 * i + lane);
+                    f[i] = __hip_atomic_load(&flags[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((uint32_t)(f[i] >> 36) == tag && ((f[i] >> 34) & 3u) != 0) pending &= ~(1u << i);
+                }
+            }
+            if (__all(pending == 0)) break;
             if (++spins >= SPIN_LIMIT) {
                 *timed_out = true;
                 return excl;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        const uint32_t st = (uint32_t)(f >> 34) & 3u;
-        uint64_t v = f & FLAG_VALUE_MASK;
-        const uint64_t pmask = __ballot(st == ST_PREFIX);
-        if (pmask) {
-            const int hp = 63 - __clzll((long long)pmask);
-            excl += wave_sum_u64(lane >= hp ? v : 0);
-            break;
+        // nearest PREFIX: smallest offset 64*i + lane among slots in state PREFIX
+        int stop = 64 * LB_SLOTS;  // offset of the nearest prefix, or none
+#pragma unroll
+        for (int i = 0; i < LB_SLOTS; ++i) {
+            const uint64_t pm = __ballot(((f[i] >> 34) & 3u) == ST_PREFIX);
+            if (pm && stop == 64 * LB_SLOTS) stop = 64 * i + (int)__builtin_ctzll(pm);
         }
-        excl += wave_sum_u64(v);
-        end -= 64;
+        uint64_t part = 0;
+#pragma unroll
+        for (int i = 0; i < LB_SLOTS; ++i)
+            if (64 * i + lane <= stop) part += f[i] & FLAG_VALUE_MASK;
+        excl += wave_sum_u64(part);
+        if (stop < 64 * LB_SLOTS) break;
+        end -= 64 * LB_SLOTS;
     }
     return excl;
 }

@@ -86,11 +86,12 @@ def header_bytes(n: int, chunk: int) -> int:
 
 
 def encoded_bound(n: int, chunk: int, max_len: int = 16) -> int:
-    """Largest possible stream size: every symbol at max_len bits plus one padding word per chunk."""
+    """Largest possible stream size (every symbol at max_len bits plus one padding word per
+    chunk), rounded up to a multiple of 16 bytes."""
     nc = num_chunks(n, chunk)
     if nc == 0:
         return 0
-    return header_bytes(n, chunk) + 4 * (-(-int(n) * int(max_len) // 32) + nc)
+    return _align16(header_bytes(n, chunk) + 4 * (-(-int(n) * int(max_len) // 32) + nc))
 
 
 def unit_starts(words: int, chunk: int) -> np.ndarray:

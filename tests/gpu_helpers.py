@@ -39,7 +39,7 @@ def _empty_encode(dcb, chunk):
 
 
 def gpu_decode(stream: np.ndarray, dcb, chunk: int, n: int):
-    buf = torch.zeros(max(16, stream.size), dtype=torch.uint8, device=DEV)
+    buf = torch.zeros((stream.size + 15) // 16 * 16 + 16, dtype=torch.uint8, device=DEV)
     if stream.size:
         buf[: stream.size] = to_dev(stream)
     out, res = lecb.decode_bytes(buf, stream.size, dcb, chunk, n)
