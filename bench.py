@@ -318,7 +318,30 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         if label in ("encode", "decode"):
             continue
         kernels[label] = T.mean_ms(label)
+    # ---------------- size accounting per stream (histogram kernel + host stats)
+    accounting = []
+    if cfg["kind"] == "bf16":
+        hh = torch.zeros(256, dtype=torch.int64, device=dev)
+        hl = torch.zeros(256, dtype=torch.int64, device=dev)
+        lecb.lecb_histogram_bf16(xd, hh, hl)
+        hists = [hh.cpu().numpy().astype(np.uint64), hl.cpu().numpy().astype(np.uint64)]
+        names = ["hi", "lo"]
+    else:
+        hx = torch.zeros(256, dtype=torch.int64, device=dev)
+        lecb.lecb_histogram(xd, hx)
+        hists = [hx.cpu().numpy().astype(np.uint64)]
+        names = ["bytes"]
+    for name, h, ln in zip(names, hists, lengths_out):
+        st = lecb.lecb_stream_stats(h, ln, 16)
+        accounting.append({
+            "stream": name,
+            "bits_per_symbol": round(st["payload_bits"] / st["n"], 5),
+            "entropy_bits": round(st["shannon_bits"] / st["n"], 5),
+            "gap_vs_shannon": round(st["payload_bits"] / max(st["shannon_bits"], 1e-9) - 1, 5),
+            "gap_vs_per_batch_optimal": round(st["payload_bits"] / max(st["optimal_bits"], 1) - 1, 5),
+        })
     info.update(
+        accounting=accounting,
         nbytes=nbytes, ms_step=ms_step, enc_ms=enc_ms, dec_ms=dec_ms, kernels=kernels,
         sizes=sizes, container=container, parity=parity,
         payload_bits=[int(v["payload_bits"]) for v in r],
@@ -361,8 +384,20 @@ def main():
     ap.add_argument("--config", default="bf16_weights", choices=list(workloads.CONFIGS))
     ap.add_argument("--scale", type=float, default=1.0, help="fraction of the config's size (tests)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 23, help="elements the oracle baseline codes")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24, help="elements the oracle baseline codes")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+
+        src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.calibrate_copy, "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the codec shards by whole chunks; see the multi-GPU notes of the design)", file=sys.stderr)
@@ -410,6 +445,7 @@ def main():
         "decode_ms": round(info["dec_ms"], 4),
         "ratio": round(nbytes / info["container"], 4),
         "bits_per_symbol": [round(b / cfg["n"], 4) for b in info["payload_bits"]],
+        "accounting": info["accounting"],
         "kernels": per_kernel,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -130,6 +130,27 @@ int lecb_build_codebook(const uint64_t hist[256], uint32_t max_len, uint32_t min
  * Errors: INVALID_ARG if a length exceeds 16 or the lengths violate Kraft. */
 int lecb_codebook_from_lengths(const uint8_t len[256], lecb_codebook* out);
 
+/* Size accounting of one coded stream ("Single-Stage Huffman Encoder for ML
+ * Compression", Key contributions and Results: the fixed codebook is compared
+ * with per-shard Huffman coding and with the Shannon bound).  From the data's
+ * histogram and the code lengths used:
+ *   n             = sum hist;
+ *   payload_bits  = sum hist[s] * len[s]       (what any encoder must emit);
+ *   shannon_bits  = n * H, H = -sum p log2 p   (empirical entropy, fp64);
+ *   optimal_bits  = payload bits of the optimal length-limited code built
+ *                   from this histogram itself (no clamp, limit max_len);
+ *   uncoded       = number of symbols whose length is 0 (cannot be coded).
+ * Errors: INVALID_ARG (null pointer, max_len not in 1..16). */
+typedef struct {
+    uint64_t n;
+    uint64_t payload_bits;
+    uint64_t optimal_bits;
+    uint64_t uncoded;
+    double shannon_bits;
+} lecb_stats;
+int lecb_stream_stats(const uint64_t hist[256], const uint8_t len[256], uint32_t max_len,
+                      lecb_stats* out);
+
 /* Size of the device-resident codebook (encode table + decode tables). */
 uint64_t lecb_device_codebook_bytes(void);
 

@@ -52,6 +52,19 @@ class lecb_codebook(ctypes.Structure):
         return np.array(self.code, dtype=np.uint32)
 
 
+class lecb_stats(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_uint64),
+        ("payload_bits", ctypes.c_uint64),
+        ("optimal_bits", ctypes.c_uint64),
+        ("uncoded", ctypes.c_uint64),
+        ("shannon_bits", ctypes.c_double),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 RESULT_DTYPE = np.dtype([("bytes", "<u8"), ("payload_bits", "<u8"), ("status", "<i4"), ("reserved", "<u4")])
 
 _u64 = ctypes.c_uint64
@@ -69,6 +82,7 @@ _SIGNATURES = {
     "lecb_build_codebook": (_int, [_vp, _u32, _u32, ctypes.POINTER(lecb_codebook)]),
     "lecb_codebook_from_lengths": (_int, [_vp, ctypes.POINTER(lecb_codebook)]),
     "lecb_device_codebook_bytes": (_u64, []),
+    "lecb_stream_stats": (_int, [_vp, _vp, _u32, ctypes.POINTER(lecb_stats)]),
     "lecb_container_write_header": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _u64, _u64]),
     "lecb_container_read_header": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lecb_workspace_init": (_int, [_vp, _u64, _vp]),
@@ -174,6 +188,17 @@ def lecb_codebook_from_lengths(lengths) -> lecb_codebook:
     _check(load().lecb_codebook_from_lengths(ln.ctypes.data, ctypes.byref(cb)),
            "lecb_codebook_from_lengths")
     return cb
+
+
+def lecb_stream_stats(hist, lengths, max_len: int = 16) -> dict:
+    h = np.ascontiguousarray(np.asarray(hist, dtype=np.uint64))
+    ln = np.ascontiguousarray(np.asarray(lengths, dtype=np.uint8))
+    if h.shape != (256,) or ln.shape != (256,):
+        raise ValueError("histogram and lengths must have 256 entries")
+    st = lecb_stats()
+    _check(load().lecb_stream_stats(h.ctypes.data, ln.ctypes.data, max_len, ctypes.byref(st)),
+           "lecb_stream_stats")
+    return st.as_dict()
 
 
 def lecb_container_write_header(n, chunk, max_len, len_hi, len_lo, bytes_hi, bytes_lo) -> np.ndarray:

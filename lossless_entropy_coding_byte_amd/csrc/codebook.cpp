@@ -15,6 +15,7 @@
 // unique): coins are ordered by (frequency, byte value); at equal weight a
 // coin is placed before a package.
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -140,6 +141,33 @@ int lecb_build_codebook(const uint64_t hist[256], uint32_t max_len, uint32_t min
 
 int lecb_codebook_from_lengths(const uint8_t len[256], lecb_codebook* out) {
     return lecb::canonical_from_lengths(len, out);
+}
+
+int lecb_stream_stats(const uint64_t hist[256], const uint8_t len[256], uint32_t max_len,
+                      lecb_stats* out) {
+    if (!hist || !len || !out || max_len < 1 || max_len > 16) return LECB_ERR_INVALID_ARG;
+    std::memset(out, 0, sizeof(*out));
+    for (int s = 0; s < 256; ++s) {
+        out->n += hist[s];
+        out->payload_bits += hist[s] * len[s];
+        if (!len[s]) out->uncoded += hist[s];
+    }
+    if (out->n) {
+        const double n = (double)out->n;
+        double h = 0.0;
+        for (int s = 0; s < 256; ++s) {
+            if (hist[s]) {
+                const double p = (double)hist[s] / n;
+                h -= p * std::log2(p);
+            }
+        }
+        out->shannon_bits = n * h;
+        uint8_t opt[256];
+        const int rc = lecb::build_lengths(hist, max_len, 0, opt);
+        if (rc == LECB_OK)
+            for (int s = 0; s < 256; ++s) out->optimal_bits += hist[s] * opt[s];
+    }
+    return LECB_OK;
 }
 
 static void put_u16(uint8_t* p, uint16_t v) { std::memcpy(p, &v, 2); }

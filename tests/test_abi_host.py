@@ -118,3 +118,20 @@ def test_container_header_matches_oracle():
     back = lecb.lecb_container_read_header(got)
     assert back["n"] == x.size and back["bytes_lo"] == enc["stream_lo"].size
     assert np.array_equal(back["len_hi"], enc["len_hi"])
+
+
+def test_stream_stats_match_oracle():
+    import workloads
+
+    x = workloads.int8_fixed(0)
+    warm = np.sum([oracle.histogram(workloads.int8_fixed(r)) for r in (1, 2, 3, 4)], axis=0, dtype=np.uint64)
+    ln = oracle.package_merge_lengths(oracle.codebook_frequencies([warm], 1), 16)
+    h = oracle.histogram(x)
+    st = lecb.lecb_stream_stats(h, ln, 16)
+    assert st["n"] == x.size and st["uncoded"] == 0
+    assert st["payload_bits"] == oracle.payload_bits_identity(h, ln)
+    assert st["optimal_bits"] == oracle.per_batch_optimal_bits(h, 16)
+    assert abs(st["shannon_bits"] - oracle.metrics.shannon_bits(h)) < 1e-6 * st["shannon_bits"]
+    ln2 = ln.copy()
+    ln2[int(np.argmax(h))] = 0
+    assert lecb.lecb_stream_stats(h, ln2, 16)["uncoded"] == int(h.max())
