@@ -8,15 +8,33 @@
 //
 // One lane per unit, 256 units per workgroup (K divides 256, so a chunk's
 // units never straddle workgroups).  Per lane:
-//   1. count the code words between its start and the next unit's start
-//      (the chunk's last unit takes the remainder of the chunk's symbols);
-//   2. exclusive scan of the counts inside each chunk -> output offsets;
-//   3. decode again, storing 16 symbols per 16-byte store.
-// Each lane reads its unit's words straight from global memory, 64 bytes per
-// refill (four 16-byte loads issued together), so a lane waits on memory once
-// per 16 payload words.  A code word is looked up with the next LUT_BITS bits
-// in an LDS table; longer ones use the canonical per-length limits.  Every
-// structural rule of the format is checked; a violation sets status CORRUPT.
+//   1. count pass: code words that start in [start, end) of the unit; the
+//      loop stops exactly at `end`, which checks that `end` is a code-word
+//      boundary and that the stored gap names the first one.  The chunk's
+//      last unit counts only the code words that start before the chunk's
+//      last payload word;
+//   2. exclusive scan of the counts inside each chunk -> output offsets; the
+//      last unit now knows how many code words remain in the last word,
+//      decodes them and checks the zero padding behind them;
+//   3. decode pass: output is written in aligned 16-byte blocks only.  A lane
+//      owns the blocks that START inside its output range; it skips the code
+//      words in front of its first block (the previous lane's last block holds
+//      them) and decodes on past its own end, into the next unit's code words,
+//      to fill its last block.  Blocks never cross a chunk: the output buffer
+//      is 16-byte aligned and a chunk holds a multiple of 256 symbols.
+//
+// Bit reader: a window of two payload words and a bit offset into it; before
+// every pair of code words the window slides by one word when its first word
+// is used up (no branch).  Afterwards the offset is below 32, so the window
+// holds >= 33 bits, enough for two code words of at most 16 bits.  The words
+// come from a per-lane ring of 16 payload words in LDS; the ring is topped up on a fixed
+// schedule (every 4 refills) by one masked 32-byte global load whose data go
+// into the ring at the next top-up, so the decode loop never waits on global
+// memory.  Ring slot q of lane L sits at ring[q][L]: each lane has its own bank.
+//
+// A code word of at most LUT_BITS bits is one LDS lookup; longer ones use the
+// canonical per-length limits.  Every structural rule of the format is
+// checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
 #include "lecb_internal.hpp"
@@ -25,7 +43,8 @@ namespace lecb {
 
 namespace {
 
-constexpr int DEC_MAX_THREADS = 256;
+constexpr int DEC_THREADS = 256;
+constexpr uint32_t RING = 16;  // payload words per lane in LDS
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 struct DecArgs {
@@ -48,102 +67,128 @@ struct DecArgs {
 };
 
 struct Tables {
-    uint16_t lut[LUT_SIZE];
-    uint32_t limit[17];
-    uint32_t first[17];
-    uint32_t base[17];
+    uint16_t lut[LUT_SIZE];   // (sym << 8) | len
+    uint32_t off[17];         // base[l] - first[l]: index in `sorted` is off[l] + code
     uint8_t sorted[256];
 };
 
-// Bit reader over one decode unit: a 64-bit bit buffer fed from a queue of
-// 16 payload words held in registers.  An empty queue is refilled with four
-// 16-byte loads at once (the lane waits for them: one wait per 16 words).
-// Loads are at a clamped address (the caller's buffer is readable up to the
-// next 16-byte boundary); words past the payload read as zero.
-struct Reader {
-    const uint32_t* p;
-    uint64_t limit;   // payload words
-    uint64_t gmax;    // last readable 16-byte group
-    uint64_t g;       // next group to load
-    uint64_t widx;    // payload index of q0.x
-    v4u q0, q1, q2, q3;
-    int nq;           // words left in the queue
-    uint64_t buf;     // pending bits, MSB first
-    int nb;           // valid bits in buf
+struct Shared {
+    uint32_t ring[RING][DEC_THREADS];
+    Tables T;
+    uint32_t cnt[DEC_THREADS];
+    uint64_t red[DEC_THREADS / 64];
+};
 
-    __device__ inline v4u ld4(uint64_t grp) const {
-        return *reinterpret_cast<const v4u*>(p + 4 * min(grp, gmax));
+// Left-aligned canonical limits of the lengths above LUT_BITS (uniform values).
+struct Limits {
+    uint32_t l13, l14, l15, l16;
+};
+
+struct Reader {
+    uint32_t* ring;      // &ring[0][lane]
+    const uint32_t* p;   // payload
+    uint64_t sw;         // chunk's first payload word
+    uint64_t gmax;       // last readable 4-word group of the payload
+    uint32_t sh;         // sw mod RING
+    uint32_t rq;         // sh + index (relative to sw) of the word held in nextw;
+                         // w1 is the word before it, w0 the one before that
+    uint32_t wr;         // next word (relative to sw) to load; sw + wr is a multiple of 8
+    uint32_t w0, w1;     // 64-bit window; the next bit is bit `off` from the top of w0
+    uint32_t off;        // < 32 after refill()
+    uint32_t nextw;
+    v4u pa, pb;          // loaded, not yet in the ring
+    bool pend;
+
+    __device__ inline uint32_t& slot(uint32_t w) {  // w relative to sw
+        return ring[((w + sh) & (RING - 1)) * DEC_THREADS];
     }
-    __device__ inline void fill() {
-        q0 = ld4(g);
-        q1 = ld4(g + 1);
-        q2 = ld4(g + 2);
-        q3 = ld4(g + 3);
-        g += 4;
-        nq = 16;
+    __device__ inline uint32_t rd() const { return rq - sh; }
+    __device__ inline v4u ld4(uint64_t g) const {
+        return *reinterpret_cast<const v4u*>(p + 4 * (g < gmax ? g : gmax));
     }
-    __device__ inline uint32_t pop() {
-        if (nq == 0) fill();
-        const uint32_t w = widx < limit ? q0.x : 0u;
-        ++widx;
-        q0.x = q0.y;
-        q0.y = q0.z;
-        q0.z = q0.w;
-        if ((--nq & 3) == 0) {
-            q0 = q1;
-            q1 = q2;
-            q2 = q3;
+    __device__ inline void put8(uint32_t w, const v4u& x, const v4u& y) {
+        uint32_t* s = &slot(w);  // w..w+7 are consecutive slots (sw + w is a multiple of 8)
+        s[0 * DEC_THREADS] = x.x;
+        s[1 * DEC_THREADS] = x.y;
+        s[2 * DEC_THREADS] = x.z;
+        s[3 * DEC_THREADS] = x.w;
+        s[4 * DEC_THREADS] = y.x;
+        s[5 * DEC_THREADS] = y.y;
+        s[6 * DEC_THREADS] = y.z;
+        s[7 * DEC_THREADS] = y.w;
+    }
+    // Ring top-up: commit the previous load, issue the next one when there is
+    // room.  Between two top-ups at most 4 words leave the ring, and after a
+    // top-up at least 5 committed words lie at or after rd, so the word read
+    // by refill() is always in the ring.
+    __device__ inline void tick() {
+        if (pend) {
+            put8(wr - 8, pa, pb);
+            pend = false;
         }
-        return w;
+        if (wr - rd() <= 8) {
+            const uint64_t g = (sw + wr) >> 2;
+            pa = ld4(g);
+            pb = ld4(g + 1);
+            wr += 8;
+            pend = true;
+        }
     }
-    __device__ inline void start(const uint32_t* payload, uint64_t words, uint64_t word,
-                                 uint32_t bit) {
-        p = payload;
-        limit = words;
-        gmax = words ? (words - 1) >> 2 : 0;
-        g = word >> 2;
-        widx = word & ~uint64_t(3);
-        fill();
-        for (uint32_t k = 0; k < (uint32_t)(word & 3); ++k) (void)pop();
-        const uint32_t w0 = pop();
-        const uint32_t w1 = pop();
-        buf = (((uint64_t)w0 << 32) | w1) << bit;
-        nb = 64 - (int)bit;
+    // Position the reader at bit `bit` of the chunk (synchronous 16-word load).
+    __device__ inline void start(uint32_t bit) {
+        const uint32_t word = bit >> 5;
+        const uint64_t a = (sw + word) & ~uint64_t(7);
+        wr = (uint32_t)(a - sw);
+        put8(wr, ld4(a >> 2), ld4((a >> 2) + 1));
+        put8(wr + 8, ld4((a >> 2) + 2), ld4((a >> 2) + 3));
+        wr += 16;
+        pend = false;
+        w0 = slot(word);
+        w1 = slot(word + 1);
+        rq = word + 2 + sh;
+        nextw = ring[(rq & (RING - 1)) * DEC_THREADS];
+        off = bit & 31;
     }
-    // afterwards at least 32 bits are buffered: room for two code words
+    // The next 32 bits, MSB first (all of them valid while off <= 32).
+    __device__ inline uint32_t peek() const {
+        return (uint32_t)(((((uint64_t)w0 << 32) | w1) << off) >> 32);
+    }
+    // bits consumed, relative to the chunk start
+    __device__ inline uint32_t pos() const { return 32 * (rd() - 2) + off; }
+    // Slide the window by one word once its first word is used up.  No
+    // branch; afterwards off < 32 (the caller never lets off reach 64).
     __device__ inline void refill() {
-        if (nb < 32) {
-            buf |= (uint64_t)pop() << (32 - nb);
-            nb += 32;
-        }
+        const bool take = off >= 32;
+        w0 = take ? w1 : w0;
+        w1 = take ? nextw : w1;
+        off &= 31;
+        rq += take ? 1u : 0u;
+        nextw = ring[(rq & (RING - 1)) * DEC_THREADS];
     }
 };
 
-// One code word: returns its length (0 = no code word matches) and the symbol.
-// The caller guarantees at least 16 buffered bits (refill() before every
-// second code word).
-template <class R>
-__device__ inline uint32_t decode_one(const Tables& T, R& r, uint32_t& sym) {
-    const uint32_t e = T.lut[r.buf >> (64 - LUT_BITS)];
-    uint32_t len;
-    if (e) {
-        len = e >> 8;
-        sym = e & 0xFFu;
-    } else {
-        const uint32_t v = (uint32_t)(r.buf >> 48);
-        len = 0;
-        for (uint32_t l = LUT_BITS + 1; l <= 16; ++l) {
-            if (v < T.limit[l]) {
-                len = l;
-                break;
-            }
+// Next code word as (sym << 8) | len, len in 1..16, from the next 32 bits
+// `top`.  An invalid code word yields len 16 and sets `inval`.
+__device__ inline uint32_t lookup(const Tables& T, const Limits& L, uint32_t top, uint32_t& inval) {
+    uint32_t e = T.lut[top >> (32 - LUT_BITS)];
+    if (e == 0) {
+        const uint32_t v = top >> 16;
+        const uint32_t len = 13u + (v >= L.l13) + (v >= L.l14) + (v >= L.l15);
+        if (v >= L.l16) {
+            inval = 1;
+            e = 16;
+        } else {
+            e = ((uint32_t)T.sorted[(T.off[len] + (v >> (16 - len))) & 255u] << 8) | len;
         }
-        if (!len) return 0;
-        sym = T.sorted[T.base[len] + (v >> (16 - len)) - T.first[len]];
     }
-    r.buf <<= len;
-    r.nb -= (int)len;
-    return len;
+    return e;
+}
+
+// Decode one code word and advance; returns (sym << 8) | len.
+__device__ inline uint32_t step(const Tables& T, const Limits& L, Reader& r, uint32_t& inval) {
+    const uint32_t e = lookup(T, L, r.peek(), inval);
+    r.off += e & 0xFFu;
+    return e;
 }
 
 __device__ inline uint32_t gap_of(const uint8_t* gaps, uint64_t i) {
@@ -151,190 +196,201 @@ __device__ inline uint32_t gap_of(const uint8_t* gaps, uint64_t i) {
     return (i & 1) ? (b >> 4) : (b & 0xFu);
 }
 
-// Per-unit geometry, computed by every lane for its own unit.
-struct Unit {
-    uint64_t c;          // chunk
-    uint32_t j;          // unit within the chunk
-    bool active, last, bad;
-    uint64_t sw, wc;     // chunk's first payload word and word count
-    uint32_t start_bit, end_bit, sj1, m_c;
-};
-
-// Count pass: code words in [start_bit, end_bit); validates the boundary.
-__device__ inline uint32_t count_unit(const Tables& T, const Unit& U, const uint32_t* payload,
-                                      uint64_t words, bool& bad) {
-    Reader r;
-    r.start(payload, words, U.sw + (U.start_bit >> 5), U.start_bit & 31);
-    uint32_t pos = U.start_bit, last_start = 0xFFFFFFFFu, cnt = 0;
-    while (pos < U.end_bit) {
-        uint32_t sym;
-        if (cnt & 1) r.refill();  // >= 32 bits after start; refill before every odd symbol
-        const uint32_t len = decode_one(T, r, sym);
-        if (!len) {
-            bad = true;
-            return cnt;
-        }
-        last_start = pos;
-        pos += len;
-        ++cnt;
-    }
-    if (pos != U.end_bit) bad = true;
-    // the stored gap must name the FIRST boundary at or after sj1
-    if (U.end_bit != U.sj1 && last_start != 0xFFFFFFFFu && last_start >= U.sj1) bad = true;
-    return cnt;
-}
-
-// Decode pass: cnt symbols to dst (byte stores to a 16-byte boundary, then
-// 16 symbols per 16-byte store, then the tail).  Returns the bits consumed.
-__device__ inline uint32_t decode_unit(const Tables& T, const Unit& U, const uint32_t* payload,
-                                       uint64_t words, uint32_t cnt, uint8_t* dst, bool& bad) {
-    Reader r;
-    r.start(payload, words, U.sw + (U.start_bit >> 5), U.start_bit & 31);
-    uint32_t pos = U.start_bit;
-    bool invalid = false;
-    uint32_t k = 0;
-    const uint32_t head = min(cnt, (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u));
-    for (; k < head; ++k) {
-        uint32_t sym = 0;
-        if (k & 1) r.refill();
-        const uint32_t len = decode_one(T, r, sym);
-        invalid |= len == 0;
-        pos += len;
-        dst[k] = (uint8_t)sym;
-    }
-    for (; k + 16 <= cnt; k += 16) {
-        uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t sym = 0;
-            if ((k + i) & 1) r.refill();  // parity of the symbol index within the unit
-            const uint32_t len = decode_one(T, r, sym);
-            invalid |= len == 0;
-            pos += len;
-            w[i >> 2] |= (sym & 0xFFu) << (8 * (i & 3));
-        }
-        v4u v;
-        v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
-        *reinterpret_cast<v4u*>(dst + k) = v;
-    }
-    for (; k < cnt; ++k) {
-        uint32_t sym = 0;
-        if (k & 1) r.refill();
-        const uint32_t len = decode_one(T, r, sym);
-        invalid |= len == 0;
-        pos += len;
-        dst[k] = (uint8_t)sym;
-    }
-    bad |= invalid;
-    if (!bad && U.last) {
-        // data must end inside the chunk's last word, followed by zero padding
-        const uint64_t endw = (uint64_t)U.wc << 5;
-        if (pos > endw || pos + 32 <= endw) bad = true;
-        else {
-            const uint32_t rest = (uint32_t)(endw - pos);
-            r.refill();
-            if (rest && (r.buf >> (64 - rest)) != 0) bad = true;
-        }
-    }
-    return pos - U.start_bit;
-}
-
-__global__ __launch_bounds__(DEC_MAX_THREADS) void decode_kernel(DecArgs a) {
-    __shared__ __attribute__((aligned(16))) Tables T;
-    __shared__ uint32_t s_cnt[DEC_MAX_THREADS];
-    __shared__ uint64_t s_lo[DEC_MAX_THREADS / 64];
-    __shared__ uint64_t s_hi[DEC_MAX_THREADS / 64];
+__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
+    __shared__ __attribute__((aligned(16))) Shared S;
+    Tables& T = S.T;
 
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
-    const int nwaves = nthreads / 64;
     {
-        // 16-byte copies of the lookup table (LUT_SIZE * 2 bytes)
         const v4u* src = reinterpret_cast<const v4u*>(a.cb->lut);
         v4u* dst = reinterpret_cast<v4u*>(T.lut);
         constexpr int NV = LUT_SIZE * 2 / 16;
-        for (int i = tid; i < NV; i += nthreads) dst[i] = src[i];
+        for (int i = tid; i < NV; i += DEC_THREADS) dst[i] = src[i];
     }
-    if (tid < 17) {
-        T.limit[tid] = a.cb->limit[tid];
-        T.first[tid] = a.cb->first[tid];
-        T.base[tid] = a.cb->base[tid];
-    }
-    for (int i = tid; i < 256; i += nthreads) T.sorted[i] = a.cb->sorted[i];
+    if (tid < 17) T.off[tid] = a.cb->base[tid] - a.cb->first[tid];
+    T.sorted[tid] = a.cb->sorted[tid];
+    Limits L;
+    L.l13 = a.cb->limit[13];
+    L.l14 = a.cb->limit[14];
+    L.l15 = a.cb->limit[15];
+    L.l16 = a.cb->limit[16];
 
     // ---- unit geometry
     const uint32_t K = 1u << a.log2k;
-    Unit U;
-    const uint64_t u = (uint64_t)blockIdx.x * nthreads + tid;
-    U.c = u >> a.log2k;
-    U.j = (uint32_t)(u & (K - 1));
-    U.active = U.c < a.nc;
-    U.last = U.j == K - 1;
-    U.bad = false;
-    U.sw = U.wc = 0;
-    U.start_bit = U.end_bit = U.sj1 = U.m_c = 0;
-    if (U.active) {
-        U.sw = U.c ? a.table[U.c - 1] : 0;
-        const uint64_t ew = a.table[U.c];
-        if (ew <= U.sw || ew > a.payload_words || ew - U.sw > a.chunk / 2) U.bad = true;
-        U.wc = U.bad ? 0 : ew - U.sw;
-        U.m_c = (uint32_t)min<uint64_t>(a.chunk, a.n - U.c * a.chunk);
-        const uint32_t sj = (uint32_t)(((uint64_t)U.j * U.wc) >> a.log2k) << 5;
+    const uint64_t u = (uint64_t)blockIdx.x * DEC_THREADS + tid;
+    const uint64_t c = u >> a.log2k;
+    const uint32_t j = (uint32_t)(u & (K - 1));
+    const bool active = c < a.nc;
+    const bool last = j == K - 1;
+    bool bad = false;
+    uint64_t sw = 0, wc = 0;
+    uint32_t start_bit = 0, end_bit = 0, sj1 = 0, m_c = 0;
+    if (active) {
+        sw = c ? a.table[c - 1] : 0;
+        const uint64_t ew = a.table[c];
+        if (ew <= sw || ew > a.payload_words || ew - sw > a.chunk / 2) bad = true;
+        wc = bad ? 0 : ew - sw;
+        m_c = (uint32_t)min<uint64_t>(a.chunk, a.n - c * a.chunk);
+        const uint32_t sj = (uint32_t)(((uint64_t)j * wc) >> a.log2k) << 5;
         const uint32_t gj = gap_of(a.gaps, u);
-        if (U.j == 0 && gj != 0) U.bad = true;
-        U.start_bit = sj + gj;
-        if (!U.last) {
-            U.sj1 = (uint32_t)(((uint64_t)(U.j + 1) * U.wc) >> a.log2k) << 5;
-            U.end_bit = U.sj1 + gap_of(a.gaps, u + 1);
+        if (j == 0 && gj != 0) bad = true;
+        start_bit = sj + gj;
+        if (!last) {
+            sj1 = (uint32_t)(((uint64_t)(j + 1) * wc) >> a.log2k) << 5;
+            end_bit = sj1 + gap_of(a.gaps, u + 1);
+            if (start_bit > end_bit) bad = true;
         } else {
-            U.end_bit = (uint32_t)(U.wc << 5);
+            end_bit = wc ? (uint32_t)((wc - 1) << 5) : 0u;  // start of the last word
         }
     }
+
+    Reader r;
+    r.ring = &S.ring[0][tid];
+    r.p = a.payload;
+    r.sw = sw;
+    r.gmax = a.payload_words ? (a.payload_words - 1) >> 2 : 0;
+    r.sh = (uint32_t)sw & (RING - 1);
+    const bool run = active && !bad;
 
     __syncthreads();  // tables complete
 
     // ---- 1. count
     uint32_t cnt = 0;
-    bool bad = U.bad;
-    if (U.active && !U.last && !bad)
-        cnt = count_unit(T, U, a.payload, a.payload_words, bad);
-
-    // ---- 2. exclusive scan of counts within each chunk (segments of K lanes)
-    s_cnt[tid] = cnt;
-    __syncthreads();
-    for (int o = 1; o < nthreads; o <<= 1) {
-        const uint32_t v = tid >= o ? s_cnt[tid - o] : 0u;
-        __syncthreads();
-        s_cnt[tid] += v;
-        __syncthreads();
-    }
-    const int seg0 = tid - (int)U.j;  // lane of unit 0 of this chunk
-    const uint32_t before_seg = seg0 > 0 ? s_cnt[seg0 - 1] : 0u;
-    const uint32_t out_off = s_cnt[tid] - cnt - before_seg;
-    if (U.active) {
-        if (U.last) {
-            if (out_off > U.m_c) bad = true;
-            else cnt = U.m_c - out_off;
-        } else if (out_off + cnt > U.m_c) {
-            bad = true;  // never store outside this chunk's slot
+    if (run) {
+        r.start(start_bit);
+        uint32_t e = 0, inval = 0;
+        // pos() < end_bit  <=>  off < thr = endq - 32 * rq
+        const int32_t endq = (int32_t)(end_bit + 32 * (r.sh + 2));
+        int32_t thr = endq - (int32_t)(r.rq << 5);
+        while ((int32_t)r.off < thr) {
+            r.tick();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                r.refill();
+                thr = endq - (int32_t)(r.rq << 5);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    if ((int32_t)r.off < thr) {
+                        e = step(T, L, r, inval);
+                        ++cnt;
+                    }
+                }
+            }
+        }
+        r.refill();
+        bad |= inval != 0;
+        if (!last) {
+            const uint32_t pos = r.pos();
+            if (pos != end_bit) bad = true;
+            // the stored gap must name the FIRST code-word boundary at or after sj1
+            if (cnt && end_bit != sj1 && pos - (e & 0xFFu) >= sj1) bad = true;
         }
     }
 
-    // ---- 3. decode and store
+    // ---- 2. exclusive scan of counts within each chunk (segments of K lanes)
+    S.cnt[tid] = cnt;
+    __syncthreads();
+    for (int o = 1; o < DEC_THREADS; o <<= 1) {
+        const uint32_t v = tid >= o ? S.cnt[tid - o] : 0u;
+        __syncthreads();
+        S.cnt[tid] += v;
+        __syncthreads();
+    }
+    const int seg0 = tid - (int)j;  // lane of unit 0 of this chunk
+    const uint32_t before_seg = seg0 > 0 ? S.cnt[seg0 - 1] : 0u;
+    const uint32_t out_off = S.cnt[tid] - cnt - before_seg;
     uint64_t used_bits = 0;
-    if (U.active && !bad) {
-        uint8_t* dst = a.out + U.c * a.chunk + out_off;
-        used_bits = decode_unit(T, U, a.payload, a.payload_words, cnt, dst, bad);
+    if (run && !bad) {
+        if (last) {
+            // the code words left in the chunk's last word, then zero padding
+            if (out_off + cnt > m_c || m_c - out_off - cnt > 32) {
+                bad = true;
+            } else {
+                const uint32_t rem = m_c - out_off - cnt;
+                uint32_t inval = 0;
+                for (uint32_t i = 0; i < rem; ++i) {
+                    if ((i & 3) == 0) r.tick();
+                    r.refill();
+                    (void)step(T, L, r, inval);
+                }
+                r.refill();
+                cnt += rem;
+                const uint32_t endw = (uint32_t)(wc << 5);
+                const uint32_t pos = r.pos();
+                if (inval || pos > endw || pos + 32 <= endw) {
+                    bad = true;
+                } else {
+                    const uint32_t rest = endw - pos;
+                    if (rest && (r.peek() >> (32 - rest)) != 0) bad = true;
+                }
+                used_bits = pos - start_bit;
+            }
+        } else {
+            if (out_off + cnt > m_c) bad = true;
+            used_bits = end_bit - start_bit;
+        }
     }
 
     // padding bytes of the header are part of the format
     if (blockIdx.x == 0) {
-        for (uint64_t b = a.table_pad_from + tid; b < a.table_pad_to; b += nthreads)
+        for (uint64_t b = a.table_pad_from + tid; b < a.table_pad_to; b += DEC_THREADS)
             bad |= a.stream[b] != 0;
-        for (uint64_t b = a.gap_pad_from + tid; b < a.gap_pad_to; b += nthreads)
+        for (uint64_t b = a.gap_pad_from + tid; b < a.gap_pad_to; b += DEC_THREADS)
             bad |= a.stream[b] != 0;
         if (tid == 0 && ((a.nc << a.log2k) & 1))
             bad |= (a.stream[a.gap_pad_from - 1] >> 4) != 0;
+    }
+    const int wg_bad = __syncthreads_or(bad);
+
+    // ---- 3. decode pass: the aligned 16-byte blocks that start in this lane's range
+    if (run && !wg_bad) {
+        uint8_t* const base = a.out + c * a.chunk + out_off;
+        const uint32_t h = (16u - (uint32_t)((uintptr_t)base & 15u)) & 15u;
+        const uint32_t nblk = cnt > h ? (cnt - h + 15u) >> 4 : 0u;
+        if (nblk) {
+            r.start(start_bit);
+            uint32_t inval = 0;  // cannot be set: the count pass read the same bits
+            for (uint32_t i = 0; i < h; ++i) {
+                if ((i & 3) == 0) r.tick();
+                r.refill();
+                (void)step(T, L, r, inval);
+            }
+            uint8_t* dst = base + h;
+            const uint32_t full = min(nblk, (m_c - out_off - h) >> 4);  // blocks before the tensor end
+            uint32_t b = 0;
+            for (; b < full; ++b) {
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if ((q & 3) == 0) r.tick();
+                    r.refill();
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const uint32_t e = step(T, L, r, inval);
+                        const int i = 2 * q + k;
+                        const uint32_t sym = e >> 8;
+                        if ((i & 3) == 0) w[i >> 2] = sym;
+                        else w[i >> 2] |= sym << (8 * (i & 3));
+                    }
+                }
+                v4u v;
+                v.x = w[0];
+                v.y = w[1];
+                v.z = w[2];
+                v.w = w[3];
+                *reinterpret_cast<v4u*>(dst + 16 * b) = v;
+            }
+            if (b < nblk) {
+                // the tensor ends inside this block: byte stores up to its end
+                const uint32_t left = m_c - out_off - h - 16 * b;
+                for (uint32_t i = 0; i < left; ++i) {
+                    if ((i & 3) == 0) r.tick();
+                    r.refill();
+                    const uint32_t e = step(T, L, r, inval);
+                    dst[16 * b + i] = (uint8_t)(e >> 8);
+                }
+            }
+        }
     }
 
     // ---- status, accounting, exit
@@ -342,11 +398,11 @@ __global__ __launch_bounds__(DEC_MAX_THREADS) void decode_kernel(DecArgs a) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     __syncthreads();
-    if ((tid & 63) == 0) s_lo[tid >> 6] = v;
+    if ((tid & 63) == 0) S.red[tid >> 6] = v;
     const int any_bad = __syncthreads_or(bad);
     if (tid == 0) {
         uint64_t tot = 0;
-        for (int w = 0; w < nwaves; ++w) tot += s_lo[w];
+        for (int w = 0; w < DEC_THREADS / 64; ++w) tot += S.red[w];
         if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(&a.ws->bits), (unsigned long long)tot);
         if (any_bad) atomicCAS(&a.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
         __threadfence();
@@ -394,8 +450,8 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
     a.ws = L.ws;
 
     const uint64_t units = L.nc * K;
-    const uint64_t grid = (units + DEC_MAX_THREADS - 1) / DEC_MAX_THREADS;
-    hipLaunchKernelGGL(decode_kernel, dim3((uint32_t)grid), dim3(DEC_MAX_THREADS), 0,
+    const uint64_t grid = (units + DEC_THREADS - 1) / DEC_THREADS;
+    hipLaunchKernelGGL(decode_kernel, dim3((uint32_t)grid), dim3(DEC_THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void codebook_kernel(CodebookArgs a, DeviceCod
         for (int l = 1; l <= LUT_BITS; ++l) {
             const uint32_t v = (uint32_t)t >> (LUT_BITS - l);
             if (a.count[l] && v >= a.first[l] && v < a.first[l] + a.count[l]) {
-                entry = (uint16_t)((l << 8) | a.sorted[a.base[l] + v - a.first[l]]);
+                entry = (uint16_t)((a.sorted[a.base[l] + v - a.first[l]] << 8) | l);
                 break;
             }
         }

@@ -15,8 +15,8 @@ constexpr int LUT_SIZE = 1 << LUT_BITS;
 
 struct DeviceCodebook {
     uint32_t enc[256];        // (code << 5) | len ; len 0 = byte has no code word
-    uint16_t lut[LUT_SIZE];   // next LUT_BITS bits -> (len << 8) | sym, len <= LUT_BITS; 0 = longer/none
-    uint32_t limit[17];       // per length l: (first[l] + count[l]) << (16 - l); 0 if no codes
+    uint16_t lut[LUT_SIZE];   // next LUT_BITS bits -> (sym << 8) | len, len <= LUT_BITS; 0 = longer/none
+    uint32_t limit[17];       // per length l: (first[l] + count[l]) << (16 - l), non-decreasing in l
     uint32_t first[17];       // first canonical code of length l
     uint32_t base[17];        // index in `sorted` of the first symbol of length l
     uint8_t sorted[256];      // coded symbols by (length, byte value)
