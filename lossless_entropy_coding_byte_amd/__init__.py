@@ -107,6 +107,13 @@ def load() -> ctypes.CDLL:
     """Load liblecb.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch first: the library's HIP runtime dependency must resolve to the
+        # runtime torch already holds, or the process ends up with two runtimes
+        # and the second one finds no device
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -m lossless_entropy_coding_byte_amd.build`"
