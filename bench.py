@@ -206,12 +206,9 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
             cb_lo = lecb.lecb_build_codebook(h[256:], 16, 0)
             lecb.lecb_codebook_upload(cb_hi, blob_hi)
             lecb.lecb_codebook_upload(cb_lo, blob_lo)
-            T.start("encode_hi")
-            lecb.lecb_encode_plane(xd, n, 1, blob_hi, chunk, out_hi, res[:24], ws)
-            T.stop("encode_hi")
-            T.start("encode_lo")
-            lecb.lecb_encode_plane(xd, n, 0, blob_lo, chunk, out_lo, res[24:], ws)
-            T.stop("encode_lo")
+            T.start("encode_pair")
+            lecb.lecb_encode_bf16(xd, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res, ws)
+            T.stop("encode_pair")
             T.stop("encode")
             r = lecb.results_to_numpy(res)
             T.start("decode")
@@ -356,8 +353,8 @@ def roofline(cfg, info):
     if cfg["kind"] == "bf16":
         s_hi, s_lo = info["sizes"]
         algo = {
-            # plane encode reads the 16-bit words (both bytes share each word) and writes its stream
-            "encode_hi": 2 * n + s_hi, "encode_lo": 2 * n + s_lo,
+            # the pair encode reads the 16-bit words once and writes both streams
+            "encode_pair": 2 * n + s_hi + s_lo,
             # plane decode reads its stream and writes one byte per element
             "decode_hi": s_hi + n, "decode_lo": s_lo + n,
             "histogram": 2 * n, "merge": 4 * n,

@@ -224,16 +224,30 @@ int lecb_encode_plane(const uint16_t* d_in, uint64_t n, int plane, const void* d
                       uint32_t chunk, uint8_t* d_out, uint64_t out_capacity,
                       lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream);
 
+/* Both byte planes of 16-bit words in ONE pass over d_in, each with its own
+ * codebook ("Lossless Compression for LLM Tensor Incremental Snapshots",
+ * Technical framework: byte grouping, then Huffman coding of each group;
+ * with codebooks built beforehand, as "Single-Stage Huffman Encoder for ML
+ * Compression", Methodology step 4).  Stream "hi" codes in >> 8 with d_blob_hi
+ * into d_out_hi, stream "lo" codes in & 0xFF with d_blob_lo into d_out_lo;
+ * each stream is the same bytes lecb_encode_plane produces.  d_res2: two
+ * lecb_result (hi, lo).  d_ws: lecb_workspace_bytes(n, chunk) (one workspace
+ * covers both streams). */
+int lecb_encode_bf16(const uint16_t* d_in, uint64_t n, const void* d_blob_hi,
+                     const void* d_blob_lo, uint32_t chunk, uint8_t* d_out_hi, uint64_t cap_hi,
+                     uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
+                     uint64_t ws_bytes, void* stream);
+
 /* Per-tensor bf16 encode, the classic three steps ("Single-Stage Huffman
  * Encoder for ML Compression", Overview) on byte planes ("Lossless
  * Compression for LLM Tensor Incremental Snapshots", Technical framework):
  * one-pass plane histograms -> read back (synchronises `stream` once) ->
  * host codebook per plane (no clamp, length limit max_len) -> upload ->
- * encode each plane.  cb_hi / cb_lo (host) receive the codebooks, whose
+ * lecb_encode_bf16.  cb_hi / cb_lo (host) receive the codebooks, whose
  * lengths a container stores.  d_hist: 512 u64 of device scratch (high
  * plane histogram in [0, 256), low plane in [256, 512)).
  * d_res2: two lecb_result (hi, lo).  d_blob_hi/lo: device codebooks.
- * d_ws: lecb_workspace_bytes(n, chunk) (the two planes use it in turn). */
+ * d_ws: lecb_workspace_bytes(n, chunk). */
 int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
                                uint32_t max_len, uint64_t* d_hist, void* d_blob_hi,
                                void* d_blob_lo, lecb_codebook* cb_hi, lecb_codebook* cb_lo,

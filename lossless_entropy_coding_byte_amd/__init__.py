@@ -94,6 +94,7 @@ _SIGNATURES = {
     "lecb_encode": (_int, [_vp, _u64, _vp, _u32, _vp, _u64, _vp, _vp, _u64, _vp]),
     "lecb_decode": (_int, [_vp, _u64, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
     "lecb_encode_plane": (_int, [_vp, _u64, _int, _vp, _u32, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lecb_encode_bf16": (_int, [_vp, _u64, _vp, _vp, _u32, _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
     "lecb_encode_bf16_pertensor": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _vp,
                                           ctypes.POINTER(lecb_codebook), ctypes.POINTER(lecb_codebook),
                                           _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
@@ -274,6 +275,14 @@ def lecb_encode_plane(x, n, plane, blob, chunk, out, res, ws, stream=None) -> No
     _check(load().lecb_encode_plane(_ptr(x), n, plane, _ptr(blob), chunk, _ptr(out), out.numel(),
                                     _ptr(res), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)), "lecb_encode_plane")
+
+
+def lecb_encode_bf16(x, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res2, ws, stream=None) -> None:
+    """Both byte planes of 16-bit words in one pass; res2 holds two results (hi, lo)."""
+    _check(load().lecb_encode_bf16(_ptr(x), n, _ptr(blob_hi), _ptr(blob_lo), chunk, _ptr(out_hi),
+                                   out_hi.numel(), _ptr(out_lo), out_lo.numel(), _ptr(res2),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_encode_bf16")
 
 
 def lecb_decode(stream_buf, stream_bytes, blob, chunk, n, out, res, ws, stream=None) -> None:

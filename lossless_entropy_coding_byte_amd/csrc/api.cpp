@@ -36,8 +36,7 @@ uint64_t header_of(uint64_t n, uint32_t chunk) {
 }
 
 uint64_t ws_bytes_of(uint64_t n, uint32_t chunk) {
-    const uint64_t nc = num_chunks_checked(n, chunk);
-    return (sizeof(WsHeader) + 8 * nc + 255) & ~uint64_t(255);
+    return 2 * ws_stream_bytes(num_chunks_checked(n, chunk));
 }
 
 int build_args(const lecb_codebook* cb, CodebookArgs* a) {
@@ -66,28 +65,43 @@ int build_args(const lecb_codebook* cb, CodebookArgs* a) {
     return LECB_OK;
 }
 
-int encode_common(const void* d_in, int plane, uint64_t n, const void* d_blob, uint32_t chunk,
+int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, uint32_t chunk,
                   uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
-                  uint64_t ws_bytes, void* stream) {
+                  uint64_t ws_bytes, void* stream, const void* d_blob2 = nullptr,
+                  uint8_t* d_out2 = nullptr, uint64_t out_capacity2 = 0) {
+    const bool pair = mode == ENC_PAIR;
     if (!valid_chunk(chunk) || !d_res || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
-    if (n == 0) return launch_result(d_res, 0, 0, LECB_OK, stream);
+    if (pair && (!d_blob2 || !aligned16(d_blob2))) return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        int rc = launch_result(d_res, 0, 0, LECB_OK, stream);
+        return (rc || !pair) ? rc : launch_result(d_res + 1, 0, 0, LECB_OK, stream);
+    }
     if (!d_in || !d_out || !d_ws || !aligned16(d_in) || !aligned16(d_out) || !aligned16(d_ws))
         return LECB_ERR_INVALID_ARG;
+    if (pair && (!d_out2 || !aligned16(d_out2))) return LECB_ERR_INVALID_ARG;
     const uint64_t nc = num_chunks_checked(n, chunk);
     if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
     if (out_capacity < header_of(n, chunk)) return LECB_ERR_CAPACITY;
+    if (pair && out_capacity2 < header_of(n, chunk)) return LECB_ERR_CAPACITY;
     EncodeLaunch L{};
     L.in = d_in;
-    L.plane = plane;
+    L.mode = mode;
     L.n = n;
     L.chunk = chunk;
     L.nc = nc;
-    L.cb = reinterpret_cast<const DeviceCodebook*>(d_blob);
-    L.out = d_out;
-    L.capacity = out_capacity;
-    L.res = d_res;
-    L.ws = reinterpret_cast<WsHeader*>(d_ws);
-    L.grid = (int)std::min<uint64_t>(nc, (uint64_t)device_cu_count() * encode_wgs_per_cu());
+    L.st[0].cb = reinterpret_cast<const DeviceCodebook*>(d_blob);
+    L.st[0].out = d_out;
+    L.st[0].capacity = out_capacity;
+    L.st[0].res = d_res;
+    L.st[0].ws = reinterpret_cast<WsHeader*>(d_ws);
+    if (pair) {
+        L.st[1].cb = reinterpret_cast<const DeviceCodebook*>(d_blob2);
+        L.st[1].out = d_out2;
+        L.st[1].capacity = out_capacity2;
+        L.st[1].res = d_res + 1;
+        L.st[1].ws = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + ws_stream_bytes(nc));
+    }
+    L.grid = device_cu_count() * encode_wgs_per_cu();
     return launch_encode(L, stream);
 }
 
@@ -174,7 +188,7 @@ int lecb_merge_bf16(const uint8_t* d_hi, const uint8_t* d_lo, uint64_t n, uint16
 int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t chunk,
                 uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
                 uint64_t ws_bytes, void* stream) {
-    return encode_common(d_in, -1, n, d_blob, chunk, d_out, out_capacity, d_res, d_ws, ws_bytes,
+    return encode_common(d_in, ENC_BYTES, n, d_blob, chunk, d_out, out_capacity, d_res, d_ws, ws_bytes,
                          stream);
 }
 
@@ -182,8 +196,17 @@ int lecb_encode_plane(const uint16_t* d_in, uint64_t n, int plane, const void* d
                       uint32_t chunk, uint8_t* d_out, uint64_t out_capacity,
                       lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream) {
     if (plane != 0 && plane != 1) return LECB_ERR_INVALID_ARG;
-    return encode_common(d_in, plane, n, d_blob, chunk, d_out, out_capacity, d_res, d_ws,
+    return encode_common(d_in, plane ? ENC_PLANE_HI : ENC_PLANE_LO, n, d_blob, chunk, d_out,
+                         out_capacity, d_res, d_ws,
                          ws_bytes, stream);
+}
+
+int lecb_encode_bf16(const uint16_t* d_in, uint64_t n, const void* d_blob_hi,
+                     const void* d_blob_lo, uint32_t chunk, uint8_t* d_out_hi, uint64_t cap_hi,
+                     uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
+                     uint64_t ws_bytes, void* stream) {
+    return encode_common(d_in, ENC_PAIR, n, d_blob_hi, chunk, d_out_hi, cap_hi, d_res2, d_ws,
+                         ws_bytes, stream, d_blob_lo, d_out_lo, cap_lo);
 }
 
 int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_blob,
@@ -239,11 +262,8 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
     if (!rc) rc = lecb_codebook_upload(cb_hi, d_blob_hi, stream);
     if (!rc) rc = lecb_codebook_upload(cb_lo, d_blob_lo, stream);
     if (!rc)
-        rc = lecb_encode_plane(d_in, n, 1, d_blob_hi, chunk, d_out_hi, cap_hi, d_res2, d_ws,
-                               ws_bytes, stream);
-    if (!rc)
-        rc = lecb_encode_plane(d_in, n, 0, d_blob_lo, chunk, d_out_lo, cap_lo, d_res2 + 1, d_ws,
-                               ws_bytes, stream);
+        rc = lecb_encode_bf16(d_in, n, d_blob_hi, d_blob_lo, chunk, d_out_hi, cap_hi, d_out_lo,
+                              cap_lo, d_res2, d_ws, ws_bytes, stream);
     return rc;
 }
 

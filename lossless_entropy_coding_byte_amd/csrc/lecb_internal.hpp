@@ -38,8 +38,10 @@ struct CodebookArgs {
 };
 
 // ---------------------------------------------------------------- workspace
-// Encode: chunk tickets, look-back flags (epoch-tagged so they never need
+// Encode: ticket counter, look-back flags (epoch-tagged so they never need
 // clearing), exit counter and accumulators.  Decode: exit counter + status.
+// A workspace holds two of them (header + flags each, 256-byte aligned): a
+// two-stream encode uses both; everything else uses the first.
 struct WsHeader {
     uint32_t ticket;
     uint32_t exit_count;
@@ -65,6 +67,8 @@ inline uint64_t table_bytes(uint64_t nc) { return align16(4 * nc); }
 inline uint64_t gap_bytes(uint64_t nc, uint32_t chunk) {
     return align16((nc * units_per_chunk(chunk) + 1) / 2);
 }
+// Bytes of one stream's part of the workspace: header + one flag per chunk.
+inline uint64_t ws_stream_bytes(uint64_t nc) { return (sizeof(WsHeader) + 8 * nc + 255) & ~uint64_t(255); }
 
 // ---------------------------------------------------------------- host helpers
 int build_lengths(const uint64_t freq[256], uint32_t max_len, uint32_t min_freq,
@@ -72,18 +76,26 @@ int build_lengths(const uint64_t freq[256], uint32_t max_len, uint32_t min_freq,
 int canonical_from_lengths(const uint8_t len[256], lecb_codebook* out);
 
 // ---------------------------------------------------------------- launches (kernels_*.hip)
-struct EncodeLaunch {
-    const void* in;          // u8 symbols, or u16 words when plane >= 0
-    int plane;               // -1 = bytes; 0 = low byte of u16; 1 = high byte of u16
-    uint64_t n;
-    uint32_t chunk;
-    uint64_t nc;
+// Input kinds of the encode kernel.  ENC_PAIR codes both bytes of 16-bit
+// words in one pass: stream 0 = high bytes, stream 1 = low bytes.
+enum EncodeMode { ENC_BYTES = 0, ENC_PLANE_LO = 1, ENC_PLANE_HI = 2, ENC_PAIR = 3 };
+
+struct EncodeStream {
     const DeviceCodebook* cb;
     uint8_t* out;            // stream base
     uint64_t capacity;       // bytes
     lecb_result* res;
-    WsHeader* ws;            // followed by nc u64 flags
-    int grid;
+    WsHeader* ws;            // followed by one u64 flag per ticket
+};
+
+struct EncodeLaunch {
+    const void* in;          // u8 symbols (ENC_BYTES) or u16 words
+    int mode;                // EncodeMode
+    uint64_t n;
+    uint32_t chunk;
+    uint64_t nc;
+    EncodeStream st[2];      // st[1] only for ENC_PAIR
+    int grid;                // upper bound on workgroups (persistent grid)
 };
 int launch_encode(const EncodeLaunch& a, void* stream);
 

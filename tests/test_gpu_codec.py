@@ -189,6 +189,41 @@ def test_plane_encode_matches_oracle():
         assert np.array_equal(out[: int(r["bytes"])].cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("n,chunk", [(77, 256), (50_001, 1024), (200_003, 4096), (300_001, 16384),
+                                     (100_000, 32768), ((1 << 20) + 77, 65536)])
+def test_bf16_pair_encode_fixed_codebooks(n, chunk):
+    """Both planes in one pass with codebooks from other data (every byte coded):
+    each stream is bit-exact with the oracle and with the single-plane encode."""
+    _say(f"bf16 pair encode n={n} chunk={chunk}")
+    x = workloads.bf16_weights(n)
+    warm = workloads.bf16_weights(1 << 16)
+    hi_w, lo_w = oracle.split_bf16(warm)
+    hi, lo = oracle.split_bf16(x)
+    ln_hi = oracle.package_merge_lengths(oracle.codebook_frequencies([oracle.histogram(hi_w)], 1), 16)
+    ln_lo = oracle.package_merge_lengths(oracle.codebook_frequencies([oracle.histogram(lo_w)], 1), 16)
+    bh = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln_hi), DEV)
+    bl = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln_lo), DEV)
+    xd = to_dev(x.view(np.int16))
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(2, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    lecb.lecb_encode_bf16(xd, n, bh.blob, bl.blob, chunk, oh, ol, res, ws)
+    r = lecb.results_to_numpy(res)
+    for k, (data, ln, o) in enumerate(((hi, ln_hi, oh), (lo, ln_lo, ol))):
+        ref, bits = oracle.encode(data, ln, oracle.canonical_codes(ln), chunk)
+        assert int(r[k]["status"]) == 0 and int(r[k]["payload_bits"]) == bits
+        assert np.array_equal(o[: int(r[k]["bytes"])].cpu().numpy(), ref)
+    # the single-plane path gives the same bytes
+    one = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    res1 = lecb.new_results(1, DEV)
+    lecb.lecb_encode_plane(xd, n, 0, bl.blob, chunk, one, res1, ws)
+    r1 = lecb.results_to_numpy(res1)[0]
+    assert int(r1["bytes"]) == int(r[1]["bytes"])
+    assert torch.equal(one[: int(r1["bytes"])], ol[: int(r1["bytes"])])
+
+
 @pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), (1 << 20, 65536)])
 def test_bf16_pertensor_pipeline(n, chunk):
     _say(f"bf16 per-tensor n={n} chunk={chunk}")
