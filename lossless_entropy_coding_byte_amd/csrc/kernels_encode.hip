@@ -182,42 +182,65 @@ __device__ inline uint64_t make_flag(uint32_t tag, uint32_t state, uint64_t valu
 // the call gives up with status WORKSPACE instead of waiting forever.
 constexpr uint32_t SPIN_LIMIT = 1u << 24;
 
+constexpr int LB_SLOTS = 4;  // tickets each lane watches per round: 256 per round
+
 // Exclusive prefix (in payload words) of ticket c; run by the 64 lanes of one
-// wave.  Lane l watches ticket end-1-l.  A round is complete once every
-// ticket nearer than the nearest inclusive prefix (state PREFIX) in the
-// window is published; then their values and that prefix are added up.  With
-// no prefix in the window all 64 aggregates are added and the window moves
-// down.  *timed_out is set when SPIN_LIMIT was reached.
+// wave.  A round covers the 256 tickets below `end`: slot i of lane l watches
+// ticket end-1-(64*i+l), so offset 64*i+l counts outwards from the nearest.
+// The round is complete once every ticket nearer than the nearest inclusive
+// prefix (state PREFIX) in it is published; then their values and that prefix
+// are added up.  With no prefix in the round all 256 aggregates are added and
+// the window moves down.  *timed_out is set when SPIN_LIMIT was reached.
 __device__ uint64_t look_back(uint64_t* flags, int64_t c, uint32_t tag, bool* timed_out) {
     const int lane = threadIdx.x & 63;
     uint64_t excl = 0;
     int64_t end = c;
     uint32_t spins = 0;
     while (end > 0) {
-        const int64_t idx = end - 1 - lane;
-        uint64_t f = make_flag(tag, ST_PREFIX, 0);  // before ticket 0: prefix 0
-        bool have = idx < 0;
-        uint64_t pm, vm;
+        uint64_t f[LB_SLOTS];
+        bool have[LB_SLOTS];
+#pragma unroll
+        for (int i = 0; i < LB_SLOTS; ++i) {
+            f[i] = make_flag(tag, ST_PREFIX, 0);  // before ticket 0: prefix 0
+            have[i] = end - 1 - (64 * i + lane) < 0;
+        }
+        int stop;  // offset of the nearest prefix, or 64*LB_SLOTS when none
         for (;;) {
-            if (!have) {
-                f = __hip_atomic_load(&flags[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                have = (uint32_t)(f >> 36) == tag && ((f >> 34) & 3u) != 0;
+#pragma unroll
+            for (int i = 0; i < LB_SLOTS; ++i) {
+                if (!have[i]) {
+                    f[i] = __hip_atomic_load(&flags[end - 1 - (64 * i + lane)], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+                    have[i] = (uint32_t)(f[i] >> 36) == tag && ((f[i] >> 34) & 3u) != 0;
+                }
             }
-            pm = __ballot(have && ((f >> 34) & 3u) == ST_PREFIX);
-            vm = __ballot(have);
-            // lanes up to and including the nearest prefix must be published
-            const uint64_t need = pm ? (pm ^ (pm - 1)) : ~0ull;
-            if ((vm & need) == need) break;
+            // every slot nearer than the nearest prefix (and that prefix) must be published
+            bool ok = true;
+            stop = 64 * LB_SLOTS;
+#pragma unroll
+            for (int i = 0; i < LB_SLOTS; ++i) {
+                if (stop == 64 * LB_SLOTS) {
+                    const uint64_t pm = __ballot(have[i] && ((f[i] >> 34) & 3u) == ST_PREFIX);
+                    const uint64_t vm = __ballot(have[i]);
+                    const uint64_t need = pm ? (pm ^ (pm - 1)) : ~0ull;
+                    ok = ok && (vm & need) == need;
+                    if (pm) stop = 64 * i + (int)__builtin_ctzll(pm);
+                }
+            }
+            if (ok) break;
             if (++spins >= SPIN_LIMIT) {
                 *timed_out = true;
                 return excl;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        const int stop = pm ? (int)__builtin_ctzll(pm) : 64;
-        excl += wave_sum_u64(lane <= stop ? (f & FLAG_VALUE_MASK) : 0ull);
-        if (pm) break;
-        end -= 64;
+        uint64_t part = 0;
+#pragma unroll
+        for (int i = 0; i < LB_SLOTS; ++i)
+            if (64 * i + lane <= stop) part += f[i] & FLAG_VALUE_MASK;
+        excl += wave_sum_u64(part);
+        if (stop < 64 * LB_SLOTS) break;
+        end -= 64 * LB_SLOTS;
     }
     return excl;
 }
@@ -271,32 +294,47 @@ __device__ inline uint64_t count_bits(const Shared& S, const uint32_t w[][16], i
     return packed;
 }
 
-// Pack the thread's 64 code words into the stage at bit `pos` and record the
-// gaps of the unit starts in its chunk-relative bit range [ts, ...).
+// Record the gaps of all unit starts s_j in (prev, p]: their first code-word
+// start at or after them is p.  j/nb: the next unit start and its index.
+__device__ inline void gaps_upto(uint32_t p, uint32_t& j, uint32_t& nb, uint32_t wc, uint32_t K,
+                                 uint32_t log2k, uint8_t* gap) {
+    while (nb <= p) {
+        gap[j] = (uint8_t)(p - nb);
+        ++j;
+        nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
+    }
+}
+
+// Pack the thread's code words into the stage at bit `pos` and record the
+// gaps of the unit starts in its chunk-relative bit range [ts, ...).  FULL:
+// all 64 symbols valid (else the first nv).
+template <bool FULL>
 __device__ inline void pack64(Shared& S, int s, const uint32_t w[16], int nv, uint32_t pos,
                               uint32_t ts, uint32_t wc, uint32_t K, uint32_t log2k, uint8_t* gap) {
     // first unit start at or after ts: s_j = 32*floor(j*wc/K) >= ts
     uint32_t j = wc ? (uint32_t)((((uint64_t)((ts + 31) >> 5)) * K + wc - 1) / wc) : K;
     uint32_t nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
-    uint32_t p = ts;  // chunk-relative start of the current code word
+    uint32_t p = ts;  // chunk-relative start of the next code word
     uint32_t widx = pos >> 5;
     uint32_t used = pos & 31u;
     uint64_t acc = 0;
+    gaps_upto(p, j, nb, wc, K, log2k, gap);  // a unit starting exactly at ts
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
-        const uint32_t e = k < nv ? S.enc[s][sym_of(w, k)] : 0u;
-        if (p >= nb) {  // a unit starts at or before this code word (rare)
-            do {
-                gap[j] = (uint8_t)(p - nb);
-                ++j;
-                nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
-            } while (p >= nb);
-        }
+        const uint32_t e = (FULL || k < nv) ? S.enc[s][sym_of(w, k)] : 0u;
         const uint32_t len = e & 31u;
+        const uint32_t pk = p;  // start of code word k
         p += len;
         used += len;
         acc |= (uint64_t)(e >> 5) << ((64 - used) & 63);  // ends at bit `used` from the top
         if (k & 1) {
+            // unit starts in (start of word k-1, start of word k+1]: checked once
+            // per pair; the one after the start of word k-1 but at or before pk
+            // gets pk, the rest (up to p) get p
+            if (p >= nb) {
+                gaps_upto(pk, j, nb, wc, K, log2k, gap);
+                if (k + 1 < SPT) gaps_upto(p, j, nb, wc, K, log2k, gap);
+            }
             // OR the word being filled (idempotent while it grows), move on once full
             atomicOr(&S.stage[widx], (uint32_t)(acc >> 32));
             const bool full = used >= 32;
@@ -307,7 +345,7 @@ __device__ inline void pack64(Shared& S, int s, const uint32_t w[16], int nv, ui
     }
     if (used) atomicOr(&S.stage[widx], (uint32_t)(acc >> 32));
     // unit starts after the last code word's start but before the range end:
-    // their first boundary is the end of this thread's range
+    // their first boundary is the end of this thread's range (= p)
     while (nb < p) {
         gap[j] = (uint8_t)(p - nb);
         ++j;
@@ -316,7 +354,7 @@ __device__ inline void pack64(Shared& S, int s, const uint32_t w[16], int nv, ui
 }
 
 template <int MODE>
-__global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncArgs a) {
+__global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_kernel(EncArgs a) {
     constexpr int NS = Streams<MODE>::value;
     __shared__ Shared S;
 
@@ -451,11 +489,13 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncArgs a) {
                     TB += seg_bits;
                 }
                 __syncthreads();
-                if (nv > 0 && ch < nch)
-                    pack64(S, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
+                if (nv == SPT && ch < nch)
+                    pack64<true>(S, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
+                else if (nv > 0 && ch < nch)
+                    pack64<false>(S, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
                 if (s == 0 && g == 0 && wave < NS) {
-                    // ---- B (look-back), after the first packing: by now the
-                    // tickets before this one have mostly published prefixes
+                    // ---- B (look-back), after the first packing: by now more of
+                    // the tickets before this one have published prefixes
                     const int sl = wave;
                     const StreamArgs& sa = a.st[sl];
                     const uint32_t tw = S.twords[sl];
