@@ -212,13 +212,11 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
             T.stop("encode")
             r = lecb.results_to_numpy(res)
             T.start("decode")
-            T.start("decode_hi")
-            lecb.lecb_decode(out_hi, int(r[0]["bytes"]), blob_hi, chunk, n, scratch, res_dec[:24], ws)
-            T.stop("decode_hi")
             half = (n + 15) // 16 * 16
-            T.start("decode_lo")
-            lecb.lecb_decode(out_lo, int(r[1]["bytes"]), blob_lo, chunk, n, scratch[half:], res_dec[24:], ws)
-            T.stop("decode_lo")
+            T.start("decode_pair")
+            lecb.lecb_decode_bf16_planes(out_hi, int(r[0]["bytes"]), out_lo, int(r[1]["bytes"]), blob_hi,
+                                         blob_lo, chunk, n, scratch, scratch[half:], res_dec, ws)
+            T.stop("decode_pair")
             T.start("merge")
             lecb.lecb_merge_bf16(scratch[:n], scratch[half:half + n], y)
             T.stop("merge")
@@ -355,8 +353,8 @@ def roofline(cfg, info):
         algo = {
             # the pair encode reads the 16-bit words once and writes both streams
             "encode_pair": 2 * n + s_hi + s_lo,
-            # plane decode reads its stream and writes one byte per element
-            "decode_hi": s_hi + n, "decode_lo": s_lo + n,
+            # the two-plane decode reads both streams and writes one byte per element per plane
+            "decode_pair": s_hi + s_lo + 2 * n,
             "histogram": 2 * n, "merge": 4 * n,
         }
     else:

@@ -255,6 +255,17 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
                                uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
                                uint64_t ws_bytes, void* stream);
 
+/* Decode both byte planes in ONE launch (the two streams' decode units run
+ * side by side) into d_out_hi[n] and d_out_lo[n]; same rules as lecb_decode
+ * for each stream.  d_res2: two lecb_result (hi, lo).  d_ws:
+ * lecb_workspace_bytes(n, chunk).  Reverse path of "Lossless Compression for
+ * LLM Tensor Incremental Snapshots", Technical framework (Huffman-decode of
+ * each byte group). */
+int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
+                            uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
+                            uint32_t chunk, uint64_t n, uint8_t* d_out_hi, uint8_t* d_out_lo,
+                            lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
+
 /* Decode both planes and restore the 16-bit words.  d_scratch: 2*align16(n)
  * bytes of device memory for the decoded planes.  d_ws: lecb_workspace_bytes(n, chunk). */
 int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,

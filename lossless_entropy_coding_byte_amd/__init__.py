@@ -98,6 +98,7 @@ _SIGNATURES = {
     "lecb_encode_bf16_pertensor": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _vp,
                                           ctypes.POINTER(lecb_codebook), ctypes.POINTER(lecb_codebook),
                                           _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lecb_decode_bf16_planes": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
 }
 
@@ -283,6 +284,16 @@ def lecb_encode_bf16(x, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res2, ws, st
                                    out_hi.numel(), _ptr(out_lo), out_lo.numel(), _ptr(res2),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_encode_bf16")
+
+
+def lecb_decode_bf16_planes(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, out_hi, out_lo,
+                            res2, ws, stream=None) -> None:
+    """Both byte planes decoded in one launch into two byte tensors."""
+    _check(load().lecb_decode_bf16_planes(_ptr(hi), hi_bytes, _ptr(lo), lo_bytes, _ptr(blob_hi),
+                                          _ptr(blob_lo), chunk, n, _ptr(out_hi), _ptr(out_lo),
+                                          _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream)),
+           "lecb_decode_bf16_planes")
 
 
 def lecb_decode(stream_buf, stream_bytes, blob, chunk, n, out, res, ws, stream=None) -> None:

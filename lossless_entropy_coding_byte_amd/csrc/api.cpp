@@ -105,6 +105,45 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
     return launch_encode(L, stream);
 }
 
+int decode_common(int ns, const uint8_t* const* d_stream, const uint64_t* stream_bytes,
+                  const void* const* d_blob, uint32_t chunk, uint64_t n, uint8_t* const* d_out,
+                  lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || !d_res) return LECB_ERR_INVALID_ARG;
+    for (int k = 0; k < ns; ++k)
+        if (!d_blob[k] || !aligned16(d_blob[k])) return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        for (int k = 0; k < ns; ++k) {
+            const int rc = launch_result(d_res + k, 0, 0, stream_bytes[k] == 0 ? LECB_OK : LECB_ERR_CORRUPT,
+                                         stream);
+            if (rc) return rc;
+        }
+        return LECB_OK;
+    }
+    if (!d_ws || !aligned16(d_ws)) return LECB_ERR_INVALID_ARG;
+    const uint64_t hb = header_of(n, chunk);
+    for (int k = 0; k < ns; ++k) {
+        if (!d_stream[k] || !d_out[k] || !aligned16(d_stream[k]) || !aligned16(d_out[k]))
+            return LECB_ERR_INVALID_ARG;
+        if (stream_bytes[k] < hb + 4 || (stream_bytes[k] - hb) % 4) return LECB_ERR_CORRUPT;
+    }
+    if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
+    const uint64_t nc = num_chunks_checked(n, chunk);
+    DecodeLaunch L{};
+    L.nstreams = ns;
+    for (int k = 0; k < ns; ++k) {
+        L.stream_base[k] = d_stream[k];
+        L.stream_bytes[k] = stream_bytes[k];
+        L.cb[k] = reinterpret_cast<const DeviceCodebook*>(d_blob[k]);
+        L.out[k] = d_out[k];
+        L.res[k] = d_res + k;
+        L.ws[k] = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + k * ws_stream_bytes(nc));
+    }
+    L.chunk = chunk;
+    L.n = n;
+    L.nc = nc;
+    return launch_decode(L, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,26 +251,22 @@ int lecb_encode_bf16(const uint16_t* d_in, uint64_t n, const void* d_blob_hi,
 int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_blob,
                 uint32_t chunk, uint64_t n, uint8_t* d_out, lecb_result* d_res, void* d_ws,
                 uint64_t ws_bytes, void* stream) {
-    if (!valid_chunk(chunk) || !d_res || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
-    if (n == 0)
-        return launch_result(d_res, 0, 0, stream_bytes == 0 ? LECB_OK : LECB_ERR_CORRUPT, stream);
-    if (!d_stream || !d_out || !d_ws || !aligned16(d_stream) || !aligned16(d_out) ||
-        !aligned16(d_ws))
-        return LECB_ERR_INVALID_ARG;
-    const uint64_t hb = header_of(n, chunk);
-    if (stream_bytes < hb + 4 || (stream_bytes - hb) % 4) return LECB_ERR_CORRUPT;
-    if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
-    DecodeLaunch L{};
-    L.stream_base = d_stream;
-    L.stream_bytes = stream_bytes;
-    L.cb = reinterpret_cast<const DeviceCodebook*>(d_blob);
-    L.chunk = chunk;
-    L.n = n;
-    L.nc = num_chunks_checked(n, chunk);
-    L.out = d_out;
-    L.res = d_res;
-    L.ws = reinterpret_cast<WsHeader*>(d_ws);
-    return launch_decode(L, stream);
+    const uint8_t* st[1] = {d_stream};
+    const uint64_t sb[1] = {stream_bytes};
+    const void* bl[1] = {d_blob};
+    uint8_t* out[1] = {d_out};
+    return decode_common(1, st, sb, bl, chunk, n, out, d_res, d_ws, ws_bytes, stream);
+}
+
+int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
+                            uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
+                            uint32_t chunk, uint64_t n, uint8_t* d_out_hi, uint8_t* d_out_lo,
+                            lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream) {
+    const uint8_t* st[2] = {d_hi, d_lo};
+    const uint64_t sb[2] = {hi_bytes, lo_bytes};
+    const void* bl[2] = {d_blob_hi, d_blob_lo};
+    uint8_t* out[2] = {d_out_hi, d_out_lo};
+    return decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream);
 }
 
 int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
@@ -276,8 +311,8 @@ int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo
         return LECB_ERR_INVALID_ARG;
     uint8_t* hi = d_scratch;
     uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
-    int rc = lecb_decode(d_hi, hi_bytes, d_blob_hi, chunk, n, hi, d_res2, d_ws, ws_bytes, stream);
-    if (!rc) rc = lecb_decode(d_lo, lo_bytes, d_blob_lo, chunk, n, lo, d_res2 + 1, d_ws, ws_bytes, stream);
+    int rc = lecb_decode_bf16_planes(d_hi, hi_bytes, d_lo, lo_bytes, d_blob_hi, d_blob_lo, chunk,
+                                     n, hi, lo, d_res2, d_ws, ws_bytes, stream);
     if (!rc) rc = lecb_merge_bf16(hi, lo, n, d_out, stream);
     return rc;
 }

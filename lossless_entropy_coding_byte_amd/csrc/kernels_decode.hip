@@ -16,12 +16,14 @@
 //   2. exclusive scan of the counts inside each chunk -> output offsets; the
 //      last unit now knows how many code words remain in the last word,
 //      decodes them and checks the zero padding behind them;
-//   3. decode pass: output is written in aligned 16-byte blocks only.  A lane
-//      owns the blocks that START inside its output range; it skips the code
-//      words in front of its first block (the previous lane's last block holds
-//      them) and decodes on past its own end, into the next unit's code words,
-//      to fill its last block.  Blocks never cross a chunk: the output buffer
-//      is 16-byte aligned and a chunk holds a multiple of 256 symbols.
+//   3. decode pass: output is written in whole DEC_BLOCK-byte blocks, aligned
+//      within the chunk's output.  A lane owns the blocks that START inside
+//      its output range; it skips the code words in front of its first block
+//      (the previous lane's last block holds them) and decodes on past its
+//      own end, into the next unit's code words, to fill its last block.
+//      Blocks never cross a chunk (a chunk holds a multiple of 256 symbols),
+//      and with a 32-byte aligned output buffer every store fills whole
+//      32-byte sectors.
 //
 // Bit reader: a window of two payload words and a bit offset into it; before
 // every pair of code words the window slides by one word when its first word
@@ -45,18 +47,15 @@ namespace {
 
 constexpr int DEC_THREADS = 256;
 constexpr uint32_t RING = 16;  // payload words per lane in LDS
+constexpr uint32_t DEC_BLOCK = 32;  // output block a lane owns (bytes)
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-struct DecArgs {
+struct DecStream {
     const uint32_t* table;
     const uint8_t* gaps;
     const uint32_t* payload;
     uint64_t payload_words;   // words present in the caller's buffer
     const DeviceCodebook* cb;
-    uint32_t chunk;
-    uint32_t log2k;
-    uint64_t n;
-    uint64_t nc;
     uint64_t header_bytes;
     uint64_t table_pad_from, table_pad_to;   // stream bytes that must be zero
     uint64_t gap_pad_from, gap_pad_to;
@@ -64,6 +63,16 @@ struct DecArgs {
     uint8_t* out;
     lecb_result* res;
     WsHeader* ws;
+};
+
+struct DecArgs {
+    uint32_t chunk;
+    uint32_t log2k;
+    uint64_t n;
+    uint64_t nc;
+    uint32_t wg_per_stream;   // workgroups of one stream; stream = blockIdx.x / wg_per_stream
+    uint32_t nstreams;
+    DecStream st[2];
 };
 
 struct Tables {
@@ -201,23 +210,26 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
     Tables& T = S.T;
 
     const int tid = threadIdx.x;
+    const uint32_t sidx = blockIdx.x / a.wg_per_stream;
+    const uint32_t bid = blockIdx.x - sidx * a.wg_per_stream;
+    const DecStream& d = a.st[sidx];
     {
-        const v4u* src = reinterpret_cast<const v4u*>(a.cb->lut);
+        const v4u* src = reinterpret_cast<const v4u*>(d.cb->lut);
         v4u* dst = reinterpret_cast<v4u*>(T.lut);
         constexpr int NV = LUT_SIZE * 2 / 16;
         for (int i = tid; i < NV; i += DEC_THREADS) dst[i] = src[i];
     }
-    if (tid < 17) T.off[tid] = a.cb->base[tid] - a.cb->first[tid];
-    T.sorted[tid] = a.cb->sorted[tid];
+    if (tid < 17) T.off[tid] = d.cb->base[tid] - d.cb->first[tid];
+    T.sorted[tid] = d.cb->sorted[tid];
     Limits L;
-    L.l13 = a.cb->limit[13];
-    L.l14 = a.cb->limit[14];
-    L.l15 = a.cb->limit[15];
-    L.l16 = a.cb->limit[16];
+    L.l13 = d.cb->limit[13];
+    L.l14 = d.cb->limit[14];
+    L.l15 = d.cb->limit[15];
+    L.l16 = d.cb->limit[16];
 
     // ---- unit geometry
     const uint32_t K = 1u << a.log2k;
-    const uint64_t u = (uint64_t)blockIdx.x * DEC_THREADS + tid;
+    const uint64_t u = (uint64_t)bid * DEC_THREADS + tid;
     const uint64_t c = u >> a.log2k;
     const uint32_t j = (uint32_t)(u & (K - 1));
     const bool active = c < a.nc;
@@ -226,18 +238,18 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
     uint64_t sw = 0, wc = 0;
     uint32_t start_bit = 0, end_bit = 0, sj1 = 0, m_c = 0;
     if (active) {
-        sw = c ? a.table[c - 1] : 0;
-        const uint64_t ew = a.table[c];
-        if (ew <= sw || ew > a.payload_words || ew - sw > a.chunk / 2) bad = true;
+        sw = c ? d.table[c - 1] : 0;
+        const uint64_t ew = d.table[c];
+        if (ew <= sw || ew > d.payload_words || ew - sw > a.chunk / 2) bad = true;
         wc = bad ? 0 : ew - sw;
         m_c = (uint32_t)min<uint64_t>(a.chunk, a.n - c * a.chunk);
         const uint32_t sj = (uint32_t)(((uint64_t)j * wc) >> a.log2k) << 5;
-        const uint32_t gj = gap_of(a.gaps, u);
+        const uint32_t gj = gap_of(d.gaps, u);
         if (j == 0 && gj != 0) bad = true;
         start_bit = sj + gj;
         if (!last) {
             sj1 = (uint32_t)(((uint64_t)(j + 1) * wc) >> a.log2k) << 5;
-            end_bit = sj1 + gap_of(a.gaps, u + 1);
+            end_bit = sj1 + gap_of(d.gaps, u + 1);
             if (start_bit > end_bit) bad = true;
         } else {
             end_bit = wc ? (uint32_t)((wc - 1) << 5) : 0u;  // start of the last word
@@ -246,9 +258,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
 
     Reader r;
     r.ring = &S.ring[0][tid];
-    r.p = a.payload;
+    r.p = d.payload;
     r.sw = sw;
-    r.gmax = a.payload_words ? (a.payload_words - 1) >> 2 : 0;
+    r.gmax = d.payload_words ? (d.payload_words - 1) >> 2 : 0;
     r.sh = (uint32_t)sw & (RING - 1);
     const bool run = active && !bad;
 
@@ -332,21 +344,23 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
     }
 
     // padding bytes of the header are part of the format
-    if (blockIdx.x == 0) {
-        for (uint64_t b = a.table_pad_from + tid; b < a.table_pad_to; b += DEC_THREADS)
-            bad |= a.stream[b] != 0;
-        for (uint64_t b = a.gap_pad_from + tid; b < a.gap_pad_to; b += DEC_THREADS)
-            bad |= a.stream[b] != 0;
+    if (bid == 0) {
+        for (uint64_t b = d.table_pad_from + tid; b < d.table_pad_to; b += DEC_THREADS)
+            bad |= d.stream[b] != 0;
+        for (uint64_t b = d.gap_pad_from + tid; b < d.gap_pad_to; b += DEC_THREADS)
+            bad |= d.stream[b] != 0;
         if (tid == 0 && ((a.nc << a.log2k) & 1))
-            bad |= (a.stream[a.gap_pad_from - 1] >> 4) != 0;
+            bad |= (d.stream[d.gap_pad_from - 1] >> 4) != 0;
     }
     const int wg_bad = __syncthreads_or(bad);
 
-    // ---- 3. decode pass: the aligned 16-byte blocks that start in this lane's range
+    // ---- 3. decode pass: the DEC_BLOCK-byte blocks (aligned within the chunk's
+    // output) that start in this lane's range; each goes out as whole 16-byte
+    // stores, so every written sector of the output is written completely
     if (run && !wg_bad) {
-        uint8_t* const base = a.out + c * a.chunk + out_off;
-        const uint32_t h = (16u - (uint32_t)((uintptr_t)base & 15u)) & 15u;
-        const uint32_t nblk = cnt > h ? (cnt - h + 15u) >> 4 : 0u;
+        uint8_t* const base = d.out + c * a.chunk + out_off;
+        const uint32_t h = (DEC_BLOCK - (out_off & (DEC_BLOCK - 1))) & (DEC_BLOCK - 1);
+        const uint32_t nblk = cnt > h ? (cnt - h + DEC_BLOCK - 1) / DEC_BLOCK : 0u;
         if (nblk) {
             r.start(start_bit);
             uint32_t inval = 0;  // cannot be set: the count pass read the same bits
@@ -356,12 +370,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
                 (void)step(T, L, r, inval);
             }
             uint8_t* dst = base + h;
-            const uint32_t full = min(nblk, (m_c - out_off - h) >> 4);  // blocks before the tensor end
+            // blocks before the tensor end
+            const uint32_t full = min(nblk, (m_c - out_off - h) / DEC_BLOCK);
             uint32_t b = 0;
             for (; b < full; ++b) {
-                uint32_t w[4];
+                uint32_t w[DEC_BLOCK / 4];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < DEC_BLOCK / 2; ++q) {
                     if ((q & 3) == 0) r.tick();
                     r.refill();
 #pragma unroll
@@ -373,21 +388,24 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
                         else w[i >> 2] |= sym << (8 * (i & 3));
                     }
                 }
-                v4u v;
-                v.x = w[0];
-                v.y = w[1];
-                v.z = w[2];
-                v.w = w[3];
-                *reinterpret_cast<v4u*>(dst + 16 * b) = v;
+#pragma unroll
+                for (int q = 0; q < DEC_BLOCK / 16; ++q) {
+                    v4u v;
+                    v.x = w[4 * q];
+                    v.y = w[4 * q + 1];
+                    v.z = w[4 * q + 2];
+                    v.w = w[4 * q + 3];
+                    *reinterpret_cast<v4u*>(dst + DEC_BLOCK * b + 16 * q) = v;
+                }
             }
             if (b < nblk) {
                 // the tensor ends inside this block: byte stores up to its end
-                const uint32_t left = m_c - out_off - h - 16 * b;
+                const uint32_t left = m_c - out_off - h - DEC_BLOCK * b;
                 for (uint32_t i = 0; i < left; ++i) {
                     if ((i & 3) == 0) r.tick();
                     r.refill();
                     const uint32_t e = step(T, L, r, inval);
-                    dst[16 * b + i] = (uint8_t)(e >> 8);
+                    dst[DEC_BLOCK * b + i] = (uint8_t)(e >> 8);
                 }
             }
         }
@@ -403,23 +421,27 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
     if (tid == 0) {
         uint64_t tot = 0;
         for (int w = 0; w < DEC_THREADS / 64; ++w) tot += S.red[w];
-        if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(&a.ws->bits), (unsigned long long)tot);
-        if (any_bad) atomicCAS(&a.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
+        if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(&d.ws->bits), (unsigned long long)tot);
+        if (any_bad) atomicCAS(&d.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
         __threadfence();
-        const uint32_t done = __hip_atomic_fetch_add(&a.ws->exit_count, 1u, __ATOMIC_ACQ_REL,
+        WsHeader* ws0 = a.st[0].ws;
+        const uint32_t done = __hip_atomic_fetch_add(&ws0->exit_count, 1u, __ATOMIC_ACQ_REL,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
-            const uint64_t bits = __hip_atomic_load(&a.ws->bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int32_t st = __hip_atomic_load(&a.ws->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t W = a.table[a.nc - 1];
-            a.res->bytes = a.header_bytes + 4 * W;
-            a.res->payload_bits = bits;
-            a.res->status = (st == 0 && W != a.payload_words) ? (int32_t)LECB_ERR_CORRUPT : st;
-            a.res->reserved = 0;
-            a.ws->bits = 0;
-            a.ws->status = 0;
+            for (uint32_t k = 0; k < a.nstreams; ++k) {
+                const DecStream& e = a.st[k];
+                const uint64_t bits = __hip_atomic_load(&e.ws->bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int32_t st = __hip_atomic_load(&e.ws->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t W = e.table[a.nc - 1];
+                e.res->bytes = e.header_bytes + 4 * W;
+                e.res->payload_bits = bits;
+                e.res->status = (st == 0 && W != e.payload_words) ? (int32_t)LECB_ERR_CORRUPT : st;
+                e.res->reserved = 0;
+                e.ws->bits = 0;
+                e.ws->status = 0;
+            }
             __threadfence();
-            __hip_atomic_store(&a.ws->exit_count, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ws0->exit_count, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -429,28 +451,32 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
 int launch_decode(const DecodeLaunch& L, void* stream) {
     DecArgs a{};
     const uint64_t tb = table_bytes(L.nc), gb = gap_bytes(L.nc, L.chunk);
-    a.table = reinterpret_cast<const uint32_t*>(L.stream_base);
-    a.gaps = L.stream_base + tb;
-    a.payload = reinterpret_cast<const uint32_t*>(L.stream_base + tb + gb);
-    a.payload_words = (L.stream_bytes - tb - gb) / 4;
-    a.cb = L.cb;
-    a.chunk = L.chunk;
     const uint32_t K = units_per_chunk(L.chunk);
+    a.chunk = L.chunk;
     a.log2k = (uint32_t)ilog2(K);
     a.n = L.n;
     a.nc = L.nc;
-    a.header_bytes = tb + gb;
-    a.stream = L.stream_base;
-    a.table_pad_from = 4 * L.nc;
-    a.table_pad_to = tb;
-    a.gap_pad_from = tb + (L.nc * K + 1) / 2;
-    a.gap_pad_to = tb + gb;
-    a.out = L.out;
-    a.res = L.res;
-    a.ws = L.ws;
-
+    a.nstreams = L.nstreams;
+    for (int s = 0; s < L.nstreams; ++s) {
+        DecStream& st = a.st[s];
+        st.table = reinterpret_cast<const uint32_t*>(L.stream_base[s]);
+        st.gaps = L.stream_base[s] + tb;
+        st.payload = reinterpret_cast<const uint32_t*>(L.stream_base[s] + tb + gb);
+        st.payload_words = (L.stream_bytes[s] - tb - gb) / 4;
+        st.cb = L.cb[s];
+        st.header_bytes = tb + gb;
+        st.stream = L.stream_base[s];
+        st.table_pad_from = 4 * L.nc;
+        st.table_pad_to = tb;
+        st.gap_pad_from = tb + (L.nc * K + 1) / 2;
+        st.gap_pad_to = tb + gb;
+        st.out = L.out[s];
+        st.res = L.res[s];
+        st.ws = L.ws[s];
+    }
     const uint64_t units = L.nc * K;
-    const uint64_t grid = (units + DEC_THREADS - 1) / DEC_THREADS;
+    a.wg_per_stream = (uint32_t)((units + DEC_THREADS - 1) / DEC_THREADS);
+    const uint64_t grid = (uint64_t)a.wg_per_stream * L.nstreams;
     hipLaunchKernelGGL(decode_kernel, dim3((uint32_t)grid), dim3(DEC_THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;

@@ -99,16 +99,19 @@ struct EncodeLaunch {
 };
 int launch_encode(const EncodeLaunch& a, void* stream);
 
+// One or two streams of the same n and chunk decoded in one launch (the two
+// byte planes of 16-bit words); stream k uses workspace part ws[k].
 struct DecodeLaunch {
-    const uint8_t* stream_base;
-    uint64_t stream_bytes;
-    const DeviceCodebook* cb;
+    int nstreams;
+    const uint8_t* stream_base[2];
+    uint64_t stream_bytes[2];
+    const DeviceCodebook* cb[2];
+    uint8_t* out[2];
+    lecb_result* res[2];
+    WsHeader* ws[2];
     uint32_t chunk;
     uint64_t n;
     uint64_t nc;
-    uint8_t* out;
-    lecb_result* res;
-    WsHeader* ws;
 };
 int launch_decode(const DecodeLaunch& a, void* stream);
 

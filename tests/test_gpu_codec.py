@@ -224,6 +224,49 @@ def test_bf16_pair_encode_fixed_codebooks(n, chunk):
     assert torch.equal(one[: int(r1["bytes"])], ol[: int(r1["bytes"])])
 
 
+@pytest.mark.parametrize("n,chunk", [(77, 256), (200_003, 4096), ((1 << 20) + 77, 65536)])
+def test_bf16_two_plane_decode(n, chunk):
+    """One launch decodes both planes; each plane equals the oracle's, and a
+    corrupt low stream is reported in the low result only."""
+    _say(f"bf16 two-plane decode n={n} chunk={chunk}")
+    x = workloads.bf16_weights(n)
+    enc = oracle.encode_bf16(x, chunk)
+    hi, lo = oracle.split_bf16(x)
+    bh = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_hi"]), DEV)
+    bl = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_lo"]), DEV)
+
+    def dev_stream(a):
+        buf = torch.zeros((a.size + 15) // 16 * 16 + 16, dtype=torch.uint8, device=DEV)
+        buf[: a.size] = to_dev(a)
+        return buf
+
+    sh, sl = dev_stream(enc["stream_hi"]), dev_stream(enc["stream_lo"])
+    oh = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=DEV)
+    ol = torch.empty_like(oh)
+    res = lecb.new_results(2, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    lecb.lecb_decode_bf16_planes(sh, enc["stream_hi"].size, sl, enc["stream_lo"].size, bh.blob, bl.blob,
+                                 chunk, n, oh, ol, res, ws)
+    r = lecb.results_to_numpy(res)
+    assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
+    assert np.array_equal(oh[:n].cpu().numpy(), hi) and np.array_equal(ol[:n].cpu().numpy(), lo)
+    bad = enc["stream_lo"].copy()
+    bad[-1] ^= 0x01  # last payload word: a padding bit or a code bit changes
+    sl2 = dev_stream(bad)
+    lecb.lecb_decode_bf16_planes(sh, enc["stream_hi"].size, sl2, bad.size, bh.blob, bl.blob,
+                                 chunk, n, oh, ol, res, ws)
+    r = lecb.results_to_numpy(res)
+    assert int(r[0]["status"]) == 0
+    try:
+        oracle.decode(bad, enc["len_lo"], chunk, n)
+        lo_ok = True
+    except oracle.CorruptStream:
+        lo_ok = False
+    assert (int(r[1]["status"]) == 0) == lo_ok
+    if lo_ok:
+        assert np.array_equal(ol[:n].cpu().numpy(), oracle.decode(bad, enc["len_lo"], chunk, n))
+
+
 @pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), (1 << 20, 65536)])
 def test_bf16_pertensor_pipeline(n, chunk):
     _say(f"bf16 per-tensor n={n} chunk={chunk}")
