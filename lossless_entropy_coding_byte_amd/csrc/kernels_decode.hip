@@ -77,6 +77,7 @@ struct DecArgs {
 
 struct Tables {
     uint16_t lut[LUT_SIZE];   // (sym << 8) | len
+    uint8_t mlut[LUT_SIZE];   // (count << 4) | bits of the whole code words in the next LUT_BITS
     uint32_t off[17];         // base[l] - first[l]: index in `sorted` is off[l] + code
     uint8_t sorted[256];
 };
@@ -218,6 +219,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
         v4u* dst = reinterpret_cast<v4u*>(T.lut);
         constexpr int NV = LUT_SIZE * 2 / 16;
         for (int i = tid; i < NV; i += DEC_THREADS) dst[i] = src[i];
+        const v4u* msrc = reinterpret_cast<const v4u*>(d.cb->mlut);
+        v4u* mdst = reinterpret_cast<v4u*>(T.mlut);
+        for (int i = tid; i < LUT_SIZE / 16; i += DEC_THREADS) mdst[i] = msrc[i];
     }
     if (tid < 17) T.off[tid] = d.cb->base[tid] - d.cb->first[tid];
     T.sorted[tid] = d.cb->sorted[tid];
@@ -274,6 +278,30 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
         // pos() < end_bit  <=>  off < thr = endq - 32 * rq
         const int32_t endq = (int32_t)(end_bit + 32 * (r.sh + 2));
         int32_t thr = endq - (int32_t)(r.rq << 5);
+        // (a) far from the end: all code words that lie wholly inside the next
+        // LUT_BITS bits at once, two such steps per refill; a step whose first
+        // code word is longer decodes that one alone.  It stops while at least
+        // 16 bits are left, so the last code word before `end` is decoded by
+        // (b) and its length is known for the gap check.
+        for (uint32_t it = 0; (int32_t)r.off + 2 * 16 + 16 <= thr; ++it) {
+            if ((it & 3) == 0) r.tick();
+            r.refill();
+            thr = endq - (int32_t)(r.rq << 5);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t top = r.peek();
+                const uint32_t m = T.mlut[top >> (32 - LUT_BITS)];
+                if (m >= 16) {
+                    r.off += m & 15u;
+                    cnt += m >> 4;
+                } else {
+                    e = lookup(T, L, top, inval);
+                    r.off += e & 0xFFu;
+                    ++cnt;
+                }
+            }
+        }
+        // (b) the rest, one code word at a time, stopping exactly at `end`
         while ((int32_t)r.off < thr) {
             r.tick();
 #pragma unroll

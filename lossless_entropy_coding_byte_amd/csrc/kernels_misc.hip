@@ -197,6 +197,22 @@ __global__ __launch_bounds__(256) void codebook_kernel(CodebookArgs a, DeviceCod
             }
         }
         cb->lut[t] = entry;
+        // how many code words follow one another wholly inside these bits
+        uint32_t used = 0, cnt = 0;
+        for (;;) {
+            uint32_t len = 0;
+            for (uint32_t l = 1; l + used <= (uint32_t)LUT_BITS; ++l) {
+                const uint32_t v = ((uint32_t)t >> (LUT_BITS - used - l)) & ((1u << l) - 1u);
+                if (a.count[l] && v >= a.first[l] && v < a.first[l] + a.count[l]) {
+                    len = l;
+                    break;
+                }
+            }
+            if (!len) break;
+            used += len;
+            ++cnt;
+        }
+        cb->mlut[t] = (uint8_t)((cnt << 4) | used);
     }
 }
 

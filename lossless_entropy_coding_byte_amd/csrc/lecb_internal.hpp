@@ -20,6 +20,8 @@ struct DeviceCodebook {
     uint32_t first[17];       // first canonical code of length l
     uint32_t base[17];        // index in `sorted` of the first symbol of length l
     uint8_t sorted[256];      // coded symbols by (length, byte value)
+    uint8_t mlut[LUT_SIZE];   // next LUT_BITS bits -> (count << 4) | bits: the code words that lie
+                              // wholly inside them, greedily from the top; 0 when the first is longer
     uint32_t max_len;
     uint32_t num_coded;
     uint32_t pad[3];
