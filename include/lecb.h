@@ -218,6 +218,14 @@ int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_bl
                 uint32_t chunk, uint64_t n, uint8_t* d_out, lecb_result* d_res, void* d_ws,
                 uint64_t ws_bytes, void* stream);
 
+/* lecb_decode with the stream's size taken on the device from the result an
+ * encode wrote (d_enc_res->bytes), so an encode -> decode chain needs no host
+ * synchronisation.  An encoder status other than LECB_OK, or a size that
+ * lecb_decode would refuse, gives status CORRUPT in *d_res. */
+int lecb_decode_from_result(const uint8_t* d_stream, const lecb_result* d_enc_res,
+                            const void* d_blob, uint32_t chunk, uint64_t n, uint8_t* d_out,
+                            lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream);
+
 /* Encode one byte plane of 16-bit words without materialising it:
  * plane 1 = high bytes (in >> 8), plane 0 = low bytes (in & 0xFF). */
 int lecb_encode_plane(const uint16_t* d_in, uint64_t n, int plane, const void* d_blob,
@@ -265,6 +273,16 @@ int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_
                             uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
                             uint32_t chunk, uint64_t n, uint8_t* d_out_hi, uint8_t* d_out_lo,
                             lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* lecb_decode_bf16 with both streams' sizes taken on the device from the
+ * two results an encode wrote (d_enc_res2, hi then lo), so a per-tensor
+ * encode -> decode chain needs no host synchronisation; errors as in
+ * lecb_decode_from_result. */
+int lecb_decode_bf16_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
+                                  const lecb_result* d_enc_res2, const void* d_blob_hi,
+                                  const void* d_blob_lo, uint32_t chunk, uint64_t n,
+                                  uint16_t* d_out, uint8_t* d_scratch, lecb_result* d_res2,
+                                  void* d_ws, uint64_t ws_bytes, void* stream);
 
 /* Decode both planes and restore the 16-bit words.  d_scratch: 2*align16(n)
  * bytes of device memory for the decoded planes.  d_ws: lecb_workspace_bytes(n, chunk). */

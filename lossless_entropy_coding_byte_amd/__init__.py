@@ -98,6 +98,8 @@ _SIGNATURES = {
     "lecb_encode_bf16_pertensor": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _vp,
                                           ctypes.POINTER(lecb_codebook), ctypes.POINTER(lecb_codebook),
                                           _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lecb_decode_from_result": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_bf16_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16_planes": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
 }
@@ -284,6 +286,24 @@ def lecb_encode_bf16(x, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res2, ws, st
                                    out_hi.numel(), _ptr(out_lo), out_lo.numel(), _ptr(res2),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_encode_bf16")
+
+
+def lecb_decode_from_result(stream_buf, enc_res, blob, chunk, n, out, res, ws, stream=None) -> None:
+    """Decode with the stream size read on the device from the encoder's result."""
+    _check(load().lecb_decode_from_result(_ptr(stream_buf), _ptr(enc_res), _ptr(blob), chunk, n,
+                                          _ptr(out), _ptr(res), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_decode_from_result")
+
+
+def lecb_decode_bf16_from_results(hi, lo, enc_res2, blob_hi, blob_lo, chunk, n, out, scratch, res2, ws,
+                                  stream=None) -> None:
+    """Both planes decoded and merged, sizes read on the device from the encoder's results."""
+    _check(load().lecb_decode_bf16_from_results(_ptr(hi), _ptr(lo), _ptr(enc_res2), _ptr(blob_hi),
+                                                _ptr(blob_lo), chunk, n, _ptr(out), _ptr(scratch),
+                                                _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
+                                                _stream(stream)),
+           "lecb_decode_bf16_from_results")
 
 
 def lecb_decode_bf16_planes(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, out_hi, out_lo,

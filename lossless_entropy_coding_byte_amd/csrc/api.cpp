@@ -107,13 +107,16 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
 
 int decode_common(int ns, const uint8_t* const* d_stream, const uint64_t* stream_bytes,
                   const void* const* d_blob, uint32_t chunk, uint64_t n, uint8_t* const* d_out,
-                  lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream) {
+                  lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream,
+                  const lecb_result* d_sizes = nullptr) {
     if (!valid_chunk(chunk) || !d_res) return LECB_ERR_INVALID_ARG;
     for (int k = 0; k < ns; ++k)
         if (!d_blob[k] || !aligned16(d_blob[k])) return LECB_ERR_INVALID_ARG;
     if (n == 0) {
         for (int k = 0; k < ns; ++k) {
-            const int rc = launch_result(d_res + k, 0, 0, stream_bytes[k] == 0 ? LECB_OK : LECB_ERR_CORRUPT,
+            // (with device-side sizes the encoder of 0 symbols wrote an empty result)
+            const int rc = launch_result(d_res + k, 0, 0,
+                                         d_sizes || stream_bytes[k] == 0 ? LECB_OK : LECB_ERR_CORRUPT,
                                          stream);
             if (rc) return rc;
         }
@@ -124,15 +127,17 @@ int decode_common(int ns, const uint8_t* const* d_stream, const uint64_t* stream
     for (int k = 0; k < ns; ++k) {
         if (!d_stream[k] || !d_out[k] || !aligned16(d_stream[k]) || !aligned16(d_out[k]))
             return LECB_ERR_INVALID_ARG;
-        if (stream_bytes[k] < hb + 4 || (stream_bytes[k] - hb) % 4) return LECB_ERR_CORRUPT;
+        if (!d_sizes && (stream_bytes[k] < hb + 4 || (stream_bytes[k] - hb) % 4)) return LECB_ERR_CORRUPT;
     }
     if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
     const uint64_t nc = num_chunks_checked(n, chunk);
+    if (d_sizes && !aligned16(d_sizes)) return LECB_ERR_INVALID_ARG;
     DecodeLaunch L{};
     L.nstreams = ns;
+    L.dev_sizes = d_sizes;
     for (int k = 0; k < ns; ++k) {
         L.stream_base[k] = d_stream[k];
-        L.stream_bytes[k] = stream_bytes[k];
+        L.stream_bytes[k] = d_sizes ? 0 : stream_bytes[k];
         L.cb[k] = reinterpret_cast<const DeviceCodebook*>(d_blob[k]);
         L.out[k] = d_out[k];
         L.res[k] = d_res + k;
@@ -256,6 +261,36 @@ int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_bl
     const void* bl[1] = {d_blob};
     uint8_t* out[1] = {d_out};
     return decode_common(1, st, sb, bl, chunk, n, out, d_res, d_ws, ws_bytes, stream);
+}
+
+int lecb_decode_from_result(const uint8_t* d_stream, const lecb_result* d_enc_res,
+                            const void* d_blob, uint32_t chunk, uint64_t n, uint8_t* d_out,
+                            lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!d_enc_res) return LECB_ERR_INVALID_ARG;
+    const uint8_t* st[1] = {d_stream};
+    const uint64_t sb[1] = {0};
+    const void* bl[1] = {d_blob};
+    uint8_t* out[1] = {d_out};
+    return decode_common(1, st, sb, bl, chunk, n, out, d_res, d_ws, ws_bytes, stream, d_enc_res);
+}
+
+int lecb_decode_bf16_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
+                                  const lecb_result* d_enc_res2, const void* d_blob_hi,
+                                  const void* d_blob_lo, uint32_t chunk, uint64_t n,
+                                  uint16_t* d_out, uint8_t* d_scratch, lecb_result* d_res2,
+                                  void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!d_res2 || !d_enc_res2) return LECB_ERR_INVALID_ARG;
+    if (n && (!d_scratch || !aligned16(d_scratch) || !d_out || !aligned16(d_out)))
+        return LECB_ERR_INVALID_ARG;
+    uint8_t* hi = d_scratch;
+    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
+    const uint8_t* st[2] = {d_hi, d_lo};
+    const uint64_t sb[2] = {0, 0};
+    const void* bl[2] = {d_blob_hi, d_blob_lo};
+    uint8_t* out[2] = {hi, lo};
+    int rc = decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream, d_enc_res2);
+    if (!rc) rc = lecb_merge_bf16(hi, lo, n, d_out, stream);
+    return rc;
 }
 
 int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,

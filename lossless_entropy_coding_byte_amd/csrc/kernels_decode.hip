@@ -66,6 +66,7 @@ struct DecStream {
 };
 
 struct DecArgs {
+    const lecb_result* sizes;  // non-null: stream k's size is sizes[k].bytes (an encoder's result)
     uint32_t chunk;
     uint32_t log2k;
     uint64_t n;
@@ -213,7 +214,16 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
     const int tid = threadIdx.x;
     const uint32_t sidx = blockIdx.x / a.wg_per_stream;
     const uint32_t bid = blockIdx.x - sidx * a.wg_per_stream;
-    const DecStream& d = a.st[sidx];
+    const DecStream& d0 = a.st[sidx];
+    DecStream d = d0;
+    bool size_bad = false;
+    if (a.sizes) {
+        // the stream's size comes from the encoder's result on the device
+        const uint64_t bytes = a.sizes[sidx].bytes;
+        size_bad = a.sizes[sidx].status != 0 || bytes < d.header_bytes + 4 ||
+                   ((bytes - d.header_bytes) & 3) != 0;
+        d.payload_words = size_bad ? 0 : (bytes - d.header_bytes) / 4;
+    }
     {
         const v4u* src = reinterpret_cast<const v4u*>(d.cb->lut);
         v4u* dst = reinterpret_cast<v4u*>(T.lut);
@@ -236,9 +246,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
     const uint64_t u = (uint64_t)bid * DEC_THREADS + tid;
     const uint64_t c = u >> a.log2k;
     const uint32_t j = (uint32_t)(u & (K - 1));
-    const bool active = c < a.nc;
+    const bool active = c < a.nc && !size_bad;
     const bool last = j == K - 1;
-    bool bad = false;
+    bool bad = size_bad;
     uint64_t sw = 0, wc = 0;
     uint32_t start_bit = 0, end_bit = 0, sj1 = 0, m_c = 0;
     if (active) {
@@ -457,7 +467,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             for (uint32_t k = 0; k < a.nstreams; ++k) {
-                const DecStream& e = a.st[k];
+                DecStream e = a.st[k];
+                if (a.sizes) {
+                    const uint64_t bytes = a.sizes[k].bytes;
+                    e.payload_words = bytes >= e.header_bytes ? (bytes - e.header_bytes) / 4 : 0;
+                }
                 const uint64_t bits = __hip_atomic_load(&e.ws->bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const int32_t st = __hip_atomic_load(&e.ws->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const uint64_t W = e.table[a.nc - 1];
@@ -485,12 +499,13 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
     a.n = L.n;
     a.nc = L.nc;
     a.nstreams = L.nstreams;
+    a.sizes = L.dev_sizes;
     for (int s = 0; s < L.nstreams; ++s) {
         DecStream& st = a.st[s];
         st.table = reinterpret_cast<const uint32_t*>(L.stream_base[s]);
         st.gaps = L.stream_base[s] + tb;
         st.payload = reinterpret_cast<const uint32_t*>(L.stream_base[s] + tb + gb);
-        st.payload_words = (L.stream_bytes[s] - tb - gb) / 4;
+        st.payload_words = L.dev_sizes ? 0 : (L.stream_bytes[s] - tb - gb) / 4;
         st.cb = L.cb[s];
         st.header_bytes = tb + gb;
         st.stream = L.stream_base[s];

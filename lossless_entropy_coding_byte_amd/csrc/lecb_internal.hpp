@@ -105,6 +105,7 @@ int launch_encode(const EncodeLaunch& a, void* stream);
 // byte planes of 16-bit words); stream k uses workspace part ws[k].
 struct DecodeLaunch {
     int nstreams;
+    const lecb_result* dev_sizes;   // non-null: stream sizes are read on the device from these
     const uint8_t* stream_base[2];
     uint64_t stream_bytes[2];
     const DeviceCodebook* cb[2];

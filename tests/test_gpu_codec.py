@@ -295,6 +295,64 @@ def test_bf16_pertensor_pipeline(n, chunk):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
 
 
+# ----------------------------------------------------------------------------- sizes on the device
+
+@pytest.mark.parametrize("n,chunk", [(1, 256), (100_003, 4096), (1 << 20, 65536)])
+def test_decode_from_encoder_result(n, chunk):
+    """Encode then decode with the size read on the device: no host round trip."""
+    _say(f"decode from result n={n} chunk={chunk}")
+    x = workloads.skewed_bytes(5, n)
+    ln = codebook_for(x, True)
+    dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+    xd = to_dev(x)
+    out, res = lecb.encode_bytes(xd, dcb, chunk)
+    y = torch.empty(max(16, n), dtype=torch.uint8, device=DEV)
+    rd = lecb.new_results(1, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    lecb.lecb_decode_from_result(out, res, dcb.blob, chunk, n, y, rd, ws)
+    r, q = lecb.results_to_numpy(res)[0], lecb.results_to_numpy(rd)[0]
+    assert int(q["status"]) == 0 and int(q["bytes"]) == int(r["bytes"])
+    assert int(q["payload_bits"]) == int(r["payload_bits"])
+    assert np.array_equal(y[:n].cpu().numpy(), x)
+
+
+def test_decode_from_failed_encode_is_corrupt():
+    """A failed encode leaves a result the decoder refuses, without a host check."""
+    x = _gauss(18, 50_000, 3.0)
+    ln = codebook_for(x, False)
+    x[25_000] = np.uint8(np.flatnonzero(ln == 0)[0])  # a byte value with no code word
+    dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+    out, res = lecb.encode_bytes(to_dev(x), dcb, 4096)
+    assert int(lecb.results_to_numpy(res)[0]["status"]) == lecb.LECB_ERR_UNCODED_SYMBOL
+    y = torch.empty(x.size, dtype=torch.uint8, device=DEV)
+    rd = lecb.new_results(1, DEV)
+    ws = lecb.new_workspace(x.size, 4096, DEV)
+    lecb.lecb_decode_from_result(out, res, dcb.blob, 4096, x.size, y, rd, ws)
+    assert int(lecb.results_to_numpy(rd)[0]["status"]) == lecb.LECB_ERR_CORRUPT
+
+
+@pytest.mark.parametrize("n,chunk", [(300_001, 16384), ((1 << 20) + 3, 65536)])
+def test_bf16_decode_from_encoder_results(n, chunk):
+    _say(f"bf16 decode from results n={n} chunk={chunk}")
+    x = workloads.bf16_weights(n)
+    xd = to_dev(x.view(np.int16))
+    hist = torch.zeros(512, dtype=torch.int64, device=DEV)
+    bh, bl = lecb.new_codebook_blob(DEV), lecb.new_codebook_blob(DEV)
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(2, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
+    y = torch.empty(n, dtype=torch.int16, device=DEV)
+    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
+    rd = lecb.new_results(2, DEV)
+    lecb.lecb_decode_bf16_from_results(oh, ol, res, bh, bl, chunk, n, y, scratch, rd, ws)
+    q = lecb.results_to_numpy(rd)
+    assert int(q[0]["status"]) == 0 and int(q[1]["status"]) == 0
+    assert torch.equal(y, xd)
+
+
 # ----------------------------------------------------------------------------- device-side errors
 
 def test_uncoded_symbol_sets_status():
