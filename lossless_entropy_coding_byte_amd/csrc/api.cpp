@@ -15,13 +15,14 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Encode workgroups launched per compute unit (persistent grid).  Tunable with
-// LECB_ENCODE_WGS_PER_CU for launch-shape sweeps; 4 by default.
+// Encode workgroups launched per compute unit (persistent grid).  0: as many
+// as fit on a compute unit at once (asked of the runtime per kernel);
+// LECB_ENCODE_WGS_PER_CU overrides it for launch-shape sweeps.
 int encode_wgs_per_cu() {
     static int v = [] {
         const char* e = std::getenv("LECB_ENCODE_WGS_PER_CU");
         const int x = e ? std::atoi(e) : 0;
-        return x >= 1 && x <= 64 ? x : 4;
+        return x >= 1 && x <= 64 ? x : 0;
     }();
     return v;
 }

@@ -9,24 +9,26 @@
 //
 // Work unit: a ticket of max(chunk, 16384) symbols -- G = 16384/chunk whole
 // chunks, or one chunk made of chunk/16384 segments.  A segment is 256
-// threads x 64 consecutive symbols.  One 256-thread workgroup owns one ticket
-// at a time (persistent grid; tickets come from an atomic counter, so every
-// ticket a workgroup waits on is owned by a running workgroup).  Per ticket:
-//   A. each thread loads its 64 symbols (all loads in flight at once) and
-//      sums their code lengths; a block scan gives every thread's bit offset
-//      inside its chunk and every chunk's size.  With one segment per ticket
-//      the symbols stay in registers for step C;
-//   B. per stream, the ticket's word count is published at once; decoupled
-//      look-back over the tickets before it -> the ticket's first payload
-//      word.  Flags are 64-bit {epoch tag, state, value}, so no call ever
-//      clears them; the look-back waits only on the tickets nearer than the
-//      nearest published inclusive prefix, and it runs after the first
-//      packing below, when those are mostly published;
-//   C. per stream: every thread ORs its code words into an LDS image of the
-//      ticket's payload (each chunk starts on a word), then the image goes
-//      out with coalesced stores.  While packing, a thread whose bit range
-//      holds the start s_j of a decode unit records that unit's gap: the
-//      distance from s_j to the first code word that starts at or after it.
+// threads x 64 consecutive symbols.  The grid is persistent and workgroup w
+// owns the contiguous tickets [w*T/W, (w+1)*T/W).  Two launches:
+//   1. count_kernel: every workgroup sums the payload words of its tickets
+//      (per chunk: ceil(bits / 32)) and stores that total;
+//   2. encode_kernel: workgroup w starts at the sum of the totals of
+//      workgroups 0..w-1 (the device-wide exclusive scan, done by one wave
+//      per stream) and then, ticket by ticket:
+//      A. each thread loads its 64 symbols (all loads in flight at once) and
+//         sums their code lengths; a block scan gives every thread's bit
+//         offset inside its chunk and every chunk's size.  With one segment
+//         per ticket the symbols stay in registers for step C;
+//      B. the ticket's first payload word is the running sum of the words of
+//         the workgroup's earlier tickets; the chunk table entries follow;
+//      C. per stream: every thread ORs its code words into an LDS image of
+//         the ticket's payload (each chunk starts on a word), then the image
+//         goes out with coalesced stores.  While packing, a thread whose bit
+//         range holds the start s_j of a decode unit records that unit's gap:
+//         the distance from s_j to the first code word that starts at or
+//         after it.
+// No workgroup ever waits for another one.
 #include <hip/hip_runtime.h>
 
 #include "lecb_internal.hpp"
@@ -40,9 +42,13 @@ constexpr int SPT = 64;                                  // symbols per thread i
 constexpr uint32_t SEG = ENC_THREADS * SPT;              // 16384
 constexpr int MAX_G = SEG / LECB_MIN_CHUNK;              // chunks per ticket at most (64)
 constexpr int STAGE_WORDS = SEG * 16 / 32 + MAX_G + 2;   // worst case 16 bits/symbol, + rounding + carry
+// The stage holds payload word k at LDS word k + k/32.  A thread's 64 code
+// words span about 64*bits/32 payload words, so with 8-bit codes the threads
+// of a wave touch words 16 apart: unpadded, all 64 lanes would fall on 2 of
+// the 32 banks; with the padding word every 32 they spread over all of them.
+__device__ inline uint32_t st_at(uint32_t k) { return k + (k >> 5); }
+constexpr int STAGE_LDS = STAGE_WORDS + STAGE_WORDS / 32 + 1;
 constexpr int MAX_K = LECB_MAX_CHUNK / LECB_UNIT_SYMBOLS; // units per chunk at most (256)
-constexpr uint64_t FLAG_VALUE_MASK = (1ull << 34) - 1;
-constexpr uint32_t ST_AGG = 1, ST_PREFIX = 2;
 constexpr uint32_t NO_BOUNDARY = 0xFFFFFFFFu;
 
 struct StreamArgs {
@@ -57,7 +63,7 @@ struct StreamArgs {
     uint8_t* stream;
     lecb_result* res;
     WsHeader* ws;
-    uint64_t* flags;                         // one per ticket
+    uint64_t* wg_words;                      // payload words of each workgroup's tickets
 };
 
 struct EncArgs {
@@ -172,85 +178,13 @@ __device__ inline uint64_t block_inclusive_scan(uint64_t v, uint64_t* s_tmp, uin
     return before + incl;
 }
 
-__device__ inline uint64_t make_flag(uint32_t tag, uint32_t state, uint64_t value) {
-    return ((uint64_t)tag << 36) | ((uint64_t)state << 34) | (value & FLAG_VALUE_MASK);
-}
-
-// Bound on polling rounds while waiting for a predecessor's flag.  Owners of
-// earlier tickets publish within microseconds; only a workspace that was not
-// zero-filled (stale ticket counter) could leave a flag unpublished, and then
-// the call gives up with status WORKSPACE instead of waiting forever.
-constexpr uint32_t SPIN_LIMIT = 1u << 24;
-
-constexpr int LB_SLOTS = 4;  // tickets each lane watches per round: 256 per round
-
-// Exclusive prefix (in payload words) of ticket c; run by the 64 lanes of one
-// wave.  A round covers the 256 tickets below `end`: slot i of lane l watches
-// ticket end-1-(64*i+l), so offset 64*i+l counts outwards from the nearest.
-// The round is complete once every ticket nearer than the nearest inclusive
-// prefix (state PREFIX) in it is published; then their values and that prefix
-// are added up.  With no prefix in the round all 256 aggregates are added and
-// the window moves down.  *timed_out is set when SPIN_LIMIT was reached.
-__device__ uint64_t look_back(uint64_t* flags, int64_t c, uint32_t tag, bool* timed_out) {
-    const int lane = threadIdx.x & 63;
-    uint64_t excl = 0;
-    int64_t end = c;
-    uint32_t spins = 0;
-    while (end > 0) {
-        uint64_t f[LB_SLOTS];
-        bool have[LB_SLOTS];
-#pragma unroll
-        for (int i = 0; i < LB_SLOTS; ++i) {
-            f[i] = make_flag(tag, ST_PREFIX, 0);  // before ticket 0: prefix 0
-            have[i] = end - 1 - (64 * i + lane) < 0;
-        }
-        int stop;  // offset of the nearest prefix, or 64*LB_SLOTS when none
-        for (;;) {
-#pragma unroll
-            for (int i = 0; i < LB_SLOTS; ++i) {
-                if (!have[i]) {
-                    f[i] = __hip_atomic_load(&flags[end - 1 - (64 * i + lane)], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-                    have[i] = (uint32_t)(f[i] >> 36) == tag && ((f[i] >> 34) & 3u) != 0;
-                }
-            }
-            // every slot nearer than the nearest prefix (and that prefix) must be published
-            bool ok = true;
-            stop = 64 * LB_SLOTS;
-#pragma unroll
-            for (int i = 0; i < LB_SLOTS; ++i) {
-                if (stop == 64 * LB_SLOTS) {
-                    const uint64_t pm = __ballot(have[i] && ((f[i] >> 34) & 3u) == ST_PREFIX);
-                    const uint64_t vm = __ballot(have[i]);
-                    const uint64_t need = pm ? (pm ^ (pm - 1)) : ~0ull;
-                    ok = ok && (vm & need) == need;
-                    if (pm) stop = 64 * i + (int)__builtin_ctzll(pm);
-                }
-            }
-            if (ok) break;
-            if (++spins >= SPIN_LIMIT) {
-                *timed_out = true;
-                return excl;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        uint64_t part = 0;
-#pragma unroll
-        for (int i = 0; i < LB_SLOTS; ++i)
-            if (64 * i + lane <= stop) part += f[i] & FLAG_VALUE_MASK;
-        excl += wave_sum_u64(part);
-        if (stop < 64 * LB_SLOTS) break;
-        end -= 64 * LB_SLOTS;
-    }
-    return excl;
-}
-
 __device__ inline void set_status(WsHeader* ws, int32_t code) {
     atomicCAS(&ws->status, 0, code);
 }
 
 struct Shared {
-    uint32_t stage[STAGE_WORDS];   // payload image of the ticket (one stream at a time)
+    uint32_t stage[STAGE_LDS];     // payload image of the ticket (one stream at a time), padded
+    uint32_t dump[ENC_THREADS];    // target of the stores of pairs that complete no word
     uint32_t enc[2][256];          // (code << 5) | len per stream
     uint8_t len[2][256];
     uint64_t incl[ENC_THREADS];    // inclusive scan of per-thread bits (stream 1 in the high half)
@@ -261,15 +195,14 @@ struct Shared {
     uint64_t tbase[2];
     uint64_t tbits[2];
     uint32_t twords[2];
-    uint32_t ticket;
-    uint32_t tag;
+    uint64_t run[2];               // first payload word of the next ticket
     uint32_t uncoded;
 };
 
 // Bits of the thread's 64 symbols, per stream (nv valid); sets *unc when a
 // valid symbol has no code word.
 template <int NS>
-__device__ inline uint64_t count_bits(const Shared& S, const uint32_t w[][16], int nv, bool* unc) {
+__device__ inline uint64_t count_bits(const uint8_t (&len)[2][256], const uint32_t w[][16], int nv, bool* unc) {
     uint64_t packed = 0;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -277,13 +210,13 @@ __device__ inline uint64_t count_bits(const Shared& S, const uint32_t w[][16], i
         if (nv == SPT) {
 #pragma unroll
             for (int k = 0; k < SPT; ++k) {
-                const uint32_t l = S.len[s][sym_of(w[s], k)];
+                const uint32_t l = len[s][sym_of(w[s], k)];
                 bits += l;
                 mn = min(mn, l);
             }
         } else {
             for (int k = 0; k < nv; ++k) {
-                const uint32_t l = S.len[s][sym_of(w[s], k)];
+                const uint32_t l = len[s][sym_of(w[s], k)];
                 bits += l;
                 mn = min(mn, l);
             }
@@ -305,54 +238,196 @@ __device__ inline void gaps_upto(uint32_t p, uint32_t& j, uint32_t& nb, uint32_t
     }
 }
 
-// Pack the thread's code words into the stage at bit `pos` and record the
-// gaps of the unit starts in its chunk-relative bit range [ts, ...).  FULL:
-// all 64 symbols valid (else the first nv).
-template <bool FULL>
-__device__ inline void pack64(Shared& S, int s, const uint32_t w[16], int nv, uint32_t pos,
-                              uint32_t ts, uint32_t wc, uint32_t K, uint32_t log2k, uint8_t* gap) {
-    // first unit start at or after ts: s_j = 32*floor(j*wc/K) >= ts
-    uint32_t j = wc ? (uint32_t)((((uint64_t)((ts + 31) >> 5)) * K + wc - 1) / wc) : K;
-    uint32_t nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
-    uint32_t p = ts;  // chunk-relative start of the next code word
-    uint32_t widx = pos >> 5;
-    uint32_t used = pos & 31u;
-    uint64_t acc = 0;
-    gaps_upto(p, j, nb, wc, K, log2k, gap);  // a unit starting exactly at ts
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-        const uint32_t e = (FULL || k < nv) ? S.enc[s][sym_of(w, k)] : 0u;
-        const uint32_t len = e & 31u;
-        const uint32_t pk = p;  // start of code word k
-        p += len;
-        used += len;
-        acc |= (uint64_t)(e >> 5) << ((64 - used) & 63);  // ends at bit `used` from the top
-        if (k & 1) {
-            // unit starts in (start of word k-1, start of word k+1]: checked once
-            // per pair; the one after the start of word k-1 but at or before pk
-            // gets pk, the rest (up to p) get p
-            if (p >= nb) {
-                gaps_upto(pk, j, nb, wc, K, log2k, gap);
-                if (k + 1 < SPT) gaps_upto(p, j, nb, wc, K, log2k, gap);
-            }
-            // OR the word being filled (idempotent while it grows), move on once full
-            atomicOr(&S.stage[widx], (uint32_t)(acc >> 32));
-            const bool full = used >= 32;
-            acc = full ? acc << 32 : acc;
-            widx += full ? 1u : 0u;
-            used &= 31u;
-        }
-    }
-    if (used) atomicOr(&S.stage[widx], (uint32_t)(acc >> 32));
-    // unit starts after the last code word's start but before the range end:
-    // their first boundary is the end of this thread's range (= p)
-    while (nb < p) {
-        gap[j] = (uint8_t)(p - nb);
-        ++j;
-        nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
+// Symbol i of stream s, read from the input (for the rare re-walk below).
+template <int MODE>
+__device__ inline uint32_t input_symbol(const EncArgs& a, int s, uint64_t i) {
+    if constexpr (MODE == ENC_BYTES) {
+        return static_cast<const uint8_t*>(a.in)[i];
+    } else {
+        const uint32_t x = static_cast<const uint16_t*>(a.in)[i];
+        const bool lo = MODE == ENC_PLANE_LO || (MODE == ENC_PAIR && s == 1);
+        return lo ? (x & 0xFFu) : (x >> 8);
     }
 }
 
+// Gaps of all unit starts in the thread's range (ts, end], by walking its
+// code words again (symbols re-read from the input).  Only for the rare
+// thread that owns more than one unit start: units are 8+ words apart
+// except in a short last chunk.
+template <int MODE>
+__device__ inline void gaps_walk(const Shared& S, const EncArgs& a, int s, uint64_t i0, int nv,
+                                 uint32_t ts, uint32_t j, uint32_t nb, uint32_t wc, uint32_t K,
+                                 uint32_t log2k, uint8_t* gap) {
+    uint32_t p = ts;
+    for (int k = 0; k < nv; ++k) {
+        p += S.len[s][input_symbol<MODE>(a, s, i0 + k)];  // start of code word k + 1
+        gaps_upto(p, j, nb, wc, K, log2k, gap);
+    }
+}
+
+// Pack the thread's code words into the stage at bit `pos` and record the
+// gaps of the unit starts in its chunk-relative bit range [ts, ...).  FULL:
+// all 64 symbols valid (else the first nv; the rest are zero bytes and get
+// no code word).
+//   * Code words are looked up 16 at a time (one LDS latency per 16) and
+//     joined in pairs: a pair is at most 32 bits, so it enters the 64-bit
+//     accumulator in one step and completes at most one word.
+//   * No branches per pair.  Every pair stores one word: the completed word
+//     when the thread owns all of it, otherwise a dummy slot.  The thread's
+//     first word, when it starts before `pos` (the previous thread's code
+//     words end in it), and its last, partial word are ORed in afterwards
+//     (the stage is zero before packing).
+//   * The first unit start after ts is found on the way (a compare per
+//     pair); a thread that owns a second one walks its code words again.
+template <bool FULL, int MODE>
+__device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, uint32_t w[16], int nv,
+                              uint32_t pos, uint32_t ts, uint32_t wc, uint32_t K, uint32_t log2k,
+                              uint8_t* gap) {
+    // first unit start at or after ts: s_j = 32*floor(j*wc/K) >= ts
+    uint32_t j = wc ? (uint32_t)((((uint64_t)((ts + 31) >> 5)) * K + wc - 1) / wc) : K;
+    uint32_t nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
+    gaps_upto(ts, j, nb, wc, K, log2k, gap);  // unit starts exactly at ts: gap 0
+    const uint32_t j0 = j, nb0 = nb;          // next unit start, after ts
+    uint32_t g0 = 0;
+    uint32_t p = ts;  // chunk-relative start of the next code word
+    uint32_t widx = pos >> 5;
+    const uint32_t widx0 = widx;
+    uint32_t first_left = (pos & 31u) ? 1u : 0u;  // 1 until the shared first word completes
+    uint32_t first_val = 0;
+    uint32_t used = pos & 31u;
+    uint64_t acc = 0;
+    // LDS byte addresses: the dump slot, and the stage (word k at k + k/32)
+    const uint32_t dump_at = (uint32_t)(uintptr_t)&S.dump[threadIdx.x];
+    const uint32_t stage_at = (uint32_t)(uintptr_t)&S.stage[0];
+    // 16 symbols per round; the symbol words move down by 4 after each round
+    // (w is used up), so every index stays a constant without unrolling all
+    // 64 symbols
+    uint32_t* const ww = w;
+#pragma unroll 1
+    for (int g = 0; g < SPT / 16; ++g) {
+        uint32_t e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t x = S.enc[s][sym_of(ww, i)];
+            e[i] = (FULL || 16 * g + i < nv) ? x : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
+            const uint32_t l0 = e0 & 31u, l1 = e1 & 31u;
+            const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);  // at most 32 bits
+            const uint32_t pmid = p + l0, pend = pmid + l1;
+            // the first code-word start at or after nb0
+            g0 = (p < nb0 && nb0 <= pmid) ? pmid - nb0 : g0;
+            g0 = (pmid < nb0 && nb0 <= pend) ? pend - nb0 : g0;
+            p = pend;
+            used += l0 + l1;
+            acc |= (uint64_t)c2 << ((64 - used) & 63);  // ends at bit `used` from the top
+            // 0/1 arithmetic instead of branches and masks
+            const uint32_t full = used >> 5;             // used <= 63
+            const uint32_t v = (uint32_t)(acc >> 32);
+            const uint32_t to_first = full & first_left;
+            first_val |= v & (0u - to_first);
+            const uint32_t own = full - to_first;
+            const uint32_t at = own ? stage_at + 4u * st_at(widx) : dump_at;
+            *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(at) = v;
+            first_left -= to_first;
+            acc <<= 32 * full;
+            widx += full;
+            used &= 31u;
+        }
+#pragma unroll
+        for (int i = 0; i < 12; ++i) ww[i] = ww[i + 4];
+    }
+    if (pos & 31u) atomicOr(&S.stage[st_at(widx0)], first_val);
+    if (used) atomicOr(&S.stage[st_at(widx)], (uint32_t)(acc >> 32));
+    // unit starts in (ts, p]; p is the range end
+    if (nb0 <= p) {
+        gap[j0] = (uint8_t)g0;
+        const uint32_t j1 = j0 + 1;
+        const uint32_t nb1 = j1 < K ? (uint32_t)(((uint64_t)j1 * wc) >> log2k) << 5 : NO_BOUNDARY;
+        if (nb1 <= p) gaps_walk<MODE>(S, a, s, i0, FULL ? SPT : nv, ts, j1, nb1, wc, K, log2k, gap);
+    }
+}
+
+// First ticket of workgroup w when T tickets are split over W workgroups.
+__device__ inline uint64_t first_ticket(uint64_t w, uint64_t T, uint64_t W) { return w * T / W; }
+
+// Bits of each chunk of ticket `tk` (per stream, lanes 0..nch-1 of wave s
+// receive chunk `lane`'s bits); w keeps the symbols when the ticket is one
+// segment, and incl/tmp/len are the caller's LDS.
+template <int MODE>
+__device__ inline void ticket_bits(const EncArgs& a, uint64_t tk, const uint8_t (&len)[2][256],
+                                   uint64_t* incl_lds, uint64_t* tmp, uint32_t w[][16], bool* unc,
+                                   uint32_t* nch_out, uint32_t* nseg_out, uint64_t* chunk_acc) {
+    constexpr int NS = Streams<MODE>::value;
+    const int tid = threadIdx.x;
+    const uint64_t c0 = tk * a.G;
+    const uint32_t nch = (uint32_t)min<uint64_t>(a.G, a.nc - c0);
+    const uint64_t tbeg = c0 * a.chunk;
+    const uint64_t tend = min(tbeg + (uint64_t)a.G * a.chunk, a.n);
+    const uint32_t nseg = (uint32_t)((tend - tbeg + SEG - 1) / SEG);
+    uint64_t acc = 0;
+    for (uint32_t g = 0; g < nseg; ++g) {
+        const uint64_t i0 = tbeg + (uint64_t)g * SEG + (uint64_t)tid * SPT;
+        const int nv = i0 >= tend ? 0 : (int)min<uint64_t>(SPT, tend - i0);
+        load64<MODE>(a, i0, nv, w);
+        const uint64_t bits = count_bits<NS>(len, w, nv, unc);
+        uint64_t total;
+        const uint64_t incl = block_inclusive_scan(bits, tmp, &total);
+        if (nseg == 1) incl_lds[tid] = incl;
+        acc += total;
+    }
+    *nch_out = nch;
+    *nseg_out = nseg;
+    *chunk_acc = acc;
+}
+
+// Bits of chunk `lane` of the ticket for stream s (0 for lanes >= nch).
+__device__ inline uint32_t chunk_bits_of(const uint64_t* incl_lds, int lane, int s, uint32_t nch,
+                                         uint32_t nseg, uint32_t L, uint64_t chunk_acc) {
+    if (nseg == 1) {
+        if (lane >= (int)nch) return 0;
+        const uint64_t hi = incl_lds[(lane + 1) * L - 1];
+        const uint64_t lo = lane ? incl_lds[lane * L - 1] : 0ull;
+        return (uint32_t)((hi - lo) >> (32 * s));
+    }
+    return lane == 0 ? (uint32_t)(chunk_acc >> (32 * s)) : 0u;
+}
+
+// Launch 1: payload words of every workgroup's tickets, per stream.
+template <int MODE>
+__global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
+    constexpr int NS = Streams<MODE>::value;
+    __shared__ uint8_t len[2][256];
+    __shared__ uint64_t incl[ENC_THREADS];
+    __shared__ uint64_t tmp[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) len[s][tid] = (uint8_t)(a.st[s].cb->enc[tid] & 31u);
+    __syncthreads();
+    const uint32_t L = a.chunk >= SEG ? ENC_THREADS : a.chunk / SPT;
+    const uint64_t t0 = first_ticket(blockIdx.x, a.ntickets, gridDim.x);
+    const uint64_t t1 = first_ticket(blockIdx.x + 1ull, a.ntickets, gridDim.x);
+    uint64_t words = 0;  // wave s, stream s
+    for (uint64_t tk = t0; tk < t1; ++tk) {
+        uint32_t w[NS][16];
+        bool unc = false;
+        uint32_t nch, nseg;
+        uint64_t acc;
+        ticket_bits<MODE>(a, tk, len, incl, tmp, w, &unc, &nch, &nseg, &acc);
+        __syncthreads();
+        if (wave < NS) {
+            const uint32_t cb = chunk_bits_of(incl, lane, wave, nch, nseg, L, acc);
+            words += wave_sum_u64((cb + 31) >> 5);
+        }
+        __syncthreads();
+    }
+    if (wave < NS && lane == 0) a.st[wave].wg_words[blockIdx.x] = words;
+}
+
+// Launch 2: pack (see the top of the file).
 template <int MODE>
 __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_kernel(EncArgs a) {
     constexpr int NS = Streams<MODE>::value;
@@ -366,59 +441,53 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
         S.enc[s][tid] = e;
         S.len[s][tid] = (uint8_t)(e & 31u);
     }
-    if (tid == 0) {
-        const uint32_t e = __hip_atomic_load(&a.st[0].ws->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        S.tag = (e % 0x0FFFFFFFu) + 1;
+    // first payload word of this workgroup: the words of workgroups 0..w-1,
+    // summed by all threads (independent loads, one latency)
+    {
+        uint64_t part[2] = {0, 0};
+#pragma unroll 4
+        for (uint32_t v = tid; v < blockIdx.x; v += ENC_THREADS) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) part[s] += a.st[s].wg_words[v];
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint64_t x = wave_sum_u64(part[s]);
+            if (lane == 0) S.incl[NS * wave + s] = x;
+        }
+    }
+    if (tid == 0) S.uncoded = 0;
+    __syncthreads();
+    if (tid < NS) {
+        uint64_t sum = 0;
+        for (int v = 0; v < ENC_THREADS / 64; ++v) sum += S.incl[NS * v + tid];
+        S.run[tid] = sum;
     }
     __syncthreads();
-    const uint32_t tag = S.tag;
     const uint32_t K = 1u << a.log2k;
     const uint32_t L = a.chunk >= SEG ? ENC_THREADS : a.chunk / SPT;  // threads per chunk in a segment
+    const uint64_t t0 = first_ticket(blockIdx.x, a.ntickets, gridDim.x);
+    const uint64_t t1 = first_ticket(blockIdx.x + 1ull, a.ntickets, gridDim.x);
 
-    for (;;) {
-        if (tid == 0) {
-            S.ticket = atomicAdd(&a.st[0].ws->ticket, 1u);
-            S.uncoded = 0;
-        }
-        __syncthreads();
-        const uint64_t T = S.ticket;
-        if (T >= a.ntickets) break;
-
+    for (uint64_t T = t0; T < t1; ++T) {
         const uint64_t c0 = T * a.G;                                   // first chunk
-        const uint32_t nch = (uint32_t)min<uint64_t>(a.G, a.nc - c0);   // chunks in the ticket
         const uint64_t tbeg = c0 * a.chunk;                            // first symbol
         const uint64_t tend = min(tbeg + (uint64_t)a.G * a.chunk, a.n);
-        const uint32_t nseg = (uint32_t)((tend - tbeg + SEG - 1) / SEG);
 
         // ---- A: bits of every chunk of the ticket
         uint32_t w[NS][16];
         bool unc = false;
-        uint64_t chunk_bits_acc = 0;  // S > 1: the one chunk's bits so far (packed per stream)
-        for (uint32_t g = 0; g < nseg; ++g) {
-            const uint64_t i0 = tbeg + (uint64_t)g * SEG + (uint64_t)tid * SPT;
-            const int nv = i0 >= tend ? 0 : (int)min<uint64_t>(SPT, tend - i0);
-            load64<MODE>(a, i0, nv, w);
-            const uint64_t bits = count_bits<NS>(S, w, nv, &unc);
-            uint64_t total;
-            const uint64_t incl = block_inclusive_scan(bits, S.tmp, &total);
-            if (nseg == 1) S.incl[tid] = incl;
-            chunk_bits_acc += total;
-        }
+        uint32_t nch, nseg;
+        uint64_t chunk_bits_acc;  // nseg > 1: the one chunk's bits (packed per stream)
+        ticket_bits<MODE>(a, T, S.len, S.incl, S.tmp, w, &unc, &nch, &nseg, &chunk_bits_acc);
         if (unc) atomicOr(&S.uncoded, 1u);
         __syncthreads();
-        // chunk sizes and ticket-relative word offsets: wave s handles stream s
+        // ---- B: chunk sizes, word offsets and the ticket's place in the
+        // payload (wave s handles stream s)
         if (wave < NS) {
             const int s = wave;
-            uint32_t cb = 0;
-            if (nseg == 1) {
-                if (lane < (int)nch) {
-                    const uint64_t hi = S.incl[(lane + 1) * L - 1];
-                    const uint64_t lo = lane ? S.incl[lane * L - 1] : 0ull;
-                    cb = (uint32_t)((hi - lo) >> (32 * s));
-                }
-            } else if (lane == 0) {
-                cb = (uint32_t)(chunk_bits_acc >> (32 * s));
-            }
+            const StreamArgs& sa = a.st[s];
+            const uint32_t cb = chunk_bits_of(S.incl, lane, s, nch, nseg, L, chunk_bits_acc);
             const uint32_t cw = (cb + 31) >> 5;
             uint32_t incl = cw;
 #pragma unroll
@@ -430,15 +499,20 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
                 S.cword[s][lane] = incl - cw;
                 S.cbits[s][lane] = cb;
             }
-            const uint32_t twords = __shfl(incl, 63, 64);
+            const uint32_t tw = __shfl(incl, 63, 64);
             const uint64_t tbits = wave_sum_u64(cb);
-            // ---- B (publish): this ticket's aggregate for stream s
+            const uint64_t base = S.run[s];
+            if (lane < (int)nch) sa.table[c0 + lane] = (uint32_t)(base + incl);
             if (lane == 0) {
-                __hip_atomic_store(&a.st[s].flags[T],
-                                   make_flag(tag, T == 0 ? ST_PREFIX : ST_AGG, twords),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                S.twords[s] = twords;
-                S.tbits[s] = tbits;
+                S.twords[s] = tw;
+                S.tbase[s] = base;
+                S.run[s] = base + tw;
+                atomicAdd(reinterpret_cast<unsigned long long*>(&sa.ws->bits), (unsigned long long)tbits);
+                if (T == a.ntickets - 1)
+                    __hip_atomic_store(&sa.ws->words, base + tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (S.uncoded) set_status(sa.ws, LECB_ERR_UNCODED_SYMBOL);
+                if (base + tw >= (1ull << 32)) set_status(sa.ws, LECB_ERR_TOO_LARGE);
+                else if (base + tw > sa.capacity_words) set_status(sa.ws, LECB_ERR_CAPACITY);
             }
         }
         __syncthreads();
@@ -461,7 +535,7 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
                     // the segment's scan again (step A kept only totals)
                     load64<MODE>(a, i0, nv, w);
                     bool unused = false;
-                    own = count_bits<NS>(S, w, nv, &unused);
+                    own = count_bits<NS>(S.len, w, nv, &unused);
                     incl = block_inclusive_scan(own, S.tmp, &seg_total);
                 }
                 const uint32_t mine = (uint32_t)(own >> (32 * s));  // this thread's bits
@@ -474,7 +548,7 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
                     wc = (S.cbits[s][min(ch, (uint32_t)MAX_G - 1)] + 31) >> 5;
                     pos = (ch < nch ? S.cword[s][ch] * 32u : 0u) + ts;
                     touched = twords;
-                    for (uint32_t k = tid; k < touched; k += ENC_THREADS) S.stage[k] = 0u;
+                    for (uint32_t k = tid; k < touched; k += ENC_THREADS) S.stage[st_at(k)] = 0u;
                 } else {
                     ch = 0;
                     const uint32_t seg_bits = (uint32_t)(seg_total >> (32 * s));
@@ -485,50 +559,29 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
                     w0 = TB >> 5;
                     pos = r0 + excl;
                     touched = (r0 + seg_bits + 31) >> 5;
-                    for (uint32_t k = tid; k <= touched; k += ENC_THREADS) S.stage[k] = k ? 0u : carry;
+                    for (uint32_t k = tid; k <= touched; k += ENC_THREADS) S.stage[st_at(k)] = k ? 0u : carry;
                     TB += seg_bits;
                 }
                 __syncthreads();
                 if (nv == SPT && ch < nch)
-                    pack64<true>(S, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
+                    pack64<true, MODE>(S, a, i0, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
                 else if (nv > 0 && ch < nch)
-                    pack64<false>(S, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
-                if (s == 0 && g == 0 && wave < NS) {
-                    // ---- B (look-back), after the first packing: by now more of
-                    // the tickets before this one have published prefixes
-                    const int sl = wave;
-                    const StreamArgs& sa = a.st[sl];
-                    const uint32_t tw = S.twords[sl];
-                    bool timed_out = false;
-                    const uint64_t excl = T == 0 ? 0 : look_back(sa.flags, (int64_t)T, tag, &timed_out);
-                    if (lane == 0) {
-                        if (timed_out) set_status(sa.ws, LECB_ERR_WORKSPACE);
-                        if (T) {
-                            __hip_atomic_store(&sa.flags[T], make_flag(tag, ST_PREFIX, excl + tw),
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                        S.tbase[sl] = excl;
-                        atomicAdd(reinterpret_cast<unsigned long long*>(&sa.ws->bits),
-                                  (unsigned long long)S.tbits[sl]);
-                        if (T == a.ntickets - 1) {
-                            __hip_atomic_store(&sa.ws->words, excl + tw, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                        if (S.uncoded) set_status(sa.ws, LECB_ERR_UNCODED_SYMBOL);
-                        if (excl + tw >= (1ull << 32)) set_status(sa.ws, LECB_ERR_TOO_LARGE);
-                        else if (excl + tw > sa.capacity_words) set_status(sa.ws, LECB_ERR_CAPACITY);
-                    }
-                    if (lane < (int)nch)
-                        sa.table[c0 + lane] =
-                            (uint32_t)(excl + S.cword[sl][lane] + ((S.cbits[sl][lane] + 31) >> 5));
-                }
-                __syncthreads();  // stage complete (and, the first time, the ticket bases known)
+                    pack64<false, MODE>(S, a, i0, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
+                __syncthreads();  // stage complete
                 const uint64_t tbase = S.tbase[s];
                 const bool write_ok = tbase + twords <= st.capacity_words && !S.uncoded;
                 if (nseg == 1) {
                     if (write_ok) {
                         uint32_t* dst = st.payload + tbase;
-                        for (uint32_t k = tid; k < twords; k += ENC_THREADS) dst[k] = S.stage[k];
+                        uint32_t k = tid;
+                        for (; k + 3 * ENC_THREADS < twords; k += 4 * ENC_THREADS) {
+                            uint32_t v[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) v[q] = S.stage[st_at(k + q * ENC_THREADS)];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) dst[k + q * ENC_THREADS] = v[q];
+                        }
+                        for (; k < twords; k += ENC_THREADS) dst[k] = S.stage[st_at(k)];
                     }
                 } else {
                     const bool last_seg = g + 1 == nseg;
@@ -536,9 +589,9 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
                     const uint32_t nwrite = last_seg ? touched : full;
                     if (write_ok) {
                         uint32_t* dst = st.payload + tbase + w0;
-                        for (uint32_t k = tid; k < nwrite; k += ENC_THREADS) dst[k] = S.stage[k];
+                        for (uint32_t k = tid; k < nwrite; k += ENC_THREADS) dst[k] = S.stage[st_at(k)];
                     }
-                    carry = S.stage[full];
+                    carry = S.stage[st_at(full)];
                 }
                 __syncthreads();
             }
@@ -582,9 +635,6 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
                 ws->bits = 0;
                 ws->status = 0;
             }
-            ws0->ticket = 0;
-            const uint32_t ep = ws0->epoch;
-            ws0->epoch = ep + 1;
             __threadfence();
             __hip_atomic_store(&ws0->exit_count, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -620,16 +670,50 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
         st.gap_pad_to = tb + gb;
         st.res = L.st[s].res;
         st.ws = L.st[s].ws;
-        st.flags = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);
+        st.wg_words = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);  // room for nc >= grid values
     }
-    const uint64_t nwg = (uint64_t)L.grid < a.ntickets ? (uint64_t)L.grid : a.ntickets;
+    // Both launches split the tickets over the same workgroups.  The ranges
+    // are static, so the grid must be resident at once: by default it is the
+    // number of pack workgroups that fit on all compute units together.
+    uint64_t grid_wgs = L.grid;
+    if (grid_wgs == 0) {
+        static int per_cu[4] = {0, 0, 0, 0};
+        const int m = (int)L.mode & 3;
+        if (per_cu[m] == 0) {
+            int nb = 0;
+            hipError_t e = hipErrorInvalidValue;
+            switch (L.mode) {
+                case ENC_BYTES: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_BYTES>, ENC_THREADS, 0); break;
+                case ENC_PLANE_LO: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PLANE_LO>, ENC_THREADS, 0); break;
+                case ENC_PLANE_HI: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PLANE_HI>, ENC_THREADS, 0); break;
+                case ENC_PAIR: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PAIR>, ENC_THREADS, 0); break;
+                default: return LECB_ERR_INVALID_ARG;
+            }
+            if (e != hipSuccess || nb < 1) return LECB_ERR_HIP;
+            per_cu[m] = nb;
+        }
+        grid_wgs = (uint64_t)device_cu_count() * per_cu[m];
+    }
+    const uint64_t nwg = grid_wgs < a.ntickets ? grid_wgs : a.ntickets;
     const dim3 grid((uint32_t)nwg), block(ENC_THREADS);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     switch (L.mode) {
-        case ENC_BYTES: hipLaunchKernelGGL(encode_kernel<ENC_BYTES>, grid, block, 0, hs, a); break;
-        case ENC_PLANE_LO: hipLaunchKernelGGL(encode_kernel<ENC_PLANE_LO>, grid, block, 0, hs, a); break;
-        case ENC_PLANE_HI: hipLaunchKernelGGL(encode_kernel<ENC_PLANE_HI>, grid, block, 0, hs, a); break;
-        case ENC_PAIR: hipLaunchKernelGGL(encode_kernel<ENC_PAIR>, grid, block, 0, hs, a); break;
+        case ENC_BYTES:
+            hipLaunchKernelGGL(count_kernel<ENC_BYTES>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(encode_kernel<ENC_BYTES>, grid, block, 0, hs, a);
+            break;
+        case ENC_PLANE_LO:
+            hipLaunchKernelGGL(count_kernel<ENC_PLANE_LO>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(encode_kernel<ENC_PLANE_LO>, grid, block, 0, hs, a);
+            break;
+        case ENC_PLANE_HI:
+            hipLaunchKernelGGL(count_kernel<ENC_PLANE_HI>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(encode_kernel<ENC_PLANE_HI>, grid, block, 0, hs, a);
+            break;
+        case ENC_PAIR:
+            hipLaunchKernelGGL(count_kernel<ENC_PAIR>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(encode_kernel<ENC_PAIR>, grid, block, 0, hs, a);
+            break;
         default: return LECB_ERR_INVALID_ARG;
     }
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;

@@ -40,14 +40,17 @@ struct CodebookArgs {
 };
 
 // ---------------------------------------------------------------- workspace
-// Encode: ticket counter, look-back flags (epoch-tagged so they never need
-// clearing), exit counter and accumulators.  Decode: exit counter + status.
-// A workspace holds two of them (header + flags each, 256-byte aligned): a
-// two-stream encode uses both; everything else uses the first.
+// Encode: exit counter and accumulators, followed by the payload words of
+// each encode workgroup (written by the count launch, read by the pack
+// launch of the same call).  Decode: exit counter + status.  A workspace
+// holds two of them (header + one u64 per chunk each, 256-byte aligned): a
+// two-stream encode uses both; everything else uses the first.  The last
+// workgroup of every call resets the header, so only the first use needs a
+// zero-filled workspace.
 struct WsHeader {
-    uint32_t ticket;
+    uint32_t unused0;
     uint32_t exit_count;
-    uint32_t epoch;
+    uint32_t unused1;
     int32_t status;
     uint64_t bits;
     uint64_t words;
@@ -87,7 +90,7 @@ struct EncodeStream {
     uint8_t* out;            // stream base
     uint64_t capacity;       // bytes
     lecb_result* res;
-    WsHeader* ws;            // followed by one u64 flag per ticket
+    WsHeader* ws;            // followed by one u64 per chunk (workgroup word totals)
 };
 
 struct EncodeLaunch {

@@ -150,7 +150,7 @@ def test_determinism_repeat_encode():
 
 
 def test_workspace_reuse_across_calls():
-    # the epoch-tagged look-back flags must not leak between calls sharing a workspace
+    # per-workgroup word totals and the exit counter must not leak between calls sharing a workspace
     x1 = _gauss(14, 4096 * 300 + 9)
     x2 = _gauss(15, 4096 * 120 + 1, 40.0)
     ln = codebook_for(np.concatenate([x1, x2]), True)
