@@ -39,13 +39,15 @@
 // checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "lecb_internal.hpp"
 
 namespace lecb {
 
 namespace {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_MAX_THREADS = 1024;  // lanes (decode units) per workgroup: 256, 512 or 1024
 constexpr uint32_t RING = 16;  // payload words per lane in LDS
 constexpr uint32_t DEC_BLOCK = 32;  // output block a lane owns (bytes)
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -83,11 +85,11 @@ struct Tables {
     uint8_t sorted[256];
 };
 
+template <int NT>
 struct Shared {
-    uint32_t ring[RING][DEC_THREADS];
+    uint32_t ring[RING][NT];  // row 0 doubles as the counts of the scan
     Tables T;
-    uint32_t cnt[DEC_THREADS];
-    uint64_t red[DEC_THREADS / 64];
+    uint64_t red[NT / 64];
 };
 
 // Left-aligned canonical limits of the lengths above LUT_BITS (uniform values).
@@ -95,6 +97,7 @@ struct Limits {
     uint32_t l13, l14, l15, l16;
 };
 
+template <int NT>
 struct Reader {
     uint32_t* ring;      // &ring[0][lane]
     const uint32_t* p;   // payload
@@ -111,7 +114,7 @@ struct Reader {
     bool pend;
 
     __device__ inline uint32_t& slot(uint32_t w) {  // w relative to sw
-        return ring[((w + sh) & (RING - 1)) * DEC_THREADS];
+        return ring[((w + sh) & (RING - 1)) * NT];
     }
     __device__ inline uint32_t rd() const { return rq - sh; }
     __device__ inline v4u ld4(uint64_t g) const {
@@ -119,14 +122,14 @@ struct Reader {
     }
     __device__ inline void put8(uint32_t w, const v4u& x, const v4u& y) {
         uint32_t* s = &slot(w);  // w..w+7 are consecutive slots (sw + w is a multiple of 8)
-        s[0 * DEC_THREADS] = x.x;
-        s[1 * DEC_THREADS] = x.y;
-        s[2 * DEC_THREADS] = x.z;
-        s[3 * DEC_THREADS] = x.w;
-        s[4 * DEC_THREADS] = y.x;
-        s[5 * DEC_THREADS] = y.y;
-        s[6 * DEC_THREADS] = y.z;
-        s[7 * DEC_THREADS] = y.w;
+        s[0 * NT] = x.x;
+        s[1 * NT] = x.y;
+        s[2 * NT] = x.z;
+        s[3 * NT] = x.w;
+        s[4 * NT] = y.x;
+        s[5 * NT] = y.y;
+        s[6 * NT] = y.z;
+        s[7 * NT] = y.w;
     }
     // Ring top-up: commit the previous load, issue the next one when there is
     // room.  Between two top-ups at most 4 words leave the ring, and after a
@@ -157,7 +160,7 @@ struct Reader {
         w0 = slot(word);
         w1 = slot(word + 1);
         rq = word + 2 + sh;
-        nextw = ring[(rq & (RING - 1)) * DEC_THREADS];
+        nextw = ring[(rq & (RING - 1)) * NT];
         off = bit & 31;
     }
     // The next 32 bits, MSB first (all of them valid while off <= 32).
@@ -174,7 +177,7 @@ struct Reader {
         w1 = take ? nextw : w1;
         off &= 31;
         rq += take ? 1u : 0u;
-        nextw = ring[(rq & (RING - 1)) * DEC_THREADS];
+        nextw = ring[(rq & (RING - 1)) * NT];
     }
 };
 
@@ -196,7 +199,8 @@ __device__ inline uint32_t lookup(const Tables& T, const Limits& L, uint32_t top
 }
 
 // Decode one code word and advance; returns (sym << 8) | len.
-__device__ inline uint32_t step(const Tables& T, const Limits& L, Reader& r, uint32_t& inval) {
+template <int NT>
+__device__ inline uint32_t step(const Tables& T, const Limits& L, Reader<NT>& r, uint32_t& inval) {
     const uint32_t e = lookup(T, L, r.peek(), inval);
     r.off += e & 0xFFu;
     return e;
@@ -207,8 +211,11 @@ __device__ inline uint32_t gap_of(const uint8_t* gaps, uint64_t i) {
     return (i & 1) ? (b >> 4) : (b & 0xFu);
 }
 
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
-    __shared__ __attribute__((aligned(16))) Shared S;
+// 64 VGPRs at most: two 1024-lane workgroups (8 waves per SIMD) fit a CU.
+template <int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_kernel(DecArgs a) {
+    constexpr int DEC_THREADS = NT;
+    __shared__ __attribute__((aligned(16))) Shared<NT> S;
     Tables& T = S.T;
 
     const int tid = threadIdx.x;
@@ -270,7 +277,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
         }
     }
 
-    Reader r;
+    Reader<NT> r;
     r.ring = &S.ring[0][tid];
     r.p = d.payload;
     r.sw = sw;
@@ -338,17 +345,20 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
     }
 
     // ---- 2. exclusive scan of counts within each chunk (segments of K lanes)
-    S.cnt[tid] = cnt;
+    // ring row 0 holds the counts now: a lane's column is its own, and no lane
+    // touches the ring again before the barrier ahead of the decode pass
+    uint32_t* const scnt = &S.ring[0][0];
+    scnt[tid] = cnt;
     __syncthreads();
     for (int o = 1; o < DEC_THREADS; o <<= 1) {
-        const uint32_t v = tid >= o ? S.cnt[tid - o] : 0u;
+        const uint32_t v = tid >= o ? scnt[tid - o] : 0u;
         __syncthreads();
-        S.cnt[tid] += v;
+        scnt[tid] += v;
         __syncthreads();
     }
     const int seg0 = tid - (int)j;  // lane of unit 0 of this chunk
-    const uint32_t before_seg = seg0 > 0 ? S.cnt[seg0 - 1] : 0u;
-    const uint32_t out_off = S.cnt[tid] - cnt - before_seg;
+    const uint32_t before_seg = seg0 > 0 ? scnt[seg0 - 1] : 0u;
+    const uint32_t out_off = scnt[tid] - cnt - before_seg;
     uint64_t used_bits = 0;
     if (run && !bad) {
         if (last) {
@@ -356,10 +366,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecArgs a) {
             if (out_off + cnt > m_c || m_c - out_off - cnt > 32) {
                 bad = true;
             } else {
+                // they lie in the last payload word, which the window holds
+                // after the count pass (w0): no ring words are needed (the
+                // ring's row 0 holds the counts)
                 const uint32_t rem = m_c - out_off - cnt;
                 uint32_t inval = 0;
                 for (uint32_t i = 0; i < rem; ++i) {
-                    if ((i & 3) == 0) r.tick();
                     r.refill();
                     (void)step(T, L, r, inval);
                 }
@@ -518,10 +530,23 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
         st.ws = L.ws[s];
     }
     const uint64_t units = L.nc * K;
-    a.wg_per_stream = (uint32_t)((units + DEC_THREADS - 1) / DEC_THREADS);
-    const uint64_t grid = (uint64_t)a.wg_per_stream * L.nstreams;
-    hipLaunchKernelGGL(decode_kernel, dim3((uint32_t)grid), dim3(DEC_THREADS), 0,
-                       reinterpret_cast<hipStream_t>(stream), a);
+    // Lanes per workgroup: the tables are one copy per workgroup, so bigger
+    // workgroups leave more LDS for lanes (2 x 1024 lanes fit a CU against
+    // 5 x 256), and fewer, bigger workgroups spread evenly over the CUs.
+    // Take the biggest size that still gives every CU a workgroup.
+    const uint64_t all = units * (uint64_t)L.nstreams;
+    const uint64_t cus = (uint64_t)device_cu_count();
+    int nt = all >= cus * 1024 ? 1024 : all >= cus * 512 ? 512 : 256;
+    if (const char* e = std::getenv("LECB_DECODE_THREADS")) {
+        const int x = std::atoi(e);
+        if (x == 256 || x == 512 || x == 1024) nt = x;
+    }
+    a.wg_per_stream = (uint32_t)((units + nt - 1) / nt);
+    const dim3 grid((uint32_t)((uint64_t)a.wg_per_stream * L.nstreams));
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (nt == 1024) hipLaunchKernelGGL(decode_kernel<1024>, grid, dim3(1024), 0, hs, a);
+    else if (nt == 512) hipLaunchKernelGGL(decode_kernel<512>, grid, dim3(512), 0, hs, a);
+    else hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(256), 0, hs, a);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

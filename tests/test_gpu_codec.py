@@ -295,6 +295,49 @@ def test_bf16_pertensor_pipeline(n, chunk):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
 
 
+# ----------------------------------------------------------------------------- decode workgroup sizes
+
+@pytest.mark.parametrize("nt", [256, 512, 1024])
+@pytest.mark.parametrize("n,chunk", [(300_007, 4096), (700_001, 65536), (1 << 20, 16384)])
+def test_decode_every_workgroup_size(monkeypatch, nt, n, chunk):
+    """The decoder picks 256, 512 or 1024 lanes per workgroup from the size of
+    the job; every size decodes the oracle's stream exactly (ragged tails and
+    chunks that end inside a workgroup included)."""
+    _say(f"decode nt={nt} n={n} chunk={chunk}")
+    monkeypatch.setenv("LECB_DECODE_THREADS", str(nt))
+    x = _gauss(40 + nt, n, 12.0)
+    ln = codebook_for(x, True)
+    ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), chunk)
+    dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+    got, r = gpu_decode(ref, dcb, chunk, n)
+    assert int(r["status"]) == 0
+    assert np.array_equal(got, x)
+
+
+@pytest.mark.parametrize("nt", [256, 1024])
+def test_bf16_two_plane_decode_workgroup_sizes(monkeypatch, nt):
+    monkeypatch.setenv("LECB_DECODE_THREADS", str(nt))
+    n, chunk = 1_000_003, 16384
+    x = workloads.bf16_weights(n)
+    enc = oracle.encode_bf16(x, chunk)
+    hi, lo = oracle.split_bf16(x)
+    bh = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_hi"]), DEV)
+    bl = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_lo"]), DEV)
+    sh = torch.zeros(enc["stream_hi"].size + 32, dtype=torch.uint8, device=DEV)
+    sl = torch.zeros(enc["stream_lo"].size + 32, dtype=torch.uint8, device=DEV)
+    sh[: enc["stream_hi"].size] = to_dev(enc["stream_hi"])
+    sl[: enc["stream_lo"].size] = to_dev(enc["stream_lo"])
+    oh = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=DEV)
+    ol = torch.empty_like(oh)
+    res = lecb.new_results(2, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    lecb.lecb_decode_bf16_planes(sh, enc["stream_hi"].size, sl, enc["stream_lo"].size, bh.blob, bl.blob,
+                                 chunk, n, oh, ol, res, ws)
+    r = lecb.results_to_numpy(res)
+    assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
+    assert np.array_equal(oh[:n].cpu().numpy(), hi) and np.array_equal(ol[:n].cpu().numpy(), lo)
+
+
 # ----------------------------------------------------------------------------- sizes on the device
 
 @pytest.mark.parametrize("n,chunk", [(1, 256), (100_003, 4096), (1 << 20, 65536)])
