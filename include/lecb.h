@@ -41,7 +41,9 @@
  *    hipStream_t passed as void* (NULL = the null stream).
  *  - Device entry points only enqueue work on `stream`; they never
  *    synchronise and never allocate.  The one exception is
- *    lecb_encode_bf16_pertensor, which must read the histograms back.
+ *    lecb_encode_bf16_pertensor, which must read the histograms back: it
+ *    synchronises `stream` once and, on its first call in a host thread,
+ *    allocates a 4 KiB pinned host buffer that the thread keeps.
  *  - Return values: LECB_OK or a negative lecb_status detected on the host
  *    (bad argument, too small a buffer).  Problems only the GPU can see
  *    (a byte with no code word, a corrupt stream, output overflow) are

@@ -322,9 +322,15 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
     }
     int rc = lecb_histogram_bf16(d_in, n, d_hist, d_hist + 256, 0, stream);
     if (rc) return rc;
-    uint64_t h[512];
+    // the two histograms come back through a pinned buffer (one per host
+    // thread, allocated on first use and kept): a direct DMA, no staging copy
+    thread_local uint64_t* h = nullptr;
+    if (!h && hipHostMalloc(reinterpret_cast<void**>(&h), 512 * sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) {
+        h = nullptr;
+        return LECB_ERR_HIP;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (hipMemcpyAsync(h, d_hist, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+    if (hipMemcpyAsync(h, d_hist, 512 * sizeof(uint64_t), hipMemcpyDeviceToHost, s) != hipSuccess)
         return LECB_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return LECB_ERR_HIP;
     // d_hist[0:256] = high plane, d_hist[256:512] = low plane

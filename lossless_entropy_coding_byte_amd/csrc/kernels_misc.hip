@@ -54,7 +54,21 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u8_kernel(const uint8_t* __
     const uint64_t n16 = n / 16;
     const uint4* in4 = reinterpret_cast<const uint4*>(in);
     const uint64_t stride = (uint64_t)gridDim.x * HIST_THREADS;
-    for (uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x; i < n16; i += stride) {
+    // four 16-byte loads in flight per thread, then their 64 increments
+    uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        v4u v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ld_stream(&in4[i + q * stride]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hist_add<R>(s, v[q].x, r);
+            hist_add<R>(s, v[q].y, r);
+            hist_add<R>(s, v[q].z, r);
+            hist_add<R>(s, v[q].w, r);
+        }
+    }
+    for (; i < n16; i += stride) {
         const v4u v = ld_stream(&in4[i]);
         hist_add<R>(s, v.x, r);
         hist_add<R>(s, v.y, r);
@@ -85,8 +99,7 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
     const uint64_t n8 = n / 8;
     const uint4* in4 = reinterpret_cast<const uint4*>(in);
     const uint64_t stride = (uint64_t)gridDim.x * HIST_THREADS;
-    for (uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x; i < n8; i += stride) {
-        const v4u v = ld_stream(&in4[i]);
+    auto add8 = [&](const v4u& v) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -95,7 +108,17 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
             atomicAdd(&s_lo[((w[k] >> 16) & 0xFFu) * R + r], 1u);
             atomicAdd(&s_hi[(w[k] >> 24) * R + r], 1u);
         }
+    };
+    // four 16-byte loads in flight per thread, then their 64 increments
+    uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x;
+    for (; i + 3 * stride < n8; i += 4 * stride) {
+        v4u v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ld_stream(&in4[i + q * stride]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) add8(v[q]);
     }
+    for (; i < n8; i += stride) add8(ld_stream(&in4[i]));
     if (blockIdx.x == gridDim.x - 1) {
         for (uint64_t i = n8 * 8 + threadIdx.x; i < n; i += HIST_THREADS) {
             atomicAdd(&s_lo[(in[i] & 0xFFu) * R + r], 1u);
