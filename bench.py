@@ -379,6 +379,36 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
             "gap_vs_shannon_first_last": [round(float(gap_h[0]), 5), round(float(gap_h[-1]), 5)],
             "per_batch_ratio": [round(float(v), 4) for v in ratio],
         }
+        # the same batches through the refresh rule (lecb_encode_adaptive,
+        # tolerance 1 %): histogram, host decision, rebuild when needed, encode
+        tol = 10_000
+        cb_a = lecb.lecb_codebook_from_lengths(lengths_out[0])
+        cb_a.max_len = 16
+        blob_a = lecb.new_codebook_blob(dev)
+        lecb.lecb_codebook_upload(cb_a, blob_a)
+        hist_a = torch.zeros(256, dtype=torch.int64, device=dev)
+        out_a = torch.empty(lecb.lecb_encoded_bound(B, chunk), dtype=torch.uint8, device=dev)
+        res_a = lecb.new_results(1, dev)
+        ws_a = lecb.new_workspace(B, chunk, dev)
+        refreshes, bits_a, status_a = 0, 0, 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(cfg["batches"]):
+            refreshes += lecb.lecb_encode_adaptive(xd[k * B:(k + 1) * B], B, chunk, 16, tol, hist_a, cb_a,
+                                                   blob_a, out_a, res_a, ws_a)
+            ra = lecb.results_to_numpy(res_a)[0]
+            bits_a += int(ra["payload_bits"])
+            status_a |= int(ra["status"])
+        t_a = time.perf_counter() - t0
+        batches["adaptive"] = {
+            "rule": "refresh when the batch costs more than tol over its best fixed codebook",
+            "tol_ppm": tol, "refreshes": int(refreshes), "status": status_a,
+            "payload_ratio": round(8.0 * B * cfg["batches"] / bits_a, 4),
+            "payload_ratio_fixed": round(8.0 * B * cfg["batches"] / float(rows[:, 0].sum()), 4),
+            "payload_vs_fixed": round(bits_a / float(rows[:, 0].sum()) - 1, 5),
+            "payload_vs_per_batch_optimal": round(bits_a / float(rows[:, 1].sum()) - 1, 5),
+            "encode_GBps_with_decisions": round(B * cfg["batches"] / t_a / 1e9, 2),
+        }
     info.update(
         batches=batches,
         accounting=accounting,

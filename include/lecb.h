@@ -153,6 +153,21 @@ typedef struct {
 int lecb_stream_stats(const uint64_t hist[256], const uint8_t len[256], uint32_t max_len,
                       lecb_stats* out);
 
+/* Codebook refresh rule for a drifting stream in fixed-codebook mode.  The
+ * page ("Single-Stage Huffman Encoder for ML Compression", Limitations and
+ * future work, distribution drift) names adaptive refresh as open work; the
+ * rule here: the batch (host histogram `hist`) keeps `cur` unless
+ *     bits_cur * 10^6 > bits_opt * (10^6 + tol_ppm),
+ * with bits_cur = sum f[s]*len_cur[s] (infinite when a byte present in the
+ * batch has no code word in `cur`) and bits_opt the same sum for the best
+ * fixed codebook of the batch (lecb_build_codebook with min_freq 1 and
+ * max_len).  *out = that codebook when refreshing, else a copy of *cur (out
+ * may equal cur); *refreshed = 1 / 0; *bits_cur (UINT64_MAX when not
+ * codable) and *bits_opt when non-NULL.  Host only, no allocation. */
+int lecb_drift_check(const uint64_t hist[256], const lecb_codebook* cur, uint32_t max_len,
+                     uint32_t tol_ppm, lecb_codebook* out, int* refreshed, uint64_t* bits_cur,
+                     uint64_t* bits_opt);
+
 /* Size of the device-resident codebook (encode table + decode tables). */
 uint64_t lecb_device_codebook_bytes(void);
 
@@ -264,6 +279,19 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
                                uint8_t* d_out_hi, uint64_t cap_hi, uint8_t* d_out_lo,
                                uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
                                uint64_t ws_bytes, void* stream);
+
+/* Fixed-codebook encode of one batch of a drifting stream with the refresh
+ * rule of lecb_drift_check: histogram of the batch (device) -> read back
+ * (synchronises `stream` once; a 4 KiB pinned host buffer per host thread,
+ * allocated on first use) -> lecb_drift_check(tol_ppm) -> on refresh the new
+ * codebook is built on the host and uploaded into d_blob -> lecb_encode.
+ * cb (host) in: the codebook d_blob holds; out: the one this batch was coded
+ * with.  *refreshed = 1 when it changed.  d_hist: 256 u64 of device scratch.
+ * The stream decodes with lecb_decode and the codebook in *cb. */
+int lecb_encode_adaptive(const uint8_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,
+                         uint32_t tol_ppm, uint64_t* d_hist, lecb_codebook* cb, void* d_blob,
+                         int* refreshed, uint8_t* d_out, uint64_t cap, lecb_result* d_res,
+                         void* d_ws, uint64_t ws_bytes, void* stream);
 
 /* Decode both byte planes in ONE launch (the two streams' decode units run
  * side by side) into d_out_hi[n] and d_out_lo[n]; same rules as lecb_decode

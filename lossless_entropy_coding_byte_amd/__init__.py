@@ -83,6 +83,11 @@ _SIGNATURES = {
     "lecb_codebook_from_lengths": (_int, [_vp, ctypes.POINTER(lecb_codebook)]),
     "lecb_device_codebook_bytes": (_u64, []),
     "lecb_stream_stats": (_int, [_vp, _vp, _u32, ctypes.POINTER(lecb_stats)]),
+    "lecb_drift_check": (_int, [_vp, ctypes.POINTER(lecb_codebook), _u32, _u32,
+                                ctypes.POINTER(lecb_codebook), ctypes.POINTER(_int),
+                                ctypes.POINTER(_u64), ctypes.POINTER(_u64)]),
+    "lecb_encode_adaptive": (_int, [_vp, _u64, _u32, _u32, _u32, _vp, ctypes.POINTER(lecb_codebook),
+                                    _vp, ctypes.POINTER(_int), _vp, _u64, _vp, _vp, _u64, _vp]),
     "lecb_container_write_header": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _u64, _u64]),
     "lecb_container_read_header": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lecb_workspace_init": (_int, [_vp, _u64, _vp]),
@@ -212,6 +217,20 @@ def lecb_stream_stats(hist, lengths, max_len: int = 16) -> dict:
     return st.as_dict()
 
 
+def lecb_drift_check(hist, cur: lecb_codebook, max_len: int = 16, tol_ppm: int = 0):
+    """Refresh decision for one batch: (refreshed, codebook to use, bits_cur or None, bits_opt)."""
+    h = np.ascontiguousarray(np.asarray(hist, dtype=np.uint64))
+    if h.shape != (256,):
+        raise ValueError("histogram must have 256 bins")
+    out = lecb_codebook()
+    ref = _int(0)
+    bc, bo = _u64(0), _u64(0)
+    _check(load().lecb_drift_check(h.ctypes.data, ctypes.byref(cur), max_len, tol_ppm, ctypes.byref(out),
+                                   ctypes.byref(ref), ctypes.byref(bc), ctypes.byref(bo)),
+           "lecb_drift_check")
+    return bool(ref.value), out, (None if bc.value == 2**64 - 1 else int(bc.value)), int(bo.value)
+
+
 def lecb_container_write_header(n, chunk, max_len, len_hi, len_lo, bytes_hi, bytes_lo) -> np.ndarray:
     out = np.zeros(CONTAINER_HEADER_BYTES, np.uint8)
     hi = np.ascontiguousarray(len_hi, dtype=np.uint8)
@@ -331,6 +350,17 @@ def lecb_encode_bf16_pertensor(x, n, chunk, max_len, hist, blob_hi, blob_lo, out
         _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
         "lecb_encode_bf16_pertensor")
     return cb_hi, cb_lo
+
+
+def lecb_encode_adaptive(x, n, chunk, max_len, tol_ppm, hist, cb: lecb_codebook, blob, out, res, ws,
+                         stream=None) -> bool:
+    """One batch of a drifting stream; cb is updated in place.  Returns whether it was refreshed."""
+    ref = _int(0)
+    _check(load().lecb_encode_adaptive(_ptr(x), n, chunk, max_len, tol_ppm, _ptr(hist), ctypes.byref(cb),
+                                       _ptr(blob), ctypes.byref(ref), _ptr(out), out.numel(), _ptr(res),
+                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_encode_adaptive")
+    return bool(ref.value)
 
 
 def lecb_decode_bf16(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, out, scratch, res2, ws,

@@ -15,6 +15,24 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Histograms come back through a pinned buffer (one per host thread, 4 KiB,
+// allocated on first use and kept): a direct DMA, no staging copy.  Waits for
+// `stream`.
+int read_back_hist(const uint64_t* d_hist, int count, void* stream, const uint64_t** host) {
+    thread_local uint64_t* h = nullptr;
+    if (count > 512) return LECB_ERR_INVALID_ARG;
+    if (!h && hipHostMalloc(reinterpret_cast<void**>(&h), 512 * sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) {
+        h = nullptr;
+        return LECB_ERR_HIP;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(h, d_hist, count * sizeof(uint64_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return LECB_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return LECB_ERR_HIP;
+    *host = h;
+    return LECB_OK;
+}
+
 // Encode workgroups launched per compute unit (persistent grid).  0: as many
 // as fit on a compute unit at once (asked of the runtime per kernel);
 // LECB_ENCODE_WGS_PER_CU overrides it for launch-shape sweeps.
@@ -322,17 +340,9 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
     }
     int rc = lecb_histogram_bf16(d_in, n, d_hist, d_hist + 256, 0, stream);
     if (rc) return rc;
-    // the two histograms come back through a pinned buffer (one per host
-    // thread, allocated on first use and kept): a direct DMA, no staging copy
-    thread_local uint64_t* h = nullptr;
-    if (!h && hipHostMalloc(reinterpret_cast<void**>(&h), 512 * sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) {
-        h = nullptr;
-        return LECB_ERR_HIP;
-    }
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (hipMemcpyAsync(h, d_hist, 512 * sizeof(uint64_t), hipMemcpyDeviceToHost, s) != hipSuccess)
-        return LECB_ERR_HIP;
-    if (hipStreamSynchronize(s) != hipSuccess) return LECB_ERR_HIP;
+    const uint64_t* h = nullptr;
+    rc = read_back_hist(d_hist, 512, stream, &h);
+    if (rc) return rc;
     // d_hist[0:256] = high plane, d_hist[256:512] = low plane
     rc = lecb_build_codebook(h, max_len, 0, cb_hi);
     if (!rc) rc = lecb_build_codebook(h + 256, max_len, 0, cb_lo);
@@ -342,6 +352,29 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
         rc = lecb_encode_bf16(d_in, n, d_blob_hi, d_blob_lo, chunk, d_out_hi, cap_hi, d_out_lo,
                               cap_lo, d_res2, d_ws, ws_bytes, stream);
     return rc;
+}
+
+int lecb_encode_adaptive(const uint8_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,
+                         uint32_t tol_ppm, uint64_t* d_hist, lecb_codebook* cb, void* d_blob,
+                         int* refreshed, uint8_t* d_out, uint64_t cap, lecb_result* d_res,
+                         void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) || !cb ||
+        !refreshed || !d_res)
+        return LECB_ERR_INVALID_ARG;
+    *refreshed = 0;
+    if (n == 0) return launch_result(d_res, 0, 0, LECB_OK, stream);
+    int rc = lecb_histogram(d_in, n, d_hist, 0, stream);
+    if (rc) return rc;
+    const uint64_t* h = nullptr;
+    rc = read_back_hist(d_hist, 256, stream, &h);
+    if (rc) return rc;
+    rc = lecb_drift_check(h, cb, max_len, tol_ppm, cb, refreshed, nullptr, nullptr);
+    if (rc) return rc;
+    if (*refreshed) {
+        rc = lecb_codebook_upload(cb, d_blob, stream);
+        if (rc) return rc;
+    }
+    return lecb_encode(d_in, n, d_blob, chunk, d_out, cap, d_res, d_ws, ws_bytes, stream);
 }
 
 int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,

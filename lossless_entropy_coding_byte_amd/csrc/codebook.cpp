@@ -44,38 +44,48 @@ int build_lengths(const uint64_t freq_in[256], uint32_t max_len, uint32_t min_fr
     if ((uint64_t)m > (1ull << max_len)) return LECB_ERR_NO_SYMBOLS;
     std::stable_sort(order, order + m, [&](int a, int b) { return freq[a] < freq[b]; });
 
-    // levels[k] = merged order at level k: true = package, false = coin.
+    // is_pkg[k][i]: item i of level k's merged order is a package (else a
+    // coin).  A level holds m coins and at most m - 1 packages.
     const int L = (int)max_len;
-    std::vector<std::vector<uint8_t>> is_pkg(L);
-    std::vector<uint64_t> cur_w(m), next_w;
-    for (int i = 0; i < m; ++i) cur_w[i] = freq[order[i]];
-    is_pkg[0].assign(m, 0);
+    static thread_local uint8_t is_pkg[16][512];
+    static thread_local uint64_t wbuf[2][512];
+    int len_at[16];
+    uint64_t* cur_w = wbuf[0];
+    uint64_t* next_w = wbuf[1];
+    uint64_t coin_w[256];
+    for (int i = 0; i < m; ++i) coin_w[i] = freq[order[i]];
+    int cur_n = m;
+    for (int i = 0; i < m; ++i) {
+        cur_w[i] = coin_w[i];
+        is_pkg[0][i] = 0;
+    }
+    len_at[0] = m;
     for (int k = 1; k < L; ++k) {
-        const size_t np = cur_w.size() / 2;
-        next_w.clear();
-        is_pkg[k].clear();
-        size_t ic = 0, ip = 0;
+        const int np = cur_n / 2;
+        int ic = 0, ip = 0, o = 0;
         // package weights are formed on the fly from consecutive pairs of cur_w
-        while (ic < (size_t)m || ip < np) {
+        while (ic < m || ip < np) {
             const uint64_t pw = ip < np ? cur_w[2 * ip] + cur_w[2 * ip + 1] : 0;
-            const bool take_coin = ip == np || (ic < (size_t)m && freq[order[ic]] <= pw);
+            const bool take_coin = ip == np || (ic < m && coin_w[ic] <= pw);
             if (take_coin) {
-                next_w.push_back(freq[order[ic++]]);
-                is_pkg[k].push_back(0);
+                next_w[o] = coin_w[ic++];
+                is_pkg[k][o++] = 0;
             } else {
-                next_w.push_back(pw);
-                is_pkg[k].push_back(1);
+                next_w[o] = pw;
+                is_pkg[k][o++] = 1;
                 ++ip;
             }
         }
-        cur_w.swap(next_w);
+        len_at[k] = o;
+        cur_n = o;
+        std::swap(cur_w, next_w);
     }
 
     // Walk down from the top level: take the first `take` items of each level.
     size_t take = 2 * (size_t)m - 2;
     int coins_at[16] = {0};
     for (int k = L - 1; k >= 0; --k) {
-        if (take > is_pkg[k].size()) return LECB_ERR_NO_SYMBOLS;  // cannot happen when m <= 2^L
+        if (take > (size_t)len_at[k]) return LECB_ERR_NO_SYMBOLS;  // cannot happen when m <= 2^L
         size_t a = 0, p = 0;
         for (size_t i = 0; i < take; ++i) (is_pkg[k][i] ? p : a) += 1;
         coins_at[k] = (int)a;
@@ -141,6 +151,40 @@ int lecb_build_codebook(const uint64_t hist[256], uint32_t max_len, uint32_t min
 
 int lecb_codebook_from_lengths(const uint8_t len[256], lecb_codebook* out) {
     return lecb::canonical_from_lengths(len, out);
+}
+
+// Refresh rule for a drifting stream ("Single-Stage Huffman Encoder for ML
+// Compression", Limitations and future work: distribution drift; the page
+// leaves the rule open).  The batch keeps the current codebook unless its
+// payload bits under it exceed, by more than tol_ppm, those of the best fixed
+// codebook for the batch: package-merge on the batch histogram clamped to
+// frequency >= 1 (built like every fixed codebook).  Integer decision:
+// bits_cur * 10^6 > bits_opt * (10^6 + tol_ppm).
+int lecb_drift_check(const uint64_t hist[256], const lecb_codebook* cur, uint32_t max_len,
+                     uint32_t tol_ppm, lecb_codebook* out, int* refreshed, uint64_t* bits_cur,
+                     uint64_t* bits_opt) {
+    if (!hist || !cur || !out || !refreshed || max_len < 1 || max_len > 16) return LECB_ERR_INVALID_ARG;
+    lecb_codebook best;
+    const int rc = lecb_build_codebook(hist, max_len, 1, &best);
+    if (rc != LECB_OK) return rc;
+    unsigned __int128 bc = 0, bo = 0;
+    bool codable = true;
+    for (int s = 0; s < 256; ++s) {
+        if (hist[s] && !cur->len[s]) codable = false;
+        bc += (unsigned __int128)hist[s] * cur->len[s];
+        bo += (unsigned __int128)hist[s] * best.len[s];
+    }
+    const bool refresh =
+        !codable || bc * 1000000u > bo * (unsigned __int128)(1000000ull + tol_ppm);
+    if (refresh) {
+        *out = best;
+    } else if (out != cur) {
+        *out = *cur;
+    }
+    *refreshed = refresh ? 1 : 0;
+    if (bits_cur) *bits_cur = codable ? (uint64_t)bc : UINT64_MAX;
+    if (bits_opt) *bits_opt = (uint64_t)bo;
+    return LECB_OK;
 }
 
 int lecb_stream_stats(const uint64_t hist[256], const uint8_t len[256], uint32_t max_len,

@@ -10,7 +10,8 @@ step on the coding path:
                    (bit-by-bit canonical and lock-step lookup table);
 * ``bytegroup`` -- bf16 byte grouping (high / low byte planes) and the
                    two-stream container;
-* ``metrics``   -- entropy, compressed-size identities and per-batch optimum.
+* ``metrics``   -- entropy, compressed-size identities and per-batch optimum;
+* ``drift``     -- the codebook refresh rule under distribution drift.
 
 Sources: "Single-Stage Huffman Encoder for ML Compression" (summary page of
 arXiv 2601.10673; sections Overview and Methodology) and "Lossless Compression
@@ -57,6 +58,7 @@ from .stream import (
 )
 from .bytegroup import split_bf16, merge_bf16, encode_bf16, decode_bf16, container_bytes, parse_container
 from .metrics import entropy_bits, payload_bits_identity, per_batch_optimal_bits
+from .drift import payload_bits_or_none, drift_check, adaptive_codebooks
 
 __all__ = [
     "histogram", "codebook_frequencies", "package_merge_lengths", "canonical_codes",

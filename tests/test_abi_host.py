@@ -135,3 +135,36 @@ def test_stream_stats_match_oracle():
     ln2 = ln.copy()
     ln2[int(np.argmax(h))] = 0
     assert lecb.lecb_stream_stats(h, ln2, 16)["uncoded"] == int(h.max())
+
+
+def test_drift_check_matches_oracle():
+    """The C refresh rule takes the oracle's decision, bits and lengths on a
+    drifting sequence of int8 batches and on hand-made edge cases."""
+    rng = np.random.default_rng(11)
+    hists = []
+    for k in range(10):
+        x = np.clip(np.rint(rng.normal(0, 6 + 5 * k, 40_000)), -128, 127).astype(np.int8).view(np.uint8)
+        hists.append(oracle.histogram(x))
+    first = oracle.package_merge_lengths(oracle.codebook_frequencies(hists[:1], 1), 16)
+    for tol in (0, 5_000, 50_000, 10**9):
+        cur_o = first
+        cur_c = lecb.lecb_codebook_from_lengths(first)
+        cur_c.max_len = 16
+        for h in hists:
+            r_o, use_o, bc_o, bo_o = oracle.drift_check(h, cur_o, 16, tol)
+            r_c, use_c, bc_c, bo_c = lecb.lecb_drift_check(h, cur_c, 16, tol)
+            assert (r_c, bc_c, bo_c) == (r_o, bc_o, bo_o)
+            assert np.array_equal(use_c.lengths(), use_o)
+            cur_o, cur_c = use_o, use_c
+    # uncodable byte
+    cur = np.full(256, 8, np.uint8)
+    cur[5], cur[6] = 0, 7
+    h = np.full(256, 3, np.uint64)
+    r, use, bc, bo = lecb.lecb_drift_check(h, lecb.lecb_codebook_from_lengths(cur), 16, 10**9)
+    assert r and bc is None and use.lengths()[5] > 0
+    # exact boundary: a dominant byte against an all-8-bit code costs 8x the optimum
+    h = np.zeros(256, np.uint64)
+    h[0] = 10_000
+    u8 = lecb.lecb_codebook_from_lengths(np.full(256, 8, np.uint8))
+    assert lecb.lecb_drift_check(h, u8, 16, 6_999_999)[0]
+    assert not lecb.lecb_drift_check(h, u8, 16, 7_000_000)[0]

@@ -295,6 +295,44 @@ def test_bf16_pertensor_pipeline(n, chunk):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
 
 
+# ----------------------------------------------------------------------------- drift refresh
+
+@pytest.mark.parametrize("tol", [0, 20_000, 10**9])
+def test_adaptive_encode_over_drifting_batches(tol):
+    """lecb_encode_adaptive over batches whose spread grows: the refresh
+    decisions are the oracle's, every batch's stream is bit-exact to the
+    oracle's with the codebook it chose, and it decodes back."""
+    _say(f"adaptive encode tol={tol}")
+    rng = np.random.default_rng(21)
+    n, chunk = 200_003, 4096
+    batches = [np.clip(np.rint(rng.normal(0, 8 + 6 * k, n)), -128, 127).astype(np.int8).view(np.uint8)
+               for k in range(6)]
+    hists = [oracle.histogram(b) for b in batches]
+    first = oracle.package_merge_lengths(oracle.codebook_frequencies(hists[:1], 1), 16)
+    want = oracle.adaptive_codebooks(hists, first, 16, tol)
+    cb = lecb.lecb_codebook_from_lengths(first)
+    cb.max_len = 16
+    blob = lecb.new_codebook_blob(DEV)
+    lecb.lecb_codebook_upload(cb, blob)
+    hist = torch.zeros(256, dtype=torch.int64, device=DEV)
+    out = torch.empty(lecb.lecb_encoded_bound(n, chunk), dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(1, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    y = torch.empty(n, dtype=torch.uint8, device=DEV)
+    rd = lecb.new_results(1, DEV)
+    for b, (r_o, use_o, _, _) in zip(batches, want):
+        refreshed = lecb.lecb_encode_adaptive(to_dev(b), n, chunk, 16, tol, hist, cb, blob, out, res, ws)
+        assert refreshed == r_o
+        assert np.array_equal(cb.lengths(), use_o)
+        rr = lecb.results_to_numpy(res)[0]
+        assert int(rr["status"]) == 0
+        ref, _ = oracle.encode(b, use_o, oracle.canonical_codes(use_o), chunk)
+        assert np.array_equal(out[: int(rr["bytes"])].cpu().numpy(), ref)
+        lecb.lecb_decode_from_result(out, res, blob, chunk, n, y, rd, ws)
+        assert int(lecb.results_to_numpy(rd)[0]["status"]) == 0
+        assert np.array_equal(y.cpu().numpy(), b)
+
+
 # ----------------------------------------------------------------------------- decode workgroup sizes
 
 @pytest.mark.parametrize("nt", [256, 512, 1024])
