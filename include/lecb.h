@@ -280,6 +280,53 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
                                uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
                                uint64_t ws_bytes, void* stream);
 
+/* ---- incremental snapshot delta, fused ("Lossless Compression for LLM
+ * Tensor Incremental Snapshots", Technical framework: the delta of two
+ * consecutive checkpoints is byte-grouped and Huffman-coded; the delta here is
+ * the bitwise XOR of the two bf16 tensors, D[i] = W0[i] ^ W1[i]).  These
+ * entries read W0 and W1 (or W0 and the streams) directly, so D is never
+ * written to memory: the streams are those of the entries above applied to
+ * D, and the decode writes W1 = W0 ^ D.  Arguments as for the bf16 entries
+ * above, plus d_w0 / d_w1 (n u16 each, 16-byte aligned). */
+
+/* Histograms of the two byte planes of W0 ^ W1. */
+int lecb_histogram_bf16_delta(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                              uint64_t* d_hist_hi, uint64_t* d_hist_lo, int accumulate,
+                              void* stream);
+
+/* lecb_encode_bf16 of W0 ^ W1 (both planes in one pass, fixed codebooks). */
+int lecb_encode_bf16_delta(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                           const void* d_blob_hi, const void* d_blob_lo, uint32_t chunk,
+                           uint8_t* d_out_hi, uint64_t cap_hi, uint8_t* d_out_lo, uint64_t cap_lo,
+                           lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* lecb_encode_bf16_pertensor of W0 ^ W1 (per-tensor codebooks of the delta
+ * planes; synchronises `stream` once, like lecb_encode_bf16_pertensor). */
+int lecb_encode_bf16_delta_pertensor(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                                     uint32_t chunk, uint32_t max_len, uint64_t* d_hist,
+                                     void* d_blob_hi, void* d_blob_lo, lecb_codebook* cb_hi,
+                                     lecb_codebook* cb_lo, uint8_t* d_out_hi, uint64_t cap_hi,
+                                     uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2,
+                                     void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* Decode both delta planes (one launch) and write W1 = W0 ^ (hi << 8 | lo).
+ * d_scratch: 2*align16(n) bytes for the planes.  d_w1 may not alias d_w0. */
+int lecb_decode_bf16_delta(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
+                           uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
+                           uint32_t chunk, uint64_t n, const uint16_t* d_w0, uint16_t* d_w1,
+                           uint8_t* d_scratch, lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
+                           void* stream);
+
+/* As lecb_decode_bf16_delta, with the stream sizes read on the device from
+ * the encoder's two results (d_enc_res2), so encode -> decode needs no host
+ * synchronisation. */
+int lecb_decode_bf16_delta_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
+                                        const lecb_result* d_enc_res2, const void* d_blob_hi,
+                                        const void* d_blob_lo, uint32_t chunk, uint64_t n,
+                                        const uint16_t* d_w0, uint16_t* d_w1, uint8_t* d_scratch,
+                                        lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
+                                        void* stream);
+
 /* Fixed-codebook encode of one batch of a drifting stream with the refresh
  * rule of lecb_drift_check: histogram of the batch (device) -> read back
  * (synchronises `stream` once; a 4 KiB pinned host buffer per host thread,

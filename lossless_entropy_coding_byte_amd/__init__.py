@@ -83,6 +83,15 @@ _SIGNATURES = {
     "lecb_codebook_from_lengths": (_int, [_vp, ctypes.POINTER(lecb_codebook)]),
     "lecb_device_codebook_bytes": (_u64, []),
     "lecb_stream_stats": (_int, [_vp, _vp, _u32, ctypes.POINTER(lecb_stats)]),
+    "lecb_histogram_bf16_delta": (_int, [_vp, _vp, _u64, _vp, _vp, _int, _vp]),
+    "lecb_encode_bf16_delta": (_int, [_vp, _vp, _u64, _vp, _vp, _u32, _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lecb_encode_bf16_delta_pertensor": (_int, [_vp, _vp, _u64, _u32, _u32, _vp, _vp, _vp,
+                                                ctypes.POINTER(lecb_codebook), ctypes.POINTER(lecb_codebook),
+                                                _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lecb_decode_bf16_delta": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _vp,
+                                      _u64, _vp]),
+    "lecb_decode_bf16_delta_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp,
+                                                   _vp, _u64, _vp]),
     "lecb_drift_check": (_int, [_vp, ctypes.POINTER(lecb_codebook), _u32, _u32,
                                 ctypes.POINTER(lecb_codebook), ctypes.POINTER(_int),
                                 ctypes.POINTER(_u64), ctypes.POINTER(_u64)]),
@@ -350,6 +359,46 @@ def lecb_encode_bf16_pertensor(x, n, chunk, max_len, hist, blob_hi, blob_lo, out
         _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
         "lecb_encode_bf16_pertensor")
     return cb_hi, cb_lo
+
+
+def lecb_histogram_bf16_delta(w0, w1, hist_hi, hist_lo, accumulate: bool = False, stream=None) -> None:
+    """Histograms of the byte planes of w0 ^ w1."""
+    _check(load().lecb_histogram_bf16_delta(_ptr(w0), _ptr(w1), w0.numel(), _ptr(hist_hi), _ptr(hist_lo),
+                                            int(accumulate), _stream(stream)), "lecb_histogram_bf16_delta")
+
+
+def lecb_encode_bf16_delta(w0, w1, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res2, ws, stream=None) -> None:
+    _check(load().lecb_encode_bf16_delta(_ptr(w0), _ptr(w1), n, _ptr(blob_hi), _ptr(blob_lo), chunk,
+                                         _ptr(out_hi), out_hi.numel(), _ptr(out_lo), out_lo.numel(),
+                                         _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)), "lecb_encode_bf16_delta")
+
+
+def lecb_encode_bf16_delta_pertensor(w0, w1, n, chunk, max_len, hist, blob_hi, blob_lo, out_hi, out_lo,
+                                     res2, ws, stream=None):
+    cb_hi, cb_lo = lecb_codebook(), lecb_codebook()
+    _check(load().lecb_encode_bf16_delta_pertensor(
+        _ptr(w0), _ptr(w1), n, chunk, max_len, _ptr(hist), _ptr(blob_hi), _ptr(blob_lo), ctypes.byref(cb_hi),
+        ctypes.byref(cb_lo), _ptr(out_hi), out_hi.numel(), _ptr(out_lo), out_lo.numel(),
+        _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lecb_encode_bf16_delta_pertensor")
+    return cb_hi, cb_lo
+
+
+def lecb_decode_bf16_delta(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, w0, w1, scratch, res2,
+                           ws, stream=None) -> None:
+    _check(load().lecb_decode_bf16_delta(_ptr(hi), hi_bytes, _ptr(lo), lo_bytes, _ptr(blob_hi),
+                                         _ptr(blob_lo), chunk, n, _ptr(w0), _ptr(w1), _ptr(scratch),
+                                         _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)), "lecb_decode_bf16_delta")
+
+
+def lecb_decode_bf16_delta_from_results(hi, lo, enc_res2, blob_hi, blob_lo, chunk, n, w0, w1, scratch,
+                                        res2, ws, stream=None) -> None:
+    _check(load().lecb_decode_bf16_delta_from_results(
+        _ptr(hi), _ptr(lo), _ptr(enc_res2), _ptr(blob_hi), _ptr(blob_lo), chunk, n, _ptr(w0), _ptr(w1),
+        _ptr(scratch), _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lecb_decode_bf16_delta_from_results")
 
 
 def lecb_encode_adaptive(x, n, chunk, max_len, tol_ppm, hist, cb: lecb_codebook, blob, out, res, ws,

@@ -87,8 +87,9 @@ int build_args(const lecb_codebook* cb, CodebookArgs* a) {
 int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, uint32_t chunk,
                   uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
                   uint64_t ws_bytes, void* stream, const void* d_blob2 = nullptr,
-                  uint8_t* d_out2 = nullptr, uint64_t out_capacity2 = 0) {
-    const bool pair = mode == ENC_PAIR;
+                  uint8_t* d_out2 = nullptr, uint64_t out_capacity2 = 0, const void* d_in2 = nullptr) {
+    const bool pair = mode == ENC_PAIR || mode == ENC_PAIR_XOR;
+    if (mode == ENC_PAIR_XOR && n && (!d_in2 || !aligned16(d_in2))) return LECB_ERR_INVALID_ARG;
     if (!valid_chunk(chunk) || !d_res || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
     if (pair && (!d_blob2 || !aligned16(d_blob2))) return LECB_ERR_INVALID_ARG;
     if (n == 0) {
@@ -104,6 +105,7 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
     if (pair && out_capacity2 < header_of(n, chunk)) return LECB_ERR_CAPACITY;
     EncodeLaunch L{};
     L.in = d_in;
+    L.in2 = d_in2;
     L.mode = mode;
     L.n = n;
     L.chunk = chunk;
@@ -170,6 +172,41 @@ int decode_common(int ns, const uint8_t* const* d_stream, const uint64_t* stream
 
 }  // namespace
 
+// Per-tensor two-plane encode of d_in (d_in2 == nullptr) or of d_in ^ d_in2.
+static int pertensor_common(const uint16_t* d_in, const uint16_t* d_in2, uint64_t n, uint32_t chunk,
+                               uint32_t max_len, uint64_t* d_hist, void* d_blob_hi,
+                               void* d_blob_lo, lecb_codebook* cb_hi, lecb_codebook* cb_lo,
+                               uint8_t* d_out_hi, uint64_t cap_hi, uint8_t* d_out_lo,
+                               uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
+                               uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) ||
+        !cb_hi || !cb_lo || !d_res2)
+        return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        std::memset(cb_hi, 0, sizeof(*cb_hi));
+        std::memset(cb_lo, 0, sizeof(*cb_lo));
+        int rc = launch_result(d_res2, 0, 0, LECB_OK, stream);
+        return rc ? rc : launch_result(d_res2 + 1, 0, 0, LECB_OK, stream);
+    }
+    int rc = d_in2 ? lecb_histogram_bf16_delta(d_in, d_in2, n, d_hist, d_hist + 256, 0, stream)
+                   : lecb_histogram_bf16(d_in, n, d_hist, d_hist + 256, 0, stream);
+    if (rc) return rc;
+    const uint64_t* h = nullptr;
+    rc = read_back_hist(d_hist, 512, stream, &h);
+    if (rc) return rc;
+    // d_hist[0:256] = high plane, d_hist[256:512] = low plane
+    rc = lecb_build_codebook(h, max_len, 0, cb_hi);
+    if (!rc) rc = lecb_build_codebook(h + 256, max_len, 0, cb_lo);
+    if (!rc) rc = lecb_codebook_upload(cb_hi, d_blob_hi, stream);
+    if (!rc) rc = lecb_codebook_upload(cb_lo, d_blob_lo, stream);
+    if (!rc)
+        rc = d_in2 ? lecb_encode_bf16_delta(d_in, d_in2, n, d_blob_hi, d_blob_lo, chunk, d_out_hi,
+                                            cap_hi, d_out_lo, cap_lo, d_res2, d_ws, ws_bytes, stream)
+                   : lecb_encode_bf16(d_in, n, d_blob_hi, d_blob_lo, chunk, d_out_hi, cap_hi, d_out_lo,
+                                      cap_lo, d_res2, d_ws, ws_bytes, stream);
+    return rc;
+}
+
 extern "C" {
 
 uint32_t lecb_abi_version(void) { return LECB_ABI_VERSION; }
@@ -231,7 +268,7 @@ int lecb_histogram_bf16(const uint16_t* d_in, uint64_t n, uint64_t* d_hist_hi,
     if (!d_hist_hi || !d_hist_lo || !aligned16(d_hist_hi) || !aligned16(d_hist_lo) ||
         (n && (!d_in || !aligned16(d_in))))
         return LECB_ERR_INVALID_ARG;
-    return launch_histogram_u16(d_in, n, d_hist_hi, d_hist_lo, accumulate, stream);
+    return launch_histogram_u16(d_in, nullptr, n, d_hist_hi, d_hist_lo, accumulate, stream);
 }
 
 int lecb_split_bf16(const uint16_t* d_in, uint64_t n, uint8_t* d_hi, uint8_t* d_lo,
@@ -245,7 +282,7 @@ int lecb_merge_bf16(const uint8_t* d_hi, const uint8_t* d_lo, uint64_t n, uint16
                     void* stream) {
     if (n && (!d_out || !d_hi || !d_lo || !aligned16(d_out) || !aligned16(d_hi) || !aligned16(d_lo)))
         return LECB_ERR_INVALID_ARG;
-    return launch_merge(d_hi, d_lo, n, d_out, stream);
+    return launch_merge(d_hi, d_lo, nullptr, n, d_out, stream);
 }
 
 int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t chunk,
@@ -312,6 +349,44 @@ int lecb_decode_bf16_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
     return rc;
 }
 
+int lecb_decode_bf16_delta_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
+                                        const lecb_result* d_enc_res2, const void* d_blob_hi,
+                                        const void* d_blob_lo, uint32_t chunk, uint64_t n,
+                                        const uint16_t* d_w0, uint16_t* d_w1, uint8_t* d_scratch,
+                                        lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
+                                        void* stream) {
+    if (!d_res2 || !d_enc_res2) return LECB_ERR_INVALID_ARG;
+    if (n && (!d_scratch || !aligned16(d_scratch) || !d_w1 || !aligned16(d_w1) || !d_w0 ||
+              !aligned16(d_w0)))
+        return LECB_ERR_INVALID_ARG;
+    uint8_t* hi = d_scratch;
+    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
+    const uint8_t* st[2] = {d_hi, d_lo};
+    const uint64_t sb[2] = {0, 0};
+    const void* bl[2] = {d_blob_hi, d_blob_lo};
+    uint8_t* out[2] = {hi, lo};
+    int rc = decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream, d_enc_res2);
+    if (!rc && n) rc = launch_merge(hi, lo, d_w0, n, d_w1, stream);
+    return rc;
+}
+
+int lecb_decode_bf16_delta(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
+                           uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
+                           uint32_t chunk, uint64_t n, const uint16_t* d_w0, uint16_t* d_w1,
+                           uint8_t* d_scratch, lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
+                           void* stream) {
+    if (!d_res2) return LECB_ERR_INVALID_ARG;
+    if (n && (!d_scratch || !aligned16(d_scratch) || !d_w1 || !aligned16(d_w1) || !d_w0 ||
+              !aligned16(d_w0)))
+        return LECB_ERR_INVALID_ARG;
+    uint8_t* hi = d_scratch;
+    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
+    int rc = lecb_decode_bf16_planes(d_hi, hi_bytes, d_lo, lo_bytes, d_blob_hi, d_blob_lo, chunk, n,
+                                     hi, lo, d_res2, d_ws, ws_bytes, stream);
+    if (!rc && n) rc = launch_merge(hi, lo, d_w0, n, d_w1, stream);
+    return rc;
+}
+
 int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
                             uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
                             uint32_t chunk, uint64_t n, uint8_t* d_out_hi, uint8_t* d_out_lo,
@@ -329,29 +404,36 @@ int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
                                uint8_t* d_out_hi, uint64_t cap_hi, uint8_t* d_out_lo,
                                uint64_t cap_lo, lecb_result* d_res2, void* d_ws,
                                uint64_t ws_bytes, void* stream) {
-    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) ||
-        !cb_hi || !cb_lo || !d_res2)
+    return pertensor_common(d_in, nullptr, n, chunk, max_len, d_hist, d_blob_hi, d_blob_lo, cb_hi,
+                            cb_lo, d_out_hi, cap_hi, d_out_lo, cap_lo, d_res2, d_ws, ws_bytes, stream);
+}
+
+int lecb_histogram_bf16_delta(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                              uint64_t* d_hist_hi, uint64_t* d_hist_lo, int accumulate,
+                              void* stream) {
+    if (!d_hist_hi || !d_hist_lo || !aligned16(d_hist_hi) || !aligned16(d_hist_lo) ||
+        (n && (!d_w0 || !d_w1 || !aligned16(d_w0) || !aligned16(d_w1))))
         return LECB_ERR_INVALID_ARG;
-    if (n == 0) {
-        std::memset(cb_hi, 0, sizeof(*cb_hi));
-        std::memset(cb_lo, 0, sizeof(*cb_lo));
-        int rc = launch_result(d_res2, 0, 0, LECB_OK, stream);
-        return rc ? rc : launch_result(d_res2 + 1, 0, 0, LECB_OK, stream);
-    }
-    int rc = lecb_histogram_bf16(d_in, n, d_hist, d_hist + 256, 0, stream);
-    if (rc) return rc;
-    const uint64_t* h = nullptr;
-    rc = read_back_hist(d_hist, 512, stream, &h);
-    if (rc) return rc;
-    // d_hist[0:256] = high plane, d_hist[256:512] = low plane
-    rc = lecb_build_codebook(h, max_len, 0, cb_hi);
-    if (!rc) rc = lecb_build_codebook(h + 256, max_len, 0, cb_lo);
-    if (!rc) rc = lecb_codebook_upload(cb_hi, d_blob_hi, stream);
-    if (!rc) rc = lecb_codebook_upload(cb_lo, d_blob_lo, stream);
-    if (!rc)
-        rc = lecb_encode_bf16(d_in, n, d_blob_hi, d_blob_lo, chunk, d_out_hi, cap_hi, d_out_lo,
-                              cap_lo, d_res2, d_ws, ws_bytes, stream);
-    return rc;
+    return launch_histogram_u16(d_w0, d_w1, n, d_hist_hi, d_hist_lo, accumulate, stream);
+}
+
+int lecb_encode_bf16_delta(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                           const void* d_blob_hi, const void* d_blob_lo, uint32_t chunk,
+                           uint8_t* d_out_hi, uint64_t cap_hi, uint8_t* d_out_lo, uint64_t cap_lo,
+                           lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream) {
+    return encode_common(d_w0, ENC_PAIR_XOR, n, d_blob_hi, chunk, d_out_hi, cap_hi, d_res2, d_ws,
+                         ws_bytes, stream, d_blob_lo, d_out_lo, cap_lo, d_w1);
+}
+
+int lecb_encode_bf16_delta_pertensor(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                                     uint32_t chunk, uint32_t max_len, uint64_t* d_hist,
+                                     void* d_blob_hi, void* d_blob_lo, lecb_codebook* cb_hi,
+                                     lecb_codebook* cb_lo, uint8_t* d_out_hi, uint64_t cap_hi,
+                                     uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2,
+                                     void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (n && !d_w1) return LECB_ERR_INVALID_ARG;
+    return pertensor_common(d_w0, d_w1, n, chunk, max_len, d_hist, d_blob_hi, d_blob_lo, cb_hi,
+                            cb_lo, d_out_hi, cap_hi, d_out_lo, cap_lo, d_res2, d_ws, ws_bytes, stream);
 }
 
 int lecb_encode_adaptive(const uint8_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,

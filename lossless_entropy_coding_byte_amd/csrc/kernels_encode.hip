@@ -68,6 +68,7 @@ struct StreamArgs {
 
 struct EncArgs {
     const void* in;
+    const void* in2;     // ENC_PAIR_XOR: symbols are the planes of in[i] ^ in2[i]
     uint64_t n;
     uint32_t chunk;
     uint32_t log2k;
@@ -78,7 +79,8 @@ struct EncArgs {
     StreamArgs st[2];
 };
 
-template <int MODE> struct Streams { static constexpr int value = MODE == ENC_PAIR ? 2 : 1; };
+constexpr bool pair_mode(int m) { return m == ENC_PAIR || m == ENC_PAIR_XOR; }
+template <int MODE> struct Streams { static constexpr int value = pair_mode(MODE) ? 2 : 1; };
 
 __device__ inline uint32_t lo_plane(uint32_t a, uint32_t b) {
     return (a & 0xFFu) | ((a >> 8) & 0xFF00u) | ((b & 0xFFu) << 16) | ((b << 8) & 0xFF000000u);
@@ -113,6 +115,14 @@ __device__ inline void load64(const EncArgs& a, uint64_t i0, int nv, uint32_t w[
             uint4 v[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] = p[q];
+            if constexpr (MODE == ENC_PAIR_XOR) {
+                const uint4* p2 = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in2) + i0);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint4 u = p2[q];
+                    v[q].x ^= u.x; v[q].y ^= u.y; v[q].z ^= u.z; v[q].w ^= u.w;
+                }
+            }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 if constexpr (MODE == ENC_PLANE_LO) {
@@ -138,7 +148,8 @@ __device__ inline void load64(const EncArgs& a, uint64_t i0, int nv, uint32_t w[
             if constexpr (MODE == ENC_BYTES) {
                 b0 = static_cast<const uint8_t*>(a.in)[i0 + k];
             } else {
-                const uint32_t x = static_cast<const uint16_t*>(a.in)[i0 + k];
+                uint32_t x = static_cast<const uint16_t*>(a.in)[i0 + k];
+                if constexpr (MODE == ENC_PAIR_XOR) x ^= static_cast<const uint16_t*>(a.in2)[i0 + k];
                 b0 = MODE == ENC_PLANE_LO ? (x & 0xFFu) : (x >> 8);
                 b1 = x & 0xFFu;
             }
@@ -244,8 +255,9 @@ __device__ inline uint32_t input_symbol(const EncArgs& a, int s, uint64_t i) {
     if constexpr (MODE == ENC_BYTES) {
         return static_cast<const uint8_t*>(a.in)[i];
     } else {
-        const uint32_t x = static_cast<const uint16_t*>(a.in)[i];
-        const bool lo = MODE == ENC_PLANE_LO || (MODE == ENC_PAIR && s == 1);
+        uint32_t x = static_cast<const uint16_t*>(a.in)[i];
+        if constexpr (MODE == ENC_PAIR_XOR) x ^= static_cast<const uint16_t*>(a.in2)[i];
+        const bool lo = MODE == ENC_PLANE_LO || (pair_mode(MODE) && s == 1);
         return lo ? (x & 0xFFu) : (x >> 8);
     }
 }
@@ -429,7 +441,7 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
 
 // Launch 2: pack (see the top of the file).
 template <int MODE>
-__global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_kernel(EncArgs a) {
+__global__ __launch_bounds__(ENC_THREADS, pair_mode(MODE) ? 2 : 4) void encode_kernel(EncArgs a) {
     constexpr int NS = Streams<MODE>::value;
     __shared__ Shared S;
 
@@ -646,6 +658,7 @@ __global__ __launch_bounds__(ENC_THREADS, MODE == ENC_PAIR ? 2 : 4) void encode_
 int launch_encode(const EncodeLaunch& L, void* stream) {
     EncArgs a{};
     a.in = L.in;
+    a.in2 = L.in2;
     a.n = L.n;
     a.chunk = L.chunk;
     a.log2k = (uint32_t)ilog2(units_per_chunk(L.chunk));
@@ -653,7 +666,7 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     a.G = L.chunk >= SEG ? 1u : SEG / L.chunk;
     a.S = L.chunk > SEG ? L.chunk / SEG : 1u;
     a.ntickets = (L.nc + a.G - 1) / a.G;
-    const int ns = L.mode == ENC_PAIR ? 2 : 1;
+    const int ns = pair_mode(L.mode) ? 2 : 1;
     const uint64_t tb = table_bytes(L.nc), gb = gap_bytes(L.nc, L.chunk);
     for (int s = 0; s < ns; ++s) {
         StreamArgs& st = a.st[s];
@@ -677,8 +690,8 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     // number of pack workgroups that fit on all compute units together.
     uint64_t grid_wgs = L.grid;
     if (grid_wgs == 0) {
-        static int per_cu[4] = {0, 0, 0, 0};
-        const int m = (int)L.mode & 3;
+        static int per_cu[5] = {0, 0, 0, 0, 0};
+        const int m = L.mode >= 0 && L.mode <= 4 ? (int)L.mode : 0;
         if (per_cu[m] == 0) {
             int nb = 0;
             hipError_t e = hipErrorInvalidValue;
@@ -687,6 +700,7 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
                 case ENC_PLANE_LO: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PLANE_LO>, ENC_THREADS, 0); break;
                 case ENC_PLANE_HI: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PLANE_HI>, ENC_THREADS, 0); break;
                 case ENC_PAIR: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PAIR>, ENC_THREADS, 0); break;
+                case ENC_PAIR_XOR: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PAIR_XOR>, ENC_THREADS, 0); break;
                 default: return LECB_ERR_INVALID_ARG;
             }
             if (e != hipSuccess || nb < 1) return LECB_ERR_HIP;
@@ -713,6 +727,10 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
         case ENC_PAIR:
             hipLaunchKernelGGL(count_kernel<ENC_PAIR>, grid, block, 0, hs, a);
             hipLaunchKernelGGL(encode_kernel<ENC_PAIR>, grid, block, 0, hs, a);
+            break;
+        case ENC_PAIR_XOR:
+            hipLaunchKernelGGL(count_kernel<ENC_PAIR_XOR>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(encode_kernel<ENC_PAIR_XOR>, grid, block, 0, hs, a);
             break;
         default: return LECB_ERR_INVALID_ARG;
     }

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u8_kernel(const uint8_t* __
     hist_flush<R>(s, hist);
 }
 
+// in2 != nullptr: histograms of the planes of in[i] ^ in2[i] (snapshot delta)
 __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* __restrict__ in,
+                                                                const uint16_t* __restrict__ in2,
                                                                 uint64_t n,
                                                                 unsigned long long* hist_hi,
                                                                 unsigned long long* hist_lo) {
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
     const int r = threadIdx.x & (R - 1);
     const uint64_t n8 = n / 8;
     const uint4* in4 = reinterpret_cast<const uint4*>(in);
+    const uint4* in24 = reinterpret_cast<const uint4*>(in2);
     const uint64_t stride = (uint64_t)gridDim.x * HIST_THREADS;
     auto add8 = [&](const v4u& v) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -115,14 +118,19 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
         v4u v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = ld_stream(&in4[i + q * stride]);
+        if (in2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] ^= ld_stream(&in24[i + q * stride]);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) add8(v[q]);
     }
-    for (; i < n8; i += stride) add8(ld_stream(&in4[i]));
+    for (; i < n8; i += stride) add8(in2 ? ld_stream(&in4[i]) ^ ld_stream(&in24[i]) : ld_stream(&in4[i]));
     if (blockIdx.x == gridDim.x - 1) {
         for (uint64_t i = n8 * 8 + threadIdx.x; i < n; i += HIST_THREADS) {
-            atomicAdd(&s_lo[(in[i] & 0xFFu) * R + r], 1u);
-            atomicAdd(&s_hi[(in[i] >> 8) * R + r], 1u);
+            const uint32_t x = in2 ? (uint32_t)(in[i] ^ in2[i]) : in[i];
+            atomicAdd(&s_lo[(x & 0xFFu) * R + r], 1u);
+            atomicAdd(&s_hi[(x >> 8) * R + r], 1u);
         }
     }
     __syncthreads();
@@ -169,8 +177,10 @@ __device__ inline uint32_t join2(uint32_t h, uint32_t l, int half) {
     return (ls & 0xFFu) | ((hs & 0xFFu) << 8) | ((ls & 0xFF00u) << 8) | ((hs & 0xFF00u) << 16);
 }
 
+// w0 != nullptr: out = w0 ^ (hi << 8 | lo) (a snapshot from its delta)
 __global__ __launch_bounds__(BG_THREADS) void merge_kernel(const uint8_t* __restrict__ hi,
                                                            const uint8_t* __restrict__ lo,
+                                                           const uint16_t* __restrict__ w0,
                                                            uint64_t n, uint16_t* __restrict__ out) {
     const uint64_t n16 = n / 16;
     const uint64_t stride = (uint64_t)gridDim.x * BG_THREADS;
@@ -182,12 +192,16 @@ __global__ __launch_bounds__(BG_THREADS) void merge_kernel(const uint8_t* __rest
         a.z = join2(h.y, l.y, 0); a.w = join2(h.y, l.y, 1);
         b.x = join2(h.z, l.z, 0); b.y = join2(h.z, l.z, 1);
         b.z = join2(h.w, l.w, 0); b.w = join2(h.w, l.w, 1);
+        if (w0) {
+            a ^= ld_stream(reinterpret_cast<const uint4*>(w0) + 2 * i);
+            b ^= ld_stream(reinterpret_cast<const uint4*>(w0) + 2 * i + 1);
+        }
         st_stream(reinterpret_cast<uint4*>(out) + 2 * i, a);
         st_stream(reinterpret_cast<uint4*>(out) + 2 * i + 1, b);
     }
     if (blockIdx.x == gridDim.x - 1) {
         for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += BG_THREADS)
-            out[i] = (uint16_t)(((uint16_t)hi[i] << 8) | lo[i]);
+            out[i] = (uint16_t)((((uint16_t)hi[i] << 8) | lo[i]) ^ (w0 ? w0[i] : 0));
     }
 }
 
@@ -293,8 +307,8 @@ int launch_histogram_u8(const uint8_t* in, uint64_t n, uint64_t* hist, int accum
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 
-int launch_histogram_u16(const uint16_t* in, uint64_t n, uint64_t* hist_hi, uint64_t* hist_lo,
-                         int accumulate, void* stream) {
+int launch_histogram_u16(const uint16_t* in, const uint16_t* in2, uint64_t n, uint64_t* hist_hi,
+                         uint64_t* hist_lo, int accumulate, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (!accumulate) {
         int rc = launch_fill_zero(hist_hi, 256 * sizeof(uint64_t), stream);
@@ -303,7 +317,7 @@ int launch_histogram_u16(const uint16_t* in, uint64_t n, uint64_t* hist_hi, uint
     }
     if (n == 0) return LECB_OK;
     const int grid = grid_for(n / 8 + 1, HIST_THREADS * 8, device_cu_count() * 4);
-    hipLaunchKernelGGL(hist_u16_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, n,
+    hipLaunchKernelGGL(hist_u16_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, in2, n,
                        reinterpret_cast<unsigned long long*>(hist_hi),
                        reinterpret_cast<unsigned long long*>(hist_lo));
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
@@ -317,11 +331,12 @@ int launch_split(const uint16_t* in, uint64_t n, uint8_t* hi, uint8_t* lo, void*
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 
-int launch_merge(const uint8_t* hi, const uint8_t* lo, uint64_t n, uint16_t* out, void* stream) {
+int launch_merge(const uint8_t* hi, const uint8_t* lo, const uint16_t* w0, uint64_t n, uint16_t* out,
+                 void* stream) {
     if (n == 0) return LECB_OK;
     const int grid = grid_for(n / 16 + 1, BG_THREADS, device_cu_count() * 16);
     hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(BG_THREADS), 0,
-                       reinterpret_cast<hipStream_t>(stream), hi, lo, n, out);
+                       reinterpret_cast<hipStream_t>(stream), hi, lo, w0, n, out);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

@@ -83,7 +83,8 @@ int canonical_from_lengths(const uint8_t len[256], lecb_codebook* out);
 // ---------------------------------------------------------------- launches (kernels_*.hip)
 // Input kinds of the encode kernel.  ENC_PAIR codes both bytes of 16-bit
 // words in one pass: stream 0 = high bytes, stream 1 = low bytes.
-enum EncodeMode { ENC_BYTES = 0, ENC_PLANE_LO = 1, ENC_PLANE_HI = 2, ENC_PAIR = 3 };
+// ENC_PAIR_XOR: both planes of w0[i] ^ w1[i] (the incremental snapshot delta)
+enum EncodeMode { ENC_BYTES = 0, ENC_PLANE_LO = 1, ENC_PLANE_HI = 2, ENC_PAIR = 3, ENC_PAIR_XOR = 4 };
 
 struct EncodeStream {
     const DeviceCodebook* cb;
@@ -95,11 +96,12 @@ struct EncodeStream {
 
 struct EncodeLaunch {
     const void* in;          // u8 symbols (ENC_BYTES) or u16 words
+    const void* in2;         // ENC_PAIR_XOR: the second u16 tensor (symbols of in ^ in2)
     int mode;                // EncodeMode
     uint64_t n;
     uint32_t chunk;
     uint64_t nc;
-    EncodeStream st[2];      // st[1] only for ENC_PAIR
+    EncodeStream st[2];      // st[1] only for ENC_PAIR / ENC_PAIR_XOR
     int grid;                // upper bound on workgroups (persistent grid)
 };
 int launch_encode(const EncodeLaunch& a, void* stream);
@@ -123,10 +125,11 @@ int launch_decode(const DecodeLaunch& a, void* stream);
 
 int launch_histogram_u8(const uint8_t* in, uint64_t n, uint64_t* hist, int accumulate,
                         void* stream);
-int launch_histogram_u16(const uint16_t* in, uint64_t n, uint64_t* hist_hi, uint64_t* hist_lo,
-                         int accumulate, void* stream);
+int launch_histogram_u16(const uint16_t* in, const uint16_t* in2, uint64_t n, uint64_t* hist_hi,
+                         uint64_t* hist_lo, int accumulate, void* stream);
 int launch_split(const uint16_t* in, uint64_t n, uint8_t* hi, uint8_t* lo, void* stream);
-int launch_merge(const uint8_t* hi, const uint8_t* lo, uint64_t n, uint16_t* out, void* stream);
+int launch_merge(const uint8_t* hi, const uint8_t* lo, const uint16_t* w0, uint64_t n, uint16_t* out,
+                 void* stream);
 int launch_codebook_upload(const CodebookArgs& args, DeviceCodebook* blob, void* stream);
 int launch_fill_zero(void* ptr, uint64_t bytes, void* stream);
 int launch_result(lecb_result* r, uint64_t bytes, uint64_t bits, int32_t status, void* stream);

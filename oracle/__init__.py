@@ -56,7 +56,8 @@ from .stream import (
     chunk_word_counts,
     parse_table,
 )
-from .bytegroup import split_bf16, merge_bf16, encode_bf16, decode_bf16, container_bytes, parse_container
+from .bytegroup import (split_bf16, merge_bf16, encode_bf16, decode_bf16, container_bytes, parse_container,
+                        snapshot_delta, apply_delta)
 from .metrics import entropy_bits, payload_bits_identity, per_batch_optimal_bits
 from .drift import payload_bits_or_none, drift_check, adaptive_codebooks
 
@@ -66,5 +67,6 @@ __all__ = [
     "table_bytes", "header_bytes", "gap_bytes", "units_per_chunk", "encoded_bound", "encode_bitstring", "encode", "decode_bitwise", "decode",
     "chunk_word_counts", "parse_table", "split_bf16", "merge_bf16", "encode_bf16", "decode_bf16",
     "container_bytes", "parse_container", "entropy_bits", "payload_bits_identity",
-    "per_batch_optimal_bits",
+    "per_batch_optimal_bits", "snapshot_delta", "apply_delta", "payload_bits_or_none", "drift_check",
+    "adaptive_codebooks",
 ]

@@ -59,6 +59,26 @@ def merge_bf16(hi, lo) -> np.ndarray:
     return ((hi << 8) | lo).astype(np.uint16)
 
 
+def snapshot_delta(w0, w1) -> np.ndarray:
+    """D[i] = W0[i] ^ W1[i] on the 16-bit patterns.
+
+    "Lossless Compression for LLM Tensor Incremental Snapshots", Technical
+    framework (incremental delta between consecutive checkpoints) and the
+    original abstract.  Reading: the pages do not define the delta operator;
+    the bitwise XOR of the stored bit patterns is taken (exactly invertible,
+    no floating-point rounding)."""
+    w0 = np.ascontiguousarray(w0).view(np.uint16).ravel()
+    w1 = np.ascontiguousarray(w1).view(np.uint16).ravel()
+    if w0.shape != w1.shape:
+        raise ValueError("snapshots differ in size")
+    return np.bitwise_xor(w0, w1)
+
+
+def apply_delta(w0, d) -> np.ndarray:
+    """W1[i] = W0[i] ^ D[i]: the later snapshot from the earlier one and the delta."""
+    return snapshot_delta(w0, d)
+
+
 def encode_bf16(x, chunk: int, max_len: int = 16) -> dict:
     """Per-tensor coding of one bf16 tensor: split, histogram, codebook and stream per plane."""
     hi, lo = split_bf16(x)

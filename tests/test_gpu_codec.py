@@ -295,6 +295,49 @@ def test_bf16_pertensor_pipeline(n, chunk):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
 
 
+# ----------------------------------------------------------------------------- fused snapshot delta
+
+@pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), ((1 << 20) + 5, 65536)])
+def test_fused_snapshot_delta(n, chunk):
+    """Encode from (W0, W1) and decode to W1: the delta planes' histograms,
+    codebooks and streams equal the oracle's for D = W0 ^ W1 (the XOR never
+    materialised), and the decode reproduces W1 exactly."""
+    _say(f"fused delta n={n} chunk={chunk}")
+    d, w0, w1 = workloads.bf16_delta(n, return_snapshots=True)
+    enc = oracle.encode_bf16(oracle.snapshot_delta(w0, w1), chunk)
+    w0d, w1d = to_dev(w0.view(np.int16)), to_dev(w1.view(np.int16))
+    hh = torch.zeros(256, dtype=torch.int64, device=DEV)
+    hl = torch.zeros(256, dtype=torch.int64, device=DEV)
+    lecb.lecb_histogram_bf16_delta(w0d, w1d, hh, hl)
+    dh, dl = oracle.split_bf16(d)
+    assert np.array_equal(hh.cpu().numpy().astype(np.uint64), oracle.histogram(dh))
+    assert np.array_equal(hl.cpu().numpy().astype(np.uint64), oracle.histogram(dl))
+    hist = torch.zeros(512, dtype=torch.int64, device=DEV)
+    bh, bl = lecb.new_codebook_blob(DEV), lecb.new_codebook_blob(DEV)
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(2, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    cb_hi, cb_lo = lecb.lecb_encode_bf16_delta_pertensor(w0d, w1d, n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
+    assert np.array_equal(cb_hi.lengths(), enc["len_hi"]) and np.array_equal(cb_lo.lengths(), enc["len_lo"])
+    r = lecb.results_to_numpy(res)
+    assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
+    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), enc["stream_hi"])
+    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), enc["stream_lo"])
+    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty(n, dtype=torch.int16, device=DEV)
+    rd = lecb.new_results(2, DEV)
+    lecb.lecb_decode_bf16_delta_from_results(oh, ol, res, bh, bl, chunk, n, w0d, out, scratch, rd, ws)
+    q = lecb.results_to_numpy(rd)
+    assert int(q[0]["status"]) == 0 and int(q[1]["status"]) == 0
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
+    out.zero_()
+    lecb.lecb_decode_bf16_delta(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, w0d, out,
+                                scratch, rd, ws)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
+
+
 # ----------------------------------------------------------------------------- drift refresh
 
 @pytest.mark.parametrize("tol", [0, 20_000, 10**9])

@@ -65,3 +65,21 @@ def test_payload_identity_and_optimum():
     assert shannon <= opt_bits <= fixed_bits
     assert fixed_bits / opt_bits - 1 < 0.005  # the page's "within 0.5 % of per-shard Huffman" holds here
     assert fixed_bits / shannon - 1 < 0.01
+
+
+def test_snapshot_delta_pins():
+    """XOR delta: the identities that fix it (involution, zero on equal
+    snapshots, bit-flip count) checked on random patterns and by hand."""
+    import workloads
+    rng = np.random.default_rng(5)
+    w0 = rng.integers(0, 1 << 16, 10_001, dtype=np.uint16)
+    w1 = rng.integers(0, 1 << 16, 10_001, dtype=np.uint16)
+    d = oracle.snapshot_delta(w0, w1)
+    assert np.array_equal(oracle.apply_delta(w0, d), w1)
+    assert np.array_equal(oracle.apply_delta(w1, d), w0)
+    assert not oracle.snapshot_delta(w0, w0).any()
+    # by hand: 0x3F80 (1.0) and 0x4000 (2.0) differ in bits 14..7 -> 0x7F80
+    assert int(oracle.snapshot_delta(np.array([0x3F80], np.uint16), np.array([0x4000], np.uint16))[0]) == 0x7F80
+    # the snapshot workload's delta is this operator
+    ds, w0s, w1s = workloads.bf16_delta(1 << 16, return_snapshots=True)
+    assert np.array_equal(oracle.snapshot_delta(w0s, w1s), ds)
