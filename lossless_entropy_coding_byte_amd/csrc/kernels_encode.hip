@@ -76,6 +76,8 @@ struct EncArgs {
     uint32_t G;          // chunks per ticket
     uint32_t S;          // segments per ticket
     uint64_t ntickets;
+    uint32_t npack;      // pack workgroups W (ticket ranges); the count launch has F*W
+    uint32_t fsplit;     // F: count workgroups per pack workgroup's range
     StreamArgs st[2];
 };
 
@@ -407,7 +409,9 @@ __device__ inline uint32_t chunk_bits_of(const uint64_t* incl_lds, int lane, int
     return lane == 0 ? (uint32_t)(chunk_acc >> (32 * s)) : 0u;
 }
 
-// Launch 1: payload words of every workgroup's tickets, per stream.
+// Launch 1: payload words of every workgroup's tickets, per stream.  Each
+// pack workgroup's ticket range is counted by F workgroups (more loads in
+// flight than one workgroup walking it), whose totals follow each other.
 template <int MODE>
 __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
     constexpr int NS = Streams<MODE>::value;
@@ -420,8 +424,10 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
     for (int s = 0; s < NS; ++s) len[s][tid] = (uint8_t)(a.st[s].cb->enc[tid] & 31u);
     __syncthreads();
     const uint32_t L = a.chunk >= SEG ? ENC_THREADS : a.chunk / SPT;
-    const uint64_t t0 = first_ticket(blockIdx.x, a.ntickets, gridDim.x);
-    const uint64_t t1 = first_ticket(blockIdx.x + 1ull, a.ntickets, gridDim.x);
+    // the range of pack workgroup w = blockIdx / F, split F ways
+    const uint64_t pw = blockIdx.x / a.fsplit, f = blockIdx.x % a.fsplit;
+    const uint64_t r0 = first_ticket(pw, a.ntickets, a.npack), r1 = first_ticket(pw + 1, a.ntickets, a.npack);
+    const uint64_t t0 = r0 + (r1 - r0) * f / a.fsplit, t1 = r0 + (r1 - r0) * (f + 1) / a.fsplit;
     uint64_t words = 0;  // wave s, stream s
     for (uint64_t tk = t0; tk < t1; ++tk) {
         uint32_t w[NS][16];
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(ENC_THREADS, pair_mode(MODE) ? 2 : 4) void encode_k
     {
         uint64_t part[2] = {0, 0};
 #pragma unroll 4
-        for (uint32_t v = tid; v < blockIdx.x; v += ENC_THREADS) {
+        for (uint32_t v = tid; v < blockIdx.x * a.fsplit; v += ENC_THREADS) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) part[s] += a.st[s].wg_words[v];
         }
@@ -710,26 +716,30 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     }
     const uint64_t nwg = grid_wgs < a.ntickets ? grid_wgs : a.ntickets;
     const dim3 grid((uint32_t)nwg), block(ENC_THREADS);
+    // the workspace holds one total per chunk: F * W of them must fit
+    a.npack = (uint32_t)nwg;
+    a.fsplit = 4 * nwg <= a.nc ? 4u : 1u;
+    const dim3 cgrid((uint32_t)(nwg * a.fsplit));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     switch (L.mode) {
         case ENC_BYTES:
-            hipLaunchKernelGGL(count_kernel<ENC_BYTES>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(count_kernel<ENC_BYTES>, cgrid, block, 0, hs, a);
             hipLaunchKernelGGL(encode_kernel<ENC_BYTES>, grid, block, 0, hs, a);
             break;
         case ENC_PLANE_LO:
-            hipLaunchKernelGGL(count_kernel<ENC_PLANE_LO>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(count_kernel<ENC_PLANE_LO>, cgrid, block, 0, hs, a);
             hipLaunchKernelGGL(encode_kernel<ENC_PLANE_LO>, grid, block, 0, hs, a);
             break;
         case ENC_PLANE_HI:
-            hipLaunchKernelGGL(count_kernel<ENC_PLANE_HI>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(count_kernel<ENC_PLANE_HI>, cgrid, block, 0, hs, a);
             hipLaunchKernelGGL(encode_kernel<ENC_PLANE_HI>, grid, block, 0, hs, a);
             break;
         case ENC_PAIR:
-            hipLaunchKernelGGL(count_kernel<ENC_PAIR>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(count_kernel<ENC_PAIR>, cgrid, block, 0, hs, a);
             hipLaunchKernelGGL(encode_kernel<ENC_PAIR>, grid, block, 0, hs, a);
             break;
         case ENC_PAIR_XOR:
-            hipLaunchKernelGGL(count_kernel<ENC_PAIR_XOR>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(count_kernel<ENC_PAIR_XOR>, cgrid, block, 0, hs, a);
             hipLaunchKernelGGL(encode_kernel<ENC_PAIR_XOR>, grid, block, 0, hs, a);
             break;
         default: return LECB_ERR_INVALID_ARG;
