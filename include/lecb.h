@@ -15,7 +15,9 @@
  *    for LLM Tensor Incremental Snapshots", Technical framework steps 1-3 and
  *    the reverse path): the 16-bit words are split into a high-byte and a
  *    low-byte plane, each plane gets its own histogram and its own codebook,
- *    and decoding restores the 16-bit words.
+ *    and decoding restores the 16-bit words.  32-bit elements (fp32) are
+ *    grouped the same way into four byte planes (the byte-group size is a
+ *    design knob of the same page, Key design item 1).
  *
  * Stream format v1 (identical, bit for bit, to the oracle's):
  *   stream  = u32 end[nc] | zero pad to 16 B | gap nibbles[nc*K] | zero pad to 16 B | u32 payload[W]
@@ -40,10 +42,12 @@
  *    memory on the current device, 16-byte aligned.  `stream` arguments are
  *    hipStream_t passed as void* (NULL = the null stream).
  *  - Device entry points only enqueue work on `stream`; they never
- *    synchronise and never allocate.  The one exception is
- *    lecb_encode_bf16_pertensor, which must read the histograms back: it
- *    synchronises `stream` once and, on its first call in a host thread,
- *    allocates a 4 KiB pinned host buffer that the thread keeps.
+ *    synchronise and never allocate.  The exceptions are the entries that
+ *    build a codebook from the tensor itself (lecb_encode_bf16_pertensor,
+ *    lecb_encode_bf16_delta_pertensor, lecb_encode_fp32_pertensor,
+ *    lecb_encode_adaptive): they read the histograms back, which
+ *    synchronises `stream` once, and on their first call in a host thread
+ *    allocate an 8 KiB pinned host buffer that the thread keeps.
  *  - Return values: LECB_OK or a negative lecb_status detected on the host
  *    (bad argument, too small a buffer).  Problems only the GPU can see
  *    (a byte with no code word, a corrupt stream, output overflow) are
@@ -367,6 +371,59 @@ int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo
                      uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
                      uint32_t chunk, uint64_t n, uint16_t* d_out, uint8_t* d_scratch,
                      lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ 32-bit elements (fp32)
+ * Byte grouping with four planes ("Lossless Compression for LLM Tensor
+ * Incremental Snapshots", Technical framework step 1 and Key design item 1,
+ * the byte-group size): plane p holds byte 3-p of every element (elements
+ * little-endian), so plane 0 = sign and high exponent bits, plane 3 = the
+ * lowest mantissa byte.  Every per-plane array below (codebooks, streams,
+ * capacities, results, histograms) is in that plane order.  Works on any
+ * 32-bit elements; n counts elements.  The workspace is the one of
+ * lecb_workspace_bytes(n, chunk): the two halves of the work use it one
+ * after the other on `stream`. */
+
+/* Histograms of the four planes: d_hist = u64[4*256], plane p at 256*p.
+ * accumulate != 0 adds to d_hist instead of overwriting it. */
+int lecb_histogram_fp32(const uint32_t* d_in, uint64_t n, uint64_t* d_hist, int accumulate,
+                        void* stream);
+
+/* out[i] = planes[0][i] << 24 | planes[1][i] << 16 | planes[2][i] << 8 | planes[3][i].
+ * d_planes: host array of four device pointers. */
+int lecb_merge_fp32(const uint8_t* const d_planes[4], uint64_t n, uint32_t* d_out, void* stream);
+
+/* Encode the four planes with four device codebooks (host arrays of device
+ * pointers d_blob, d_out and of capacities cap); d_res4 = four results.  Two
+ * launch pairs, each coding two planes in one pass over the elements.
+ * Errors as lecb_encode_bf16, per plane. */
+int lecb_encode_fp32(const uint32_t* d_in, uint64_t n, const void* const d_blob[4], uint32_t chunk,
+                     uint8_t* const d_out[4], const uint64_t cap[4], lecb_result* d_res4, void* d_ws,
+                     uint64_t ws_bytes, void* stream);
+
+/* Per-tensor mode: plane histograms (d_hist, u64[1024]) -> read back -> four
+ * optimal codebooks built on the host (returned in cb[4], absent bytes get
+ * no code) -> uploaded to d_blob[4] -> lecb_encode_fp32.  Synchronises
+ * `stream` once (the histogram read-back). */
+int lecb_encode_fp32_pertensor(const uint32_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,
+                               uint64_t* d_hist, void* const d_blob[4], lecb_codebook cb[4],
+                               uint8_t* const d_out[4], const uint64_t cap[4], lecb_result* d_res4,
+                               void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* Decode the four streams (exact sizes in stream_bytes[4]) and restore the
+ * 32-bit elements.  d_scratch: 4*align16(n) bytes of device memory for the
+ * decoded planes (plane p at p*align16(n)).  Errors as lecb_decode_bf16. */
+int lecb_decode_fp32(const uint8_t* const d_stream[4], const uint64_t stream_bytes[4],
+                     const void* const d_blob[4], uint32_t chunk, uint64_t n, uint32_t* d_out,
+                     uint8_t* d_scratch, lecb_result* d_res4, void* d_ws, uint64_t ws_bytes,
+                     void* stream);
+
+/* lecb_decode_fp32 with the four sizes read on the device from the results
+ * an encode wrote (d_enc_res4), so encode -> decode needs no host
+ * synchronisation. */
+int lecb_decode_fp32_from_results(const uint8_t* const d_stream[4], const lecb_result* d_enc_res4,
+                                  const void* const d_blob[4], uint32_t chunk, uint64_t n,
+                                  uint32_t* d_out, uint8_t* d_scratch, lecb_result* d_res4,
+                                  void* d_ws, uint64_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -116,6 +116,13 @@ _SIGNATURES = {
     "lecb_decode_bf16_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16_planes": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_histogram_fp32": (_int, [_vp, _u64, _vp, _int, _vp]),
+    "lecb_merge_fp32": (_int, [_vp, _u64, _vp, _vp]),
+    "lecb_encode_fp32": (_int, [_vp, _u64, _vp, _u32, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_encode_fp32_pertensor": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, ctypes.POINTER(lecb_codebook),
+                                          _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_fp32": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_fp32_from_results": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
 }
 
 _lib = None
@@ -418,6 +425,60 @@ def lecb_decode_bf16(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, out
                                    _ptr(blob_lo), chunk, n, _ptr(out), _ptr(scratch), _ptr(res2),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_decode_bf16")
+
+
+# --------------------------------------------------------------------------- 32-bit elements, four planes
+# Per-plane lists are in plane order: byte 3 (sign, high exponent bits) first.
+
+def _ptrs4(ts):
+    if len(ts) != 4:
+        raise ValueError("four planes expected")
+    return (ctypes.c_void_p * 4)(*[t.data_ptr() for t in ts])
+
+
+def _caps4(ts):
+    return (_u64 * 4)(*[t.numel() for t in ts])
+
+
+def lecb_histogram_fp32(x, hist, accumulate: bool = False, stream=None) -> None:
+    """Histograms of the four byte planes of 32-bit elements into hist (int64[1024])."""
+    _check(load().lecb_histogram_fp32(_ptr(x), x.numel(), _ptr(hist), int(accumulate), _stream(stream)),
+           "lecb_histogram_fp32")
+
+
+def lecb_merge_fp32(planes, out, stream=None) -> None:
+    _check(load().lecb_merge_fp32(_ptrs4(planes), out.numel(), _ptr(out), _stream(stream)), "lecb_merge_fp32")
+
+
+def lecb_encode_fp32(x, n, blobs, chunk, outs, res4, ws, stream=None) -> None:
+    _check(load().lecb_encode_fp32(_ptr(x), n, _ptrs4(blobs), chunk, _ptrs4(outs), _caps4(outs), _ptr(res4),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_encode_fp32")
+
+
+def lecb_encode_fp32_pertensor(x, n, chunk, max_len, hist, blobs, outs, res4, ws, stream=None):
+    """Per-tensor four-plane encode; returns the four host codebooks."""
+    cbs = (lecb_codebook * 4)()
+    _check(load().lecb_encode_fp32_pertensor(_ptr(x), n, chunk, max_len, _ptr(hist), _ptrs4(blobs), cbs,
+                                             _ptrs4(outs), _caps4(outs), _ptr(res4), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_encode_fp32_pertensor")
+    return list(cbs)
+
+
+def lecb_decode_fp32(streams, stream_bytes, blobs, chunk, n, out, scratch, res4, ws, stream=None) -> None:
+    sb = (_u64 * 4)(*[int(b) for b in stream_bytes])
+    _check(load().lecb_decode_fp32(_ptrs4(streams), sb, _ptrs4(blobs), chunk, n, _ptr(out), _ptr(scratch),
+                                   _ptr(res4), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_decode_fp32")
+
+
+def lecb_decode_fp32_from_results(streams, enc_res4, blobs, chunk, n, out, scratch, res4, ws,
+                                  stream=None) -> None:
+    _check(load().lecb_decode_fp32_from_results(_ptrs4(streams), _ptr(enc_res4), _ptrs4(blobs), chunk, n,
+                                                _ptr(out), _ptr(scratch), _ptr(res4), _ptr(ws),
+                                                ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_decode_fp32_from_results")
 
 
 # --------------------------------------------------------------------------- buffer helpers

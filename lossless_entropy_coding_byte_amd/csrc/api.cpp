@@ -15,13 +15,13 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Histograms come back through a pinned buffer (one per host thread, 4 KiB,
+// Histograms come back through a pinned buffer (one per host thread, 8 KiB,
 // allocated on first use and kept): a direct DMA, no staging copy.  Waits for
 // `stream`.
 int read_back_hist(const uint64_t* d_hist, int count, void* stream, const uint64_t** host) {
     thread_local uint64_t* h = nullptr;
-    if (count > 512) return LECB_ERR_INVALID_ARG;
-    if (!h && hipHostMalloc(reinterpret_cast<void**>(&h), 512 * sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) {
+    if (count > 1024) return LECB_ERR_INVALID_ARG;
+    if (!h && hipHostMalloc(reinterpret_cast<void**>(&h), 1024 * sizeof(uint64_t), hipHostMallocDefault) != hipSuccess) {
         h = nullptr;
         return LECB_ERR_HIP;
     }
@@ -88,7 +88,7 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
                   uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
                   uint64_t ws_bytes, void* stream, const void* d_blob2 = nullptr,
                   uint8_t* d_out2 = nullptr, uint64_t out_capacity2 = 0, const void* d_in2 = nullptr) {
-    const bool pair = mode == ENC_PAIR || mode == ENC_PAIR_XOR;
+    const bool pair = two_stream_mode(mode);
     if (mode == ENC_PAIR_XOR && n && (!d_in2 || !aligned16(d_in2))) return LECB_ERR_INVALID_ARG;
     if (!valid_chunk(chunk) || !d_res || !d_blob || !aligned16(d_blob)) return LECB_ERR_INVALID_ARG;
     if (pair && (!d_blob2 || !aligned16(d_blob2))) return LECB_ERR_INVALID_ARG;
@@ -472,6 +472,103 @@ int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo
                                      n, hi, lo, d_res2, d_ws, ws_bytes, stream);
     if (!rc) rc = lecb_merge_bf16(hi, lo, n, d_out, stream);
     return rc;
+}
+
+// ---------------------------------------------------------------- 32-bit elements, four planes
+
+int lecb_histogram_fp32(const uint32_t* d_in, uint64_t n, uint64_t* d_hist, int accumulate, void* stream) {
+    if (!d_hist || !aligned16(d_hist) || (n && (!d_in || !aligned16(d_in)))) return LECB_ERR_INVALID_ARG;
+    return launch_histogram_u32(d_in, n, d_hist, accumulate, stream);
+}
+
+int lecb_merge_fp32(const uint8_t* const d_planes[4], uint64_t n, uint32_t* d_out, void* stream) {
+    if (!d_planes) return LECB_ERR_INVALID_ARG;
+    if (n) {
+        if (!d_out || !aligned16(d_out)) return LECB_ERR_INVALID_ARG;
+        for (int k = 0; k < 4; ++k)
+            if (!d_planes[k] || !aligned16(d_planes[k])) return LECB_ERR_INVALID_ARG;
+    }
+    return launch_merge4(d_planes[0], d_planes[1], d_planes[2], d_planes[3], n, d_out, stream);
+}
+
+int lecb_encode_fp32(const uint32_t* d_in, uint64_t n, const void* const d_blob[4], uint32_t chunk,
+                     uint8_t* const d_out[4], const uint64_t cap[4], lecb_result* d_res4, void* d_ws,
+                     uint64_t ws_bytes, void* stream) {
+    if (!d_blob || !d_out || !cap || !d_res4) return LECB_ERR_INVALID_ARG;
+    // bytes 3 and 2 (upper 16 bits), then bytes 1 and 0; the two launches
+    // share the workspace one after the other on `stream`
+    int rc = encode_common(d_in, ENC_PAIR32_HI, n, d_blob[0], chunk, d_out[0], cap[0], d_res4, d_ws,
+                           ws_bytes, stream, d_blob[1], d_out[1], cap[1]);
+    if (!rc)
+        rc = encode_common(d_in, ENC_PAIR32_LO, n, d_blob[2], chunk, d_out[2], cap[2], d_res4 + 2, d_ws,
+                           ws_bytes, stream, d_blob[3], d_out[3], cap[3]);
+    return rc;
+}
+
+int lecb_encode_fp32_pertensor(const uint32_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,
+                               uint64_t* d_hist, void* const d_blob[4], lecb_codebook cb[4],
+                               uint8_t* const d_out[4], const uint64_t cap[4], lecb_result* d_res4,
+                               void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) || !d_blob ||
+        !cb || !d_out || !cap || !d_res4)
+        return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        for (int k = 0; k < 4; ++k) {
+            std::memset(&cb[k], 0, sizeof(cb[k]));
+            const int rc = launch_result(d_res4 + k, 0, 0, LECB_OK, stream);
+            if (rc) return rc;
+        }
+        return LECB_OK;
+    }
+    int rc = lecb_histogram_fp32(d_in, n, d_hist, 0, stream);
+    if (rc) return rc;
+    const uint64_t* h = nullptr;
+    rc = read_back_hist(d_hist, 1024, stream, &h);
+    if (rc) return rc;
+    for (int k = 0; k < 4 && !rc; ++k) rc = lecb_build_codebook(h + 256 * k, max_len, 0, &cb[k]);
+    for (int k = 0; k < 4 && !rc; ++k) rc = lecb_codebook_upload(&cb[k], d_blob[k], stream);
+    if (!rc) rc = lecb_encode_fp32(d_in, n, d_blob, chunk, d_out, cap, d_res4, d_ws, ws_bytes, stream);
+    return rc;
+}
+
+static int decode_fp32_common(const uint8_t* const d_stream[4], const uint64_t* stream_bytes,
+                              const lecb_result* d_enc_res4, const void* const d_blob[4], uint32_t chunk,
+                              uint64_t n, uint32_t* d_out, uint8_t* d_scratch, lecb_result* d_res4,
+                              void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!d_stream || !d_blob || !d_res4 || (!stream_bytes && !d_enc_res4)) return LECB_ERR_INVALID_ARG;
+    if (n && (!d_scratch || !aligned16(d_scratch) || !d_out || !aligned16(d_out))) return LECB_ERR_INVALID_ARG;
+    const uint64_t plane = (n + 15) & ~uint64_t(15);
+    uint8_t* p[4];
+    for (int k = 0; k < 4; ++k) p[k] = d_scratch ? d_scratch + k * plane : nullptr;
+    const uint64_t none[2] = {0, 0};
+    int rc = LECB_OK;
+    for (int h = 0; h < 2 && !rc; ++h) {
+        const uint8_t* st[2] = {d_stream[2 * h], d_stream[2 * h + 1]};
+        const void* bl[2] = {d_blob[2 * h], d_blob[2 * h + 1]};
+        uint8_t* out[2] = {p[2 * h], p[2 * h + 1]};
+        rc = decode_common(2, st, stream_bytes ? stream_bytes + 2 * h : none, bl, chunk, n, out,
+                           d_res4 + 2 * h, d_ws, ws_bytes, stream,
+                           d_enc_res4 ? d_enc_res4 + 2 * h : nullptr);
+    }
+    if (!rc && n) rc = launch_merge4(p[0], p[1], p[2], p[3], n, d_out, stream);
+    return rc;
+}
+
+int lecb_decode_fp32(const uint8_t* const d_stream[4], const uint64_t stream_bytes[4],
+                     const void* const d_blob[4], uint32_t chunk, uint64_t n, uint32_t* d_out,
+                     uint8_t* d_scratch, lecb_result* d_res4, void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!stream_bytes) return LECB_ERR_INVALID_ARG;
+    return decode_fp32_common(d_stream, stream_bytes, nullptr, d_blob, chunk, n, d_out, d_scratch, d_res4,
+                              d_ws, ws_bytes, stream);
+}
+
+int lecb_decode_fp32_from_results(const uint8_t* const d_stream[4], const lecb_result* d_enc_res4,
+                                  const void* const d_blob[4], uint32_t chunk, uint64_t n, uint32_t* d_out,
+                                  uint8_t* d_scratch, lecb_result* d_res4, void* d_ws, uint64_t ws_bytes,
+                                  void* stream) {
+    if (!d_enc_res4) return LECB_ERR_INVALID_ARG;
+    return decode_fp32_common(d_stream, nullptr, d_enc_res4, d_blob, chunk, n, d_out, d_scratch, d_res4,
+                              d_ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -31,6 +31,8 @@
 // No workgroup ever waits for another one.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "lecb_internal.hpp"
 
 namespace lecb {
@@ -81,7 +83,8 @@ struct EncArgs {
     StreamArgs st[2];
 };
 
-constexpr bool pair_mode(int m) { return m == ENC_PAIR || m == ENC_PAIR_XOR; }
+constexpr bool pair32_mode(int m) { return m == ENC_PAIR32_HI || m == ENC_PAIR32_LO; }
+constexpr bool pair_mode(int m) { return two_stream_mode(m); }
 template <int MODE> struct Streams { static constexpr int value = pair_mode(MODE) ? 2 : 1; };
 
 __device__ inline uint32_t lo_plane(uint32_t a, uint32_t b) {
@@ -89,6 +92,26 @@ __device__ inline uint32_t lo_plane(uint32_t a, uint32_t b) {
 }
 __device__ inline uint32_t hi_plane(uint32_t a, uint32_t b) {
     return ((a >> 8) & 0xFFu) | ((a >> 16) & 0xFF00u) | ((b << 8) & 0xFF0000u) | (b & 0xFF000000u);
+}
+
+// The selected 16 bits of two 32-bit elements, as one word of two 16-bit values.
+template <int MODE>
+__device__ inline uint32_t half2(uint32_t e0, uint32_t e1) {
+    if constexpr (MODE == ENC_PAIR32_HI) return (e0 >> 16) | (e1 & 0xFFFF0000u);
+    else return (e0 & 0xFFFFu) | (e1 << 16);
+}
+
+// 16-bit value of element i: the word itself, its delta, or half of a 32-bit element.
+template <int MODE>
+__device__ inline uint32_t input_word(const EncArgs& a, uint64_t i) {
+    if constexpr (pair32_mode(MODE)) {
+        const uint32_t e = static_cast<const uint32_t*>(a.in)[i];
+        return MODE == ENC_PAIR32_HI ? (e >> 16) : (e & 0xFFFFu);
+    } else {
+        uint32_t x = static_cast<const uint16_t*>(a.in)[i];
+        if constexpr (MODE == ENC_PAIR_XOR) x ^= static_cast<const uint16_t*>(a.in2)[i];
+        return x;
+    }
 }
 
 // Symbol k of a thread's 64 (little-endian in w[16]).
@@ -113,10 +136,24 @@ __device__ inline void load64(const EncArgs& a, uint64_t i0, int nv, uint32_t w[
                 w[0][4 * q + 2] = v[q].z; w[0][4 * q + 3] = v[q].w;
             }
         } else {
-            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in) + i0);
             uint4 v[8];
+            if constexpr (pair32_mode(MODE)) {
+                const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(a.in) + i0);
+                uint4 e[16];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = p[q];
+                for (int q = 0; q < 16; ++q) e[q] = p[q];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    v[q].x = half2<MODE>(e[2 * q].x, e[2 * q].y);
+                    v[q].y = half2<MODE>(e[2 * q].z, e[2 * q].w);
+                    v[q].z = half2<MODE>(e[2 * q + 1].x, e[2 * q + 1].y);
+                    v[q].w = half2<MODE>(e[2 * q + 1].z, e[2 * q + 1].w);
+                }
+            } else {
+                const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in) + i0);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = p[q];
+            }
             if constexpr (MODE == ENC_PAIR_XOR) {
                 const uint4* p2 = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in2) + i0);
 #pragma unroll
@@ -150,8 +187,7 @@ __device__ inline void load64(const EncArgs& a, uint64_t i0, int nv, uint32_t w[
             if constexpr (MODE == ENC_BYTES) {
                 b0 = static_cast<const uint8_t*>(a.in)[i0 + k];
             } else {
-                uint32_t x = static_cast<const uint16_t*>(a.in)[i0 + k];
-                if constexpr (MODE == ENC_PAIR_XOR) x ^= static_cast<const uint16_t*>(a.in2)[i0 + k];
+                const uint32_t x = input_word<MODE>(a, i0 + k);
                 b0 = MODE == ENC_PLANE_LO ? (x & 0xFFu) : (x >> 8);
                 b1 = x & 0xFFu;
             }
@@ -257,8 +293,7 @@ __device__ inline uint32_t input_symbol(const EncArgs& a, int s, uint64_t i) {
     if constexpr (MODE == ENC_BYTES) {
         return static_cast<const uint8_t*>(a.in)[i];
     } else {
-        uint32_t x = static_cast<const uint16_t*>(a.in)[i];
-        if constexpr (MODE == ENC_PAIR_XOR) x ^= static_cast<const uint16_t*>(a.in2)[i];
+        const uint32_t x = input_word<MODE>(a, i);
         const bool lo = MODE == ENC_PLANE_LO || (pair_mode(MODE) && s == 1);
         return lo ? (x & 0xFFu) : (x >> 8);
     }
@@ -661,6 +696,25 @@ __global__ __launch_bounds__(ENC_THREADS, pair_mode(MODE) ? 2 : 4) void encode_k
 
 }  // namespace
 
+namespace {
+
+// Calls f(std::integral_constant<int, mode>) for a valid mode.
+template <typename F>
+hipError_t with_mode(int mode, F&& f) {
+    switch (mode) {
+        case ENC_BYTES: return f(std::integral_constant<int, ENC_BYTES>{});
+        case ENC_PLANE_LO: return f(std::integral_constant<int, ENC_PLANE_LO>{});
+        case ENC_PLANE_HI: return f(std::integral_constant<int, ENC_PLANE_HI>{});
+        case ENC_PAIR: return f(std::integral_constant<int, ENC_PAIR>{});
+        case ENC_PAIR_XOR: return f(std::integral_constant<int, ENC_PAIR_XOR>{});
+        case ENC_PAIR32_HI: return f(std::integral_constant<int, ENC_PAIR32_HI>{});
+        case ENC_PAIR32_LO: return f(std::integral_constant<int, ENC_PAIR32_LO>{});
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
 int launch_encode(const EncodeLaunch& L, void* stream) {
     EncArgs a{};
     a.in = L.in;
@@ -673,6 +727,8 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     a.S = L.chunk > SEG ? L.chunk / SEG : 1u;
     a.ntickets = (L.nc + a.G - 1) / a.G;
     const int ns = pair_mode(L.mode) ? 2 : 1;
+    for (int s = 0; s < ns; ++s)
+        if (!L.st[s].cb || !L.st[s].out || !L.st[s].res || !L.st[s].ws) return LECB_ERR_INVALID_ARG;
     const uint64_t tb = table_bytes(L.nc), gb = gap_bytes(L.nc, L.chunk);
     for (int s = 0; s < ns; ++s) {
         StreamArgs& st = a.st[s];
@@ -695,24 +751,19 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     // are static, so the grid must be resident at once: by default it is the
     // number of pack workgroups that fit on all compute units together.
     uint64_t grid_wgs = L.grid;
+    if (L.mode < 0 || L.mode >= ENC_NUM_MODES) return LECB_ERR_INVALID_ARG;
     if (grid_wgs == 0) {
-        static int per_cu[5] = {0, 0, 0, 0, 0};
-        const int m = L.mode >= 0 && L.mode <= 4 ? (int)L.mode : 0;
-        if (per_cu[m] == 0) {
+        static int per_cu[ENC_NUM_MODES] = {};
+        if (per_cu[L.mode] == 0) {
             int nb = 0;
-            hipError_t e = hipErrorInvalidValue;
-            switch (L.mode) {
-                case ENC_BYTES: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_BYTES>, ENC_THREADS, 0); break;
-                case ENC_PLANE_LO: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PLANE_LO>, ENC_THREADS, 0); break;
-                case ENC_PLANE_HI: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PLANE_HI>, ENC_THREADS, 0); break;
-                case ENC_PAIR: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PAIR>, ENC_THREADS, 0); break;
-                case ENC_PAIR_XOR: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<ENC_PAIR_XOR>, ENC_THREADS, 0); break;
-                default: return LECB_ERR_INVALID_ARG;
-            }
+            const hipError_t e = with_mode(L.mode, [&](auto m) {
+                return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<decltype(m)::value>,
+                                                                    ENC_THREADS, 0);
+            });
             if (e != hipSuccess || nb < 1) return LECB_ERR_HIP;
-            per_cu[m] = nb;
+            per_cu[L.mode] = nb;
         }
-        grid_wgs = (uint64_t)device_cu_count() * per_cu[m];
+        grid_wgs = (uint64_t)device_cu_count() * per_cu[L.mode];
     }
     const uint64_t nwg = grid_wgs < a.ntickets ? grid_wgs : a.ntickets;
     const dim3 grid((uint32_t)nwg), block(ENC_THREADS);
@@ -721,29 +772,12 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     a.fsplit = 4 * nwg <= a.nc ? 4u : 1u;
     const dim3 cgrid((uint32_t)(nwg * a.fsplit));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    switch (L.mode) {
-        case ENC_BYTES:
-            hipLaunchKernelGGL(count_kernel<ENC_BYTES>, cgrid, block, 0, hs, a);
-            hipLaunchKernelGGL(encode_kernel<ENC_BYTES>, grid, block, 0, hs, a);
-            break;
-        case ENC_PLANE_LO:
-            hipLaunchKernelGGL(count_kernel<ENC_PLANE_LO>, cgrid, block, 0, hs, a);
-            hipLaunchKernelGGL(encode_kernel<ENC_PLANE_LO>, grid, block, 0, hs, a);
-            break;
-        case ENC_PLANE_HI:
-            hipLaunchKernelGGL(count_kernel<ENC_PLANE_HI>, cgrid, block, 0, hs, a);
-            hipLaunchKernelGGL(encode_kernel<ENC_PLANE_HI>, grid, block, 0, hs, a);
-            break;
-        case ENC_PAIR:
-            hipLaunchKernelGGL(count_kernel<ENC_PAIR>, cgrid, block, 0, hs, a);
-            hipLaunchKernelGGL(encode_kernel<ENC_PAIR>, grid, block, 0, hs, a);
-            break;
-        case ENC_PAIR_XOR:
-            hipLaunchKernelGGL(count_kernel<ENC_PAIR_XOR>, cgrid, block, 0, hs, a);
-            hipLaunchKernelGGL(encode_kernel<ENC_PAIR_XOR>, grid, block, 0, hs, a);
-            break;
-        default: return LECB_ERR_INVALID_ARG;
-    }
+    with_mode(L.mode, [&](auto m) {
+        constexpr int M = decltype(m)::value;
+        hipLaunchKernelGGL(count_kernel<M>, cgrid, block, 0, hs, a);
+        hipLaunchKernelGGL(encode_kernel<M>, grid, block, 0, hs, a);
+        return hipSuccess;
+    });
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

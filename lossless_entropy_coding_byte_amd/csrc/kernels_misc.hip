@@ -1,4 +1,5 @@
-// Histogram, byte-group split/merge, device codebook construction, fill.
+// Histogram, byte-group split/merge (16- and 32-bit elements), device codebook
+// construction, fill.
 //
 // Histogram: "Single-Stage Huffman Encoder for ML Compression", Overview
 // (frequency analysis) and Methodology step 1; "Lossless Compression for LLM
@@ -138,6 +139,59 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
     hist_flush<R>(s_lo, hist_lo);
 }
 
+// Four byte planes of 32-bit elements; s[p] counts byte 3 - p (most
+// significant plane first), 16 replicas per plane as in hist_u16_kernel.
+__global__ __launch_bounds__(HIST_THREADS) void hist_u32_kernel(const uint32_t* __restrict__ in,
+                                                                uint64_t n,
+                                                                unsigned long long* hist) {
+    constexpr int R = 16;
+    __shared__ uint32_t s[4][256 * R];
+    for (int i = threadIdx.x; i < 256 * R; i += HIST_THREADS) {
+        s[0][i] = 0;
+        s[1][i] = 0;
+        s[2][i] = 0;
+        s[3][i] = 0;
+    }
+    __syncthreads();
+    const int r = threadIdx.x & (R - 1);
+    const uint64_t n4 = n / 4;
+    const uint4* in4 = reinterpret_cast<const uint4*>(in);
+    const uint64_t stride = (uint64_t)gridDim.x * HIST_THREADS;
+    auto add1 = [&](uint32_t x) {
+        atomicAdd(&s[3][(x & 0xFFu) * R + r], 1u);
+        atomicAdd(&s[2][((x >> 8) & 0xFFu) * R + r], 1u);
+        atomicAdd(&s[1][((x >> 16) & 0xFFu) * R + r], 1u);
+        atomicAdd(&s[0][(x >> 24) * R + r], 1u);
+    };
+    // four 16-byte loads in flight per thread, then their 64 increments
+    uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x;
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+        v4u v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ld_stream(&in4[i + q * stride]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            add1(v[q].x);
+            add1(v[q].y);
+            add1(v[q].z);
+            add1(v[q].w);
+        }
+    }
+    for (; i < n4; i += stride) {
+        const v4u v = ld_stream(&in4[i]);
+        add1(v.x);
+        add1(v.y);
+        add1(v.z);
+        add1(v.w);
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint64_t i = n4 * 4 + threadIdx.x; i < n; i += HIST_THREADS) add1(in[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) hist_flush<R>(s[p], hist + 256 * p);
+}
+
 constexpr int BG_THREADS = 256;
 
 // 16 elements per thread: two 16-byte loads of u16, two 16-byte stores.
@@ -202,6 +256,44 @@ __global__ __launch_bounds__(BG_THREADS) void merge_kernel(const uint8_t* __rest
     if (blockIdx.x == gridDim.x - 1) {
         for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += BG_THREADS)
             out[i] = (uint16_t)((((uint16_t)hi[i] << 8) | lo[i]) ^ (w0 ? w0[i] : 0));
+    }
+}
+
+// Byte k of the four plane words, as one 32-bit element (planes 3..0).
+__device__ inline uint32_t join4(uint32_t w3, uint32_t w2, uint32_t w1, uint32_t w0, int k) {
+    const int sh = 8 * k;
+    return ((w0 >> sh) & 0xFFu) | (((w1 >> sh) & 0xFFu) << 8) | (((w2 >> sh) & 0xFFu) << 16) |
+           (((w3 >> sh) & 0xFFu) << 24);
+}
+
+// 16 elements per thread: one 16-byte load per plane, four 16-byte stores.
+__global__ __launch_bounds__(BG_THREADS) void merge4_kernel(const uint8_t* __restrict__ p3,
+                                                            const uint8_t* __restrict__ p2,
+                                                            const uint8_t* __restrict__ p1,
+                                                            const uint8_t* __restrict__ p0, uint64_t n,
+                                                            uint32_t* __restrict__ out) {
+    const uint64_t n16 = n / 16;
+    const uint64_t stride = (uint64_t)gridDim.x * BG_THREADS;
+    for (uint64_t i = (uint64_t)blockIdx.x * BG_THREADS + threadIdx.x; i < n16; i += stride) {
+        const v4u a3 = ld_stream(reinterpret_cast<const uint4*>(p3) + i);
+        const v4u a2 = ld_stream(reinterpret_cast<const uint4*>(p2) + i);
+        const v4u a1 = ld_stream(reinterpret_cast<const uint4*>(p1) + i);
+        const v4u a0 = ld_stream(reinterpret_cast<const uint4*>(p0) + i);
+        const uint32_t w3[4] = {a3.x, a3.y, a3.z, a3.w}, w2[4] = {a2.x, a2.y, a2.z, a2.w};
+        const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w}, w0[4] = {a0.x, a0.y, a0.z, a0.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v4u o;
+            o.x = join4(w3[q], w2[q], w1[q], w0[q], 0);
+            o.y = join4(w3[q], w2[q], w1[q], w0[q], 1);
+            o.z = join4(w3[q], w2[q], w1[q], w0[q], 2);
+            o.w = join4(w3[q], w2[q], w1[q], w0[q], 3);
+            st_stream(reinterpret_cast<uint4*>(out) + 4 * i + q, o);
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += BG_THREADS)
+            out[i] = ((uint32_t)p3[i] << 24) | ((uint32_t)p2[i] << 16) | ((uint32_t)p1[i] << 8) | p0[i];
     }
 }
 
@@ -320,6 +412,28 @@ int launch_histogram_u16(const uint16_t* in, const uint16_t* in2, uint64_t n, ui
     hipLaunchKernelGGL(hist_u16_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, in2, n,
                        reinterpret_cast<unsigned long long*>(hist_hi),
                        reinterpret_cast<unsigned long long*>(hist_lo));
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_histogram_u32(const uint32_t* in, uint64_t n, uint64_t* hist, int accumulate, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!accumulate) {
+        const int rc = launch_fill_zero(hist, 4 * 256 * sizeof(uint64_t), stream);
+        if (rc) return rc;
+    }
+    if (n == 0) return LECB_OK;
+    const int grid = grid_for(n / 4 + 1, HIST_THREADS * 8, device_cu_count() * 2);
+    hipLaunchKernelGGL(hist_u32_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, n,
+                       reinterpret_cast<unsigned long long*>(hist));
+    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
+}
+
+int launch_merge4(const uint8_t* p3, const uint8_t* p2, const uint8_t* p1, const uint8_t* p0, uint64_t n,
+                  uint32_t* out, void* stream) {
+    if (n == 0) return LECB_OK;
+    const int grid = grid_for(n / 16 + 1, BG_THREADS, device_cu_count() * 16);
+    hipLaunchKernelGGL(merge4_kernel, dim3(grid), dim3(BG_THREADS), 0,
+                       reinterpret_cast<hipStream_t>(stream), p3, p2, p1, p0, n, out);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

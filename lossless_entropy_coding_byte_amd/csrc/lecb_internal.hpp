@@ -84,7 +84,22 @@ int canonical_from_lengths(const uint8_t len[256], lecb_codebook* out);
 // Input kinds of the encode kernel.  ENC_PAIR codes both bytes of 16-bit
 // words in one pass: stream 0 = high bytes, stream 1 = low bytes.
 // ENC_PAIR_XOR: both planes of w0[i] ^ w1[i] (the incremental snapshot delta)
-enum EncodeMode { ENC_BYTES = 0, ENC_PLANE_LO = 1, ENC_PLANE_HI = 2, ENC_PAIR = 3, ENC_PAIR_XOR = 4 };
+// ENC_PAIR32_HI / ENC_PAIR32_LO: the two bytes of the upper / lower 16 bits of
+// 32-bit elements (bytes 3 and 2 / bytes 1 and 0), as two streams.
+enum EncodeMode {
+    ENC_BYTES = 0,
+    ENC_PLANE_LO = 1,
+    ENC_PLANE_HI = 2,
+    ENC_PAIR = 3,
+    ENC_PAIR_XOR = 4,
+    ENC_PAIR32_HI = 5,
+    ENC_PAIR32_LO = 6,
+    ENC_NUM_MODES = 7
+};
+// Modes that write two streams (st[0] and st[1]).
+constexpr bool two_stream_mode(int m) {
+    return m == ENC_PAIR || m == ENC_PAIR_XOR || m == ENC_PAIR32_HI || m == ENC_PAIR32_LO;
+}
 
 struct EncodeStream {
     const DeviceCodebook* cb;
@@ -95,13 +110,13 @@ struct EncodeStream {
 };
 
 struct EncodeLaunch {
-    const void* in;          // u8 symbols (ENC_BYTES) or u16 words
+    const void* in;          // u8 symbols (ENC_BYTES), u16 words or u32 elements (ENC_PAIR32_*)
     const void* in2;         // ENC_PAIR_XOR: the second u16 tensor (symbols of in ^ in2)
     int mode;                // EncodeMode
     uint64_t n;
     uint32_t chunk;
     uint64_t nc;
-    EncodeStream st[2];      // st[1] only for ENC_PAIR / ENC_PAIR_XOR
+    EncodeStream st[2];      // st[1] only for the two-stream modes
     int grid;                // upper bound on workgroups (persistent grid)
 };
 int launch_encode(const EncodeLaunch& a, void* stream);
@@ -130,6 +145,11 @@ int launch_histogram_u16(const uint16_t* in, const uint16_t* in2, uint64_t n, ui
 int launch_split(const uint16_t* in, uint64_t n, uint8_t* hi, uint8_t* lo, void* stream);
 int launch_merge(const uint8_t* hi, const uint8_t* lo, const uint16_t* w0, uint64_t n, uint16_t* out,
                  void* stream);
+// Byte planes of 32-bit elements: hist[0:256] = byte 3, ..., hist[768:1024] = byte 0.
+int launch_histogram_u32(const uint32_t* in, uint64_t n, uint64_t* hist, int accumulate, void* stream);
+// out[i] = p3[i] << 24 | p2[i] << 16 | p1[i] << 8 | p0[i]
+int launch_merge4(const uint8_t* p3, const uint8_t* p2, const uint8_t* p1, const uint8_t* p0, uint64_t n,
+                  uint32_t* out, void* stream);
 int launch_codebook_upload(const CodebookArgs& args, DeviceCodebook* blob, void* stream);
 int launch_fill_zero(void* ptr, uint64_t bytes, void* stream);
 int launch_result(lecb_result* r, uint64_t bytes, uint64_t bits, int32_t status, void* stream);

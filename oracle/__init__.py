@@ -8,10 +8,11 @@ step on the coding path:
 * ``stream``    -- chunked stream format, two independent encoders (bit-string
                    definition and vectorised numpy) and two independent decoders
                    (bit-by-bit canonical and lock-step lookup table);
-* ``bytegroup`` -- bf16 byte grouping (high / low byte planes) and the
-                   two-stream container;
+* ``bytegroup`` -- byte grouping (bf16: high / low byte planes; fp32: four
+                   byte planes) and the two-stream container;
 * ``metrics``   -- entropy, compressed-size identities and per-batch optimum;
-* ``drift``     -- the codebook refresh rule under distribution drift.
+* ``drift``     -- the codebook refresh rule under distribution drift;
+* ``subbyte``   -- 4-bit tensors: packed pairs against 16-symbol codes.
 
 Sources: "Single-Stage Huffman Encoder for ML Compression" (summary page of
 arXiv 2601.10673; sections Overview and Methodology) and "Lossless Compression
@@ -57,7 +58,8 @@ from .stream import (
     parse_table,
 )
 from .bytegroup import (split_bf16, merge_bf16, encode_bf16, decode_bf16, container_bytes, parse_container,
-                        snapshot_delta, apply_delta)
+                        snapshot_delta, apply_delta, split_fp32, merge_fp32, encode_fp32, decode_fp32)
+from . import subbyte
 from .metrics import entropy_bits, payload_bits_identity, per_batch_optimal_bits
 from .drift import payload_bits_or_none, drift_check, adaptive_codebooks
 
@@ -68,5 +70,5 @@ __all__ = [
     "chunk_word_counts", "parse_table", "split_bf16", "merge_bf16", "encode_bf16", "decode_bf16",
     "container_bytes", "parse_container", "entropy_bits", "payload_bits_identity",
     "per_batch_optimal_bits", "snapshot_delta", "apply_delta", "payload_bits_or_none", "drift_check",
-    "adaptive_codebooks",
+    "adaptive_codebooks", "split_fp32", "merge_fp32", "encode_fp32", "decode_fp32", "subbyte",
 ]

@@ -1,4 +1,4 @@
-"""Oracle: bf16 byte grouping and the two-stream, per-tensor container.
+"""Oracle: byte grouping (bf16: two planes, fp32: four) and the two-stream container.
 
 TEST INFRASTRUCTURE (see ``oracle/__init__.py``).
 
@@ -77,6 +77,46 @@ def snapshot_delta(w0, w1) -> np.ndarray:
 def apply_delta(w0, d) -> np.ndarray:
     """W1[i] = W0[i] ^ D[i]: the later snapshot from the earlier one and the delta."""
     return snapshot_delta(w0, d)
+
+
+def split_fp32(x) -> list[np.ndarray]:
+    """Four byte planes of 32-bit patterns x, most significant first:
+    plane p holds (x[i] >> (8 * (3 - p))) & 0xFF.
+
+    Byte grouping with a 4-byte group ("Lossless Compression for LLM Tensor
+    Incremental Snapshots", Technical framework step 1; Key design item 1
+    makes the byte-group size a design choice).  Reading: the same per-byte
+    planes as for bf16, one plane per byte position of the element."""
+    x = np.ascontiguousarray(x).view(np.uint32).ravel()
+    return [((x >> np.uint32(8 * (3 - p))) & np.uint32(0xFF)).astype(np.uint8) for p in range(4)]
+
+
+def merge_fp32(planes) -> np.ndarray:
+    """x[i] = sum over p of planes[p][i] << 8 * (3 - p) (the byte-group restore)."""
+    if len(planes) != 4:
+        raise ValueError("four planes expected")
+    x = np.zeros(np.asarray(planes[0]).size, dtype=np.uint32)
+    for p, plane in enumerate(planes):
+        x |= np.asarray(plane, dtype=np.uint32) << np.uint32(8 * (3 - p))
+    return x
+
+
+def encode_fp32(x, chunk: int, max_len: int = 16) -> dict:
+    """Per-tensor coding of a 32-bit tensor: per plane histogram, optimal codebook, stream."""
+    planes = split_fp32(x)
+    out = {"n": planes[0].size, "chunk": chunk, "max_len": max_len, "len": [], "stream": [], "bits": []}
+    for plane in planes:
+        ln = package_merge_lengths(histogram(plane), max_len)
+        stream, bits = encode(plane, ln, canonical_codes(ln), chunk)
+        out["len"].append(ln)
+        out["stream"].append(stream)
+        out["bits"].append(bits)
+    return out
+
+
+def decode_fp32(enc: dict) -> np.ndarray:
+    n, chunk = enc["n"], enc["chunk"]
+    return merge_fp32([decode(s, ln, chunk, n) for s, ln in zip(enc["stream"], enc["len"])])
 
 
 def encode_bf16(x, chunk: int, max_len: int = 16) -> dict:

@@ -338,6 +338,90 @@ def test_fused_snapshot_delta(n, chunk):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
 
 
+# ----------------------------------------------------------------------------- 32-bit elements, four planes
+
+@pytest.mark.parametrize("n", [1, 3, 4099, 1 << 20])
+def test_histogram_and_merge_fp32_exact(n):
+    _say(f"fp32 histogram/merge n={n}")
+    x = workloads.fp32_weights(n)
+    xd = to_dev(x.view(np.int32))
+    hist = torch.zeros(1024, dtype=torch.int64, device=DEV)
+    lecb.lecb_histogram_fp32(xd, hist)
+    h = hist.cpu().numpy().astype(np.uint64)
+    planes = oracle.split_fp32(x)
+    for p in range(4):
+        assert np.array_equal(h[256 * p:256 * (p + 1)], oracle.histogram(planes[p])), p
+    lecb.lecb_histogram_fp32(xd, hist, accumulate=True)
+    assert np.array_equal(hist.cpu().numpy().astype(np.uint64), 2 * h)
+    pd = [to_dev(pl) for pl in planes]
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    lecb.lecb_merge_fp32(pd, out)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
+
+
+@pytest.mark.parametrize("n,chunk", [(1, 256), (5000, 4096), (300_001, 16384), ((1 << 20) + 7, 65536)])
+def test_fp32_pertensor_pipeline(n, chunk):
+    """Four byte planes: histograms, codebooks and all four streams equal the
+    oracle's; both decode entries restore the 32-bit elements exactly."""
+    _say(f"fp32 per-tensor n={n} chunk={chunk}")
+    x = workloads.fp32_weights(n)
+    ref = oracle.encode_fp32(x, chunk)
+    xd = to_dev(x.view(np.int32))
+    hist = torch.zeros(1024, dtype=torch.int64, device=DEV)
+    blobs = [lecb.new_codebook_blob(DEV) for _ in range(4)]
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    outs = [torch.empty(cap, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    res = lecb.new_results(4, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    cbs = lecb.lecb_encode_fp32_pertensor(xd, n, chunk, 16, hist, blobs, outs, res, ws)
+    r = lecb.results_to_numpy(res)
+    for p in range(4):
+        assert int(r[p]["status"]) == 0, p
+        assert np.array_equal(cbs[p].lengths(), ref["len"][p]), p
+        assert int(r[p]["payload_bits"]) == ref["bits"][p], p
+        assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), ref["stream"][p]), p
+    scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    rd = lecb.new_results(4, DEV)
+    lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, out, scratch, rd, ws)
+    q = lecb.results_to_numpy(rd)
+    assert all(int(q[p]["status"]) == 0 for p in range(4))
+    assert [int(q[p]["payload_bits"]) for p in range(4)] == ref["bits"]
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
+    out.zero_()
+    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, scratch, rd, ws)
+    assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
+
+
+def test_fp32_fixed_codebooks_and_corrupt_plane():
+    """lecb_encode_fp32 with given codebooks (one per plane) and a corrupted
+    third stream: that plane's status is CORRUPT, the others stay OK."""
+    n, chunk = 70_000, 4096
+    x = workloads.fp32_weights(n)
+    planes = oracle.split_fp32(x)
+    lens = [codebook_for(pl, clamp=True) for pl in planes]
+    blobs = [lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV).blob for ln in lens]
+    xd = to_dev(x.view(np.int32))
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    outs = [torch.empty(cap, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    res = lecb.new_results(4, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    lecb.lecb_encode_fp32(xd, n, blobs, chunk, outs, res, ws)
+    r = lecb.results_to_numpy(res)
+    for p in range(4):
+        want, _ = oracle.encode(planes[p], lens[p], oracle.canonical_codes(lens[p]), chunk)
+        assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), want), p
+    # a chunk-table entry past the payload: plane 2's stream is corrupt
+    outs[2][0:4] = torch.tensor([255, 255, 255, 127], dtype=torch.uint8, device=DEV)
+    scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    rd = lecb.new_results(4, DEV)
+    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, scratch, rd, ws)
+    st = [int(v) for v in lecb.results_to_numpy(rd)["status"]]
+    assert st[2] == lecb.LECB_ERR_CORRUPT and st[0] == st[1] == st[3] == 0
+
+
 # ----------------------------------------------------------------------------- drift refresh
 
 @pytest.mark.parametrize("tol", [0, 20_000, 10**9])

@@ -1,4 +1,4 @@
-"""The five workloads at their full sizes, on the launch path the bench times.
+"""The workloads at their full sizes, on the launch path the bench times.
 
 Checked against the oracle element by element where it can (the offset table
 of every chunk for tensors up to 2^28 elements, and sampled chunks' payload
@@ -117,6 +117,38 @@ def _pertensor(name, x):
     return r
 
 
+def _pertensor32(name, x):
+    cfg = workloads.CONFIGS[name]
+    n, chunk = x.size, cfg["chunk"]
+    _say(f"{name}: n={n} chunk={chunk}")
+    xd = torch.from_numpy(x.view(np.int32)).to(DEV)
+    hist = torch.zeros(1024, dtype=torch.int64, device=DEV)
+    blobs = [lecb.new_codebook_blob(DEV) for _ in range(4)]
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    outs = [torch.empty(cap, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    res = lecb.new_results(4, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    cbs = lecb.lecb_encode_fp32_pertensor(xd, n, chunk, 16, hist, blobs, outs, res, ws)
+    r = lecb.results_to_numpy(res)
+    h = hist.cpu().numpy().astype(np.uint64)
+    planes = oracle.split_fp32(x)
+    for p in range(4):
+        assert int(r[p]["status"]) == 0
+        hp = h[256 * p:256 * (p + 1)]
+        assert np.array_equal(hp, oracle.histogram(planes[p]))
+        ln = cbs[p].lengths()
+        assert np.array_equal(ln, oracle.package_merge_lengths(hp, 16))
+        assert int(r[p]["payload_bits"]) == oracle.payload_bits_identity(hp, ln)
+        _sampled_parity(outs[p], planes[p], ln, chunk, n, _picks(oracle.num_chunks(n, chunk), 21 + p), True)
+    y = torch.empty(n, dtype=torch.int32, device=DEV)
+    scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
+    rd = lecb.new_results(4, DEV)
+    lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, scratch, rd, ws)
+    assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
+    assert torch.equal(y, xd)
+    return r
+
+
 def test_config_int8_fixed():
     x = workloads.int8_fixed(0)
     hist = np.sum([oracle.histogram(workloads.int8_fixed(k)) for k in (1, 2, 3, 4)], axis=0, dtype=np.uint64)
@@ -149,3 +181,19 @@ def test_config_int8_drift():
     r, h, ln = _fixed_mode("int8_drift", x, hist)
     # the stream expands where the data drift away from batch 0's code
     assert int(r["payload_bits"]) > 0
+
+
+def test_config_int4_packed():
+    """4-bit weights two per byte, coded as packed pairs with a fixed codebook
+    from warm-up batches; the pair code of the tensor is never longer than the
+    best 16-symbol code of its 4-bit values (oracle)."""
+    from oracle import subbyte
+
+    x = workloads.int4_packed(0)
+    hist = np.sum([oracle.histogram(workloads.int4_packed(k)) for k in (1, 2, 3, 4)], axis=0, dtype=np.uint64)
+    r, h, ln = _fixed_mode("int4_packed", x, hist)
+    assert oracle.per_batch_optimal_bits(h, 16) <= subbyte.nibble_code_bits(x, 8)
+
+
+def test_config_fp32_weights():
+    _pertensor32("fp32_weights", workloads.fp32_weights())

@@ -83,3 +83,39 @@ def test_snapshot_delta_pins():
     # the snapshot workload's delta is this operator
     ds, w0s, w1s = workloads.bf16_delta(1 << 16, return_snapshots=True)
     assert np.array_equal(oracle.snapshot_delta(w0s, w1s), ds)
+
+
+def test_fp32_planes_of_ieee_patterns():
+    # IEEE 754 binary32 patterns (sign | 8-bit exponent | 23-bit fraction):
+    # 1.0 = 0x3F800000, -2.5 = 0xC0200000, the float nearest pi = 0x40490FDB
+    pats = np.array([0x3F800000, 0xC0200000, 0x40490FDB], np.uint32)
+    assert np.array_equal(np.array([1.0, -2.5, np.pi], np.float32).view(np.uint32), pats)
+    planes = oracle.split_fp32(pats)
+    assert [p.tolist() for p in planes] == [[0x3F, 0xC0, 0x40], [0x80, 0x20, 0x49], [0x00, 0x00, 0x0F],
+                                            [0x00, 0x00, 0xDB]]
+    # little-endian bytes: plane p is byte 3 - p of the stored element
+    b = pats.view(np.uint8).reshape(-1, 4)
+    for p in range(4):
+        assert np.array_equal(planes[p], b[:, 3 - p])
+    assert np.array_equal(oracle.merge_fp32(planes), pats)
+
+
+def test_fp32_upper_planes_are_the_bf16_planes():
+    # a float32 whose low 16 bits are zero is a bf16 value: its two upper
+    # planes are that bf16 value's high and low byte planes
+    x32 = workloads.bf16_to_f32(workloads.bf16_weights(4096)).view(np.uint32)
+    p = oracle.split_fp32(x32)
+    hi, lo = oracle.split_bf16((x32 >> 16).astype(np.uint16))
+    assert np.array_equal(p[0], hi) and np.array_equal(p[1], lo)
+    assert not p[2].any() and not p[3].any()
+
+
+def test_fp32_round_trip_and_plane_streams():
+    x = workloads.fp32_weights(40_000)
+    enc = oracle.encode_fp32(x, 4096)
+    assert np.array_equal(oracle.decode_fp32(enc), x)
+    planes = oracle.split_fp32(x)
+    for p in range(4):
+        assert enc["bits"][p] == oracle.payload_bits_identity(oracle.histogram(planes[p]), enc["len"][p])
+    # the sign/exponent plane compresses, the low mantissa bytes hardly at all
+    assert enc["bits"][0] < 4 * x.size and enc["bits"][3] > 7.9 * x.size

@@ -21,7 +21,13 @@ stand-ins take their shapes and value distributions from the workload list:
 * ``bf16_delta``   512 Mi bf16 XOR snapshot delta, W1 = bf16(W0 + N(0, 1e-4^2)),
                    chunk 65536;
 * ``int8_drift``   64 batches of 64 Mi int8 from round(N(0, s_k^2)),
-                   s_k = 10 + 30 k / 63, chunk 4096.
+                   s_k = 10 + 30 k / 63, chunk 4096;
+* ``int4_packed``  64 Mi int4 weights, two per byte (32 Mi bytes): N(0, 1)
+                   values quantised per group of 128 with scale absmax / 7,
+                   four warm-up batches from other seeds, chunk 4096 (a 4-bit
+                   tensor; the pages name 4-bit data as open work);
+* ``fp32_weights`` 64 Mi float32 from N(0, 0.02^2) with 0.1 % outliers x20
+                   (the bf16_weights recipe kept in float32), chunk 16384.
 
 RNG: ``numpy.random.default_rng([cfg, role, block])`` (PCG64).  Tensors are
 drawn in blocks of 2^26 elements; block j uses ``block = j``.  ``scale`` < 1
@@ -40,6 +46,8 @@ CONFIGS = {
     "int8_acts": dict(cfg=3, kind="u8", mode="fixed", n=8 * 2048 * 2048, chunk=4096),
     "bf16_delta": dict(cfg=4, kind="bf16", mode="pertensor", n=1 << 29, chunk=65536),
     "int8_drift": dict(cfg=5, kind="u8", mode="fixed", n=1 << 32, chunk=4096),
+    "int4_packed": dict(cfg=6, kind="u8", mode="fixed", n=1 << 25, chunk=4096),
+    "fp32_weights": dict(cfg=7, kind="fp32", mode="pertensor", n=1 << 26, chunk=16384),
 }
 
 
@@ -96,6 +104,31 @@ def int8_drift_batch(k: int, n: int = BLOCK) -> np.ndarray:
     return q8(rng(5, 0, k).normal(0.0, drift_sigma(k), n))
 
 
+# --------------------------------------------------------------------------- int4, two per byte
+
+INT4_GROUP = 128
+
+
+def int4_values(role: int = 0, count: int = 1 << 26) -> np.ndarray:
+    """Signed 4-bit weights as int8 in -7..7: N(0, 1) draws quantised per group of
+    INT4_GROUP consecutive values with scale = group absmax / 7 (round half to even).
+    ``count`` is a multiple of INT4_GROUP."""
+    x = rng(6, role, 0).normal(0.0, 1.0, count).reshape(-1, INT4_GROUP)
+    scale = np.abs(x).max(axis=1, keepdims=True) / 7.0
+    return np.clip(np.rint(x / scale), -8, 7).astype(np.int8).ravel()
+
+
+def pack_int4(v: np.ndarray) -> np.ndarray:
+    """Two 4-bit two's-complement values per byte: value 2i in bits 0-3, 2i+1 in bits 4-7."""
+    u = (np.asarray(v, dtype=np.int8).view(np.uint8) & 0x0F).reshape(-1, 2)
+    return (u[:, 0] | (u[:, 1] << 4)).astype(np.uint8)
+
+
+def int4_packed(role: int = 0, nbytes: int = 1 << 25) -> np.ndarray:
+    """Eval batch (role 0) or warm-up batch (roles 1..4) of packed int4 weights, as bytes."""
+    return pack_int4(int4_values(role, 2 * nbytes))
+
+
 # --------------------------------------------------------------------------- bf16, per tensor
 
 def bf16_weights(n: int = 1 << 26) -> np.ndarray:
@@ -108,6 +141,19 @@ def bf16_weights(n: int = 1 << 26) -> np.ndarray:
         u = g.random(m)
         w[u < 0.001] *= np.float32(20.0)
         out[s:s + m] = bf16_bits(w)
+    return out
+
+
+def fp32_weights(n: int = 1 << 26) -> np.ndarray:
+    """float32 weights N(0, 0.02^2) with i.i.d. 0.1 % outliers scaled x20, as uint32 bit patterns."""
+    out = np.empty(n, dtype=np.uint32)
+    for j, s in enumerate(range(0, n, BLOCK)):
+        m = min(BLOCK, n - s)
+        g = rng(7, 0, j)
+        w = g.normal(0.0, 0.02, m).astype(np.float32)
+        u = g.random(m)
+        w[u < 0.001] *= np.float32(20.0)
+        out[s:s + m] = w.view(np.uint32)
     return out
 
 
