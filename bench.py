@@ -219,17 +219,26 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         state = {}
 
         def step():
-            # the C per-tensor entry: histograms -> read back -> host codebooks ->
-            # upload -> two-plane encode; decode takes the sizes on the device
+            # the C per-tensor entry: histograms -> codebooks built on the device
+            # -> two-plane encode; decode takes the sizes on the device (no host
+            # synchronisation anywhere in the step)
             T.start("encode")
-            cb_hi, cb_lo = lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist_d, blob_hi, blob_lo,
-                                                           out_hi, out_lo, res, ws)
+            lecb.lecb_encode_bf16_pertensor_nosync(xd, n, chunk, 16, hist_d, blob_hi, blob_lo, out_hi, out_lo,
+                                                   res, ws)
             T.stop("encode")
             T.start("decode")
             lecb.lecb_decode_bf16_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, y,
                                                scratch, res_dec, ws)
             T.stop("decode")
-            state.update(cb_hi=cb_hi, cb_lo=cb_lo)
+
+        def host_codebook_step():
+            # the same step with the codebooks built on the host (histogram read-back)
+            lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist_d, blob_hi, blob_lo, out_hi, out_lo, res, ws)
+            lecb.lecb_decode_bf16_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, y,
+                                               scratch, res_dec, ws)
+
+        def codebooks():
+            state.update(cb_hi=lecb.lecb_codebook_download(blob_hi), cb_lo=lecb.lecb_codebook_download(blob_lo))
 
         def kernels_alone(reps):
             # each kernel of the path on its own, same buffers and codebooks
@@ -239,6 +248,9 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
                 T.start("histogram")
                 lecb.lecb_histogram_bf16(xd, hist_d[:256], hist_d[256:])
                 T.stop("histogram")
+                T.start("codebook_build")
+                lecb.lecb_build_codebook_device(hist_d, [blob_hi, blob_lo])
+                T.stop("codebook_build")
                 T.start("encode_pair")
                 lecb.lecb_encode_bf16(xd, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res, ws)
                 T.stop("encode_pair")
@@ -267,15 +279,21 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         state = {}
 
         def step():
-            # histograms -> read back -> four host codebooks -> upload -> two
-            # two-plane encodes; decode takes the sizes on the device
+            # histograms -> four codebooks built on the device -> two two-plane
+            # encodes; decode takes the sizes on the device
             T.start("encode")
-            cbs = lecb.lecb_encode_fp32_pertensor(xd, n, chunk, 16, hist_d, blobs, outs, res, ws)
+            lecb.lecb_encode_fp32_pertensor_nosync(xd, n, chunk, 16, hist_d, blobs, outs, res, ws)
             T.stop("encode")
             T.start("decode")
             lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, scratch, res_dec, ws)
             T.stop("decode")
-            state.update(cbs=cbs)
+
+        def host_codebook_step():
+            lecb.lecb_encode_fp32_pertensor(xd, n, chunk, 16, hist_d, blobs, outs, res, ws)
+            lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, scratch, res_dec, ws)
+
+        def codebooks():
+            state.update(cbs=[lecb.lecb_codebook_download(b) for b in blobs])
 
         def kernels_alone(reps):
             r = lecb.results_to_numpy(res)
@@ -283,6 +301,9 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
                 T.start("histogram")
                 lecb.lecb_histogram_fp32(xd, hist_d)
                 T.stop("histogram")
+                T.start("codebook_build")
+                lecb.lecb_build_codebook_device(hist_d, blobs)
+                T.stop("codebook_build")
                 T.start("encode_pair")
                 lecb.lecb_encode_fp32(xd, n, blobs, chunk, outs, res, ws)
                 T.stop("encode_pair")
@@ -321,6 +342,11 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         def kernels_alone(reps):
             pass  # one kernel each: the encode and decode timers above
 
+        host_codebook_step = None
+
+        def codebooks():
+            pass
+
         nbytes = n
 
     for _ in range(warmup):
@@ -334,6 +360,19 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
     wall = time.perf_counter() - t0
     kernels_alone(max(3, min(steps, 10)))
     torch.cuda.synchronize()
+    # per-tensor mode, for comparison: the step with host-built codebooks
+    # (histogram read-back, package-merge on the host, upload)
+    host_ms = None
+    if host_codebook_step is not None:
+        for _ in range(2):
+            host_codebook_step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            host_codebook_step()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t1) / steps * 1e3
+    codebooks()
 
     # ---------------- checks of the timed outputs, on the device and through the
     # library only (the element-by-element parity against the oracle at these
@@ -392,8 +431,8 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
 
         def fused_step():
             T.start("fused_encode")
-            lecb.lecb_encode_bf16_delta_pertensor(w0d, w1d, n, chunk, 16, hist_d, blob_hi, blob_lo,
-                                                  out_hi, out_lo, res, ws)
+            lecb.lecb_encode_bf16_delta_pertensor_nosync(w0d, w1d, n, chunk, 16, hist_d, blob_hi, blob_lo,
+                                                         out_hi, out_lo, res, ws)
             T.stop("fused_encode")
             T.start("fused_decode")
             lecb.lecb_decode_bf16_delta_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, w0d,
@@ -516,6 +555,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         fused=fused,
         batches=batches,
         subbyte=subbyte,
+        host_ms=host_ms,
         accounting=accounting,
         nbytes=nbytes, ms_step=ms_step, enc_ms=enc_ms, dec_ms=dec_ms, kernels=kernels,
         sizes=sizes, container=container, parity=parity,
@@ -574,11 +614,14 @@ def roofline(cfg, info):
         s = info["sizes"][0]
         algo = {"encode": n + s, "decode": s + n}
         k = {"encode": info["enc_ms"], "decode": info["dec_ms"]}
-    dom = max(k, key=lambda lbl: k[lbl])
+    dom = max((lbl for lbl in k if lbl in algo), key=lambda lbl: k[lbl])
     ach = algo[dom] / (k[dom] * 1e-3) / 1e9
     per_kernel = {lbl: {"ms": round(k[lbl], 4), "GBps": round(algo[lbl] / (k[lbl] * 1e-3) / 1e9, 1),
                         "frac": round(algo[lbl] / (k[lbl] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
                   for lbl in k if lbl in algo and k[lbl] > 0}
+    if k.get("codebook_build"):
+        # one workgroup per plane, latency-bound: time only
+        per_kernel["codebook_build"] = {"ms": round(k["codebook_build"], 4)}
     return {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(cfg["name"], dom),
@@ -654,6 +697,7 @@ def main():
         "batches": info["batches"],
         "fused_delta": info["fused"],
         "int4": info["subbyte"],
+        "pertensor_host_codebooks_ms_per_step": None if info["host_ms"] is None else round(info["host_ms"], 4),
         "kernels": per_kernel,
         "roofline": roof,
         "cpu_baseline": cpu,

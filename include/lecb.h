@@ -372,6 +372,45 @@ int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo
                      uint32_t chunk, uint64_t n, uint16_t* d_out, uint8_t* d_scratch,
                      lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ codebooks built on the device
+ * Per-shard codebook generation ("Single-Stage Huffman Encoder for ML
+ * Compression", Overview: frequency analysis, codebook generation, codebook
+ * transmission) done on the accelerator, so a per-tensor encode needs no host
+ * round trip.  The result is bit for bit the one of lecb_build_codebook with
+ * the same arguments (package-merge, the same tie rule, canonical codes), in
+ * the device layout of lecb_codebook_upload. */
+
+/* For p < nplanes (1..4): the codebook of histogram d_hist[256*p : 256*p+256]
+ * (u64 counts in device memory), frequencies raised to min_freq, lengths at
+ * most max_len (1..16), written to the device codebook d_blob[p] (host array
+ * of device pointers, each lecb_device_codebook_bytes() bytes).  When no code
+ * exists (every count 0 after the clamp, or more than 2^max_len coded
+ * values) the device codebook holds no code word, and an encode with it
+ * reports LECB_ERR_UNCODED_SYMBOL.  Two launches on `stream`; no
+ * synchronisation. */
+int lecb_build_codebook_device(const uint64_t* d_hist, uint32_t nplanes, uint32_t max_len,
+                               uint32_t min_freq, void* const d_blob[], void* stream);
+
+/* The host codebook (lengths and canonical codes) of a device codebook, e.g.
+ * for the container header.  Copies 1 KiB and synchronises `stream`. */
+int lecb_codebook_download(const void* d_blob, lecb_codebook* out, void* stream);
+
+/* Per-tensor encodes whose codebooks are built on the device: plane
+ * histograms -> lecb_build_codebook_device (min_freq 0) -> the two-plane /
+ * four-plane encode.  Same streams as the _pertensor entries; they neither
+ * synchronise nor return host codebooks (lecb_codebook_download gives them). */
+int lecb_encode_bf16_pertensor_nosync(const uint16_t* d_in, uint64_t n, uint32_t chunk,
+                                      uint32_t max_len, uint64_t* d_hist, void* d_blob_hi,
+                                      void* d_blob_lo, uint8_t* d_out_hi, uint64_t cap_hi,
+                                      uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2,
+                                      void* d_ws, uint64_t ws_bytes, void* stream);
+int lecb_encode_bf16_delta_pertensor_nosync(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                                            uint32_t chunk, uint32_t max_len, uint64_t* d_hist,
+                                            void* d_blob_hi, void* d_blob_lo, uint8_t* d_out_hi,
+                                            uint64_t cap_hi, uint8_t* d_out_lo, uint64_t cap_lo,
+                                            lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
+                                            void* stream);
+
 /* ------------------------------------------------------------------ 32-bit elements (fp32)
  * Byte grouping with four planes ("Lossless Compression for LLM Tensor
  * Incremental Snapshots", Technical framework step 1 and Key design item 1,
@@ -408,6 +447,14 @@ int lecb_encode_fp32_pertensor(const uint32_t* d_in, uint64_t n, uint32_t chunk,
                                uint64_t* d_hist, void* const d_blob[4], lecb_codebook cb[4],
                                uint8_t* const d_out[4], const uint64_t cap[4], lecb_result* d_res4,
                                void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* lecb_encode_fp32_pertensor with the four codebooks built on the device
+ * (see lecb_build_codebook_device): never synchronises. */
+int lecb_encode_fp32_pertensor_nosync(const uint32_t* d_in, uint64_t n, uint32_t chunk,
+                                      uint32_t max_len, uint64_t* d_hist, void* const d_blob[4],
+                                      uint8_t* const d_out[4], const uint64_t cap[4],
+                                      lecb_result* d_res4, void* d_ws, uint64_t ws_bytes,
+                                      void* stream);
 
 /* Decode the four streams (exact sizes in stream_bytes[4]) and restore the
  * 32-bit elements.  d_scratch: 4*align16(n) bytes of device memory for the

@@ -116,6 +116,14 @@ _SIGNATURES = {
     "lecb_decode_bf16_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16_planes": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_build_codebook_device": (_int, [_vp, _u32, _u32, _u32, _vp, _vp]),
+    "lecb_codebook_download": (_int, [_vp, ctypes.POINTER(lecb_codebook), _vp]),
+    "lecb_encode_bf16_pertensor_nosync": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _u64, _vp, _u64,
+                                                 _vp, _vp, _u64, _vp]),
+    "lecb_encode_bf16_delta_pertensor_nosync": (_int, [_vp, _vp, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _u64,
+                                                       _vp, _u64, _vp, _vp, _u64, _vp]),
+    "lecb_encode_fp32_pertensor_nosync": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _u64,
+                                                 _vp]),
     "lecb_histogram_fp32": (_int, [_vp, _u64, _vp, _int, _vp]),
     "lecb_merge_fp32": (_int, [_vp, _u64, _vp, _vp]),
     "lecb_encode_fp32": (_int, [_vp, _u64, _vp, _u32, _vp, _vp, _vp, _vp, _u64, _vp]),
@@ -425,6 +433,44 @@ def lecb_decode_bf16(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, out
                                    _ptr(blob_lo), chunk, n, _ptr(out), _ptr(scratch), _ptr(res2),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_decode_bf16")
+
+
+# --------------------------------------------------------------------------- codebooks built on the device
+
+def lecb_build_codebook_device(hist, blobs, max_len: int = 16, min_freq: int = 0, stream=None) -> None:
+    """Codebook of each 256-bin histogram in hist (int64[256 * len(blobs)]) into the device blobs."""
+    ptrs = (ctypes.c_void_p * len(blobs))(*[b.data_ptr() for b in blobs])
+    _check(load().lecb_build_codebook_device(_ptr(hist), len(blobs), max_len, min_freq, ptrs, _stream(stream)),
+           "lecb_build_codebook_device")
+
+
+def lecb_codebook_download(blob, stream=None) -> lecb_codebook:
+    cb = lecb_codebook()
+    _check(load().lecb_codebook_download(_ptr(blob), ctypes.byref(cb), _stream(stream)), "lecb_codebook_download")
+    return cb
+
+
+def lecb_encode_bf16_pertensor_nosync(x, n, chunk, max_len, hist, blob_hi, blob_lo, out_hi, out_lo, res2, ws,
+                                      stream=None) -> None:
+    _check(load().lecb_encode_bf16_pertensor_nosync(
+        _ptr(x), n, chunk, max_len, _ptr(hist), _ptr(blob_hi), _ptr(blob_lo), _ptr(out_hi), out_hi.numel(),
+        _ptr(out_lo), out_lo.numel(), _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        "lecb_encode_bf16_pertensor_nosync")
+
+
+def lecb_encode_bf16_delta_pertensor_nosync(w0, w1, n, chunk, max_len, hist, blob_hi, blob_lo, out_hi, out_lo,
+                                            res2, ws, stream=None) -> None:
+    _check(load().lecb_encode_bf16_delta_pertensor_nosync(
+        _ptr(w0), _ptr(w1), n, chunk, max_len, _ptr(hist), _ptr(blob_hi), _ptr(blob_lo), _ptr(out_hi),
+        out_hi.numel(), _ptr(out_lo), out_lo.numel(), _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "lecb_encode_bf16_delta_pertensor_nosync")
+
+
+def lecb_encode_fp32_pertensor_nosync(x, n, chunk, max_len, hist, blobs, outs, res4, ws, stream=None) -> None:
+    _check(load().lecb_encode_fp32_pertensor_nosync(_ptr(x), n, chunk, max_len, _ptr(hist), _ptrs4(blobs),
+                                                    _ptrs4(outs), _caps4(outs), _ptr(res4), _ptr(ws),
+                                                    ws.numel() * ws.element_size(), _stream(stream)),
+           "lecb_encode_fp32_pertensor_nosync")
 
 
 # --------------------------------------------------------------------------- 32-bit elements, four planes

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblecb.so")
 ARCH = "gfx950"
 
-SOURCES = ["kernels_misc.hip", "kernels_encode.hip", "kernels_decode.hip", "codebook.cpp", "api.cpp"]
+SOURCES = ["kernels_misc.hip", "kernels_codebook.hip", "kernels_encode.hip", "kernels_decode.hip", "codebook.cpp",
+           "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

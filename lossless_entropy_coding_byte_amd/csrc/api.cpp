@@ -474,6 +474,74 @@ int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo
     return rc;
 }
 
+// ---------------------------------------------------------------- codebooks built on the device
+
+int lecb_build_codebook_device(const uint64_t* d_hist, uint32_t nplanes, uint32_t max_len, uint32_t min_freq,
+                               void* const d_blob[], void* stream) {
+    if (!d_hist || !aligned16(d_hist) || !d_blob || nplanes < 1 || nplanes > 4 || max_len < 1 || max_len > 16)
+        return LECB_ERR_INVALID_ARG;
+    const uint64_t* h[4];
+    DeviceCodebook* cb[4];
+    for (uint32_t p = 0; p < nplanes; ++p) {
+        if (!d_blob[p] || !aligned16(d_blob[p])) return LECB_ERR_INVALID_ARG;
+        h[p] = d_hist + 256 * p;
+        cb[p] = reinterpret_cast<DeviceCodebook*>(d_blob[p]);
+    }
+    return launch_build_codebooks(h, cb, (int)nplanes, max_len, min_freq, stream);
+}
+
+int lecb_codebook_download(const void* d_blob, lecb_codebook* out, void* stream) {
+    if (!d_blob || !aligned16(d_blob) || !out) return LECB_ERR_INVALID_ARG;
+    uint32_t enc[256];
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(enc, reinterpret_cast<const DeviceCodebook*>(d_blob)->enc, sizeof(enc),
+                       hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return LECB_ERR_HIP;
+    uint8_t len[256];
+    for (int k = 0; k < 256; ++k) len[k] = (uint8_t)(enc[k] & 31u);
+    return canonical_from_lengths(len, out);
+}
+
+int lecb_encode_bf16_pertensor_nosync(const uint16_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,
+                                      uint64_t* d_hist, void* d_blob_hi, void* d_blob_lo, uint8_t* d_out_hi,
+                                      uint64_t cap_hi, uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2,
+                                      void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) || !d_res2)
+        return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        int rc = launch_result(d_res2, 0, 0, LECB_OK, stream);
+        return rc ? rc : launch_result(d_res2 + 1, 0, 0, LECB_OK, stream);
+    }
+    void* blobs[2] = {d_blob_hi, d_blob_lo};
+    int rc = lecb_histogram_bf16(d_in, n, d_hist, d_hist + 256, 0, stream);
+    if (!rc) rc = lecb_build_codebook_device(d_hist, 2, max_len, 0, blobs, stream);
+    if (!rc)
+        rc = lecb_encode_bf16(d_in, n, d_blob_hi, d_blob_lo, chunk, d_out_hi, cap_hi, d_out_lo, cap_lo, d_res2,
+                              d_ws, ws_bytes, stream);
+    return rc;
+}
+
+int lecb_encode_bf16_delta_pertensor_nosync(const uint16_t* d_w0, const uint16_t* d_w1, uint64_t n,
+                                            uint32_t chunk, uint32_t max_len, uint64_t* d_hist,
+                                            void* d_blob_hi, void* d_blob_lo, uint8_t* d_out_hi,
+                                            uint64_t cap_hi, uint8_t* d_out_lo, uint64_t cap_lo,
+                                            lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) || !d_res2)
+        return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        int rc = launch_result(d_res2, 0, 0, LECB_OK, stream);
+        return rc ? rc : launch_result(d_res2 + 1, 0, 0, LECB_OK, stream);
+    }
+    void* blobs[2] = {d_blob_hi, d_blob_lo};
+    int rc = lecb_histogram_bf16_delta(d_w0, d_w1, n, d_hist, d_hist + 256, 0, stream);
+    if (!rc) rc = lecb_build_codebook_device(d_hist, 2, max_len, 0, blobs, stream);
+    if (!rc)
+        rc = lecb_encode_bf16_delta(d_w0, d_w1, n, d_blob_hi, d_blob_lo, chunk, d_out_hi, cap_hi, d_out_lo, cap_lo,
+                                    d_res2, d_ws, ws_bytes, stream);
+    return rc;
+}
+
 // ---------------------------------------------------------------- 32-bit elements, four planes
 
 int lecb_histogram_fp32(const uint32_t* d_in, uint64_t n, uint64_t* d_hist, int accumulate, void* stream) {
@@ -527,6 +595,26 @@ int lecb_encode_fp32_pertensor(const uint32_t* d_in, uint64_t n, uint32_t chunk,
     if (rc) return rc;
     for (int k = 0; k < 4 && !rc; ++k) rc = lecb_build_codebook(h + 256 * k, max_len, 0, &cb[k]);
     for (int k = 0; k < 4 && !rc; ++k) rc = lecb_codebook_upload(&cb[k], d_blob[k], stream);
+    if (!rc) rc = lecb_encode_fp32(d_in, n, d_blob, chunk, d_out, cap, d_res4, d_ws, ws_bytes, stream);
+    return rc;
+}
+
+int lecb_encode_fp32_pertensor_nosync(const uint32_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,
+                                      uint64_t* d_hist, void* const d_blob[4], uint8_t* const d_out[4],
+                                      const uint64_t cap[4], lecb_result* d_res4, void* d_ws, uint64_t ws_bytes,
+                                      void* stream) {
+    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) || !d_blob ||
+        !d_out || !cap || !d_res4)
+        return LECB_ERR_INVALID_ARG;
+    if (n == 0) {
+        for (int k = 0; k < 4; ++k) {
+            const int rc = launch_result(d_res4 + k, 0, 0, LECB_OK, stream);
+            if (rc) return rc;
+        }
+        return LECB_OK;
+    }
+    int rc = lecb_histogram_fp32(d_in, n, d_hist, 0, stream);
+    if (!rc) rc = lecb_build_codebook_device(d_hist, 4, max_len, 0, d_blob, stream);
     if (!rc) rc = lecb_encode_fp32(d_in, n, d_blob, chunk, d_out, cap, d_res4, d_ws, ws_bytes, stream);
     return rc;
 }

@@ -1,5 +1,4 @@
-// Histogram, byte-group split/merge (16- and 32-bit elements), device codebook
-// construction, fill.
+// Histogram, byte-group split/merge (16- and 32-bit elements), fill.
 //
 // Histogram: "Single-Stage Huffman Encoder for ML Compression", Overview
 // (frequency analysis) and Methodology step 1; "Lossless Compression for LLM
@@ -297,54 +296,6 @@ __global__ __launch_bounds__(BG_THREADS) void merge4_kernel(const uint8_t* __res
     }
 }
 
-// Device codebook: encode table and decode tables from the canonical
-// description passed by value.  Grid covers the LUT_SIZE lookup entries.
-__global__ __launch_bounds__(256) void codebook_kernel(CodebookArgs a, DeviceCodebook* cb) {
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < 256) {
-        cb->enc[t] = a.enc[t];
-        cb->sorted[t] = a.sorted[t];
-    }
-    if (t < 17) {
-        cb->first[t] = a.first[t];
-        cb->base[t] = a.base[t];
-        cb->limit[t] = t ? (a.first[t] + a.count[t]) << (16 - t) : 0;
-    }
-    if (t == 0) {
-        cb->max_len = a.max_len;
-        cb->num_coded = a.num_coded;
-        cb->pad[0] = cb->pad[1] = cb->pad[2] = 0;
-    }
-    if (t < LUT_SIZE) {
-        // canonical decode of the LUT_BITS-bit prefix t
-        uint16_t entry = 0;
-        for (int l = 1; l <= LUT_BITS; ++l) {
-            const uint32_t v = (uint32_t)t >> (LUT_BITS - l);
-            if (a.count[l] && v >= a.first[l] && v < a.first[l] + a.count[l]) {
-                entry = (uint16_t)((a.sorted[a.base[l] + v - a.first[l]] << 8) | l);
-                break;
-            }
-        }
-        cb->lut[t] = entry;
-        // how many code words follow one another wholly inside these bits
-        uint32_t used = 0, cnt = 0;
-        for (;;) {
-            uint32_t len = 0;
-            for (uint32_t l = 1; l + used <= (uint32_t)LUT_BITS; ++l) {
-                const uint32_t v = ((uint32_t)t >> (LUT_BITS - used - l)) & ((1u << l) - 1u);
-                if (a.count[l] && v >= a.first[l] && v < a.first[l] + a.count[l]) {
-                    len = l;
-                    break;
-                }
-            }
-            if (!len) break;
-            used += len;
-            ++cnt;
-        }
-        cb->mlut[t] = (uint8_t)((cnt << 4) | used);
-    }
-}
-
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* p, uint64_t bytes) {
     const uint64_t n16 = bytes / 16;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -451,12 +402,6 @@ int launch_merge(const uint8_t* hi, const uint8_t* lo, const uint16_t* w0, uint6
     const int grid = grid_for(n / 16 + 1, BG_THREADS, device_cu_count() * 16);
     hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(BG_THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), hi, lo, w0, n, out);
-    return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
-}
-
-int launch_codebook_upload(const CodebookArgs& args, DeviceCodebook* blob, void* stream) {
-    hipLaunchKernelGGL(codebook_kernel, dim3(LUT_SIZE / 256), dim3(256), 0,
-                       reinterpret_cast<hipStream_t>(stream), args, blob);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

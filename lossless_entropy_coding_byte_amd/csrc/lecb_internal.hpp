@@ -151,6 +151,9 @@ int launch_histogram_u32(const uint32_t* in, uint64_t n, uint64_t* hist, int acc
 int launch_merge4(const uint8_t* p3, const uint8_t* p2, const uint8_t* p1, const uint8_t* p0, uint64_t n,
                   uint32_t* out, void* stream);
 int launch_codebook_upload(const CodebookArgs& args, DeviceCodebook* blob, void* stream);
+// Codebooks built on the device from n (1..4) device histograms of 256 u64.
+int launch_build_codebooks(const uint64_t* const* hist, DeviceCodebook* const* cb, int n, uint32_t max_len,
+                           uint32_t min_freq, void* stream);
 int launch_fill_zero(void* ptr, uint64_t bytes, void* stream);
 int launch_result(lecb_result* r, uint64_t bytes, uint64_t bits, int32_t status, void* stream);
 

@@ -338,6 +338,122 @@ def test_fused_snapshot_delta(n, chunk):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
 
 
+# ----------------------------------------------------------------------------- codebooks built on the device
+
+def _test_histograms(seed, count):
+    r = np.random.default_rng(seed)
+    out = []
+    for t in range(count):
+        kind = t % 6
+        if kind == 0:
+            h = r.integers(0, 1000, 256)
+        elif kind == 1:
+            h = np.zeros(256, np.int64)
+            h[r.integers(0, 256, r.integers(1, 8))] = r.integers(1, 50)
+        elif kind == 2:
+            h = (r.pareto(1.0, 256) * 10).astype(np.int64)
+        elif kind == 3:
+            h = np.full(256, 7)
+            h[: r.integers(0, 256)] = 0
+        elif kind == 4:
+            h = (2.0 ** r.integers(0, 40, 256)).astype(np.int64)
+            h[r.random(256) < 0.3] = 0
+        else:
+            h = r.integers(0, 3, 256)
+        out.append(h.astype(np.uint64))
+    return out
+
+
+@pytest.mark.parametrize("max_len,min_freq", [(16, 0), (16, 1), (12, 0), (9, 1), (8, 0), (1, 0)])
+def test_device_codebook_build_matches_host(max_len, min_freq):
+    """The device builder's codebook blob equals, byte for byte, the blob of the
+    host builder + upload (lengths, codes, tables); where no code exists the
+    device codebook has no code word.  Lengths also against the oracle."""
+    hists = _test_histograms(40 + max_len, 48)
+    for g in range(0, len(hists), 4):
+        group = hists[g:g + 4]
+        hd = to_dev(np.concatenate(group).view(np.int64))
+        blobs = [lecb.new_codebook_blob(DEV) for _ in group]
+        lecb.lecb_build_codebook_device(hd, blobs, max_len, min_freq)
+        for h, blob in zip(group, blobs):
+            F = oracle.codebook_frequencies([h], min_freq)
+            m = int((F > 0).sum())
+            got = lecb.lecb_codebook_download(blob)
+            if m == 0 or m > (1 << max_len):
+                assert not got.lengths().any()
+                continue
+            assert np.array_equal(got.lengths(), oracle.package_merge_lengths(F, max_len))
+            ref = lecb.new_codebook_blob(DEV)
+            lecb.lecb_codebook_upload(lecb.lecb_build_codebook(h, max_len, min_freq), ref)
+            assert torch.equal(blob, ref)
+
+
+def test_device_codebook_special_cases():
+    cases = [np.zeros(256, np.uint64)]
+    one = np.zeros(256, np.uint64); one[77] = 5; cases.append(one)
+    two = np.zeros(256, np.uint64); two[3] = 1; two[200] = 1 << 40; cases.append(two)
+    cases.append(np.ones(256, np.uint64))
+    hd = to_dev(np.concatenate(cases).view(np.int64))
+    blobs = [lecb.new_codebook_blob(DEV) for _ in cases]
+    for g in range(0, 4):
+        lecb.lecb_build_codebook_device(hd[256 * g:], blobs[g:g + 1], 16, 0)
+    ln = [lecb.lecb_codebook_download(b).lengths() for b in blobs]
+    assert not ln[0].any()
+    assert ln[1][77] == 1 and ln[1].sum() == 1
+    assert ln[2][3] == 1 and ln[2][200] == 1 and ln[2].sum() == 2
+    assert np.all(ln[3] == 8)
+    # empty codebook: an encode with it reports the uncoded byte
+    xd = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    out = torch.empty(lecb.lecb_encoded_bound(4096, 4096), dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(1, DEV)
+    lecb.lecb_encode(xd, 4096, blobs[0], 4096, out, res, lecb.new_workspace(4096, 4096, DEV))
+    assert int(lecb.results_to_numpy(res)[0]["status"]) == lecb.LECB_ERR_UNCODED_SYMBOL
+
+
+@pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), ((1 << 20) + 3, 65536)])
+def test_pertensor_nosync_entries(n, chunk):
+    """bf16, snapshot-delta and fp32 per-tensor encodes with device-built
+    codebooks: streams and lengths equal the oracle's."""
+    _say(f"per-tensor nosync n={n} chunk={chunk}")
+    cap = lecb.lecb_encoded_bound(n, chunk)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    # bf16
+    x = workloads.bf16_weights(n)
+    ref = oracle.encode_bf16(x, chunk)
+    hist = torch.zeros(512, dtype=torch.int64, device=DEV)
+    bh, bl = lecb.new_codebook_blob(DEV), lecb.new_codebook_blob(DEV)
+    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(2, DEV)
+    lecb.lecb_encode_bf16_pertensor_nosync(to_dev(x.view(np.int16)), n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
+    r = lecb.results_to_numpy(res)
+    assert np.array_equal(lecb.lecb_codebook_download(bh).lengths(), ref["len_hi"])
+    assert np.array_equal(lecb.lecb_codebook_download(bl).lengths(), ref["len_lo"])
+    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), ref["stream_hi"])
+    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), ref["stream_lo"])
+    # snapshot delta from the two snapshots
+    d, w0, w1 = workloads.bf16_delta(n, return_snapshots=True)
+    ref = oracle.encode_bf16(d, chunk)
+    lecb.lecb_encode_bf16_delta_pertensor_nosync(to_dev(w0.view(np.int16)), to_dev(w1.view(np.int16)), n, chunk,
+                                                 16, hist, bh, bl, oh, ol, res, ws)
+    r = lecb.results_to_numpy(res)
+    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), ref["stream_hi"])
+    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), ref["stream_lo"])
+    # fp32
+    x = workloads.fp32_weights(n)
+    ref = oracle.encode_fp32(x, chunk)
+    h4 = torch.zeros(1024, dtype=torch.int64, device=DEV)
+    blobs = [lecb.new_codebook_blob(DEV) for _ in range(4)]
+    outs = [torch.empty(cap, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    res4 = lecb.new_results(4, DEV)
+    lecb.lecb_encode_fp32_pertensor_nosync(to_dev(x.view(np.int32)), n, chunk, 16, h4, blobs, outs, res4, ws)
+    r = lecb.results_to_numpy(res4)
+    for p in range(4):
+        assert int(r[p]["status"]) == 0
+        assert np.array_equal(lecb.lecb_codebook_download(blobs[p]).lengths(), ref["len"][p])
+        assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), ref["stream"][p])
+
+
 # ----------------------------------------------------------------------------- 32-bit elements, four planes
 
 @pytest.mark.parametrize("n", [1, 3, 4099, 1 << 20])
