@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
 
+STEP_LABELS = ("histogram", "codebook_build", "encode_pair", "decode_pair", "merge")
 METRIC = "encode / decode GB/s of uncompressed input on 1 MI355X; % of HBM peak; ratio"
 HBM_PEAK_GBPS = 8000.0
 
@@ -190,6 +191,22 @@ class Timer:
         e.record()
         self.pairs[label][-1][1] = e
 
+    def chain(self, labels):
+        """Record events at the boundaries of consecutive launches: returns a
+        function to call after each one (label i spans boundary i to i + 1)."""
+        first = self.torch.cuda.Event(enable_timing=True)
+        first.record()
+        state = {"prev": first, "i": 0}
+
+        def mark():
+            e = self.torch.cuda.Event(enable_timing=True)
+            e.record()
+            self.pairs.setdefault(labels[state["i"]], []).append([state["prev"], e])
+            state["prev"] = e
+            state["i"] += 1
+
+        return mark
+
     def mean_ms(self, label, skip=0):
         ps = self.pairs.get(label, [])[skip:]
         return float(np.mean([a.elapsed_time(b) for a, b in ps])) if ps else 0.0
@@ -218,49 +235,38 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=dev)
         state = {}
 
+        half = (n + 15) // 16 * 16
+        p_hi, p_lo = scratch[:n], scratch[half:half + n]
+
         def step():
-            # the C per-tensor entry: histograms -> codebooks built on the device
-            # -> two-plane encode; decode takes the sizes on the device (no host
-            # synchronisation anywhere in the step)
-            T.start("encode")
-            lecb.lecb_encode_bf16_pertensor_nosync(xd, n, chunk, 16, hist_d, blob_hi, blob_lo, out_hi, out_lo,
-                                                   res, ws)
-            T.stop("encode")
-            T.start("decode")
-            lecb.lecb_decode_bf16_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, y,
-                                               scratch, res_dec, ws)
-            T.stop("decode")
+            # the per-tensor path kernel by kernel -- what
+            # lecb_encode_bf16_pertensor_nosync and lecb_decode_bf16_from_results
+            # enqueue -- with events on the launch stream between the kernels:
+            # histograms -> codebooks built on the device -> two-plane encode ->
+            # two-plane decode (stream sizes read on the device) -> merge.
+            # No host synchronisation anywhere in the step.
+            mark = T.chain(STEP_LABELS)
+            lecb.lecb_histogram_bf16(xd, hist_d[:256], hist_d[256:])
+            mark()
+            lecb.lecb_build_codebook_device(hist_d, [blob_hi, blob_lo])
+            mark()
+            lecb.lecb_encode_bf16(xd, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res, ws)
+            mark()
+            lecb.lecb_decode_bf16_planes_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, p_hi, p_lo,
+                                                      res_dec, ws)
+            mark()
+            lecb.lecb_merge_bf16(p_hi, p_lo, y)
+            mark()
 
         def host_codebook_step():
-            # the same step with the codebooks built on the host (histogram read-back)
+            # the same step through the composite entries, codebooks built on the
+            # host (histogram read-back, package-merge, upload)
             lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist_d, blob_hi, blob_lo, out_hi, out_lo, res, ws)
             lecb.lecb_decode_bf16_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, y,
                                                scratch, res_dec, ws)
 
         def codebooks():
             state.update(cb_hi=lecb.lecb_codebook_download(blob_hi), cb_lo=lecb.lecb_codebook_download(blob_lo))
-
-        def kernels_alone(reps):
-            # each kernel of the path on its own, same buffers and codebooks
-            r = lecb.results_to_numpy(res)
-            half = (n + 15) // 16 * 16
-            for _ in range(reps):
-                T.start("histogram")
-                lecb.lecb_histogram_bf16(xd, hist_d[:256], hist_d[256:])
-                T.stop("histogram")
-                T.start("codebook_build")
-                lecb.lecb_build_codebook_device(hist_d, [blob_hi, blob_lo])
-                T.stop("codebook_build")
-                T.start("encode_pair")
-                lecb.lecb_encode_bf16(xd, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res, ws)
-                T.stop("encode_pair")
-                T.start("decode_pair")
-                lecb.lecb_decode_bf16_planes(out_hi, int(r[0]["bytes"]), out_lo, int(r[1]["bytes"]), blob_hi,
-                                             blob_lo, chunk, n, scratch, scratch[half:], res_dec, ws)
-                T.stop("decode_pair")
-                T.start("merge")
-                lecb.lecb_merge_bf16(scratch[:n], scratch[half:half + n], y)
-                T.stop("merge")
 
         nbytes = 2 * n
     elif cfg["kind"] == "fp32":
@@ -279,14 +285,25 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         state = {}
 
         def step():
-            # histograms -> four codebooks built on the device -> two two-plane
-            # encodes; decode takes the sizes on the device
-            T.start("encode")
-            lecb.lecb_encode_fp32_pertensor_nosync(xd, n, chunk, 16, hist_d, blobs, outs, res, ws)
-            T.stop("encode")
-            T.start("decode")
-            lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, scratch, res_dec, ws)
-            T.stop("decode")
+            # kernel by kernel, as lecb_encode_fp32_pertensor_nosync and
+            # lecb_decode_fp32_from_results enqueue it: histograms -> four
+            # codebooks built on the device -> two two-plane encodes -> two
+            # two-plane decodes (sizes read on the device) -> merge
+            mark = T.chain(STEP_LABELS)
+            lecb.lecb_histogram_fp32(xd, hist_d)
+            mark()
+            lecb.lecb_build_codebook_device(hist_d, blobs)
+            mark()
+            lecb.lecb_encode_fp32(xd, n, blobs, chunk, outs, res, ws)
+            mark()
+            for h in range(2):
+                off = 2 * h * lecb.RESULT_DTYPE.itemsize
+                lecb.lecb_decode_bf16_planes_from_results(outs[2 * h], outs[2 * h + 1], res[off:], blobs[2 * h],
+                                                          blobs[2 * h + 1], chunk, n, planes[2 * h],
+                                                          planes[2 * h + 1], res_dec[off:], ws)
+            mark()
+            lecb.lecb_merge_fp32(planes, y)
+            mark()
 
         def host_codebook_step():
             lecb.lecb_encode_fp32_pertensor(xd, n, chunk, 16, hist_d, blobs, outs, res, ws)
@@ -294,29 +311,6 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
 
         def codebooks():
             state.update(cbs=[lecb.lecb_codebook_download(b) for b in blobs])
-
-        def kernels_alone(reps):
-            r = lecb.results_to_numpy(res)
-            for _ in range(reps):
-                T.start("histogram")
-                lecb.lecb_histogram_fp32(xd, hist_d)
-                T.stop("histogram")
-                T.start("codebook_build")
-                lecb.lecb_build_codebook_device(hist_d, blobs)
-                T.stop("codebook_build")
-                T.start("encode_pair")
-                lecb.lecb_encode_fp32(xd, n, blobs, chunk, outs, res, ws)
-                T.stop("encode_pair")
-                T.start("decode_pair")
-                for h in range(2):
-                    lecb.lecb_decode_bf16_planes(outs[2 * h], int(r[2 * h]["bytes"]), outs[2 * h + 1],
-                                                 int(r[2 * h + 1]["bytes"]), blobs[2 * h], blobs[2 * h + 1],
-                                                 chunk, n, planes[2 * h], planes[2 * h + 1],
-                                                 res_dec[2 * h * lecb.RESULT_DTYPE.itemsize:], ws)
-                T.stop("decode_pair")
-                T.start("merge")
-                lecb.lecb_merge_fp32(planes, y)
-                T.stop("merge")
 
         nbytes = 4 * n
     else:
@@ -339,9 +333,6 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
             lecb.lecb_decode_from_result(out, res, dcb.blob, chunk, n, y, res_dec, ws)
             T.stop("decode")
 
-        def kernels_alone(reps):
-            pass  # one kernel each: the encode and decode timers above
-
         host_codebook_step = None
 
         def codebooks():
@@ -358,8 +349,6 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernels_alone(max(3, min(steps, 10)))
-    torch.cuda.synchronize()
     # per-tensor mode, for comparison: the step with host-built codebooks
     # (histogram read-back, package-merge on the host, upload)
     host_ms = None
@@ -467,12 +456,12 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
 
     # ---------------- timings
     ms_step = wall / steps * 1e3
-    enc_ms, dec_ms = T.mean_ms("encode"), T.mean_ms("decode")
-    kernels = {}
-    for label in T.pairs:
-        if label in ("encode", "decode"):
-            continue
-        kernels[label] = T.mean_ms(label)
+    kernels = {label: T.mean_ms(label) for label in T.pairs if label not in ("encode", "decode")}
+    if cfg["kind"] in ("bf16", "fp32"):
+        enc_ms = sum(kernels[lb] for lb in ("histogram", "codebook_build", "encode_pair"))
+        dec_ms = kernels["decode_pair"] + kernels["merge"]
+    else:
+        enc_ms, dec_ms = T.mean_ms("encode"), T.mean_ms("decode")
     # ---------------- size accounting per stream (histogram kernel + host stats)
     accounting = []
     for name, h, ln in zip(names, hists, lengths_out):

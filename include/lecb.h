@@ -355,6 +355,15 @@ int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_
                             uint32_t chunk, uint64_t n, uint8_t* d_out_hi, uint8_t* d_out_lo,
                             lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
 
+/* lecb_decode_bf16_planes with both streams' sizes taken on the device from
+ * the two results an encode wrote (d_enc_res2, hi then lo): the two byte
+ * planes, not merged.  Errors as lecb_decode_from_result. */
+int lecb_decode_bf16_planes_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
+                                         const lecb_result* d_enc_res2, const void* d_blob_hi,
+                                         const void* d_blob_lo, uint32_t chunk, uint64_t n,
+                                         uint8_t* d_out_hi, uint8_t* d_out_lo, lecb_result* d_res2,
+                                         void* d_ws, uint64_t ws_bytes, void* stream);
+
 /* lecb_decode_bf16 with both streams' sizes taken on the device from the
  * two results an encode wrote (d_enc_res2, hi then lo), so a per-tensor
  * encode -> decode chain needs no host synchronisation; errors as in

@@ -114,6 +114,8 @@ _SIGNATURES = {
                                           _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
     "lecb_decode_from_result": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_bf16_planes_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp,
+                                                    _u64, _vp]),
     "lecb_decode_bf16_planes": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_build_codebook_device": (_int, [_vp, _u32, _u32, _u32, _vp, _vp]),
@@ -357,6 +359,16 @@ def lecb_decode_bf16_planes(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk,
                                           _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
                                           _stream(stream)),
            "lecb_decode_bf16_planes")
+
+
+def lecb_decode_bf16_planes_from_results(hi, lo, enc_res2, blob_hi, blob_lo, chunk, n, out_hi, out_lo, res2, ws,
+                                         stream=None) -> None:
+    """Both byte planes decoded in one launch, sizes read on the device from the encoder's results."""
+    _check(load().lecb_decode_bf16_planes_from_results(_ptr(hi), _ptr(lo), _ptr(enc_res2), _ptr(blob_hi),
+                                                       _ptr(blob_lo), chunk, n, _ptr(out_hi), _ptr(out_lo),
+                                                       _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
+                                                       _stream(stream)),
+           "lecb_decode_bf16_planes_from_results")
 
 
 def lecb_decode(stream_buf, stream_bytes, blob, chunk, n, out, res, ws, stream=None) -> None:

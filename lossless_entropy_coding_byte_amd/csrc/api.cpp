@@ -398,6 +398,19 @@ int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_
     return decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream);
 }
 
+int lecb_decode_bf16_planes_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
+                                         const lecb_result* d_enc_res2, const void* d_blob_hi,
+                                         const void* d_blob_lo, uint32_t chunk, uint64_t n,
+                                         uint8_t* d_out_hi, uint8_t* d_out_lo, lecb_result* d_res2,
+                                         void* d_ws, uint64_t ws_bytes, void* stream) {
+    if (!d_enc_res2) return LECB_ERR_INVALID_ARG;
+    const uint8_t* st[2] = {d_hi, d_lo};
+    const uint64_t sb[2] = {0, 0};
+    const void* bl[2] = {d_blob_hi, d_blob_lo};
+    uint8_t* out[2] = {d_out_hi, d_out_lo};
+    return decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream, d_enc_res2);
+}
+
 int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
                                uint32_t max_len, uint64_t* d_hist, void* d_blob_hi,
                                void* d_blob_lo, lecb_codebook* cb_hi, lecb_codebook* cb_lo,
