@@ -41,7 +41,8 @@ sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
 
-STEP_LABELS = ("histogram", "codebook_build", "encode_pair", "decode_pair", "merge")
+DEVICE_LABELS = ("histogram", "codebook_build", "encode_pair", "decode_pair", "merge")
+HOST_LABELS = ("histogram+codebooks", "encode_pair", "decode_pair", "merge")
 METRIC = "encode / decode GB/s of uncompressed input on 1 MI355X; % of HBM peak; ratio"
 HBM_PEAK_GBPS = 8000.0
 
@@ -238,18 +239,29 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         half = (n + 15) // 16 * 16
         p_hi, p_lo = scratch[:n], scratch[half:half + n]
 
-        def step():
+        def step_device(tm):
             # the per-tensor path kernel by kernel -- what
             # lecb_encode_bf16_pertensor_nosync and lecb_decode_bf16_from_results
             # enqueue -- with events on the launch stream between the kernels:
             # histograms -> codebooks built on the device -> two-plane encode ->
             # two-plane decode (stream sizes read on the device) -> merge.
             # No host synchronisation anywhere in the step.
-            mark = T.chain(STEP_LABELS)
+            mark = tm.chain(DEVICE_LABELS)
             lecb.lecb_histogram_bf16(xd, hist_d[:256], hist_d[256:])
             mark()
             lecb.lecb_build_codebook_device(hist_d, [blob_hi, blob_lo])
             mark()
+            tail(mark)
+
+        def step_host(tm):
+            # the same with the codebooks built on the host: histograms -> read
+            # back -> package-merge -> upload (what lecb_encode_bf16_pertensor does)
+            mark = tm.chain(HOST_LABELS)
+            lecb.lecb_pertensor_codebooks(xd, n, 16, hist_d, [blob_hi, blob_lo])
+            mark()
+            tail(mark)
+
+        def tail(mark):
             lecb.lecb_encode_bf16(xd, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res, ws)
             mark()
             lecb.lecb_decode_bf16_planes_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, p_hi, p_lo,
@@ -257,13 +269,6 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
             mark()
             lecb.lecb_merge_bf16(p_hi, p_lo, y)
             mark()
-
-        def host_codebook_step():
-            # the same step through the composite entries, codebooks built on the
-            # host (histogram read-back, package-merge, upload)
-            lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist_d, blob_hi, blob_lo, out_hi, out_lo, res, ws)
-            lecb.lecb_decode_bf16_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, y,
-                                               scratch, res_dec, ws)
 
         def codebooks():
             state.update(cb_hi=lecb.lecb_codebook_download(blob_hi), cb_lo=lecb.lecb_codebook_download(blob_lo))
@@ -284,16 +289,25 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         planes = [scratch[k * plane:k * plane + n] for k in range(4)]
         state = {}
 
-        def step():
+        def step_device(tm):
             # kernel by kernel, as lecb_encode_fp32_pertensor_nosync and
             # lecb_decode_fp32_from_results enqueue it: histograms -> four
             # codebooks built on the device -> two two-plane encodes -> two
             # two-plane decodes (sizes read on the device) -> merge
-            mark = T.chain(STEP_LABELS)
+            mark = tm.chain(DEVICE_LABELS)
             lecb.lecb_histogram_fp32(xd, hist_d)
             mark()
             lecb.lecb_build_codebook_device(hist_d, blobs)
             mark()
+            tail(mark)
+
+        def step_host(tm):
+            mark = tm.chain(HOST_LABELS)
+            lecb.lecb_pertensor_codebooks(xd, n, 16, hist_d, blobs)
+            mark()
+            tail(mark)
+
+        def tail(mark):
             lecb.lecb_encode_fp32(xd, n, blobs, chunk, outs, res, ws)
             mark()
             for h in range(2):
@@ -304,10 +318,6 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
             mark()
             lecb.lecb_merge_fp32(planes, y)
             mark()
-
-        def host_codebook_step():
-            lecb.lecb_encode_fp32_pertensor(xd, n, chunk, 16, hist_d, blobs, outs, res, ws)
-            lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, scratch, res_dec, ws)
 
         def codebooks():
             state.update(cbs=[lecb.lecb_codebook_download(b) for b in blobs])
@@ -325,21 +335,29 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         y = torch.empty(n, dtype=torch.uint8, device=dev)
         state = {"cb": cb}
 
-        def step():
-            T.start("encode")
+        def step_device(tm):
+            tm.start("encode")
             lecb.lecb_encode(xd, n, dcb.blob, chunk, out, res, ws)
-            T.stop("encode")
-            T.start("decode")
+            tm.stop("encode")
+            tm.start("decode")
             lecb.lecb_decode_from_result(out, res, dcb.blob, chunk, n, y, res_dec, ws)
-            T.stop("decode")
+            tm.stop("decode")
 
-        host_codebook_step = None
+        step_host = None
 
         def codebooks():
             pass
 
         nbytes = n
 
+    # per-tensor mode has two codebook paths: built on the device (timed,
+    # no host synchronisation in the step) and built on the host (histogram
+    # read-back; timed afterwards for the report)
+    variants = {"device": step_device}
+    if step_host is not None:
+        variants["host"] = step_host
+    chosen = "device"
+    step = lambda: variants[chosen](T)  # noqa: E731
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -349,18 +367,18 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-tensor mode, for comparison: the step with host-built codebooks
-    # (histogram read-back, package-merge on the host, upload)
-    host_ms = None
-    if host_codebook_step is not None:
-        for _ in range(2):
-            host_codebook_step()
+    other_ms = None
+    if len(variants) > 1:
+        other = [v for v in variants if v != chosen][0]
+        # the other path ends with the same streams (both build the same codebooks)
+        for _ in range(warmup):
+            variants[other](Timer(torch))
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(steps):
-            host_codebook_step()
+            variants[other](Timer(torch))
         torch.cuda.synchronize()
-        host_ms = (time.perf_counter() - t1) / steps * 1e3
+        other_ms = {other: round((time.perf_counter() - t1) / steps * 1e3, 4)}
     codebooks()
 
     # ---------------- checks of the timed outputs, on the device and through the
@@ -458,7 +476,8 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
     ms_step = wall / steps * 1e3
     kernels = {label: T.mean_ms(label) for label in T.pairs if label not in ("encode", "decode")}
     if cfg["kind"] in ("bf16", "fp32"):
-        enc_ms = sum(kernels[lb] for lb in ("histogram", "codebook_build", "encode_pair"))
+        enc_ms = sum(kernels[lb] for lb in kernels if lb in ("histogram", "codebook_build", "histogram+codebooks",
+                                                              "encode_pair"))
         dec_ms = kernels["decode_pair"] + kernels["merge"]
     else:
         enc_ms, dec_ms = T.mean_ms("encode"), T.mean_ms("decode")
@@ -544,7 +563,8 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         fused=fused,
         batches=batches,
         subbyte=subbyte,
-        host_ms=host_ms,
+        codebook_path=chosen if cfg["kind"] in ("bf16", "fp32") else None,
+        other_ms=other_ms,
         accounting=accounting,
         nbytes=nbytes, ms_step=ms_step, enc_ms=enc_ms, dec_ms=dec_ms, kernels=kernels,
         sizes=sizes, container=container, parity=parity,
@@ -686,7 +706,8 @@ def main():
         "batches": info["batches"],
         "fused_delta": info["fused"],
         "int4": info["subbyte"],
-        "pertensor_host_codebooks_ms_per_step": None if info["host_ms"] is None else round(info["host_ms"], 4),
+        "pertensor_codebooks": info["codebook_path"],
+        "pertensor_other_codebooks_ms_per_step": info["other_ms"],
         "kernels": per_kernel,
         "roofline": roof,
         "cpu_baseline": cpu,

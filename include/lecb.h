@@ -404,6 +404,17 @@ int lecb_build_codebook_device(const uint64_t* d_hist, uint32_t nplanes, uint32_
  * for the container header.  Copies 1 KiB and synchronises `stream`. */
 int lecb_codebook_download(const void* d_blob, lecb_codebook* out, void* stream);
 
+/* The codebook half of a per-tensor encode, built on the host: plane
+ * histograms of the n elements of d_in (elem_bytes 2: bf16 planes, high byte
+ * first; 4: fp32 planes, byte 3 first) into d_hist (u64[256*elem_bytes]) ->
+ * read back (synchronises `stream` once) -> one optimal codebook per plane
+ * (min_freq 0) returned in cb[] and uploaded to d_blob[] (host array of
+ * device pointers).  lecb_encode_bf16 / lecb_encode_fp32 with these blobs
+ * then give the streams of lecb_encode_bf16_pertensor / _fp32_pertensor.
+ * n must be > 0. */
+int lecb_pertensor_codebooks(const void* d_in, uint32_t elem_bytes, uint64_t n, uint32_t max_len,
+                             uint64_t* d_hist, void* const d_blob[], lecb_codebook cb[], void* stream);
+
 /* Per-tensor encodes whose codebooks are built on the device: plane
  * histograms -> lecb_build_codebook_device (min_freq 0) -> the two-plane /
  * four-plane encode.  Same streams as the _pertensor entries; they neither

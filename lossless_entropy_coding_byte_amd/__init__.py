@@ -118,6 +118,7 @@ _SIGNATURES = {
                                                     _u64, _vp]),
     "lecb_decode_bf16_planes": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_pertensor_codebooks": (_int, [_vp, _u32, _u64, _u32, _vp, _vp, ctypes.POINTER(lecb_codebook), _vp]),
     "lecb_build_codebook_device": (_int, [_vp, _u32, _u32, _u32, _vp, _vp]),
     "lecb_codebook_download": (_int, [_vp, ctypes.POINTER(lecb_codebook), _vp]),
     "lecb_encode_bf16_pertensor_nosync": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _u64, _vp, _u64,
@@ -454,6 +455,18 @@ def lecb_build_codebook_device(hist, blobs, max_len: int = 16, min_freq: int = 0
     ptrs = (ctypes.c_void_p * len(blobs))(*[b.data_ptr() for b in blobs])
     _check(load().lecb_build_codebook_device(_ptr(hist), len(blobs), max_len, min_freq, ptrs, _stream(stream)),
            "lecb_build_codebook_device")
+
+
+def lecb_pertensor_codebooks(x, n, max_len, hist, blobs, stream=None) -> list:
+    """Plane histograms -> read back -> host codebooks -> upload; x is int16 (bf16) or int32 (fp32)."""
+    eb = x.element_size()
+    cbs = (lecb_codebook * eb)()
+    ptrs = (ctypes.c_void_p * len(blobs))(*[b.data_ptr() for b in blobs])
+    if len(blobs) != eb:
+        raise ValueError("one codebook blob per byte plane")
+    _check(load().lecb_pertensor_codebooks(_ptr(x), eb, n, max_len, _ptr(hist), ptrs, cbs, _stream(stream)),
+           "lecb_pertensor_codebooks")
+    return list(cbs)
 
 
 def lecb_codebook_download(blob, stream=None) -> lecb_codebook:

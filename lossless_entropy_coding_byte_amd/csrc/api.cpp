@@ -516,6 +516,23 @@ int lecb_codebook_download(const void* d_blob, lecb_codebook* out, void* stream)
     return canonical_from_lengths(len, out);
 }
 
+int lecb_pertensor_codebooks(const void* d_in, uint32_t elem_bytes, uint64_t n, uint32_t max_len,
+                             uint64_t* d_hist, void* const d_blob[], lecb_codebook cb[], void* stream) {
+    if ((elem_bytes != 2 && elem_bytes != 4) || max_len < 1 || max_len > 16 || !d_hist || !aligned16(d_hist) ||
+        !d_blob || !cb || n == 0)
+        return LECB_ERR_INVALID_ARG;
+    const int planes = (int)elem_bytes;
+    int rc = elem_bytes == 2
+                 ? lecb_histogram_bf16(static_cast<const uint16_t*>(d_in), n, d_hist, d_hist + 256, 0, stream)
+                 : lecb_histogram_fp32(static_cast<const uint32_t*>(d_in), n, d_hist, 0, stream);
+    if (rc) return rc;
+    const uint64_t* h = nullptr;
+    rc = read_back_hist(d_hist, 256 * planes, stream, &h);
+    for (int p = 0; p < planes && !rc; ++p) rc = lecb_build_codebook(h + 256 * p, max_len, 0, &cb[p]);
+    for (int p = 0; p < planes && !rc; ++p) rc = lecb_codebook_upload(&cb[p], d_blob[p], stream);
+    return rc;
+}
+
 int lecb_encode_bf16_pertensor_nosync(const uint16_t* d_in, uint64_t n, uint32_t chunk, uint32_t max_len,
                                       uint64_t* d_hist, void* d_blob_hi, void* d_blob_lo, uint8_t* d_out_hi,
                                       uint64_t cap_hi, uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2,

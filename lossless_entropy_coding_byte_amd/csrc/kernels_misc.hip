@@ -223,37 +223,40 @@ __global__ __launch_bounds__(BG_THREADS) void split_kernel(const uint16_t* __res
     }
 }
 
+// Restores: every lane writes 16 consecutive output bytes per store, and the
+// lanes of a wave write consecutive 16-byte pieces, so each store instruction
+// covers whole cache lines (no partly written lines reach HBM).
+
+// Elements 2*half, 2*half+1 from the high and low byte words h, l.
 __device__ inline uint32_t join2(uint32_t h, uint32_t l, int half) {
-    // elements 2*half, 2*half+1 from byte pairs
     const uint32_t hs = half ? (h >> 16) : h;
     const uint32_t ls = half ? (l >> 16) : l;
     return (ls & 0xFFu) | ((hs & 0xFFu) << 8) | ((ls & 0xFF00u) << 8) | ((hs & 0xFF00u) << 16);
 }
 
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// 8 elements per lane and step: 8 bytes of each plane in, 16 bytes out.
 // w0 != nullptr: out = w0 ^ (hi << 8 | lo) (a snapshot from its delta)
 __global__ __launch_bounds__(BG_THREADS) void merge_kernel(const uint8_t* __restrict__ hi,
                                                            const uint8_t* __restrict__ lo,
                                                            const uint16_t* __restrict__ w0,
                                                            uint64_t n, uint16_t* __restrict__ out) {
-    const uint64_t n16 = n / 16;
+    const uint64_t n8 = n / 8;
     const uint64_t stride = (uint64_t)gridDim.x * BG_THREADS;
-    for (uint64_t i = (uint64_t)blockIdx.x * BG_THREADS + threadIdx.x; i < n16; i += stride) {
-        const v4u h = ld_stream(reinterpret_cast<const uint4*>(hi) + i);
-        const v4u l = ld_stream(reinterpret_cast<const uint4*>(lo) + i);
-        v4u a, b;
-        a.x = join2(h.x, l.x, 0); a.y = join2(h.x, l.x, 1);
-        a.z = join2(h.y, l.y, 0); a.w = join2(h.y, l.y, 1);
-        b.x = join2(h.z, l.z, 0); b.y = join2(h.z, l.z, 1);
-        b.z = join2(h.w, l.w, 0); b.w = join2(h.w, l.w, 1);
-        if (w0) {
-            a ^= ld_stream(reinterpret_cast<const uint4*>(w0) + 2 * i);
-            b ^= ld_stream(reinterpret_cast<const uint4*>(w0) + 2 * i + 1);
-        }
-        st_stream(reinterpret_cast<uint4*>(out) + 2 * i, a);
-        st_stream(reinterpret_cast<uint4*>(out) + 2 * i + 1, b);
+    for (uint64_t i = (uint64_t)blockIdx.x * BG_THREADS + threadIdx.x; i < n8; i += stride) {
+        const v2u h = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(hi) + i);
+        const v2u l = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(lo) + i);
+        v4u a;
+        a.x = join2(h.x, l.x, 0);
+        a.y = join2(h.x, l.x, 1);
+        a.z = join2(h.y, l.y, 0);
+        a.w = join2(h.y, l.y, 1);
+        if (w0) a ^= ld_stream(reinterpret_cast<const uint4*>(w0) + i);
+        st_stream(reinterpret_cast<uint4*>(out) + i, a);
     }
     if (blockIdx.x == gridDim.x - 1) {
-        for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += BG_THREADS)
+        for (uint64_t i = n8 * 8 + threadIdx.x; i < n; i += BG_THREADS)
             out[i] = (uint16_t)((((uint16_t)hi[i] << 8) | lo[i]) ^ (w0 ? w0[i] : 0));
     }
 }
@@ -265,33 +268,28 @@ __device__ inline uint32_t join4(uint32_t w3, uint32_t w2, uint32_t w1, uint32_t
            (((w3 >> sh) & 0xFFu) << 24);
 }
 
-// 16 elements per thread: one 16-byte load per plane, four 16-byte stores.
+// 4 elements per lane and step: 4 bytes of each plane in, 16 bytes out.
 __global__ __launch_bounds__(BG_THREADS) void merge4_kernel(const uint8_t* __restrict__ p3,
                                                             const uint8_t* __restrict__ p2,
                                                             const uint8_t* __restrict__ p1,
                                                             const uint8_t* __restrict__ p0, uint64_t n,
                                                             uint32_t* __restrict__ out) {
-    const uint64_t n16 = n / 16;
+    const uint64_t n4 = n / 4;
     const uint64_t stride = (uint64_t)gridDim.x * BG_THREADS;
-    for (uint64_t i = (uint64_t)blockIdx.x * BG_THREADS + threadIdx.x; i < n16; i += stride) {
-        const v4u a3 = ld_stream(reinterpret_cast<const uint4*>(p3) + i);
-        const v4u a2 = ld_stream(reinterpret_cast<const uint4*>(p2) + i);
-        const v4u a1 = ld_stream(reinterpret_cast<const uint4*>(p1) + i);
-        const v4u a0 = ld_stream(reinterpret_cast<const uint4*>(p0) + i);
-        const uint32_t w3[4] = {a3.x, a3.y, a3.z, a3.w}, w2[4] = {a2.x, a2.y, a2.z, a2.w};
-        const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w}, w0[4] = {a0.x, a0.y, a0.z, a0.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v4u o;
-            o.x = join4(w3[q], w2[q], w1[q], w0[q], 0);
-            o.y = join4(w3[q], w2[q], w1[q], w0[q], 1);
-            o.z = join4(w3[q], w2[q], w1[q], w0[q], 2);
-            o.w = join4(w3[q], w2[q], w1[q], w0[q], 3);
-            st_stream(reinterpret_cast<uint4*>(out) + 4 * i + q, o);
-        }
+    for (uint64_t i = (uint64_t)blockIdx.x * BG_THREADS + threadIdx.x; i < n4; i += stride) {
+        const uint32_t w3 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p3) + i);
+        const uint32_t w2 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p2) + i);
+        const uint32_t w1 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p1) + i);
+        const uint32_t w0 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p0) + i);
+        v4u o;
+        o.x = join4(w3, w2, w1, w0, 0);
+        o.y = join4(w3, w2, w1, w0, 1);
+        o.z = join4(w3, w2, w1, w0, 2);
+        o.w = join4(w3, w2, w1, w0, 3);
+        st_stream(reinterpret_cast<uint4*>(out) + i, o);
     }
     if (blockIdx.x == gridDim.x - 1) {
-        for (uint64_t i = n16 * 16 + threadIdx.x; i < n; i += BG_THREADS)
+        for (uint64_t i = n4 * 4 + threadIdx.x; i < n; i += BG_THREADS)
             out[i] = ((uint32_t)p3[i] << 24) | ((uint32_t)p2[i] << 16) | ((uint32_t)p1[i] << 8) | p0[i];
     }
 }
@@ -344,7 +342,9 @@ int launch_histogram_u8(const uint8_t* in, uint64_t n, uint64_t* hist, int accum
         if (rc) return rc;
     }
     if (n == 0) return LECB_OK;
-    const int grid = grid_for(n / 16 + 1, HIST_THREADS * 8, device_cu_count() * 4);
+    // one workgroup per compute unit: fewer flushes of the 256 bins into the
+    // same global counters (measured best for this kernel)
+    const int grid = grid_for(n / 16 + 1, HIST_THREADS * 8, device_cu_count());
     hipLaunchKernelGGL(hist_u8_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, n,
                        reinterpret_cast<unsigned long long*>(hist));
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
@@ -354,12 +354,19 @@ int launch_histogram_u16(const uint16_t* in, const uint16_t* in2, uint64_t n, ui
                          uint64_t* hist_lo, int accumulate, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (!accumulate) {
-        int rc = launch_fill_zero(hist_hi, 256 * sizeof(uint64_t), stream);
-        if (!rc) rc = launch_fill_zero(hist_lo, 256 * sizeof(uint64_t), stream);
+        // one fill when the two histograms are adjacent (the usual layout)
+        int rc;
+        if (hist_lo == hist_hi + 256) {
+            rc = launch_fill_zero(hist_hi, 512 * sizeof(uint64_t), stream);
+        } else {
+            rc = launch_fill_zero(hist_hi, 256 * sizeof(uint64_t), stream);
+            if (!rc) rc = launch_fill_zero(hist_lo, 256 * sizeof(uint64_t), stream);
+        }
         if (rc) return rc;
     }
     if (n == 0) return LECB_OK;
-    const int grid = grid_for(n / 8 + 1, HIST_THREADS * 8, device_cu_count() * 4);
+    // two workgroups per compute unit (measured best: fewer global flushes)
+    const int grid = grid_for(n / 8 + 1, HIST_THREADS * 8, device_cu_count() * 2);
     hipLaunchKernelGGL(hist_u16_kernel, dim3(grid), dim3(HIST_THREADS), 0, s, in, in2, n,
                        reinterpret_cast<unsigned long long*>(hist_hi),
                        reinterpret_cast<unsigned long long*>(hist_lo));
@@ -382,7 +389,7 @@ int launch_histogram_u32(const uint32_t* in, uint64_t n, uint64_t* hist, int acc
 int launch_merge4(const uint8_t* p3, const uint8_t* p2, const uint8_t* p1, const uint8_t* p0, uint64_t n,
                   uint32_t* out, void* stream) {
     if (n == 0) return LECB_OK;
-    const int grid = grid_for(n / 16 + 1, BG_THREADS, device_cu_count() * 16);
+    const int grid = grid_for(n / 4 + 1, BG_THREADS, device_cu_count() * 16);
     hipLaunchKernelGGL(merge4_kernel, dim3(grid), dim3(BG_THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), p3, p2, p1, p0, n, out);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
@@ -399,7 +406,7 @@ int launch_split(const uint16_t* in, uint64_t n, uint8_t* hi, uint8_t* lo, void*
 int launch_merge(const uint8_t* hi, const uint8_t* lo, const uint16_t* w0, uint64_t n, uint16_t* out,
                  void* stream) {
     if (n == 0) return LECB_OK;
-    const int grid = grid_for(n / 16 + 1, BG_THREADS, device_cu_count() * 16);
+    const int grid = grid_for(n / 8 + 1, BG_THREADS, device_cu_count() * 16);
     hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(BG_THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), hi, lo, w0, n, out);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
