@@ -615,3 +615,77 @@ def decode_bytes(stream_buf, stream_bytes: int, dcb: DeviceCodebook, chunk: int,
     ws = ws if ws is not None else new_workspace(n, chunk, dev)
     lecb_decode(stream_buf, stream_bytes, dcb.blob, chunk, n, out, res, ws)
     return out, res
+
+
+# --------------------------------------------------------------------------- tensor-level helpers
+
+def encode(x, dcb: DeviceCodebook, chunk: int):
+    """Fixed-codebook encode of a uint8 device tensor: (stream buffer, result tensor)."""
+    return encode_bytes(x, dcb, chunk)
+
+
+def decode(stream_buf, stream_bytes: int, dcb: DeviceCodebook, chunk: int, n: int):
+    """Decode a stream back to n bytes: (uint8 tensor, result tensor)."""
+    return decode_bytes(stream_buf, stream_bytes, dcb, chunk, n)
+
+
+def encode_bf16(x, chunk: int, max_len: int = 16) -> np.ndarray:
+    """Per-tensor coding of a 16-bit tensor on its device, written as the container
+    (header with both plane codebooks' lengths, then both streams) in host memory.
+
+    The codebooks are built on the device; the host reads the two results and
+    lengths once, to size and label the container."""
+    import torch
+
+    dev = x.device
+    xv = x.contiguous().view(torch.int16).view(-1)
+    n = xv.numel()
+    cap = max(16, lecb_encoded_bound(n, chunk, max_len))
+    hist = torch.zeros(512, dtype=torch.int64, device=dev)
+    bh, bl = new_codebook_blob(dev), new_codebook_blob(dev)
+    oh = torch.empty(cap, dtype=torch.uint8, device=dev)
+    ol = torch.empty(cap, dtype=torch.uint8, device=dev)
+    res = new_results(2, dev)
+    ws = new_workspace(n, chunk, dev)
+    if n:
+        lecb_encode_bf16_pertensor_nosync(xv, n, chunk, max_len, hist, bh, bl, oh, ol, res, ws)
+    r = results_to_numpy(res)
+    for k in range(2):
+        if int(r[k]["status"]) != LECB_OK:
+            raise LecbError(int(r[k]["status"]), "encode_bf16")
+    len_hi = lecb_codebook_download(bh).lengths() if n else np.zeros(256, np.uint8)
+    len_lo = lecb_codebook_download(bl).lengths() if n else np.zeros(256, np.uint8)
+    sh, sl = int(r[0]["bytes"]), int(r[1]["bytes"])
+    head = lecb_container_write_header(n, chunk, max_len, len_hi, len_lo, sh, sl)
+    pad = (-sh) % 16
+    return np.concatenate([head, oh[:sh].cpu().numpy(), np.zeros(pad, np.uint8), ol[:sl].cpu().numpy()])
+
+
+def decode_bf16(container, device):
+    """Decode a container written by encode_bf16 into a 16-bit tensor (int16 view) on device."""
+    import torch
+
+    buf = np.ascontiguousarray(np.asarray(container, dtype=np.uint8))
+    h = lecb_container_read_header(buf)
+    n, chunk, sh, sl = h["n"], h["chunk"], h["bytes_hi"], h["bytes_lo"]
+    out = torch.empty(max(n, 1), dtype=torch.int16, device=device)
+    if n == 0:
+        return out[:0]
+    off_lo = CONTAINER_HEADER_BYTES + sh + (-sh) % 16
+    if buf.size != off_lo + sl:
+        raise LecbError(LECB_ERR_CORRUPT, "decode_bf16: container size")
+    dh = torch.zeros(sh + 16, dtype=torch.uint8, device=device)
+    dl = torch.zeros(sl + 16, dtype=torch.uint8, device=device)
+    dh[:sh] = torch.from_numpy(buf[CONTAINER_HEADER_BYTES:CONTAINER_HEADER_BYTES + sh]).to(device)
+    dl[:sl] = torch.from_numpy(buf[off_lo:off_lo + sl]).to(device)
+    ch = DeviceCodebook.upload(lecb_codebook_from_lengths(h["len_hi"]), device)
+    cl = DeviceCodebook.upload(lecb_codebook_from_lengths(h["len_lo"]), device)
+    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=device)
+    res = new_results(2, device)
+    ws = new_workspace(n, chunk, device)
+    lecb_decode_bf16(dh, sh, dl, sl, ch.blob, cl.blob, chunk, n, out, scratch, res, ws)
+    r = results_to_numpy(res)
+    for k in range(2):
+        if int(r[k]["status"]) != LECB_OK:
+            raise LecbError(int(r[k]["status"]), "decode_bf16")
+    return out

@@ -729,3 +729,28 @@ def test_corrupt_streams_set_status():
     # a size below the header is rejected on the host
     with pytest.raises(lecb.LecbError):
         gpu_decode(ref[: hb - 4], dcb, 4096, x.size)
+
+
+# ----------------------------------------------------------------------------- tensor-level helpers
+
+@pytest.mark.parametrize("n,chunk", [(1, 256), (70_001, 16384)])
+def test_tensor_helpers_and_container(n, chunk):
+    """encode / decode on uint8 tensors, and the per-tensor bf16 container:
+    byte-identical to the oracle's container, decoded back exactly."""
+    _say(f"tensor helpers n={n} chunk={chunk}")
+    x = workloads.bf16_weights(n)
+    t = to_dev(x.view(np.int16)).view(torch.bfloat16)
+    buf = lecb.encode_bf16(t, chunk)
+    assert np.array_equal(buf, oracle.container_bytes(oracle.encode_bf16(x, chunk)))
+    y = lecb.decode_bf16(buf, DEV)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), x)
+    b = workloads.int8_fixed(0, n)
+    ln = codebook_for(b, clamp=True)
+    dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+    s, res = lecb.encode(to_dev(b), dcb, chunk)
+    r = lecb.results_to_numpy(res)[0]
+    want, _ = oracle.encode(b, ln, oracle.canonical_codes(ln), chunk)
+    assert np.array_equal(s[: int(r["bytes"])].cpu().numpy(), want)
+    out, rd = lecb.decode(s, int(r["bytes"]), dcb, chunk, n)
+    assert int(lecb.results_to_numpy(rd)[0]["status"]) == 0
+    assert np.array_equal(out[:n].cpu().numpy(), b)
