@@ -55,7 +55,7 @@ uint64_t header_of(uint64_t n, uint32_t chunk) {
 }
 
 uint64_t ws_bytes_of(uint64_t n, uint32_t chunk) {
-    return 2 * ws_stream_bytes(num_chunks_checked(n, chunk));
+    return 2 * ws_stream_bytes(num_chunks_checked(n, chunk)) + ws_count_bytes(n);
 }
 
 int build_args(const lecb_codebook* cb, CodebookArgs* a) {
@@ -122,6 +122,7 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
         L.st[1].res = d_res + 1;
         L.st[1].ws = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + ws_stream_bytes(nc));
     }
+    L.counts = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_ws) + 2 * ws_stream_bytes(nc));
     L.grid = device_cu_count() * encode_wgs_per_cu();
     return launch_encode(L, stream);
 }

@@ -12,14 +12,16 @@
 // threads x 64 consecutive symbols.  The grid is persistent and workgroup w
 // owns the contiguous tickets [w*T/W, (w+1)*T/W).  Two launches:
 //   1. count_kernel: every workgroup sums the payload words of its tickets
-//      (per chunk: ceil(bits / 32)) and stores that total;
+//      (per chunk: ceil(bits / 32)) and stores that total; every thread
+//      also stores the code bits of its 64 symbols;
 //   2. encode_kernel: workgroup w starts at the sum of the totals of
 //      workgroups 0..w-1 (the device-wide exclusive scan, done by one wave
 //      per stream) and then, ticket by ticket:
-//      A. each thread loads its 64 symbols (all loads in flight at once) and
-//         sums their code lengths; a block scan gives every thread's bit
-//         offset inside its chunk and every chunk's size.  With one segment
-//         per ticket the symbols stay in registers for step C;
+//      A. each thread reads the code bits of its 64 symbols stored by the
+//         count launch; a block scan gives every thread's bit offset inside
+//         its chunk and every chunk's size.  With one segment per ticket the
+//         thread also loads its symbols (all loads in flight at once), which
+//         stay in registers for step C;
 //      B. the ticket's first payload word is the running sum of the words of
 //         the workgroup's earlier tickets; the chunk table entries follow;
 //      C. per stream: every thread ORs its code words into an LDS image of
@@ -40,6 +42,7 @@ namespace lecb {
 namespace {
 
 constexpr int ENC_THREADS = 256;
+constexpr int ENC_WGS_PER_CU = 2;   // pack workgroups per compute unit at most (default grid)
 constexpr int SPT = 64;                                  // symbols per thread in a segment
 constexpr uint32_t SEG = ENC_THREADS * SPT;              // 16384
 constexpr int MAX_G = SEG / LECB_MIN_CHUNK;              // chunks per ticket at most (64)
@@ -80,6 +83,7 @@ struct EncArgs {
     uint64_t ntickets;
     uint32_t npack;      // pack workgroups W (ticket ranges); the count launch has F*W
     uint32_t fsplit;     // F: count workgroups per pack workgroup's range
+    uint32_t* counts;    // code bits of every 64 consecutive symbols (pack_counts)
     StreamArgs st[2];
 };
 
@@ -233,7 +237,6 @@ __device__ inline void set_status(WsHeader* ws, int32_t code) {
 
 struct Shared {
     uint32_t stage[STAGE_LDS];     // payload image of the ticket (one stream at a time), padded
-    uint32_t dump[ENC_THREADS];    // target of the stores of pairs that complete no word
     uint32_t enc[2][256];          // (code << 5) | len per stream
     uint8_t len[2][256];
     uint64_t incl[ENC_THREADS];    // inclusive scan of per-thread bits (stream 1 in the high half)
@@ -247,6 +250,16 @@ struct Shared {
     uint64_t run[2];               // first payload word of the next ticket
     uint32_t uncoded;
 };
+
+// The code bits of 64 consecutive symbols as the count launch stores them
+// for the pack launch: stream 0 in bits 0-14, stream 1 in bits 16-30 (at
+// most 64 * 16 each), bit 31 set when a valid symbol has no code word.
+__device__ inline uint32_t pack_counts(uint64_t bits, bool unc) {
+    return (uint32_t)(bits & 0x7FFFu) | ((uint32_t)(bits >> 32) << 16) | (unc ? 0x80000000u : 0u);
+}
+__device__ inline uint64_t unpack_counts(uint32_t c) {
+    return (uint64_t)(c & 0x7FFFu) | ((uint64_t)((c >> 16) & 0x7FFFu) << 32);
+}
 
 // Bits of the thread's 64 symbols, per stream (nv valid); sets *unc when a
 // valid symbol has no code word.
@@ -321,13 +334,14 @@ __device__ inline void gaps_walk(const Shared& S, const EncArgs& a, int s, uint6
 //   * Code words are looked up 16 at a time (one LDS latency per 16) and
 //     joined in pairs: a pair is at most 32 bits, so it enters the 64-bit
 //     accumulator in one step and completes at most one word.
-//   * No branches per pair.  Every pair stores one word: the completed word
-//     when the thread owns all of it, otherwise a dummy slot.  The thread's
-//     first word, when it starts before `pos` (the previous thread's code
-//     words end in it), and its last, partial word are ORed in afterwards
-//     (the stage is zero before packing).
-//   * The first unit start after ts is found on the way (a compare per
-//     pair); a thread that owns a second one walks its code words again.
+//   * No branches per pair.  Every pair ORs one word into the stage (which
+//     is zero before packing): the completed word, or zero into the word
+//     being filled.  A word shared with the neighbouring threads (the first
+//     and the last) gets each thread's bits by the same OR.
+//   * The first unit start nb0 after ts gets the first code-word start at or
+//     after it: the smallest unsigned difference (start - nb0) over the code
+//     starts (a start before nb0 wraps to a huge value); a thread that owns
+//     a second unit start walks its code words again.
 template <bool FULL, int MODE>
 __device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, uint32_t w[16], int nv,
                               uint32_t pos, uint32_t ts, uint32_t wc, uint32_t K, uint32_t log2k,
@@ -337,17 +351,11 @@ __device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, u
     uint32_t nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
     gaps_upto(ts, j, nb, wc, K, log2k, gap);  // unit starts exactly at ts: gap 0
     const uint32_t j0 = j, nb0 = nb;          // next unit start, after ts
-    uint32_t g0 = 0;
+    uint32_t g0 = 0xFFFFFFFFu;
     uint32_t p = ts;  // chunk-relative start of the next code word
     uint32_t widx = pos >> 5;
-    const uint32_t widx0 = widx;
-    uint32_t first_left = (pos & 31u) ? 1u : 0u;  // 1 until the shared first word completes
-    uint32_t first_val = 0;
     uint32_t used = pos & 31u;
     uint64_t acc = 0;
-    // LDS byte addresses: the dump slot, and the stage (word k at k + k/32)
-    const uint32_t dump_at = (uint32_t)(uintptr_t)&S.dump[threadIdx.x];
-    const uint32_t stage_at = (uint32_t)(uintptr_t)&S.stage[0];
     // 16 symbols per round; the symbol words move down by 4 after each round
     // (w is used up), so every index stays a constant without unrolling all
     // 64 symbols
@@ -366,21 +374,12 @@ __device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, u
             const uint32_t l0 = e0 & 31u, l1 = e1 & 31u;
             const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);  // at most 32 bits
             const uint32_t pmid = p + l0, pend = pmid + l1;
-            // the first code-word start at or after nb0
-            g0 = (p < nb0 && nb0 <= pmid) ? pmid - nb0 : g0;
-            g0 = (pmid < nb0 && nb0 <= pend) ? pend - nb0 : g0;
+            g0 = min(g0, min(pmid - nb0, pend - nb0));
             p = pend;
             used += l0 + l1;
             acc |= (uint64_t)c2 << ((64 - used) & 63);  // ends at bit `used` from the top
-            // 0/1 arithmetic instead of branches and masks
             const uint32_t full = used >> 5;             // used <= 63
-            const uint32_t v = (uint32_t)(acc >> 32);
-            const uint32_t to_first = full & first_left;
-            first_val |= v & (0u - to_first);
-            const uint32_t own = full - to_first;
-            const uint32_t at = own ? stage_at + 4u * st_at(widx) : dump_at;
-            *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(at) = v;
-            first_left -= to_first;
+            atomicOr(&S.stage[st_at(widx)], (uint32_t)(acc >> 32) & (0u - full));
             acc <<= 32 * full;
             widx += full;
             used &= 31u;
@@ -388,7 +387,6 @@ __device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, u
 #pragma unroll
         for (int i = 0; i < 12; ++i) ww[i] = ww[i + 4];
     }
-    if (pos & 31u) atomicOr(&S.stage[st_at(widx0)], first_val);
     if (used) atomicOr(&S.stage[st_at(widx)], (uint32_t)(acc >> 32));
     // unit starts in (ts, p]; p is the range end
     if (nb0 <= p) {
@@ -404,8 +402,11 @@ __device__ inline uint64_t first_ticket(uint64_t w, uint64_t T, uint64_t W) { re
 
 // Bits of each chunk of ticket `tk` (per stream, lanes 0..nch-1 of wave s
 // receive chunk `lane`'s bits); w keeps the symbols when the ticket is one
-// segment, and incl/tmp/len are the caller's LDS.
-template <int MODE>
+// segment, and incl/tmp/len are the caller's LDS.  STORED: the bits come
+// from the count launch's per-thread totals (the symbols are loaded only
+// when the ticket is one segment); otherwise they are summed here from the
+// symbols and stored for the pack launch.
+template <int MODE, bool STORED>
 __device__ inline void ticket_bits(const EncArgs& a, uint64_t tk, const uint8_t (&len)[2][256],
                                    uint64_t* incl_lds, uint64_t* tmp, uint32_t w[][16], bool* unc,
                                    uint32_t* nch_out, uint32_t* nseg_out, uint64_t* chunk_acc) {
@@ -420,8 +421,19 @@ __device__ inline void ticket_bits(const EncArgs& a, uint64_t tk, const uint8_t 
     for (uint32_t g = 0; g < nseg; ++g) {
         const uint64_t i0 = tbeg + (uint64_t)g * SEG + (uint64_t)tid * SPT;
         const int nv = i0 >= tend ? 0 : (int)min<uint64_t>(SPT, tend - i0);
-        load64<MODE>(a, i0, nv, w);
-        const uint64_t bits = count_bits<NS>(len, w, nv, unc);
+        uint64_t bits;
+        if constexpr (STORED) {
+            const uint32_t c = nv > 0 ? a.counts[i0 / SPT] : 0u;
+            if (nseg == 1) load64<MODE>(a, i0, nv, w);
+            bits = unpack_counts(c);
+            *unc |= (c >> 31) != 0;
+        } else {
+            load64<MODE>(a, i0, nv, w);
+            bool u = false;
+            bits = count_bits<NS>(len, w, nv, &u);
+            *unc |= u;
+            if (nv > 0) a.counts[i0 / SPT] = pack_counts(bits, u);
+        }
         uint64_t total;
         const uint64_t incl = block_inclusive_scan(bits, tmp, &total);
         if (nseg == 1) incl_lds[tid] = incl;
@@ -469,7 +481,7 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
         bool unc = false;
         uint32_t nch, nseg;
         uint64_t acc;
-        ticket_bits<MODE>(a, tk, len, incl, tmp, w, &unc, &nch, &nseg, &acc);
+        ticket_bits<MODE, false>(a, tk, len, incl, tmp, w, &unc, &nch, &nseg, &acc);
         __syncthreads();
         if (wave < NS) {
             const uint32_t cb = chunk_bits_of(incl, lane, wave, nch, nseg, L, acc);
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
 
 // Launch 2: pack (see the top of the file).
 template <int MODE>
-__global__ __launch_bounds__(ENC_THREADS, pair_mode(MODE) ? 2 : 4) void encode_kernel(EncArgs a) {
+__global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(EncArgs a) {
     constexpr int NS = Streams<MODE>::value;
     __shared__ Shared S;
 
@@ -532,7 +544,7 @@ __global__ __launch_bounds__(ENC_THREADS, pair_mode(MODE) ? 2 : 4) void encode_k
         bool unc = false;
         uint32_t nch, nseg;
         uint64_t chunk_bits_acc;  // nseg > 1: the one chunk's bits (packed per stream)
-        ticket_bits<MODE>(a, T, S.len, S.incl, S.tmp, w, &unc, &nch, &nseg, &chunk_bits_acc);
+        ticket_bits<MODE, true>(a, T, S.len, S.incl, S.tmp, w, &unc, &nch, &nseg, &chunk_bits_acc);
         if (unc) atomicOr(&S.uncoded, 1u);
         __syncthreads();
         // ---- B: chunk sizes, word offsets and the ticket's place in the
@@ -586,9 +598,9 @@ __global__ __launch_bounds__(ENC_THREADS, pair_mode(MODE) ? 2 : 4) void encode_k
                     own = incl - (tid ? S.incl[tid - 1] : 0ull);
                 } else {
                     // the segment's scan again (step A kept only totals)
+                    const uint32_t c = nv > 0 ? a.counts[i0 / SPT] : 0u;
                     load64<MODE>(a, i0, nv, w);
-                    bool unused = false;
-                    own = count_bits<NS>(S.len, w, nv, &unused);
+                    own = unpack_counts(c);
                     incl = block_inclusive_scan(own, S.tmp, &seg_total);
                 }
                 const uint32_t mine = (uint32_t)(own >> (32 * s));  // this thread's bits
@@ -723,6 +735,8 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     a.chunk = L.chunk;
     a.log2k = (uint32_t)ilog2(units_per_chunk(L.chunk));
     a.nc = L.nc;
+    a.counts = L.counts;
+    if (!a.counts) return LECB_ERR_INVALID_ARG;
     a.G = L.chunk >= SEG ? 1u : SEG / L.chunk;
     a.S = L.chunk > SEG ? L.chunk / SEG : 1u;
     a.ntickets = (L.nc + a.G - 1) / a.G;
@@ -747,9 +761,12 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
         st.ws = L.st[s].ws;
         st.wg_words = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);  // room for nc >= grid values
     }
-    // Both launches split the tickets over the same workgroups.  The ranges
-    // are static, so the grid must be resident at once: by default it is the
-    // number of pack workgroups that fit on all compute units together.
+    // Both launches split the tickets over the same workgroups (static
+    // ranges; no workgroup waits for another).  By default the grid is the
+    // number of pack workgroups that fit on all compute units together, at
+    // most ENC_WGS_PER_CU per unit: measured on 32 Mi int8 symbols, byte-mode
+    // pack workgroups at 2 per CU took 70 us against 89 at 3 and 108 at 4 (the
+    // ones that fit), and the two-plane mode is fastest at the 2 that fit.
     uint64_t grid_wgs = L.grid;
     if (L.mode < 0 || L.mode >= ENC_NUM_MODES) return LECB_ERR_INVALID_ARG;
     if (grid_wgs == 0) {
@@ -761,7 +778,7 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
                                                                     ENC_THREADS, 0);
             });
             if (e != hipSuccess || nb < 1) return LECB_ERR_HIP;
-            per_cu[L.mode] = nb;
+            per_cu[L.mode] = nb < ENC_WGS_PER_CU ? nb : ENC_WGS_PER_CU;
         }
         grid_wgs = (uint64_t)device_cu_count() * per_cu[L.mode];
     }

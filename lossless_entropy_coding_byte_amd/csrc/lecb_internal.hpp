@@ -44,9 +44,11 @@ struct CodebookArgs {
 // each encode workgroup (written by the count launch, read by the pack
 // launch of the same call).  Decode: exit counter + status.  A workspace
 // holds two of them (header + one u64 per chunk each, 256-byte aligned): a
-// two-stream encode uses both; everything else uses the first.  The last
-// workgroup of every call resets the header, so only the first use needs a
-// zero-filled workspace.
+// two-stream encode uses both; everything else uses the first.  After them
+// comes one u32 per 64 consecutive symbols: the code bits of those symbols
+// per stream, written by the encode's count launch and read by its pack
+// launch.  The last workgroup of every call resets the headers, so only the
+// first use needs a zero-filled workspace.
 struct WsHeader {
     uint32_t unused0;
     uint32_t exit_count;
@@ -74,6 +76,8 @@ inline uint64_t gap_bytes(uint64_t nc, uint32_t chunk) {
 }
 // Bytes of one stream's part of the workspace: header + one flag per chunk.
 inline uint64_t ws_stream_bytes(uint64_t nc) { return (sizeof(WsHeader) + 8 * nc + 255) & ~uint64_t(255); }
+// Bytes of the per-64-symbol bit counts that follow the two stream parts.
+inline uint64_t ws_count_bytes(uint64_t n) { return (4 * ((n + 63) / 64) + 255) & ~uint64_t(255); }
 
 // ---------------------------------------------------------------- host helpers
 int build_lengths(const uint64_t freq[256], uint32_t max_len, uint32_t min_freq,
@@ -117,6 +121,7 @@ struct EncodeLaunch {
     uint32_t chunk;
     uint64_t nc;
     EncodeStream st[2];      // st[1] only for the two-stream modes
+    uint32_t* counts;        // workspace: one u32 per 64 symbols (count launch -> pack launch)
     int grid;                // upper bound on workgroups (persistent grid)
 };
 int launch_encode(const EncodeLaunch& a, void* stream);
