@@ -85,10 +85,13 @@ struct Tables {
     uint8_t sorted[256];
 };
 
+// The tables come first: their LDS offsets (and the ring's base) fit the
+// 16-bit offset field of the LDS instructions, so a table lookup needs no
+// base-address add.
 template <int NT>
 struct Shared {
-    uint32_t ring[RING][NT];  // row 0 doubles as the counts of the scan
     Tables T;
+    alignas(16) uint32_t ring[RING][NT];  // row 0 doubles as the counts of the scan
     uint64_t red[NT / 64];
 };
 
@@ -204,6 +207,14 @@ __device__ inline uint32_t step(const Tables& T, const Limits& L, Reader<NT>& r,
     const uint32_t e = lookup(T, L, r.peek(), inval);
     r.off += e & 0xFFu;
     return e;
+}
+
+// The symbols (byte 1) of four table entries as one little-endian word:
+// two byte permutes gather the pairs, a third joins them.
+__device__ inline uint32_t syms4(const uint32_t (&e)[4]) {
+    const uint32_t p01 = __builtin_amdgcn_perm(e[1], e[0], 0x0c0c0501u);
+    const uint32_t p23 = __builtin_amdgcn_perm(e[3], e[2], 0x0c0c0501u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
 __device__ inline uint32_t gap_of(const uint8_t* gaps, uint64_t i) {
@@ -425,17 +436,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             uint32_t b = 0;
             for (; b < full; ++b) {
                 uint32_t w[DEC_BLOCK / 4];
+                uint32_t ev[4];
 #pragma unroll
                 for (int q = 0; q < DEC_BLOCK / 2; ++q) {
                     if ((q & 3) == 0) r.tick();
                     r.refill();
 #pragma unroll
                     for (int k = 0; k < 2; ++k) {
-                        const uint32_t e = step(T, L, r, inval);
                         const int i = 2 * q + k;
-                        const uint32_t sym = e >> 8;
-                        if ((i & 3) == 0) w[i >> 2] = sym;
-                        else w[i >> 2] |= sym << (8 * (i & 3));
+                        ev[i & 3] = step(T, L, r, inval);
+                        if ((i & 3) == 3) w[i >> 2] = syms4(ev);
                     }
                 }
 #pragma unroll

@@ -582,27 +582,30 @@ __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(Enc
         }
         __syncthreads();
 
-        // ---- C: pack, stream by stream
+        // ---- C: pack, segment by segment (the symbols of a segment are loaded
+        // once for both streams), stream by stream
+        uint32_t TB[NS];      // S > 1: chunk-relative bit offset of the segment
+        uint32_t carry[NS];   // S > 1: partial last word of the previous segment
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const StreamArgs& st = a.st[s];
-            const uint32_t twords = S.twords[s];
-            uint32_t TB = 0;      // S > 1: chunk-relative bit offset of the segment
-            uint32_t carry = 0;   // S > 1: partial last word of the previous segment
-            for (uint32_t g = 0; g < nseg; ++g) {
-                const uint64_t i0 = tbeg + (uint64_t)g * SEG + (uint64_t)tid * SPT;
-                const int nv = i0 >= tend ? 0 : (int)min<uint64_t>(SPT, tend - i0);
-                uint64_t incl, own, seg_total = 0;
-                if (nseg == 1) {
-                    incl = S.incl[tid];
-                    own = incl - (tid ? S.incl[tid - 1] : 0ull);
-                } else {
-                    // the segment's scan again (step A kept only totals)
-                    const uint32_t c = nv > 0 ? a.counts[i0 / SPT] : 0u;
-                    load64<MODE>(a, i0, nv, w);
-                    own = unpack_counts(c);
-                    incl = block_inclusive_scan(own, S.tmp, &seg_total);
-                }
+        for (int s = 0; s < NS; ++s) TB[s] = carry[s] = 0;
+        for (uint32_t g = 0; g < nseg; ++g) {
+            const uint64_t i0 = tbeg + (uint64_t)g * SEG + (uint64_t)tid * SPT;
+            const int nv = i0 >= tend ? 0 : (int)min<uint64_t>(SPT, tend - i0);
+            uint64_t incl, own, seg_total = 0;
+            if (nseg == 1) {
+                incl = S.incl[tid];
+                own = incl - (tid ? S.incl[tid - 1] : 0ull);
+            } else {
+                // the segment's scan again (step A kept only totals)
+                const uint32_t c = nv > 0 ? a.counts[i0 / SPT] : 0u;
+                load64<MODE>(a, i0, nv, w);
+                own = unpack_counts(c);
+                incl = block_inclusive_scan(own, S.tmp, &seg_total);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const StreamArgs& st = a.st[s];
+                const uint32_t twords = S.twords[s];
                 const uint32_t mine = (uint32_t)(own >> (32 * s));  // this thread's bits
                 uint32_t pos, ts, wc, ch;
                 uint32_t r0 = 0, w0 = 0, touched;
@@ -618,14 +621,14 @@ __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(Enc
                     ch = 0;
                     const uint32_t seg_bits = (uint32_t)(seg_total >> (32 * s));
                     const uint32_t excl = (uint32_t)(incl >> (32 * s)) - mine;
-                    ts = TB + excl;
+                    ts = TB[s] + excl;
                     wc = (S.cbits[s][0] + 31) >> 5;
-                    r0 = TB & 31u;
-                    w0 = TB >> 5;
+                    r0 = TB[s] & 31u;
+                    w0 = TB[s] >> 5;
                     pos = r0 + excl;
                     touched = (r0 + seg_bits + 31) >> 5;
-                    for (uint32_t k = tid; k <= touched; k += ENC_THREADS) S.stage[st_at(k)] = k ? 0u : carry;
-                    TB += seg_bits;
+                    for (uint32_t k = tid; k <= touched; k += ENC_THREADS) S.stage[st_at(k)] = k ? 0u : carry[s];
+                    TB[s] += seg_bits;
                 }
                 __syncthreads();
                 if (nv == SPT && ch < nch)
@@ -650,16 +653,20 @@ __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(Enc
                     }
                 } else {
                     const bool last_seg = g + 1 == nseg;
-                    const uint32_t full = TB / 32 - w0;  // words completed by this segment
+                    const uint32_t full = TB[s] / 32 - w0;  // words completed by this segment
                     const uint32_t nwrite = last_seg ? touched : full;
                     if (write_ok) {
                         uint32_t* dst = st.payload + tbase + w0;
                         for (uint32_t k = tid; k < nwrite; k += ENC_THREADS) dst[k] = S.stage[st_at(k)];
                     }
-                    carry = S.stage[st_at(full)];
+                    carry[s] = S.stage[st_at(full)];
                 }
                 __syncthreads();
             }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const StreamArgs& st = a.st[s];
             // unit gaps of the ticket's chunks, K nibbles each
             if (K >= 2) {
                 const uint32_t nbytes = nch * K / 2;
