@@ -89,7 +89,10 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
                                                                 uint64_t n,
                                                                 unsigned long long* hist_hi,
                                                                 unsigned long long* hist_lo) {
-    constexpr int R = 16;
+    // 32 replicas per plane (64 KiB of LDS): with 16, lanes l and l + 16 of a
+    // half-wave shared a replica, and on a skewed plane they collided on the
+    // same counter
+    constexpr int R = 32;
     __shared__ uint32_t s_hi[256 * R];
     __shared__ uint32_t s_lo[256 * R];
     for (int i = threadIdx.x; i < 256 * R; i += HIST_THREADS) {
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
 }
 
 // Four byte planes of 32-bit elements; s[p] counts byte 3 - p (most
-// significant plane first), 16 replicas per plane as in hist_u16_kernel.
+// significant plane first), 16 replicas per plane (64 KiB of LDS).
 __global__ __launch_bounds__(HIST_THREADS) void hist_u32_kernel(const uint32_t* __restrict__ in,
                                                                 uint64_t n,
                                                                 unsigned long long* hist) {
