@@ -155,6 +155,44 @@ def test_config_int8_fixed():
     _fixed_mode("int8_fixed", x, hist)
 
 
+def test_config_int8_fixed_batched():
+    """64 independent 1 Mi eval batches coded as one call (the bench's batched
+    supplement): the fixed-mode checks at 64 Mi, plus the chunk payloads of a
+    sampled batch equal the oracle's stream of that batch alone."""
+    n1 = workloads.CONFIGS["int8_fixed"]["n"]
+    chunk = workloads.CONFIGS["int8_fixed"]["chunk"]
+    x = np.concatenate([workloads.int8_fixed_batch(b, n1) for b in range(64)])
+    warm = [oracle.histogram(workloads.int8_fixed(r, n1)) for r in (1, 2, 3, 4)]
+    hist = np.sum(warm, axis=0, dtype=np.uint64)
+    r, _, ln = _fixed_mode("int8_fixed", x, hist)
+    # batch 37 alone through the library and through the oracle
+    b = 37
+    one = workloads.int8_fixed_batch(b, n1)
+    assert np.array_equal(one, x[b * n1:(b + 1) * n1])
+    ref, _ = oracle.encode(one, ln, oracle.canonical_codes(ln), chunk)
+    cb = lecb.lecb_build_codebook(hist, 16, 1)
+    assert np.array_equal(cb.lengths(), ln)
+    dcb = lecb.DeviceCodebook.upload(cb, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    out = torch.empty(lecb.lecb_encoded_bound(x.size, chunk), dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(1, DEV)
+    lecb.lecb_encode(xd, x.size, dcb.blob, chunk, out, res, lecb.new_workspace(x.size, chunk, DEV))
+    nc, cpb = oracle.num_chunks(x.size, chunk), n1 // chunk
+    hb = oracle.header_bytes(x.size, chunk)
+    table = out[: 4 * nc].cpu().numpy().view("<u4").astype(np.int64)
+    s0, s1 = int(table[b * cpb - 1]), int(table[(b + 1) * cpb - 1])
+    words = out[hb + 4 * s0: hb + 4 * s1].cpu().numpy()
+    assert np.array_equal(words, ref[oracle.header_bytes(n1, chunk):])
+    rt = ref[: 4 * cpb].view("<u4").astype(np.int64)
+    assert np.array_equal(table[b * cpb:(b + 1) * cpb] - s0, rt)
+    # unit gaps: K nibbles per chunk, K even, so a batch's gaps are whole bytes
+    K = oracle.units_per_chunk(chunk)
+    tb = oracle.table_bytes(x.size, chunk)
+    g = out[tb + b * cpb * K // 2: tb + (b + 1) * cpb * K // 2].cpu().numpy()
+    tb1 = oracle.table_bytes(n1, chunk)
+    assert np.array_equal(g, ref[tb1: tb1 + cpb * K // 2])
+
+
 def test_config_bf16_weights():
     _pertensor("bf16_weights", workloads.bf16_weights())
 

@@ -77,6 +77,11 @@ def int8_fixed(role: int = 0, n: int = 1 << 20) -> np.ndarray:
     return q8(rng(1, role, 0).normal(0.0, 20.0, n))
 
 
+def int8_fixed_batch(block: int, n: int = 1 << 20) -> np.ndarray:
+    """Independent eval batch number ``block`` (role 0); block 0 is ``int8_fixed(0, n)``."""
+    return q8(rng(1, 0, block).normal(0.0, 20.0, n))
+
+
 _C3_SHAPE = (8, 2048, 2048)
 
 
