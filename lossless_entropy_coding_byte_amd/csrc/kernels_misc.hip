@@ -115,18 +115,18 @@ __global__ __launch_bounds__(HIST_THREADS) void hist_u16_kernel(const uint16_t* 
             atomicAdd(&s_hi[(w[k] >> 24) * R + r], 1u);
         }
     };
-    // four 16-byte loads in flight per thread, then their 64 increments
+    // eight 16-byte loads in flight per thread, then their 128 increments
     uint64_t i = (uint64_t)blockIdx.x * HIST_THREADS + threadIdx.x;
-    for (; i + 3 * stride < n8; i += 4 * stride) {
-        v4u v[4];
+    for (; i + 7 * stride < n8; i += 8 * stride) {
+        v4u v[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = ld_stream(&in4[i + q * stride]);
+        for (int q = 0; q < 8; ++q) v[q] = ld_stream(&in4[i + q * stride]);
         if (in2) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] ^= ld_stream(&in24[i + q * stride]);
+            for (int q = 0; q < 8; ++q) v[q] ^= ld_stream(&in24[i + q * stride]);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) add8(v[q]);
+        for (int q = 0; q < 8; ++q) add8(v[q]);
     }
     for (; i < n8; i += stride) add8(in2 ? ld_stream(&in4[i]) ^ ld_stream(&in24[i]) : ld_stream(&in4[i]));
     if (blockIdx.x == gridDim.x - 1) {
