@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on the GPU machine only; without a device they are skipped, never faked.
+    # GPU tests need a visible device; without one they are skipped, never faked.
     try:
         import torch
 
