@@ -43,6 +43,8 @@ namespace {
 
 constexpr int ENC_THREADS = 256;
 constexpr int ENC_WGS_PER_CU = 2;   // pack workgroups per compute unit at most (default grid)
+constexpr int ENC_WGS_PER_CU_LONG = 3;   // the same for long inputs (see launch_encode)
+constexpr uint64_t ENC_LONG_SEGS = 32;   // segments per workgroup that make an input long
 constexpr int SPT = 64;                                  // symbols per thread in a segment
 constexpr uint32_t SEG = ENC_THREADS * SPT;              // 16384
 constexpr int MAX_G = SEG / LECB_MIN_CHUNK;              // chunks per ticket at most (64)
@@ -774,6 +776,10 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     // most ENC_WGS_PER_CU per unit: measured on 32 Mi int8 symbols, byte-mode
     // pack workgroups at 2 per CU took 70 us against 89 at 3 and 108 at 4 (the
     // ones that fit), and the two-plane mode is fastest at the 2 that fit.
+    // Long inputs (at least ENC_LONG_SEGS segments per workgroup at that
+    // grid) take 3 per CU, even where only 2 fit: the finer ticket ranges
+    // even out the workgroups' ends (512 Mi 16-bit words in 65536-symbol
+    // chunks: 0.99 ms against 1.09; 4 GiB of bytes: no change, ~4.9 ms).
     uint64_t grid_wgs = L.grid;
     if (L.mode < 0 || L.mode >= ENC_NUM_MODES) return LECB_ERR_INVALID_ARG;
     if (grid_wgs == 0) {
@@ -787,7 +793,9 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
             if (e != hipSuccess || nb < 1) return LECB_ERR_HIP;
             per_cu[L.mode] = nb < ENC_WGS_PER_CU ? nb : ENC_WGS_PER_CU;
         }
-        grid_wgs = (uint64_t)device_cu_count() * per_cu[L.mode];
+        const uint64_t cus = (uint64_t)device_cu_count();
+        grid_wgs = cus * per_cu[L.mode];
+        if (a.ntickets * a.S >= ENC_LONG_SEGS * grid_wgs) grid_wgs = cus * ENC_WGS_PER_CU_LONG;
     }
     const uint64_t nwg = grid_wgs < a.ntickets ? grid_wgs : a.ntickets;
     const dim3 grid((uint32_t)nwg), block(ENC_THREADS);
