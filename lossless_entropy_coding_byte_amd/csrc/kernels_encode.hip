@@ -494,7 +494,10 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
     if (wave < NS && lane == 0) a.st[wave].wg_words[blockIdx.x] = words;
 }
 
-// Launch 2: pack (see the top of the file).
+// Launch 2: pack (see the top of the file).  A 256-lane workgroup is one
+// wave per SIMD, so ENC_WGS_PER_CU workgroups per CU are as many waves per
+// SIMD: the second launch bound (minimum waves per SIMD) allows registers for
+// that many.
 template <int MODE>
 __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(EncArgs a) {
     constexpr int NS = Streams<MODE>::value;
