@@ -41,6 +41,22 @@ def test_sizes_match_oracle():
     assert lecb.lecb_encoded_bound(100, 4096, 17) == 0
 
 
+def test_workspace_bytes_contract():
+    """The workspace holds, per stream (two), a 64-byte header and one 64-bit
+    slot per chunk, then one 32-bit count per 64 symbols; every part is
+    256-byte aligned, and a bad chunk size gives 0."""
+    for n in (1, 63, 64, 65, 4096, 123457, 1 << 20, (1 << 32) + 5):
+        for chunk in (256, 4096, 16384, 65536):
+            nc = -(-n // chunk)
+            part = -(-(64 + 8 * nc) // 256) * 256
+            counts = -(-(4 * -(-n // 64)) // 256) * 256
+            ws = lecb.lecb_workspace_bytes(n, chunk)
+            assert ws == 2 * part + counts, (n, chunk)
+            assert ws % 256 == 0
+    assert lecb.lecb_workspace_bytes(1000, 300) == 0
+    assert lecb.lecb_workspace_bytes(1000, 128) == 0
+
+
 def _random_hist(rng, kind):
     h = np.zeros(256, np.uint64)
     m = int(rng.integers(1, 257))
