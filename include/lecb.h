@@ -374,8 +374,12 @@ int lecb_decode_bf16_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
                                   uint16_t* d_out, uint8_t* d_scratch, lecb_result* d_res2,
                                   void* d_ws, uint64_t ws_bytes, void* stream);
 
-/* Decode both planes and restore the 16-bit words.  d_scratch: 2*align16(n)
- * bytes of device memory for the decoded planes.  d_ws: lecb_workspace_bytes(n, chunk). */
+/* Decode both planes and restore the 16-bit words, out[i] = hi[i] << 8 | lo[i]:
+ * the reverse path of "Lossless Compression for LLM Tensor Incremental
+ * Snapshots", Technical framework (Huffman-decode each byte group, then
+ * restore the byte groups).  d_scratch: 2*align16(n) bytes of device memory
+ * (caller-owned) that receive the decoded planes before the restore.  d_ws:
+ * lecb_workspace_bytes(n, chunk).  Errors as lecb_decode, per plane. */
 int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
                      uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
                      uint32_t chunk, uint64_t n, uint16_t* d_out, uint8_t* d_scratch,

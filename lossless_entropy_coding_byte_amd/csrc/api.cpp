@@ -33,18 +33,6 @@ int read_back_hist(const uint64_t* d_hist, int count, void* stream, const uint64
     return LECB_OK;
 }
 
-// Encode workgroups launched per compute unit (persistent grid).  0: as many
-// as fit on a compute unit at once (asked of the runtime per kernel);
-// LECB_ENCODE_WGS_PER_CU overrides it for launch-shape sweeps.
-int encode_wgs_per_cu() {
-    static int v = [] {
-        const char* e = std::getenv("LECB_ENCODE_WGS_PER_CU");
-        const int x = e ? std::atoi(e) : 0;
-        return x >= 1 && x <= 64 ? x : 0;
-    }();
-    return v;
-}
-
 uint64_t num_chunks_checked(uint64_t n, uint32_t chunk) {
     return valid_chunk(chunk) ? (n + chunk - 1) / chunk : 0;
 }
@@ -123,7 +111,7 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
         L.st[1].ws = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + ws_stream_bytes(nc));
     }
     L.counts = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_ws) + 2 * ws_stream_bytes(nc));
-    L.grid = device_cu_count() * encode_wgs_per_cu();
+    L.grid = 0;  // the encoder sizes its persistent grid from the device
     return launch_encode(L, stream);
 }
 

@@ -39,8 +39,6 @@
 // checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-
 #include "lecb_internal.hpp"
 
 namespace lecb {
@@ -252,7 +250,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         for (int i = tid; i < LUT_SIZE / 16; i += DEC_THREADS) mdst[i] = msrc[i];
     }
     if (tid < 17) T.off[tid] = d.cb->base[tid] - d.cb->first[tid];
-    T.sorted[tid] = d.cb->sorted[tid];
+    if (tid < 256) T.sorted[tid] = d.cb->sorted[tid];
     Limits L;
     L.l13 = d.cb->limit[13];
     L.l14 = d.cb->limit[14];
@@ -546,11 +544,7 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
     // Take the biggest size that still gives every CU a workgroup.
     const uint64_t all = units * (uint64_t)L.nstreams;
     const uint64_t cus = (uint64_t)device_cu_count();
-    int nt = all >= cus * 1024 ? 1024 : all >= cus * 512 ? 512 : 256;
-    if (const char* e = std::getenv("LECB_DECODE_THREADS")) {
-        const int x = std::atoi(e);
-        if (x == 256 || x == 512 || x == 1024) nt = x;
-    }
+    const int nt = all >= cus * 1024 ? 1024 : all >= cus * 512 ? 512 : 256;
     a.wg_per_stream = (uint32_t)((units + nt - 1) / nt);
     const dim3 grid((uint32_t)((uint64_t)a.wg_per_stream * L.nstreams));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);

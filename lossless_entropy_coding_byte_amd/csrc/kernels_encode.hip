@@ -1,4 +1,5 @@
-// Huffman encode of byte symbols into stream format v1, in ONE launch.
+// Huffman encode of byte symbols into stream format v1, in two launches
+// (a count launch, then a pack launch).
 //
 // "Single-Stage Huffman Encoder for ML Compression", Methodology step 4: each
 // tensor is coded directly with the codebook already resident on the device.
@@ -33,6 +34,7 @@
 // No workgroup ever waits for another one.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "lecb_internal.hpp"
@@ -786,18 +788,24 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     uint64_t grid_wgs = L.grid;
     if (L.mode < 0 || L.mode >= ENC_NUM_MODES) return LECB_ERR_INVALID_ARG;
     if (grid_wgs == 0) {
-        static int per_cu[ENC_NUM_MODES] = {};
-        if (per_cu[L.mode] == 0) {
+        // resident pack workgroups per CU, asked of the runtime once per
+        // (device, mode); concurrent first calls store the same value
+        static std::atomic<int> per_cu[MAX_DEVICES][ENC_NUM_MODES];
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return LECB_ERR_HIP;
+        int pc = per_cu[dev][L.mode].load(std::memory_order_relaxed);
+        if (pc == 0) {
             int nb = 0;
             const hipError_t e = with_mode(L.mode, [&](auto m) {
                 return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<decltype(m)::value>,
                                                                     ENC_THREADS, 0);
             });
             if (e != hipSuccess || nb < 1) return LECB_ERR_HIP;
-            per_cu[L.mode] = nb < ENC_WGS_PER_CU ? nb : ENC_WGS_PER_CU;
+            pc = nb < ENC_WGS_PER_CU ? nb : ENC_WGS_PER_CU;
+            per_cu[dev][L.mode].store(pc, std::memory_order_relaxed);
         }
         const uint64_t cus = (uint64_t)device_cu_count();
-        grid_wgs = cus * per_cu[L.mode];
+        grid_wgs = cus * pc;
         if (a.ntickets * a.S >= ENC_LONG_SEGS * grid_wgs) grid_wgs = cus * ENC_WGS_PER_CU_LONG;
     }
     const uint64_t nwg = grid_wgs < a.ntickets ? grid_wgs : a.ntickets;

@@ -6,6 +6,8 @@
 // same page, Technical framework step 1 and the byte-group restore.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "lecb_internal.hpp"
 
 namespace lecb {
@@ -324,17 +326,18 @@ int grid_for(uint64_t items, int threads, int max_blocks) {
 }  // namespace
 
 int device_cu_count() {
-    static int cached[64] = {0};
+    // per device, asked once; concurrent first calls store the same value
+    static std::atomic<int> cached[MAX_DEVICES];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 256;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (!cus) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return cus;
 }
 
 int launch_histogram_u8(const uint8_t* in, uint64_t n, uint64_t* hist, int accumulate,

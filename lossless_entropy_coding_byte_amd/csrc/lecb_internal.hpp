@@ -162,6 +162,8 @@ int launch_build_codebooks(const uint64_t* const* hist, DeviceCodebook* const* c
 int launch_fill_zero(void* ptr, uint64_t bytes, void* stream);
 int launch_result(lecb_result* r, uint64_t bytes, uint64_t bits, int32_t status, void* stream);
 
+// Devices the per-device caches of the host code cover (ordinals 0..MAX_DEVICES-1).
+constexpr int MAX_DEVICES = 64;
 int device_cu_count();
 
 }  // namespace lecb
