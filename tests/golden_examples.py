@@ -50,3 +50,29 @@ def load():
             ex["payload_bits"] = int(b["payload_bits"])
         examples.append(ex)
     return examples
+
+
+CONTAINER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "container_header.txt")
+
+
+def load_container():
+    """The hand-derived container header: its fields and its 560 bytes."""
+    fields, head = {}, np.zeros(560, np.uint8)
+    with open(CONTAINER) as f:
+        for raw in f:
+            line = raw.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            key = key.strip()
+            if key.isdigit():
+                b = [int(t, 16) for t in val.split()]
+                head[int(key):int(key) + len(b)] = b
+            elif key in ("len_hi", "len_lo"):
+                ln = np.zeros(256, np.uint8)
+                for s, v in _pairs(val, 10).items():
+                    ln[s] = v
+                fields[key] = ln
+            else:
+                fields[key] = int(val)
+    return fields, head

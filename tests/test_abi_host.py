@@ -124,6 +124,18 @@ def test_builder_errors():
         lecb.lecb_codebook_from_lengths(bad)
 
 
+def test_container_header_golden_bytes():
+    from golden_examples import load_container
+
+    f, head = load_container()
+    got = lecb.lecb_container_write_header(f["n"], f["chunk"], f["max_len"], f["len_hi"], f["len_lo"],
+                                           f["bytes_hi"], f["bytes_lo"])
+    assert np.array_equal(got, head)
+    back = lecb.lecb_container_read_header(head)
+    assert (back["n"], back["bytes_hi"], back["bytes_lo"]) == (f["n"], f["bytes_hi"], f["bytes_lo"])
+    assert np.array_equal(back["len_hi"], f["len_hi"]) and np.array_equal(back["len_lo"], f["len_lo"])
+
+
 def test_container_header_matches_oracle():
     x = np.random.default_rng(3).integers(0, 65536, 5000, dtype=np.uint16)
     enc = oracle.encode_bf16(x, 4096)

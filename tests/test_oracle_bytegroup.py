@@ -5,6 +5,7 @@ import torch
 
 import oracle
 import workloads
+from golden_examples import load_container
 
 
 def test_split_matches_torch_bf16_bit_view():
@@ -119,3 +120,19 @@ def test_fp32_round_trip_and_plane_streams():
         assert enc["bits"][p] == oracle.payload_bits_identity(oracle.histogram(planes[p]), enc["len"][p])
     # the sign/exponent plane compresses, the low mantissa bytes hardly at all
     assert enc["bits"][0] < 4 * x.size and enc["bits"][3] > 7.9 * x.size
+
+
+def test_container_header_golden_bytes():
+    """The container header against hand-derived bytes (tests/golden/container_header.txt):
+    every field at its offset, hi and lo tables and sizes distinguishable."""
+    f, head = load_container()
+    enc = {"n": f["n"], "chunk": f["chunk"], "max_len": f["max_len"], "len_hi": f["len_hi"],
+           "len_lo": f["len_lo"], "stream_hi": np.zeros(f["bytes_hi"], np.uint8),
+           "stream_lo": np.zeros(f["bytes_lo"], np.uint8)}
+    buf = oracle.container_bytes(enc)
+    assert np.array_equal(buf[:560], head)
+    assert buf.size == f["total_bytes"]
+    back = oracle.parse_container(buf)
+    assert (back["n"], back["chunk"], back["max_len"]) == (f["n"], f["chunk"], f["max_len"])
+    assert np.array_equal(back["len_hi"], f["len_hi"]) and np.array_equal(back["len_lo"], f["len_lo"])
+    assert back["stream_hi"].size == f["bytes_hi"] and back["stream_lo"].size == f["bytes_lo"]
