@@ -6,23 +6,29 @@
 One step = one pass of the whole coding path over one synthetic tensor, with
 inputs resident in HBM:
 
-* per-tensor bf16 (default, ``bf16_weights``: 64 Mi bf16 elements, chunk
-  16384; also ``bf16_delta``): plane histograms -> read back -> two host
-  codebooks -> upload -> encode both byte planes -> read back stream sizes ->
-  decode both planes -> restore the 16-bit words;
-* per-tensor fp32 (``fp32_weights``): the same with four byte planes;
-* fixed codebook (``int8_fixed``, ``int8_acts``, ``int8_drift``,
-  ``int4_packed``): encode + decode with a codebook built once from warm-up
-  batches (untimed, as in single-stage coding).
+* fixed codebook (default ``int8_drift``: 64 batches of 64 Mi int8 symbols,
+  sigma 10 -> 40, coded as one 4 GiB call with batch 0's codebook, chunk
+  4096; also ``int8_fixed``, ``int8_acts``, ``int4_packed``): encode +
+  decode with a codebook built once beforehand (untimed, as in single-stage
+  coding);
+* per-tensor bf16 (``bf16_weights``: 64 Mi bf16 elements, chunk 16384;
+  ``bf16_delta``): plane histograms -> codebooks built on the device ->
+  encode both byte planes -> decode both planes (stream sizes read on the
+  device) -> restore the 16-bit words;
+* per-tensor fp32 (``fp32_weights``): the same with four byte planes.
 
-Prints ONE JSON line.  ``value`` = uncompressed bytes / wall-clock step time
-(GB/s, 1e9).  Encode and decode rates, the ratio, per-kernel timings from HIP
-events on the launch stream, the roofline of the dominant kernel and the CPU
-oracle baseline (timed on host worker processes started before the GPU is
-touched) ride along.  The timed outputs are checked on the device before
-anything is reported (exact round trip, statuses, payload bits = sum of count x
-code length, a well-formed chunk table); the element-by-element parity against
-the oracle at the same sizes and launch configuration is in the GPU tests.
+Prints ONE JSON line.  Every timed step follows a 1 GiB device write (outside
+its HIP events), so no step finds its input or streams in the 256 MB
+Infinity Cache; ``value`` = uncompressed bytes / median step time (GB/s,
+1e9), and the per-kernel times behind encode / decode rates and the roofline
+of the dominant kernel are medians of the same steps.  The same steps run back
+to back are reported beside them as ``warm_cache``.  The CPU oracle baseline
+runs on worker processes over all host cores, started before the GPU is
+touched (median of three runs when a run takes under a minute).  The timed
+outputs are checked on the device before anything is reported (exact round
+trip, statuses, payload bits = sum of count x code length, a well-formed chunk
+table); the element-by-element parity against the oracle at the same sizes
+and launch configuration is in the GPU tests.
 """
 
 from __future__ import annotations
@@ -75,35 +81,60 @@ def _cpu_worker(args):
     return t1 - t0, t2 - t1
 
 
-def cpu_baseline(cfg: dict, x: np.ndarray, hist, sample_elems: int) -> dict:
-    """Oracle encode + decode of a bounded sample, split over chunk ranges across host cores."""
+def _cpu_sample(cfg: dict, x: np.ndarray, sample_elems: int) -> tuple:
+    """The bounded sample the oracle codes: the first sample_elems elements, or
+    for the drift stream the same number taken as equal runs of whole chunks
+    from the start of every batch (so every sigma is represented)."""
+    chunk = cfg["chunk"]
+    if cfg.get("batches") and sample_elems < x.size:
+        B = x.size // cfg["batches"]
+        per = max(chunk, sample_elems // cfg["batches"] // chunk * chunk)
+        pieces = [x[k * B:k * B + per] for k in range(cfg["batches"])]
+        return pieces, (f"{per} symbols from the start of each of the {cfg['batches']} batches "
+                        f"({per * cfg['batches']} symbols in all)")
+    return [x[:sample_elems]], f"first {min(sample_elems, x.size)} elements of the same tensor"
+
+
+def cpu_baseline(cfg: dict, x: np.ndarray, hist, sample_elems: int, pool, cores: int) -> dict:
+    """Oracle encode + decode of a bounded sample, split over chunk ranges across all host cores."""
     import oracle
 
     chunk = cfg["chunk"]
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    sample = x[:sample_elems]
+    pieces, what = _cpu_sample(cfg, x, sample_elems)
     t0 = time.perf_counter()
     if cfg["kind"] == "u8":
         # fixed codebook, built once from the warm-up statistics (not timed)
         lengths = [oracle.package_merge_lengths(oracle.codebook_frequencies([hist], 1), 16)]
-        t0 = time.perf_counter()
+        t_build = 0.0
     else:
         # per-tensor mode: the histograms and codebooks are part of the encode
+        sample = pieces[0]
         planes = oracle.split_bf16(sample) if cfg["kind"] == "bf16" else oracle.split_fp32(sample)
         lengths = [oracle.package_merge_lengths(oracle.histogram(p), 16) for p in planes]
-    t_build = time.perf_counter() - t0
-    per = -(-sample.size // cores)
-    per = -(-per // chunk) * chunk
+        t_build = time.perf_counter() - t0
     kind = "bytes" if cfg["kind"] == "u8" else cfg["kind"]
-    jobs = [(kind, sample[i:i + per], lengths, chunk) for i in range(0, sample.size, per)]
-    ctx = mp.get_context("spawn")
-    t0 = time.perf_counter()
-    with ctx.Pool(len(jobs)) as pool:
+    total = sum(p.size for p in pieces)
+    per = -(-total // cores)
+    per = -(-per // chunk) * chunk
+    jobs = []
+    for piece in pieces:
+        for i in range(0, piece.size, per):
+            jobs.append((kind, piece[i:i + per], lengths, chunk))
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
         times = pool.map(_cpu_worker, jobs)
-    wall = time.perf_counter() - t0
-    enc = max(t[0] for t in times) + t_build
-    dec = max(t[1] for t in times)
-    nbytes = sample.size * sample.itemsize
+        wall = time.perf_counter() - t0
+        # wall-clock of the whole map (every worker encodes, then decodes its
+        # jobs); split into encode and decode by the workers' summed phase times
+        se, sd = sum(t[0] for t in times), sum(t[1] for t in times)
+        runs.append((wall + t_build, (wall * se / (se + sd)) + t_build, wall * sd / (se + sd)))
+        if wall > 60:
+            break
+    nbytes = total * x.itemsize
+    used = min(cores, len(jobs))
+    i = int(np.argsort([r[0] for r in runs])[len(runs) // 2])
+    tot, enc, dec = runs[i]
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -113,22 +144,28 @@ def cpu_baseline(cfg: dict, x: np.ndarray, hist, sample_elems: int) -> dict:
     except OSError:
         pass
     return {
-        "value": round(nbytes / (enc + dec) / 1e9, 4),
+        "value": round(nbytes / tot / 1e9, 4),
         "unit": "GB/s",
-        "cores": len(jobs),
+        "cores": used,
         "kind": "oracle",
-        "sample": f"first {sample.size} elements ({nbytes} bytes) of the same tensor, "
-                  f"{len(jobs)} worker processes over chunk ranges",
+        "sample": f"{what} ({nbytes} bytes), {len(jobs)} jobs over chunk ranges on {used} worker processes",
         "encode_GBps": round(nbytes / enc / 1e9, 4),
         "decode_GBps": round(nbytes / dec / 1e9, 4),
-        "wall_s": round(wall, 2),
+        "runs": len(runs),
+        "statistic": "median of the runs" if len(runs) > 1 else "one run (over a minute)",
+        "wall_s": round(runs[i][0], 2),
         "cpu_model": cpu_model,
     }
 
 
 # ============================================================================ inputs
 
-def make_input(name: str, scale: float):
+def _drift_batch(args):
+    k, batch = args
+    return k, workloads.int8_drift_batch(k, batch)
+
+
+def make_input(name: str, scale: float, pool):
     cfg = dict(workloads.CONFIGS[name])
     cfg["name"] = name
     n = int(cfg["n"] * scale)
@@ -153,8 +190,11 @@ def make_input(name: str, scale: float):
         batch = min(workloads.BLOCK, n)
         cfg["batches"] = n // batch
         x = np.empty(cfg["batches"] * batch, dtype=np.uint8)
-        for k in range(cfg["batches"]):
-            x[k * batch:(k + 1) * batch] = workloads.int8_drift_batch(k, batch)
+        # the 64 batches are drawn in the worker processes (same recipe, same seeds)
+        t0 = time.perf_counter()
+        for k, xb in pool.imap_unordered(_drift_batch, [(k, batch) for k in range(cfg["batches"])]):
+            x[k * batch:(k + 1) * batch] = xb
+        cfg["generate_s"] = round(time.perf_counter() - t0, 2)
         cfg["n"] = n = x.size
         # one fixed codebook from batch 0, every byte coded
         hist = np.bincount(x[:batch], minlength=256).astype(np.uint64)
@@ -358,20 +398,17 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         variants["host"] = step_host
     chosen = "device"
     step = lambda: variants[chosen](T)  # noqa: E731
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    T.pairs.clear()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # cold-cache leg: the 256 MB Infinity Cache holds the smaller workloads, so
-    # each step here follows a 1 GiB device write, outside the step's events
-    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    # Timed steps, cold cache: the 256 MB Infinity Cache would hold the smaller
+    # workloads' inputs and streams between steps, so every step follows a
+    # 1 GiB device write, outside the step's events.  HIP events on the launch
+    # stream bracket each step and each kernel; the median step is the figure.
     Tc = Timer(torch)
     cold_pairs = []
+    t0 = time.perf_counter()
     for i in range(steps):
         flush.fill_(i)
         e0 = torch.cuda.Event(enable_timing=True)
@@ -381,15 +418,23 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         e1.record()
         cold_pairs.append((e0, e1))
     torch.cuda.synchronize()
+    cold_wall = time.perf_counter() - t0
     cold_ms = [a.elapsed_time(b) for a, b in cold_pairs]
-    cold = {
-        "flush_bytes_before_each_step": 1 << 30,
-        "ms_per_step_median": round(float(np.median(cold_ms)), 4),
-        "ms_per_step_min": round(float(np.min(cold_ms)), 4),
-        "kernels_ms_median": {lb: round(float(np.median([a.elapsed_time(b) for a, b in ps])), 4)
-                              for lb, ps in Tc.pairs.items()},
-    }
+    cold_kernels = {lb: float(np.median([a.elapsed_time(b) for a, b in ps])) for lb, ps in Tc.pairs.items()}
     del flush
+    # Warm cache, labelled as such: the same K steps back to back.
+    T.pairs.clear()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    warm_wall = time.perf_counter() - t0
+    warm = {
+        "what": "the same steps back to back, inputs and streams left in the caches (not the headline)",
+        "ms_per_step": round(warm_wall / steps * 1e3, 4),
+        "kernels_ms_mean": {lb: round(T.mean_ms(lb), 4) for lb in T.pairs},
+    }
+    warm["GBps"] = None  # filled in by main() (needs the byte count)
     other_ms = None
     if len(variants) > 1:
         other = [v for v in variants if v != chosen][0]
@@ -495,15 +540,22 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         parity["fused_delta_ok"] = fused["round_trip"] and same and not any(fused["status"])
         del w0d, w1d, w1_out
 
-    # ---------------- timings
-    ms_step = wall / steps * 1e3
-    kernels = {label: T.mean_ms(label) for label in T.pairs if label not in ("encode", "decode")}
+    # ---------------- timings (cold-cache medians)
+    ms_step = float(np.median(cold_ms))
+    kernels = {label: v for label, v in cold_kernels.items() if label not in ("encode", "decode")}
     if cfg["kind"] in ("bf16", "fp32"):
         enc_ms = sum(kernels[lb] for lb in kernels if lb in ("histogram", "codebook_build", "histogram+codebooks",
                                                               "encode_pair"))
         dec_ms = kernels["decode_pair"] + kernels["merge"]
     else:
-        enc_ms, dec_ms = T.mean_ms("encode"), T.mean_ms("decode")
+        enc_ms, dec_ms = cold_kernels["encode"], cold_kernels["decode"]
+    cold = {
+        "flush_bytes_before_each_step": 1 << 30,
+        "ms_per_step_median": round(ms_step, 4),
+        "ms_per_step_min": round(float(np.min(cold_ms)), 4),
+        "wall_s_of_the_timed_steps_with_flushes": round(cold_wall, 4),
+        "kernels_ms_median": {lb: round(v, 4) for lb, v in cold_kernels.items()},
+    }
     # ---------------- size accounting per stream (histogram kernel + host stats)
     accounting = []
     for name, h, ln in zip(names, hists, lengths_out):
@@ -637,6 +689,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         subbyte=subbyte,
         codebook_path=chosen if cfg["kind"] in ("bf16", "fp32") else None,
         cold=cold,
+        warm=warm,
         other_ms=other_ms,
         accounting=accounting,
         nbytes=nbytes, ms_step=ms_step, enc_ms=enc_ms, dec_ms=dec_ms, kernels=kernels,
@@ -715,10 +768,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="bf16_weights", choices=list(workloads.CONFIGS))
+    ap.add_argument("--config", default="int8_drift", choices=list(workloads.CONFIGS))
     ap.add_argument("--scale", type=float, default=1.0, help="fraction of the config's size (tests)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 25, help="elements the oracle baseline codes")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 26,
+                    help="elements the oracle baseline codes (spread over the batches of the drift stream)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -737,12 +791,14 @@ def main():
               "(the codec shards by whole chunks; see the multi-GPU notes of the design)", file=sys.stderr)
         sys.exit(2)
 
-    cfg, x, hist = make_input(args.config, args.scale)
-
-    # CPU baseline first: the worker processes start before this process touches the GPU.
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, x, hist, min(args.cpu_sample, x.size))
+    # Worker processes first: they start before this process touches the GPU,
+    # draw the long inputs in parallel and run the CPU oracle baseline.
+    cores = len(os.sched_getaffinity(0))
+    with mp.get_context("spawn").Pool(cores) as pool:
+        cfg, x, hist = make_input(args.config, args.scale, pool)
+        cpu = None
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(cfg, x, hist, min(args.cpu_sample, x.size), pool, cores)
 
     lengths = []
     info = run_gpu(cfg, x, hist, args.steps, args.warmup, lengths)
@@ -769,7 +825,8 @@ def main():
         "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": args.config, "elements": cfg["n"], "element_bytes": x.itemsize,
-                   "chunk": cfg["chunk"], "mode": cfg["mode"], "max_len": 16},
+                   "chunk": cfg["chunk"], "mode": cfg["mode"], "max_len": 16,
+                   **({"batches": cfg["batches"], "generate_s": cfg.get("generate_s")} if cfg.get("batches") else {})},
         "encode_GBps": round(enc_gbps, 2),
         "decode_GBps": round(dec_gbps, 2),
         "encode_ms": round(info["enc_ms"], 4),
@@ -782,7 +839,11 @@ def main():
         "fused_delta": info["fused"],
         "int4": info["subbyte"],
         "pertensor_codebooks": info["codebook_path"],
-        "cold_cache": dict(info["cold"], GBps_median=round(nbytes / (info["cold"]["ms_per_step_median"] * 1e-3) / 1e9, 2)),
+        "timing": "cold cache: a 1 GiB device write before every timed step (outside its events); "
+                  "value, ms_per_step, encode/decode and roofline are medians of those steps",
+        "cold_cache": dict(info["cold"], GBps_median=round(value, 2)),
+        "warm_cache": dict(info["warm"], GBps=round(nbytes / (info["warm"]["ms_per_step"] * 1e-3) / 1e9, 2)),
+        "strict_frac_of_hbm": {"encode": round(enc_gbps / HBM_PEAK_GBPS, 4), "decode": round(dec_gbps / HBM_PEAK_GBPS, 4)},
         "pertensor_other_codebooks_ms_per_step": info["other_ms"],
         "kernels": per_kernel,
         "roofline": roof,

@@ -85,6 +85,16 @@ def header_bytes(n: int, chunk: int) -> int:
     return table_bytes(n, chunk) + gap_bytes(n, chunk)
 
 
+def unit_meta_span(n: int, chunk: int, c0: int, c1: int):
+    """Byte range [a, b) of the stream that holds the per-unit metadata of chunks
+    [c0, c1) (unit j of chunk c is entry c*K + j); the range must cover whole bytes."""
+    K = units_per_chunk(chunk)
+    if (c0 * K) % 2 or (c1 * K) % 2:
+        raise ValueError("these chunks do not cover whole bytes of gap nibbles")
+    tb = table_bytes(n, chunk)
+    return tb + c0 * K // 2, tb + c1 * K // 2
+
+
 def encoded_bound(n: int, chunk: int, max_len: int = 16) -> int:
     """Largest possible stream size (every symbol at max_len bits plus one padding word per
     chunk), rounded up to a multiple of 16 bytes."""
