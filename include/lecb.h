@@ -74,6 +74,7 @@ extern "C" {
 #define LECB_MIN_CHUNK 256u
 #define LECB_MAX_CHUNK 65536u
 #define LECB_CONTAINER_HEADER_BYTES 560u
+#define LECB_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum {
     LECB_OK = 0,
@@ -83,6 +84,7 @@ typedef enum {
     LECB_ERR_NO_SYMBOLS = -4,     /* histogram empty, or more coded symbols than 2^max_len */
     LECB_ERR_HIP = -5,            /* a HIP runtime call failed */
     LECB_ERR_WORKSPACE = -6,      /* workspace too small */
+    LECB_ERR_SCRATCH = -7,        /* input too large for the static scratch of lecb_encode_noalloc */
     LECB_ERR_UNCODED_SYMBOL = -16,/* device: input holds a byte whose code length is 0 */
     LECB_ERR_CORRUPT = -17        /* device: stream is not a valid v1 stream for these arguments */
 } lecb_status;
@@ -246,6 +248,21 @@ int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_bl
 int lecb_decode_from_result(const uint8_t* d_stream, const lecb_result* d_enc_res,
                             const void* d_blob, uint32_t chunk, uint64_t n, uint8_t* d_out,
                             lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream);
+
+/* lecb_encode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument, no allocation of any kind.  Its workspace is a static
+ * device array of LECB_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; inputs up to
+ * lecb_workspace_bytes(n, chunk) <= LECB_NOALLOC_SCRATCH_BYTES fit (about
+ * 250 Mi symbols at chunk 4096), larger ones return LECB_ERR_SCRATCH before
+ * any work is enqueued.  The stream, d_res and every other rule are those of
+ * lecb_encode.  All calls on one GPU share its array: calls that overlap in
+ * time on one GPU (different streams or host threads) race and must be
+ * serialised by the caller.  Each call clears the part of the array that must
+ * start at zero (a fill kernel, no memset) before its encode. */
+int lecb_encode_noalloc(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t chunk,
+                        uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* stream);
 
 /* Encode one byte plane of 16-bit words without materialising it:
  * plane 1 = high bytes (in >> 8), plane 0 = low bytes (in & 0xFF). */

@@ -26,9 +26,11 @@ LECB_ERR_TOO_LARGE = -3
 LECB_ERR_NO_SYMBOLS = -4
 LECB_ERR_HIP = -5
 LECB_ERR_WORKSPACE = -6
+LECB_ERR_SCRATCH = -7
 LECB_ERR_UNCODED_SYMBOL = -16
 LECB_ERR_CORRUPT = -17
 CONTAINER_HEADER_BYTES = 560
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class LecbError(RuntimeError):
@@ -127,6 +129,7 @@ _SIGNATURES = {
                                                        _vp, _u64, _vp, _vp, _u64, _vp]),
     "lecb_encode_fp32_pertensor_nosync": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _u64,
                                                  _vp]),
+    "lecb_encode_noalloc": (_int, [_vp, _u64, _vp, _u32, _vp, _u64, _vp, _vp]),
     "lecb_histogram_fp32": (_int, [_vp, _u64, _vp, _int, _vp]),
     "lecb_merge_fp32": (_int, [_vp, _u64, _vp, _vp]),
     "lecb_encode_fp32": (_int, [_vp, _u64, _vp, _u32, _vp, _vp, _vp, _vp, _u64, _vp]),
@@ -318,6 +321,12 @@ def lecb_encode(x, n, blob, chunk, out, res, ws, stream=None) -> None:
     _check(load().lecb_encode(_ptr(x), n, _ptr(blob), chunk, _ptr(out), out.numel(), _ptr(res),
                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_encode")
+
+
+def lecb_encode_noalloc(x, n, blob, chunk, out, res, stream=None) -> None:
+    _check(load().lecb_encode_noalloc(_ptr(x), n, _ptr(blob), chunk, _ptr(out), out.numel(), _ptr(res),
+                                      _stream(stream)),
+           "lecb_encode_noalloc")
 
 
 def lecb_encode_plane(x, n, plane, blob, chunk, out, res, ws, stream=None) -> None:

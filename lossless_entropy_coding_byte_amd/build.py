@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "liblecb.so")
 ARCH = "gfx950"
 
 SOURCES = ["kernels_misc.hip", "kernels_codebook.hip", "kernels_encode.hip", "kernels_decode.hip", "codebook.cpp",
-           "api.cpp"]
+           "api.cpp", "noalloc.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

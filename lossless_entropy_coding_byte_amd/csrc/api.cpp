@@ -209,6 +209,7 @@ const char* lecb_status_str(int status) {
         case LECB_ERR_NO_SYMBOLS: return "no codebook possible for this histogram";
         case LECB_ERR_HIP: return "HIP runtime error";
         case LECB_ERR_WORKSPACE: return "workspace too small";
+        case LECB_ERR_SCRATCH: return "input too large for the static scratch of the no-allocation encode";
         case LECB_ERR_UNCODED_SYMBOL: return "input holds a byte with no code word";
         case LECB_ERR_CORRUPT: return "corrupt stream";
         default: return "unknown status";
