@@ -12,8 +12,8 @@ Page basis
   Huffman-decode, restore the byte groups); Key design item 3: the work is cut
   into independent tasks that run in parallel.
 
-The pages fix no stream layout.  Reading (stream format v1), chosen before any
-kernel and followed bit for bit by the library:
+The pages fix no stream layout.  Reading (stream format v2), chosen before the
+kernels that follow it and followed bit for bit by the library:
 
 * ``n`` symbols are cut into ``nc = ceil(n / chunk)`` chunks; chunk c holds
   symbols ``[c*chunk, min((c+1)*chunk, n))`` -- the independent work unit;
@@ -21,22 +21,20 @@ kernel and followed bit for bit by the library:
   significant bit first, starting at bit 31 of a fresh 32-bit word and filling
   downwards; the chunk's last word is zero-padded; words are stored
   little-endian; chunks follow each other with no gap;
-* decode units: a chunk of Wc payload words is cut at K = max(1, chunk // 256)
-  word-aligned bit positions s_j = 32 * floor(j * Wc / K), j = 0..K-1; the
-  GAP of unit j is the distance in bits from s_j to the first code-word
-  boundary at or after s_j (boundaries = code-word starts and the end of the
-  chunk's data); it is always 0..15 because no code word exceeds 16 bits.
-  The gaps let a decoder start K independent decoders per chunk at exact
-  code-word starts (the "gap array" of Yamamoto et al., 2020 -- prior art, not
-  on the pages; the pages' Key design item 3 asks for independent parallel
-  tasks);
+* decode units: a chunk is cut into K = ceil(chunk / 256) units of 256
+  consecutive symbols (the last one shorter when the chunk is not a multiple
+  of 256, units past n empty); ULEN[c*K + j] = the number of code bits of
+  unit j of chunk c.  Unit j's code words start at bit sum(ULEN[c*K : c*K+j])
+  of the chunk, so a decoder can start K independent decoders per chunk, each
+  at a known bit and a known output position (the pages' Key design item 3
+  asks for independent parallel tasks; storing per-part bit counts is our
+  reading, not the pages');
 * stream = ``u32 end[nc]`` (end[c] = index, counted in payload words, one past
   chunk c's last word; chunk c spans words [end[c-1], end[c]) with
-  end[-1] = 0) || zero bytes up to a 16-byte boundary || gap nibbles
-  (nibble i = c*K + j is the low half of byte i//2 when i is even, the high
-  half when odd) || zero bytes up to a 16-byte boundary || ``u32 payload[W]``
+  end[-1] = 0) || zero bytes up to a 16-byte boundary || ``u16 ULEN[nc*K]``
+  (little-endian) || zero bytes up to a 16-byte boundary || ``u32 payload[W]``
   with W = end[nc-1];
-  size = align16(4*nc) + align16(ceil(nc*K/2)) + 4*W;  n = 0 -> empty stream;
+  size = align16(4*nc) + align16(2*nc*K) + 4*W;  n = 0 -> empty stream;
 * nothing else is stored: chunk size, n and the codebook travel outside
   (the fixed codebook is never transmitted, per Methodology step 4).
 """
@@ -68,65 +66,55 @@ def num_chunks(n: int, chunk: int) -> int:
     return -(-int(n) // int(chunk))
 
 
+UNIT = 256  # symbols per decode unit
+
+
 def units_per_chunk(chunk: int) -> int:
-    return max(1, int(chunk) // 256)
+    return -(-int(chunk) // UNIT)
 
 
 def table_bytes(n: int, chunk: int) -> int:
     return _align16(4 * num_chunks(n, chunk))
 
 
-def gap_bytes(n: int, chunk: int) -> int:
-    return _align16(-(-num_chunks(n, chunk) * units_per_chunk(chunk) // 2))
+def ulen_bytes(n: int, chunk: int) -> int:
+    return _align16(2 * num_chunks(n, chunk) * units_per_chunk(chunk))
 
 
 def header_bytes(n: int, chunk: int) -> int:
-    """Bytes before the payload: offset table and gap nibbles, each padded to 16 bytes."""
-    return table_bytes(n, chunk) + gap_bytes(n, chunk)
+    """Bytes before the payload: offset table and unit bit counts, each padded to 16 bytes."""
+    return table_bytes(n, chunk) + ulen_bytes(n, chunk)
 
 
 def unit_meta_span(n: int, chunk: int, c0: int, c1: int):
-    """Byte range [a, b) of the stream that holds the per-unit metadata of chunks
-    [c0, c1) (unit j of chunk c is entry c*K + j); the range must cover whole bytes."""
+    """Byte range [a, b) of the stream that holds the unit bit counts of chunks [c0, c1)."""
     K = units_per_chunk(chunk)
-    if (c0 * K) % 2 or (c1 * K) % 2:
-        raise ValueError("these chunks do not cover whole bytes of gap nibbles")
     tb = table_bytes(n, chunk)
-    return tb + c0 * K // 2, tb + c1 * K // 2
+    return tb + 2 * c0 * K, tb + 2 * c1 * K
 
 
 def encoded_bound(n: int, chunk: int, max_len: int = 16) -> int:
-    """Largest possible stream size (every symbol at max_len bits plus one padding word per
-    chunk), rounded up to a multiple of 16 bytes."""
+    """Largest stream any code with lengths <= max_len can give, rounded up to 16 bytes:
+    chunk c of m_c symbols takes at most ceil(m_c * max_len / 32) words, reached when
+    every symbol has a max_len-bit code word."""
     nc = num_chunks(n, chunk)
     if nc == 0:
         return 0
-    return _align16(header_bytes(n, chunk) + 4 * (-(-int(n) * int(max_len) // 32) + nc))
+    full, last = nc - 1, int(n) - (nc - 1) * int(chunk)
+    words = full * -(-int(chunk) * int(max_len) // 32) + -(-last * int(max_len) // 32)
+    return _align16(header_bytes(n, chunk) + 4 * words)
 
 
-def unit_starts(words: int, chunk: int) -> np.ndarray:
-    """Word index of each decode-unit boundary of a chunk with ``words`` payload words."""
+def unit_ranges(n: int, chunk: int):
+    """(first symbol, end symbol) of every unit, as int64[nc, K] arrays (empty units: first == end)."""
+    nc = num_chunks(n, chunk)
     K = units_per_chunk(chunk)
-    return (np.arange(K, dtype=np.int64) * int(words)) // K
-
-
-def _gap_of(boundaries, s):
-    """First element of the sorted ``boundaries`` at or after bit s, minus s."""
-    i = int(np.searchsorted(boundaries, s, side="left"))
-    return int(boundaries[i]) - s
-
-
-def _pack_nibbles(gaps: np.ndarray, nbytes: int) -> np.ndarray:
-    g = np.zeros(2 * nbytes, dtype=np.uint8)
-    g[: gaps.size] = gaps
-    return (g[0::2] | (g[1::2] << 4)).astype(np.uint8)
-
-
-def _unpack_nibbles(raw: np.ndarray) -> np.ndarray:
-    out = np.empty(2 * raw.size, dtype=np.uint8)
-    out[0::2] = raw & 0xF
-    out[1::2] = raw >> 4
-    return out
+    c = np.arange(nc, dtype=np.int64)[:, None]
+    j = np.arange(K, dtype=np.int64)[None, :]
+    chunk_end = np.minimum((c + 1) * chunk, n)
+    first = np.minimum(c * chunk + j * UNIT, chunk_end)
+    end = np.minimum(first + UNIT, chunk_end)
+    return first, end
 
 
 def _check_args(sym, lengths, chunk):
@@ -143,13 +131,14 @@ def _check_args(sym, lengths, chunk):
 # encoder (i): the definition, one character per bit.  Small inputs only.
 # --------------------------------------------------------------------------
 
-def _assemble(n, chunk, ends, gaps, payload_words):
+def _assemble(n, chunk, ends, ulen, payload_words):
     nc = num_chunks(n, chunk)
     table = np.zeros(table_bytes(n, chunk) // 4, dtype="<u4")
     table[:nc] = ends
-    gap = _pack_nibbles(np.asarray(gaps, dtype=np.uint8), gap_bytes(n, chunk))
+    units = np.zeros(ulen_bytes(n, chunk) // 2, dtype="<u2")
+    units[: nc * units_per_chunk(chunk)] = np.asarray(ulen, dtype=np.int64).ravel()
     payload = np.asarray(payload_words, dtype=np.uint64).astype("<u4")
-    return np.concatenate([table.view(np.uint8), gap, payload.view(np.uint8)])
+    return np.concatenate([table.view(np.uint8), units.view(np.uint8), payload.view(np.uint8)])
 
 
 def encode_bitstring(sym, lengths, codes, chunk: int):
@@ -163,31 +152,29 @@ def encode_bitstring(sym, lengths, codes, chunk: int):
     nc = num_chunks(n, chunk)
     if nc == 0:
         return np.zeros(0, dtype=np.uint8), 0
-    words, ends, gaps = [], [], []
+    K = units_per_chunk(chunk)
+    words, ends, ulen = [], [], []
     payload_bits = 0
     for c in range(nc):
-        parts = []
-        for s in sym[c * chunk: min((c + 1) * chunk, n)]:
-            ln = int(lengths[s])
-            if ln == 0:
-                raise UncodedSymbol(f"byte {int(s)} has no code")
-            parts.append(format(int(codes[s]), f"0{ln}b"))
-        bits = "".join(parts)
+        chunk_syms = sym[c * chunk: min((c + 1) * chunk, n)]
+        bits = ""
+        for j in range(K):
+            unit = ""
+            for s in chunk_syms[j * UNIT:(j + 1) * UNIT]:
+                ln = int(lengths[s])
+                if ln == 0:
+                    raise UncodedSymbol(f"byte {int(s)} has no code")
+                unit += format(int(codes[s]), f"0{ln}b")
+            ulen.append(len(unit))
+            bits += unit
         payload_bits += len(bits)
-        boundaries = [0]
-        for part in parts:
-            boundaries.append(boundaries[-1] + len(part))  # starts of the next word, then the data end
         bits += "0" * (-len(bits) % 32)
-        nwords = len(bits) // 32
-        for w in unit_starts(nwords, chunk):
-            s_j = 32 * int(w)
-            gaps.append(min(b for b in boundaries if b >= s_j) - s_j)
         for i in range(0, len(bits), 32):
             words.append(int(bits[i:i + 32], 2))
         ends.append(len(words))
     if len(words) >= 1 << 32:
         raise OverflowError("payload too large for 32-bit word offsets")
-    return _assemble(n, chunk, ends, gaps, words), payload_bits
+    return _assemble(n, chunk, ends, ulen, words), payload_bits
 
 
 # --------------------------------------------------------------------------
@@ -225,8 +212,8 @@ def encode(sym, lengths, codes, chunk: int):
     bit 31-(g&31), spilling into the next word when it crosses the boundary.
     Fields of distinct symbols are disjoint, so each word is the plain SUM of
     its fields; sums stay below 2^32 and are exact in float64 bincount.
-    Gaps: for each unit boundary S (global bit), the first code-word start at
-    or after S inside the same chunk, else the chunk's data end.
+    Unit bit counts: the code lengths summed per unit (symbol i of chunk c is
+    in unit (i - c*chunk) // 256).
     """
     sym, lengths = _check_args(sym, lengths, chunk)
     codes = np.asarray(codes, dtype=np.int64).ravel()
@@ -242,9 +229,7 @@ def encode(sym, lengths, codes, chunk: int):
     if W >= 1 << 32:
         raise OverflowError("payload too large for 32-bit word offsets")
     starts = ends - words
-    data_end = 32 * starts + bits  # global bit just past each chunk's last code word
-    unit_bit = 32 * (starts[:, None] + (np.arange(K, dtype=np.int64)[None, :] * words[:, None]) // K)
-    gaps = np.full((nc, K), -1, dtype=np.int64)
+    ulen = np.zeros(nc * K, dtype=np.int64)
     payload = np.zeros(W + 1, dtype=np.float64)
     block = max(1, (1 << 22) // chunk) * chunk
     for start in range(0, n, block):
@@ -265,18 +250,15 @@ def encode(sym, lengths, codes, chunk: int):
         lo = np.where(fits, 0, (cd << np.maximum(32 + shift, 0)) & 0xFFFFFFFF)
         payload += np.bincount(w, weights=hi.astype(np.float64), minlength=W + 1)
         payload += np.bincount(w + 1, weights=lo.astype(np.float64), minlength=W + 2)[: W + 1]
-        # gaps of the unit boundaries of this block's chunks
-        c0, c1 = int(cid[0]), int(cid[-1]) + 1
-        S = unit_bit[c0:c1]
-        i = np.searchsorted(g, S.ravel(), side="left").reshape(S.shape)
-        inside = (i < g.size)
-        inside[inside] &= cid[i[inside]] == np.arange(c0, c1)[:, None].repeat(K, 1)[inside]
-        nxt = np.where(inside, g[np.minimum(i, g.size - 1)], data_end[c0:c1, None])
-        gaps[c0:c1] = nxt - S
-    assert np.all((gaps >= 0) & (gaps <= 15))
+        # bit counts of the units of this block's symbols
+        uid = cid * K + ((start + np.arange(s.size, dtype=np.int64)) - cid * chunk) // UNIT
+        u0 = int(uid[0])
+        part = np.bincount(uid - u0, weights=ln).astype(np.int64)
+        ulen[u0:u0 + part.size] += part
+    assert np.all(ulen <= UNIT * 16)
     payload = payload[:W].astype(np.uint64)
     assert np.all(payload < (1 << 32))
-    return _assemble(n, chunk, ends, gaps.ravel(), payload), int(bits.sum())
+    return _assemble(n, chunk, ends, ulen, payload), int(bits.sum())
 
 
 # --------------------------------------------------------------------------
@@ -284,7 +266,7 @@ def encode(sym, lengths, codes, chunk: int):
 # --------------------------------------------------------------------------
 
 def parse_table(stream, n: int, chunk: int):
-    """Validate the layout; return (starts, ends, gaps[nc, K], payload words as uint64)."""
+    """Validate the layout; return (starts, ends, ulen[nc, K], payload words as uint64)."""
     stream = np.ascontiguousarray(stream).view(np.uint8).ravel()
     nc = num_chunks(n, chunk)
     K = units_per_chunk(chunk)
@@ -300,10 +282,9 @@ def parse_table(stream, n: int, chunk: int):
     ends = stream[: 4 * nc].view("<u4").astype(np.int64)
     if np.any(stream[4 * nc: tb] != 0):
         raise CorruptStream("non-zero table padding")
-    nib = _unpack_nibbles(stream[tb:hb])
-    if np.any(nib[nc * K:] != 0):
-        raise CorruptStream("non-zero gap padding")
-    gaps = nib[: nc * K].astype(np.int64).reshape(nc, K)
+    if np.any(stream[tb + 2 * nc * K: hb] != 0):
+        raise CorruptStream("non-zero unit-count padding")
+    ulen = stream[tb: tb + 2 * nc * K].view("<u2").astype(np.int64).reshape(nc, K)
     W = (stream.size - hb) // 4
     starts = np.concatenate([[0], ends[:-1]])
     if np.any(ends <= starts):
@@ -311,16 +292,13 @@ def parse_table(stream, n: int, chunk: int):
     if int(ends[-1]) != W:
         raise CorruptStream("offset table disagrees with the stream size")
     payload = stream[hb:].view("<u4").astype(np.uint64)
-    return starts, ends, gaps, payload
+    return starts, ends, ulen, payload
 
 
-def _check_gaps(starts, ends, gaps, boundary_lists, chunk):
-    """Every stored gap must equal the distance to the first boundary at or after its unit start."""
-    for c in range(starts.size):
-        b = np.asarray(boundary_lists[c], dtype=np.int64)
-        for j, w in enumerate(unit_starts(int(ends[c] - starts[c]), chunk)):
-            if _gap_of(b, 32 * int(w)) != int(gaps[c, j]):
-                raise CorruptStream("gap disagrees with the code-word boundaries")
+def _check_units(ulen, unit_bits):
+    """The stored unit bit counts must be the bits the decode found for each unit."""
+    if not np.array_equal(np.asarray(unit_bits, dtype=np.int64).reshape(ulen.shape), ulen):
+        raise CorruptStream("unit bit count disagrees with the code words")
 
 
 def _canonical_tables(lengths):
@@ -351,15 +329,16 @@ def decode_bitwise(stream, lengths, chunk: int, n: int) -> np.ndarray:
     (v - first[l])-th symbol of length l in canonical order.
     """
     lengths = np.asarray(lengths, dtype=np.int64).ravel()
-    starts, ends, gaps, payload = parse_table(stream, n, chunk)
+    starts, ends, ulen, payload = parse_table(stream, n, chunk)
     first, count, index, syms = _canonical_tables(lengths)
+    K = units_per_chunk(chunk)
     out = np.zeros(n, dtype=np.uint8)
-    boundary_lists = []
+    unit_bits = np.zeros(ulen.shape, dtype=np.int64)
     for c in range(starts.size):
         words = payload[starts[c]:ends[c]]
         bitstr = "".join(format(int(w), "032b") for w in words)
         p = 0
-        bl = [0]
+        at = [0]  # bit position at every unit boundary
         for k in range(min(chunk, n - c * chunk)):
             v = 0
             ln = 0
@@ -374,13 +353,15 @@ def decode_bitwise(stream, lengths, chunk: int, n: int) -> np.ndarray:
                 if count[ln] and first[ln] <= v < first[ln] + count[ln]:
                     out[c * chunk + k] = syms[index[ln] + v - first[ln]]
                     break
-            bl.append(p)
+            if (k + 1) % UNIT == 0:
+                at.append(p)
+        at += [p] * (K + 1 - len(at))
+        unit_bits[c] = np.diff(at[:K + 1])
         if (len(bitstr) - p) >= 32:
             raise CorruptStream("chunk holds more words than its symbols need")
         if "1" in bitstr[p:]:
             raise CorruptStream("non-zero padding after the last code word")
-        boundary_lists.append(bl)
-    _check_gaps(starts, ends, gaps, boundary_lists, chunk)
+    _check_units(ulen, unit_bits)
     return out
 
 
@@ -405,15 +386,15 @@ def _lookup_table(lengths, codes):
 def decode(stream, lengths, chunk: int, n: int, codes=None) -> np.ndarray:
     """Decoder (ii): all chunks advance one symbol per step through a 16-bit lookup table.
 
-    The gaps are not needed to decode sequentially; they are checked afterwards
-    against the code-word boundaries the decode found.
+    The unit bit counts are not needed to decode sequentially; they are checked
+    afterwards against the positions the decode reached at the unit boundaries.
     """
     from .huffman import canonical_codes
 
     lengths = np.asarray(lengths, dtype=np.int64).ravel()
     if codes is None:
         codes = canonical_codes(lengths)
-    starts, ends, gaps, payload = parse_table(stream, n, chunk)
+    starts, ends, ulen, payload = parse_table(stream, n, chunk)
     nc = starts.size
     out = np.zeros(n, dtype=np.uint8)
     if nc == 0:
@@ -425,23 +406,8 @@ def decode(stream, lengths, chunk: int, n: int, codes=None) -> np.ndarray:
     endbit = ends * 32
     m = np.minimum(chunk, n - np.arange(nc, dtype=np.int64) * chunk)
     base = np.arange(nc, dtype=np.int64) * chunk
-    # unit boundaries (global bits) and the first code-word boundary found at or after each
-    wc = ends - starts
-    ubit = 32 * (starts[:, None] + (np.arange(K, dtype=np.int64)[None, :] * wc[:, None]) // K)
-    found = np.full((nc, K), -1, dtype=np.int64)
-
-    def mark(act, p):
-        # a boundary at p settles every unit boundary in (previous boundary, p]
-        sub = ubit[act] if not isinstance(act, slice) else ubit
-        f = found[act] if not isinstance(act, slice) else found
-        hit = (f < 0) & (sub <= p[:, None])
-        f[hit] = np.broadcast_to(p[:, None], f.shape)[hit]
-        if isinstance(act, slice):
-            found[:] = f
-        else:
-            found[act] = f
-
-    mark(slice(None), pos.copy())
+    at = np.zeros((nc, K + 1), dtype=np.int64)  # bit position at every unit boundary
+    at[:, 0] = pos
     for k in range(int(m.max())):
         act = np.nonzero(m > k)[0] if m[-1] <= k else slice(None)
         p = pos[act]
@@ -455,7 +421,11 @@ def decode(stream, lengths, chunk: int, n: int, codes=None) -> np.ndarray:
             raise CorruptStream("code word runs past the end of its chunk")
         out[base[act] + k] = sym_of[peek.astype(np.int64)]
         pos[act] = p + ln
-        mark(act, pos[act])
+        if (k + 1) % UNIT == 0:
+            at[act, (k + 1) // UNIT] = pos[act]
+    # boundaries at or after a chunk's last symbol are its end position
+    done = np.arange(K + 1)[None, :] >= (-(-m // UNIT))[:, None]
+    at = np.where(done, pos[:, None], at)
     if np.any(endbit - pos >= 32):
         raise CorruptStream("chunk holds more words than its symbols need")
     rest = endbit - pos
@@ -463,6 +433,5 @@ def decode(stream, lengths, chunk: int, n: int, codes=None) -> np.ndarray:
     mask = (np.uint64(1) << rest.astype(np.uint64)) - np.uint64(1)
     if np.any(last & mask):
         raise CorruptStream("non-zero padding after the last code word")
-    if np.any(found - ubit != gaps):
-        raise CorruptStream("gap disagrees with the code-word boundaries")
+    _check_units(ulen, np.diff(at, axis=1))
     return out

@@ -15,6 +15,15 @@ def _pairs(text, base):
     return out
 
 
+def _hex_bytes(text):
+    """Hex byte tokens; "xx*k" is k bytes of value xx."""
+    out = []
+    for tok in text.split():
+        v, _, k = tok.partition("*")
+        out += [int(v, 16)] * (int(k) if k else 1)
+    return np.array(out, np.uint8)
+
+
 def load():
     blocks, cur = [], {}
     with open(GOLDEN) as f:
@@ -45,8 +54,8 @@ def load():
         ex["codes"] = _pairs(b["codes"], None)  # sym -> bit string
         if "input" in b:
             ex["chunk"] = int(b["chunk"])
-            ex["input"] = np.array([int(t, 16) for t in b["input"].split()], np.uint8)
-            ex["stream"] = np.array([int(t, 16) for t in b["stream"].split()], np.uint8)
+            ex["input"] = _hex_bytes(b["input"])
+            ex["stream"] = _hex_bytes(b["stream"])
             ex["payload_bits"] = int(b["payload_bits"])
         examples.append(ex)
     return examples

@@ -118,9 +118,11 @@ def test_corrupt_streams_detected():
     bits0 = int(oracle.stream.chunk_bit_counts(x[:chunk], ln, chunk)[0])
     if bits0 % 32:
         t = s.copy(); off = tb + 4 * (int(ends[0]) - 1); t[off] |= 1; bad.append(("padding bit", t))
-    # gap section: chunk 0 has K = 4 units; change the gap of unit 1, then its padding nibble area
-    t = s.copy(); t[gb] ^= 0x10; bad.append(("gap value", t))
-    t = s.copy(); t[tb - 1] = 0x01; bad.append(("gap padding", t))
+    # unit bit counts: chunk 0 has K = 4 units; move one bit from unit 0 to unit 1
+    # (same chunk total), then change the padding after the counts
+    t = s.copy(); u = t[gb:gb + 4].view("<u2").copy(); u[0] -= 1; u[1] += 1
+    t[gb:gb + 4] = u.view(np.uint8); bad.append(("unit count", t))
+    t = s.copy(); t[tb - 1] = 0x01; bad.append(("unit count padding", t))
     for name, t in bad:
         with pytest.raises(CorruptStream):
             decode(t, ln, chunk, n)
@@ -142,33 +144,66 @@ def test_incomplete_code_rejects_unmatched_prefix():
 
 def test_chunks_are_independent():
     # The payload of chunk c depends only on chunk c's bytes: encoding a chunk alone
-    # gives the same words as its slice of the whole stream.
+    # gives the same words and unit counts as its slice of the whole stream.
     x = workloads.skewed_bytes(12, 10 * 512 + 33, sigma=30)
     ln, cd = _codebook(x)
     s, _ = encode(x, ln, cd, 512)
     nc = oracle.num_chunks(x.size, 512)
     tb = oracle.header_bytes(x.size, 512)
-    gb = oracle.table_bytes(x.size, 512)
     ends = s[:4 * nc].view("<u4").astype(np.int64)
     starts = np.concatenate([[0], ends[:-1]])
     for c in range(nc):
-        one, _ = encode(x[c * 512:(c + 1) * 512], ln, cd, 512)
+        piece = x[c * 512:(c + 1) * 512]
+        one, _ = encode(piece, ln, cd, 512)
         assert np.array_equal(one[32:], s[tb + 4 * starts[c]: tb + 4 * ends[c]])
-        assert one[16] == s[gb + c]  # K = 2 nibbles per chunk = one gap byte per chunk
+        a, b = oracle.unit_meta_span(x.size, 512, c, c + 1)
+        a1, b1 = oracle.unit_meta_span(piece.size, 512, 0, 1)
+        assert np.array_equal(one[a1:b1], s[a:b])  # K = 2 counts per chunk
 
 
-def test_gaps_point_at_code_word_starts():
-    # Every nonzero gap lands on a code-word start (or the data end) that is not word-aligned.
-    x = workloads.skewed_bytes(13, 20 * 4096 + 100, sigma=25)
+def test_unit_counts_are_the_units_code_bits():
+    # Unit j of chunk c holds symbols [c*C + 256j, c*C + 256(j+1)) (cut at the
+    # chunk's and the tensor's end); its count is the sum of their code lengths.
+    n, chunk = 20 * 4096 + 100, 4096
+    x = workloads.skewed_bytes(13, n, sigma=25)
     ln, cd = _codebook(x)
-    s, _ = encode(x, ln, cd, 4096)
-    starts, ends, gaps, payload = oracle.parse_table(s, x.size, 4096)
-    assert gaps.shape == (21, 16) and np.all(gaps[:, 0] == 0) and gaps.max() <= 15
-    assert (gaps > 0).mean() > 0.5  # most unit boundaries fall inside a code word
-    for c in range(starts.size):
-        lens = ln[x[c * 4096:(c + 1) * 4096]].astype(np.int64)
-        bnd = set(np.concatenate([[0], np.cumsum(lens)]).tolist())
-        for j, w in enumerate(oracle.stream.unit_starts(int(ends[c] - starts[c]), 4096)):
-            p = 32 * int(w) + int(gaps[c, j])
-            assert p in bnd
-            assert not any(q in bnd for q in range(32 * int(w), p))
+    s, bits = encode(x, ln, cd, chunk)
+    starts, ends, ulen, payload = oracle.parse_table(s, n, chunk)
+    assert ulen.shape == (21, 16)
+    first, end = oracle.unit_ranges(n, chunk)
+    lens = ln[x].astype(np.int64)
+    for c in range(21):
+        for j in range(16):
+            assert ulen[c, j] == lens[first[c, j]:end[c, j]].sum()
+    assert ulen.sum() == bits
+    assert np.all(ulen[20, 1:] == 0) and ulen[20, 0] == lens[20 * 4096:].sum()  # 100 symbols, one unit
+
+
+@pytest.mark.parametrize("n,chunk,L", [(1000003, 4096, 16), (5000, 1024, 9), (300, 256, 12), (65536 * 2 + 7, 65536, 16)])
+def test_encoded_bound_is_reached(n, chunk, L):
+    # The bound is the size of the stream in which every symbol has an L-bit code
+    # word (rounded up to 16 bytes): a codebook with an L-bit code and an input made
+    # of that symbol reaches it; no stream of a code with lengths <= L exceeds it.
+    f = np.array([max(1, (1 << 40) >> min(s, 39)) for s in range(256)], np.uint64)
+    ln = package_merge_lengths(f, L)
+    assert int(ln.max()) == L
+    sym = int(np.argmax(ln))
+    x = np.full(n, sym, np.uint8)
+    s, bits = encode(x, ln, canonical_codes(ln), chunk)
+    assert bits == L * n
+    assert oracle.encoded_bound(n, chunk, L) == (s.size + 15) // 16 * 16
+    y = workloads.uniform_bytes(14, n)
+    assert encode(y, ln, canonical_codes(ln), chunk)[0].size <= oracle.encoded_bound(n, chunk, L)
+
+
+def test_encoded_bound_hand_value():
+    # n = 1000003, chunk 4096, L = 16: nc = 245 chunks (244 full + 579 symbols);
+    # table align16(980) = 992 bytes; unit counts 245 * 16 * 2 = 7840 bytes
+    # (already a multiple of 16); words 244 * 4096*16/32 + ceil(579*16/32) =
+    # 499712 + 290 = 500002 -> 2000008 bytes; 992 + 7840 + 2000008 = 2008840
+    # = 125552 * 16 + 8, rounded up to 2008848.
+    assert oracle.encoded_bound(1000003, 4096, 16) == 2008848
+    # chunk 256, L = 9, n = 1000: nc = 4 (3 full + 232); table 16; counts 4*1*2 = 8 -> 16;
+    # words 3 * ceil(256*9/32) + ceil(232*9/32) = 3*72 + 66 = 282 -> 1128; 16 + 16 + 1128
+    # = 1160 = 72 * 16 + 8, rounded up to 1168.
+    assert oracle.encoded_bound(1000, 256, 9) == 1168
