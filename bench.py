@@ -47,8 +47,8 @@ sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
 
-DEVICE_LABELS = ("histogram", "codebook_build", "encode_pair", "decode_pair", "merge")
-HOST_LABELS = ("histogram+codebooks", "encode_pair", "decode_pair", "merge")
+DEVICE_LABELS = ("histogram", "codebook_build", "encode_pair", "decode_pair")
+HOST_LABELS = ("histogram+codebooks", "encode_pair", "decode_pair")
 METRIC = "encode / decode GB/s of uncompressed input on 1 MI355X; % of HBM peak; ratio"
 HBM_PEAK_GBPS = 8000.0
 
@@ -273,19 +273,15 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         res_dec = lecb.new_results(2, dev)
         ws = lecb.new_workspace(n, chunk, dev)
         y = torch.empty(n, dtype=torch.int16, device=dev)
-        scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=dev)
         state = {}
-
-        half = (n + 15) // 16 * 16
-        p_hi, p_lo = scratch[:n], scratch[half:half + n]
 
         def step_device(tm):
             # the per-tensor path kernel by kernel -- what
             # lecb_encode_bf16_pertensor_nosync and lecb_decode_bf16_from_results
             # enqueue -- with events on the launch stream between the kernels:
             # histograms -> codebooks built on the device -> two-plane encode ->
-            # two-plane decode (stream sizes read on the device) -> merge.
-            # No host synchronisation anywhere in the step.
+            # two-plane decode that writes the 16-bit words (stream sizes read on
+            # the device).  No host synchronisation anywhere in the step.
             mark = tm.chain(DEVICE_LABELS)
             lecb.lecb_histogram_bf16(xd, hist_d[:256], hist_d[256:])
             mark()
@@ -304,10 +300,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         def tail(mark):
             lecb.lecb_encode_bf16(xd, n, blob_hi, blob_lo, chunk, out_hi, out_lo, res, ws)
             mark()
-            lecb.lecb_decode_bf16_planes_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, p_hi, p_lo,
-                                                      res_dec, ws)
-            mark()
-            lecb.lecb_merge_bf16(p_hi, p_lo, y)
+            lecb.lecb_decode_bf16_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, y, res_dec, ws)
             mark()
 
         def codebooks():
@@ -324,16 +317,13 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         res_dec = lecb.new_results(4, dev)
         ws = lecb.new_workspace(n, chunk, dev)
         y = torch.empty(n, dtype=torch.int32, device=dev)
-        plane = (n + 15) // 16 * 16
-        scratch = torch.empty(4 * plane, dtype=torch.uint8, device=dev)
-        planes = [scratch[k * plane:k * plane + n] for k in range(4)]
         state = {}
 
         def step_device(tm):
             # kernel by kernel, as lecb_encode_fp32_pertensor_nosync and
             # lecb_decode_fp32_from_results enqueue it: histograms -> four
-            # codebooks built on the device -> two two-plane encodes -> two
-            # two-plane decodes (sizes read on the device) -> merge
+            # codebooks built on the device -> two two-plane encodes -> one
+            # four-plane decode that writes the elements (sizes read on the device)
             mark = tm.chain(DEVICE_LABELS)
             lecb.lecb_histogram_fp32(xd, hist_d)
             mark()
@@ -350,13 +340,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         def tail(mark):
             lecb.lecb_encode_fp32(xd, n, blobs, chunk, outs, res, ws)
             mark()
-            for h in range(2):
-                off = 2 * h * lecb.RESULT_DTYPE.itemsize
-                lecb.lecb_decode_bf16_planes_from_results(outs[2 * h], outs[2 * h + 1], res[off:], blobs[2 * h],
-                                                          blobs[2 * h + 1], chunk, n, planes[2 * h],
-                                                          planes[2 * h + 1], res_dec[off:], ws)
-            mark()
-            lecb.lecb_merge_fp32(planes, y)
+            lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, res_dec, ws)
             mark()
 
         def codebooks():
@@ -511,7 +495,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
             T.stop("fused_encode")
             T.start("fused_decode")
             lecb.lecb_decode_bf16_delta_from_results(out_hi, out_lo, res, blob_hi, blob_lo, chunk, n, w0d,
-                                                     w1_out, scratch, res_dec, ws)
+                                                     w1_out, res_dec, ws)
             T.stop("fused_decode")
 
         fused_step()
@@ -530,7 +514,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
         rr, rq = lecb.results_to_numpy(res), lecb.results_to_numpy(res_dec)
         same = [int(v["bytes"]) for v in rr] == sizes
         fused = {
-            "what": "W0, W1 -> delta streams -> W1 (XOR fused into the histogram, encode and merge)",
+            "what": "W0, W1 -> delta streams -> W1 (XOR fused into the histogram, the encode and the decode's restore)",
             "step_ms": round(fw * 1e3, 4), "encode_ms": round(fe, 4), "decode_ms": round(fd, 4),
             "GBps_snapshot": round(2 * n / fw / 1e9, 2),
             "round_trip": bool(torch.equal(w1_out, w1d)),
@@ -546,7 +530,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
     if cfg["kind"] in ("bf16", "fp32"):
         enc_ms = sum(kernels[lb] for lb in kernels if lb in ("histogram", "codebook_build", "histogram+codebooks",
                                                               "encode_pair"))
-        dec_ms = kernels["decode_pair"] + kernels["merge"]
+        dec_ms = kernels["decode_pair"]
     else:
         enc_ms, dec_ms = cold_kernels["encode"], cold_kernels["decode"]
     cold = {
@@ -701,7 +685,7 @@ def run_gpu(cfg, x, hist, steps, warmup, lengths_out):
 
 KERNEL_SOURCES = {"encode": "kernels_encode.hip", "encode_pair": "kernels_encode.hip",
                   "decode": "kernels_decode.hip", "decode_pair": "kernels_decode.hip",
-                  "histogram": "kernels_misc.hip", "merge": "kernels_misc.hip"}
+                  "histogram": "kernels_misc.hip"}
 
 
 def source_sha(label):
@@ -736,15 +720,16 @@ def roofline(cfg, info):
         algo = {
             # the pair encode reads the 16-bit words once and writes both streams
             "encode_pair": 2 * n + s_hi + s_lo,
-            # the two-plane decode reads both streams and writes one byte per element per plane
+            # the two-plane decode reads both streams and writes the 16-bit words
             "decode_pair": s_hi + s_lo + 2 * n,
-            "histogram": 2 * n, "merge": 4 * n,
+            "histogram": 2 * n,
         }
     elif cfg["kind"] == "fp32":
-        # two launch pairs each way (bytes 3, 2 and bytes 1, 0); the
-        # algorithmic bytes are those of the whole four-plane operation
+        # encode: two launch pairs (bytes 3, 2 and bytes 1, 0); decode: one
+        # four-plane launch; the algorithmic bytes are those of the whole
+        # four-plane operation
         S = sum(info["sizes"])
-        algo = {"encode_pair": 4 * n + S, "decode_pair": S + 4 * n, "histogram": 4 * n, "merge": 8 * n}
+        algo = {"encode_pair": 4 * n + S, "decode_pair": S + 4 * n, "histogram": 4 * n}
     else:
         s = info["sizes"][0]
         algo = {"encode": n + s, "decode": s + n}

@@ -19,20 +19,19 @@
  *    grouped the same way into four byte planes (the byte-group size is a
  *    design knob of the same page, Key design item 1).
  *
- * Stream format v1 (identical, bit for bit, to the oracle's):
- *   stream  = u32 end[nc] | zero pad to 16 B | gap nibbles[nc*K] | zero pad to 16 B | u32 payload[W]
+ * Stream format v2 (identical, bit for bit, to the oracle's):
+ *   stream  = u32 end[nc] | zero pad to 16 B | u16 ulen[nc*K] | zero pad to 16 B | u32 payload[W]
  *   nc      = ceil(n / chunk); chunk c holds symbols [c*chunk, min((c+1)*chunk, n));
  *   end[c]  = payload word one past chunk c's last word (chunk c spans
  *             [end[c-1], end[c]) with end[-1] = 0); W = end[nc-1];
  *   payload = per chunk, the code words of its symbols concatenated, most
  *             significant bit first within 32-bit words (words stored
  *             little-endian), starting on a fresh word, last word zero-padded;
- *   gaps    = K = chunk/256 decode units per chunk; unit j of a chunk with
- *             Wc words starts at bit s_j = 32*floor(j*Wc/K); its gap (0..15)
- *             is the distance from s_j to the first code-word boundary at or
- *             after s_j (code-word starts and the chunk's data end count);
- *             nibble i = c*K + j is the low half of byte i/2 if i is even;
- *   size    = align16(4*nc) + align16(ceil(nc*K/2)) + 4*W  (0 when n == 0).
+ *   ulen    = K = chunk/256 decode units per chunk, unit j = the chunk's
+ *             symbols [256j, 256j+256) (empty past n); ulen[c*K + j] = the
+ *             code bits of unit j, so unit j starts at bit
+ *             ulen[c*K] + ... + ulen[c*K + j-1] of its chunk;
+ *   size    = align16(4*nc) + align16(2*nc*K) + 4*W  (0 when n == 0).
  * The codebook is not in the stream.  Code words are canonical: they follow
  * from the 256 code lengths alone (shorter codes first, ties by symbol).
  *
@@ -68,7 +67,7 @@
 extern "C" {
 #endif
 
-#define LECB_ABI_VERSION 1u
+#define LECB_ABI_VERSION 2u
 #define LECB_MAX_CODE_LEN 16u
 #define LECB_UNIT_SYMBOLS 256u
 #define LECB_MIN_CHUNK 256u
@@ -86,7 +85,7 @@ typedef enum {
     LECB_ERR_WORKSPACE = -6,      /* workspace too small */
     LECB_ERR_SCRATCH = -7,        /* input too large for the static scratch of lecb_encode_noalloc */
     LECB_ERR_UNCODED_SYMBOL = -16,/* device: input holds a byte whose code length is 0 */
-    LECB_ERR_CORRUPT = -17        /* device: stream is not a valid v1 stream for these arguments */
+    LECB_ERR_CORRUPT = -17        /* device: stream is not a valid v2 stream for these arguments */
 } lecb_status;
 
 /* Canonical codebook, host side.  Fully determined by len[]. */
@@ -112,11 +111,12 @@ const char* lecb_status_str(int status);
 
 /* ceil(n / chunk); 0 on a bad chunk. */
 uint64_t lecb_num_chunks(uint64_t n, uint32_t chunk);
-/* Bytes before the payload: align16(4*nc) + align16(ceil(nc*K/2)). */
+/* Bytes before the payload: align16(4*nc) + align16(2*nc*K). */
 uint64_t lecb_header_bytes(uint64_t n, uint32_t chunk);
 /* Largest stream any codebook with lengths <= max_len can produce, rounded
- * up to 16 bytes: align16(header + 4*(ceil(n*max_len/32) + nc)).  0 on bad
- * arguments. */
+ * up to 16 bytes: align16(header + 4 * sum over chunks of ceil(m_c*max_len/32))
+ * for chunks of m_c symbols -- the size when every symbol has a max_len-bit
+ * code word.  0 on bad arguments. */
 uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len);
 /* Workspace bytes an encode or decode of n symbols with this chunk needs. */
 uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk);
@@ -218,7 +218,7 @@ int lecb_split_bf16(const uint16_t* d_in, uint64_t n, uint8_t* d_hi, uint8_t* d_
 int lecb_merge_bf16(const uint8_t* d_hi, const uint8_t* d_lo, uint64_t n, uint16_t* d_out,
                     void* stream);
 
-/* Encode n bytes with an uploaded codebook into a v1 stream ("Single-Stage
+/* Encode n bytes with an uploaded codebook into a v2 stream ("Single-Stage
  * Huffman Encoder for ML Compression", Methodology step 4).  out_capacity must
  * be at least lecb_header_bytes(n, chunk); a payload that does not fit sets
  * status CAPACITY (lecb_encoded_bound gives a size that always fits).
@@ -227,7 +227,7 @@ int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t ch
                 uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
                 uint64_t ws_bytes, void* stream);
 
-/* Decode a v1 stream of n symbols into d_out[n] (reverse path of "Lossless
+/* Decode a v2 stream of n symbols into d_out[n] (reverse path of "Lossless
  * Compression for LLM Tensor Incremental Snapshots", Technical framework).
  * stream_bytes must be the exact stream size (lecb_result.bytes of the
  * encode).  The buffer must be readable up to align16(stream_bytes) (the
@@ -235,7 +235,8 @@ int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t ch
  * number of payload words returns LECB_ERR_CORRUPT at once.  A stream that is not exactly what
  * lecb_encode produces for these arguments sets status CORRUPT (offset table
  * not increasing or past the stream, a bit pattern with no code word, a code
- * word crossing a unit or chunk end, a gap that is not the first boundary,
+ * word crossing its chunk's end, a unit whose code words do not take exactly
+ * its stored bit count, a chunk whose bit counts disagree with its words,
  * non-zero padding, too many words). */
 int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_blob,
                 uint32_t chunk, uint64_t n, uint8_t* d_out, lecb_result* d_res, void* d_ws,
@@ -330,13 +331,12 @@ int lecb_encode_bf16_delta_pertensor(const uint16_t* d_w0, const uint16_t* d_w1,
                                      uint8_t* d_out_lo, uint64_t cap_lo, lecb_result* d_res2,
                                      void* d_ws, uint64_t ws_bytes, void* stream);
 
-/* Decode both delta planes (one launch) and write W1 = W0 ^ (hi << 8 | lo).
- * d_scratch: 2*align16(n) bytes for the planes.  d_w1 may not alias d_w0. */
+/* Decode both delta planes and write W1 = W0 ^ (hi << 8 | lo) in the same
+ * launch (the decoded planes never go to memory).  d_w1 may not be d_w0. */
 int lecb_decode_bf16_delta(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
                            uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
                            uint32_t chunk, uint64_t n, const uint16_t* d_w0, uint16_t* d_w1,
-                           uint8_t* d_scratch, lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
-                           void* stream);
+                           lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
 
 /* As lecb_decode_bf16_delta, with the stream sizes read on the device from
  * the encoder's two results (d_enc_res2), so encode -> decode needs no host
@@ -344,7 +344,7 @@ int lecb_decode_bf16_delta(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t
 int lecb_decode_bf16_delta_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
                                         const lecb_result* d_enc_res2, const void* d_blob_hi,
                                         const void* d_blob_lo, uint32_t chunk, uint64_t n,
-                                        const uint16_t* d_w0, uint16_t* d_w1, uint8_t* d_scratch,
+                                        const uint16_t* d_w0, uint16_t* d_w1,
                                         lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
                                         void* stream);
 
@@ -388,18 +388,20 @@ int lecb_decode_bf16_planes_from_results(const uint8_t* d_hi, const uint8_t* d_l
 int lecb_decode_bf16_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
                                   const lecb_result* d_enc_res2, const void* d_blob_hi,
                                   const void* d_blob_lo, uint32_t chunk, uint64_t n,
-                                  uint16_t* d_out, uint8_t* d_scratch, lecb_result* d_res2,
+                                  uint16_t* d_out, lecb_result* d_res2,
                                   void* d_ws, uint64_t ws_bytes, void* stream);
 
 /* Decode both planes and restore the 16-bit words, out[i] = hi[i] << 8 | lo[i]:
  * the reverse path of "Lossless Compression for LLM Tensor Incremental
  * Snapshots", Technical framework (Huffman-decode each byte group, then
- * restore the byte groups).  d_scratch: 2*align16(n) bytes of device memory
- * (caller-owned) that receive the decoded planes before the restore.  d_ws:
- * lecb_workspace_bytes(n, chunk).  Errors as lecb_decode, per plane. */
+ * restore the byte groups), in ONE launch: the lanes that decode the two
+ * planes of the same 256 elements sit side by side and write the restored
+ * words directly (the planes never go to memory).  d_out: n u16, 16-byte
+ * aligned.  d_ws: lecb_workspace_bytes(n, chunk).  Errors as lecb_decode,
+ * per plane. */
 int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
                      uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
-                     uint32_t chunk, uint64_t n, uint16_t* d_out, uint8_t* d_scratch,
+                     uint32_t chunk, uint64_t n, uint16_t* d_out,
                      lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ codebooks built on the device
@@ -498,19 +500,18 @@ int lecb_encode_fp32_pertensor_nosync(const uint32_t* d_in, uint64_t n, uint32_t
                                       void* stream);
 
 /* Decode the four streams (exact sizes in stream_bytes[4]) and restore the
- * 32-bit elements.  d_scratch: 4*align16(n) bytes of device memory for the
- * decoded planes (plane p at p*align16(n)).  Errors as lecb_decode_bf16. */
+ * 32-bit elements in ONE launch (the four lanes of the same 256 elements sit
+ * side by side and write the elements directly).  Errors as lecb_decode_bf16. */
 int lecb_decode_fp32(const uint8_t* const d_stream[4], const uint64_t stream_bytes[4],
                      const void* const d_blob[4], uint32_t chunk, uint64_t n, uint32_t* d_out,
-                     uint8_t* d_scratch, lecb_result* d_res4, void* d_ws, uint64_t ws_bytes,
-                     void* stream);
+                     lecb_result* d_res4, void* d_ws, uint64_t ws_bytes, void* stream);
 
 /* lecb_decode_fp32 with the four sizes read on the device from the results
  * an encode wrote (d_enc_res4), so encode -> decode needs no host
  * synchronisation. */
 int lecb_decode_fp32_from_results(const uint8_t* const d_stream[4], const lecb_result* d_enc_res4,
                                   const void* const d_blob[4], uint32_t chunk, uint64_t n,
-                                  uint32_t* d_out, uint8_t* d_scratch, lecb_result* d_res4,
+                                  uint32_t* d_out, lecb_result* d_res4,
                                   void* d_ws, uint64_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

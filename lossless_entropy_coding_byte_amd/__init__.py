@@ -90,9 +90,9 @@ _SIGNATURES = {
     "lecb_encode_bf16_delta_pertensor": (_int, [_vp, _vp, _u64, _u32, _u32, _vp, _vp, _vp,
                                                 ctypes.POINTER(lecb_codebook), ctypes.POINTER(lecb_codebook),
                                                 _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
-    "lecb_decode_bf16_delta": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _vp,
+    "lecb_decode_bf16_delta": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp,
                                       _u64, _vp]),
-    "lecb_decode_bf16_delta_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp,
+    "lecb_decode_bf16_delta_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp,
                                                    _vp, _u64, _vp]),
     "lecb_drift_check": (_int, [_vp, ctypes.POINTER(lecb_codebook), _u32, _u32,
                                 ctypes.POINTER(lecb_codebook), ctypes.POINTER(_int),
@@ -115,11 +115,11 @@ _SIGNATURES = {
                                           ctypes.POINTER(lecb_codebook), ctypes.POINTER(lecb_codebook),
                                           _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp]),
     "lecb_decode_from_result": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
-    "lecb_decode_bf16_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_bf16_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
     "lecb_decode_bf16_planes_from_results": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp,
                                                     _u64, _vp]),
     "lecb_decode_bf16_planes": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
-    "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_bf16": (_int, [_vp, _u64, _vp, _u64, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
     "lecb_pertensor_codebooks": (_int, [_vp, _u32, _u64, _u32, _vp, _vp, ctypes.POINTER(lecb_codebook), _vp]),
     "lecb_build_codebook_device": (_int, [_vp, _u32, _u32, _u32, _vp, _vp]),
     "lecb_codebook_download": (_int, [_vp, ctypes.POINTER(lecb_codebook), _vp]),
@@ -135,8 +135,8 @@ _SIGNATURES = {
     "lecb_encode_fp32": (_int, [_vp, _u64, _vp, _u32, _vp, _vp, _vp, _vp, _u64, _vp]),
     "lecb_encode_fp32_pertensor": (_int, [_vp, _u64, _u32, _u32, _vp, _vp, ctypes.POINTER(lecb_codebook),
                                           _vp, _vp, _vp, _vp, _u64, _vp]),
-    "lecb_decode_fp32": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
-    "lecb_decode_fp32_from_results": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_fp32": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
+    "lecb_decode_fp32_from_results": (_int, [_vp, _vp, _vp, _u32, _u64, _vp, _vp, _vp, _u64, _vp]),
 }
 
 _lib = None
@@ -351,11 +351,11 @@ def lecb_decode_from_result(stream_buf, enc_res, blob, chunk, n, out, res, ws, s
            "lecb_decode_from_result")
 
 
-def lecb_decode_bf16_from_results(hi, lo, enc_res2, blob_hi, blob_lo, chunk, n, out, scratch, res2, ws,
+def lecb_decode_bf16_from_results(hi, lo, enc_res2, blob_hi, blob_lo, chunk, n, out, res2, ws,
                                   stream=None) -> None:
-    """Both planes decoded and merged, sizes read on the device from the encoder's results."""
+    """Both planes decoded into the 16-bit words, sizes read on the device from the encoder's results."""
     _check(load().lecb_decode_bf16_from_results(_ptr(hi), _ptr(lo), _ptr(enc_res2), _ptr(blob_hi),
-                                                _ptr(blob_lo), chunk, n, _ptr(out), _ptr(scratch),
+                                                _ptr(blob_lo), chunk, n, _ptr(out),
                                                 _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
                                                 _stream(stream)),
            "lecb_decode_bf16_from_results")
@@ -422,19 +422,19 @@ def lecb_encode_bf16_delta_pertensor(w0, w1, n, chunk, max_len, hist, blob_hi, b
     return cb_hi, cb_lo
 
 
-def lecb_decode_bf16_delta(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, w0, w1, scratch, res2,
+def lecb_decode_bf16_delta(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, w0, w1, res2,
                            ws, stream=None) -> None:
     _check(load().lecb_decode_bf16_delta(_ptr(hi), hi_bytes, _ptr(lo), lo_bytes, _ptr(blob_hi),
-                                         _ptr(blob_lo), chunk, n, _ptr(w0), _ptr(w1), _ptr(scratch),
+                                         _ptr(blob_lo), chunk, n, _ptr(w0), _ptr(w1),
                                          _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream(stream)), "lecb_decode_bf16_delta")
 
 
-def lecb_decode_bf16_delta_from_results(hi, lo, enc_res2, blob_hi, blob_lo, chunk, n, w0, w1, scratch,
+def lecb_decode_bf16_delta_from_results(hi, lo, enc_res2, blob_hi, blob_lo, chunk, n, w0, w1,
                                         res2, ws, stream=None) -> None:
     _check(load().lecb_decode_bf16_delta_from_results(
         _ptr(hi), _ptr(lo), _ptr(enc_res2), _ptr(blob_hi), _ptr(blob_lo), chunk, n, _ptr(w0), _ptr(w1),
-        _ptr(scratch), _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+        _ptr(res2), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
         "lecb_decode_bf16_delta_from_results")
 
 
@@ -449,10 +449,10 @@ def lecb_encode_adaptive(x, n, chunk, max_len, tol_ppm, hist, cb: lecb_codebook,
     return bool(ref.value)
 
 
-def lecb_decode_bf16(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, out, scratch, res2, ws,
+def lecb_decode_bf16(hi, hi_bytes, lo, lo_bytes, blob_hi, blob_lo, chunk, n, out, res2, ws,
                      stream=None) -> None:
     _check(load().lecb_decode_bf16(_ptr(hi), hi_bytes, _ptr(lo), lo_bytes, _ptr(blob_hi),
-                                   _ptr(blob_lo), chunk, n, _ptr(out), _ptr(scratch), _ptr(res2),
+                                   _ptr(blob_lo), chunk, n, _ptr(out), _ptr(res2),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_decode_bf16")
 
@@ -546,17 +546,17 @@ def lecb_encode_fp32_pertensor(x, n, chunk, max_len, hist, blobs, outs, res4, ws
     return list(cbs)
 
 
-def lecb_decode_fp32(streams, stream_bytes, blobs, chunk, n, out, scratch, res4, ws, stream=None) -> None:
+def lecb_decode_fp32(streams, stream_bytes, blobs, chunk, n, out, res4, ws, stream=None) -> None:
     sb = (_u64 * 4)(*[int(b) for b in stream_bytes])
-    _check(load().lecb_decode_fp32(_ptrs4(streams), sb, _ptrs4(blobs), chunk, n, _ptr(out), _ptr(scratch),
+    _check(load().lecb_decode_fp32(_ptrs4(streams), sb, _ptrs4(blobs), chunk, n, _ptr(out),
                                    _ptr(res4), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_decode_fp32")
 
 
-def lecb_decode_fp32_from_results(streams, enc_res4, blobs, chunk, n, out, scratch, res4, ws,
+def lecb_decode_fp32_from_results(streams, enc_res4, blobs, chunk, n, out, res4, ws,
                                   stream=None) -> None:
     _check(load().lecb_decode_fp32_from_results(_ptrs4(streams), _ptr(enc_res4), _ptrs4(blobs), chunk, n,
-                                                _ptr(out), _ptr(scratch), _ptr(res4), _ptr(ws),
+                                                _ptr(out), _ptr(res4), _ptr(ws),
                                                 ws.numel() * ws.element_size(), _stream(stream)),
            "lecb_decode_fp32_from_results")
 
@@ -689,10 +689,9 @@ def decode_bf16(container, device):
     dl[:sl] = torch.from_numpy(buf[off_lo:off_lo + sl]).to(device)
     ch = DeviceCodebook.upload(lecb_codebook_from_lengths(h["len_hi"]), device)
     cl = DeviceCodebook.upload(lecb_codebook_from_lengths(h["len_lo"]), device)
-    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=device)
     res = new_results(2, device)
     ws = new_workspace(n, chunk, device)
-    lecb_decode_bf16(dh, sh, dl, sl, ch.blob, cl.blob, chunk, n, out, scratch, res, ws)
+    lecb_decode_bf16(dh, sh, dl, sl, ch.blob, cl.blob, chunk, n, out, res, ws)
     r = results_to_numpy(res)
     for k in range(2):
         if int(r[k]["status"]) != LECB_OK:

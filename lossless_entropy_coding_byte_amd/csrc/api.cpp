@@ -39,11 +39,11 @@ uint64_t num_chunks_checked(uint64_t n, uint32_t chunk) {
 
 uint64_t header_of(uint64_t n, uint32_t chunk) {
     const uint64_t nc = num_chunks_checked(n, chunk);
-    return nc ? table_bytes(nc) + gap_bytes(nc, chunk) : 0;
+    return nc ? table_bytes(nc) + ulen_bytes(nc, chunk) : 0;
 }
 
 uint64_t ws_bytes_of(uint64_t n, uint32_t chunk) {
-    return 2 * ws_stream_bytes(num_chunks_checked(n, chunk)) + ws_count_bytes(n);
+    return ws_total_bytes(n, num_chunks_checked(n, chunk));
 }
 
 int build_args(const lecb_codebook* cb, CodebookArgs* a) {
@@ -115,10 +115,12 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
     return launch_encode(L, stream);
 }
 
-int decode_common(int ns, const uint8_t* const* d_stream, const uint64_t* stream_bytes,
+// Decode ns streams of the same n and chunk in one launch: into their own
+// byte outputs (DEC_OUT_PLANES), or restored into the elements `merged`.
+int decode_common(int ns, int kind, const uint8_t* const* d_stream, const uint64_t* stream_bytes,
                   const void* const* d_blob, uint32_t chunk, uint64_t n, uint8_t* const* d_out,
-                  lecb_result* d_res, void* d_ws, uint64_t ws_bytes, void* stream,
-                  const lecb_result* d_sizes = nullptr) {
+                  uint8_t* merged, const uint8_t* w0, lecb_result* d_res, void* d_ws, uint64_t ws_bytes,
+                  void* stream, const lecb_result* d_sizes = nullptr) {
     if (!valid_chunk(chunk) || !d_res) return LECB_ERR_INVALID_ARG;
     for (int k = 0; k < ns; ++k)
         if (!d_blob[k] || !aligned16(d_blob[k])) return LECB_ERR_INVALID_ARG;
@@ -133,10 +135,12 @@ int decode_common(int ns, const uint8_t* const* d_stream, const uint64_t* stream
         return LECB_OK;
     }
     if (!d_ws || !aligned16(d_ws)) return LECB_ERR_INVALID_ARG;
+    if (kind != DEC_OUT_PLANES && (!merged || !aligned16(merged))) return LECB_ERR_INVALID_ARG;
+    if (kind == DEC_OUT_U16_XOR && (!w0 || !aligned16(w0))) return LECB_ERR_INVALID_ARG;
     const uint64_t hb = header_of(n, chunk);
     for (int k = 0; k < ns; ++k) {
-        if (!d_stream[k] || !d_out[k] || !aligned16(d_stream[k]) || !aligned16(d_out[k]))
-            return LECB_ERR_INVALID_ARG;
+        if (!d_stream[k] || !aligned16(d_stream[k])) return LECB_ERR_INVALID_ARG;
+        if (kind == DEC_OUT_PLANES && (!d_out[k] || !aligned16(d_out[k]))) return LECB_ERR_INVALID_ARG;
         if (!d_sizes && (stream_bytes[k] < hb + 4 || (stream_bytes[k] - hb) % 4)) return LECB_ERR_CORRUPT;
     }
     if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
@@ -144,14 +148,17 @@ int decode_common(int ns, const uint8_t* const* d_stream, const uint64_t* stream
     if (d_sizes && !aligned16(d_sizes)) return LECB_ERR_INVALID_ARG;
     DecodeLaunch L{};
     L.nstreams = ns;
+    L.out_kind = kind;
     L.dev_sizes = d_sizes;
+    L.merged = merged;
+    L.w0 = w0;
     for (int k = 0; k < ns; ++k) {
         L.stream_base[k] = d_stream[k];
         L.stream_bytes[k] = d_sizes ? 0 : stream_bytes[k];
         L.cb[k] = reinterpret_cast<const DeviceCodebook*>(d_blob[k]);
-        L.out[k] = d_out[k];
+        L.out[k] = kind == DEC_OUT_PLANES ? d_out[k] : nullptr;
         L.res[k] = d_res + k;
-        L.ws[k] = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + k * ws_stream_bytes(nc));
+        L.ws[k] = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + ws_header_offset(k, n, nc));
     }
     L.chunk = chunk;
     L.n = n;
@@ -224,7 +231,10 @@ uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len) {
     if (!valid_chunk(chunk) || max_len < 1 || max_len > 16) return 0;
     const uint64_t nc = num_chunks_checked(n, chunk);
     if (!nc) return 0;
-    return align16(header_of(n, chunk) + 4 * ((n * max_len + 31) / 32 + nc));
+    // chunk c of m_c symbols takes at most ceil(m_c * max_len / 32) words
+    const uint64_t last = n - (nc - 1) * chunk;
+    const uint64_t words = (nc - 1) * (((uint64_t)chunk * max_len + 31) / 32) + (last * max_len + 31) / 32;
+    return align16(header_of(n, chunk) + 4 * words);
 }
 
 uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk) {
@@ -306,7 +316,8 @@ int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_bl
     const uint64_t sb[1] = {stream_bytes};
     const void* bl[1] = {d_blob};
     uint8_t* out[1] = {d_out};
-    return decode_common(1, st, sb, bl, chunk, n, out, d_res, d_ws, ws_bytes, stream);
+    return decode_common(1, DEC_OUT_PLANES, st, sb, bl, chunk, n, out, nullptr, nullptr, d_res, d_ws, ws_bytes,
+                         stream);
 }
 
 int lecb_decode_from_result(const uint8_t* d_stream, const lecb_result* d_enc_res,
@@ -317,64 +328,50 @@ int lecb_decode_from_result(const uint8_t* d_stream, const lecb_result* d_enc_re
     const uint64_t sb[1] = {0};
     const void* bl[1] = {d_blob};
     uint8_t* out[1] = {d_out};
-    return decode_common(1, st, sb, bl, chunk, n, out, d_res, d_ws, ws_bytes, stream, d_enc_res);
+    return decode_common(1, DEC_OUT_PLANES, st, sb, bl, chunk, n, out, nullptr, nullptr, d_res, d_ws, ws_bytes,
+                         stream, d_enc_res);
 }
 
 int lecb_decode_bf16_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
                                   const lecb_result* d_enc_res2, const void* d_blob_hi,
                                   const void* d_blob_lo, uint32_t chunk, uint64_t n,
-                                  uint16_t* d_out, uint8_t* d_scratch, lecb_result* d_res2,
+                                  uint16_t* d_out, lecb_result* d_res2,
                                   void* d_ws, uint64_t ws_bytes, void* stream) {
     if (!d_res2 || !d_enc_res2) return LECB_ERR_INVALID_ARG;
-    if (n && (!d_scratch || !aligned16(d_scratch) || !d_out || !aligned16(d_out)))
-        return LECB_ERR_INVALID_ARG;
-    uint8_t* hi = d_scratch;
-    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
     const uint8_t* st[2] = {d_hi, d_lo};
     const uint64_t sb[2] = {0, 0};
     const void* bl[2] = {d_blob_hi, d_blob_lo};
-    uint8_t* out[2] = {hi, lo};
-    int rc = decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream, d_enc_res2);
-    if (!rc) rc = lecb_merge_bf16(hi, lo, n, d_out, stream);
-    return rc;
+    return decode_common(2, DEC_OUT_U16, st, sb, bl, chunk, n, nullptr, reinterpret_cast<uint8_t*>(d_out), nullptr,
+                         d_res2, d_ws, ws_bytes, stream, d_enc_res2);
 }
 
 int lecb_decode_bf16_delta_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
                                         const lecb_result* d_enc_res2, const void* d_blob_hi,
                                         const void* d_blob_lo, uint32_t chunk, uint64_t n,
-                                        const uint16_t* d_w0, uint16_t* d_w1, uint8_t* d_scratch,
+                                        const uint16_t* d_w0, uint16_t* d_w1,
                                         lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
                                         void* stream) {
     if (!d_res2 || !d_enc_res2) return LECB_ERR_INVALID_ARG;
-    if (n && (!d_scratch || !aligned16(d_scratch) || !d_w1 || !aligned16(d_w1) || !d_w0 ||
-              !aligned16(d_w0)))
-        return LECB_ERR_INVALID_ARG;
-    uint8_t* hi = d_scratch;
-    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
+    if (n && d_w0 == d_w1) return LECB_ERR_INVALID_ARG;
     const uint8_t* st[2] = {d_hi, d_lo};
     const uint64_t sb[2] = {0, 0};
     const void* bl[2] = {d_blob_hi, d_blob_lo};
-    uint8_t* out[2] = {hi, lo};
-    int rc = decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream, d_enc_res2);
-    if (!rc && n) rc = launch_merge(hi, lo, d_w0, n, d_w1, stream);
-    return rc;
+    return decode_common(2, DEC_OUT_U16_XOR, st, sb, bl, chunk, n, nullptr, reinterpret_cast<uint8_t*>(d_w1),
+                         reinterpret_cast<const uint8_t*>(d_w0), d_res2, d_ws, ws_bytes, stream, d_enc_res2);
 }
 
 int lecb_decode_bf16_delta(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
                            uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
                            uint32_t chunk, uint64_t n, const uint16_t* d_w0, uint16_t* d_w1,
-                           uint8_t* d_scratch, lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
+                           lecb_result* d_res2, void* d_ws, uint64_t ws_bytes,
                            void* stream) {
     if (!d_res2) return LECB_ERR_INVALID_ARG;
-    if (n && (!d_scratch || !aligned16(d_scratch) || !d_w1 || !aligned16(d_w1) || !d_w0 ||
-              !aligned16(d_w0)))
-        return LECB_ERR_INVALID_ARG;
-    uint8_t* hi = d_scratch;
-    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
-    int rc = lecb_decode_bf16_planes(d_hi, hi_bytes, d_lo, lo_bytes, d_blob_hi, d_blob_lo, chunk, n,
-                                     hi, lo, d_res2, d_ws, ws_bytes, stream);
-    if (!rc && n) rc = launch_merge(hi, lo, d_w0, n, d_w1, stream);
-    return rc;
+    if (n && d_w0 == d_w1) return LECB_ERR_INVALID_ARG;
+    const uint8_t* st[2] = {d_hi, d_lo};
+    const uint64_t sb[2] = {hi_bytes, lo_bytes};
+    const void* bl[2] = {d_blob_hi, d_blob_lo};
+    return decode_common(2, DEC_OUT_U16_XOR, st, sb, bl, chunk, n, nullptr, reinterpret_cast<uint8_t*>(d_w1),
+                         reinterpret_cast<const uint8_t*>(d_w0), d_res2, d_ws, ws_bytes, stream);
 }
 
 int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
@@ -385,7 +382,8 @@ int lecb_decode_bf16_planes(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_
     const uint64_t sb[2] = {hi_bytes, lo_bytes};
     const void* bl[2] = {d_blob_hi, d_blob_lo};
     uint8_t* out[2] = {d_out_hi, d_out_lo};
-    return decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream);
+    return decode_common(2, DEC_OUT_PLANES, st, sb, bl, chunk, n, out, nullptr, nullptr, d_res2, d_ws, ws_bytes,
+                         stream);
 }
 
 int lecb_decode_bf16_planes_from_results(const uint8_t* d_hi, const uint8_t* d_lo,
@@ -398,7 +396,8 @@ int lecb_decode_bf16_planes_from_results(const uint8_t* d_hi, const uint8_t* d_l
     const uint64_t sb[2] = {0, 0};
     const void* bl[2] = {d_blob_hi, d_blob_lo};
     uint8_t* out[2] = {d_out_hi, d_out_lo};
-    return decode_common(2, st, sb, bl, chunk, n, out, d_res2, d_ws, ws_bytes, stream, d_enc_res2);
+    return decode_common(2, DEC_OUT_PLANES, st, sb, bl, chunk, n, out, nullptr, nullptr, d_res2, d_ws, ws_bytes,
+                         stream, d_enc_res2);
 }
 
 int lecb_encode_bf16_pertensor(const uint16_t* d_in, uint64_t n, uint32_t chunk,
@@ -464,17 +463,14 @@ int lecb_encode_adaptive(const uint8_t* d_in, uint64_t n, uint32_t chunk, uint32
 
 int lecb_decode_bf16(const uint8_t* d_hi, uint64_t hi_bytes, const uint8_t* d_lo,
                      uint64_t lo_bytes, const void* d_blob_hi, const void* d_blob_lo,
-                     uint32_t chunk, uint64_t n, uint16_t* d_out, uint8_t* d_scratch,
+                     uint32_t chunk, uint64_t n, uint16_t* d_out,
                      lecb_result* d_res2, void* d_ws, uint64_t ws_bytes, void* stream) {
     if (!d_res2) return LECB_ERR_INVALID_ARG;
-    if (n && (!d_scratch || !aligned16(d_scratch) || !d_out || !aligned16(d_out)))
-        return LECB_ERR_INVALID_ARG;
-    uint8_t* hi = d_scratch;
-    uint8_t* lo = d_scratch ? d_scratch + ((n + 15) & ~uint64_t(15)) : nullptr;
-    int rc = lecb_decode_bf16_planes(d_hi, hi_bytes, d_lo, lo_bytes, d_blob_hi, d_blob_lo, chunk,
-                                     n, hi, lo, d_res2, d_ws, ws_bytes, stream);
-    if (!rc) rc = lecb_merge_bf16(hi, lo, n, d_out, stream);
-    return rc;
+    const uint8_t* st[2] = {d_hi, d_lo};
+    const uint64_t sb[2] = {hi_bytes, lo_bytes};
+    const void* bl[2] = {d_blob_hi, d_blob_lo};
+    return decode_common(2, DEC_OUT_U16, st, sb, bl, chunk, n, nullptr, reinterpret_cast<uint8_t*>(d_out), nullptr,
+                         d_res2, d_ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- codebooks built on the device
@@ -641,42 +637,28 @@ int lecb_encode_fp32_pertensor_nosync(const uint32_t* d_in, uint64_t n, uint32_t
 
 static int decode_fp32_common(const uint8_t* const d_stream[4], const uint64_t* stream_bytes,
                               const lecb_result* d_enc_res4, const void* const d_blob[4], uint32_t chunk,
-                              uint64_t n, uint32_t* d_out, uint8_t* d_scratch, lecb_result* d_res4,
+                              uint64_t n, uint32_t* d_out, lecb_result* d_res4,
                               void* d_ws, uint64_t ws_bytes, void* stream) {
     if (!d_stream || !d_blob || !d_res4 || (!stream_bytes && !d_enc_res4)) return LECB_ERR_INVALID_ARG;
-    if (n && (!d_scratch || !aligned16(d_scratch) || !d_out || !aligned16(d_out))) return LECB_ERR_INVALID_ARG;
-    const uint64_t plane = (n + 15) & ~uint64_t(15);
-    uint8_t* p[4];
-    for (int k = 0; k < 4; ++k) p[k] = d_scratch ? d_scratch + k * plane : nullptr;
-    const uint64_t none[2] = {0, 0};
-    int rc = LECB_OK;
-    for (int h = 0; h < 2 && !rc; ++h) {
-        const uint8_t* st[2] = {d_stream[2 * h], d_stream[2 * h + 1]};
-        const void* bl[2] = {d_blob[2 * h], d_blob[2 * h + 1]};
-        uint8_t* out[2] = {p[2 * h], p[2 * h + 1]};
-        rc = decode_common(2, st, stream_bytes ? stream_bytes + 2 * h : none, bl, chunk, n, out,
-                           d_res4 + 2 * h, d_ws, ws_bytes, stream,
-                           d_enc_res4 ? d_enc_res4 + 2 * h : nullptr);
-    }
-    if (!rc && n) rc = launch_merge4(p[0], p[1], p[2], p[3], n, d_out, stream);
-    return rc;
+    const uint64_t none[4] = {0, 0, 0, 0};
+    return decode_common(4, DEC_OUT_U32, d_stream, stream_bytes ? stream_bytes : none, d_blob, chunk, n, nullptr,
+                         reinterpret_cast<uint8_t*>(d_out), nullptr, d_res4, d_ws, ws_bytes, stream, d_enc_res4);
 }
 
 int lecb_decode_fp32(const uint8_t* const d_stream[4], const uint64_t stream_bytes[4],
                      const void* const d_blob[4], uint32_t chunk, uint64_t n, uint32_t* d_out,
-                     uint8_t* d_scratch, lecb_result* d_res4, void* d_ws, uint64_t ws_bytes, void* stream) {
+                     lecb_result* d_res4, void* d_ws, uint64_t ws_bytes, void* stream) {
     if (!stream_bytes) return LECB_ERR_INVALID_ARG;
-    return decode_fp32_common(d_stream, stream_bytes, nullptr, d_blob, chunk, n, d_out, d_scratch, d_res4,
-                              d_ws, ws_bytes, stream);
+    return decode_fp32_common(d_stream, stream_bytes, nullptr, d_blob, chunk, n, d_out, d_res4, d_ws, ws_bytes,
+                              stream);
 }
 
 int lecb_decode_fp32_from_results(const uint8_t* const d_stream[4], const lecb_result* d_enc_res4,
                                   const void* const d_blob[4], uint32_t chunk, uint64_t n, uint32_t* d_out,
-                                  uint8_t* d_scratch, lecb_result* d_res4, void* d_ws, uint64_t ws_bytes,
-                                  void* stream) {
+                                  lecb_result* d_res4, void* d_ws, uint64_t ws_bytes, void* stream) {
     if (!d_enc_res4) return LECB_ERR_INVALID_ARG;
-    return decode_fp32_common(d_stream, nullptr, d_enc_res4, d_blob, chunk, n, d_out, d_scratch, d_res4,
-                              d_ws, ws_bytes, stream);
+    return decode_fp32_common(d_stream, nullptr, d_enc_res4, d_blob, chunk, n, d_out, d_res4, d_ws, ws_bytes,
+                              stream);
 }
 
 }  // extern "C"

@@ -1,43 +1,51 @@
-// Huffman decode of stream format v1 back to bytes.
+// Huffman decode of stream format v2 back to bytes, and back to 16-bit or
+// 32-bit elements when the byte groups are decoded together.
 //
 // Reverse path of "Lossless Compression for LLM Tensor Incremental
-// Snapshots", Technical framework (read, Huffman-decode); the independent
-// parallel tasks of its Key design item 3 are the decode units: every chunk
-// is split into K = chunk/256 units whose exact starting code-word boundary
-// is its word-aligned start plus the stored 4-bit gap.
+// Snapshots", Technical framework (read, Huffman-decode, restore the byte
+// groups); the independent parallel tasks of its Key design item 3 are the
+// decode units: unit j of a chunk is its symbols [256j, 256j + 256), and the
+// stored code-bit counts of the chunk's units give every unit's first bit.
 //
-// One lane per unit, 256 units per workgroup (K divides 256, so a chunk's
-// units never straddle workgroups).  Per lane:
-//   1. count pass: code words that start in [start, end) of the unit; the
-//      loop stops exactly at `end`, which checks that `end` is a code-word
-//      boundary and that the stored gap names the first one.  The chunk's
-//      last unit counts only the code words that start before the chunk's
-//      last payload word;
-//   2. exclusive scan of the counts inside each chunk -> output offsets; the
-//      last unit now knows how many code words remain in the last word,
-//      decodes them and checks the zero padding behind them;
-//   3. decode pass: output is written in whole DEC_BLOCK-byte blocks, aligned
-//      within the chunk's output.  A lane owns the blocks that START inside
-//      its output range; it skips the code words in front of its first block
-//      (the previous lane's last block holds them) and decodes on past its
-//      own end, into the next unit's code words, to fill its last block.
-//      Blocks never cross a chunk (a chunk holds a multiple of 256 symbols),
-//      and with a 32-byte aligned output buffer every store fills whole
-//      32-byte sectors.
+// One lane per unit and byte plane.  P planes of the same element are coded
+// as P streams whose units cover the same symbols, so the P lanes of a unit
+// (neighbouring lanes of one wave) produce the P bytes of the same 256
+// elements in lockstep:
+//   * P = 1, OUT_PLANES: each stream's units in workgroups of their own, one
+//     byte per symbol written to that stream's output;
+//   * P = 2, OUT_U16 / OUT_U16_XOR: lane 2u decodes the high plane and lane
+//     2u + 1 the low plane of unit u; after every 16 symbols the pair swaps
+//     half of its bytes (one lane exchange) and each lane stores 8 restored
+//     16-bit words (16 bytes), XORed with the other snapshot for a delta;
+//   * P = 4, OUT_U32: lanes 4u..4u+3 decode planes 0..3 (bytes 3..0 of the
+//     32-bit elements) of unit u; after every 16 symbols the quad transposes
+//     its words and each lane stores 4 restored elements.
+//
+// Per lane:
+//   1. its unit's first bit = the sum of the bit counts of the chunk's
+//      earlier units (a segmented scan over the workgroup's lanes: a chunk's
+//      units never straddle workgroups);
+//   2. decode the unit's symbols (256, fewer only at the end of the tensor)
+//      from that bit; the unit must end exactly at first bit + its count, and
+//      the unit holding the chunk's last symbol checks the zero padding to
+//      the end of the chunk's last word.
 //
 // Bit reader: a window of two payload words and a bit offset into it; before
 // every pair of code words the window slides by one word when its first word
 // is used up (no branch).  Afterwards the offset is below 32, so the window
 // holds >= 33 bits, enough for two code words of at most 16 bits.  The words
-// come from a per-lane ring of 16 payload words in LDS; the ring is topped up on a fixed
-// schedule (every 4 refills) by one masked 32-byte global load whose data go
-// into the ring at the next top-up, so the decode loop never waits on global
-// memory.  Ring slot q of lane L sits at ring[q][L]: each lane has its own bank.
+// come from a per-lane ring of 16 payload words in LDS; the ring is topped up
+// on a fixed schedule (every 4 refills) by one 32-byte global load whose data
+// go into the ring at the next top-up, so the decode loop never waits on
+// global memory.  Ring slot q of lane L sits at ring[q][L]: each lane has its
+// own bank.
 //
 // A code word of at most LUT_BITS bits is one LDS lookup; longer ones use the
 // canonical per-length limits.  Every structural rule of the format is
 // checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "lecb_internal.hpp"
 
@@ -45,22 +53,21 @@ namespace lecb {
 
 namespace {
 
-constexpr int DEC_MAX_THREADS = 1024;  // lanes (decode units) per workgroup: 256, 512 or 1024
-constexpr uint32_t RING = 16;  // payload words per lane in LDS
-constexpr uint32_t DEC_BLOCK = 32;  // output block a lane owns (bytes)
+constexpr uint32_t RING = 16;   // payload words per lane in LDS
+constexpr uint32_t UNIT = LECB_UNIT_SYMBOLS;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 struct DecStream {
     const uint32_t* table;
-    const uint8_t* gaps;
+    const uint16_t* ulen;
     const uint32_t* payload;
     uint64_t payload_words;   // words present in the caller's buffer
     const DeviceCodebook* cb;
     uint64_t header_bytes;
     uint64_t table_pad_from, table_pad_to;   // stream bytes that must be zero
-    uint64_t gap_pad_from, gap_pad_to;
+    uint64_t ulen_pad_from, ulen_pad_to;
     const uint8_t* stream;
-    uint8_t* out;
+    uint8_t* out;             // OUT_PLANES: the decoded bytes of this stream
     lecb_result* res;
     WsHeader* ws;
 };
@@ -71,29 +78,34 @@ struct DecArgs {
     uint32_t log2k;
     uint64_t n;
     uint64_t nc;
-    uint32_t wg_per_stream;   // workgroups of one stream; stream = blockIdx.x / wg_per_stream
+    uint32_t wg_per_group;     // OUT_PLANES: workgroups of one stream; stream = blockIdx.x / wg_per_group
     uint32_t nstreams;
-    DecStream st[2];
+    uint8_t* merged;           // OUT_U16, OUT_U16_XOR, OUT_U32: the restored elements
+    const uint8_t* w0;         // OUT_U16_XOR: the other snapshot (element i ^ restored i is written)
+    DecStream st[4];
 };
 
-struct Tables {
-    uint16_t lut[LUT_SIZE];   // (sym << 8) | len
-    uint8_t mlut[LUT_SIZE];   // (count << 4) | bits of the whole code words in the next LUT_BITS
-    uint32_t off[17];         // base[l] - first[l]: index in `sorted` is off[l] + code
-    uint8_t sorted[256];
-};
-
-// The tables come first: their LDS offsets (and the ring's base) fit the
-// 16-bit offset field of the LDS instructions, so a table lookup needs no
-// base-address add.
+// One stream's tables in a workgroup with one stream per workgroup: the
+// decode table and the canonical tables of the longer code words.
 template <int NT>
-struct Shared {
-    Tables T;
-    alignas(16) uint32_t ring[RING][NT];  // row 0 doubles as the counts of the scan
-    uint64_t red[NT / 64];
+struct SharedOne {
+    uint16_t lut[1][LUT_SIZE];   // (sym << 8) | len
+    uint32_t off[17];            // base[l] - first[l]: index in `sorted` is off[l] + code
+    uint8_t sorted[256];
+    alignas(16) uint32_t ring[RING][NT];
 };
+// P streams in every workgroup: P decode tables (code words longer than
+// LUT_BITS read the canonical tables from the device codebook).  With P = 2
+// and 1024 lanes this is exactly 80 KiB, so two workgroups fill a CU's LDS.
+template <int NT, int P>
+struct SharedMany {
+    uint16_t lut[P][LUT_SIZE];
+    alignas(16) uint32_t ring[RING][NT];
+};
+template <int NT, int P>
+using Shared = std::conditional_t<P == 1, SharedOne<NT>, SharedMany<NT, P>>;
 
-// Left-aligned canonical limits of the lengths above LUT_BITS (uniform values).
+// Left-aligned canonical limits of the lengths above LUT_BITS.
 struct Limits {
     uint32_t l13, l14, l15, l16;
 };
@@ -182,28 +194,65 @@ struct Reader {
     }
 };
 
+// What a lane needs of its stream (selected per lane when a workgroup holds
+// several streams).
+struct Lane {
+    const uint32_t* table;
+    const uint16_t* ulen;
+    const uint32_t* payload;
+    uint64_t payload_words;
+    const DeviceCodebook* cb;
+    uint8_t* out;
+    const uint8_t* stream;
+    uint64_t table_pad_from, table_pad_to, ulen_pad_from, ulen_pad_to;
+};
+
+template <int P>
+__device__ inline Lane lane_stream(const DecArgs& a, uint32_t k, const uint64_t (&words)[4]) {
+    Lane l;
+#define LECB_PICK(field, expr)                                            \
+    if constexpr (P == 1) {                                               \
+        l.field = a.st[k].expr;                                           \
+    } else if constexpr (P == 2) {                                        \
+        l.field = k ? a.st[1].expr : a.st[0].expr;                        \
+    } else {                                                              \
+        l.field = k & 2 ? (k & 1 ? a.st[3].expr : a.st[2].expr)           \
+                        : (k & 1 ? a.st[1].expr : a.st[0].expr);          \
+    }
+    LECB_PICK(table, table)
+    LECB_PICK(ulen, ulen)
+    LECB_PICK(payload, payload)
+    LECB_PICK(cb, cb)
+    LECB_PICK(out, out)
+    LECB_PICK(stream, stream)
+    LECB_PICK(table_pad_from, table_pad_from)
+    LECB_PICK(table_pad_to, table_pad_to)
+    LECB_PICK(ulen_pad_from, ulen_pad_from)
+    LECB_PICK(ulen_pad_to, ulen_pad_to)
+#undef LECB_PICK
+    l.payload_words = P == 1 ? words[0] : (k & 2 ? (k & 1 ? words[3] : words[2]) : (k & 1 ? words[1] : words[0]));
+    return l;
+}
+
 // Next code word as (sym << 8) | len, len in 1..16, from the next 32 bits
 // `top`.  An invalid code word yields len 16 and sets `inval`.
-__device__ inline uint32_t lookup(const Tables& T, const Limits& L, uint32_t top, uint32_t& inval) {
-    uint32_t e = T.lut[top >> (32 - LUT_BITS)];
+template <int P, typename S>
+__device__ inline uint32_t lookup(const S& sh, const uint16_t* lut, const DeviceCodebook* cb, const Limits& L,
+                                  uint32_t top, uint32_t& inval) {
+    uint32_t e = lut[top >> (32 - LUT_BITS)];
     if (e == 0) {
         const uint32_t v = top >> 16;
         const uint32_t len = 13u + (v >= L.l13) + (v >= L.l14) + (v >= L.l15);
         if (v >= L.l16) {
             inval = 1;
             e = 16;
+        } else if constexpr (P == 1) {
+            e = ((uint32_t)sh.sorted[(sh.off[len] + (v >> (16 - len))) & 255u] << 8) | len;
         } else {
-            e = ((uint32_t)T.sorted[(T.off[len] + (v >> (16 - len))) & 255u] << 8) | len;
+            const uint32_t idx = (cb->base[len] - cb->first[len] + (v >> (16 - len))) & 255u;
+            e = ((uint32_t)cb->sorted[idx] << 8) | len;
         }
     }
-    return e;
-}
-
-// Decode one code word and advance; returns (sym << 8) | len.
-template <int NT>
-__device__ inline uint32_t step(const Tables& T, const Limits& L, Reader<NT>& r, uint32_t& inval) {
-    const uint32_t e = lookup(T, L, r.peek(), inval);
-    r.off += e & 0xFFu;
     return e;
 }
 
@@ -215,281 +264,271 @@ __device__ inline uint32_t syms4(const uint32_t (&e)[4]) {
     return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
-__device__ inline uint32_t gap_of(const uint8_t* gaps, uint64_t i) {
-    const uint8_t b = gaps[i >> 1];
-    return (i & 1) ? (b >> 4) : (b & 0xFu);
+// 16 restored 16-bit words from the high-plane bytes hi[0..3] (lane 2u) and
+// the low-plane bytes lo[0..3] (lane 2u + 1) of 16 symbols: the pair swaps
+// half of its words, then lane 2u builds words 0..7 and lane 2u + 1 words
+// 8..15 (little-endian: low byte first).
+__device__ inline v4u restore16(const uint32_t (&w)[4], uint32_t odd) {
+    const uint32_t s0 = __shfl_xor(odd ? w[0] : w[2], 1, 64);
+    const uint32_t s1 = __shfl_xor(odd ? w[1] : w[3], 1, 64);
+    const uint32_t h0 = odd ? s0 : w[0], h1 = odd ? s1 : w[1];
+    const uint32_t l0 = odd ? w[2] : s0, l1 = odd ? w[3] : s1;
+    v4u o;
+    o.x = __builtin_amdgcn_perm(h0, l0, 0x05010400u);
+    o.y = __builtin_amdgcn_perm(h0, l0, 0x07030602u);
+    o.z = __builtin_amdgcn_perm(h1, l1, 0x05010400u);
+    o.w = __builtin_amdgcn_perm(h1, l1, 0x07030602u);
+    return o;
+}
+
+// 16 restored 32-bit elements from four lanes q = 0..3 holding the bytes of
+// planes 0..3 (element bytes 3..0) of 16 symbols: lane q gathers word q of
+// every plane (three exchanges) and builds elements 4q..4q+3.
+__device__ inline v4u restore32(const uint32_t (&w)[4], uint32_t q) {
+    uint32_t x[4];  // x[p] = word q of plane p
+#pragma unroll
+    for (uint32_t r = 0; r < 4; ++r) {
+        // round r: lane q reads from lane (q + r) & 3, which sends its word q
+        const uint32_t src = (q + r) & 3u;
+        const uint32_t want = (q - r) & 3u;  // the word this lane sends
+        const uint32_t mine = want == 0 ? w[0] : want == 1 ? w[1] : want == 2 ? w[2] : w[3];
+        const uint32_t got = r ? __shfl(mine, (int)((threadIdx.x & ~3u) | src), 64) : mine;
+        if (src == 0) x[0] = got;
+        if (src == 1) x[1] = got;
+        if (src == 2) x[2] = got;
+        if (src == 3) x[3] = got;
+    }
+    // element k: bytes [x3[k], x2[k], x1[k], x0[k]] (little-endian)
+    const uint32_t a01 = __builtin_amdgcn_perm(x[0], x[1], 0x05010400u);  // x1_0 x0_0 x1_1 x0_1
+    const uint32_t b01 = __builtin_amdgcn_perm(x[0], x[1], 0x07030602u);  // x1_2 x0_2 x1_3 x0_3
+    const uint32_t a23 = __builtin_amdgcn_perm(x[2], x[3], 0x05010400u);  // x3_0 x2_0 x3_1 x2_1
+    const uint32_t b23 = __builtin_amdgcn_perm(x[2], x[3], 0x07030602u);
+    v4u o;
+    o.x = __builtin_amdgcn_perm(a01, a23, 0x05040100u);  // x3_0 x2_0 x1_0 x0_0
+    o.y = __builtin_amdgcn_perm(a01, a23, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(b01, b23, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(b01, b23, 0x07060302u);
+    return o;
+}
+
+template <int NT, int P>
+__device__ inline const uint16_t* lut_of(const Shared<NT, P>& S, uint32_t k) {
+    return &S.lut[P == 1 ? 0 : k][0];
 }
 
 // 64 VGPRs at most: two 1024-lane workgroups (8 waves per SIMD) fit a CU.
-template <int NT>
+template <int NT, int P, int OUT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_kernel(DecArgs a) {
-    constexpr int DEC_THREADS = NT;
-    __shared__ __attribute__((aligned(16))) Shared<NT> S;
-    Tables& T = S.T;
-
+    static_assert(P == 1 || OUT != DEC_OUT_PLANES, "plane outputs decode one stream per workgroup");
+    __shared__ __attribute__((aligned(16))) Shared<NT, P> S;
     const int tid = threadIdx.x;
-    const uint32_t sidx = blockIdx.x / a.wg_per_stream;
-    const uint32_t bid = blockIdx.x - sidx * a.wg_per_stream;
-    const DecStream& d0 = a.st[sidx];
-    DecStream d = d0;
-    bool size_bad = false;
-    if (a.sizes) {
-        // the stream's size comes from the encoder's result on the device
-        const uint64_t bytes = a.sizes[sidx].bytes;
-        size_bad = a.sizes[sidx].status != 0 || bytes < d.header_bytes + 4 ||
-                   ((bytes - d.header_bytes) & 3) != 0;
-        d.payload_words = size_bad ? 0 : (bytes - d.header_bytes) / 4;
-    }
-    {
-        const v4u* src = reinterpret_cast<const v4u*>(d.cb->lut);
-        v4u* dst = reinterpret_cast<v4u*>(T.lut);
-        constexpr int NV = LUT_SIZE * 2 / 16;
-        for (int i = tid; i < NV; i += DEC_THREADS) dst[i] = src[i];
-        const v4u* msrc = reinterpret_cast<const v4u*>(d.cb->mlut);
-        v4u* mdst = reinterpret_cast<v4u*>(T.mlut);
-        for (int i = tid; i < LUT_SIZE / 16; i += DEC_THREADS) mdst[i] = msrc[i];
-    }
-    if (tid < 17) T.off[tid] = d.cb->base[tid] - d.cb->first[tid];
-    if (tid < 256) T.sorted[tid] = d.cb->sorted[tid];
-    Limits L;
-    L.l13 = d.cb->limit[13];
-    L.l14 = d.cb->limit[14];
-    L.l15 = d.cb->limit[15];
-    L.l16 = d.cb->limit[16];
 
-    // ---- unit geometry
+    // ---- which stream, unit and chunk this lane decodes
+    const uint32_t sidx = P == 1 ? blockIdx.x / a.wg_per_group : 0u;     // P == 1: stream of the workgroup
+    const uint32_t bid = P == 1 ? blockIdx.x - sidx * a.wg_per_group : blockIdx.x;
+    const uint32_t k = P == 1 ? sidx : (uint32_t)tid & (P - 1);           // this lane's stream
+    const uint64_t u = P == 1 ? (uint64_t)bid * NT + tid : ((uint64_t)bid * NT + tid) / P;
+    // stream sizes: given, or read from the encoder's results
+    uint64_t words[4] = {0, 0, 0, 0};
+    bool size_bad[4] = {false, false, false, false};
+#pragma unroll
+    for (int q = 0; q < (P == 1 ? 1 : P); ++q) {
+        const uint32_t s = P == 1 ? sidx : (uint32_t)q;
+        const DecStream& d = a.st[s];
+        uint64_t w = d.payload_words;
+        if (a.sizes) {
+            const uint64_t bytes = a.sizes[s].bytes;
+            size_bad[q] = a.sizes[s].status != 0 || bytes < d.header_bytes + 4 || ((bytes - d.header_bytes) & 3) != 0;
+            w = size_bad[q] ? 0 : (bytes - d.header_bytes) / 4;
+        }
+        words[q] = w;
+    }
+    const Lane ln = lane_stream<P>(a, k, words);
+    const bool my_size_bad = P == 1 ? size_bad[0] : (k & 2 ? (k & 1 ? size_bad[3] : size_bad[2]) : (k & 1 ? size_bad[1] : size_bad[0]));
+
+    // ---- tables
+    {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const v4u* src = reinterpret_cast<const v4u*>(a.st[P == 1 ? sidx : (uint32_t)q].cb->lut);
+            v4u* dst = reinterpret_cast<v4u*>(&S.lut[q][0]);
+            constexpr int NV = LUT_SIZE * 2 / 16;
+            for (int i = tid; i < NV; i += NT) dst[i] = src[i];
+        }
+        if constexpr (P == 1) {
+            const DeviceCodebook* cb = a.st[sidx].cb;
+            if (tid < 17) S.off[tid] = cb->base[tid] - cb->first[tid];
+            if (tid < 256) S.sorted[tid] = cb->sorted[tid];
+        }
+    }
+    Limits L;
+    L.l13 = ln.cb->limit[13];
+    L.l14 = ln.cb->limit[14];
+    L.l15 = ln.cb->limit[15];
+    L.l16 = ln.cb->limit[16];
+
+    // ---- unit geometry and the stream's structure around it
     const uint32_t K = 1u << a.log2k;
-    const uint64_t u = (uint64_t)bid * DEC_THREADS + tid;
     const uint64_t c = u >> a.log2k;
     const uint32_t j = (uint32_t)(u & (K - 1));
-    const bool active = c < a.nc && !size_bad;
-    const bool last = j == K - 1;
-    bool bad = size_bad;
+    const bool active = c < a.nc && !my_size_bad;
+    bool bad = my_size_bad && c < a.nc;
     uint64_t sw = 0, wc = 0;
-    uint32_t start_bit = 0, end_bit = 0, sj1 = 0, m_c = 0;
+    uint32_t m_c = 0, cnt = 0, my_bits = 0;
     if (active) {
-        sw = c ? d.table[c - 1] : 0;
-        const uint64_t ew = d.table[c];
-        if (ew <= sw || ew > d.payload_words || ew - sw > a.chunk / 2) bad = true;
+        sw = c ? ln.table[c - 1] : 0;
+        const uint64_t ew = ln.table[c];
+        if (ew <= sw || ew > ln.payload_words || ew - sw > a.chunk / 2) bad = true;
         wc = bad ? 0 : ew - sw;
         m_c = (uint32_t)min<uint64_t>(a.chunk, a.n - c * a.chunk);
-        const uint32_t sj = (uint32_t)(((uint64_t)j * wc) >> a.log2k) << 5;
-        const uint32_t gj = gap_of(d.gaps, u);
-        if (j == 0 && gj != 0) bad = true;
-        start_bit = sj + gj;
-        if (!last) {
-            sj1 = (uint32_t)(((uint64_t)(j + 1) * wc) >> a.log2k) << 5;
-            end_bit = sj1 + gap_of(d.gaps, u + 1);
-            if (start_bit > end_bit) bad = true;
-        } else {
-            end_bit = wc ? (uint32_t)((wc - 1) << 5) : 0u;  // start of the last word
-        }
+        cnt = m_c > j * UNIT ? min(m_c - j * UNIT, UNIT) : 0u;
+        my_bits = ln.ulen[u];
+        if (my_bits < cnt || my_bits > 16 * cnt) bad = true;
+    }
+    // first bit of every unit: exclusive sum of the bit counts of the chunk's
+    // earlier units of the same stream (segments of K*P lanes; the ring's first
+    // row holds the sums until the decode starts)
+    uint32_t* const scan = &S.ring[0][0];
+    scan[tid] = my_bits;
+    __syncthreads();
+    const uint32_t seg = K * P;  // lanes of one chunk (all streams); divides NT
+    const uint32_t in_seg = (uint32_t)tid & (seg - 1);
+    for (uint32_t o = P; o < seg; o <<= 1) {
+        const uint32_t v = in_seg >= o ? scan[tid - o] : 0u;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const uint32_t first_bit = scan[tid] - my_bits;
+    const uint32_t chunk_bits = scan[(tid - in_seg) + (K - 1) * P + (tid & (P - 1))];
+    __syncthreads();  // the ring is written from here on
+    if (active && !bad) {
+        // the chunk's bits fill its words to within one word
+        if (chunk_bits == 0 || (uint64_t)chunk_bits > 32 * wc || (uint64_t)chunk_bits + 32 <= 32 * wc) bad = true;
     }
 
+    // padding bytes of the header are part of the format (checked by the
+    // first workgroup of each stream, spread over that stream's lanes)
+    if (bid == 0) {
+        const uint32_t lane_in = (uint32_t)tid / P;
+        for (uint64_t b = ln.table_pad_from + lane_in; b < ln.table_pad_to; b += NT / P) bad |= ln.stream[b] != 0;
+        for (uint64_t b = ln.ulen_pad_from + lane_in; b < ln.ulen_pad_to; b += NT / P) bad |= ln.stream[b] != 0;
+    }
+
+    // ---- decode
     Reader<NT> r;
     r.ring = &S.ring[0][tid];
-    r.p = d.payload;
+    r.p = ln.payload;
     r.sw = sw;
-    r.gmax = d.payload_words ? (d.payload_words - 1) >> 2 : 0;
+    r.gmax = ln.payload_words ? (ln.payload_words - 1) >> 2 : 0;
     r.sh = (uint32_t)sw & (RING - 1);
+    const uint16_t* lut = lut_of<NT, P>(S, k);
+    const uint64_t e0 = c * a.chunk + (uint64_t)j * UNIT;  // first element of the unit
     const bool run = active && !bad;
-
-    __syncthreads();  // tables complete
-
-    // ---- 1. count
-    uint32_t cnt = 0;
-    if (run) {
-        r.start(start_bit);
-        uint32_t e = 0, inval = 0;
-        // pos() < end_bit  <=>  off < thr = endq - 32 * rq
-        const int32_t endq = (int32_t)(end_bit + 32 * (r.sh + 2));
-        int32_t thr = endq - (int32_t)(r.rq << 5);
-        // (a) far from the end: all code words that lie wholly inside the next
-        // LUT_BITS bits at once, two such steps per refill; a step whose first
-        // code word is longer decodes that one alone.  It stops while at least
-        // 16 bits are left, so the last code word before `end` is decoded by
-        // (b) and its length is known for the gap check.
-        for (uint32_t it = 0; (int32_t)r.off + 2 * 16 + 16 <= thr; ++it) {
-            if ((it & 3) == 0) r.tick();
-            r.refill();
-            thr = endq - (int32_t)(r.rq << 5);
+    const uint32_t ngrp = run ? cnt >> 4 : 0u;
+    // lanes of one unit keep the same group count so that the exchanges of
+    // the fused outputs pair up (a unit's P lanes see the same cnt)
+    uint32_t inval = 0;
+    if (run && cnt) r.start(first_bit);
+    for (uint32_t g = 0; g < ngrp; ++g) {
+        uint32_t w[4];
+        uint32_t ev[4];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const uint32_t top = r.peek();
-                const uint32_t m = T.mlut[top >> (32 - LUT_BITS)];
-                if (m >= 16) {
-                    r.off += m & 15u;
-                    cnt += m >> 4;
-                } else {
-                    e = lookup(T, L, top, inval);
-                    r.off += e & 0xFFu;
-                    ++cnt;
-                }
+        for (int q = 0; q < 8; ++q) {
+            if ((q & 3) == 0) r.tick();
+            r.refill();
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 2 * q + h;
+                const uint32_t e = lookup<P>(S, lut, ln.cb, L, r.peek(), inval);
+                r.off += e & 0xFFu;
+                ev[i & 3] = e;
+                if ((i & 3) == 3) w[i >> 2] = syms4(ev);
             }
         }
-        // (b) the rest, one code word at a time, stopping exactly at `end`
-        while ((int32_t)r.off < thr) {
-            r.tick();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                r.refill();
-                thr = endq - (int32_t)(r.rq << 5);
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    if ((int32_t)r.off < thr) {
-                        e = step(T, L, r, inval);
-                        ++cnt;
-                    }
-                }
+        if constexpr (OUT == DEC_OUT_PLANES) {
+            v4u v;
+            v.x = w[0];
+            v.y = w[1];
+            v.z = w[2];
+            v.w = w[3];
+            *reinterpret_cast<v4u*>(ln.out + e0 + 16 * g) = v;
+        } else if constexpr (OUT == DEC_OUT_U16 || OUT == DEC_OUT_U16_XOR) {
+            v4u v = restore16(w, k);
+            const uint64_t at = 2 * (e0 + 16 * g) + 16 * k;
+            if constexpr (OUT == DEC_OUT_U16_XOR) v ^= *reinterpret_cast<const v4u*>(a.w0 + at);
+            *reinterpret_cast<v4u*>(a.merged + at) = v;
+        } else {
+            const v4u v = restore32(w, k);
+            *reinterpret_cast<v4u*>(a.merged + 4 * (e0 + 16 * g) + 16 * k) = v;
+        }
+    }
+    if (run && cnt) {
+        // the tensor's last unit: the symbols after the last full group
+        const uint32_t rem = cnt & 15u;
+        for (uint32_t i = 0; i < rem; ++i) {
+            if ((i & 3) == 0) r.tick();
+            r.refill();
+            const uint32_t e = lookup<P>(S, lut, ln.cb, L, r.peek(), inval);
+            r.off += e & 0xFFu;
+            const uint64_t el = e0 + 16 * ngrp + i;
+            const uint8_t sym = (uint8_t)(e >> 8);
+            if constexpr (OUT == DEC_OUT_PLANES) {
+                ln.out[el] = sym;
+            } else {
+                // byte P-1-k of element el (plane k holds byte P-1-k)
+                const uint64_t at = (uint64_t)P * el + (P - 1 - k);
+                a.merged[at] = OUT == DEC_OUT_U16_XOR ? (uint8_t)(sym ^ a.w0[at]) : sym;
             }
         }
         r.refill();
-        bad |= inval != 0;
-        if (!last) {
-            const uint32_t pos = r.pos();
-            if (pos != end_bit) bad = true;
-            // the stored gap must name the FIRST code-word boundary at or after sj1
-            if (cnt && end_bit != sj1 && pos - (e & 0xFFu) >= sj1) bad = true;
-        }
-    }
-
-    // ---- 2. exclusive scan of counts within each chunk (segments of K lanes)
-    // ring row 0 holds the counts now: a lane's column is its own, and no lane
-    // touches the ring again before the barrier ahead of the decode pass
-    uint32_t* const scnt = &S.ring[0][0];
-    scnt[tid] = cnt;
-    __syncthreads();
-    for (int o = 1; o < DEC_THREADS; o <<= 1) {
-        const uint32_t v = tid >= o ? scnt[tid - o] : 0u;
-        __syncthreads();
-        scnt[tid] += v;
-        __syncthreads();
-    }
-    const int seg0 = tid - (int)j;  // lane of unit 0 of this chunk
-    const uint32_t before_seg = seg0 > 0 ? scnt[seg0 - 1] : 0u;
-    const uint32_t out_off = scnt[tid] - cnt - before_seg;
-    uint64_t used_bits = 0;
-    if (run && !bad) {
-        if (last) {
-            // the code words left in the chunk's last word, then zero padding
-            if (out_off + cnt > m_c || m_c - out_off - cnt > 32) {
-                bad = true;
-            } else {
-                // they lie in the last payload word, which the window holds
-                // after the count pass (w0): no ring words are needed (the
-                // ring's row 0 holds the counts)
-                const uint32_t rem = m_c - out_off - cnt;
-                uint32_t inval = 0;
-                for (uint32_t i = 0; i < rem; ++i) {
-                    r.refill();
-                    (void)step(T, L, r, inval);
-                }
-                r.refill();
-                cnt += rem;
-                const uint32_t endw = (uint32_t)(wc << 5);
-                const uint32_t pos = r.pos();
-                if (inval || pos > endw || pos + 32 <= endw) {
-                    bad = true;
-                } else {
-                    const uint32_t rest = endw - pos;
-                    if (rest && (r.peek() >> (32 - rest)) != 0) bad = true;
-                }
-                used_bits = pos - start_bit;
-            }
-        } else {
-            if (out_off + cnt > m_c) bad = true;
-            used_bits = end_bit - start_bit;
-        }
-    }
-
-    // padding bytes of the header are part of the format
-    if (bid == 0) {
-        for (uint64_t b = d.table_pad_from + tid; b < d.table_pad_to; b += DEC_THREADS)
-            bad |= d.stream[b] != 0;
-        for (uint64_t b = d.gap_pad_from + tid; b < d.gap_pad_to; b += DEC_THREADS)
-            bad |= d.stream[b] != 0;
-        if (tid == 0 && ((a.nc << a.log2k) & 1))
-            bad |= (d.stream[d.gap_pad_from - 1] >> 4) != 0;
-    }
-    const int wg_bad = __syncthreads_or(bad);
-
-    // ---- 3. decode pass: the DEC_BLOCK-byte blocks (aligned within the chunk's
-    // output) that start in this lane's range; each goes out as whole 16-byte
-    // stores, so every written sector of the output is written completely
-    if (run && !wg_bad) {
-        uint8_t* const base = d.out + c * a.chunk + out_off;
-        const uint32_t h = (DEC_BLOCK - (out_off & (DEC_BLOCK - 1))) & (DEC_BLOCK - 1);
-        const uint32_t nblk = cnt > h ? (cnt - h + DEC_BLOCK - 1) / DEC_BLOCK : 0u;
-        if (nblk) {
-            r.start(start_bit);
-            uint32_t inval = 0;  // cannot be set: the count pass read the same bits
-            for (uint32_t i = 0; i < h; ++i) {
-                if ((i & 3) == 0) r.tick();
-                r.refill();
-                (void)step(T, L, r, inval);
-            }
-            uint8_t* dst = base + h;
-            // blocks before the tensor end
-            const uint32_t full = min(nblk, (m_c - out_off - h) / DEC_BLOCK);
-            uint32_t b = 0;
-            for (; b < full; ++b) {
-                uint32_t w[DEC_BLOCK / 4];
-                uint32_t ev[4];
-#pragma unroll
-                for (int q = 0; q < DEC_BLOCK / 2; ++q) {
-                    if ((q & 3) == 0) r.tick();
-                    r.refill();
-#pragma unroll
-                    for (int k = 0; k < 2; ++k) {
-                        const int i = 2 * q + k;
-                        ev[i & 3] = step(T, L, r, inval);
-                        if ((i & 3) == 3) w[i >> 2] = syms4(ev);
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < DEC_BLOCK / 16; ++q) {
-                    v4u v;
-                    v.x = w[4 * q];
-                    v.y = w[4 * q + 1];
-                    v.z = w[4 * q + 2];
-                    v.w = w[4 * q + 3];
-                    *reinterpret_cast<v4u*>(dst + DEC_BLOCK * b + 16 * q) = v;
-                }
-            }
-            if (b < nblk) {
-                // the tensor ends inside this block: byte stores up to its end
-                const uint32_t left = m_c - out_off - h - DEC_BLOCK * b;
-                for (uint32_t i = 0; i < left; ++i) {
-                    if ((i & 3) == 0) r.tick();
-                    r.refill();
-                    const uint32_t e = step(T, L, r, inval);
-                    dst[DEC_BLOCK * b + i] = (uint8_t)(e >> 8);
-                }
-            }
+        const uint32_t end = r.pos();
+        if (inval || end != first_bit + my_bits) bad = true;
+        // the unit with the chunk's last symbol: zero padding to the end of the word
+        if (!bad && j == ((m_c - 1) >> 8)) {
+            const uint32_t rest = (uint32_t)(32 * wc) - end;
+            if (rest >= 32 || (rest && (r.peek() >> (32 - rest)) != 0)) bad = true;
         }
     }
 
     // ---- status, accounting, exit
-    uint64_t v = used_bits;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    constexpr int NS = P == 1 ? 1 : P;  // streams in this workgroup
+    const uint32_t slot = P == 1 ? 0u : k;
+    __syncthreads();  // the ring is free again: per-stream flags and bit sums
+    uint32_t* const flag = &S.ring[0][0];                                                    // [NS]
+    unsigned long long* const bsum = reinterpret_cast<unsigned long long*>(&S.ring[1][0]);  // [NS]
+    if (tid < NS) {
+        flag[tid] = 0u;
+        bsum[tid] = 0ull;
+    }
     __syncthreads();
-    if ((tid & 63) == 0) S.red[tid >> 6] = v;
-    const int any_bad = __syncthreads_or(bad);
+    if (bad) atomicOr(&flag[slot], 1u);
+    {
+        // bits of the units decoded without fault, summed per stream
+        uint64_t v = (run && !bad) ? my_bits : 0u;
+#pragma unroll
+        for (int o = 32; o >= P; o >>= 1) v += __shfl_xor(v, o, 64);
+        if ((tid & 63) < P && v) atomicAdd(&bsum[tid & 63], (unsigned long long)v);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        if (tid == q) {
+            const DecStream& d = a.st[P == 1 ? sidx : (uint32_t)q];
+            if (bsum[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&d.ws->bits), bsum[q]);
+            if (flag[q]) atomicCAS(&d.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
+        }
+    }
     if (tid == 0) {
-        uint64_t tot = 0;
-        for (int w = 0; w < DEC_THREADS / 64; ++w) tot += S.red[w];
-        if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(&d.ws->bits), (unsigned long long)tot);
-        if (any_bad) atomicCAS(&d.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
         __threadfence();
         WsHeader* ws0 = a.st[0].ws;
         const uint32_t done = __hip_atomic_fetch_add(&ws0->exit_count, 1u, __ATOMIC_ACQ_REL,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
-            for (uint32_t k = 0; k < a.nstreams; ++k) {
-                DecStream e = a.st[k];
+            for (uint32_t s = 0; s < a.nstreams; ++s) {
+                DecStream e = a.st[s];
                 if (a.sizes) {
-                    const uint64_t bytes = a.sizes[k].bytes;
+                    const uint64_t bytes = a.sizes[s].bytes;
                     e.payload_words = bytes >= e.header_bytes ? (bytes - e.header_bytes) / 4 : 0;
                 }
                 const uint64_t bits = __hip_atomic_load(&e.ws->bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -508,11 +547,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     }
 }
 
+template <int NT, int P, int OUT>
+void launch(const DecArgs& a, uint32_t wgs, hipStream_t hs) {
+    hipLaunchKernelGGL((decode_kernel<NT, P, OUT>), dim3(wgs), dim3(NT), 0, hs, a);
+}
+
 }  // namespace
 
 int launch_decode(const DecodeLaunch& L, void* stream) {
     DecArgs a{};
-    const uint64_t tb = table_bytes(L.nc), gb = gap_bytes(L.nc, L.chunk);
+    const uint64_t tb = table_bytes(L.nc), ub = ulen_bytes(L.nc, L.chunk);
     const uint32_t K = units_per_chunk(L.chunk);
     a.chunk = L.chunk;
     a.log2k = (uint32_t)ilog2(K);
@@ -520,37 +564,67 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
     a.nc = L.nc;
     a.nstreams = L.nstreams;
     a.sizes = L.dev_sizes;
+    a.merged = L.merged;
+    a.w0 = L.w0;
+    if (L.nstreams < 1 || L.nstreams > 4) return LECB_ERR_INVALID_ARG;
     for (int s = 0; s < L.nstreams; ++s) {
         DecStream& st = a.st[s];
         st.table = reinterpret_cast<const uint32_t*>(L.stream_base[s]);
-        st.gaps = L.stream_base[s] + tb;
-        st.payload = reinterpret_cast<const uint32_t*>(L.stream_base[s] + tb + gb);
-        st.payload_words = L.dev_sizes ? 0 : (L.stream_bytes[s] - tb - gb) / 4;
+        st.ulen = reinterpret_cast<const uint16_t*>(L.stream_base[s] + tb);
+        st.payload = reinterpret_cast<const uint32_t*>(L.stream_base[s] + tb + ub);
+        st.payload_words = L.dev_sizes ? 0 : (L.stream_bytes[s] - tb - ub) / 4;
         st.cb = L.cb[s];
-        st.header_bytes = tb + gb;
+        st.header_bytes = tb + ub;
         st.stream = L.stream_base[s];
         st.table_pad_from = 4 * L.nc;
         st.table_pad_to = tb;
-        st.gap_pad_from = tb + (L.nc * K + 1) / 2;
-        st.gap_pad_to = tb + gb;
+        st.ulen_pad_from = tb + 2 * L.nc * K;
+        st.ulen_pad_to = tb + ub;
         st.out = L.out[s];
         st.res = L.res[s];
         st.ws = L.ws[s];
     }
     const uint64_t units = L.nc * K;
-    // Lanes per workgroup: the tables are one copy per workgroup, so bigger
-    // workgroups leave more LDS for lanes (2 x 1024 lanes fit a CU against
-    // 5 x 256), and fewer, bigger workgroups spread evenly over the CUs.
-    // Take the biggest size that still gives every CU a workgroup.
-    const uint64_t all = units * (uint64_t)L.nstreams;
     const uint64_t cus = (uint64_t)device_cu_count();
-    const int nt = all >= cus * 1024 ? 1024 : all >= cus * 512 ? 512 : 256;
-    a.wg_per_stream = (uint32_t)((units + nt - 1) / nt);
-    const dim3 grid((uint32_t)((uint64_t)a.wg_per_stream * L.nstreams));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    if (nt == 1024) hipLaunchKernelGGL(decode_kernel<1024>, grid, dim3(1024), 0, hs, a);
-    else if (nt == 512) hipLaunchKernelGGL(decode_kernel<512>, grid, dim3(512), 0, hs, a);
-    else hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(256), 0, hs, a);
+    if (L.out_kind == DEC_OUT_PLANES) {
+        // One stream per workgroup.  Lanes per workgroup: the tables are one
+        // copy per workgroup, so bigger workgroups leave more LDS for lanes
+        // (2 x 1024 lanes fit a CU against 5 x 256), and fewer, bigger
+        // workgroups spread evenly over the CUs.  Take the biggest size that
+        // still gives every CU a workgroup (every size holds whole chunks:
+        // K <= 256 units).
+        const uint64_t all = units * (uint64_t)L.nstreams;
+        const int nt = all >= cus * 1024 ? 1024 : all >= cus * 512 ? 512 : 256;
+        a.wg_per_group = (uint32_t)((units + nt - 1) / nt);
+        const uint32_t wgs = a.wg_per_group * (uint32_t)L.nstreams;
+        if (nt == 1024) launch<1024, 1, DEC_OUT_PLANES>(a, wgs, hs);
+        else if (nt == 512) launch<512, 1, DEC_OUT_PLANES>(a, wgs, hs);
+        else launch<256, 1, DEC_OUT_PLANES>(a, wgs, hs);
+    } else if (L.out_kind == DEC_OUT_U16 || L.out_kind == DEC_OUT_U16_XOR) {
+        // two lanes per unit; a workgroup holds whole chunks (2K <= 512 lanes)
+        if (L.nstreams != 2 || !L.merged || (L.out_kind == DEC_OUT_U16_XOR && !L.w0)) return LECB_ERR_INVALID_ARG;
+        const uint64_t lanes = 2 * units;
+        const int nt = lanes >= cus * 1024 ? 1024 : 512;
+        const uint32_t wgs = (uint32_t)((lanes + nt - 1) / nt);
+        if (L.out_kind == DEC_OUT_U16) {
+            if (nt == 1024) launch<1024, 2, DEC_OUT_U16>(a, wgs, hs);
+            else launch<512, 2, DEC_OUT_U16>(a, wgs, hs);
+        } else {
+            if (nt == 1024) launch<1024, 2, DEC_OUT_U16_XOR>(a, wgs, hs);
+            else launch<512, 2, DEC_OUT_U16_XOR>(a, wgs, hs);
+        }
+    } else if (L.out_kind == DEC_OUT_U32) {
+        // four lanes per unit; a workgroup holds whole chunks (4K lanes)
+        if (L.nstreams != 4 || !L.merged) return LECB_ERR_INVALID_ARG;
+        const uint64_t lanes = 4 * units;
+        const int nt = 4 * K > 512 ? 1024 : 512;
+        const uint32_t wgs = (uint32_t)((lanes + nt - 1) / nt);
+        if (nt == 1024) launch<1024, 4, DEC_OUT_U32>(a, wgs, hs);
+        else launch<512, 4, DEC_OUT_U32>(a, wgs, hs);
+    } else {
+        return LECB_ERR_INVALID_ARG;
+    }
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

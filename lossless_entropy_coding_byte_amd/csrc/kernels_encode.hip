@@ -1,4 +1,4 @@
-// Huffman encode of byte symbols into stream format v1, in two launches
+// Huffman encode of byte symbols into stream format v2, in two launches
 // (a count launch, then a pack launch).
 //
 // "Single-Stage Huffman Encoder for ML Compression", Methodology step 4: each
@@ -27,10 +27,9 @@
 //         the workgroup's earlier tickets; the chunk table entries follow;
 //      C. per stream: every thread ORs its code words into an LDS image of
 //         the ticket's payload (each chunk starts on a word), then the image
-//         goes out with coalesced stores.  While packing, a thread whose bit
-//         range holds the start s_j of a decode unit records that unit's gap:
-//         the distance from s_j to the first code word that starts at or
-//         after it.
+//         goes out with coalesced stores.  The code bits of every decode
+//         unit (256 symbols = 4 threads) are the sum of its four threads'
+//         bits and go out as one u16 per unit.
 // No workgroup ever waits for another one.
 #include <hip/hip_runtime.h>
 
@@ -57,18 +56,17 @@ constexpr int STAGE_WORDS = SEG * 16 / 32 + MAX_G + 2;   // worst case 16 bits/s
 // the 32 banks; with the padding word every 32 they spread over all of them.
 __device__ inline uint32_t st_at(uint32_t k) { return k + (k >> 5); }
 constexpr int STAGE_LDS = STAGE_WORDS + STAGE_WORDS / 32 + 1;
-constexpr int MAX_K = LECB_MAX_CHUNK / LECB_UNIT_SYMBOLS; // units per chunk at most (256)
-constexpr uint32_t NO_BOUNDARY = 0xFFFFFFFFu;
+constexpr int THREADS_PER_UNIT = LECB_UNIT_SYMBOLS / SPT;   // 4
 
 struct StreamArgs {
     const DeviceCodebook* cb;
     uint32_t* table;
-    uint8_t* gaps;
+    uint16_t* ulen;                          // code bits of every decode unit
     uint32_t* payload;
     uint64_t header_bytes;
     uint64_t capacity_words;
     uint64_t table_pad_from, table_pad_to;  // byte ranges of header padding
-    uint64_t gap_pad_from, gap_pad_to;
+    uint64_t ulen_pad_from, ulen_pad_to;
     uint8_t* stream;
     lecb_result* res;
     WsHeader* ws;
@@ -247,7 +245,6 @@ struct Shared {
     uint64_t tmp[4];
     uint32_t cword[2][MAX_G];      // first payload word of each chunk, ticket-relative
     uint32_t cbits[2][MAX_G];      // bits of each chunk
-    uint8_t gap[2][MAX_K];         // unit gaps of the ticket's chunks (G*K <= MAX_K)
     uint64_t tbase[2];
     uint64_t tbits[2];
     uint32_t twords[2];
@@ -293,48 +290,9 @@ __device__ inline uint64_t count_bits(const uint8_t (&len)[2][256], const uint32
     return packed;
 }
 
-// Record the gaps of all unit starts s_j in (prev, p]: their first code-word
-// start at or after them is p.  j/nb: the next unit start and its index.
-__device__ inline void gaps_upto(uint32_t p, uint32_t& j, uint32_t& nb, uint32_t wc, uint32_t K,
-                                 uint32_t log2k, uint8_t* gap) {
-    while (nb <= p) {
-        gap[j] = (uint8_t)(p - nb);
-        ++j;
-        nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
-    }
-}
-
-// Symbol i of stream s, read from the input (for the rare re-walk below).
-template <int MODE>
-__device__ inline uint32_t input_symbol(const EncArgs& a, int s, uint64_t i) {
-    if constexpr (MODE == ENC_BYTES) {
-        return static_cast<const uint8_t*>(a.in)[i];
-    } else {
-        const uint32_t x = input_word<MODE>(a, i);
-        const bool lo = MODE == ENC_PLANE_LO || (pair_mode(MODE) && s == 1);
-        return lo ? (x & 0xFFu) : (x >> 8);
-    }
-}
-
-// Gaps of all unit starts in the thread's range (ts, end], by walking its
-// code words again (symbols re-read from the input).  Only for the rare
-// thread that owns more than one unit start: units are 8+ words apart
-// except in a short last chunk.
-template <int MODE>
-__device__ inline void gaps_walk(const Shared& S, const EncArgs& a, int s, uint64_t i0, int nv,
-                                 uint32_t ts, uint32_t j, uint32_t nb, uint32_t wc, uint32_t K,
-                                 uint32_t log2k, uint8_t* gap) {
-    uint32_t p = ts;
-    for (int k = 0; k < nv; ++k) {
-        p += S.len[s][input_symbol<MODE>(a, s, i0 + k)];  // start of code word k + 1
-        gaps_upto(p, j, nb, wc, K, log2k, gap);
-    }
-}
-
-// Pack the thread's code words into the stage at bit `pos` and record the
-// gaps of the unit starts in its chunk-relative bit range [ts, ...).  FULL:
-// all 64 symbols valid (else the first nv; the rest are zero bytes and get
-// no code word).
+// Pack the thread's code words into the stage at bit `pos`.  FULL: all 64
+// symbols valid (else the first nv; the rest are zero bytes and get no code
+// word).
 //   * Code words are looked up 16 at a time (one LDS latency per 16) and
 //     joined in pairs: a pair is at most 32 bits, so it enters the 64-bit
 //     accumulator in one step and completes at most one word.
@@ -342,21 +300,8 @@ __device__ inline void gaps_walk(const Shared& S, const EncArgs& a, int s, uint6
 //     is zero before packing): the completed word, or zero into the word
 //     being filled.  A word shared with the neighbouring threads (the first
 //     and the last) gets each thread's bits by the same OR.
-//   * The first unit start nb0 after ts gets the first code-word start at or
-//     after it: the smallest unsigned difference (start - nb0) over the code
-//     starts (a start before nb0 wraps to a huge value); a thread that owns
-//     a second unit start walks its code words again.
-template <bool FULL, int MODE>
-__device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, uint32_t w[16], int nv,
-                              uint32_t pos, uint32_t ts, uint32_t wc, uint32_t K, uint32_t log2k,
-                              uint8_t* gap) {
-    // first unit start at or after ts: s_j = 32*floor(j*wc/K) >= ts
-    uint32_t j = wc ? (uint32_t)((((uint64_t)((ts + 31) >> 5)) * K + wc - 1) / wc) : K;
-    uint32_t nb = j < K ? (uint32_t)(((uint64_t)j * wc) >> log2k) << 5 : NO_BOUNDARY;
-    gaps_upto(ts, j, nb, wc, K, log2k, gap);  // unit starts exactly at ts: gap 0
-    const uint32_t j0 = j, nb0 = nb;          // next unit start, after ts
-    uint32_t g0 = 0xFFFFFFFFu;
-    uint32_t p = ts;  // chunk-relative start of the next code word
+template <bool FULL>
+__device__ inline void pack64(Shared& S, int s, uint32_t w[16], int nv, uint32_t pos) {
     uint32_t widx = pos >> 5;
     uint32_t used = pos & 31u;
     uint64_t acc = 0;
@@ -377,9 +322,6 @@ __device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, u
             const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
             const uint32_t l0 = e0 & 31u, l1 = e1 & 31u;
             const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);  // at most 32 bits
-            const uint32_t pmid = p + l0, pend = pmid + l1;
-            g0 = min(g0, min(pmid - nb0, pend - nb0));
-            p = pend;
             used += l0 + l1;
             acc |= (uint64_t)c2 << ((64 - used) & 63);  // ends at bit `used` from the top
             const uint32_t full = used >> 5;             // used <= 63
@@ -392,13 +334,13 @@ __device__ inline void pack64(Shared& S, const EncArgs& a, uint64_t i0, int s, u
         for (int i = 0; i < 12; ++i) ww[i] = ww[i + 4];
     }
     if (used) atomicOr(&S.stage[st_at(widx)], (uint32_t)(acc >> 32));
-    // unit starts in (ts, p]; p is the range end
-    if (nb0 <= p) {
-        gap[j0] = (uint8_t)g0;
-        const uint32_t j1 = j0 + 1;
-        const uint32_t nb1 = j1 < K ? (uint32_t)(((uint64_t)j1 * wc) >> log2k) << 5 : NO_BOUNDARY;
-        if (nb1 <= p) gaps_walk<MODE>(S, a, s, i0, FULL ? SPT : nv, ts, j1, nb1, wc, K, log2k, gap);
-    }
+}
+
+// Code bits of the decode unit of the thread (the 4 threads of a unit are
+// consecutive lanes of a wave); every lane receives its unit's total.
+__device__ inline uint32_t unit_bits(uint32_t mine) {
+    uint32_t v = mine + __shfl_xor(mine, 1, 64);
+    return v + __shfl_xor(v, 2, 64);
 }
 
 // First ticket of workgroup w when T tickets are split over W workgroups.
@@ -614,13 +556,12 @@ __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(Enc
                 const StreamArgs& st = a.st[s];
                 const uint32_t twords = S.twords[s];
                 const uint32_t mine = (uint32_t)(own >> (32 * s));  // this thread's bits
-                uint32_t pos, ts, wc, ch;
+                uint32_t pos, ch;
                 uint32_t r0 = 0, w0 = 0, touched;
                 if (nseg == 1) {
                     ch = tid / L;
                     const uint64_t before = ch ? S.incl[ch * L - 1] : 0ull;
-                    ts = (uint32_t)((incl - before) >> (32 * s)) - mine;  // chunk-relative start bit
-                    wc = (S.cbits[s][min(ch, (uint32_t)MAX_G - 1)] + 31) >> 5;
+                    const uint32_t ts = (uint32_t)((incl - before) >> (32 * s)) - mine;  // chunk-relative start bit
                     pos = (ch < nch ? S.cword[s][ch] * 32u : 0u) + ts;
                     touched = twords;
                     for (uint32_t k = tid; k < touched; k += ENC_THREADS) S.stage[st_at(k)] = 0u;
@@ -628,8 +569,6 @@ __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(Enc
                     ch = 0;
                     const uint32_t seg_bits = (uint32_t)(seg_total >> (32 * s));
                     const uint32_t excl = (uint32_t)(incl >> (32 * s)) - mine;
-                    ts = TB[s] + excl;
-                    wc = (S.cbits[s][0] + 31) >> 5;
                     r0 = TB[s] & 31u;
                     w0 = TB[s] >> 5;
                     pos = r0 + excl;
@@ -637,11 +576,20 @@ __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(Enc
                     for (uint32_t k = tid; k <= touched; k += ENC_THREADS) S.stage[st_at(k)] = k ? 0u : carry[s];
                     TB[s] += seg_bits;
                 }
+                // the unit's code bits: unit u of the ticket's chunk ch (units
+                // past n hold no symbols and get 0)
+                {
+                    const uint32_t ub = unit_bits(mine);
+                    const uint64_t u = nseg == 1
+                                           ? (c0 + ch) * K + (tid % L) / THREADS_PER_UNIT
+                                           : c0 * K + (uint64_t)g * (SEG / LECB_UNIT_SYMBOLS) + tid / THREADS_PER_UNIT;
+                    if ((tid & (THREADS_PER_UNIT - 1)) == 0 && ch < nch) st.ulen[u] = (uint16_t)ub;
+                }
                 __syncthreads();
                 if (nv == SPT && ch < nch)
-                    pack64<true, MODE>(S, a, i0, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
+                    pack64<true>(S, s, w[s], nv, pos);
                 else if (nv > 0 && ch < nch)
-                    pack64<false, MODE>(S, a, i0, s, w[s], nv, pos, ts, wc, K, a.log2k, &S.gap[s][(ch * K) & (MAX_K - 1)]);
+                    pack64<false>(S, s, w[s], nv, pos);
                 __syncthreads();  // stage complete
                 const uint64_t tbase = S.tbase[s];
                 const bool write_ok = tbase + twords <= st.capacity_words && !S.uncoded;
@@ -671,22 +619,21 @@ __global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(Enc
                 __syncthreads();
             }
         }
+        // a short last chunk of a chunk size above SEG: its units past the
+        // last segment hold no symbols
+        if (a.chunk > SEG && nseg * (SEG / LECB_UNIT_SYMBOLS) < K) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                for (uint32_t u = nseg * (SEG / LECB_UNIT_SYMBOLS) + tid; u < K; u += ENC_THREADS)
+                    a.st[s].ulen[c0 * K + u] = 0;
+        }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const StreamArgs& st = a.st[s];
-            // unit gaps of the ticket's chunks, K nibbles each
-            if (K >= 2) {
-                const uint32_t nbytes = nch * K / 2;
-                for (uint32_t b = tid; b < nbytes; b += ENC_THREADS)
-                    st.gaps[c0 * (K / 2) + b] = (uint8_t)(S.gap[s][2 * b] | (S.gap[s][2 * b + 1] << 4));
-            } else {
-                // one unit per chunk, gap 0; two chunks per byte (c0 is even)
-                for (uint32_t b = tid; b < (nch + 1) / 2; b += ENC_THREADS) st.gaps[c0 / 2 + b] = 0;
-            }
             if (c0 + nch == a.nc) {
                 for (uint64_t b = st.table_pad_from + tid; b < st.table_pad_to; b += ENC_THREADS)
                     st.stream[b] = 0;
-                for (uint64_t b = st.gap_pad_from + tid; b < st.gap_pad_to; b += ENC_THREADS)
+                for (uint64_t b = st.ulen_pad_from + tid; b < st.ulen_pad_to; b += ENC_THREADS)
                     st.stream[b] = 0;
             }
         }
@@ -757,20 +704,20 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
     const int ns = pair_mode(L.mode) ? 2 : 1;
     for (int s = 0; s < ns; ++s)
         if (!L.st[s].cb || !L.st[s].out || !L.st[s].res || !L.st[s].ws) return LECB_ERR_INVALID_ARG;
-    const uint64_t tb = table_bytes(L.nc), gb = gap_bytes(L.nc, L.chunk);
+    const uint64_t tb = table_bytes(L.nc), ub = ulen_bytes(L.nc, L.chunk);
     for (int s = 0; s < ns; ++s) {
         StreamArgs& st = a.st[s];
         st.cb = L.st[s].cb;
         st.stream = L.st[s].out;
         st.table = reinterpret_cast<uint32_t*>(L.st[s].out);
-        st.gaps = L.st[s].out + tb;
-        st.payload = reinterpret_cast<uint32_t*>(L.st[s].out + tb + gb);
-        st.header_bytes = tb + gb;
-        st.capacity_words = (L.st[s].capacity - (tb + gb)) / 4;
+        st.ulen = reinterpret_cast<uint16_t*>(L.st[s].out + tb);
+        st.payload = reinterpret_cast<uint32_t*>(L.st[s].out + tb + ub);
+        st.header_bytes = tb + ub;
+        st.capacity_words = (L.st[s].capacity - (tb + ub)) / 4;
         st.table_pad_from = 4 * L.nc;
         st.table_pad_to = tb;
-        st.gap_pad_from = tb + (L.nc * units_per_chunk(L.chunk) + 1) / 2;
-        st.gap_pad_to = tb + gb;
+        st.ulen_pad_from = tb + 2 * L.nc * units_per_chunk(L.chunk);
+        st.ulen_pad_to = tb + ub;
         st.res = L.st[s].res;
         st.ws = L.st[s].ws;
         st.wg_words = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);  // room for nc >= grid values

@@ -47,8 +47,9 @@ struct CodebookArgs {
 // two-stream encode uses both; everything else uses the first.  After them
 // comes one u32 per 64 consecutive symbols: the code bits of those symbols
 // per stream, written by the encode's count launch and read by its pack
-// launch.  The last workgroup of every call resets the headers, so only the
-// first use needs a zero-filled workspace.
+// launch.  Two more headers follow them, for the third and fourth stream of
+// a four-plane decode.  The last workgroup of every call resets the headers,
+// so only the first use needs a zero-filled workspace.
 struct WsHeader {
     uint32_t unused0;
     uint32_t exit_count;
@@ -71,13 +72,21 @@ inline bool valid_chunk(uint32_t chunk) {
 }
 inline uint32_t units_per_chunk(uint32_t chunk) { return chunk / LECB_UNIT_SYMBOLS; }
 inline uint64_t table_bytes(uint64_t nc) { return align16(4 * nc); }
-inline uint64_t gap_bytes(uint64_t nc, uint32_t chunk) {
-    return align16((nc * units_per_chunk(chunk) + 1) / 2);
-}
+// The u16 code-bit count of every decode unit (K per chunk), padded to 16 bytes.
+inline uint64_t ulen_bytes(uint64_t nc, uint32_t chunk) { return align16(2 * nc * units_per_chunk(chunk)); }
 // Bytes of one stream's part of the workspace: header + one flag per chunk.
 inline uint64_t ws_stream_bytes(uint64_t nc) { return (sizeof(WsHeader) + 8 * nc + 255) & ~uint64_t(255); }
 // Bytes of the per-64-symbol bit counts that follow the two stream parts.
 inline uint64_t ws_count_bytes(uint64_t n) { return (4 * ((n + 63) / 64) + 255) & ~uint64_t(255); }
+// Two more headers after the counts (the four streams of a four-plane decode).
+constexpr uint64_t WS_EXTRA_BYTES = 256;
+inline uint64_t ws_total_bytes(uint64_t n, uint64_t nc) {
+    return 2 * ws_stream_bytes(nc) + ws_count_bytes(n) + WS_EXTRA_BYTES;
+}
+// Offset of stream k's header (k < 4): the two stream parts, then the extra headers.
+inline uint64_t ws_header_offset(int k, uint64_t n, uint64_t nc) {
+    return k < 2 ? k * ws_stream_bytes(nc) : 2 * ws_stream_bytes(nc) + ws_count_bytes(n) + (k - 2) * sizeof(WsHeader);
+}
 
 // ---------------------------------------------------------------- host helpers
 int build_lengths(const uint64_t freq[256], uint32_t max_len, uint32_t min_freq,
@@ -126,17 +135,27 @@ struct EncodeLaunch {
 };
 int launch_encode(const EncodeLaunch& a, void* stream);
 
-// One or two streams of the same n and chunk decoded in one launch (the two
-// byte planes of 16-bit words); stream k uses workspace part ws[k].
+// What a decode writes: each stream's bytes to its own output (one or two
+// streams), or the byte planes of the same elements restored on the way out
+// -- 16-bit words from two streams (high plane first), optionally XORed with
+// a second tensor (the snapshot delta), or 32-bit elements from four streams
+// (plane p = byte 3 - p).
+enum DecodeOut { DEC_OUT_PLANES = 0, DEC_OUT_U16 = 1, DEC_OUT_U16_XOR = 2, DEC_OUT_U32 = 3 };
+
+// Streams of the same n and chunk decoded in one launch; stream k uses
+// workspace header ws[k].
 struct DecodeLaunch {
     int nstreams;
+    int out_kind;                   // DecodeOut
     const lecb_result* dev_sizes;   // non-null: stream sizes are read on the device from these
-    const uint8_t* stream_base[2];
-    uint64_t stream_bytes[2];
-    const DeviceCodebook* cb[2];
-    uint8_t* out[2];
-    lecb_result* res[2];
-    WsHeader* ws[2];
+    const uint8_t* stream_base[4];
+    uint64_t stream_bytes[4];
+    const DeviceCodebook* cb[4];
+    uint8_t* out[4];                // DEC_OUT_PLANES
+    uint8_t* merged;                // the restored elements (other kinds)
+    const uint8_t* w0;              // DEC_OUT_U16_XOR: element i of the output is w0[i] ^ restored[i]
+    lecb_result* res[4];
+    WsHeader* ws[4];
     uint32_t chunk;
     uint64_t n;
     uint64_t nc;

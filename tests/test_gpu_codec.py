@@ -286,10 +286,8 @@ def test_bf16_pertensor_pipeline(n, chunk):
     assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), ref["stream_hi"])
     assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), ref["stream_lo"])
     out = torch.empty(n, dtype=torch.int16, device=DEV)
-    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
     res2 = lecb.new_results(2, DEV)
-    lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, out,
-                          scratch, res2, ws)
+    lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, out, res2, ws)
     rr = lecb.results_to_numpy(res2)
     assert int(rr[0]["status"]) == 0 and int(rr[1]["status"]) == 0
     assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
@@ -325,16 +323,14 @@ def test_fused_snapshot_delta(n, chunk):
     assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
     assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), enc["stream_hi"])
     assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), enc["stream_lo"])
-    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
     out = torch.empty(n, dtype=torch.int16, device=DEV)
     rd = lecb.new_results(2, DEV)
-    lecb.lecb_decode_bf16_delta_from_results(oh, ol, res, bh, bl, chunk, n, w0d, out, scratch, rd, ws)
+    lecb.lecb_decode_bf16_delta_from_results(oh, ol, res, bh, bl, chunk, n, w0d, out, rd, ws)
     q = lecb.results_to_numpy(rd)
     assert int(q[0]["status"]) == 0 and int(q[1]["status"]) == 0
     assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
     out.zero_()
-    lecb.lecb_decode_bf16_delta(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, w0d, out,
-                                scratch, rd, ws)
+    lecb.lecb_decode_bf16_delta(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, w0d, out, rd, ws)
     assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
 
 
@@ -496,16 +492,15 @@ def test_fp32_pertensor_pipeline(n, chunk):
         assert np.array_equal(cbs[p].lengths(), ref["len"][p]), p
         assert int(r[p]["payload_bits"]) == ref["bits"][p], p
         assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), ref["stream"][p]), p
-    scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
     out = torch.empty(n, dtype=torch.int32, device=DEV)
     rd = lecb.new_results(4, DEV)
-    lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, out, scratch, rd, ws)
+    lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, out, rd, ws)
     q = lecb.results_to_numpy(rd)
     assert all(int(q[p]["status"]) == 0 for p in range(4))
     assert [int(q[p]["payload_bits"]) for p in range(4)] == ref["bits"]
     assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
     out.zero_()
-    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, scratch, rd, ws)
+    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, rd, ws)
     assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
     assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
 
@@ -530,10 +525,9 @@ def test_fp32_fixed_codebooks_and_corrupt_plane():
         assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), want), p
     # a chunk-table entry past the payload: plane 2's stream is corrupt
     outs[2][0:4] = torch.tensor([255, 255, 255, 127], dtype=torch.uint8, device=DEV)
-    scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
     out = torch.empty(n, dtype=torch.int32, device=DEV)
     rd = lecb.new_results(4, DEV)
-    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, scratch, rd, ws)
+    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, rd, ws)
     st = [int(v) for v in lecb.results_to_numpy(rd)["status"]]
     assert st[2] == lecb.LECB_ERR_CORRUPT and st[0] == st[1] == st[3] == 0
 
@@ -583,8 +577,8 @@ def _cus():
 
 
 def _lanes_chosen(n, chunk, nstreams):
-    """Lanes per decode workgroup the host picks: the largest of 1024, 512,
-    256 whose workgroups still give every compute unit one."""
+    """Lanes per decode workgroup the host picks for separate byte planes: the
+    largest of 1024, 512, 256 whose workgroups still give every compute unit one."""
     units = -(-n // chunk) * (chunk // 256) * nstreams
     return 1024 if units >= _cus() * 1024 else 512 if units >= _cus() * 512 else 256
 
@@ -614,373 +608,6 @@ def test_bf16_two_plane_decode_workgroup_sizes(nt):
     n = 1_000_003 if nt == 256 else _cus() * 512 * 256 + 3
     assert _lanes_chosen(n, chunk, 2) == nt
     _say(f"two-plane decode nt={nt} n={n}")
-    x = workloads.bf16_weights(n)
-    enc = oracle.encode_bf16(x, chunk)
-    hi, lo = oracle.split_bf16(x)
-    bh = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_hi"]), DEV)
-    bl = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_lo"]), DEV)
-    sh = torch.zeros(enc["stream_hi"].size + 32, dtype=torch.uint8, device=DEV)
-    sl = torch.zeros(enc["stream_lo"].size + 32, dtype=torch.uint8, device=DEV)
-    sh[: enc["stream_hi"].size] = to_dev(enc["stream_hi"])
-    sl[: enc["stream_lo"].size] = to_dev(enc["stream_lo"])
-    oh = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=DEV)
-    ol = torch.empty_like(oh)
-    res = lecb.new_results(2, DEV)
-    ws = lecb.new_workspace(n, chunk, DEV)
-    lecb.lecb_decode_bf16_planes(sh, enc["stream_hi"].size, sl, enc["stream_lo"].size, bh.blob, bl.blob,
-                                 chunk, n, oh, ol, res, ws)
-    r = lecb.results_to_numpy(res)
-    assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
-    assert np.array_equal(oh[:n].cpu().numpy(), hi) and np.array_equal(ol[:n].cpu().numpy(), lo)
-    bad = enc["stream_lo"].copy()
-    bad[-1] ^= 0x01  # last payload word: a padding bit or a code bit changes
-    sl2 = dev_stream(bad)
-    lecb.lecb_decode_bf16_planes(sh, enc["stream_hi"].size, sl2, bad.size, bh.blob, bl.blob,
-                                 chunk, n, oh, ol, res, ws)
-    r = lecb.results_to_numpy(res)
-    assert int(r[0]["status"]) == 0
-    try:
-        oracle.decode(bad, enc["len_lo"], chunk, n)
-        lo_ok = True
-    except oracle.CorruptStream:
-        lo_ok = False
-    assert (int(r[1]["status"]) == 0) == lo_ok
-    if lo_ok:
-        assert np.array_equal(ol[:n].cpu().numpy(), oracle.decode(bad, enc["len_lo"], chunk, n))
-
-
-@pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), (1 << 20, 65536)])
-def test_bf16_pertensor_pipeline(n, chunk):
-    _say(f"bf16 per-tensor n={n} chunk={chunk}")
-    x = workloads.bf16_weights(n)
-    ref = oracle.encode_bf16(x, chunk)
-    xd = to_dev(x.view(np.int16))
-    hist = torch.zeros(512, dtype=torch.int64, device=DEV)
-    bh, bl = lecb.new_codebook_blob(DEV), lecb.new_codebook_blob(DEV)
-    cap = lecb.lecb_encoded_bound(n, chunk)
-    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
-    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
-    res = lecb.new_results(2, DEV)
-    ws = lecb.new_workspace(n, chunk, DEV)
-    cb_hi, cb_lo = lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
-    r = lecb.results_to_numpy(res)
-    assert np.array_equal(cb_hi.lengths(), ref["len_hi"]) and np.array_equal(cb_lo.lengths(), ref["len_lo"])
-    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), ref["stream_hi"])
-    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), ref["stream_lo"])
-    out = torch.empty(n, dtype=torch.int16, device=DEV)
-    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
-    res2 = lecb.new_results(2, DEV)
-    lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, out,
-                          scratch, res2, ws)
-    rr = lecb.results_to_numpy(res2)
-    assert int(rr[0]["status"]) == 0 and int(rr[1]["status"]) == 0
-    assert np.array_equal(out.cpu().numpy().view(np.uint16), x)
-
-
-# ----------------------------------------------------------------------------- fused snapshot delta
-
-@pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), ((1 << 20) + 5, 65536)])
-def test_fused_snapshot_delta(n, chunk):
-    """Encode from (W0, W1) and decode to W1: the delta planes' histograms,
-    codebooks and streams equal the oracle's for D = W0 ^ W1 (the XOR never
-    materialised), and the decode reproduces W1 exactly."""
-    _say(f"fused delta n={n} chunk={chunk}")
-    d, w0, w1 = workloads.bf16_delta(n, return_snapshots=True)
-    enc = oracle.encode_bf16(oracle.snapshot_delta(w0, w1), chunk)
-    w0d, w1d = to_dev(w0.view(np.int16)), to_dev(w1.view(np.int16))
-    hh = torch.zeros(256, dtype=torch.int64, device=DEV)
-    hl = torch.zeros(256, dtype=torch.int64, device=DEV)
-    lecb.lecb_histogram_bf16_delta(w0d, w1d, hh, hl)
-    dh, dl = oracle.split_bf16(d)
-    assert np.array_equal(hh.cpu().numpy().astype(np.uint64), oracle.histogram(dh))
-    assert np.array_equal(hl.cpu().numpy().astype(np.uint64), oracle.histogram(dl))
-    hist = torch.zeros(512, dtype=torch.int64, device=DEV)
-    bh, bl = lecb.new_codebook_blob(DEV), lecb.new_codebook_blob(DEV)
-    cap = lecb.lecb_encoded_bound(n, chunk)
-    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
-    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
-    res = lecb.new_results(2, DEV)
-    ws = lecb.new_workspace(n, chunk, DEV)
-    cb_hi, cb_lo = lecb.lecb_encode_bf16_delta_pertensor(w0d, w1d, n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
-    assert np.array_equal(cb_hi.lengths(), enc["len_hi"]) and np.array_equal(cb_lo.lengths(), enc["len_lo"])
-    r = lecb.results_to_numpy(res)
-    assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
-    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), enc["stream_hi"])
-    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), enc["stream_lo"])
-    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
-    out = torch.empty(n, dtype=torch.int16, device=DEV)
-    rd = lecb.new_results(2, DEV)
-    lecb.lecb_decode_bf16_delta_from_results(oh, ol, res, bh, bl, chunk, n, w0d, out, scratch, rd, ws)
-    q = lecb.results_to_numpy(rd)
-    assert int(q[0]["status"]) == 0 and int(q[1]["status"]) == 0
-    assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
-    out.zero_()
-    lecb.lecb_decode_bf16_delta(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, w0d, out,
-                                scratch, rd, ws)
-    assert np.array_equal(out.cpu().numpy().view(np.uint16), w1)
-
-
-# ----------------------------------------------------------------------------- codebooks built on the device
-
-def _test_histograms(seed, count):
-    r = np.random.default_rng(seed)
-    out = []
-    for t in range(count):
-        kind = t % 6
-        if kind == 0:
-            h = r.integers(0, 1000, 256)
-        elif kind == 1:
-            h = np.zeros(256, np.int64)
-            h[r.integers(0, 256, r.integers(1, 8))] = r.integers(1, 50)
-        elif kind == 2:
-            h = (r.pareto(1.0, 256) * 10).astype(np.int64)
-        elif kind == 3:
-            h = np.full(256, 7)
-            h[: r.integers(0, 256)] = 0
-        elif kind == 4:
-            h = (2.0 ** r.integers(0, 40, 256)).astype(np.int64)
-            h[r.random(256) < 0.3] = 0
-        else:
-            h = r.integers(0, 3, 256)
-        out.append(h.astype(np.uint64))
-    return out
-
-
-@pytest.mark.parametrize("max_len,min_freq", [(16, 0), (16, 1), (12, 0), (9, 1), (8, 0), (1, 0)])
-def test_device_codebook_build_matches_host(max_len, min_freq):
-    """The device builder's codebook blob equals, byte for byte, the blob of the
-    host builder + upload (lengths, codes, tables); where no code exists the
-    device codebook has no code word.  Lengths also against the oracle."""
-    hists = _test_histograms(40 + max_len, 48)
-    for g in range(0, len(hists), 4):
-        group = hists[g:g + 4]
-        hd = to_dev(np.concatenate(group).view(np.int64))
-        blobs = [lecb.new_codebook_blob(DEV) for _ in group]
-        lecb.lecb_build_codebook_device(hd, blobs, max_len, min_freq)
-        for h, blob in zip(group, blobs):
-            F = oracle.codebook_frequencies([h], min_freq)
-            m = int((F > 0).sum())
-            got = lecb.lecb_codebook_download(blob)
-            if m == 0 or m > (1 << max_len):
-                assert not got.lengths().any()
-                continue
-            assert np.array_equal(got.lengths(), oracle.package_merge_lengths(F, max_len))
-            ref = lecb.new_codebook_blob(DEV)
-            lecb.lecb_codebook_upload(lecb.lecb_build_codebook(h, max_len, min_freq), ref)
-            assert torch.equal(blob, ref)
-
-
-def test_device_codebook_special_cases():
-    cases = [np.zeros(256, np.uint64)]
-    one = np.zeros(256, np.uint64); one[77] = 5; cases.append(one)
-    two = np.zeros(256, np.uint64); two[3] = 1; two[200] = 1 << 40; cases.append(two)
-    cases.append(np.ones(256, np.uint64))
-    hd = to_dev(np.concatenate(cases).view(np.int64))
-    blobs = [lecb.new_codebook_blob(DEV) for _ in cases]
-    for g in range(0, 4):
-        lecb.lecb_build_codebook_device(hd[256 * g:], blobs[g:g + 1], 16, 0)
-    ln = [lecb.lecb_codebook_download(b).lengths() for b in blobs]
-    assert not ln[0].any()
-    assert ln[1][77] == 1 and ln[1].sum() == 1
-    assert ln[2][3] == 1 and ln[2][200] == 1 and ln[2].sum() == 2
-    assert np.all(ln[3] == 8)
-    # empty codebook: an encode with it reports the uncoded byte
-    xd = torch.zeros(4096, dtype=torch.uint8, device=DEV)
-    out = torch.empty(lecb.lecb_encoded_bound(4096, 4096), dtype=torch.uint8, device=DEV)
-    res = lecb.new_results(1, DEV)
-    lecb.lecb_encode(xd, 4096, blobs[0], 4096, out, res, lecb.new_workspace(4096, 4096, DEV))
-    assert int(lecb.results_to_numpy(res)[0]["status"]) == lecb.LECB_ERR_UNCODED_SYMBOL
-
-
-@pytest.mark.parametrize("n,chunk", [(1, 256), (300_001, 16384), ((1 << 20) + 3, 65536)])
-def test_pertensor_nosync_entries(n, chunk):
-    """bf16, snapshot-delta and fp32 per-tensor encodes with device-built
-    codebooks: streams and lengths equal the oracle's."""
-    _say(f"per-tensor nosync n={n} chunk={chunk}")
-    cap = lecb.lecb_encoded_bound(n, chunk)
-    ws = lecb.new_workspace(n, chunk, DEV)
-    # bf16
-    x = workloads.bf16_weights(n)
-    ref = oracle.encode_bf16(x, chunk)
-    hist = torch.zeros(512, dtype=torch.int64, device=DEV)
-    bh, bl = lecb.new_codebook_blob(DEV), lecb.new_codebook_blob(DEV)
-    oh = torch.empty(cap, dtype=torch.uint8, device=DEV)
-    ol = torch.empty(cap, dtype=torch.uint8, device=DEV)
-    res = lecb.new_results(2, DEV)
-    lecb.lecb_encode_bf16_pertensor_nosync(to_dev(x.view(np.int16)), n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
-    r = lecb.results_to_numpy(res)
-    assert np.array_equal(lecb.lecb_codebook_download(bh).lengths(), ref["len_hi"])
-    assert np.array_equal(lecb.lecb_codebook_download(bl).lengths(), ref["len_lo"])
-    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), ref["stream_hi"])
-    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), ref["stream_lo"])
-    # snapshot delta from the two snapshots
-    d, w0, w1 = workloads.bf16_delta(n, return_snapshots=True)
-    ref = oracle.encode_bf16(d, chunk)
-    lecb.lecb_encode_bf16_delta_pertensor_nosync(to_dev(w0.view(np.int16)), to_dev(w1.view(np.int16)), n, chunk,
-                                                 16, hist, bh, bl, oh, ol, res, ws)
-    r = lecb.results_to_numpy(res)
-    assert np.array_equal(oh[: int(r[0]["bytes"])].cpu().numpy(), ref["stream_hi"])
-    assert np.array_equal(ol[: int(r[1]["bytes"])].cpu().numpy(), ref["stream_lo"])
-    # fp32
-    x = workloads.fp32_weights(n)
-    ref = oracle.encode_fp32(x, chunk)
-    h4 = torch.zeros(1024, dtype=torch.int64, device=DEV)
-    blobs = [lecb.new_codebook_blob(DEV) for _ in range(4)]
-    outs = [torch.empty(cap, dtype=torch.uint8, device=DEV) for _ in range(4)]
-    res4 = lecb.new_results(4, DEV)
-    lecb.lecb_encode_fp32_pertensor_nosync(to_dev(x.view(np.int32)), n, chunk, 16, h4, blobs, outs, res4, ws)
-    r = lecb.results_to_numpy(res4)
-    for p in range(4):
-        assert int(r[p]["status"]) == 0
-        assert np.array_equal(lecb.lecb_codebook_download(blobs[p]).lengths(), ref["len"][p])
-        assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), ref["stream"][p])
-
-
-# ----------------------------------------------------------------------------- 32-bit elements, four planes
-
-@pytest.mark.parametrize("n", [1, 3, 4099, 1 << 20])
-def test_histogram_and_merge_fp32_exact(n):
-    _say(f"fp32 histogram/merge n={n}")
-    x = workloads.fp32_weights(n)
-    xd = to_dev(x.view(np.int32))
-    hist = torch.zeros(1024, dtype=torch.int64, device=DEV)
-    lecb.lecb_histogram_fp32(xd, hist)
-    h = hist.cpu().numpy().astype(np.uint64)
-    planes = oracle.split_fp32(x)
-    for p in range(4):
-        assert np.array_equal(h[256 * p:256 * (p + 1)], oracle.histogram(planes[p])), p
-    lecb.lecb_histogram_fp32(xd, hist, accumulate=True)
-    assert np.array_equal(hist.cpu().numpy().astype(np.uint64), 2 * h)
-    pd = [to_dev(pl) for pl in planes]
-    out = torch.empty(n, dtype=torch.int32, device=DEV)
-    lecb.lecb_merge_fp32(pd, out)
-    assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
-
-
-@pytest.mark.parametrize("n,chunk", [(1, 256), (5000, 4096), (300_001, 16384), ((1 << 20) + 7, 65536)])
-def test_fp32_pertensor_pipeline(n, chunk):
-    """Four byte planes: histograms, codebooks and all four streams equal the
-    oracle's; both decode entries restore the 32-bit elements exactly."""
-    _say(f"fp32 per-tensor n={n} chunk={chunk}")
-    x = workloads.fp32_weights(n)
-    ref = oracle.encode_fp32(x, chunk)
-    xd = to_dev(x.view(np.int32))
-    hist = torch.zeros(1024, dtype=torch.int64, device=DEV)
-    blobs = [lecb.new_codebook_blob(DEV) for _ in range(4)]
-    cap = lecb.lecb_encoded_bound(n, chunk)
-    outs = [torch.empty(cap, dtype=torch.uint8, device=DEV) for _ in range(4)]
-    res = lecb.new_results(4, DEV)
-    ws = lecb.new_workspace(n, chunk, DEV)
-    cbs = lecb.lecb_encode_fp32_pertensor(xd, n, chunk, 16, hist, blobs, outs, res, ws)
-    r = lecb.results_to_numpy(res)
-    for p in range(4):
-        assert int(r[p]["status"]) == 0, p
-        assert np.array_equal(cbs[p].lengths(), ref["len"][p]), p
-        assert int(r[p]["payload_bits"]) == ref["bits"][p], p
-        assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), ref["stream"][p]), p
-    scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
-    out = torch.empty(n, dtype=torch.int32, device=DEV)
-    rd = lecb.new_results(4, DEV)
-    lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, out, scratch, rd, ws)
-    q = lecb.results_to_numpy(rd)
-    assert all(int(q[p]["status"]) == 0 for p in range(4))
-    assert [int(q[p]["payload_bits"]) for p in range(4)] == ref["bits"]
-    assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
-    out.zero_()
-    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, scratch, rd, ws)
-    assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
-    assert np.array_equal(out.cpu().numpy().view(np.uint32), x)
-
-
-def test_fp32_fixed_codebooks_and_corrupt_plane():
-    """lecb_encode_fp32 with given codebooks (one per plane) and a corrupted
-    third stream: that plane's status is CORRUPT, the others stay OK."""
-    n, chunk = 70_000, 4096
-    x = workloads.fp32_weights(n)
-    planes = oracle.split_fp32(x)
-    lens = [codebook_for(pl, clamp=True) for pl in planes]
-    blobs = [lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV).blob for ln in lens]
-    xd = to_dev(x.view(np.int32))
-    cap = lecb.lecb_encoded_bound(n, chunk)
-    outs = [torch.empty(cap, dtype=torch.uint8, device=DEV) for _ in range(4)]
-    res = lecb.new_results(4, DEV)
-    ws = lecb.new_workspace(n, chunk, DEV)
-    lecb.lecb_encode_fp32(xd, n, blobs, chunk, outs, res, ws)
-    r = lecb.results_to_numpy(res)
-    for p in range(4):
-        want, _ = oracle.encode(planes[p], lens[p], oracle.canonical_codes(lens[p]), chunk)
-        assert np.array_equal(outs[p][: int(r[p]["bytes"])].cpu().numpy(), want), p
-    # a chunk-table entry past the payload: plane 2's stream is corrupt
-    outs[2][0:4] = torch.tensor([255, 255, 255, 127], dtype=torch.uint8, device=DEV)
-    scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
-    out = torch.empty(n, dtype=torch.int32, device=DEV)
-    rd = lecb.new_results(4, DEV)
-    lecb.lecb_decode_fp32(outs, [int(r[p]["bytes"]) for p in range(4)], blobs, chunk, n, out, scratch, rd, ws)
-    st = [int(v) for v in lecb.results_to_numpy(rd)["status"]]
-    assert st[2] == lecb.LECB_ERR_CORRUPT and st[0] == st[1] == st[3] == 0
-
-
-# ----------------------------------------------------------------------------- drift refresh
-
-@pytest.mark.parametrize("tol", [0, 20_000, 10**9])
-def test_adaptive_encode_over_drifting_batches(tol):
-    """lecb_encode_adaptive over batches whose spread grows: the refresh
-    decisions are the oracle's, every batch's stream is bit-exact to the
-    oracle's with the codebook it chose, and it decodes back."""
-    _say(f"adaptive encode tol={tol}")
-    rng = np.random.default_rng(21)
-    n, chunk = 200_003, 4096
-    batches = [np.clip(np.rint(rng.normal(0, 8 + 6 * k, n)), -128, 127).astype(np.int8).view(np.uint8)
-               for k in range(6)]
-    hists = [oracle.histogram(b) for b in batches]
-    first = oracle.package_merge_lengths(oracle.codebook_frequencies(hists[:1], 1), 16)
-    want = oracle.adaptive_codebooks(hists, first, 16, tol)
-    cb = lecb.lecb_codebook_from_lengths(first)
-    cb.max_len = 16
-    blob = lecb.new_codebook_blob(DEV)
-    lecb.lecb_codebook_upload(cb, blob)
-    hist = torch.zeros(256, dtype=torch.int64, device=DEV)
-    out = torch.empty(lecb.lecb_encoded_bound(n, chunk), dtype=torch.uint8, device=DEV)
-    res = lecb.new_results(1, DEV)
-    ws = lecb.new_workspace(n, chunk, DEV)
-    y = torch.empty(n, dtype=torch.uint8, device=DEV)
-    rd = lecb.new_results(1, DEV)
-    for b, (r_o, use_o, _, _) in zip(batches, want):
-        refreshed = lecb.lecb_encode_adaptive(to_dev(b), n, chunk, 16, tol, hist, cb, blob, out, res, ws)
-        assert refreshed == r_o
-        assert np.array_equal(cb.lengths(), use_o)
-        rr = lecb.results_to_numpy(res)[0]
-        assert int(rr["status"]) == 0
-        ref, _ = oracle.encode(b, use_o, oracle.canonical_codes(use_o), chunk)
-        assert np.array_equal(out[: int(rr["bytes"])].cpu().numpy(), ref)
-        lecb.lecb_decode_from_result(out, res, blob, chunk, n, y, rd, ws)
-        assert int(lecb.results_to_numpy(rd)[0]["status"]) == 0
-        assert np.array_equal(y.cpu().numpy(), b)
-
-
-# ----------------------------------------------------------------------------- decode workgroup sizes
-
-@pytest.mark.parametrize("nt", [256, 512, 1024])
-@pytest.mark.parametrize("n,chunk", [(300_007, 4096), (700_001, 65536), (1 << 20, 16384)])
-def test_decode_every_workgroup_size(monkeypatch, nt, n, chunk):
-    """The decoder picks 256, 512 or 1024 lanes per workgroup from the size of
-    the job; every size decodes the oracle's stream exactly (ragged tails and
-    chunks that end inside a workgroup included)."""
-    _say(f"decode nt={nt} n={n} chunk={chunk}")
-    monkeypatch.setenv("LECB_DECODE_THREADS", str(nt))
-    x = _gauss(40 + nt, n, 12.0)
-    ln = codebook_for(x, True)
-    ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), chunk)
-    dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
-    got, r = gpu_decode(ref, dcb, chunk, n)
-    assert int(r["status"]) == 0
-    assert np.array_equal(got, x)
-
-
-@pytest.mark.parametrize("nt", [256, 1024])
-def test_bf16_two_plane_decode_workgroup_sizes(monkeypatch, nt):
-    monkeypatch.setenv("LECB_DECODE_THREADS", str(nt))
-    n, chunk = 1_000_003, 16384
     x = workloads.bf16_weights(n)
     enc = oracle.encode_bf16(x, chunk)
     hi, lo = oracle.split_bf16(x)
@@ -1051,9 +678,8 @@ def test_bf16_decode_from_encoder_results(n, chunk):
     ws = lecb.new_workspace(n, chunk, DEV)
     lecb.lecb_encode_bf16_pertensor(xd, n, chunk, 16, hist, bh, bl, oh, ol, res, ws)
     y = torch.empty(n, dtype=torch.int16, device=DEV)
-    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
     rd = lecb.new_results(2, DEV)
-    lecb.lecb_decode_bf16_from_results(oh, ol, res, bh, bl, chunk, n, y, scratch, rd, ws)
+    lecb.lecb_decode_bf16_from_results(oh, ol, res, bh, bl, chunk, n, y, rd, ws)
     q = lecb.results_to_numpy(rd)
     assert int(q[0]["status"]) == 0 and int(q[1]["status"]) == 0
     assert torch.equal(y, xd)
@@ -1092,22 +718,30 @@ def test_corrupt_streams_set_status():
     t = ref.copy(); t[0:4] = 0; bad["zero end"] = t
     t = ref.copy(); e = t[:4 * nc].view("<u4").copy(); e[1], e[2] = e[2], e[1]; t[:4 * nc] = e.view(np.uint8); bad["non-monotone"] = t
     t = ref.copy(); t[4 * nc] = 1; bad["table padding"] = t
-    t = ref.copy(); t[tb] ^= 0x10; bad["gap value"] = t
-    t = ref.copy(); t[hb - 1] = 1; bad["gap padding"] = t
+    # unit bit counts: one bit moved from unit 0 to unit 1 of chunk 0 (same
+    # chunk total); the count of an empty unit (past the data) made non-zero
+    t = ref.copy(); u = t[tb:tb + 4].view("<u2").copy(); u[0] -= 1; u[1] += 1
+    t[tb:tb + 4] = u.view(np.uint8); bad["unit count moved"] = t
+    t = ref.copy(); t[hb - 2] = 1; bad["empty unit count"] = t
     t = ref.copy(); t[hb + 40:hb + 48] ^= 0xFF; bad["payload bits"] = t
-    for name, t in bad.items():
+    # chunk 256 (one unit per chunk): the zero padding after the unit counts
+    x2 = _gauss(20, 256 * 5 + 7, 12.0)
+    ref2, _ = oracle.encode(x2, ln, oracle.canonical_codes(ln), 256)
+    t = ref2.copy(); t[oracle.header_bytes(x2.size, 256) - 1] = 1
+    cases = [(name, t, x, 4096) for name, t in bad.items()] + [("unit count padding", t, x2, 256)]
+    for name, t, xx, chunk in cases:
         try:
-            oracle.decode(t, ln, 4096, x.size)
+            oracle.decode(t, ln, chunk, xx.size)
             oracle_bad = False
         except oracle.CorruptStream:
             oracle_bad = True
-        y, r = gpu_decode(t, dcb, 4096, x.size)
+        y, r = gpu_decode(t, dcb, chunk, xx.size)
         # the two decoders accept and reject exactly the same streams
         assert (int(r["status"]) == lecb.LECB_ERR_CORRUPT) == oracle_bad, name
         if name != "payload bits":
             assert oracle_bad, name
         elif not oracle_bad:
-            assert np.array_equal(y, oracle.decode(t, ln, 4096, x.size))
+            assert np.array_equal(y, oracle.decode(t, ln, chunk, xx.size))
     # a size below the header is rejected on the host
     with pytest.raises(lecb.LecbError):
         gpu_decode(ref[: hb - 4], dcb, 4096, x.size)

@@ -92,9 +92,8 @@ def _pertensor(name, x, pool):
     assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
     h = hist.cpu().numpy().astype(np.uint64)
     y = torch.empty(n, dtype=torch.int16, device=DEV)
-    scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
     rd = lecb.new_results(2, DEV)
-    lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, y, scratch, rd, ws)
+    lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, y, rd, ws)
     rdn = lecb.results_to_numpy(rd)
     assert int(rdn[0]["status"]) == 0 and int(rdn[1]["status"]) == 0
     assert torch.equal(y, xd)
@@ -190,9 +189,8 @@ def test_config_fp32_weights():
         r = lecb.results_to_numpy(res)
         h = hist.cpu().numpy().astype(np.uint64)
         y = torch.empty(n, dtype=torch.int32, device=DEV)
-        scratch = torch.empty(4 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
         rd = lecb.new_results(4, DEV)
-        lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, scratch, rd, ws)
+        lecb.lecb_decode_fp32_from_results(outs, res, blobs, chunk, n, y, rd, ws)
         assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
         assert torch.equal(y, xd)
         for p in range(4):
@@ -242,9 +240,8 @@ def test_config_bf16_delta():
         h = hist.cpu().numpy().astype(np.uint64)
         assert np.array_equal(h[:256], oracle.histogram(hi)) and np.array_equal(h[256:], oracle.histogram(lo))
         y = torch.empty(n, dtype=torch.int16, device=DEV)
-        scratch = torch.empty(2 * ((n + 15) // 16 * 16), dtype=torch.uint8, device=DEV)
         rd = lecb.new_results(2, DEV)
-        lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, y, scratch, rd,
+        lecb.lecb_decode_bf16(oh, int(r[0]["bytes"]), ol, int(r[1]["bytes"]), bh, bl, chunk, n, y, rd,
                               ws)
         assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
         assert torch.equal(y, xd)
@@ -262,8 +259,7 @@ def test_config_bf16_delta():
             assert int(fr[k]["bytes"]) == nb and int(fr[k]["status"]) == 0
             assert torch.equal(a[:nb], b[:nb]), "fused snapshot stream differs from the delta stream"
         w1o = torch.empty_like(w1d)
-        lecb.lecb_decode_bf16_delta(fh, int(fr[0]["bytes"]), fl, int(fr[1]["bytes"]), bh, bl, chunk, n, w0d, w1o,
-                                    scratch, rd, ws)
+        lecb.lecb_decode_bf16_delta(fh, int(fr[0]["bytes"]), fl, int(fr[1]["bytes"]), bh, bl, chunk, n, w0d, w1o, rd, ws)
         assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
         assert torch.equal(w1o, w1d)
         del w0d, w1d, w1o, fh, fl
