@@ -165,7 +165,7 @@ def _drift_batch(args):
     return k, workloads.int8_drift_batch(k, batch)
 
 
-def make_input(name: str, scale: float, pool):
+def make_input(name: str, scale: float, pool, cache_dir=None):
     cfg = dict(workloads.CONFIGS[name])
     cfg["name"] = name
     n = int(cfg["n"] * scale)
@@ -189,11 +189,20 @@ def make_input(name: str, scale: float, pool):
     elif name == "int8_drift":
         batch = min(workloads.BLOCK, n)
         cfg["batches"] = n // batch
-        x = np.empty(cfg["batches"] * batch, dtype=np.uint8)
-        # the 64 batches are drawn in the worker processes (same recipe, same seeds)
         t0 = time.perf_counter()
-        for k, xb in pool.imap_unordered(_drift_batch, [(k, batch) for k in range(cfg["batches"])]):
-            x[k * batch:(k + 1) * batch] = xb
+        cached = os.path.join(cache_dir, f"int8_drift_{cfg['batches']}x{batch}.npy") if cache_dir else None
+        if cached and os.path.exists(cached):
+            x = np.load(cached)
+        else:
+            x = np.empty(cfg["batches"] * batch, dtype=np.uint8)
+            jobs = [(k, batch) for k in range(cfg["batches"])]
+            # the 64 batches are drawn in the worker processes (same recipe,
+            # same seeds), or here one after the other when there are none
+            for k, xb in (pool.imap_unordered(_drift_batch, jobs) if pool else map(_drift_batch, jobs)):
+                x[k * batch:(k + 1) * batch] = xb
+            if cached:
+                os.makedirs(cache_dir, exist_ok=True)
+                np.save(cached, x)
         cfg["generate_s"] = round(time.perf_counter() - t0, 2)
         cfg["n"] = n = x.size
         # one fixed codebook from batch 0, every byte coded
@@ -756,6 +765,10 @@ def main():
     ap.add_argument("--config", default="int8_drift", choices=list(workloads.CONFIGS))
     ap.add_argument("--scale", type=float, default=1.0, help="fraction of the config's size (tests)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workers", action="store_true",
+                    help="no worker processes (inputs drawn in this process, no CPU baseline): for profilers")
+    ap.add_argument("--inputs-cache", default=None, metavar="DIR",
+                    help="keep the drawn 4 GiB drift stream in DIR as .npy and reuse it on later runs")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements the oracle baseline codes (spread over the batches of the drift stream)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -777,13 +790,18 @@ def main():
         sys.exit(2)
 
     # Worker processes first: they start before this process touches the GPU,
-    # draw the long inputs in parallel and run the CPU oracle baseline.
+    # draw the long inputs in parallel and run the CPU oracle baseline.  Under
+    # a profiler that sets up the GPU before the program starts there must be
+    # no worker processes (--no-workers: inputs drawn here, no baseline).
     cores = len(os.sched_getaffinity(0))
-    with mp.get_context("spawn").Pool(cores) as pool:
-        cfg, x, hist = make_input(args.config, args.scale, pool)
-        cpu = None
-        if not args.no_cpu_baseline:
-            cpu = cpu_baseline(cfg, x, hist, min(args.cpu_sample, x.size), pool, cores)
+    cpu = None
+    if args.no_workers:
+        cfg, x, hist = make_input(args.config, args.scale, None, args.inputs_cache)
+    else:
+        with mp.get_context("spawn").Pool(cores) as pool:
+            cfg, x, hist = make_input(args.config, args.scale, pool, args.inputs_cache)
+            if not args.no_cpu_baseline:
+                cpu = cpu_baseline(cfg, x, hist, min(args.cpu_sample, x.size), pool, cores)
 
     lengths = []
     info = run_gpu(cfg, x, hist, args.steps, args.warmup, lengths)
