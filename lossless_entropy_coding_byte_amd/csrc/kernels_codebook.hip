@@ -28,8 +28,8 @@ namespace {
 
 constexpr int CB_THREADS = 256;
 
-// LUT entry t (the LUT_BITS-bit prefix t): the first code word, and how many
-// code words follow one another wholly inside these bits.
+// LUT entry t (the LUT_BITS-bit prefix t): the code word it starts with when
+// that word has at most LUT_BITS bits, else 0.
 __device__ inline void lut_entry(const uint32_t* count, const uint32_t* first, const uint32_t* base,
                                  const uint8_t* sorted, DeviceCodebook* cb, int t) {
     uint16_t entry = 0;
@@ -41,21 +41,23 @@ __device__ inline void lut_entry(const uint32_t* count, const uint32_t* first, c
         }
     }
     cb->lut[t] = entry;
-    uint32_t used = 0, cnt = 0;
-    for (;;) {
-        uint32_t len = 0;
-        for (uint32_t l = 1; l + used <= (uint32_t)LUT_BITS; ++l) {
-            const uint32_t v = ((uint32_t)t >> (LUT_BITS - used - l)) & ((1u << l) - 1u);
-            if (count[l] && v >= first[l] && v < first[l] + count[l]) {
-                len = l;
-                break;
-            }
-        }
-        if (!len) break;
-        used += len;
-        ++cnt;
-    }
-    cb->mlut[t] = (uint8_t)((cnt << 4) | used);
+}
+
+// Second-table entry i: the 16-bit window v = limit[LUT_BITS] + i, read as
+// the longer code word it starts with (its length is 1 + the number of
+// left-aligned limits at or below v), or 0 past the last code word.
+__device__ inline uint16_t lut2_entry(const uint32_t* limit, const uint32_t* first, const uint32_t* base,
+                                      const uint8_t* sorted, uint32_t i) {
+    const uint32_t v = limit[LUT_BITS] + i;
+    if (v >= limit[16]) return 0;
+    uint32_t len = 1;
+    for (int l = 1; l <= 16; ++l) len += v >= limit[l];
+    return (uint16_t)((sorted[(base[len] + (v >> (16 - len)) - first[len]) & 255u] << 8) | len);
+}
+
+__device__ inline void lut2_fields(const uint32_t* limit, DeviceCodebook* cb) {
+    cb->lut2_base = limit[LUT_BITS];
+    cb->pad[0] = cb->pad[1] = 0;
 }
 
 // Tables from the canonical description passed by value (host-built codebook).
@@ -74,9 +76,13 @@ __global__ __launch_bounds__(CB_THREADS) void codebook_kernel(CodebookArgs a, De
     if (t == 0) {
         cb->max_len = a.max_len;
         cb->num_coded = a.num_coded;
-        cb->pad[0] = cb->pad[1] = cb->pad[2] = 0;
     }
+    uint32_t limit[17];
+    limit[0] = 0;
+    for (int l = 1; l <= 16; ++l) limit[l] = (a.first[l] + a.count[l]) << (16 - l);
+    if (t == 0) lut2_fields(limit, cb);
     if (t < LUT_SIZE) lut_entry(a.count, a.first, a.base, a.sorted, cb, t);
+    if (t < LUT2_SIZE) cb->lut2[t] = lut2_entry(limit, a.first, a.base, a.sorted, (uint32_t)t);
 }
 
 struct BuildArgs {
@@ -291,7 +297,6 @@ __global__ __launch_bounds__(CB_THREADS) void build_kernel(BuildArgs a) {
     if (tid == 0) {
         cb->max_len = maxl;
         cb->num_coded = (uint32_t)ncoded;
-        cb->pad[0] = cb->pad[1] = cb->pad[2] = 0;
     }
 }
 
@@ -299,10 +304,7 @@ __global__ __launch_bounds__(CB_THREADS) void build_kernel(BuildArgs a) {
 // wrote; grid (LUT_SIZE / 256, codebooks).  A code word's length is read off
 // the left-aligned limits: the windows of length-l code words are
 // [limit[l-1], limit[l]), so the length is 1 + the number of limits at or
-// below the window (17: no code word starts here).  A window padded with
-// zeros gives the same answer for every code word that fits before the
-// padding, so the same count finds the code words that lie wholly inside the
-// LUT_BITS bits.
+// below the window (17: no code word starts here).
 __global__ __launch_bounds__(CB_THREADS) void tables_kernel(BuildArgs a) {
     __shared__ uint32_t first[17], base[17], lim[17];
     __shared__ uint8_t sorted[256];
@@ -330,14 +332,8 @@ __global__ __launch_bounds__(CB_THREADS) void tables_kernel(BuildArgs a) {
     if (l0 <= (uint32_t)LUT_BITS)
         entry = (uint16_t)((sorted[base[l0] + (t >> (LUT_BITS - l0)) - first[l0]] << 8) | l0);
     cb->lut[t] = entry;
-    uint32_t used = 0, cnt = 0;
-    for (;;) {
-        const uint32_t l = code_len((t << (16 - LUT_BITS + used)) & 0xFFFFu);
-        if (used + l > (uint32_t)LUT_BITS) break;
-        used += l;
-        ++cnt;
-    }
-    cb->mlut[t] = (uint8_t)((cnt << 4) | used);
+    if (t < LUT2_SIZE) cb->lut2[t] = lut2_entry(lim, first, base, sorted, t);
+    if (t == 0) lut2_fields(lim, cb);
 }
 
 }  // namespace

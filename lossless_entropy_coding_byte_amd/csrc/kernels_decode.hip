@@ -15,7 +15,7 @@
 //     byte per symbol written to that stream's output;
 //   * P = 2, OUT_U16 / OUT_U16_XOR: lane 2u decodes the high plane and lane
 //     2u + 1 the low plane of unit u; after every 16 symbols the pair swaps
-//     half of its bytes (one lane exchange) and each lane stores 8 restored
+//     half of its bytes (lane exchanges) and each lane stores 8 restored
 //     16-bit words (16 bytes), XORed with the other snapshot for a delta;
 //   * P = 4, OUT_U32: lanes 4u..4u+3 decode planes 0..3 (bytes 3..0 of the
 //     32-bit elements) of unit u; after every 16 symbols the quad transposes
@@ -40,9 +40,9 @@
 // global memory.  Ring slot q of lane L sits at ring[q][L]: each lane has its
 // own bank.
 //
-// A code word of at most LUT_BITS bits is one LDS lookup; longer ones use the
-// canonical per-length limits.  Every structural rule of the format is
-// checked; a violation sets status CORRUPT.
+// A code word of at most LUT_BITS bits is one LDS lookup, a longer one a
+// lookup in a second table.  Every structural rule of the format is checked;
+// a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -89,14 +89,14 @@ struct DecArgs {
 // decode table and the canonical tables of the longer code words.
 template <int NT>
 struct SharedOne {
-    uint16_t lut[1][LUT_SIZE];   // (sym << 8) | len
-    uint32_t off[17];            // base[l] - first[l]: index in `sorted` is off[l] + code
-    uint8_t sorted[256];
+    uint16_t lut[1][LUT_SIZE];   // (sym << 8) | len of the code words of at most LUT_BITS bits
+    uint16_t lut2[LUT2_SIZE];    // the same for the longer code words
     alignas(16) uint32_t ring[RING][NT];
 };
-// P streams in every workgroup: P decode tables (code words longer than
-// LUT_BITS read the canonical tables from the device codebook).  With P = 2
-// and 1024 lanes this is exactly 80 KiB, so two workgroups fill a CU's LDS.
+// P streams in every workgroup: P first tables (code words longer than
+// LUT_BITS -- rare in byte planes -- read the second table of the device
+// codebook in memory).  With P = 2 and 1024 lanes this is exactly 80 KiB, so
+// two workgroups fill a CU's LDS.
 template <int NT, int P>
 struct SharedMany {
     uint16_t lut[P][LUT_SIZE];
@@ -104,11 +104,6 @@ struct SharedMany {
 };
 template <int NT, int P>
 using Shared = std::conditional_t<P == 1, SharedOne<NT>, SharedMany<NT, P>>;
-
-// Left-aligned canonical limits of the lengths above LUT_BITS.
-struct Limits {
-    uint32_t l13, l14, l15, l16;
-};
 
 template <int NT>
 struct Reader {
@@ -208,7 +203,7 @@ struct Lane {
 };
 
 template <int P>
-__device__ inline Lane lane_stream(const DecArgs& a, uint32_t k, const uint64_t (&words)[4]) {
+__device__ inline Lane lane_stream(const DecArgs& a, uint32_t k, uint64_t payload_words) {
     Lane l;
 #define LECB_PICK(field, expr)                                            \
     if constexpr (P == 1) {                                               \
@@ -230,27 +225,26 @@ __device__ inline Lane lane_stream(const DecArgs& a, uint32_t k, const uint64_t 
     LECB_PICK(ulen_pad_from, ulen_pad_from)
     LECB_PICK(ulen_pad_to, ulen_pad_to)
 #undef LECB_PICK
-    l.payload_words = P == 1 ? words[0] : (k & 2 ? (k & 1 ? words[3] : words[2]) : (k & 1 ? words[1] : words[0]));
+    l.payload_words = payload_words;
     return l;
 }
 
 // Next code word as (sym << 8) | len, len in 1..16, from the next 32 bits
-// `top`.  An invalid code word yields len 16 and sets `inval`.
+// `top`.  An invalid code word yields len 16 and sets `inval`.  A code word
+// of at most LUT_BITS bits is one probe of the first table, a longer one one
+// probe of the second (which always holds every longer code word: at most 256
+// of them, each covering at most 2^(16 - 13) = 8 of its entries).
 template <int P, typename S>
-__device__ inline uint32_t lookup(const S& sh, const uint16_t* lut, const DeviceCodebook* cb, const Limits& L,
+__device__ inline uint32_t lookup(const S& sh, const uint16_t* lut, const DeviceCodebook* cb, uint32_t base2,
                                   uint32_t top, uint32_t& inval) {
     uint32_t e = lut[top >> (32 - LUT_BITS)];
     if (e == 0) {
-        const uint32_t v = top >> 16;
-        const uint32_t len = 13u + (v >= L.l13) + (v >= L.l14) + (v >= L.l15);
-        if (v >= L.l16) {
+        const uint32_t i = (top >> 16) - base2;
+        if constexpr (P == 1) e = i < (uint32_t)LUT2_SIZE ? sh.lut2[i] : 0u;
+        else e = i < (uint32_t)LUT2_SIZE ? cb->lut2[i] : 0u;
+        if (e == 0) {
             inval = 1;
             e = 16;
-        } else if constexpr (P == 1) {
-            e = ((uint32_t)sh.sorted[(sh.off[len] + (v >> (16 - len))) & 255u] << 8) | len;
-        } else {
-            const uint32_t idx = (cb->base[len] - cb->first[len] + (v >> (16 - len))) & 255u;
-            e = ((uint32_t)cb->sorted[idx] << 8) | len;
         }
     }
     return e;
@@ -264,11 +258,11 @@ __device__ inline uint32_t syms4(const uint32_t (&e)[4]) {
     return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
-// 16 restored 16-bit words from the high-plane bytes hi[0..3] (lane 2u) and
-// the low-plane bytes lo[0..3] (lane 2u + 1) of 16 symbols: the pair swaps
-// half of its words, then lane 2u builds words 0..7 and lane 2u + 1 words
-// 8..15 (little-endian: low byte first).
-__device__ inline v4u restore16(const uint32_t (&w)[4], uint32_t odd) {
+// 16 restored 16-bit words from the high-plane bytes of 16 symbols (lane 2u,
+// w[0..3]) and the low-plane bytes (lane 2u + 1): the pair swaps half of its
+// words, then lane 2u builds words 0..7 and lane 2u + 1 words 8..15
+// (little-endian: low byte first).
+__device__ inline v4u restore_u16(const uint32_t (&w)[4], uint32_t odd) {
     const uint32_t s0 = __shfl_xor(odd ? w[0] : w[2], 1, 64);
     const uint32_t s1 = __shfl_xor(odd ? w[1] : w[3], 1, 64);
     const uint32_t h0 = odd ? s0 : w[0], h1 = odd ? s1 : w[1];
@@ -284,25 +278,27 @@ __device__ inline v4u restore16(const uint32_t (&w)[4], uint32_t odd) {
 // 16 restored 32-bit elements from four lanes q = 0..3 holding the bytes of
 // planes 0..3 (element bytes 3..0) of 16 symbols: lane q gathers word q of
 // every plane (three exchanges) and builds elements 4q..4q+3.
-__device__ inline v4u restore32(const uint32_t (&w)[4], uint32_t q) {
-    uint32_t x[4];  // x[p] = word q of plane p
+__device__ inline v4u restore_u32(const uint32_t (&w)[4], uint32_t q) {
+    uint32_t x0 = 0, x1 = 0, x2 = 0, x3 = 0;  // word q of planes 0..3
 #pragma unroll
     for (uint32_t r = 0; r < 4; ++r) {
-        // round r: lane q reads from lane (q + r) & 3, which sends its word q
+        // round r: lane q reads lane (q + r) & 3, which sends its word (self - r) & 3
         const uint32_t src = (q + r) & 3u;
-        const uint32_t want = (q - r) & 3u;  // the word this lane sends
-        const uint32_t mine = want == 0 ? w[0] : want == 1 ? w[1] : want == 2 ? w[2] : w[3];
+        const uint32_t want = (q - r) & 3u;
+        // (masks rather than an index: the words stay in registers)
+        const uint32_t mine = (w[0] & (0u - (uint32_t)(want == 0))) | (w[1] & (0u - (uint32_t)(want == 1))) |
+                              (w[2] & (0u - (uint32_t)(want == 2))) | (w[3] & (0u - (uint32_t)(want == 3)));
         const uint32_t got = r ? __shfl(mine, (int)((threadIdx.x & ~3u) | src), 64) : mine;
-        if (src == 0) x[0] = got;
-        if (src == 1) x[1] = got;
-        if (src == 2) x[2] = got;
-        if (src == 3) x[3] = got;
+        x0 = src == 0 ? got : x0;
+        x1 = src == 1 ? got : x1;
+        x2 = src == 2 ? got : x2;
+        x3 = src == 3 ? got : x3;
     }
     // element k: bytes [x3[k], x2[k], x1[k], x0[k]] (little-endian)
-    const uint32_t a01 = __builtin_amdgcn_perm(x[0], x[1], 0x05010400u);  // x1_0 x0_0 x1_1 x0_1
-    const uint32_t b01 = __builtin_amdgcn_perm(x[0], x[1], 0x07030602u);  // x1_2 x0_2 x1_3 x0_3
-    const uint32_t a23 = __builtin_amdgcn_perm(x[2], x[3], 0x05010400u);  // x3_0 x2_0 x3_1 x2_1
-    const uint32_t b23 = __builtin_amdgcn_perm(x[2], x[3], 0x07030602u);
+    const uint32_t a01 = __builtin_amdgcn_perm(x0, x1, 0x05010400u);  // x1_0 x0_0 x1_1 x0_1
+    const uint32_t b01 = __builtin_amdgcn_perm(x0, x1, 0x07030602u);  // x1_2 x0_2 x1_3 x0_3
+    const uint32_t a23 = __builtin_amdgcn_perm(x2, x3, 0x05010400u);  // x3_0 x2_0 x3_1 x2_1
+    const uint32_t b23 = __builtin_amdgcn_perm(x2, x3, 0x07030602u);
     v4u o;
     o.x = __builtin_amdgcn_perm(a01, a23, 0x05040100u);  // x3_0 x2_0 x1_0 x0_0
     o.y = __builtin_amdgcn_perm(a01, a23, 0x07060302u);
@@ -328,24 +324,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     const uint32_t bid = P == 1 ? blockIdx.x - sidx * a.wg_per_group : blockIdx.x;
     const uint32_t k = P == 1 ? sidx : (uint32_t)tid & (P - 1);           // this lane's stream
     const uint64_t u = P == 1 ? (uint64_t)bid * NT + tid : ((uint64_t)bid * NT + tid) / P;
-    // stream sizes: given, or read from the encoder's results
-    uint64_t words[4] = {0, 0, 0, 0};
-    bool size_bad[4] = {false, false, false, false};
+    // stream sizes: given, or read from the encoder's results (this lane's
+    // stream picked by conditional moves, not by an index into an array)
+    uint64_t my_words = 0;
+    bool my_size_bad = false;
 #pragma unroll
     for (int q = 0; q < (P == 1 ? 1 : P); ++q) {
         const uint32_t s = P == 1 ? sidx : (uint32_t)q;
         const DecStream& d = a.st[s];
         uint64_t w = d.payload_words;
+        bool sb = false;
         if (a.sizes) {
             const uint64_t bytes = a.sizes[s].bytes;
-            size_bad[q] = a.sizes[s].status != 0 || bytes < d.header_bytes + 4 || ((bytes - d.header_bytes) & 3) != 0;
-            w = size_bad[q] ? 0 : (bytes - d.header_bytes) / 4;
+            sb = a.sizes[s].status != 0 || bytes < d.header_bytes + 4 || ((bytes - d.header_bytes) & 3) != 0;
+            w = sb ? 0 : (bytes - d.header_bytes) / 4;
         }
-        words[q] = w;
+        const bool mine = P == 1 || (uint32_t)q == k;
+        my_words = mine ? w : my_words;
+        my_size_bad = mine ? sb : my_size_bad;
     }
-    const Lane ln = lane_stream<P>(a, k, words);
-    const bool my_size_bad = P == 1 ? size_bad[0] : (k & 2 ? (k & 1 ? size_bad[3] : size_bad[2]) : (k & 1 ? size_bad[1] : size_bad[0]));
-
+    const Lane ln = lane_stream<P>(a, k, my_words);
     // ---- tables
     {
 #pragma unroll
@@ -356,16 +354,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             for (int i = tid; i < NV; i += NT) dst[i] = src[i];
         }
         if constexpr (P == 1) {
-            const DeviceCodebook* cb = a.st[sidx].cb;
-            if (tid < 17) S.off[tid] = cb->base[tid] - cb->first[tid];
-            if (tid < 256) S.sorted[tid] = cb->sorted[tid];
+            const v4u* src2 = reinterpret_cast<const v4u*>(a.st[sidx].cb->lut2);
+            v4u* dst2 = reinterpret_cast<v4u*>(S.lut2);
+            for (int i = tid; i < LUT2_SIZE * 2 / 16; i += NT) dst2[i] = src2[i];
         }
     }
-    Limits L;
-    L.l13 = ln.cb->limit[13];
-    L.l14 = ln.cb->limit[14];
-    L.l15 = ln.cb->limit[15];
-    L.l16 = ln.cb->limit[16];
+    const uint32_t base2 = ln.cb->lut2_base;
 
     // ---- unit geometry and the stream's structure around it
     const uint32_t K = 1u << a.log2k;
@@ -440,7 +434,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int i = 2 * q + h;
-                const uint32_t e = lookup<P>(S, lut, ln.cb, L, r.peek(), inval);
+                const uint32_t e = lookup<P>(S, lut, ln.cb, base2, r.peek(), inval);
                 r.off += e & 0xFFu;
                 ev[i & 3] = e;
                 if ((i & 3) == 3) w[i >> 2] = syms4(ev);
@@ -454,12 +448,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             v.w = w[3];
             *reinterpret_cast<v4u*>(ln.out + e0 + 16 * g) = v;
         } else if constexpr (OUT == DEC_OUT_U16 || OUT == DEC_OUT_U16_XOR) {
-            v4u v = restore16(w, k);
+            v4u v = restore_u16(w, k);
             const uint64_t at = 2 * (e0 + 16 * g) + 16 * k;
             if constexpr (OUT == DEC_OUT_U16_XOR) v ^= *reinterpret_cast<const v4u*>(a.w0 + at);
             *reinterpret_cast<v4u*>(a.merged + at) = v;
         } else {
-            const v4u v = restore32(w, k);
+            const v4u v = restore_u32(w, k);
             *reinterpret_cast<v4u*>(a.merged + 4 * (e0 + 16 * g) + 16 * k) = v;
         }
     }
@@ -469,7 +463,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         for (uint32_t i = 0; i < rem; ++i) {
             if ((i & 3) == 0) r.tick();
             r.refill();
-            const uint32_t e = lookup<P>(S, lut, ln.cb, L, r.peek(), inval);
+            const uint32_t e = lookup<P>(S, lut, ln.cb, base2, r.peek(), inval);
             r.off += e & 0xFFu;
             const uint64_t el = e0 + 16 * ngrp + i;
             const uint8_t sym = (uint8_t)(e >> 8);

@@ -12,6 +12,11 @@ namespace lecb {
 // ones go through the canonical per-length limits.
 constexpr int LUT_BITS = 12;
 constexpr int LUT_SIZE = 1 << LUT_BITS;
+// Code words longer than LUT_BITS: a second table indexed by the next 16 bits
+// minus limit[LUT_BITS] (the left-aligned start of the longer code words).
+// It holds all of them: at most 256 code words of 13..16 bits cover at most
+// 256 * 2^(16-13) = LUT2_SIZE of the 16-bit values.
+constexpr int LUT2_SIZE = 2048;
 
 struct DeviceCodebook {
     uint32_t enc[256];        // (code << 5) | len ; len 0 = byte has no code word
@@ -20,11 +25,12 @@ struct DeviceCodebook {
     uint32_t first[17];       // first canonical code of length l
     uint32_t base[17];        // index in `sorted` of the first symbol of length l
     uint8_t sorted[256];      // coded symbols by (length, byte value)
-    uint8_t mlut[LUT_SIZE];   // next LUT_BITS bits -> (count << 4) | bits: the code words that lie
-                              // wholly inside them, greedily from the top; 0 when the first is longer
+    uint16_t lut2[LUT2_SIZE]; // next 16 bits v -> (sym << 8) | len for v - lut2_base < LUT2_SIZE,
+                              // len > LUT_BITS; 0 = no code word
     uint32_t max_len;
     uint32_t num_coded;
-    uint32_t pad[3];
+    uint32_t lut2_base;       // limit[LUT_BITS]
+    uint32_t pad[2];
 };
 static_assert(sizeof(DeviceCodebook) % 16 == 0, "device codebook must stay 16-byte sized");
 
