@@ -48,15 +48,17 @@ from .stream import (
     table_bytes,
     encoded_bound,
     header_bytes,
-    ulen_bytes,
-    unit_ranges,
-    units_per_chunk,
-    unit_meta_span,
+    count_bytes,
+    lanes_per_chunk,
+    lane_symbol_counts,
+    lane_positions,
+    count_span,
     encode_bitstring,
     encode,
     decode_bitwise,
     decode,
     chunk_word_counts,
+    lane_bit_counts,
     parse_table,
 )
 from .bytegroup import (split_bf16, merge_bf16, encode_bf16, decode_bf16, container_bytes, parse_container,
@@ -68,8 +70,8 @@ from .drift import payload_bits_or_none, drift_check, adaptive_codebooks
 __all__ = [
     "histogram", "codebook_frequencies", "package_merge_lengths", "canonical_codes",
     "kraft_sum_scaled", "OracleError", "CorruptStream", "UncodedSymbol", "num_chunks",
-    "table_bytes", "header_bytes", "ulen_bytes", "unit_ranges", "units_per_chunk", "unit_meta_span", "encoded_bound", "encode_bitstring", "encode", "decode_bitwise", "decode",
-    "chunk_word_counts", "parse_table", "split_bf16", "merge_bf16", "encode_bf16", "decode_bf16",
+    "table_bytes", "header_bytes", "count_bytes", "lanes_per_chunk", "lane_symbol_counts", "lane_positions", "count_span", "encoded_bound", "encode_bitstring", "encode", "decode_bitwise", "decode",
+    "chunk_word_counts", "lane_bit_counts", "parse_table", "split_bf16", "merge_bf16", "encode_bf16", "decode_bf16",
     "container_bytes", "parse_container", "entropy_bits", "payload_bits_identity",
     "per_batch_optimal_bits", "snapshot_delta", "apply_delta", "payload_bits_or_none", "drift_check",
     "adaptive_codebooks", "split_fp32", "merge_fp32", "encode_fp32", "decode_fp32", "subbyte",

@@ -109,8 +109,8 @@ def compare_chunk_run(stream, n, chunk, c0, ref, ref_n):
     if not np.array_equal(got, rt):
         bad = int(np.argmax(got != rt))
         raise AssertionError(f"offset table differs at chunk {c0 + bad}")
-    a, b = oracle.unit_meta_span(n, chunk, c0, c0 + nb)
-    ra, rb = oracle.unit_meta_span(ref_n, chunk, 0, nb)
+    a, b = oracle.count_span(n, chunk, c0, c0 + nb)
+    ra, rb = oracle.count_span(ref_n, chunk, 0, nb)
     if not np.array_equal(stream[a:b], ref[ra:rb]):
         raise AssertionError(f"unit metadata differs in chunks [{c0}, {c0 + nb})")
     hb, rhb = oracle.header_bytes(n, chunk), oracle.header_bytes(ref_n, chunk)

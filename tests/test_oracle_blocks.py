@@ -38,7 +38,7 @@ def test_blocks_catch_any_changed_part():
     whole, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), chunk)
     blocks = oracle_jobs.encode_blocks(x, ln, chunk)
     nc = oracle.num_chunks(n, chunk)
-    a, _ = oracle.unit_meta_span(n, chunk, 0, nc - (nc % 2))
+    a, _ = oracle.count_span(n, chunk, 0, nc - (nc % 2))
     hb = oracle.header_bytes(n, chunk)
     for where in (4 * (nc // 2), a + 3, hb + 5, whole.size - 1):
         bad = whole.copy()

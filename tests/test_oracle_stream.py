@@ -46,16 +46,24 @@ def test_two_encoders_and_two_decoders_agree(name, n, chunk, gen):
     assert np.array_equal(y1, x) and np.array_equal(y2, x)
 
 
-def test_uniform_code_closed_form_byteswap():
-    # All 256 lengths 8 -> code[s] = s; each payload word holds 4 input bytes MSB first,
-    # so the payload is the input with every aligned 4-byte group reversed.
+def test_uniform_code_closed_form_block_transpose():
+    # All 256 lengths 8 -> code[s] = s, so every word holds 4 input bytes MSB first
+    # (the aligned 4-byte group reversed).  Chunk 4096 -> 16 lanes of 256 bytes; every
+    # pair takes 16 bits, so each lane reads word k >= 2 before pair 2(k-1) and all
+    # lanes read in step: the chunk's payload is word k of lanes 0..15, k = 0..63.
+    # Lane j's word k is word k%4 of block (k//4)*16 + j, so the payload is the
+    # chunk's byte-reversed words with the block index and the word-in-lane swapped.
     x = workloads.uniform_bytes(5, 4096 * 3)
     ln = np.full(256, 8, np.uint8)
     s, bits = encode(x, ln, canonical_codes(ln), 4096)
     tb = oracle.header_bytes(x.size, 4096)
     assert bits == 8 * x.size
-    assert np.array_equal(s[tb:], x.view(">u4").astype("<u4").view(np.uint8))
+    natural = x.view(">u4").astype(np.int64).reshape(3, 16, 16, 4)   # chunk, block row, lane, word
+    k, j = np.meshgrid(np.arange(64), np.arange(16), indexing="ij")
+    want = natural[:, k // 4, j, k % 4]                               # chunk, k, j
+    assert np.array_equal(s[tb:].view("<u4").astype(np.int64), want.ravel())
     assert list(s[:12].view("<u4")) == [1024, 2048, 3072]
+    assert np.all(s[16:16 + 3 * 32].view("<u2") == 64)               # 64 words per lane
 
 
 def test_golden_streams():
@@ -104,7 +112,7 @@ def _corruptions():
 
 def test_corrupt_streams_detected():
     x, ln, s = _corruptions()
-    n, chunk = x.size, 1024
+    n, chunk = x.size, 1024            # 5 chunks of 4 lanes, the last one 904 symbols
     tb = oracle.header_bytes(n, chunk)
     gb = oracle.table_bytes(n, chunk)
     bad = []
@@ -113,21 +121,40 @@ def test_corrupt_streams_detected():
     bad.append(("truncated", s[:-4].copy()))
     bad.append(("extra word", np.concatenate([s, np.zeros(4, np.uint8)])))
     t = s.copy(); t[4 * 5] = 1; bad.append(("table padding", t))
-    # flip the lowest bit of chunk 0's last word: it is padding (chunk 0 ends mid-word by construction below)
-    ends = s[:4 * 5].view("<u4")
-    bits0 = int(oracle.stream.chunk_bit_counts(x[:chunk], ln, chunk)[0])
-    if bits0 % 32:
-        t = s.copy(); off = tb + 4 * (int(ends[0]) - 1); t[off] |= 1; bad.append(("padding bit", t))
-    # unit bit counts: chunk 0 has K = 4 units; move one bit from unit 0 to unit 1
-    # (same chunk total), then change the padding after the counts
+    # word counts: move one word from lane 0 to lane 1 of chunk 0 (same chunk total)
     t = s.copy(); u = t[gb:gb + 4].view("<u2").copy(); u[0] -= 1; u[1] += 1
-    t[gb:gb + 4] = u.view(np.uint8); bad.append(("unit count", t))
-    t = s.copy(); t[tb - 1] = 0x01; bad.append(("unit count padding", t))
+    t[gb:gb + 4] = u.view(np.uint8); bad.append(("word count moved", t))
+    # one word more for lane 0 and one less in the chunk's last word ... the totals disagree
+    t = s.copy(); u = t[gb:gb + 2].view("<u2").copy(); u[0] += 1
+    t[gb:gb + 2] = u.view(np.uint8); bad.append(("word count total", t))
+    t = s.copy(); t[tb - 1] = 0x01; bad.append(("word count padding", t))
     for name, t in bad:
         with pytest.raises(CorruptStream):
             decode(t, ln, chunk, n)
         with pytest.raises(CorruptStream):
             decode_bitwise(t, ln, chunk, n)
+
+
+def test_corrupt_padding_and_empty_lanes():
+    # Golden B7 (chunk 512, 2 lanes): lane 1's last word is 16 zero code bits and 16
+    # bits of padding, and it is the chunk's last word; its lowest bit is padding.
+    ex = next(e for e in load_golden() if e["name"].startswith("B7"))
+    ln, n, s = ex["lengths"], ex["input"].size, ex["stream"]
+    t = s.copy(); t[-4] |= 1
+    # B6 (chunk 1024, 300 symbols): lane 3 of 4 holds 64 symbols; give it no words and
+    # lane 2 one more (same total) -> a lane with symbols and no words
+    b6 = next(e for e in load_golden() if e["name"].startswith("B6"))
+    u = b6["stream"].copy(); u[16 + 4] += 1; u[16 + 6] = 0
+    # a chunk of 300 symbols at chunk 4096 has lanes 1..15 empty: B1-like stream with a
+    # word moved to an empty lane
+    b1 = next(e for e in load_golden() if e["name"] == "B1 no ties, one chunk")
+    v = b1["stream"].copy(); v[16] = 0; v[18] = 1
+    for stream, lens, nn, ch in ((t, ln, n, ex["chunk"]), (u, b6["lengths"], 300, 1024),
+                                 (v, b1["lengths"], b1["input"].size, 4096)):
+        with pytest.raises(CorruptStream):
+            decode(stream, lens, ch, nn)
+        with pytest.raises(CorruptStream):
+            decode_bitwise(stream, lens, ch, nn)
 
 
 def test_incomplete_code_rejects_unmatched_prefix():
@@ -156,27 +183,32 @@ def test_chunks_are_independent():
         piece = x[c * 512:(c + 1) * 512]
         one, _ = encode(piece, ln, cd, 512)
         assert np.array_equal(one[32:], s[tb + 4 * starts[c]: tb + 4 * ends[c]])
-        a, b = oracle.unit_meta_span(x.size, 512, c, c + 1)
-        a1, b1 = oracle.unit_meta_span(piece.size, 512, 0, 1)
-        assert np.array_equal(one[a1:b1], s[a:b])  # K = 2 counts per chunk
+        a, b = oracle.count_span(x.size, 512, c, c + 1)
+        a1, b1 = oracle.count_span(piece.size, 512, 0, 1)
+        assert np.array_equal(one[a1:b1], s[a:b])  # G = 2 counts per chunk
 
 
-def test_unit_counts_are_the_units_code_bits():
-    # Unit j of chunk c holds symbols [c*C + 256j, c*C + 256(j+1)) (cut at the
-    # chunk's and the tensor's end); its count is the sum of their code lengths.
+def test_lane_counts_are_the_lanes_words():
+    # Block b (16 symbols) of chunk c belongs to lane b mod 16 (chunk 4096); a lane's
+    # count is ceil(sum of its code lengths / 32).  Checked with explicit loops over
+    # the blocks, independently of the encoder's sorting.
     n, chunk = 20 * 4096 + 100, 4096
     x = workloads.skewed_bytes(13, n, sigma=25)
     ln, cd = _codebook(x)
     s, bits = encode(x, ln, cd, chunk)
-    starts, ends, ulen, payload = oracle.parse_table(s, n, chunk)
-    assert ulen.shape == (21, 16)
-    first, end = oracle.unit_ranges(n, chunk)
+    starts, ends, counts, payload = oracle.parse_table(s, n, chunk)
+    assert counts.shape == (21, 16)
     lens = ln[x].astype(np.int64)
+    lane_bits = np.zeros((21, 16), np.int64)
     for c in range(21):
-        for j in range(16):
-            assert ulen[c, j] == lens[first[c, j]:end[c, j]].sum()
-    assert ulen.sum() == bits
-    assert np.all(ulen[20, 1:] == 0) and ulen[20, 0] == lens[20 * 4096:].sum()  # 100 symbols, one unit
+        for b in range(0, min(chunk, n - c * chunk), 16):
+            lane_bits[c, (b // 16) % 16] += lens[c * chunk + b: min(c * chunk + b + 16, n)].sum()
+    assert np.array_equal(counts, (lane_bits + 31) // 32)
+    assert lane_bits.sum() == bits
+    assert np.array_equal(ends - starts, counts.sum(axis=1))
+    # the last chunk's 100 symbols: blocks 0..5 full and 4 symbols in block 6 -> lanes 0..6
+    assert np.array_equal(oracle.lane_symbol_counts(n, chunk)[20], [16] * 6 + [4] + [0] * 9)
+    assert np.all(counts[20, 7:] == 0) and np.all(counts[20, :7] > 0)
 
 
 @pytest.mark.parametrize("n,chunk,L", [(1000003, 4096, 16), (5000, 1024, 9), (300, 256, 12), (65536 * 2 + 7, 65536, 16)])
@@ -207,3 +239,9 @@ def test_encoded_bound_hand_value():
     # words 3 * ceil(256*9/32) + ceil(232*9/32) = 3*72 + 66 = 282 -> 1128; 16 + 16 + 1128
     # = 1160 = 72 * 16 + 8, rounded up to 1168.
     assert oracle.encoded_bound(1000, 256, 9) == 1168
+    # chunk 4096, L = 3, n = 4136: chunk 0 = 16 lanes x 256 x 3 bits = 24 words each
+    # (384); chunk 1 = 40 symbols = blocks 0, 1 (16 each, lanes 0 and 1: 48 bits -> 2
+    # words) and block 2 (8 symbols, lane 2: 24 bits -> 1 word) = 5 words (a per-chunk
+    # rounding would give ceil(120/32) = 4).  389 words = 1556 bytes; table 16, counts
+    # 2*16*2 = 64: 1636 -> 1648.
+    assert oracle.encoded_bound(4136, 4096, 3) == 1648
