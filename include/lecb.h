@@ -19,19 +19,28 @@
  *    grouped the same way into four byte planes (the byte-group size is a
  *    design knob of the same page, Key design item 1).
  *
- * Stream format v2 (identical, bit for bit, to the oracle's):
- *   stream  = u32 end[nc] | zero pad to 16 B | u16 ulen[nc*K] | zero pad to 16 B | u32 payload[W]
+ * Stream format v3 (identical, bit for bit, to the oracle's):
+ *   stream  = u32 end[nc] | zero pad to 16 B | u16 nw[nc*G] | zero pad to 16 B | u32 payload[W]
  *   nc      = ceil(n / chunk); chunk c holds symbols [c*chunk, min((c+1)*chunk, n));
+ *   lanes   = G = min(chunk/256, 16) per chunk: the chunk's blocks of 16
+ *             symbols (the last one shorter) go round-robin to the lanes,
+ *             block b to lane b mod G;
+ *   lane    = its symbols' code words concatenated, most significant bit
+ *             first, in 32-bit words, the last one zero-padded; nw[c*G + j]
+ *             = the words of lane j of chunk c (0 for a lane with no symbols);
+ *   payload = per chunk, its lanes' words in the order a lane-parallel
+ *             decoder reads them: every lane's word 0, then every lane's
+ *             word 1 (lane order, only words that exist), then, pair of
+ *             symbols by pair, a lane's word k >= 2 just before its first pair
+ *             that starts at or after bit 32(k-1) of the lane (lane order
+ *             within a pair); words stored little-endian;
  *   end[c]  = payload word one past chunk c's last word (chunk c spans
  *             [end[c-1], end[c]) with end[-1] = 0); W = end[nc-1];
- *   payload = per chunk, the code words of its symbols concatenated, most
- *             significant bit first within 32-bit words (words stored
- *             little-endian), starting on a fresh word, last word zero-padded;
- *   ulen    = K = chunk/256 decode units per chunk, unit j = the chunk's
- *             symbols [256j, 256j+256) (empty past n); ulen[c*K + j] = the
- *             code bits of unit j, so unit j starts at bit
- *             ulen[c*K] + ... + ulen[c*K + j-1] of its chunk;
- *   size    = align16(4*nc) + align16(2*nc*K) + 4*W  (0 when n == 0).
+ *   size    = align16(4*nc) + align16(2*nc*G) + 4*W  (0 when n == 0).
+ * The lanes are the independent parallel tasks of "Lossless Compression for
+ * LLM Tensor Incremental Snapshots", Key design item 3; the layout is this
+ * library's choice (the pages fix none): lanes of a chunk write neighbouring
+ * output blocks and read one shared, sequential word stream.
  * The codebook is not in the stream.  Code words are canonical: they follow
  * from the 256 code lengths alone (shorter codes first, ties by symbol).
  *
@@ -67,9 +76,10 @@
 extern "C" {
 #endif
 
-#define LECB_ABI_VERSION 2u
+#define LECB_ABI_VERSION 3u
 #define LECB_MAX_CODE_LEN 16u
-#define LECB_UNIT_SYMBOLS 256u
+#define LECB_LANE_SYMBOLS 256u   /* a chunk has one lane per 256 symbols ... */
+#define LECB_LANES_MAX 16u       /* ... and at most 16 */
 #define LECB_MIN_CHUNK 256u
 #define LECB_MAX_CHUNK 65536u
 #define LECB_CONTAINER_HEADER_BYTES 560u
@@ -85,7 +95,7 @@ typedef enum {
     LECB_ERR_WORKSPACE = -6,      /* workspace too small */
     LECB_ERR_SCRATCH = -7,        /* input too large for the static scratch of lecb_encode_noalloc */
     LECB_ERR_UNCODED_SYMBOL = -16,/* device: input holds a byte whose code length is 0 */
-    LECB_ERR_CORRUPT = -17        /* device: stream is not a valid v2 stream for these arguments */
+    LECB_ERR_CORRUPT = -17        /* device: stream is not a valid v3 stream for these arguments */
 } lecb_status;
 
 /* Canonical codebook, host side.  Fully determined by len[]. */
@@ -111,11 +121,11 @@ const char* lecb_status_str(int status);
 
 /* ceil(n / chunk); 0 on a bad chunk. */
 uint64_t lecb_num_chunks(uint64_t n, uint32_t chunk);
-/* Bytes before the payload: align16(4*nc) + align16(2*nc*K). */
+/* Bytes before the payload: align16(4*nc) + align16(2*nc*G). */
 uint64_t lecb_header_bytes(uint64_t n, uint32_t chunk);
 /* Largest stream any codebook with lengths <= max_len can produce, rounded
- * up to 16 bytes: align16(header + 4 * sum over chunks of ceil(m_c*max_len/32))
- * for chunks of m_c symbols -- the size when every symbol has a max_len-bit
+ * up to 16 bytes: align16(header + 4 * sum over lanes of ceil(m*max_len/32))
+ * for lanes of m symbols -- the size when every symbol has a max_len-bit
  * code word.  0 on bad arguments. */
 uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len);
 /* Workspace bytes an encode or decode of n symbols with this chunk needs. */
@@ -218,7 +228,7 @@ int lecb_split_bf16(const uint16_t* d_in, uint64_t n, uint8_t* d_hi, uint8_t* d_
 int lecb_merge_bf16(const uint8_t* d_hi, const uint8_t* d_lo, uint64_t n, uint16_t* d_out,
                     void* stream);
 
-/* Encode n bytes with an uploaded codebook into a v2 stream ("Single-Stage
+/* Encode n bytes with an uploaded codebook into a v3 stream ("Single-Stage
  * Huffman Encoder for ML Compression", Methodology step 4).  out_capacity must
  * be at least lecb_header_bytes(n, chunk); a payload that does not fit sets
  * status CAPACITY (lecb_encoded_bound gives a size that always fits).
@@ -227,17 +237,17 @@ int lecb_encode(const uint8_t* d_in, uint64_t n, const void* d_blob, uint32_t ch
                 uint8_t* d_out, uint64_t out_capacity, lecb_result* d_res, void* d_ws,
                 uint64_t ws_bytes, void* stream);
 
-/* Decode a v2 stream of n symbols into d_out[n] (reverse path of "Lossless
+/* Decode a v3 stream of n symbols into d_out[n] (reverse path of "Lossless
  * Compression for LLM Tensor Incremental Snapshots", Technical framework).
  * stream_bytes must be the exact stream size (lecb_result.bytes of the
  * encode).  The buffer must be readable up to align16(stream_bytes) (the
  * decoder fetches whole 16-byte groups; bytes past stream_bytes are ignored).  A size below the header or not a whole
  * number of payload words returns LECB_ERR_CORRUPT at once.  A stream that is not exactly what
  * lecb_encode produces for these arguments sets status CORRUPT (offset table
- * not increasing or past the stream, a bit pattern with no code word, a code
- * word crossing its chunk's end, a unit whose code words do not take exactly
- * its stored bit count, a chunk whose bit counts disagree with its words,
- * non-zero padding, too many words). */
+ * not increasing or past the stream, lane word counts that disagree with
+ * their chunk's words or give words to an empty lane, a bit pattern with no
+ * code word, a code word past its lane's last word, a lane word that is
+ * never needed, non-zero padding). */
 int lecb_decode(const uint8_t* d_stream, uint64_t stream_bytes, const void* d_blob,
                 uint32_t chunk, uint64_t n, uint8_t* d_out, lecb_result* d_res, void* d_ws,
                 uint64_t ws_bytes, void* stream);
@@ -256,7 +266,7 @@ int lecb_decode_from_result(const uint8_t* d_stream, const lecb_result* d_enc_re
  * device array of LECB_NOALLOC_SCRATCH_BYTES that the library holds on every
  * GPU it runs on until the process ends; inputs up to
  * lecb_workspace_bytes(n, chunk) <= LECB_NOALLOC_SCRATCH_BYTES fit (about
- * 250 Mi symbols at chunk 4096), larger ones return LECB_ERR_SCRATCH before
+ * 4 Gi symbols at chunk 4096), larger ones return LECB_ERR_SCRATCH before
  * any work is enqueued.  The stream, d_res and every other rule are those of
  * lecb_encode.  All calls on one GPU share its array: calls that overlap in
  * time on one GPU (different streams or host threads) race and must be

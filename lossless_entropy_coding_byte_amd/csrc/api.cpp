@@ -39,11 +39,11 @@ uint64_t num_chunks_checked(uint64_t n, uint32_t chunk) {
 
 uint64_t header_of(uint64_t n, uint32_t chunk) {
     const uint64_t nc = num_chunks_checked(n, chunk);
-    return nc ? table_bytes(nc) + ulen_bytes(nc, chunk) : 0;
+    return nc ? table_bytes(nc) + count_bytes(nc, chunk) : 0;
 }
 
 uint64_t ws_bytes_of(uint64_t n, uint32_t chunk) {
-    return ws_total_bytes(n, num_chunks_checked(n, chunk));
+    return ws_total_bytes(num_chunks_checked(n, chunk));
 }
 
 int build_args(const lecb_codebook* cb, CodebookArgs* a) {
@@ -110,8 +110,6 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
         L.st[1].res = d_res + 1;
         L.st[1].ws = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + ws_stream_bytes(nc));
     }
-    L.counts = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_ws) + 2 * ws_stream_bytes(nc));
-    L.grid = 0;  // the encoder sizes its persistent grid from the device
     return launch_encode(L, stream);
 }
 
@@ -158,7 +156,7 @@ int decode_common(int ns, int kind, const uint8_t* const* d_stream, const uint64
         L.cb[k] = reinterpret_cast<const DeviceCodebook*>(d_blob[k]);
         L.out[k] = kind == DEC_OUT_PLANES ? d_out[k] : nullptr;
         L.res[k] = d_res + k;
-        L.ws[k] = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + ws_header_offset(k, n, nc));
+        L.ws[k] = reinterpret_cast<WsHeader*>(static_cast<uint8_t*>(d_ws) + ws_header_offset(k, nc));
     }
     L.chunk = chunk;
     L.n = n;
@@ -231,9 +229,17 @@ uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len) {
     if (!valid_chunk(chunk) || max_len < 1 || max_len > 16) return 0;
     const uint64_t nc = num_chunks_checked(n, chunk);
     if (!nc) return 0;
-    // chunk c of m_c symbols takes at most ceil(m_c * max_len / 32) words
-    const uint64_t last = n - (nc - 1) * chunk;
-    const uint64_t words = (nc - 1) * (((uint64_t)chunk * max_len + 31) / 32) + (last * max_len + 31) / 32;
+    // a lane of m symbols takes at most ceil(m * max_len / 32) words; every
+    // chunk but the last has G lanes of chunk / G symbols
+    const uint64_t G = lanes_per_chunk(chunk);
+    uint64_t words = (nc - 1) * G * (((uint64_t)chunk / G * max_len + 31) / 32);
+    const uint64_t last = n - (nc - 1) * chunk;   // symbols of the last chunk
+    const uint64_t full = last / 16, rest = last % 16;
+    for (uint64_t j = 0; j < G; ++j) {
+        const uint64_t whole = full > j ? (full - j + G - 1) / G : 0;
+        const uint64_t m = whole * 16 + ((full % G) == j && rest ? rest : 0);
+        words += (m * max_len + 31) / 32;
+    }
     return align16(header_of(n, chunk) + 4 * words);
 }
 

@@ -1,71 +1,65 @@
-// Huffman decode of stream format v2 back to bytes, and back to 16-bit or
-// 32-bit elements when the byte groups are decoded together.
+// Huffman decode of stream format v3 back to bytes, and back to 16-bit or
+// 32-bit elements when the byte planes are decoded together.
 //
 // Reverse path of "Lossless Compression for LLM Tensor Incremental
 // Snapshots", Technical framework (read, Huffman-decode, restore the byte
 // groups); the independent parallel tasks of its Key design item 3 are the
-// decode units: unit j of a chunk is its symbols [256j, 256j + 256), and the
-// stored code-bit counts of the chunk's units give every unit's first bit.
+// lanes of the format.
 //
-// One lane per unit and byte plane.  P planes of the same element are coded
-// as P streams whose units cover the same symbols, so the P lanes of a unit
-// (neighbouring lanes of one wave) produce the P bytes of the same 256
-// elements in lockstep:
-//   * P = 1, OUT_PLANES: each stream's units in workgroups of their own, one
-//     byte per symbol written to that stream's output;
-//   * P = 2, OUT_U16 / OUT_U16_XOR: lane 2u decodes the high plane and lane
-//     2u + 1 the low plane of unit u; after every 16 symbols the pair swaps
-//     half of its bytes (lane exchanges) and each lane stores 8 restored
-//     16-bit words (16 bytes), XORed with the other snapshot for a delta;
-//   * P = 4, OUT_U32: lanes 4u..4u+3 decode planes 0..3 (bytes 3..0 of the
-//     32-bit elements) of unit u; after every 16 symbols the quad transposes
-//     its words and each lane stores 4 restored elements.
+// One hardware lane runs one lane of the format (lane geometry: lanes.hpp);
+// a wave decodes one task, 4 rows of 16 lanes:
+//   * P = 1, OUT_PLANES: the rows hold lanes of one stream, one byte per
+//     symbol written to that stream's output (a stream's tasks run in
+//     workgroups of their own);
+//   * P = 2, OUT_U16 / OUT_U16_XOR: rows 2g and 2g + 1 decode the high and the
+//     low plane of the same chunks; after every block of 16 symbols lanes L
+//     and L ^ 16 swap half of their bytes and each stores 8 restored 16-bit
+//     words (16 bytes), XORed with the other snapshot for a delta;
+//   * P = 4, OUT_U32: rows 0..3 decode planes 0..3 (bytes 3..0 of the 32-bit
+//     elements) of the same chunks; after every block the four lanes i,
+//     16 + i, 32 + i, 48 + i transpose their words and each stores 4 restored
+//     elements.
+// The lanes of a row write neighbouring blocks: a row's block stores cover
+// 256 contiguous bytes of output per plane.
 //
-// Per lane:
-//   1. its unit's first bit = the sum of the bit counts of the chunk's
-//      earlier units (a segmented scan over the workgroup's lanes: a chunk's
-//      units never straddle workgroups);
-//   2. decode the unit's symbols (256, fewer only at the end of the tensor)
-//      from that bit; the unit must end exactly at first bit + its count, and
-//      the unit holding the chunk's last symbol checks the zero padding to
-//      the end of the chunk's last word.
+// Reading: the G lanes of a chunk consume one sequential word stream, the
+// chunk's payload, in the format's read order.  Each group keeps a ring of
+// 16G payload words in LDS, filled by group-wide loads of consecutive words
+// (16 bytes per lane, 4G words per load); before every pair of symbols the
+// lanes whose first window word is used up take the next words of the ring,
+// in lane order (a count over the group's lanes gives each its word).  The
+// ring is topped up every 4 pairs: the load issued at one top-up is written
+// to the ring at the next, and a load is issued only when the ring has room
+// for it; 4 pairs read at most 4G words, so every word read is in the ring.
 //
-// Bit reader: a window of two payload words and a bit offset into it; before
-// every pair of code words the window slides by one word when its first word
-// is used up (no branch).  Afterwards the offset is below 32, so the window
-// holds >= 33 bits, enough for two code words of at most 16 bits.  The words
-// come from a per-lane ring of 16 payload words in LDS; the ring is topped up
-// on a fixed schedule (every 4 refills) by one 32-byte global load whose data
-// go into the ring at the next top-up, so the decode loop never waits on
-// global memory.  Ring slot q of lane L sits at ring[q][L]: each lane has its
-// own bank.
-//
-// A code word of at most LUT_BITS bits is one LDS lookup, a longer one a
-// lookup in a second table.  Every structural rule of the format is checked;
-// a violation sets status CORRUPT.
+// Bit reader: a window of two words and a bit offset into it; before every
+// pair the window slides by one word when its first word is used up.
+// Afterwards the offset is below 32 and the window holds > 32 bits, enough
+// for two code words of at most 16 bits.  A code word of at most LUT_BITS
+// bits is one LDS lookup, a longer one a lookup in a second table.  Every
+// structural rule of the format is checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
 
-#include "lecb_internal.hpp"
+#include "lanes.hpp"
 
 namespace lecb {
 
 namespace {
 
-constexpr uint32_t RING = 16;   // payload words per lane in LDS
-constexpr uint32_t UNIT = LECB_UNIT_SYMBOLS;
+constexpr uint32_t ROW_WORDS = 256;   // ring words per row of 16 lanes (16 per lane)
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 struct DecStream {
     const uint32_t* table;
-    const uint16_t* ulen;
+    const uint16_t* nw;
     const uint32_t* payload;
     uint64_t payload_words;   // words present in the caller's buffer
     const DeviceCodebook* cb;
     uint64_t header_bytes;
     uint64_t table_pad_from, table_pad_to;   // stream bytes that must be zero
-    uint64_t ulen_pad_from, ulen_pad_to;
+    uint64_t nw_pad_from, nw_pad_to;
     const uint8_t* stream;
     uint8_t* out;             // OUT_PLANES: the decoded bytes of this stream
     lecb_result* res;
@@ -75,7 +69,6 @@ struct DecStream {
 struct DecArgs {
     const lecb_result* sizes;  // non-null: stream k's size is sizes[k].bytes (an encoder's result)
     uint32_t chunk;
-    uint32_t log2k;
     uint64_t n;
     uint64_t nc;
     uint32_t wg_per_group;     // OUT_PLANES: workgroups of one stream; stream = blockIdx.x / wg_per_group
@@ -85,145 +78,59 @@ struct DecArgs {
     DecStream st[4];
 };
 
-// One stream's tables in a workgroup with one stream per workgroup: the
-// decode table and the canonical tables of the longer code words.
-template <int NT>
+// One stream per workgroup: its decode table and the table of the longer code words.
+template <int NW>
 struct SharedOne {
     uint16_t lut[1][LUT_SIZE];   // (sym << 8) | len of the code words of at most LUT_BITS bits
     uint16_t lut2[LUT2_SIZE];    // the same for the longer code words
-    alignas(16) uint32_t ring[RING][NT];
+    alignas(16) uint32_t ring[NW][4][ROW_WORDS];
 };
 // P streams in every workgroup: P first tables (code words longer than
 // LUT_BITS -- rare in byte planes -- read the second table of the device
-// codebook in memory).  With P = 2 and 1024 lanes this is exactly 80 KiB, so
+// codebook in memory).  With P = 2 and 16 waves this is exactly 80 KiB, so
 // two workgroups fill a CU's LDS.
-template <int NT, int P>
+template <int NW, int P>
 struct SharedMany {
     uint16_t lut[P][LUT_SIZE];
-    alignas(16) uint32_t ring[RING][NT];
+    alignas(16) uint32_t ring[NW][4][ROW_WORDS];
 };
-template <int NT, int P>
-using Shared = std::conditional_t<P == 1, SharedOne<NT>, SharedMany<NT, P>>;
+template <int NW, int P>
+using Shared = std::conditional_t<P == 1, SharedOne<NW>, SharedMany<NW, P>>;
 
-template <int NT>
-struct Reader {
-    uint32_t* ring;      // &ring[0][lane]
-    const uint32_t* p;   // payload
-    uint64_t sw;         // chunk's first payload word
-    uint64_t gmax;       // last readable 4-word group of the payload
-    uint32_t sh;         // sw mod RING
-    uint32_t rq;         // sh + index (relative to sw) of the word held in nextw;
-                         // w1 is the word before it, w0 the one before that
-    uint32_t wr;         // next word (relative to sw) to load; sw + wr is a multiple of 8
-    uint32_t w0, w1;     // 64-bit window; the next bit is bit `off` from the top of w0
-    uint32_t off;        // < 32 after refill()
-    uint32_t nextw;
-    v4u pa, pb;          // loaded, not yet in the ring
-    bool pend;
-
-    __device__ inline uint32_t& slot(uint32_t w) {  // w relative to sw
-        return ring[((w + sh) & (RING - 1)) * NT];
-    }
-    __device__ inline uint32_t rd() const { return rq - sh; }
-    __device__ inline v4u ld4(uint64_t g) const {
-        return *reinterpret_cast<const v4u*>(p + 4 * (g < gmax ? g : gmax));
-    }
-    __device__ inline void put8(uint32_t w, const v4u& x, const v4u& y) {
-        uint32_t* s = &slot(w);  // w..w+7 are consecutive slots (sw + w is a multiple of 8)
-        s[0 * NT] = x.x;
-        s[1 * NT] = x.y;
-        s[2 * NT] = x.z;
-        s[3 * NT] = x.w;
-        s[4 * NT] = y.x;
-        s[5 * NT] = y.y;
-        s[6 * NT] = y.z;
-        s[7 * NT] = y.w;
-    }
-    // Ring top-up: commit the previous load, issue the next one when there is
-    // room.  Between two top-ups at most 4 words leave the ring, and after a
-    // top-up at least 5 committed words lie at or after rd, so the word read
-    // by refill() is always in the ring.
-    __device__ inline void tick() {
-        if (pend) {
-            put8(wr - 8, pa, pb);
-            pend = false;
-        }
-        if (wr - rd() <= 8) {
-            const uint64_t g = (sw + wr) >> 2;
-            pa = ld4(g);
-            pb = ld4(g + 1);
-            wr += 8;
-            pend = true;
-        }
-    }
-    // Position the reader at bit `bit` of the chunk (synchronous 16-word load).
-    __device__ inline void start(uint32_t bit) {
-        const uint32_t word = bit >> 5;
-        const uint64_t a = (sw + word) & ~uint64_t(7);
-        wr = (uint32_t)(a - sw);
-        put8(wr, ld4(a >> 2), ld4((a >> 2) + 1));
-        put8(wr + 8, ld4((a >> 2) + 2), ld4((a >> 2) + 3));
-        wr += 16;
-        pend = false;
-        w0 = slot(word);
-        w1 = slot(word + 1);
-        rq = word + 2 + sh;
-        nextw = ring[(rq & (RING - 1)) * NT];
-        off = bit & 31;
-    }
-    // The next 32 bits, MSB first (all of them valid while off <= 32).
-    __device__ inline uint32_t peek() const {
-        return (uint32_t)(((((uint64_t)w0 << 32) | w1) << off) >> 32);
-    }
-    // bits consumed, relative to the chunk start
-    __device__ inline uint32_t pos() const { return 32 * (rd() - 2) + off; }
-    // Slide the window by one word once its first word is used up.  No
-    // branch; afterwards off < 32 (the caller never lets off reach 64).
-    __device__ inline void refill() {
-        const bool take = off >= 32;
-        w0 = take ? w1 : w0;
-        w1 = take ? nextw : w1;
-        off &= 31;
-        rq += take ? 1u : 0u;
-        nextw = ring[(rq & (RING - 1)) * NT];
-    }
-};
-
-// What a lane needs of its stream (selected per lane when a workgroup holds
-// several streams).
+// What a lane needs of its stream (selected per lane when a wave holds several streams).
 struct Lane {
     const uint32_t* table;
-    const uint16_t* ulen;
+    const uint16_t* nw;
     const uint32_t* payload;
     uint64_t payload_words;
     const DeviceCodebook* cb;
     uint8_t* out;
     const uint8_t* stream;
-    uint64_t table_pad_from, table_pad_to, ulen_pad_from, ulen_pad_to;
+    uint64_t table_pad_from, table_pad_to, nw_pad_from, nw_pad_to;
 };
 
 template <int P>
 __device__ inline Lane lane_stream(const DecArgs& a, uint32_t k, uint64_t payload_words) {
     Lane l;
-#define LECB_PICK(field, expr)                                            \
-    if constexpr (P == 1) {                                               \
-        l.field = a.st[k].expr;                                           \
-    } else if constexpr (P == 2) {                                        \
-        l.field = k ? a.st[1].expr : a.st[0].expr;                        \
-    } else {                                                              \
-        l.field = k & 2 ? (k & 1 ? a.st[3].expr : a.st[2].expr)           \
-                        : (k & 1 ? a.st[1].expr : a.st[0].expr);          \
+#define LECB_PICK(field)                                                              \
+    if constexpr (P == 1) {                                                           \
+        l.field = a.st[k].field;                                                      \
+    } else if constexpr (P == 2) {                                                    \
+        l.field = k ? a.st[1].field : a.st[0].field;                                  \
+    } else {                                                                          \
+        l.field = k & 2 ? (k & 1 ? a.st[3].field : a.st[2].field)                     \
+                        : (k & 1 ? a.st[1].field : a.st[0].field);                    \
     }
-    LECB_PICK(table, table)
-    LECB_PICK(ulen, ulen)
-    LECB_PICK(payload, payload)
-    LECB_PICK(cb, cb)
-    LECB_PICK(out, out)
-    LECB_PICK(stream, stream)
-    LECB_PICK(table_pad_from, table_pad_from)
-    LECB_PICK(table_pad_to, table_pad_to)
-    LECB_PICK(ulen_pad_from, ulen_pad_from)
-    LECB_PICK(ulen_pad_to, ulen_pad_to)
+    LECB_PICK(table)
+    LECB_PICK(nw)
+    LECB_PICK(payload)
+    LECB_PICK(cb)
+    LECB_PICK(out)
+    LECB_PICK(stream)
+    LECB_PICK(table_pad_from)
+    LECB_PICK(table_pad_to)
+    LECB_PICK(nw_pad_from)
+    LECB_PICK(nw_pad_to)
 #undef LECB_PICK
     l.payload_words = payload_words;
     return l;
@@ -250,21 +157,20 @@ __device__ inline uint32_t lookup(const S& sh, const uint16_t* lut, const Device
     return e;
 }
 
-// The symbols (byte 1) of four table entries as one little-endian word:
-// two byte permutes gather the pairs, a third joins them.
+// The symbols (byte 1) of four table entries as one little-endian word.
 __device__ inline uint32_t syms4(const uint32_t (&e)[4]) {
     const uint32_t p01 = __builtin_amdgcn_perm(e[1], e[0], 0x0c0c0501u);
     const uint32_t p23 = __builtin_amdgcn_perm(e[3], e[2], 0x0c0c0501u);
     return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
-// 16 restored 16-bit words from the high-plane bytes of 16 symbols (lane 2u,
-// w[0..3]) and the low-plane bytes (lane 2u + 1): the pair swaps half of its
-// words, then lane 2u builds words 0..7 and lane 2u + 1 words 8..15
-// (little-endian: low byte first).
+// 16 restored 16-bit words from the high-plane bytes of 16 symbols (lane L of
+// an even row, w[0..3]) and the low-plane bytes (lane L ^ 16, odd row): the
+// pair swaps half of its words, then the high lane builds words 0..7 and the
+// low lane words 8..15 (little-endian: low byte first).
 __device__ inline v4u restore_u16(const uint32_t (&w)[4], uint32_t odd) {
-    const uint32_t s0 = __shfl_xor(odd ? w[0] : w[2], 1, 64);
-    const uint32_t s1 = __shfl_xor(odd ? w[1] : w[3], 1, 64);
+    const uint32_t s0 = __shfl_xor(odd ? w[0] : w[2], 16, 64);
+    const uint32_t s1 = __shfl_xor(odd ? w[1] : w[3], 16, 64);
     const uint32_t h0 = odd ? s0 : w[0], h1 = odd ? s1 : w[1];
     const uint32_t l0 = odd ? w[2] : s0, l1 = odd ? w[3] : s1;
     v4u o;
@@ -275,55 +181,65 @@ __device__ inline v4u restore_u16(const uint32_t (&w)[4], uint32_t odd) {
     return o;
 }
 
-// 16 restored 32-bit elements from four lanes q = 0..3 holding the bytes of
-// planes 0..3 (element bytes 3..0) of 16 symbols: lane q gathers word q of
-// every plane (three exchanges) and builds elements 4q..4q+3.
+// 16 restored 32-bit elements from the four rows q = 0..3 holding the bytes of
+// planes 0..3 (element bytes 3..0) of the same 16 symbols: the lane of row q
+// gathers word q of every plane (three exchanges) and builds elements
+// 4q..4q+3.
 __device__ inline v4u restore_u32(const uint32_t (&w)[4], uint32_t q) {
     uint32_t x0 = 0, x1 = 0, x2 = 0, x3 = 0;  // word q of planes 0..3
+    const uint32_t i = threadIdx.x & 15u;
 #pragma unroll
     for (uint32_t r = 0; r < 4; ++r) {
-        // round r: lane q reads lane (q + r) & 3, which sends its word (self - r) & 3
+        // round r: row q reads row (q + r) & 3, which sends its word (row - r) & 3
         const uint32_t src = (q + r) & 3u;
         const uint32_t want = (q - r) & 3u;
         // (masks rather than an index: the words stay in registers)
         const uint32_t mine = (w[0] & (0u - (uint32_t)(want == 0))) | (w[1] & (0u - (uint32_t)(want == 1))) |
                               (w[2] & (0u - (uint32_t)(want == 2))) | (w[3] & (0u - (uint32_t)(want == 3)));
-        const uint32_t got = r ? __shfl(mine, (int)((threadIdx.x & ~3u) | src), 64) : mine;
+        const uint32_t got = r ? __shfl(mine, (int)((src << 4) | i), 64) : mine;
         x0 = src == 0 ? got : x0;
         x1 = src == 1 ? got : x1;
         x2 = src == 2 ? got : x2;
         x3 = src == 3 ? got : x3;
     }
     // element k: bytes [x3[k], x2[k], x1[k], x0[k]] (little-endian)
-    const uint32_t a01 = __builtin_amdgcn_perm(x0, x1, 0x05010400u);  // x1_0 x0_0 x1_1 x0_1
-    const uint32_t b01 = __builtin_amdgcn_perm(x0, x1, 0x07030602u);  // x1_2 x0_2 x1_3 x0_3
-    const uint32_t a23 = __builtin_amdgcn_perm(x2, x3, 0x05010400u);  // x3_0 x2_0 x3_1 x2_1
+    const uint32_t a01 = __builtin_amdgcn_perm(x0, x1, 0x05010400u);
+    const uint32_t b01 = __builtin_amdgcn_perm(x0, x1, 0x07030602u);
+    const uint32_t a23 = __builtin_amdgcn_perm(x2, x3, 0x05010400u);
     const uint32_t b23 = __builtin_amdgcn_perm(x2, x3, 0x07030602u);
     v4u o;
-    o.x = __builtin_amdgcn_perm(a01, a23, 0x05040100u);  // x3_0 x2_0 x1_0 x0_0
+    o.x = __builtin_amdgcn_perm(a01, a23, 0x05040100u);
     o.y = __builtin_amdgcn_perm(a01, a23, 0x07060302u);
     o.z = __builtin_amdgcn_perm(b01, b23, 0x05040100u);
     o.w = __builtin_amdgcn_perm(b01, b23, 0x07060302u);
     return o;
 }
 
-template <int NT, int P>
-__device__ inline const uint16_t* lut_of(const Shared<NT, P>& S, uint32_t k) {
+template <int NW, int P>
+__device__ inline const uint16_t* lut_of(const Shared<NW, P>& S, uint32_t k) {
     return &S.lut[P == 1 ? 0 : k][0];
 }
 
-// 64 VGPRs at most: two 1024-lane workgroups (8 waves per SIMD) fit a CU.
-template <int NT, int P, int OUT>
+// 64 VGPRs at most: with 16-wave workgroups two fit a CU (8 waves per SIMD).
+template <int NT, int P, int OUT, int LG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_kernel(DecArgs a) {
     static_assert(P == 1 || OUT != DEC_OUT_PLANES, "plane outputs decode one stream per workgroup");
-    __shared__ __attribute__((aligned(16))) Shared<NT, P> S;
+    constexpr int NW = NT / 64;
+    constexpr uint32_t G = 1u << LG;
+    constexpr uint32_t R = 16 * G;                    // ring words of a group
+    __shared__ __attribute__((aligned(16))) Shared<NW, P> S;
     const int tid = threadIdx.x;
+    const uint32_t lane = tid & 63u, wave = tid >> 6;
+    const uint32_t row = lane >> 4, i16 = lane & 15u;
 
-    // ---- which stream, unit and chunk this lane decodes
+    // ---- which stream, task, chunk and lane this hardware lane decodes
     const uint32_t sidx = P == 1 ? blockIdx.x / a.wg_per_group : 0u;     // P == 1: stream of the workgroup
     const uint32_t bid = P == 1 ? blockIdx.x - sidx * a.wg_per_group : blockIdx.x;
-    const uint32_t k = P == 1 ? sidx : (uint32_t)tid & (P - 1);           // this lane's stream
-    const uint64_t u = P == 1 ? (uint64_t)bid * NT + tid : ((uint64_t)bid * NT + tid) / P;
+    const uint32_t k = P == 1 ? sidx : row % P;                           // this lane's stream
+    const uint64_t task = (uint64_t)bid * NW + wave;
+    constexpr uint32_t CPT = (4 / P) * (16u >> LG);
+    const uint64_t c = task * CPT + (row / P) * (16u >> LG) + (i16 >> LG);
+    const uint32_t j = i16 & (G - 1);
     // stream sizes: given, or read from the encoder's results (this lane's
     // stream picked by conditional moves, not by an index into an array)
     uint64_t my_words = 0;
@@ -351,146 +267,201 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             const v4u* src = reinterpret_cast<const v4u*>(a.st[P == 1 ? sidx : (uint32_t)q].cb->lut);
             v4u* dst = reinterpret_cast<v4u*>(&S.lut[q][0]);
             constexpr int NV = LUT_SIZE * 2 / 16;
-            for (int i = tid; i < NV; i += NT) dst[i] = src[i];
+            for (int x = tid; x < NV; x += NT) dst[x] = src[x];
         }
         if constexpr (P == 1) {
             const v4u* src2 = reinterpret_cast<const v4u*>(a.st[sidx].cb->lut2);
             v4u* dst2 = reinterpret_cast<v4u*>(S.lut2);
-            for (int i = tid; i < LUT2_SIZE * 2 / 16; i += NT) dst2[i] = src2[i];
+            for (int x = tid; x < LUT2_SIZE * 2 / 16; x += NT) dst2[x] = src2[x];
         }
     }
     const uint32_t base2 = ln.cb->lut2_base;
 
-    // ---- unit geometry and the stream's structure around it
-    const uint32_t K = 1u << a.log2k;
-    const uint64_t c = u >> a.log2k;
-    const uint32_t j = (uint32_t)(u & (K - 1));
-    const bool active = c < a.nc && !my_size_bad;
-    bool bad = my_size_bad && c < a.nc;
+    // ---- the chunk and its structure
+    const bool valid = c < a.nc;
+    bool bad = my_size_bad && valid;
     uint64_t sw = 0, wc = 0;
-    uint32_t m_c = 0, cnt = 0, my_bits = 0;
-    if (active) {
+    uint32_t m = 0, N = 0;
+    if (valid && !my_size_bad) {
         sw = c ? ln.table[c - 1] : 0;
         const uint64_t ew = ln.table[c];
-        if (ew <= sw || ew > ln.payload_words || ew - sw > a.chunk / 2) bad = true;
+        if (ew <= sw || ew > ln.payload_words) bad = true;
         wc = bad ? 0 : ew - sw;
-        m_c = (uint32_t)min<uint64_t>(a.chunk, a.n - c * a.chunk);
-        cnt = m_c > j * UNIT ? min(m_c - j * UNIT, UNIT) : 0u;
-        my_bits = ln.ulen[u];
-        if (my_bits < cnt || my_bits > 16 * cnt) bad = true;
+        const uint32_t mc = (uint32_t)min<uint64_t>(a.chunk, a.n - c * a.chunk);
+        m = lane_symbols<LG>(mc, j);
+        N = ln.nw[(c << LG) + j];
+        if ((m == 0) != (N == 0)) bad = true;
     }
-    // first bit of every unit: exclusive sum of the bit counts of the chunk's
-    // earlier units of the same stream (segments of K*P lanes; the ring's first
-    // row holds the sums until the decode starts)
-    uint32_t* const scan = &S.ring[0][0];
-    scan[tid] = my_bits;
-    __syncthreads();
-    const uint32_t seg = K * P;  // lanes of one chunk (all streams); divides NT
-    const uint32_t in_seg = (uint32_t)tid & (seg - 1);
-    for (uint32_t o = P; o < seg; o <<= 1) {
-        const uint32_t v = in_seg >= o ? scan[tid - o] : 0u;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    const uint32_t first_bit = scan[tid] - my_bits;
-    const uint32_t chunk_bits = scan[(tid - in_seg) + (K - 1) * P + (tid & (P - 1))];
-    __syncthreads();  // the ring is written from here on
-    if (active && !bad) {
-        // the chunk's bits fill its words to within one word
-        if (chunk_bits == 0 || (uint64_t)chunk_bits > 32 * wc || (uint64_t)chunk_bits + 32 <= 32 * wc) bad = true;
+    // the chunk's word counts must add up to its words; a bad lane stops its chunk
+    if (group_sum<LG>(N) != (uint32_t)wc && valid && !my_size_bad) bad = true;
+    const bool run = valid && group_sum<LG>(bad ? 1u : 0u) == 0;
+    if (!run) {
+        m = 0;
+        N = 0;
+        sw = 0;   // a chunk that is not decoded reads payload word 0 onwards (always in the buffer)
     }
 
     // padding bytes of the header are part of the format (checked by the
     // first workgroup of each stream, spread over that stream's lanes)
     if (bid == 0) {
-        const uint32_t lane_in = (uint32_t)tid / P;
+        const uint32_t lane_in = wave * (64 / P) + (row / P) * 16 + i16;
         for (uint64_t b = ln.table_pad_from + lane_in; b < ln.table_pad_to; b += NT / P) bad |= ln.stream[b] != 0;
-        for (uint64_t b = ln.ulen_pad_from + lane_in; b < ln.ulen_pad_to; b += NT / P) bad |= ln.stream[b] != 0;
+        for (uint64_t b = ln.nw_pad_from + lane_in; b < ln.nw_pad_to; b += NT / P) bad |= ln.stream[b] != 0;
     }
 
-    // ---- decode
-    Reader<NT> r;
-    r.ring = &S.ring[0][tid];
-    r.p = ln.payload;
-    r.sw = sw;
-    r.gmax = ln.payload_words ? (ln.payload_words - 1) >> 2 : 0;
-    r.sh = (uint32_t)sw & (RING - 1);
-    const uint16_t* lut = lut_of<NT, P>(S, k);
-    const uint64_t e0 = c * a.chunk + (uint64_t)j * UNIT;  // first element of the unit
-    const bool run = active && !bad;
-    const uint32_t ngrp = run ? cnt >> 4 : 0u;
-    // lanes of one unit keep the same group count so that the exchanges of
-    // the fused outputs pair up (a unit's P lanes see the same cnt)
-    uint32_t inval = 0;
-    if (run && cnt) r.start(first_bit);
-    for (uint32_t g = 0; g < ngrp; ++g) {
+    // ---- the group's ring: words of the chunk's payload, slot = word & (R - 1).
+    // Loads are counted in words from a0 = sw rounded down to 4 (16-byte groups).
+    uint32_t* const ring = &S.ring[wave][row][(i16 >> LG) * R];
+    const uint64_t a0 = sw & ~uint64_t(3);
+    const v4u* const grp = reinterpret_cast<const v4u*>(ln.payload + a0);
+    // groups past the caller's payload are read as its last group (a0 lies in
+    // the payload whenever the payload has a word)
+    const uint64_t gall = ln.payload_words ? ((ln.payload_words - 1) >> 2) - (a0 >> 2) : 0;
+    const uint32_t glast = (uint32_t)min<uint64_t>(gall, 0xFFFFFFFFull);
+    auto load4 = [&](uint32_t word) -> v4u {   // this lane's 16 bytes of a group load at word a0 + word
+        const uint32_t g = (word >> 2) + j;
+        v4u v = {0, 0, 0, 0};
+        if (run) v = grp[g < glast ? g : glast];   // (a chunk that is not decoded reads nothing)
+        return v;
+    };
+    const uint32_t slot0 = (uint32_t)a0 & (R - 1);
+    auto put4 = [&](uint32_t word, const v4u& v) {
+        *reinterpret_cast<v4u*>(&ring[(slot0 + word + 4 * j) & (R - 1)]) = v;
+    };
+    {
+        const v4u v0 = load4(0), v1 = load4(4 * G), v2 = load4(8 * G), v3 = load4(12 * G);
+        put4(0, v0);
+        put4(4 * G, v1);
+        put4(8 * G, v2);
+        put4(12 * G, v3);
+    }
+    uint32_t wr = R;                            // next word to load (from a0)
+    __builtin_amdgcn_wave_barrier();
+    uint32_t pend_at = 0;
+    v4u pend_v = {0, 0, 0, 0};
+    bool pend = false;
+
+    // ---- words 0 and 1
+    uint32_t b0, n0, b1, n1;
+    group_count<LG>(N >= 1, b0, n0);
+    group_count<LG>(N >= 2, b1, n1);
+    const uint32_t d0 = (uint32_t)(sw - a0);    // the chunk's first word, from a0
+    uint32_t cons = d0 + n0 + n1;               // next word the group reads, from a0
+    uint32_t w0 = N >= 1 ? ring[(slot0 + d0 + b0) & (R - 1)] : 0u;
+    uint32_t w1 = N >= 2 ? ring[(slot0 + d0 + n0 + b1) & (R - 1)] : 0u;
+    uint32_t rd = min(N, 2u), off = 0, shifts = 0, inval = 0;
+    const uint16_t* lut = lut_of<NW, P>(S, k);
+
+    // ---- decode, block by block
+    uint32_t mmax = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mmax = max(mmax, (uint32_t)__shfl_xor(mmax, o, 64));
+    const uint32_t nblk = (mmax + BLOCK - 1) / BLOCK;
+    const uint64_t lane_e0 = c * a.chunk + (uint64_t)j * BLOCK;   // first element of the lane's block 0
+    for (uint32_t t = 0; t < nblk; ++t) {
         uint32_t w[4];
         uint32_t ev[4];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            if ((q & 3) == 0) r.tick();
-            r.refill();
+            if ((q & 3) == 0) {
+                // ring top-up (group-uniform): commit the previous load, issue the next
+                if (pend) put4(pend_at, pend_v);
+                pend = false;
+                if (wr - cons <= R - 4 * G) {
+                    pend_v = load4(wr);
+                    pend_at = wr;
+                    wr += 4 * G;
+                    pend = true;
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            const uint32_t s0 = t * BLOCK + 2 * q;   // the pair's first symbol in the lane
+            const bool act = s0 < m;
+            const bool sh = act && off >= 32;
+            const bool fetch = sh && rd < N;
+            uint32_t bf, nf;
+            group_count<LG>(fetch, bf, nf);
+            const uint32_t word = ring[(slot0 + cons + bf) & (R - 1)];
+            w0 = sh ? w1 : w0;
+            w1 = sh ? (fetch ? word : 0u) : w1;
+            off -= sh ? 32u : 0u;
+            shifts += sh ? 1u : 0u;
+            rd += fetch ? 1u : 0u;
+            cons += nf;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int i = 2 * q + h;
-                const uint32_t e = lookup<P>(S, lut, ln.cb, base2, r.peek(), inval);
-                r.off += e & 0xFFu;
-                ev[i & 3] = e;
-                if ((i & 3) == 3) w[i >> 2] = syms4(ev);
+                const uint32_t top = (uint32_t)(((((uint64_t)w0 << 32) | w1) << off) >> 32);
+                uint32_t iv = 0;
+                uint32_t e = lookup<P>(S, lut, ln.cb, base2, top, iv);
+                const bool use = s0 + h < m;
+                e = use ? e : 0u;
+                inval |= use ? iv : 0u;
+                off += e & 0xFFu;
+                const int x = 2 * q + h;
+                ev[x & 3] = e;
+                if ((x & 3) == 3) w[x >> 2] = syms4(ev);
             }
         }
+        // the block's output: 16 symbols of block tG + j of the chunk
+        const uint32_t cnt = m > t * BLOCK ? min(BLOCK, m - t * BLOCK) : 0u;
+        const uint64_t e0 = lane_e0 + (uint64_t)(t << LG) * BLOCK;
         if constexpr (OUT == DEC_OUT_PLANES) {
-            v4u v;
-            v.x = w[0];
-            v.y = w[1];
-            v.z = w[2];
-            v.w = w[3];
-            *reinterpret_cast<v4u*>(ln.out + e0 + 16 * g) = v;
-        } else if constexpr (OUT == DEC_OUT_U16 || OUT == DEC_OUT_U16_XOR) {
-            v4u v = restore_u16(w, k);
-            const uint64_t at = 2 * (e0 + 16 * g) + 16 * k;
-            if constexpr (OUT == DEC_OUT_U16_XOR) v ^= *reinterpret_cast<const v4u*>(a.w0 + at);
-            *reinterpret_cast<v4u*>(a.merged + at) = v;
+            if (cnt == BLOCK) {
+                v4u v;
+                v.x = w[0];
+                v.y = w[1];
+                v.z = w[2];
+                v.w = w[3];
+                *reinterpret_cast<v4u*>(ln.out + e0) = v;
+            } else {
+                for (uint32_t x = 0; x < cnt; ++x) ln.out[e0 + x] = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
+            }
         } else {
-            const v4u v = restore_u32(w, k);
-            *reinterpret_cast<v4u*>(a.merged + 4 * (e0 + 16 * g) + 16 * k) = v;
+            // every lane takes part in the exchanges; the lanes of one element
+            // group have the same cnt
+            if constexpr (OUT == DEC_OUT_U16 || OUT == DEC_OUT_U16_XOR) {
+                v4u v = restore_u16(w, k);
+                const uint64_t at = 2 * e0 + 16 * k;
+                if (cnt == BLOCK) {
+                    if constexpr (OUT == DEC_OUT_U16_XOR) v ^= *reinterpret_cast<const v4u*>(a.w0 + at);
+                    *reinterpret_cast<v4u*>(a.merged + at) = v;
+                }
+            } else {
+                const v4u v = restore_u32(w, k);
+                if (cnt == BLOCK) *reinterpret_cast<v4u*>(a.merged + 4 * e0 + 16 * k) = v;
+            }
+            if (cnt && cnt < BLOCK) {
+                // the tensor's last block: byte P-1-k of each element (plane k holds byte P-1-k)
+                for (uint32_t x = 0; x < cnt; ++x) {
+                    const uint64_t at = (uint64_t)P * (e0 + x) + (P - 1 - k);
+                    const uint8_t sym = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
+                    a.merged[at] = OUT == DEC_OUT_U16_XOR ? (uint8_t)(sym ^ a.w0[at]) : sym;
+                }
+            }
         }
     }
-    if (run && cnt) {
-        // the tensor's last unit: the symbols after the last full group
-        const uint32_t rem = cnt & 15u;
-        for (uint32_t i = 0; i < rem; ++i) {
-            if ((i & 3) == 0) r.tick();
-            r.refill();
-            const uint32_t e = lookup<P>(S, lut, ln.cb, base2, r.peek(), inval);
-            r.off += e & 0xFFu;
-            const uint64_t el = e0 + 16 * ngrp + i;
-            const uint8_t sym = (uint8_t)(e >> 8);
-            if constexpr (OUT == DEC_OUT_PLANES) {
-                ln.out[el] = sym;
-            } else {
-                // byte P-1-k of element el (plane k holds byte P-1-k)
-                const uint64_t at = (uint64_t)P * el + (P - 1 - k);
-                a.merged[at] = OUT == DEC_OUT_U16_XOR ? (uint8_t)(sym ^ a.w0[at]) : sym;
-            }
+    // ---- the lane's end: every word read, the last one needed, zero padding
+    uint32_t bits = 0;
+    if (run && m) {
+        if (off >= 32) {   // slide past a used-up first word (all words are read by now)
+            w0 = w1;
+            w1 = 0;
+            off -= 32;
+            shifts += 1;
         }
-        r.refill();
-        const uint32_t end = r.pos();
-        if (inval || end != first_bit + my_bits) bad = true;
-        // the unit with the chunk's last symbol: zero padding to the end of the word
-        if (!bad && j == ((m_c - 1) >> 8)) {
-            const uint32_t rest = (uint32_t)(32 * wc) - end;
-            if (rest >= 32 || (rest && (r.peek() >> (32 - rest)) != 0)) bad = true;
-        }
+        bits = 32 * shifts + off;
+        if (inval || rd != N || bits > 32 * N || bits <= 32 * (N - 1)) bad = true;
+        const uint32_t rest = 32 * N - bits;
+        const uint32_t top = (uint32_t)(((((uint64_t)w0 << 32) | w1) << off) >> 32);
+        if (!bad && rest && (top >> (32 - rest)) != 0) bad = true;
     }
 
     // ---- status, accounting, exit
     constexpr int NS = P == 1 ? 1 : P;  // streams in this workgroup
     const uint32_t slot = P == 1 ? 0u : k;
-    __syncthreads();  // the ring is free again: per-stream flags and bit sums
-    uint32_t* const flag = &S.ring[0][0];                                                    // [NS]
-    unsigned long long* const bsum = reinterpret_cast<unsigned long long*>(&S.ring[1][0]);  // [NS]
+    __syncthreads();  // the rings are free again: per-stream flags and bit sums
+    uint32_t* const flag = &S.ring[0][0][0];                                                    // [NS]
+    unsigned long long* const bsum = reinterpret_cast<unsigned long long*>(&S.ring[0][1][0]);  // [NS]
     if (tid < NS) {
         flag[tid] = 0u;
         bsum[tid] = 0ull;
@@ -498,11 +469,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     __syncthreads();
     if (bad) atomicOr(&flag[slot], 1u);
     {
-        // bits of the units decoded without fault, summed per stream
-        uint64_t v = (run && !bad) ? my_bits : 0u;
+        // bits of the lanes decoded without fault, summed per row (one stream per row)
+        uint64_t v = (run && !bad) ? bits : 0u;
 #pragma unroll
-        for (int o = 32; o >= P; o >>= 1) v += __shfl_xor(v, o, 64);
-        if ((tid & 63) < P && v) atomicAdd(&bsum[tid & 63], (unsigned long long)v);
+        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+        if (i16 == 0 && v) atomicAdd(&bsum[slot], (unsigned long long)v);
     }
     __syncthreads();
 #pragma unroll
@@ -525,11 +496,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
                     const uint64_t bytes = a.sizes[s].bytes;
                     e.payload_words = bytes >= e.header_bytes ? (bytes - e.header_bytes) / 4 : 0;
                 }
-                const uint64_t bits = __hip_atomic_load(&e.ws->bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t bits_all = __hip_atomic_load(&e.ws->bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const int32_t st = __hip_atomic_load(&e.ws->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const uint64_t W = e.table[a.nc - 1];
                 e.res->bytes = e.header_bytes + 4 * W;
-                e.res->payload_bits = bits;
+                e.res->payload_bits = bits_all;
                 e.res->status = (st == 0 && W != e.payload_words) ? (int32_t)LECB_ERR_CORRUPT : st;
                 e.res->reserved = 0;
                 e.ws->bits = 0;
@@ -542,18 +513,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
 }
 
 template <int NT, int P, int OUT>
-void launch(const DecArgs& a, uint32_t wgs, hipStream_t hs) {
-    hipLaunchKernelGGL((decode_kernel<NT, P, OUT>), dim3(wgs), dim3(NT), 0, hs, a);
+hipError_t launch(const DecArgs& a, uint32_t lg, uint32_t wgs, hipStream_t hs) {
+    switch (lg) {
+        case 0: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 0>), dim3(wgs), dim3(NT), 0, hs, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 1>), dim3(wgs), dim3(NT), 0, hs, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 2>), dim3(wgs), dim3(NT), 0, hs, a); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 3>), dim3(wgs), dim3(NT), 0, hs, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 4>), dim3(wgs), dim3(NT), 0, hs, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
 
 int launch_decode(const DecodeLaunch& L, void* stream) {
     DecArgs a{};
-    const uint64_t tb = table_bytes(L.nc), ub = ulen_bytes(L.nc, L.chunk);
-    const uint32_t K = units_per_chunk(L.chunk);
+    const uint64_t tb = table_bytes(L.nc), cb = count_bytes(L.nc, L.chunk);
+    const uint32_t G = lanes_per_chunk(L.chunk);
+    const uint32_t lg = (uint32_t)ilog2(G);
     a.chunk = L.chunk;
-    a.log2k = (uint32_t)ilog2(K);
     a.n = L.n;
     a.nc = L.nc;
     a.nstreams = L.nstreams;
@@ -564,61 +543,59 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
     for (int s = 0; s < L.nstreams; ++s) {
         DecStream& st = a.st[s];
         st.table = reinterpret_cast<const uint32_t*>(L.stream_base[s]);
-        st.ulen = reinterpret_cast<const uint16_t*>(L.stream_base[s] + tb);
-        st.payload = reinterpret_cast<const uint32_t*>(L.stream_base[s] + tb + ub);
-        st.payload_words = L.dev_sizes ? 0 : (L.stream_bytes[s] - tb - ub) / 4;
+        st.nw = reinterpret_cast<const uint16_t*>(L.stream_base[s] + tb);
+        st.payload = reinterpret_cast<const uint32_t*>(L.stream_base[s] + tb + cb);
+        st.payload_words = L.dev_sizes ? 0 : (L.stream_bytes[s] - tb - cb) / 4;
         st.cb = L.cb[s];
-        st.header_bytes = tb + ub;
+        st.header_bytes = tb + cb;
         st.stream = L.stream_base[s];
         st.table_pad_from = 4 * L.nc;
         st.table_pad_to = tb;
-        st.ulen_pad_from = tb + 2 * L.nc * K;
-        st.ulen_pad_to = tb + ub;
+        st.nw_pad_from = tb + 2 * L.nc * G;
+        st.nw_pad_to = tb + cb;
         st.out = L.out[s];
         st.res = L.res[s];
         st.ws = L.ws[s];
     }
-    const uint64_t units = L.nc * K;
     const uint64_t cus = (uint64_t)device_cu_count();
+    if (cus == 0) return LECB_ERR_HIP;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    // Workgroup size: 16 waves (the tables are one copy per workgroup, 8 for
+    // four planes) when the tasks give every CU such a workgroup, else 4
+    // waves, so that small inputs still spread over the CUs.
     if (L.out_kind == DEC_OUT_PLANES) {
-        // One stream per workgroup.  Lanes per workgroup: the tables are one
-        // copy per workgroup, so bigger workgroups leave more LDS for lanes
-        // (2 x 1024 lanes fit a CU against 5 x 256), and fewer, bigger
-        // workgroups spread evenly over the CUs.  Take the biggest size that
-        // still gives every CU a workgroup (every size holds whole chunks:
-        // K <= 256 units).
-        const uint64_t all = units * (uint64_t)L.nstreams;
-        const int nt = all >= cus * 1024 ? 1024 : all >= cus * 512 ? 512 : 256;
-        a.wg_per_group = (uint32_t)((units + nt - 1) / nt);
+        const uint64_t cpt = 4 * (16 >> lg);
+        const uint64_t tasks = (L.nc + cpt - 1) / cpt;
+        const bool big = tasks * (uint64_t)L.nstreams >= cus * 16;
+        const uint32_t nw = big ? 16 : 4;
+        a.wg_per_group = (uint32_t)((tasks + nw - 1) / nw);
         const uint32_t wgs = a.wg_per_group * (uint32_t)L.nstreams;
-        if (nt == 1024) launch<1024, 1, DEC_OUT_PLANES>(a, wgs, hs);
-        else if (nt == 512) launch<512, 1, DEC_OUT_PLANES>(a, wgs, hs);
-        else launch<256, 1, DEC_OUT_PLANES>(a, wgs, hs);
+        e = big ? launch<1024, 1, DEC_OUT_PLANES>(a, lg, wgs, hs) : launch<256, 1, DEC_OUT_PLANES>(a, lg, wgs, hs);
     } else if (L.out_kind == DEC_OUT_U16 || L.out_kind == DEC_OUT_U16_XOR) {
-        // two lanes per unit; a workgroup holds whole chunks (2K <= 512 lanes)
         if (L.nstreams != 2 || !L.merged || (L.out_kind == DEC_OUT_U16_XOR && !L.w0)) return LECB_ERR_INVALID_ARG;
-        const uint64_t lanes = 2 * units;
-        const int nt = lanes >= cus * 1024 ? 1024 : 512;
-        const uint32_t wgs = (uint32_t)((lanes + nt - 1) / nt);
-        if (L.out_kind == DEC_OUT_U16) {
-            if (nt == 1024) launch<1024, 2, DEC_OUT_U16>(a, wgs, hs);
-            else launch<512, 2, DEC_OUT_U16>(a, wgs, hs);
-        } else {
-            if (nt == 1024) launch<1024, 2, DEC_OUT_U16_XOR>(a, wgs, hs);
-            else launch<512, 2, DEC_OUT_U16_XOR>(a, wgs, hs);
-        }
+        const uint64_t cpt = 2 * (16 >> lg);
+        const uint64_t tasks = (L.nc + cpt - 1) / cpt;
+        const bool big = tasks >= cus * 16;
+        const uint32_t nw = big ? 16 : 4;
+        const uint32_t wgs = (uint32_t)((tasks + nw - 1) / nw);
+        if (L.out_kind == DEC_OUT_U16)
+            e = big ? launch<1024, 2, DEC_OUT_U16>(a, lg, wgs, hs) : launch<256, 2, DEC_OUT_U16>(a, lg, wgs, hs);
+        else
+            e = big ? launch<1024, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs)
+                    : launch<256, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs);
     } else if (L.out_kind == DEC_OUT_U32) {
-        // four lanes per unit; a workgroup holds whole chunks (4K lanes)
         if (L.nstreams != 4 || !L.merged) return LECB_ERR_INVALID_ARG;
-        const uint64_t lanes = 4 * units;
-        const int nt = 4 * K > 512 ? 1024 : 512;
-        const uint32_t wgs = (uint32_t)((lanes + nt - 1) / nt);
-        if (nt == 1024) launch<1024, 4, DEC_OUT_U32>(a, wgs, hs);
-        else launch<512, 4, DEC_OUT_U32>(a, wgs, hs);
+        const uint64_t cpt = 16 >> lg;
+        const uint64_t tasks = (L.nc + cpt - 1) / cpt;
+        const bool big = tasks >= cus * 8;
+        const uint32_t nw = big ? 8 : 4;
+        const uint32_t wgs = (uint32_t)((tasks + nw - 1) / nw);
+        e = big ? launch<512, 4, DEC_OUT_U32>(a, lg, wgs, hs) : launch<256, 4, DEC_OUT_U32>(a, lg, wgs, hs);
     } else {
         return LECB_ERR_INVALID_ARG;
     }
+    if (e != hipSuccess) return LECB_ERR_INVALID_ARG;
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

@@ -1,76 +1,62 @@
-// Huffman encode of byte symbols into stream format v2, in two launches
-// (a count launch, then a pack launch).
+// Huffman encode of byte symbols into stream format v3, in three launches
+// (count, offsets, pack).
 //
 // "Single-Stage Huffman Encoder for ML Compression", Methodology step 4: each
 // tensor is coded directly with the codebook already resident on the device.
 // "Lossless Compression for LLM Tensor Incremental Snapshots", Technical
 // framework step 3 (Huffman coding of the byte groups): the plane modes read
-// one byte plane straight out of the 16-bit words, and the pair mode codes
-// both planes in one pass over the words (two streams, two codebooks).
+// one byte plane straight out of 16-bit words, and the pair modes code two
+// planes of the same elements in one pass (two streams, two codebooks); Key
+// design item 3 (independent parallel tasks): the lanes of the format.
 //
-// Work unit: a ticket of max(chunk, 16384) symbols -- G = 16384/chunk whole
-// chunks, or one chunk made of chunk/16384 segments.  A segment is 256
-// threads x 64 consecutive symbols.  The grid is persistent and workgroup w
-// owns the contiguous tickets [w*T/W, (w+1)*T/W).  Two launches:
-//   1. count_kernel: every workgroup sums the payload words of its tickets
-//      (per chunk: ceil(bits / 32)) and stores that total; every thread
-//      also stores the code bits of its 64 symbols;
-//   2. encode_kernel: workgroup w starts at the sum of the totals of
-//      workgroups 0..w-1 (the device-wide exclusive scan, done by one wave
-//      per stream) and then, ticket by ticket:
-//      A. each thread reads the code bits of its 64 symbols stored by the
-//         count launch; a block scan gives every thread's bit offset inside
-//         its chunk and every chunk's size.  With one segment per ticket the
-//         thread also loads its symbols (all loads in flight at once), which
-//         stay in registers for step C;
-//      B. the ticket's first payload word is the running sum of the words of
-//         the workgroup's earlier tickets; the chunk table entries follow;
-//      C. per stream: every thread ORs its code words into an LDS image of
-//         the ticket's payload (each chunk starts on a word), then the image
-//         goes out with coalesced stores.  The code bits of every decode
-//         unit (256 symbols = 4 threads) are the sum of its four threads'
-//         bits and go out as one u16 per unit.
-// No workgroup ever waits for another one.
+// One hardware lane codes one lane of the format (lane geometry: lanes.hpp).
+// A wave's task is 4 rows of 16 lanes, i.e. 4/P row groups of 16/G chunks.
+// The waves of a launch split the tasks into contiguous ranges, the same
+// ranges in the count and the pack launch:
+//   1. count: every lane sums the code lengths of its symbols, stores its
+//      word count nw = ceil(bits / 32) in the stream, and every wave stores
+//      the words of its range (per stream) in the workspace;
+//   2. offsets: one workgroup turns the ranges' words into their first
+//      payload words (exclusive scan) and checks the total against the
+//      capacity;
+//   3. pack: every wave walks its range task by task.  A chunk's first word
+//      is the range's first word plus the words of the range's earlier
+//      chunks; the chunk's end goes to the table.  Every lane then runs the
+//      decoder's read order in lock step with its group: before each pair
+//      of symbols, the lanes that completed a word in the previous pair get
+//      the next read positions of the chunk (a count over the group's lanes),
+//      and a lane writes each word it completes to the position reserved for
+//      it two reads earlier (or by the reads of words 0 and 1).  Input blocks
+//      of 16 symbols are read with one 16-byte load per lane: the lanes of a
+//      row read neighbouring blocks.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <type_traits>
 
-#include "lecb_internal.hpp"
+#include "lanes.hpp"
 
 namespace lecb {
 
 namespace {
 
-constexpr int ENC_THREADS = 256;
-constexpr int ENC_WGS_PER_CU = 2;   // pack workgroups per compute unit at most (default grid)
-constexpr int ENC_WGS_PER_CU_LONG = 3;   // the same for long inputs (see launch_encode)
-constexpr uint64_t ENC_LONG_SEGS = 32;   // segments per workgroup that make an input long
-constexpr int SPT = 64;                                  // symbols per thread in a segment
-constexpr uint32_t SEG = ENC_THREADS * SPT;              // 16384
-constexpr int MAX_G = SEG / LECB_MIN_CHUNK;              // chunks per ticket at most (64)
-constexpr int STAGE_WORDS = SEG * 16 / 32 + MAX_G + 2;   // worst case 16 bits/symbol, + rounding + carry
-// The stage holds payload word k at LDS word k + k/32.  A thread's 64 code
-// words span about 64*bits/32 payload words, so with 8-bit codes the threads
-// of a wave touch words 16 apart: unpadded, all 64 lanes would fall on 2 of
-// the 32 banks; with the padding word every 32 they spread over all of them.
-__device__ inline uint32_t st_at(uint32_t k) { return k + (k >> 5); }
-constexpr int STAGE_LDS = STAGE_WORDS + STAGE_WORDS / 32 + 1;
-constexpr int THREADS_PER_UNIT = LECB_UNIT_SYMBOLS / SPT;   // 4
+constexpr int ENC_THREADS = 256;                 // four independent waves
+constexpr int ENC_WAVES = ENC_THREADS / 64;
+constexpr int ENC_WAVES_PER_CU = 32;             // pack and count waves per compute unit (grid size)
+constexpr int OFF_THREADS = 1024;
 
 struct StreamArgs {
     const DeviceCodebook* cb;
     uint32_t* table;
-    uint16_t* ulen;                          // code bits of every decode unit
+    uint16_t* nw;                            // word count of every lane
     uint32_t* payload;
     uint64_t header_bytes;
     uint64_t capacity_words;
     uint64_t table_pad_from, table_pad_to;  // byte ranges of header padding
-    uint64_t ulen_pad_from, ulen_pad_to;
+    uint64_t nw_pad_from, nw_pad_to;
     uint8_t* stream;
     lecb_result* res;
     WsHeader* ws;
-    uint64_t* wg_words;                      // payload words of each workgroup's tickets
+    uint64_t* range_words;                   // count: words of each range; offsets: first word of each
 };
 
 struct EncArgs {
@@ -78,20 +64,16 @@ struct EncArgs {
     const void* in2;     // ENC_PAIR_XOR: symbols are the planes of in[i] ^ in2[i]
     uint64_t n;
     uint32_t chunk;
-    uint32_t log2k;
+    uint32_t lg;         // log2 of the lanes per chunk
     uint64_t nc;
-    uint32_t G;          // chunks per ticket
-    uint32_t S;          // segments per ticket
-    uint64_t ntickets;
-    uint32_t npack;      // pack workgroups W (ticket ranges); the count launch has F*W
-    uint32_t fsplit;     // F: count workgroups per pack workgroup's range
-    uint32_t* counts;    // code bits of every 64 consecutive symbols (pack_counts)
+    uint64_t ntasks;     // tasks of chunks_per_task chunks
+    uint32_t cpt;        // chunks per task
+    uint32_t nranges;    // waves of the count and of the pack launch
     StreamArgs st[2];
 };
 
 constexpr bool pair32_mode(int m) { return m == ENC_PAIR32_HI || m == ENC_PAIR32_LO; }
-constexpr bool pair_mode(int m) { return two_stream_mode(m); }
-template <int MODE> struct Streams { static constexpr int value = pair_mode(MODE) ? 2 : 1; };
+template <int MODE> struct Streams { static constexpr int value = two_stream_mode(MODE) ? 2 : 1; };
 
 __device__ inline uint32_t lo_plane(uint32_t a, uint32_t b) {
     return (a & 0xFFu) | ((a >> 8) & 0xFF00u) | ((b & 0xFFu) << 16) | ((b << 8) & 0xFF000000u);
@@ -99,556 +81,332 @@ __device__ inline uint32_t lo_plane(uint32_t a, uint32_t b) {
 __device__ inline uint32_t hi_plane(uint32_t a, uint32_t b) {
     return ((a >> 8) & 0xFFu) | ((a >> 16) & 0xFF00u) | ((b << 8) & 0xFF0000u) | (b & 0xFF000000u);
 }
-
-// The selected 16 bits of two 32-bit elements, as one word of two 16-bit values.
-template <int MODE>
-__device__ inline uint32_t half2(uint32_t e0, uint32_t e1) {
-    if constexpr (MODE == ENC_PAIR32_HI) return (e0 >> 16) | (e1 & 0xFFFF0000u);
-    else return (e0 & 0xFFFFu) | (e1 << 16);
+// Byte `b` of four 32-bit elements as one word (element 0 in the low byte).
+__device__ inline uint32_t byte_of4(const uint4& e, uint32_t b) {
+    const uint32_t sel = b | ((b + 4u) << 8) | 0x0C0C0000u;   // bytes b of (lo, hi); 0x0C = zero
+    const uint32_t t01 = __builtin_amdgcn_perm(e.y, e.x, sel);
+    const uint32_t t23 = __builtin_amdgcn_perm(e.w, e.z, sel);
+    return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
 }
 
-// 16-bit value of element i: the word itself, its delta, or half of a 32-bit element.
+// Byte of element i that plane `plane` (0 or 1 of the mode's streams) codes.
 template <int MODE>
-__device__ inline uint32_t input_word(const EncArgs& a, uint64_t i) {
-    if constexpr (pair32_mode(MODE)) {
+__device__ inline uint32_t symbol_at(const EncArgs& a, uint64_t i, uint32_t plane) {
+    if constexpr (MODE == ENC_BYTES) {
+        return static_cast<const uint8_t*>(a.in)[i];
+    } else if constexpr (pair32_mode(MODE)) {
         const uint32_t e = static_cast<const uint32_t*>(a.in)[i];
-        return MODE == ENC_PAIR32_HI ? (e >> 16) : (e & 0xFFFFu);
+        const uint32_t b = (MODE == ENC_PAIR32_HI ? 3u : 1u) - plane;
+        return (e >> (8 * b)) & 0xFFu;
     } else {
         uint32_t x = static_cast<const uint16_t*>(a.in)[i];
         if constexpr (MODE == ENC_PAIR_XOR) x ^= static_cast<const uint16_t*>(a.in2)[i];
-        return x;
+        const bool low = MODE == ENC_PLANE_LO || (two_stream_mode(MODE) && plane == 1);
+        return low ? (x & 0xFFu) : (x >> 8);
     }
 }
 
-// Symbol k of a thread's 64 (little-endian in w[16]).
-__device__ inline uint32_t sym_of(const uint32_t w[16], int k) {
-    return (w[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-}
-
-// The thread's 64 symbols starting at i0 (nv of them below n) into w[NS][16];
-// with nv == 64 all loads are issued before any is used.
+// The 16 symbols of the block starting at element e0 for `plane`, little-endian
+// in w[0..3]; cnt < 16 symbols valid (the rest zero) only in the tensor's last block.
 template <int MODE>
-__device__ inline void load64(const EncArgs& a, uint64_t i0, int nv, uint32_t w[][16]) {
-    constexpr int NS = Streams<MODE>::value;
-    if (nv == SPT) {
+__device__ inline void block_symbols(const EncArgs& a, uint64_t e0, uint32_t cnt, uint32_t plane, uint32_t (&w)[4]) {
+    if (cnt == BLOCK) {
         if constexpr (MODE == ENC_BYTES) {
-            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.in) + i0);
-            uint4 v[4];
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.in) + e0);
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else if constexpr (pair32_mode(MODE)) {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(a.in) + e0);
+            const uint32_t b = (MODE == ENC_PAIR32_HI ? 3u : 1u) - plane;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = p[q];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                w[0][4 * q] = v[q].x; w[0][4 * q + 1] = v[q].y;
-                w[0][4 * q + 2] = v[q].z; w[0][4 * q + 3] = v[q].w;
-            }
+            for (int q = 0; q < 4; ++q) w[q] = byte_of4(p[q], b);
         } else {
-            uint4 v[8];
-            if constexpr (pair32_mode(MODE)) {
-                const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(a.in) + i0);
-                uint4 e[16];
-#pragma unroll
-                for (int q = 0; q < 16; ++q) e[q] = p[q];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    v[q].x = half2<MODE>(e[2 * q].x, e[2 * q].y);
-                    v[q].y = half2<MODE>(e[2 * q].z, e[2 * q].w);
-                    v[q].z = half2<MODE>(e[2 * q + 1].x, e[2 * q + 1].y);
-                    v[q].w = half2<MODE>(e[2 * q + 1].z, e[2 * q + 1].w);
-                }
-            } else {
-                const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in) + i0);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = p[q];
-            }
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in) + e0);
+            uint4 v0 = p[0], v1 = p[1];
             if constexpr (MODE == ENC_PAIR_XOR) {
-                const uint4* p2 = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in2) + i0);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint4 u = p2[q];
-                    v[q].x ^= u.x; v[q].y ^= u.y; v[q].z ^= u.z; v[q].w ^= u.w;
-                }
+                const uint4* p2 = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.in2) + e0);
+                const uint4 u0 = p2[0], u1 = p2[1];
+                v0.x ^= u0.x; v0.y ^= u0.y; v0.z ^= u0.z; v0.w ^= u0.w;
+                v1.x ^= u1.x; v1.y ^= u1.y; v1.z ^= u1.z; v1.w ^= u1.w;
             }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if constexpr (MODE == ENC_PLANE_LO) {
-                    w[0][2 * q] = lo_plane(v[q].x, v[q].y);
-                    w[0][2 * q + 1] = lo_plane(v[q].z, v[q].w);
-                } else {
-                    w[0][2 * q] = hi_plane(v[q].x, v[q].y);
-                    w[0][2 * q + 1] = hi_plane(v[q].z, v[q].w);
-                }
-                if constexpr (NS == 2) {
-                    w[1][2 * q] = lo_plane(v[q].x, v[q].y);
-                    w[1][2 * q + 1] = lo_plane(v[q].z, v[q].w);
-                }
-            }
+            const bool low = MODE == ENC_PLANE_LO || (two_stream_mode(MODE) && plane == 1);
+            w[0] = low ? lo_plane(v0.x, v0.y) : hi_plane(v0.x, v0.y);
+            w[1] = low ? lo_plane(v0.z, v0.w) : hi_plane(v0.z, v0.w);
+            w[2] = low ? lo_plane(v1.x, v1.y) : hi_plane(v1.x, v1.y);
+            w[3] = low ? lo_plane(v1.z, v1.w) : hi_plane(v1.z, v1.w);
         }
     } else {
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) w[s][q] = 0;
-        for (int k = 0; k < nv; ++k) {
-            uint32_t b0, b1 = 0;
-            if constexpr (MODE == ENC_BYTES) {
-                b0 = static_cast<const uint8_t*>(a.in)[i0 + k];
-            } else {
-                const uint32_t x = input_word<MODE>(a, i0 + k);
-                b0 = MODE == ENC_PLANE_LO ? (x & 0xFFu) : (x >> 8);
-                b1 = x & 0xFFu;
-            }
-            w[0][k >> 2] |= b0 << (8 * (k & 3));
-            if constexpr (NS == 2) w[1][k >> 2] |= b1 << (8 * (k & 3));
+        w[0] = w[1] = w[2] = w[3] = 0;
+        for (uint32_t q = 0; q < cnt; ++q) {
+            const uint32_t s = symbol_at<MODE>(a, e0 + q, plane);
+            if (q < 4) w[0] |= s << (8 * q);
+            else if (q < 8) w[1] |= s << (8 * (q - 4));
+            else if (q < 12) w[2] |= s << (8 * (q - 8));
+            else w[3] |= s << (8 * (q - 12));
         }
     }
 }
+
+__device__ inline uint32_t sym_of(const uint32_t (&w)[4], int k) { return (w[k >> 2] >> (8 * (k & 3))) & 0xFFu; }
 
 __device__ inline uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
-
-// Inclusive scan of one u64 per thread over the block (two u32 counters
-// packed in one u64 never carry into each other here); *total = block sum.
-__device__ inline uint64_t block_inclusive_scan(uint64_t v, uint64_t* s_tmp, uint64_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t incl = v;
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) s_tmp[wave] = incl;
-    __syncthreads();
-    uint64_t before = 0, sum = 0;
-#pragma unroll
-    for (int w = 0; w < ENC_THREADS / 64; ++w) {
-        const uint64_t x = s_tmp[w];
-        if (w < wave) before += x;
-        sum += x;
-    }
-    *total = sum;
-    __syncthreads();  // s_tmp may be reused right after
-    return before + incl;
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
+    return v;
 }
 
-__device__ inline void set_status(WsHeader* ws, int32_t code) {
-    atomicCAS(&ws->status, 0, code);
-}
+__device__ inline void set_status(WsHeader* ws, int32_t code) { atomicCAS(&ws->status, 0, code); }
 
-struct Shared {
-    uint32_t stage[STAGE_LDS];     // payload image of the ticket (one stream at a time), padded
-    uint32_t enc[2][256];          // (code << 5) | len per stream
-    uint8_t len[2][256];
-    uint64_t incl[ENC_THREADS];    // inclusive scan of per-thread bits (stream 1 in the high half)
-    uint64_t tmp[4];
-    uint32_t cword[2][MAX_G];      // first payload word of each chunk, ticket-relative
-    uint32_t cbits[2][MAX_G];      // bits of each chunk
-    uint64_t tbase[2];
-    uint64_t tbits[2];
-    uint32_t twords[2];
-    uint64_t run[2];               // first payload word of the next ticket
-    uint32_t uncoded;
+// Tasks of range r when T tasks are split over R ranges.
+__device__ inline uint64_t range_first(uint64_t r, uint64_t T, uint64_t R) { return r * T / R; }
+
+// Where this lane works in a task: chunk, lane of the chunk, plane, symbols.
+struct Place {
+    uint64_t c;       // chunk
+    uint32_t j;       // lane of the chunk
+    uint32_t plane;   // stream
+    uint32_t m;       // symbols of the lane
+    bool valid;       // c < nc
 };
 
-// The code bits of 64 consecutive symbols as the count launch stores them
-// for the pack launch: stream 0 in bits 0-14, stream 1 in bits 16-30 (at
-// most 64 * 16 each), bit 31 set when a valid symbol has no code word.
-__device__ inline uint32_t pack_counts(uint64_t bits, bool unc) {
-    return (uint32_t)(bits & 0x7FFFu) | ((uint32_t)(bits >> 32) << 16) | (unc ? 0x80000000u : 0u);
-}
-__device__ inline uint64_t unpack_counts(uint32_t c) {
-    return (uint64_t)(c & 0x7FFFu) | ((uint64_t)((c >> 16) & 0x7FFFu) << 32);
-}
-
-// Bits of the thread's 64 symbols, per stream (nv valid); sets *unc when a
-// valid symbol has no code word.
-template <int NS>
-__device__ inline uint64_t count_bits(const uint8_t (&len)[2][256], const uint32_t w[][16], int nv, bool* unc) {
-    uint64_t packed = 0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        uint32_t bits = 0, mn = 16;
-        if (nv == SPT) {
-#pragma unroll
-            for (int k = 0; k < SPT; ++k) {
-                const uint32_t l = len[s][sym_of(w[s], k)];
-                bits += l;
-                mn = min(mn, l);
-            }
-        } else {
-            for (int k = 0; k < nv; ++k) {
-                const uint32_t l = len[s][sym_of(w[s], k)];
-                bits += l;
-                mn = min(mn, l);
-            }
-        }
-        *unc |= mn == 0;
-        packed |= (uint64_t)bits << (32 * s);
-    }
-    return packed;
+template <int P>
+__device__ inline Place place_of(const EncArgs& a, uint64_t task, uint32_t lane) {
+    const uint32_t r = lane >> 4, i = lane & 15u;
+    Place pl;
+    pl.plane = r % P;
+    pl.c = task * a.cpt + (r / P) * (16u >> a.lg) + (i >> a.lg);
+    pl.j = i & ((1u << a.lg) - 1u);
+    pl.valid = pl.c < a.nc;
+    const uint32_t mc = pl.valid ? (uint32_t)min<uint64_t>(a.chunk, a.n - pl.c * a.chunk) : 0u;
+    const uint32_t G = 1u << a.lg, full = mc / BLOCK, rest = mc % BLOCK;
+    const uint32_t whole = full > pl.j ? (full - pl.j + G - 1) >> a.lg : 0u;
+    pl.m = whole * BLOCK + ((full & (G - 1)) == pl.j && rest ? rest : 0u);
+    return pl;
 }
 
-// Pack the thread's code words into the stage at bit `pos`.  FULL: all 64
-// symbols valid (else the first nv; the rest are zero bytes and get no code
-// word).
-//   * Code words are looked up 16 at a time (one LDS latency per 16) and
-//     joined in pairs: a pair is at most 32 bits, so it enters the 64-bit
-//     accumulator in one step and completes at most one word.
-//   * No branches per pair.  Every pair ORs one word into the stage (which
-//     is zero before packing): the completed word, or zero into the word
-//     being filled.  A word shared with the neighbouring threads (the first
-//     and the last) gets each thread's bits by the same OR.
-template <bool FULL>
-__device__ inline void pack64(Shared& S, int s, uint32_t w[16], int nv, uint32_t pos) {
-    uint32_t widx = pos >> 5;
-    uint32_t used = pos & 31u;
-    uint64_t acc = 0;
-    // 16 symbols per round; the symbol words move down by 4 after each round
-    // (w is used up), so every index stays a constant without unrolling all
-    // 64 symbols
-    uint32_t* const ww = w;
-#pragma unroll 1
-    for (int g = 0; g < SPT / 16; ++g) {
-        uint32_t e[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t x = S.enc[s][sym_of(ww, i)];
-            e[i] = (FULL || 16 * g + i < nv) ? x : 0u;
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
-            const uint32_t l0 = e0 & 31u, l1 = e1 & 31u;
-            const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);  // at most 32 bits
-            used += l0 + l1;
-            acc |= (uint64_t)c2 << ((64 - used) & 63);  // ends at bit `used` from the top
-            const uint32_t full = used >> 5;             // used <= 63
-            atomicOr(&S.stage[st_at(widx)], (uint32_t)(acc >> 32) & (0u - full));
-            acc <<= 32 * full;
-            widx += full;
-            used &= 31u;
-        }
-#pragma unroll
-        for (int i = 0; i < 12; ++i) ww[i] = ww[i + 4];
-    }
-    if (used) atomicOr(&S.stage[st_at(widx)], (uint32_t)(acc >> 32));
+// First element of block t of the lane.
+__device__ inline uint64_t block_elem(const EncArgs& a, const Place& pl, uint32_t t) {
+    return pl.c * a.chunk + ((uint64_t)(t << a.lg) + pl.j) * BLOCK;
 }
 
-// Code bits of the decode unit of the thread (the 4 threads of a unit are
-// consecutive lanes of a wave); every lane receives its unit's total.
-__device__ inline uint32_t unit_bits(uint32_t mine) {
-    uint32_t v = mine + __shfl_xor(mine, 1, 64);
-    return v + __shfl_xor(v, 2, 64);
-}
-
-// First ticket of workgroup w when T tickets are split over W workgroups.
-__device__ inline uint64_t first_ticket(uint64_t w, uint64_t T, uint64_t W) { return w * T / W; }
-
-// Bits of each chunk of ticket `tk` (per stream, lanes 0..nch-1 of wave s
-// receive chunk `lane`'s bits); w keeps the symbols when the ticket is one
-// segment, and incl/tmp/len are the caller's LDS.  STORED: the bits come
-// from the count launch's per-thread totals (the symbols are loaded only
-// when the ticket is one segment); otherwise they are summed here from the
-// symbols and stored for the pack launch.
-template <int MODE, bool STORED>
-__device__ inline void ticket_bits(const EncArgs& a, uint64_t tk, const uint8_t (&len)[2][256],
-                                   uint64_t* incl_lds, uint64_t* tmp, uint32_t w[][16], bool* unc,
-                                   uint32_t* nch_out, uint32_t* nseg_out, uint64_t* chunk_acc) {
-    constexpr int NS = Streams<MODE>::value;
-    const int tid = threadIdx.x;
-    const uint64_t c0 = tk * a.G;
-    const uint32_t nch = (uint32_t)min<uint64_t>(a.G, a.nc - c0);
-    const uint64_t tbeg = c0 * a.chunk;
-    const uint64_t tend = min(tbeg + (uint64_t)a.G * a.chunk, a.n);
-    const uint32_t nseg = (uint32_t)((tend - tbeg + SEG - 1) / SEG);
-    uint64_t acc = 0;
-    for (uint32_t g = 0; g < nseg; ++g) {
-        const uint64_t i0 = tbeg + (uint64_t)g * SEG + (uint64_t)tid * SPT;
-        const int nv = i0 >= tend ? 0 : (int)min<uint64_t>(SPT, tend - i0);
-        uint64_t bits;
-        if constexpr (STORED) {
-            const uint32_t c = nv > 0 ? a.counts[i0 / SPT] : 0u;
-            if (nseg == 1) load64<MODE>(a, i0, nv, w);
-            bits = unpack_counts(c);
-            *unc |= (c >> 31) != 0;
-        } else {
-            load64<MODE>(a, i0, nv, w);
-            bool u = false;
-            bits = count_bits<NS>(len, w, nv, &u);
-            *unc |= u;
-            if (nv > 0) a.counts[i0 / SPT] = pack_counts(bits, u);
-        }
-        uint64_t total;
-        const uint64_t incl = block_inclusive_scan(bits, tmp, &total);
-        if (nseg == 1) incl_lds[tid] = incl;
-        acc += total;
-    }
-    *nch_out = nch;
-    *nseg_out = nseg;
-    *chunk_acc = acc;
-}
-
-// Bits of chunk `lane` of the ticket for stream s (0 for lanes >= nch).
-__device__ inline uint32_t chunk_bits_of(const uint64_t* incl_lds, int lane, int s, uint32_t nch,
-                                         uint32_t nseg, uint32_t L, uint64_t chunk_acc) {
-    if (nseg == 1) {
-        if (lane >= (int)nch) return 0;
-        const uint64_t hi = incl_lds[(lane + 1) * L - 1];
-        const uint64_t lo = lane ? incl_lds[lane * L - 1] : 0ull;
-        return (uint32_t)((hi - lo) >> (32 * s));
-    }
-    return lane == 0 ? (uint32_t)(chunk_acc >> (32 * s)) : 0u;
-}
-
-// Launch 1: payload words of every workgroup's tickets, per stream.  Each
-// pack workgroup's ticket range is counted by F workgroups (more loads in
-// flight than one workgroup walking it), whose totals follow each other.
+// Launch 1: word counts of every lane, words of every range.
 template <int MODE>
 __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
-    constexpr int NS = Streams<MODE>::value;
+    constexpr int P = Streams<MODE>::value;
     __shared__ uint8_t len[2][256];
-    __shared__ uint64_t incl[ENC_THREADS];
-    __shared__ uint64_t tmp[4];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t lane = tid & 63;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) len[s][tid] = (uint8_t)(a.st[s].cb->enc[tid] & 31u);
+    for (int s = 0; s < P; ++s) len[s][tid] = (uint8_t)(a.st[s].cb->enc[tid] & 31u);
     __syncthreads();
-    const uint32_t L = a.chunk >= SEG ? ENC_THREADS : a.chunk / SPT;
-    // the range of pack workgroup w = blockIdx / F, split F ways
-    const uint64_t pw = blockIdx.x / a.fsplit, f = blockIdx.x % a.fsplit;
-    const uint64_t r0 = first_ticket(pw, a.ntickets, a.npack), r1 = first_ticket(pw + 1, a.ntickets, a.npack);
-    const uint64_t t0 = r0 + (r1 - r0) * f / a.fsplit, t1 = r0 + (r1 - r0) * (f + 1) / a.fsplit;
-    uint64_t words = 0;  // wave s, stream s
+    const uint64_t r = (uint64_t)blockIdx.x * ENC_WAVES + (tid >> 6);
+    const uint64_t t0 = range_first(r, a.ntasks, a.nranges), t1 = range_first(r + 1, a.ntasks, a.nranges);
+    uint64_t words[2] = {0, 0}, bits_all[2] = {0, 0};
+    bool unc = false;
     for (uint64_t tk = t0; tk < t1; ++tk) {
-        uint32_t w[NS][16];
-        bool unc = false;
-        uint32_t nch, nseg;
-        uint64_t acc;
-        ticket_bits<MODE, false>(a, tk, len, incl, tmp, w, &unc, &nch, &nseg, &acc);
-        __syncthreads();
-        if (wave < NS) {
-            const uint32_t cb = chunk_bits_of(incl, lane, wave, nch, nseg, L, acc);
-            words += wave_sum_u64((cb + 31) >> 5);
+        const Place pl = place_of<P>(a, tk, lane);
+        const uint8_t* ln = len[P == 1 ? 0 : pl.plane];
+        uint32_t bits = 0, mn = 16;
+        const uint32_t nb = (pl.m + BLOCK - 1) / BLOCK;
+        for (uint32_t t = 0; t < nb; ++t) {
+            const uint32_t cnt = min(BLOCK, pl.m - t * BLOCK);
+            uint32_t w[4];
+            block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, w);
+            if (cnt == BLOCK) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const uint32_t l = ln[sym_of(w, k)];
+                    bits += l;
+                    mn = min(mn, l);
+                }
+            } else {
+                for (uint32_t k = 0; k < cnt; ++k) {
+                    const uint32_t l = ln[sym_of(w, (int)k)];
+                    bits += l;
+                    mn = min(mn, l);
+                }
+            }
         }
-        __syncthreads();
+        unc |= mn == 0;
+        const uint32_t nw = (bits + 31) >> 5;
+        if (pl.valid) a.st[pl.plane].nw[(pl.c << a.lg) + pl.j] = (uint16_t)nw;
+        words[0] += pl.plane ? 0u : nw;
+        words[1] += pl.plane ? nw : 0u;
+        bits_all[0] += pl.plane ? 0u : bits;
+        bits_all[1] += pl.plane ? bits : 0u;
     }
-    if (wave < NS && lane == 0) a.st[wave].wg_words[blockIdx.x] = words;
+    // words and bits per stream
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+        const uint64_t wsum = wave_sum_u64(words[s]);
+        const uint64_t bsum = wave_sum_u64(bits_all[s]);
+        if (lane == 0) {
+            a.st[s].range_words[r] = wsum;
+            if (bsum) atomicAdd(reinterpret_cast<unsigned long long*>(&a.st[s].ws->bits), (unsigned long long)bsum);
+        }
+    }
+    const bool any_unc = __ballot(unc) != 0;
+    if (any_unc && lane == 0) {
+#pragma unroll
+        for (int s = 0; s < P; ++s) set_status(a.st[s].ws, LECB_ERR_UNCODED_SYMBOL);
+    }
 }
 
-// Launch 2: pack (see the top of the file).  A 256-lane workgroup is one
-// wave per SIMD, so ENC_WGS_PER_CU workgroups per CU are as many waves per
-// SIMD: the second launch bound (minimum waves per SIMD) allows registers for
-// that many.
-template <int MODE>
-__global__ __launch_bounds__(ENC_THREADS, ENC_WGS_PER_CU) void encode_kernel(EncArgs a) {
-    constexpr int NS = Streams<MODE>::value;
-    __shared__ Shared S;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const uint32_t e = a.st[s].cb->enc[tid];
-        S.enc[s][tid] = e;
-        S.len[s][tid] = (uint8_t)(e & 31u);
-    }
-    // first payload word of this workgroup: the words of workgroups 0..w-1,
-    // summed by all threads (independent loads, one latency)
-    {
-        uint64_t part[2] = {0, 0};
-#pragma unroll 4
-        for (uint32_t v = tid; v < blockIdx.x * a.fsplit; v += ENC_THREADS) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) part[s] += a.st[s].wg_words[v];
-        }
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const uint64_t x = wave_sum_u64(part[s]);
-            if (lane == 0) S.incl[NS * wave + s] = x;
-        }
-    }
-    if (tid == 0) S.uncoded = 0;
-    __syncthreads();
-    if (tid < NS) {
-        uint64_t sum = 0;
-        for (int v = 0; v < ENC_THREADS / 64; ++v) sum += S.incl[NS * v + tid];
-        S.run[tid] = sum;
-    }
-    __syncthreads();
-    const uint32_t K = 1u << a.log2k;
-    const uint32_t L = a.chunk >= SEG ? ENC_THREADS : a.chunk / SPT;  // threads per chunk in a segment
-    const uint64_t t0 = first_ticket(blockIdx.x, a.ntickets, gridDim.x);
-    const uint64_t t1 = first_ticket(blockIdx.x + 1ull, a.ntickets, gridDim.x);
-
-    for (uint64_t T = t0; T < t1; ++T) {
-        const uint64_t c0 = T * a.G;                                   // first chunk
-        const uint64_t tbeg = c0 * a.chunk;                            // first symbol
-        const uint64_t tend = min(tbeg + (uint64_t)a.G * a.chunk, a.n);
-
-        // ---- A: bits of every chunk of the ticket
-        uint32_t w[NS][16];
-        bool unc = false;
-        uint32_t nch, nseg;
-        uint64_t chunk_bits_acc;  // nseg > 1: the one chunk's bits (packed per stream)
-        ticket_bits<MODE, true>(a, T, S.len, S.incl, S.tmp, w, &unc, &nch, &nseg, &chunk_bits_acc);
-        if (unc) atomicOr(&S.uncoded, 1u);
-        __syncthreads();
-        // ---- B: chunk sizes, word offsets and the ticket's place in the
-        // payload (wave s handles stream s)
-        if (wave < NS) {
-            const int s = wave;
-            const StreamArgs& sa = a.st[s];
-            const uint32_t cb = chunk_bits_of(S.incl, lane, s, nch, nseg, L, chunk_bits_acc);
-            const uint32_t cw = (cb + 31) >> 5;
-            uint32_t incl = cw;
+// Launch 2: first payload word of every range (exclusive scan of the ranges'
+// words, one stream after the other), total words, capacity checks.
+__global__ __launch_bounds__(OFF_THREADS) void offsets_kernel(EncArgs a, int ns) {
+    __shared__ uint64_t part[OFF_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int s = 0; s < ns; ++s) {
+        const StreamArgs& st = a.st[s];
+        uint64_t run = 0;
+        for (uint32_t b = 0; b < a.nranges; b += OFF_THREADS) {
+            const uint32_t i = b + tid;
+            const uint64_t v = i < a.nranges ? st.range_words[i] : 0ull;
+            uint64_t incl = v;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t t = __shfl_up(incl, o, 64);
+                const uint64_t t = __shfl_up(incl, o, 64);
                 if (lane >= o) incl += t;
             }
-            if (lane < (int)nch) {
-                S.cword[s][lane] = incl - cw;
-                S.cbits[s][lane] = cb;
+            if (lane == 63) part[wave] = incl;
+            __syncthreads();
+            uint64_t before = 0, total = 0;
+#pragma unroll
+            for (int w = 0; w < OFF_THREADS / 64; ++w) {
+                before += w < wave ? part[w] : 0ull;
+                total += part[w];
             }
-            const uint32_t tw = __shfl(incl, 63, 64);
-            const uint64_t tbits = wave_sum_u64(cb);
-            const uint64_t base = S.run[s];
-            if (lane < (int)nch) sa.table[c0 + lane] = (uint32_t)(base + incl);
-            if (lane == 0) {
-                S.twords[s] = tw;
-                S.tbase[s] = base;
-                S.run[s] = base + tw;
-                atomicAdd(reinterpret_cast<unsigned long long*>(&sa.ws->bits), (unsigned long long)tbits);
-                if (T == a.ntickets - 1)
-                    __hip_atomic_store(&sa.ws->words, base + tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (S.uncoded) set_status(sa.ws, LECB_ERR_UNCODED_SYMBOL);
-                if (base + tw >= (1ull << 32)) set_status(sa.ws, LECB_ERR_TOO_LARGE);
-                else if (base + tw > sa.capacity_words) set_status(sa.ws, LECB_ERR_CAPACITY);
-            }
+            if (i < a.nranges) st.range_words[i] = run + before + incl - v;
+            run += total;
+            __syncthreads();
         }
-        __syncthreads();
+        if (tid == 0) {
+            st.ws->words = run;
+            if (run >= (1ull << 32)) set_status(st.ws, LECB_ERR_TOO_LARGE);
+            else if (run > st.capacity_words) set_status(st.ws, LECB_ERR_CAPACITY);
+        }
+    }
+}
 
-        // ---- C: pack, segment by segment (the symbols of a segment are loaded
-        // once for both streams), stream by stream
-        uint32_t TB[NS];      // S > 1: chunk-relative bit offset of the segment
-        uint32_t carry[NS];   // S > 1: partial last word of the previous segment
+// Launch 3: pack (see the top of the file).
+template <int MODE, int LG>
+__global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
+    constexpr int P = Streams<MODE>::value;
+    constexpr uint32_t G = 1u << LG;
+    __shared__ uint32_t enc[2][256];
+    const int tid = threadIdx.x;
+    const uint32_t lane = tid & 63;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) TB[s] = carry[s] = 0;
-        for (uint32_t g = 0; g < nseg; ++g) {
-            const uint64_t i0 = tbeg + (uint64_t)g * SEG + (uint64_t)tid * SPT;
-            const int nv = i0 >= tend ? 0 : (int)min<uint64_t>(SPT, tend - i0);
-            uint64_t incl, own, seg_total = 0;
-            if (nseg == 1) {
-                incl = S.incl[tid];
-                own = incl - (tid ? S.incl[tid - 1] : 0ull);
-            } else {
-                // the segment's scan again (step A kept only totals)
-                const uint32_t c = nv > 0 ? a.counts[i0 / SPT] : 0u;
-                load64<MODE>(a, i0, nv, w);
-                own = unpack_counts(c);
-                incl = block_inclusive_scan(own, S.tmp, &seg_total);
+    for (int s = 0; s < P; ++s) enc[s][tid] = a.st[s].cb->enc[tid];
+    __syncthreads();
+    const uint64_t r = (uint64_t)blockIdx.x * ENC_WAVES + (tid >> 6);
+    const uint64_t t0 = range_first(r, a.ntasks, a.nranges), t1 = range_first(r + 1, a.ntasks, a.nranges);
+    const uint32_t my_plane = (lane >> 4) % P;
+    // this lane's stream, picked by conditional moves (no index into the arguments)
+    const bool second = P == 2 && my_plane == 1;
+    const uint16_t* const nwt = second ? a.st[1].nw : a.st[0].nw;
+    uint32_t* const table = second ? a.st[1].table : a.st[0].table;
+    uint32_t* const payload = second ? a.st[1].payload : a.st[0].payload;
+    WsHeader* const my_ws = second ? a.st[1].ws : a.st[0].ws;
+    // a stream with a status already (a byte without a code word, too many
+    // words) gets no payload
+    const bool skip = __hip_atomic_load(&my_ws->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    uint64_t base = (second ? a.st[1].range_words : a.st[0].range_words)[r];   // first payload word of the range
+    const uint32_t* e_tab = enc[second ? 1 : 0];
+
+    for (uint64_t tk = t0; tk < t1; ++tk) {
+        const Place pl = place_of<P>(a, tk, lane);
+        const uint32_t N = pl.valid ? nwt[(pl.c << LG) + pl.j] : 0u;
+        // the chunk's words, its first word, the task's words (per stream)
+        const uint32_t wc = group_sum<LG>(N);
+        const uint64_t mine = (pl.j == G - 1) ? (uint64_t)wc << (32 * my_plane) : 0ull;
+        uint64_t incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t t = __shfl_up(incl, o, 64);
+            if (lane >= (uint32_t)o) incl += t;
+        }
+        const uint64_t at_last = __shfl(incl, (int)(lane | (G - 1)), 64);
+        const uint64_t task_words = __shfl(incl, 63, 64);
+        const uint32_t cend = (uint32_t)(at_last >> (32 * my_plane));     // task-relative end of the chunk
+        const uint64_t cstart = base + cend - wc;
+        base += (uint32_t)(task_words >> (32 * my_plane));
+        if (pl.valid && pl.j == 0) table[pl.c] = (uint32_t)(cstart + wc);
+        uint32_t* const out = payload + cstart;
+
+        // reads of words 0 and 1
+        uint32_t b0, n0, b1, n1;
+        group_count<LG>(N >= 1, b0, n0);
+        group_count<LG>(N >= 2, b1, n1);
+        uint32_t posA = b0, posB = n0 + b1, cons = n0 + n1;
+        uint32_t nextk = min(N, 2u);
+        bool crossed = false;
+        uint64_t acc = 0;
+        uint32_t fill = 0;
+        const bool wr = !skip && pl.valid;
+        const uint32_t nblk = (wave_max_u32(pl.m) + BLOCK - 1) / BLOCK;
+        for (uint32_t t = 0; t < nblk; ++t) {
+            const uint32_t cnt = pl.m > t * BLOCK ? min(BLOCK, pl.m - t * BLOCK) : 0u;
+            uint32_t w[4] = {0, 0, 0, 0};
+            if (cnt) block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, w);
+            uint32_t e[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t x = e_tab[sym_of(w, k)];
+                e[k] = (uint32_t)k < cnt ? x : 0u;
             }
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const StreamArgs& st = a.st[s];
-                const uint32_t twords = S.twords[s];
-                const uint32_t mine = (uint32_t)(own >> (32 * s));  // this thread's bits
-                uint32_t pos, ch;
-                uint32_t r0 = 0, w0 = 0, touched;
-                if (nseg == 1) {
-                    ch = tid / L;
-                    const uint64_t before = ch ? S.incl[ch * L - 1] : 0ull;
-                    const uint32_t ts = (uint32_t)((incl - before) >> (32 * s)) - mine;  // chunk-relative start bit
-                    pos = (ch < nch ? S.cword[s][ch] * 32u : 0u) + ts;
-                    touched = twords;
-                    for (uint32_t k = tid; k < touched; k += ENC_THREADS) S.stage[st_at(k)] = 0u;
-                } else {
-                    ch = 0;
-                    const uint32_t seg_bits = (uint32_t)(seg_total >> (32 * s));
-                    const uint32_t excl = (uint32_t)(incl >> (32 * s)) - mine;
-                    r0 = TB[s] & 31u;
-                    w0 = TB[s] >> 5;
-                    pos = r0 + excl;
-                    touched = (r0 + seg_bits + 31) >> 5;
-                    for (uint32_t k = tid; k <= touched; k += ENC_THREADS) S.stage[st_at(k)] = k ? 0u : carry[s];
-                    TB[s] += seg_bits;
+            for (int q = 0; q < 8; ++q) {
+                // before the pair: the lanes that completed a word read the next one
+                const bool act = 2u * q < cnt;
+                const bool fetch = act && crossed && nextk < N;
+                uint32_t bf, nf;
+                group_count<LG>(fetch, bf, nf);
+                posB = fetch ? cons + bf : posB;
+                nextk += fetch ? 1u : 0u;
+                cons += nf;
+                crossed = false;
+                // the pair's code words (at most 32 bits) into the accumulator
+                const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
+                const uint32_t l1 = e1 & 31u;
+                const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);
+                fill += (e0 & 31u) + l1;
+                acc |= (uint64_t)c2 << ((64u - fill) & 63u);
+                if (fill >= 32) {
+                    if (wr) out[posA] = (uint32_t)(acc >> 32);
+                    acc <<= 32;
+                    fill -= 32;
+                    posA = posB;
+                    crossed = true;
                 }
-                // the unit's code bits: unit u of the ticket's chunk ch (units
-                // past n hold no symbols and get 0)
-                {
-                    const uint32_t ub = unit_bits(mine);
-                    const uint64_t u = nseg == 1
-                                           ? (c0 + ch) * K + (tid % L) / THREADS_PER_UNIT
-                                           : c0 * K + (uint64_t)g * (SEG / LECB_UNIT_SYMBOLS) + tid / THREADS_PER_UNIT;
-                    if ((tid & (THREADS_PER_UNIT - 1)) == 0 && ch < nch) st.ulen[u] = (uint16_t)ub;
-                }
-                __syncthreads();
-                if (nv == SPT && ch < nch)
-                    pack64<true>(S, s, w[s], nv, pos);
-                else if (nv > 0 && ch < nch)
-                    pack64<false>(S, s, w[s], nv, pos);
-                __syncthreads();  // stage complete
-                const uint64_t tbase = S.tbase[s];
-                const bool write_ok = tbase + twords <= st.capacity_words && !S.uncoded;
-                if (nseg == 1) {
-                    if (write_ok) {
-                        uint32_t* dst = st.payload + tbase;
-                        uint32_t k = tid;
-                        for (; k + 3 * ENC_THREADS < twords; k += 4 * ENC_THREADS) {
-                            uint32_t v[4];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) v[q] = S.stage[st_at(k + q * ENC_THREADS)];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) dst[k + q * ENC_THREADS] = v[q];
-                        }
-                        for (; k < twords; k += ENC_THREADS) dst[k] = S.stage[st_at(k)];
-                    }
-                } else {
-                    const bool last_seg = g + 1 == nseg;
-                    const uint32_t full = TB[s] / 32 - w0;  // words completed by this segment
-                    const uint32_t nwrite = last_seg ? touched : full;
-                    if (write_ok) {
-                        uint32_t* dst = st.payload + tbase + w0;
-                        for (uint32_t k = tid; k < nwrite; k += ENC_THREADS) dst[k] = S.stage[st_at(k)];
-                    }
-                    carry[s] = S.stage[st_at(full)];
-                }
-                __syncthreads();
             }
         }
-        // a short last chunk of a chunk size above SEG: its units past the
-        // last segment hold no symbols
-        if (a.chunk > SEG && nseg * (SEG / LECB_UNIT_SYMBOLS) < K) {
+        if (fill && wr) out[posA] = (uint32_t)(acc >> 32);
+        // header padding: the wave of the last task
+        if (tk + 1 == a.ntasks) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                for (uint32_t u = nseg * (SEG / LECB_UNIT_SYMBOLS) + tid; u < K; u += ENC_THREADS)
-                    a.st[s].ulen[c0 * K + u] = 0;
-        }
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const StreamArgs& st = a.st[s];
-            if (c0 + nch == a.nc) {
-                for (uint64_t b = st.table_pad_from + tid; b < st.table_pad_to; b += ENC_THREADS)
-                    st.stream[b] = 0;
-                for (uint64_t b = st.ulen_pad_from + tid; b < st.ulen_pad_to; b += ENC_THREADS)
-                    st.stream[b] = 0;
+            for (int s = 0; s < P; ++s) {
+                const StreamArgs& sa = a.st[s];
+                for (uint64_t b = sa.table_pad_from + lane; b < sa.table_pad_to; b += 64) sa.stream[b] = 0;
+                for (uint64_t b = sa.nw_pad_from + lane; b < sa.nw_pad_to; b += 64) sa.stream[b] = 0;
             }
         }
-        __syncthreads();
     }
 
-    // ---- exit: the last workgroup publishes the results and resets the workspace
-    if (tid == 0) {
+    // ---- exit: the last wave publishes the results and resets the workspace
+    if (lane == 0) {
         __threadfence();
         WsHeader* ws0 = a.st[0].ws;
         const uint32_t done = __hip_atomic_fetch_add(&ws0->exit_count, 1u, __ATOMIC_ACQ_REL,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        if (done == gridDim.x - 1) {
+        if (done == a.nranges - 1) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
+            for (int s = 0; s < P; ++s) {
                 WsHeader* ws = a.st[s].ws;
                 const uint64_t words = __hip_atomic_load(&ws->words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const uint64_t bits = __hip_atomic_load(&ws->bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -686,88 +444,73 @@ hipError_t with_mode(int mode, F&& f) {
     }
 }
 
+template <typename F>
+hipError_t with_lg(uint32_t lg, F&& f) {
+    switch (lg) {
+        case 0: return f(std::integral_constant<int, 0>{});
+        case 1: return f(std::integral_constant<int, 1>{});
+        case 2: return f(std::integral_constant<int, 2>{});
+        case 3: return f(std::integral_constant<int, 3>{});
+        case 4: return f(std::integral_constant<int, 4>{});
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 int launch_encode(const EncodeLaunch& L, void* stream) {
+    if (L.mode < 0 || L.mode >= ENC_NUM_MODES) return LECB_ERR_INVALID_ARG;
     EncArgs a{};
     a.in = L.in;
     a.in2 = L.in2;
     a.n = L.n;
     a.chunk = L.chunk;
-    a.log2k = (uint32_t)ilog2(units_per_chunk(L.chunk));
+    a.lg = (uint32_t)ilog2(lanes_per_chunk(L.chunk));
     a.nc = L.nc;
-    a.counts = L.counts;
-    if (!a.counts) return LECB_ERR_INVALID_ARG;
-    a.G = L.chunk >= SEG ? 1u : SEG / L.chunk;
-    a.S = L.chunk > SEG ? L.chunk / SEG : 1u;
-    a.ntickets = (L.nc + a.G - 1) / a.G;
-    const int ns = pair_mode(L.mode) ? 2 : 1;
+    const int ns = two_stream_mode(L.mode) ? 2 : 1;
+    a.cpt = (4u / (uint32_t)ns) * (16u >> a.lg);
+    a.ntasks = (L.nc + a.cpt - 1) / a.cpt;
     for (int s = 0; s < ns; ++s)
         if (!L.st[s].cb || !L.st[s].out || !L.st[s].res || !L.st[s].ws) return LECB_ERR_INVALID_ARG;
-    const uint64_t tb = table_bytes(L.nc), ub = ulen_bytes(L.nc, L.chunk);
+    const uint64_t tb = table_bytes(L.nc), cb = count_bytes(L.nc, L.chunk);
     for (int s = 0; s < ns; ++s) {
         StreamArgs& st = a.st[s];
         st.cb = L.st[s].cb;
         st.stream = L.st[s].out;
         st.table = reinterpret_cast<uint32_t*>(L.st[s].out);
-        st.ulen = reinterpret_cast<uint16_t*>(L.st[s].out + tb);
-        st.payload = reinterpret_cast<uint32_t*>(L.st[s].out + tb + ub);
-        st.header_bytes = tb + ub;
-        st.capacity_words = (L.st[s].capacity - (tb + ub)) / 4;
+        st.nw = reinterpret_cast<uint16_t*>(L.st[s].out + tb);
+        st.payload = reinterpret_cast<uint32_t*>(L.st[s].out + tb + cb);
+        st.header_bytes = tb + cb;
+        st.capacity_words = (L.st[s].capacity - (tb + cb)) / 4;
         st.table_pad_from = 4 * L.nc;
         st.table_pad_to = tb;
-        st.ulen_pad_from = tb + 2 * L.nc * units_per_chunk(L.chunk);
-        st.ulen_pad_to = tb + ub;
+        st.nw_pad_from = tb + 2 * L.nc * lanes_per_chunk(L.chunk);
+        st.nw_pad_to = tb + cb;
         st.res = L.st[s].res;
         st.ws = L.st[s].ws;
-        st.wg_words = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);  // room for nc >= grid values
+        st.range_words = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);  // room for nc >= nranges values
     }
-    // Both launches split the tickets over the same workgroups (static
-    // ranges; no workgroup waits for another).  By default the grid is the
-    // number of pack workgroups that fit on all compute units together, at
-    // most ENC_WGS_PER_CU per unit: measured on 32 Mi int8 symbols, byte-mode
-    // pack workgroups at 2 per CU took 70 us against 89 at 3 and 108 at 4 (the
-    // ones that fit), and the two-plane mode is fastest at the 2 that fit.
-    // Long inputs (at least ENC_LONG_SEGS segments per workgroup at that
-    // grid) take 3 per CU, even where only 2 fit: the finer ticket ranges
-    // even out the workgroups' ends (512 Mi 16-bit words in 65536-symbol
-    // chunks: 0.99 ms against 1.09; 4 GiB of bytes: no change, ~4.9 ms).
-    uint64_t grid_wgs = L.grid;
-    if (L.mode < 0 || L.mode >= ENC_NUM_MODES) return LECB_ERR_INVALID_ARG;
-    if (grid_wgs == 0) {
-        // resident pack workgroups per CU, asked of the runtime once per
-        // (device, mode); concurrent first calls store the same value
-        static std::atomic<int> per_cu[MAX_DEVICES][ENC_NUM_MODES];
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return LECB_ERR_HIP;
-        int pc = per_cu[dev][L.mode].load(std::memory_order_relaxed);
-        if (pc == 0) {
-            int nb = 0;
-            const hipError_t e = with_mode(L.mode, [&](auto m) {
-                return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, encode_kernel<decltype(m)::value>,
-                                                                    ENC_THREADS, 0);
-            });
-            if (e != hipSuccess || nb < 1) return LECB_ERR_HIP;
-            pc = nb < ENC_WGS_PER_CU ? nb : ENC_WGS_PER_CU;
-            per_cu[dev][L.mode].store(pc, std::memory_order_relaxed);
-        }
-        const uint64_t cus = (uint64_t)device_cu_count();
-        grid_wgs = cus * pc;
-        if (a.ntickets * a.S >= ENC_LONG_SEGS * grid_wgs) grid_wgs = cus * ENC_WGS_PER_CU_LONG;
-    }
-    const uint64_t nwg = grid_wgs < a.ntickets ? grid_wgs : a.ntickets;
+    // Ranges: ENC_WAVES_PER_CU waves per compute unit when there are tasks
+    // enough, never more ranges than tasks (a range is at least one task, so
+    // at most nc of them fit the workspace).
+    const uint64_t cus = (uint64_t)device_cu_count();
+    if (cus == 0) return LECB_ERR_HIP;
+    uint64_t waves = cus * ENC_WAVES_PER_CU;
+    if (waves > a.ntasks) waves = a.ntasks;
+    const uint64_t nwg = (waves + ENC_WAVES - 1) / ENC_WAVES;
+    a.nranges = (uint32_t)(nwg * ENC_WAVES);   // at most ntasks + 3 <= nc + 3: the workspace has room
     const dim3 grid((uint32_t)nwg), block(ENC_THREADS);
-    // the workspace holds one total per chunk: F * W of them must fit
-    a.npack = (uint32_t)nwg;
-    a.fsplit = 4 * nwg <= a.nc ? 4u : 1u;
-    const dim3 cgrid((uint32_t)(nwg * a.fsplit));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    with_mode(L.mode, [&](auto m) {
+    const hipError_t e = with_mode(L.mode, [&](auto m) {
         constexpr int M = decltype(m)::value;
-        hipLaunchKernelGGL(count_kernel<M>, cgrid, block, 0, hs, a);
-        hipLaunchKernelGGL(encode_kernel<M>, grid, block, 0, hs, a);
-        return hipSuccess;
+        hipLaunchKernelGGL(count_kernel<M>, grid, block, 0, hs, a);
+        hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(OFF_THREADS), 0, hs, a, ns);
+        return with_lg(a.lg, [&](auto g) {
+            hipLaunchKernelGGL((pack_kernel<M, decltype(g)::value>), grid, block, 0, hs, a);
+            return hipSuccess;
+        });
     });
+    if (e != hipSuccess) return LECB_ERR_INVALID_ARG;
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

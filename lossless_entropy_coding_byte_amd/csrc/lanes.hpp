@@ -1,0 +1,100 @@
+// Lane geometry of stream format v3 and the wave-level helpers the encoder
+// and the decoder share.
+//
+// A chunk is coded as G = min(chunk/256, 16) lanes; 16-symbol block b of the
+// chunk belongs to lane b mod G.  On the GPU one hardware lane runs one coder
+// lane, and a wave of 64 is four rows of 16: row r holds plane r % P (P byte
+// planes handled together) of the 16/G chunks of row group r / P, lane i of
+// the row being lane i mod G of chunk i / G of that row group.  The G lanes
+// of a chunk therefore sit side by side inside one row, which is what the
+// DPP broadcasts below rely on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lecb_internal.hpp"
+
+namespace lecb {
+
+constexpr uint32_t BLOCK = 16;   // symbols per block
+
+// Where hardware lane `lane` (0..63) of a wave sits for P planes and chunks of
+// G = 1 << LG lanes.
+struct LanePlace {
+    uint32_t plane;    // r % P
+    uint32_t chunk;    // chunk index within the wave's task (row group major)
+    uint32_t j;        // lane of that chunk
+};
+
+template <int P, int LG>
+__device__ inline LanePlace lane_place(uint32_t lane) {
+    const uint32_t r = lane >> 4, i = lane & 15u;
+    LanePlace p;
+    p.plane = r % P;
+    p.chunk = (r / P) * (16u >> LG) + (i >> LG);
+    p.j = i & ((1u << LG) - 1);
+    return p;
+}
+
+// Chunks of one wave's task.
+template <int P, int LG>
+constexpr uint32_t chunks_per_task() { return (4 / P) * (16u >> LG); }
+
+// Symbols of lane j of a chunk of m symbols (m <= chunk; S = chunk / G for a whole chunk).
+template <int LG>
+__device__ inline uint32_t lane_symbols(uint32_t m, uint32_t j) {
+    constexpr uint32_t G = 1u << LG;
+    const uint32_t full = m / BLOCK, rest = m % BLOCK;
+    const uint32_t whole = full > j ? (full - j + G - 1) >> LG : 0u;
+    return whole * BLOCK + ((full & (G - 1)) == j && rest ? rest : 0u);
+}
+
+// Value of lane `src` of the caller's row, broadcast over the row (DPP).
+template <int SRC>
+__device__ inline uint32_t row_bcast(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + SRC, 0xF, 0xF, false);
+}
+
+// Exclusive count of `f` over the lanes of the caller's group (G = 1 << LG
+// lanes, aligned inside a row) and the group's total.  Every lane of the wave
+// must call it (the broadcasts read neighbouring lanes).
+template <int LG>
+__device__ inline void group_count(bool f, uint32_t& before, uint32_t& total) {
+    const uint64_t m = __ballot(f);
+    const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint32_t q = p + (f ? 1u : 0u);  // inclusive
+    uint32_t first, last;
+    if constexpr (LG == 0) {
+        first = p;
+        last = q;
+    } else if constexpr (LG == 1) {
+        first = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0xA0, 0xF, 0xF, false);   // quad_perm [0,0,2,2]
+        last = (uint32_t)__builtin_amdgcn_mov_dpp((int)q, 0xF5, 0xF, 0xF, false);    // quad_perm [1,1,3,3]
+    } else if constexpr (LG == 2) {
+        first = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0x00, 0xF, 0xF, false);   // quad_perm [0,0,0,0]
+        last = (uint32_t)__builtin_amdgcn_mov_dpp((int)q, 0xFF, 0xF, 0xF, false);    // quad_perm [3,3,3,3]
+    } else if constexpr (LG == 3) {
+        const bool hi = (threadIdx.x & 8u) != 0;
+        const uint32_t f0 = row_bcast<0>(p), f8 = row_bcast<8>(p);
+        const uint32_t l7 = row_bcast<7>(q), l15 = row_bcast<15>(q);
+        first = hi ? f8 : f0;
+        last = hi ? l15 : l7;
+    } else {
+        first = row_bcast<0>(p);
+        last = row_bcast<15>(q);
+    }
+    before = p - first;
+    total = last - first;
+}
+
+// Sum of v over the caller's group of G = 1 << LG lanes (every lane gets it).
+template <int LG>
+__device__ inline uint32_t group_sum(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < (1 << LG); o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace lecb

@@ -47,15 +47,15 @@ struct CodebookArgs {
 
 // ---------------------------------------------------------------- workspace
 // Encode: exit counter and accumulators, followed by the payload words of
-// each encode workgroup (written by the count launch, read by the pack
-// launch of the same call).  Decode: exit counter + status.  A workspace
-// holds two of them (header + one u64 per chunk each, 256-byte aligned): a
-// two-stream encode uses both; everything else uses the first.  After them
-// comes one u32 per 64 consecutive symbols: the code bits of those symbols
-// per stream, written by the encode's count launch and read by its pack
-// launch.  Two more headers follow them, for the third and fourth stream of
-// a four-plane decode.  The last workgroup of every call resets the headers,
-// so only the first use needs a zero-filled workspace.
+// each count range (written by the count launch, turned into first words by
+// the offsets launch, read by the pack launch of the same call).  Decode:
+// exit counter + status.  A workspace holds two of them (header + one u64
+// per chunk and four more each, 256-byte aligned; there are never more
+// ranges than chunks + 3): a two-stream encode uses both; everything else
+// uses the first.
+// Two more headers follow, for the third and fourth stream of a four-plane
+// decode.  The last wave of every call resets the headers, so only the first
+// use needs a zero-filled workspace.
 struct WsHeader {
     uint32_t unused0;
     uint32_t exit_count;
@@ -76,22 +76,21 @@ inline int ilog2(uint32_t x) {
 inline bool valid_chunk(uint32_t chunk) {
     return chunk >= LECB_MIN_CHUNK && chunk <= LECB_MAX_CHUNK && (chunk & (chunk - 1)) == 0;
 }
-inline uint32_t units_per_chunk(uint32_t chunk) { return chunk / LECB_UNIT_SYMBOLS; }
-inline uint64_t table_bytes(uint64_t nc) { return align16(4 * nc); }
-// The u16 code-bit count of every decode unit (K per chunk), padded to 16 bytes.
-inline uint64_t ulen_bytes(uint64_t nc, uint32_t chunk) { return align16(2 * nc * units_per_chunk(chunk)); }
-// Bytes of one stream's part of the workspace: header + one flag per chunk.
-inline uint64_t ws_stream_bytes(uint64_t nc) { return (sizeof(WsHeader) + 8 * nc + 255) & ~uint64_t(255); }
-// Bytes of the per-64-symbol bit counts that follow the two stream parts.
-inline uint64_t ws_count_bytes(uint64_t n) { return (4 * ((n + 63) / 64) + 255) & ~uint64_t(255); }
-// Two more headers after the counts (the four streams of a four-plane decode).
-constexpr uint64_t WS_EXTRA_BYTES = 256;
-inline uint64_t ws_total_bytes(uint64_t n, uint64_t nc) {
-    return 2 * ws_stream_bytes(nc) + ws_count_bytes(n) + WS_EXTRA_BYTES;
+// Lanes per chunk: one per 256 symbols, at most 16 (a valid chunk has at least 256 symbols).
+inline uint32_t lanes_per_chunk(uint32_t chunk) {
+    return chunk / LECB_LANE_SYMBOLS < LECB_LANES_MAX ? chunk / LECB_LANE_SYMBOLS : LECB_LANES_MAX;
 }
+inline uint64_t table_bytes(uint64_t nc) { return align16(4 * nc); }
+// The u16 word count of every lane (G per chunk), padded to 16 bytes.
+inline uint64_t count_bytes(uint64_t nc, uint32_t chunk) { return align16(2 * nc * lanes_per_chunk(chunk)); }
+// Bytes of one stream's part of the workspace: header + one u64 per chunk and four more.
+inline uint64_t ws_stream_bytes(uint64_t nc) { return (sizeof(WsHeader) + 8 * (nc + 4) + 255) & ~uint64_t(255); }
+// Two more headers after the stream parts (the four streams of a four-plane decode).
+constexpr uint64_t WS_EXTRA_BYTES = 256;
+inline uint64_t ws_total_bytes(uint64_t nc) { return 2 * ws_stream_bytes(nc) + WS_EXTRA_BYTES; }
 // Offset of stream k's header (k < 4): the two stream parts, then the extra headers.
-inline uint64_t ws_header_offset(int k, uint64_t n, uint64_t nc) {
-    return k < 2 ? k * ws_stream_bytes(nc) : 2 * ws_stream_bytes(nc) + ws_count_bytes(n) + (k - 2) * sizeof(WsHeader);
+inline uint64_t ws_header_offset(int k, uint64_t nc) {
+    return k < 2 ? k * ws_stream_bytes(nc) : 2 * ws_stream_bytes(nc) + (k - 2) * sizeof(WsHeader);
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -125,7 +124,7 @@ struct EncodeStream {
     uint8_t* out;            // stream base
     uint64_t capacity;       // bytes
     lecb_result* res;
-    WsHeader* ws;            // followed by one u64 per chunk (workgroup word totals)
+    WsHeader* ws;            // followed by one u64 per chunk (word totals of the count ranges)
 };
 
 struct EncodeLaunch {
@@ -136,8 +135,6 @@ struct EncodeLaunch {
     uint32_t chunk;
     uint64_t nc;
     EncodeStream st[2];      // st[1] only for the two-stream modes
-    uint32_t* counts;        // workspace: one u32 per 64 symbols (count launch -> pack launch)
-    int grid;                // upper bound on workgroups (persistent grid)
 };
 int launch_encode(const EncodeLaunch& a, void* stream);
 

@@ -97,7 +97,7 @@ def plane_blocks(args):
 def compare_chunk_run(stream, n, chunk, c0, ref, ref_n):
     """Check that chunks [c0, c0 + nc(ref_n)) of `stream` (n symbols) are the
     oracle stream `ref` of those chunks' symbols: offset table (shifted by the
-    run's first payload word), per-unit metadata, payload words."""
+    run's first payload word), lane word counts, payload words."""
     import oracle
 
     nc = oracle.num_chunks(n, chunk)
@@ -112,7 +112,7 @@ def compare_chunk_run(stream, n, chunk, c0, ref, ref_n):
     a, b = oracle.count_span(n, chunk, c0, c0 + nb)
     ra, rb = oracle.count_span(ref_n, chunk, 0, nb)
     if not np.array_equal(stream[a:b], ref[ra:rb]):
-        raise AssertionError(f"unit metadata differs in chunks [{c0}, {c0 + nb})")
+        raise AssertionError(f"lane word counts differ in chunks [{c0}, {c0 + nb})")
     hb, rhb = oracle.header_bytes(n, chunk), oracle.header_bytes(ref_n, chunk)
     W = int(rt[-1])
     if ref.size != rhb + 4 * W:

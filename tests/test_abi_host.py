@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(lecb.exported_symbols()) == declared  # the binding mirrors the header 1:1
-    assert lecb.lecb_abi_version() == 2
+    assert lecb.lecb_abi_version() == 3
 
 
 def test_sizes_match_oracle():
@@ -43,16 +43,15 @@ def test_sizes_match_oracle():
 
 def test_workspace_bytes_contract():
     """The workspace holds, per stream (two), a 64-byte header and one 64-bit
-    slot per chunk, then one 32-bit count per 64 symbols, then 256 bytes for
-    the headers of a third and fourth stream; every part is 256-byte aligned,
-    and a bad chunk size gives 0."""
-    for n in (1, 63, 64, 65, 4096, 123457, 1 << 20, (1 << 32) + 5):
+    slot per chunk plus four more (the encoder's ranges: at most the chunks + 3),
+    then 256 bytes for the headers of a third and fourth stream; every part is
+    256-byte aligned."""
+    for n in (0, 1, 4096, 123457, 1 << 20, 1 << 26):
         for chunk in (256, 4096, 16384, 65536):
             nc = -(-n // chunk)
-            part = -(-(64 + 8 * nc) // 256) * 256
-            counts = -(-(4 * -(-n // 64)) // 256) * 256
+            part = -(-(64 + 8 * (nc + 4)) // 256) * 256
             ws = lecb.lecb_workspace_bytes(n, chunk)
-            assert ws == 2 * part + counts + 256, (n, chunk)
+            assert ws == 2 * part + 256, (n, chunk)
             assert ws % 256 == 0
     assert lecb.lecb_workspace_bytes(1000, 300) == 0
     assert lecb.lecb_workspace_bytes(1000, 128) == 0

@@ -12,6 +12,7 @@ import torch
 
 import oracle
 import workloads
+import oracle_jobs
 import lossless_entropy_coding_byte_amd as lecb
 from gpu_helpers import DEV, to_dev, codebook_for, gpu_encode, gpu_decode
 
@@ -576,52 +577,91 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def _lanes_chosen(n, chunk, nstreams):
-    """Lanes per decode workgroup the host picks for separate byte planes: the
-    largest of 1024, 512, 256 whose workgroups still give every compute unit one."""
-    units = -(-n // chunk) * (chunk // 256) * nstreams
-    return 1024 if units >= _cus() * 1024 else 512 if units >= _cus() * 512 else 256
+def _big_workgroups(n, chunk, waves_per_cu_needed=16, nstreams=1, planes_per_wave=1):
+    """Whether the decoder picks its big workgroups: a wave decodes 4 rows of 16
+    lanes (4 / planes_per_wave row groups of 16 / G chunks), and big workgroups
+    are taken when the waves of all streams give every compute unit
+    `waves_per_cu_needed` of them."""
+    G = min(chunk // 256, 16)
+    cpt = (4 // planes_per_wave) * (16 // G)
+    tasks = -(-(-(-n // chunk)) // cpt)
+    return tasks * (nstreams if planes_per_wave == 1 else 1) >= _cus() * waves_per_cu_needed
 
 
-@pytest.mark.parametrize("nt,chunk,extra", [(256, 4096, 0), (256, 65536, 0), (512, 4096, 4099),
-                                            (1024, 16384, 1001)])
-def test_decode_every_workgroup_size(nt, chunk, extra):
-    """The decoder picks 256, 512 or 1024 lanes per workgroup from the size of
-    the job (no override); inputs sized so that each size is chosen decode the
-    oracle's stream exactly (ragged tails and chunks that end inside a
-    workgroup included)."""
-    n = {256: 300_007 if chunk == 4096 else 700_001}.get(nt, _cus() * nt * 256 + extra)
-    assert _lanes_chosen(n, chunk, 1) == nt
-    _say(f"decode nt={nt} n={n} chunk={chunk}")
-    x = _gauss(40 + nt, n, 12.0)
+def _gpu_stream_against_oracle_blocks(xd, x, ln, chunk, dcb):
+    """GPU encode of x, the stream compared chunk by chunk with the oracle's
+    streams of blocks of x (oracle in worker processes); returns the stream."""
+    n = x.size
+    out = torch.empty(lecb.lecb_encoded_bound(n, chunk), dtype=torch.uint8, device=DEV)
+    res = lecb.new_results(1, DEV)
+    ws = lecb.new_workspace(n, chunk, DEV)
+    step = 1 << 22
+    with oracle_jobs.pool() as pool:
+        jobs = pool.map_async(oracle_jobs.plane_blocks, [(i, x[i:i + step], ln, chunk) for i in range(0, n, step)])
+        lecb.lecb_encode(xd, n, dcb.blob, chunk, out, res, ws)
+        r = lecb.results_to_numpy(res)[0]
+        assert int(r["status"]) == 0
+        got = out[: int(r["bytes"])].cpu().numpy()
+        covered = sum(oracle_jobs.check_blocks(got, n, chunk, blocks, off) for off, blocks in jobs.get())
+    assert covered == oracle.num_chunks(n, chunk)
+    return out, r
+
+
+@pytest.mark.parametrize("big,chunk,n", [(False, 4096, 300_007), (False, 65536, 700_001), (False, 256, 50_001),
+                                         (False, 1024, 77_777), (True, 4096, None)])
+def test_decode_every_workgroup_size(big, chunk, n):
+    """The decoder picks 4-wave or 16-wave workgroups from the size of the job
+    (no override); inputs sized so that each is chosen decode the oracle's
+    stream exactly (ragged tails, chunks of 1, 4 and 16 lanes).  The big case
+    decodes the GPU stream after comparing every chunk of it with the oracle."""
+    if n is None:
+        n = _cus() * 16 * 16384 + 4099
+    assert _big_workgroups(n, chunk) == big
+    _say(f"decode big={big} n={n} chunk={chunk}")
+    x = _gauss(40 + chunk % 97, n, 12.0)
     ln = codebook_for(x, True)
-    ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), chunk)
     dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
-    got, r = gpu_decode(ref, dcb, chunk, n)
-    assert int(r["status"]) == 0
-    assert np.array_equal(got, x)
+    if not big:
+        ref, _ = oracle.encode(x, ln, oracle.canonical_codes(ln), chunk)
+        got, r = gpu_decode(ref, dcb, chunk, n)
+        assert int(r["status"]) == 0
+        assert np.array_equal(got, x)
+        return
+    xd = to_dev(x)
+    out, r = _gpu_stream_against_oracle_blocks(xd, x, ln, chunk, dcb)
+    y = torch.empty(n, dtype=torch.uint8, device=DEV)
+    rd = lecb.new_results(1, DEV)
+    lecb.lecb_decode(out, int(r["bytes"]), dcb.blob, chunk, n, y, rd, lecb.new_workspace(n, chunk, DEV))
+    assert int(lecb.results_to_numpy(rd)[0]["status"]) == 0
+    assert torch.equal(y, xd)
 
 
-@pytest.mark.parametrize("nt", [256, 1024])
-def test_bf16_two_plane_decode_workgroup_sizes(nt):
-    chunk = 16384
-    n = 1_000_003 if nt == 256 else _cus() * 512 * 256 + 3
-    assert _lanes_chosen(n, chunk, 2) == nt
-    _say(f"two-plane decode nt={nt} n={n}")
+@pytest.mark.parametrize("big", [False, True])
+def test_bf16_two_plane_decode_workgroup_sizes(big):
+    chunk = 16384 if not big else 4096
+    n = 1_000_003 if not big else _cus() * 8 * 16384 + 3
+    assert _big_workgroups(n, chunk, nstreams=2) == big
+    _say(f"two-plane decode big={big} n={n}")
     x = workloads.bf16_weights(n)
-    enc = oracle.encode_bf16(x, chunk)
     hi, lo = oracle.split_bf16(x)
-    bh = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_hi"]), DEV)
-    bl = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(enc["len_lo"]), DEV)
-    sh = torch.zeros(enc["stream_hi"].size + 32, dtype=torch.uint8, device=DEV)
-    sl = torch.zeros(enc["stream_lo"].size + 32, dtype=torch.uint8, device=DEV)
-    sh[: enc["stream_hi"].size] = to_dev(enc["stream_hi"])
-    sl[: enc["stream_lo"].size] = to_dev(enc["stream_lo"])
+    lens = [codebook_for(p, False) for p in (hi, lo)]
+    bh = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(lens[0]), DEV)
+    bl = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(lens[1]), DEV)
+    streams = []
+    for p, ln, dcb in ((hi, lens[0], bh), (lo, lens[1], bl)):
+        if big:
+            out, r = _gpu_stream_against_oracle_blocks(to_dev(p), p, ln, chunk, dcb)
+            streams.append((out, int(r["bytes"])))
+        else:
+            ref, _ = oracle.encode(p, ln, oracle.canonical_codes(ln), chunk)
+            buf = torch.zeros(ref.size + 32, dtype=torch.uint8, device=DEV)
+            buf[: ref.size] = to_dev(ref)
+            streams.append((buf, ref.size))
     oh = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=DEV)
     ol = torch.empty_like(oh)
     res = lecb.new_results(2, DEV)
     ws = lecb.new_workspace(n, chunk, DEV)
-    lecb.lecb_decode_bf16_planes(sh, enc["stream_hi"].size, sl, enc["stream_lo"].size, bh.blob, bl.blob,
+    lecb.lecb_decode_bf16_planes(streams[0][0], streams[0][1], streams[1][0], streams[1][1], bh.blob, bl.blob,
                                  chunk, n, oh, ol, res, ws)
     r = lecb.results_to_numpy(res)
     assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
@@ -718,18 +758,24 @@ def test_corrupt_streams_set_status():
     t = ref.copy(); t[0:4] = 0; bad["zero end"] = t
     t = ref.copy(); e = t[:4 * nc].view("<u4").copy(); e[1], e[2] = e[2], e[1]; t[:4 * nc] = e.view(np.uint8); bad["non-monotone"] = t
     t = ref.copy(); t[4 * nc] = 1; bad["table padding"] = t
-    # unit bit counts: one bit moved from unit 0 to unit 1 of chunk 0 (same
-    # chunk total); the count of an empty unit (past the data) made non-zero
+    # lane word counts: one word moved from lane 0 to lane 1 of chunk 0 (same
+    # chunk total); a word given to an empty lane of the last chunk (100
+    # symbols: lanes 7..15 are empty) and taken from its lane 0
     t = ref.copy(); u = t[tb:tb + 4].view("<u2").copy(); u[0] -= 1; u[1] += 1
-    t[tb:tb + 4] = u.view(np.uint8); bad["unit count moved"] = t
-    t = ref.copy(); t[hb - 2] = 1; bad["empty unit count"] = t
+    t[tb:tb + 4] = u.view(np.uint8); bad["word count moved"] = t
+    t = ref.copy(); lw = t[tb + 2 * 16 * (nc - 1): tb + 2 * 16 * nc].view("<u2").copy(); lw[0] -= 1; lw[15] += 1
+    t[tb + 2 * 16 * (nc - 1): tb + 2 * 16 * nc] = lw.view(np.uint8); bad["empty lane word"] = t
+    t = ref.copy(); u = t[tb:tb + 2].view("<u2").copy(); u[0] += 1
+    t[tb:tb + 2] = u.view(np.uint8); bad["word count total"] = t
     t = ref.copy(); t[hb + 40:hb + 48] ^= 0xFF; bad["payload bits"] = t
-    # chunk 256 (one unit per chunk): the zero padding after the unit counts
+    t = ref.copy(); t[hb:hb + 4], t[hb + 4:hb + 8] = ref[hb + 4:hb + 8], ref[hb:hb + 4]; bad["words swapped"] = t
+    # chunk 256 (one lane per chunk): the zero padding after the word counts
     x2 = _gauss(20, 256 * 5 + 7, 12.0)
     ref2, _ = oracle.encode(x2, ln, oracle.canonical_codes(ln), 256)
     t = ref2.copy(); t[oracle.header_bytes(x2.size, 256) - 1] = 1
-    cases = [(name, t, x, 4096) for name, t in bad.items()] + [("unit count padding", t, x2, 256)]
+    cases = [(name, t, x, 4096) for name, t in bad.items()] + [("word count padding", t, x2, 256)]
     for name, t, xx, chunk in cases:
+        _say(f"corrupt case {name}")
         try:
             oracle.decode(t, ln, chunk, xx.size)
             oracle_bad = False
@@ -738,7 +784,7 @@ def test_corrupt_streams_set_status():
         y, r = gpu_decode(t, dcb, chunk, xx.size)
         # the two decoders accept and reject exactly the same streams
         assert (int(r["status"]) == lecb.LECB_ERR_CORRUPT) == oracle_bad, name
-        if name != "payload bits":
+        if name not in ("payload bits", "words swapped"):
             assert oracle_bad, name
         elif not oracle_bad:
             assert np.array_equal(y, oracle.decode(t, ln, chunk, xx.size))

@@ -7,7 +7,7 @@ EVERY chunk compared against the oracle.
 * bf16_delta (512 Mi elements) and int8_drift (4 GiB): the stream is compared
   block by block -- each block of 2^24 symbols (whole chunks) is encoded by
   the oracle alone and must equal the GPU stream's offset-table entries
-  (shifted by the block's first payload word), unit metadata and payload
+  (shifted by the block's first payload word), lane word counts and payload
   words of those chunks; the blocks cover every chunk;
 * histograms equal the oracle's (np.bincount, summed over blocks for the
   long inputs); code lengths equal the oracle's package-merge lengths;

@@ -40,7 +40,7 @@ def test_noalloc_equals_encode_on_two_calls():
 
 def test_noalloc_rejects_inputs_beyond_its_scratch():
     dcb = _codebook()
-    chunk = 4096
+    chunk = 256   # 4 Mi chunks: their workspace (8 bytes per chunk and stream) is over 16 MiB
     n = 1 << 30
     assert lecb.lecb_workspace_bytes(n, chunk) > lecb.NOALLOC_SCRATCH_BYTES
     buf = torch.zeros(1024, dtype=torch.uint8, device=DEV)
