@@ -28,40 +28,39 @@ namespace {
 
 constexpr int CB_THREADS = 256;
 
-// LUT entry t (the LUT_BITS-bit prefix t): the code word it starts with when
-// that word has at most LUT_BITS bits, else 0.
-__device__ inline void lut_entry(const uint32_t* count, const uint32_t* first, const uint32_t* base,
-                                 const uint8_t* sorted, DeviceCodebook* cb, int t) {
-    uint16_t entry = 0;
-    for (int l = 1; l <= LUT_BITS; ++l) {
-        const uint32_t v = (uint32_t)t >> (LUT_BITS - l);
-        if (count[l] && v >= first[l] && v < first[l] + count[l]) {
-            entry = (uint16_t)((sorted[base[l] + v - first[l]] << 8) | l);
-            break;
-        }
+// Length of the code word that the left-aligned 16-bit window w starts with:
+// the windows of length-l code words are [limit[l-1], limit[l]), so it is 1 +
+// the number of limits at or below w (17: no code word starts at w).
+__device__ inline uint32_t code_len(const uint32_t* limit, uint32_t w) {
+    uint32_t n = 1;
+#pragma unroll
+    for (int l = 1; l <= 16; ++l) n += w >= limit[l];
+    return n;
+}
+
+// Entry i of the decode table (see DeviceCodebook::dec).
+__device__ inline uint16_t dec_entry(const uint32_t* limit, const uint32_t* first, const uint32_t* base,
+                                     const uint8_t* sorted, uint32_t i) {
+    const uint32_t lb = limit[LUT_BITS], b4 = lb >> 4;
+    if (i < b4) {
+        // a code word of at most LUT_BITS bits starts every window below lb
+        const uint32_t l = code_len(limit, i << (16 - LUT_BITS));
+        return (uint16_t)((sorted[(base[l] + (i >> (LUT_BITS - l)) - first[l]) & 255u] << 8) | l);
     }
-    cb->lut[t] = entry;
+    const uint32_t v = lb + (i - b4);
+    if (i >= (uint32_t)DEC_SIZE || v >= limit[16]) return DEC_INVALID;
+    const uint32_t l = code_len(limit, v);
+    return (uint16_t)((sorted[(base[l] + (v >> (16 - l)) - first[l]) & 255u] << 8) | l);
 }
 
-// Second-table entry i: the 16-bit window v = limit[LUT_BITS] + i, read as
-// the longer code word it starts with (its length is 1 + the number of
-// left-aligned limits at or below v), or 0 past the last code word.
-__device__ inline uint16_t lut2_entry(const uint32_t* limit, const uint32_t* first, const uint32_t* base,
-                                      const uint8_t* sorted, uint32_t i) {
-    const uint32_t v = limit[LUT_BITS] + i;
-    if (v >= limit[16]) return 0;
-    uint32_t len = 1;
-    for (int l = 1; l <= 16; ++l) len += v >= limit[l];
-    return (uint16_t)((sorted[(base[len] + (v >> (16 - len)) - first[len]) & 255u] << 8) | len);
-}
-
-__device__ inline void lut2_fields(const uint32_t* limit, DeviceCodebook* cb) {
-    cb->lut2_base = limit[LUT_BITS];
-    cb->pad[0] = cb->pad[1] = 0;
+__device__ inline void long_fields(const uint32_t* limit, DeviceCodebook* cb) {
+    cb->long_base = limit[LUT_BITS];
+    cb->long_sub = limit[LUT_BITS] - (limit[LUT_BITS] >> 4);
+    cb->pad[0] = 0;
 }
 
 // Tables from the canonical description passed by value (host-built codebook).
-// Grid covers the LUT_SIZE lookup entries.
+// Grid covers the DEC_ENTRIES decode table entries.
 __global__ __launch_bounds__(CB_THREADS) void codebook_kernel(CodebookArgs a, DeviceCodebook* cb) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t < 256) {
@@ -80,9 +79,8 @@ __global__ __launch_bounds__(CB_THREADS) void codebook_kernel(CodebookArgs a, De
     uint32_t limit[17];
     limit[0] = 0;
     for (int l = 1; l <= 16; ++l) limit[l] = (a.first[l] + a.count[l]) << (16 - l);
-    if (t == 0) lut2_fields(limit, cb);
-    if (t < LUT_SIZE) lut_entry(a.count, a.first, a.base, a.sorted, cb, t);
-    if (t < LUT2_SIZE) cb->lut2[t] = lut2_entry(limit, a.first, a.base, a.sorted, (uint32_t)t);
+    if (t == 0) long_fields(limit, cb);
+    if (t < DEC_ENTRIES) cb->dec[t] = dec_entry(limit, a.first, a.base, a.sorted, (uint32_t)t);
 }
 
 struct BuildArgs {
@@ -301,10 +299,7 @@ __global__ __launch_bounds__(CB_THREADS) void build_kernel(BuildArgs a) {
 }
 
 // Decode tables of device codebooks whose canonical description build_kernel
-// wrote; grid (LUT_SIZE / 256, codebooks).  A code word's length is read off
-// the left-aligned limits: the windows of length-l code words are
-// [limit[l-1], limit[l]), so the length is 1 + the number of limits at or
-// below the window (17: no code word starts here).
+// wrote; grid (DEC_ENTRIES / 256 rounded up, codebooks).
 __global__ __launch_bounds__(CB_THREADS) void tables_kernel(BuildArgs a) {
     __shared__ uint32_t first[17], base[17], lim[17];
     __shared__ uint8_t sorted[256];
@@ -317,29 +312,15 @@ __global__ __launch_bounds__(CB_THREADS) void tables_kernel(BuildArgs a) {
     }
     sorted[tid] = cb->sorted[tid];
     __syncthreads();
-    uint32_t lv[16];
-#pragma unroll
-    for (int l = 1; l <= 16; ++l) lv[l - 1] = lim[l];
-    auto code_len = [&](uint32_t w16) {
-        uint32_t n = 1;
-#pragma unroll
-        for (int l = 0; l < 16; ++l) n += w16 >= lv[l];
-        return n;
-    };
     const uint32_t t = blockIdx.x * CB_THREADS + tid;
-    const uint32_t l0 = code_len(t << (16 - LUT_BITS));
-    uint16_t entry = 0;
-    if (l0 <= (uint32_t)LUT_BITS)
-        entry = (uint16_t)((sorted[base[l0] + (t >> (LUT_BITS - l0)) - first[l0]] << 8) | l0);
-    cb->lut[t] = entry;
-    if (t < LUT2_SIZE) cb->lut2[t] = lut2_entry(lim, first, base, sorted, t);
-    if (t == 0) lut2_fields(lim, cb);
+    if (t < (uint32_t)DEC_ENTRIES) cb->dec[t] = dec_entry(lim, first, base, sorted, t);
+    if (t == 0) long_fields(lim, cb);
 }
 
 }  // namespace
 
 int launch_codebook_upload(const CodebookArgs& args, DeviceCodebook* blob, void* stream) {
-    hipLaunchKernelGGL(codebook_kernel, dim3(LUT_SIZE / CB_THREADS), dim3(CB_THREADS), 0,
+    hipLaunchKernelGGL(codebook_kernel, dim3((DEC_ENTRIES + CB_THREADS - 1) / CB_THREADS), dim3(CB_THREADS), 0,
                        reinterpret_cast<hipStream_t>(stream), args, blob);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
@@ -356,7 +337,7 @@ int launch_build_codebooks(const uint64_t* const* hist, DeviceCodebook* const* c
     a.min_freq = min_freq;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(build_kernel, dim3(n), dim3(CB_THREADS), 0, s, a);
-    hipLaunchKernelGGL(tables_kernel, dim3(LUT_SIZE / CB_THREADS, n), dim3(CB_THREADS), 0, s, a);
+    hipLaunchKernelGGL(tables_kernel, dim3((DEC_ENTRIES + CB_THREADS - 1) / CB_THREADS, n), dim3(CB_THREADS), 0, s, a);
     return hipGetLastError() == hipSuccess ? LECB_OK : LECB_ERR_HIP;
 }
 

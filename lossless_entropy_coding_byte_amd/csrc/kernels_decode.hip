@@ -29,15 +29,17 @@
 // lanes whose first window word is used up take the next words of the ring,
 // in lane order (a count over the group's lanes gives each its word).  The
 // ring is topped up every 4 pairs: the load issued at one top-up is written
-// to the ring at the next, and a load is issued only when the ring has room
-// for it; 4 pairs read at most 4G words, so every word read is in the ring.
+// to the ring two top-ups later, and a load is issued only when the ring has
+// room for it; 4 pairs read at most 4G words, so every word read is in the
+// ring.
 //
-// Bit reader: a window of two words and a bit offset into it; before every
-// pair the window slides by one word when its first word is used up.
-// Afterwards the offset is below 32 and the window holds > 32 bits, enough
-// for two code words of at most 16 bits.  A code word of at most LUT_BITS
-// bits is one LDS lookup, a longer one a lookup in a second table.  Every
-// structural rule of the format is checked; a violation sets status CORRUPT.
+// Bit reader: a 64-bit buffer of the lane's next bits; before every pair,
+// when it holds 32 bits or fewer (the format's "first window word used up"),
+// the next word comes in below them, so it holds more than 32 bits, enough
+// for two code words of at most 16 bits.  Every code word is one lookup in
+// the decode table (LDS; for two and four planes the longer code words are
+// read from the codebook in memory).  Every structural rule of the format is
+// checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -78,21 +80,21 @@ struct DecArgs {
     DecStream st[4];
 };
 
-// One stream per workgroup: its decode table and the table of the longer code words.
+// One stream per workgroup: its whole decode table.
 template <int NW>
 struct SharedOne {
-    uint16_t lut[1][LUT_SIZE];   // (sym << 8) | len of the code words of at most LUT_BITS bits
-    uint16_t lut2[LUT2_SIZE];    // the same for the longer code words
-    alignas(16) uint32_t ring[NW][4][ROW_WORDS];
+    uint32_t ring[NW][4][ROW_WORDS];   // first: every row's ring is 1 KiB-aligned
+    uint16_t dec[DEC_ENTRIES];
 };
-// P streams in every workgroup: P first tables (code words longer than
-// LUT_BITS -- rare in byte planes -- read the second table of the device
-// codebook in memory).  With P = 2 and 16 waves this is exactly 80 KiB, so
-// two workgroups fill a CU's LDS.
+// P streams in every workgroup: the first LUT_SIZE entries of each decode
+// table (the code words of at most LUT_BITS bits, and some of the longer
+// ones); entries past them -- longer code words, rare in byte planes -- are
+// read from the device codebook in memory.  With P = 2 and 16 waves this is
+// exactly 80 KiB, so two workgroups fill a CU's LDS.
 template <int NW, int P>
 struct SharedMany {
+    uint32_t ring[NW][4][ROW_WORDS];
     uint16_t lut[P][LUT_SIZE];
-    alignas(16) uint32_t ring[NW][4][ROW_WORDS];
 };
 template <int NW, int P>
 using Shared = std::conditional_t<P == 1, SharedOne<NW>, SharedMany<NW, P>>;
@@ -136,25 +138,15 @@ __device__ inline Lane lane_stream(const DecArgs& a, uint32_t k, uint64_t payloa
     return l;
 }
 
-// Next code word as (sym << 8) | len, len in 1..16, from the next 32 bits
-// `top`.  An invalid code word yields len 16 and sets `inval`.  A code word
-// of at most LUT_BITS bits is one probe of the first table, a longer one one
-// probe of the second (which always holds every longer code word: at most 256
-// of them, each covering at most 2^(16 - 13) = 8 of its entries).
-template <int P, typename S>
-__device__ inline uint32_t lookup(const S& sh, const uint16_t* lut, const DeviceCodebook* cb, uint32_t base2,
-                                  uint32_t top, uint32_t& inval) {
-    uint32_t e = lut[top >> (32 - LUT_BITS)];
-    if (e == 0) {
-        const uint32_t i = (top >> 16) - base2;
-        if constexpr (P == 1) e = i < (uint32_t)LUT2_SIZE ? sh.lut2[i] : 0u;
-        else e = i < (uint32_t)LUT2_SIZE ? cb->lut2[i] : 0u;
-        if (e == 0) {
-            inval = 1;
-            e = 16;
-        }
-    }
-    return e;
+// Index of the decode-table entry of the code word that the next bits `top`
+// (MSB first) start with: the first LUT_BITS bits below long_base, the window
+// offset past it, the sentinel beyond the table (see DeviceCodebook::dec).
+__device__ inline uint32_t dec_index(uint32_t top, uint32_t long_sub) {
+    const int a = (int)(top >> (32 - LUT_BITS));
+    const int b = (int)(top >> 16) - (int)long_sub;
+    int r;   // median of (a, b, DEC_SIZE) = min(max(a, b), DEC_SIZE), as a <= DEC_SIZE
+    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(DEC_SIZE));
+    return (uint32_t)r;
 }
 
 // The symbols (byte 1) of four table entries as one little-endian word.
@@ -215,11 +207,6 @@ __device__ inline v4u restore_u32(const uint32_t (&w)[4], uint32_t q) {
     return o;
 }
 
-template <int NW, int P>
-__device__ inline const uint16_t* lut_of(const Shared<NW, P>& S, uint32_t k) {
-    return &S.lut[P == 1 ? 0 : k][0];
-}
-
 // 64 VGPRs at most: with 16-wave workgroups two fit a CU (8 waves per SIMD).
 template <int NT, int P, int OUT, int LG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_kernel(DecArgs a) {
@@ -261,21 +248,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     }
     const Lane ln = lane_stream<P>(a, k, my_words);
     // ---- tables
-    {
+    if constexpr (P == 1) {
+        const v4u* src = reinterpret_cast<const v4u*>(a.st[sidx].cb->dec);
+        v4u* dst = reinterpret_cast<v4u*>(S.dec);
+        for (int x = tid; x < DEC_ENTRIES * 2 / 16; x += NT) dst[x] = src[x];
+    } else {
 #pragma unroll
         for (int q = 0; q < P; ++q) {
-            const v4u* src = reinterpret_cast<const v4u*>(a.st[P == 1 ? sidx : (uint32_t)q].cb->lut);
+            const v4u* src = reinterpret_cast<const v4u*>(a.st[q].cb->dec);
             v4u* dst = reinterpret_cast<v4u*>(&S.lut[q][0]);
-            constexpr int NV = LUT_SIZE * 2 / 16;
-            for (int x = tid; x < NV; x += NT) dst[x] = src[x];
-        }
-        if constexpr (P == 1) {
-            const v4u* src2 = reinterpret_cast<const v4u*>(a.st[sidx].cb->lut2);
-            v4u* dst2 = reinterpret_cast<v4u*>(S.lut2);
-            for (int x = tid; x < LUT2_SIZE * 2 / 16; x += NT) dst2[x] = src2[x];
+            for (int x = tid; x < LUT_SIZE * 2 / 16; x += NT) dst[x] = src[x];
         }
     }
-    const uint32_t base2 = ln.cb->lut2_base;
+    __syncthreads();   // every wave reads entries that other waves copied
+    const uint32_t long_sub = ln.cb->long_sub;
 
     // ---- the chunk and its structure
     const bool valid = c < a.nc;
@@ -337,9 +323,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     }
     uint32_t wr = R;                            // next word to load (from a0)
     __builtin_amdgcn_wave_barrier();
-    uint32_t pend_at = 0;
-    v4u pend_v = {0, 0, 0, 0};
-    bool pend = false;
+    // two loads in flight: the one issued at a block's middle top-up, the one
+    // issued at its end; each is written to the ring one block later
+    uint32_t pa_at = 0, pb_at = 0;
+    v4u pa = {0, 0, 0, 0}, pb = {0, 0, 0, 0};
+    bool pa_on = false, pb_on = false;
 
     // ---- words 0 and 1
     uint32_t b0, n0, b1, n1;
@@ -347,61 +335,96 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     group_count<LG>(N >= 2, b1, n1);
     const uint32_t d0 = (uint32_t)(sw - a0);    // the chunk's first word, from a0
     uint32_t cons = d0 + n0 + n1;               // next word the group reads, from a0
-    uint32_t w0 = N >= 1 ? ring[(slot0 + d0 + b0) & (R - 1)] : 0u;
-    uint32_t w1 = N >= 2 ? ring[(slot0 + d0 + n0 + b1) & (R - 1)] : 0u;
-    uint32_t rd = min(N, 2u), off = 0, shifts = 0, inval = 0;
-    const uint16_t* lut = lut_of<NW, P>(S, k);
+    const uint32_t w0 = N >= 1 ? ring[(slot0 + d0 + b0) & (R - 1)] : 0u;
+    const uint32_t w1 = N >= 2 ? ring[(slot0 + d0 + n0 + b1) & (R - 1)] : 0u;
+    // Bit buffer: the lane's next avail = 32 - na bits, most significant first
+    // (the two-word window with its used bits shifted out).  "The first word
+    // is used up" is avail <= 32, i.e. na >= 0 as a signed value; then a word
+    // comes in below the valid bits, shifted left by na (a zero word once the
+    // lane has read all its words).  vw counts the words taken in, read or
+    // zero, so 32 * vw - avail bits are consumed.
+    uint64_t bb = ((uint64_t)w0 << 32) | w1;
+    int32_t na = -32;
+    uint32_t vw = 2;   // (the lane's next word is word vw while vw < N)
+    uint32_t inval = 0;
 
     // ---- decode, block by block
-    uint32_t mmax = m;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mmax = max(mmax, (uint32_t)__shfl_xor(mmax, o, 64));
-    const uint32_t nblk = (mmax + BLOCK - 1) / BLOCK;
-    const uint64_t lane_e0 = c * a.chunk + (uint64_t)j * BLOCK;   // first element of the lane's block 0
-    for (uint32_t t = 0; t < nblk; ++t) {
-        uint32_t w[4];
+    // One block of 16 symbols: 8 pairs, each preceded by the group's reads.
+    // FULL: every lane of the wave has the whole block (no symbol checks).
+    // Ring top-up (group-uniform), after every 4 pairs: write the load issued
+    // two top-ups ago to the ring, issue the next when the ring has room for
+    // it (room counted with the loads in flight).  With 4G-word loads, a ring
+    // of 16G words and 4 pairs reading at most 4G words between top-ups,
+    // every word a pair reads has been written, and no write lands on a word
+    // still to be read (the rule was checked exhaustively over consumption
+    // patterns).  The top-up after a block's last pair comes before the
+    // block's store, so waiting for a load gives the stores time to finish.
+    auto top_up = [&](v4u& pv, uint32_t& pat, bool& pon) {
+        if (pon) put4(pat, pv);
+        pon = false;
+        if (wr - cons <= R - 4 * G) {
+            pv = load4(wr);
+            pat = wr;
+            wr += 4 * G;
+            pon = true;
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+    auto decode_block = [&](uint32_t t, auto full_c, uint32_t (&w)[4]) {
+        constexpr bool FULL = decltype(full_c)::value;
         uint32_t ev[4];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            if ((q & 3) == 0) {
-                // ring top-up (group-uniform): commit the previous load, issue the next
-                if (pend) put4(pend_at, pend_v);
-                pend = false;
-                if (wr - cons <= R - 4 * G) {
-                    pend_v = load4(wr);
-                    pend_at = wr;
-                    wr += 4 * G;
-                    pend = true;
-                }
-                __builtin_amdgcn_wave_barrier();
-            }
+            if (q == 4) top_up(pa, pa_at, pa_on);
             const uint32_t s0 = t * BLOCK + 2 * q;   // the pair's first symbol in the lane
-            const bool act = s0 < m;
-            const bool sh = act && off >= 32;
-            const bool fetch = sh && rd < N;
+            const bool act = FULL || s0 < m;
+            const bool sh = act && na >= 0;
+            const bool fetch = sh && vw < N;
             uint32_t bf, nf;
             group_count<LG>(fetch, bf, nf);
             const uint32_t word = ring[(slot0 + cons + bf) & (R - 1)];
-            w0 = sh ? w1 : w0;
-            w1 = sh ? (fetch ? word : 0u) : w1;
-            off -= sh ? 32u : 0u;
-            shifts += sh ? 1u : 0u;
-            rd += fetch ? 1u : 0u;
+            // avail >= 1 before a pair (a pair takes at most 32 of > 32 bits): na <= 31
+            bb |= (uint64_t)(fetch ? word : 0u) << ((uint32_t)na & 63u);
+            na -= sh ? 32 : 0;
+            vw += sh ? 1u : 0u;
             cons += nf;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const uint32_t top = (uint32_t)(((((uint64_t)w0 << 32) | w1) << off) >> 32);
-                uint32_t iv = 0;
-                uint32_t e = lookup<P>(S, lut, ln.cb, base2, top, iv);
-                const bool use = s0 + h < m;
-                e = use ? e : 0u;
-                inval |= use ? iv : 0u;
-                off += e & 0xFFu;
+                const bool use = FULL || s0 + h < m;
+                const uint32_t idx = dec_index((uint32_t)(bb >> 32), long_sub);
+                uint32_t e;
+                if constexpr (P == 1) {
+                    e = S.dec[idx];
+                } else {
+                    e = S.lut[k][idx & (LUT_SIZE - 1)];
+                    if (__ballot(use && idx >= (uint32_t)LUT_SIZE)) {
+                        // a longer code word: its entry in the codebook's table in memory
+                        if (idx >= (uint32_t)LUT_SIZE) e = ln.cb->dec[idx];
+                    }
+                }
+                if constexpr (!FULL) e = use ? e : 0u;
+                inval |= e;   // bit 7: no code word starts here
+                bb <<= (e & 63u);   // (len <= 16; bits 8.. hold the symbol)
+                na += (int32_t)(e & 0xFFu);
                 const int x = 2 * q + h;
                 ev[x & 3] = e;
                 if ((x & 3) == 3) w[x >> 2] = syms4(ev);
             }
         }
+        top_up(pb, pb_at, pb_on);
+    };
+    uint32_t mmax = m, mmin = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mmax = max(mmax, (uint32_t)__shfl_xor(mmax, o, 64));
+        mmin = min(mmin, (uint32_t)__shfl_xor(mmin, o, 64));
+    }
+    const uint32_t nblk = (mmax + BLOCK - 1) / BLOCK, nfull = mmin / BLOCK;
+    const uint64_t lane_e0 = c * a.chunk + (uint64_t)j * BLOCK;   // first element of the lane's block 0
+    for (uint32_t t = 0; t < nblk; ++t) {
+        uint32_t w[4];
+        if (t < nfull) decode_block(t, std::true_type{}, w);
+        else decode_block(t, std::false_type{}, w);
         // the block's output: 16 symbols of block tG + j of the chunk
         const uint32_t cnt = m > t * BLOCK ? min(BLOCK, m - t * BLOCK) : 0u;
         const uint64_t e0 = lane_e0 + (uint64_t)(t << LG) * BLOCK;
@@ -443,17 +466,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     // ---- the lane's end: every word read, the last one needed, zero padding
     uint32_t bits = 0;
     if (run && m) {
-        if (off >= 32) {   // slide past a used-up first word (all words are read by now)
-            w0 = w1;
-            w1 = 0;
-            off -= 32;
-            shifts += 1;
-        }
-        bits = 32 * shifts + off;
-        if (inval || rd != N || bits > 32 * N || bits <= 32 * (N - 1)) bad = true;
-        const uint32_t rest = 32 * N - bits;
-        const uint32_t top = (uint32_t)(((((uint64_t)w0 << 32) | w1) << off) >> 32);
-        if (!bad && rest && (top >> (32 - rest)) != 0) bad = true;
+        bits = 32 * vw - (uint32_t)(32 - na);
+        if ((inval & 0x80u) || vw < N || bits > 32 * N || bits <= 32 * (N - 1)) bad = true;
+        const uint32_t rest = 32 * N - bits;   // padding bits: the next ones in the buffer
+        if (!bad && rest && (bb >> (64 - rest)) != 0) bad = true;
     }
 
     // ---- status, accounting, exit

@@ -54,7 +54,7 @@ __device__ inline uint32_t lane_symbols(uint32_t m, uint32_t j) {
 // Value of lane `src` of the caller's row, broadcast over the row (DPP).
 template <int SRC>
 __device__ inline uint32_t row_bcast(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + SRC, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + SRC, 0xF, 0xF, false);
 }
 
 // Exclusive count of `f` over the lanes of the caller's group (G = 1 << LG
@@ -62,9 +62,13 @@ __device__ inline uint32_t row_bcast(uint32_t v) {
 // must call it (the broadcasts read neighbouring lanes).
 template <int LG>
 __device__ inline void group_count(bool f, uint32_t& before, uint32_t& total) {
-    const uint64_t m = __ballot(f);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(f);
     const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    const uint32_t q = p + (f ? 1u : 0u);  // inclusive
+    // inclusive count: p plus this lane's bit of m, taken as the carry-in
+    uint32_t q;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(q), "=s"(carry_out) : "v"(p), "s"(m));
+    (void)carry_out;
     uint32_t first, last;
     if constexpr (LG == 0) {
         first = p;

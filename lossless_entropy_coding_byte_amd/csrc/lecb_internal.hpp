@@ -1,6 +1,7 @@
 // Internal declarations shared by the host runtime and the HIP kernels.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 
 #include "lecb.h"
@@ -8,31 +9,43 @@
 namespace lecb {
 
 // ---------------------------------------------------------------- device codebook
-// Decode lookup covers code words of up to LUT_BITS bits in one probe; longer
-// ones go through the canonical per-length limits.
+// Decode table `dec`, one probe per code word.  With v the next 16 bits
+// (left-aligned window) and long_base = the left-aligned end of the code
+// words of at most LUT_BITS bits (a multiple of 16, so the windows below it
+// are exactly the code words of at most LUT_BITS bits):
+//   * dec[i], i < long_base / 16: the code word that the LUT_BITS-bit prefix i
+//     starts with;
+//   * dec[long_base / 16 + (v - long_base)], v >= long_base: the longer code
+//     word window v starts with (a complete code has at most 256 of them, each
+//     covering at most 2^(16-13) windows: LONG_SIZE entries);
+// so the entry of v is dec[med3(v >> 4, v - long_sub, DEC_SIZE)] with
+// long_sub = long_base - long_base / 16 (the first index wins below
+// long_base, the second from it on).  Entries are (sym << 8) | len; a window
+// that starts no code word (an incomplete code), the entries past the long
+// windows and the sentinel dec[DEC_SIZE] are DEC_INVALID: length 16 with
+// bit 7 set.
 constexpr int LUT_BITS = 12;
 constexpr int LUT_SIZE = 1 << LUT_BITS;
-// Code words longer than LUT_BITS: a second table indexed by the next 16 bits
-// minus limit[LUT_BITS] (the left-aligned start of the longer code words).
-// It holds all of them: at most 256 code words of 13..16 bits cover at most
-// 256 * 2^(16-13) = LUT2_SIZE of the 16-bit values.
-constexpr int LUT2_SIZE = 2048;
+constexpr int LONG_SIZE = 2048;
+constexpr int DEC_SIZE = LUT_SIZE + LONG_SIZE;
+constexpr int DEC_ENTRIES = DEC_SIZE + 8;   // the sentinel, then padding to 16 bytes
+constexpr uint16_t DEC_INVALID = 0x0090;
 
 struct DeviceCodebook {
-    uint32_t enc[256];        // (code << 5) | len ; len 0 = byte has no code word
-    uint16_t lut[LUT_SIZE];   // next LUT_BITS bits -> (sym << 8) | len, len <= LUT_BITS; 0 = longer/none
-    uint32_t limit[17];       // per length l: (first[l] + count[l]) << (16 - l), non-decreasing in l
-    uint32_t first[17];       // first canonical code of length l
-    uint32_t base[17];        // index in `sorted` of the first symbol of length l
-    uint8_t sorted[256];      // coded symbols by (length, byte value)
-    uint16_t lut2[LUT2_SIZE]; // next 16 bits v -> (sym << 8) | len for v - lut2_base < LUT2_SIZE,
-                              // len > LUT_BITS; 0 = no code word
+    uint32_t enc[256];           // (code << 5) | len ; len 0 = byte has no code word
+    uint16_t dec[DEC_ENTRIES];   // decode table (above)
+    uint32_t limit[17];          // per length l: (first[l] + count[l]) << (16 - l), non-decreasing in l
+    uint32_t first[17];          // first canonical code of length l
+    uint32_t base[17];           // index in `sorted` of the first symbol of length l
+    uint8_t sorted[256];         // coded symbols by (length, byte value)
     uint32_t max_len;
     uint32_t num_coded;
-    uint32_t lut2_base;       // limit[LUT_BITS]
-    uint32_t pad[2];
+    uint32_t long_base;          // limit[LUT_BITS]
+    uint32_t long_sub;           // long_base - long_base / 16
+    uint32_t pad[1];
 };
 static_assert(sizeof(DeviceCodebook) % 16 == 0, "device codebook must stay 16-byte sized");
+static_assert(offsetof(DeviceCodebook, dec) % 16 == 0, "the decode table is copied in 16-byte pieces");
 
 // Everything the upload kernel needs, passed by value as a kernel argument.
 struct CodebookArgs {
