@@ -304,11 +304,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     // the payload whenever the payload has a word)
     const uint64_t gall = ln.payload_words ? ((ln.payload_words - 1) >> 2) - (a0 >> 2) : 0;
     const uint32_t glast = (uint32_t)min<uint64_t>(gall, 0xFFFFFFFFull);
+    // (a chunk that is not decoded reads 16 bytes of its codebook instead: every
+    // load is issued, so the waits for them are counted exactly)
+    // Loads past the chunk's words (and those of a chunk that is not decoded)
+    // read 16 bytes of the codebook instead.
+    const v4u* const safe = reinterpret_cast<const v4u*>(ln.cb);
+    const uint32_t wend = (uint32_t)(sw - a0 + wc);   // the chunk's end, from a0
     auto load4 = [&](uint32_t word) -> v4u {   // this lane's 16 bytes of a group load at word a0 + word
         const uint32_t g = (word >> 2) + j;
-        v4u v = {0, 0, 0, 0};
-        if (run) v = grp[g < glast ? g : glast];   // (a chunk that is not decoded reads nothing)
-        return v;
+        return *(run && word < wend ? grp + (g < glast ? g : glast) : safe);
     };
     const uint32_t slot0 = (uint32_t)a0 & (R - 1);
     auto put4 = [&](uint32_t word, const v4u& v) {
@@ -361,13 +365,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     // block's store, so waiting for a load gives the stores time to finish.
     auto top_up = [&](v4u& pv, uint32_t& pat, bool& pon) {
         if (pon) put4(pat, pv);
-        pon = false;
-        if (wr - cons <= R - 4 * G) {
-            pv = load4(wr);
-            pat = wr;
-            wr += 4 * G;
-            pon = true;
-        }
+        // a load is issued every time; it is kept only when the ring has room
+        // and the chunk has words there
+        pon = wr - cons <= R - 4 * G && wr < wend;
+        pv = load4(wr);
+        pat = wr;
+        wr += pon ? 4 * G : 0u;
         __builtin_amdgcn_wave_barrier();
     };
     auto decode_block = [&](uint32_t t, auto full_c, uint32_t (&w)[4]) {
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         const uint32_t cnt = m > t * BLOCK ? min(BLOCK, m - t * BLOCK) : 0u;
         const uint64_t e0 = lane_e0 + (uint64_t)(t << LG) * BLOCK;
         if constexpr (OUT == DEC_OUT_PLANES) {
-            if (cnt == BLOCK) {
+            if (t < nfull || cnt == BLOCK) {   // (every lane's block is whole below nfull)
                 v4u v;
                 v.x = w[0];
                 v.y = w[1];

@@ -298,7 +298,9 @@ template <int MODE, int LG>
 __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
     constexpr int P = Streams<MODE>::value;
     constexpr uint32_t G = 1u << LG;
+    constexpr uint32_t RE = 16 * G;   // staging words of a group
     __shared__ uint32_t enc[2][256];
+    __shared__ uint32_t stage[ENC_WAVES][4][256];
     const int tid = threadIdx.x;
     const uint32_t lane = tid & 63;
 #pragma unroll
@@ -339,54 +341,94 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
         if (pl.valid && pl.j == 0) table[pl.c] = (uint32_t)(cstart + wc);
         uint32_t* const out = payload + cstart;
 
-        // reads of words 0 and 1
-        uint32_t b0, n0, b1, n1;
-        group_count<LG>(N >= 1, b0, n0);
-        group_count<LG>(N >= 2, b1, n1);
-        uint32_t posA = b0, posB = n0 + b1, cons = n0 + n1;
-        uint32_t nextk = min(N, 2u);
-        bool crossed = false;
-        uint64_t acc = 0;
-        uint32_t fill = 0;
+        // Reads of words 0 and 1, then the pairs.  STAGED: a completed word goes
+        // to the group's staging ring in LDS, and every 4 pairs the words below
+        // the group's lowest unwritten position go out with coalesced stores (a
+        // lane writes every G-th word); a word that would land on a slot not
+        // yet stored sets `over`, and the task is then coded again with direct
+        // stores of each word (the words stored so far are the same).
         const bool wr = !skip && pl.valid;
         const uint32_t nblk = (wave_max_u32(pl.m) + BLOCK - 1) / BLOCK;
-        for (uint32_t t = 0; t < nblk; ++t) {
-            const uint32_t cnt = pl.m > t * BLOCK ? min(BLOCK, pl.m - t * BLOCK) : 0u;
-            uint32_t w[4] = {0, 0, 0, 0};
-            if (cnt) block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, w);
-            uint32_t e[16];
+        uint32_t* const ring = &stage[tid >> 6][lane >> 4][((lane & 15u) >> LG) * RE];
+        auto code_task = [&](auto staged_c) -> bool {
+            constexpr bool STAGED = decltype(staged_c)::value;
+            uint32_t b0, n0, b1, n1;
+            group_count<LG>(N >= 1, b0, n0);
+            group_count<LG>(N >= 2, b1, n1);
+            uint32_t posA = b0, posB = n0 + b1, cons = n0 + n1;
+            uint32_t nextk = min(N, 2u), done = 0;   // words read, words written
+            bool crossed = false, over = false;
+            uint64_t acc = 0;
+            uint32_t fill = 0, flushed = 0;
+            auto put = [&](uint32_t pos, uint32_t word) {
+                if constexpr (STAGED) {
+                    if (pos - flushed < RE) ring[pos & (RE - 1)] = word;
+                    else over = true;
+                } else {
+                    if (wr) out[pos] = word;
+                }
+            };
+            // STAGED: store the group's words below the lowest position still to be written
+            auto flush = [&](bool all) {
+                uint32_t f = all ? cons : (done < N ? posA : cons);
+                f = group_min<LG>(f);
+                __builtin_amdgcn_wave_barrier();
+                for (uint32_t x = flushed + (lane & (G - 1)); __ballot(x < f); x += G)
+                    if (x < f && wr) out[x] = ring[x & (RE - 1)];
+                flushed = f;
+                __builtin_amdgcn_wave_barrier();
+            };
+            for (uint32_t t = 0; t < nblk; ++t) {
+                const uint32_t cnt = pl.m > t * BLOCK ? min(BLOCK, pl.m - t * BLOCK) : 0u;
+                uint32_t w[4] = {0, 0, 0, 0};
+                if (cnt) block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, w);
+                uint32_t e[16];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t x = e_tab[sym_of(w, k)];
-                e[k] = (uint32_t)k < cnt ? x : 0u;
-            }
+                for (int k = 0; k < 16; ++k) {
+                    const uint32_t x = e_tab[sym_of(w, k)];
+                    e[k] = (uint32_t)k < cnt ? x : 0u;
+                }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                // before the pair: the lanes that completed a word read the next one
-                const bool act = 2u * q < cnt;
-                const bool fetch = act && crossed && nextk < N;
-                uint32_t bf, nf;
-                group_count<LG>(fetch, bf, nf);
-                posB = fetch ? cons + bf : posB;
-                nextk += fetch ? 1u : 0u;
-                cons += nf;
-                crossed = false;
-                // the pair's code words (at most 32 bits) into the accumulator
-                const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
-                const uint32_t l1 = e1 & 31u;
-                const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);
-                fill += (e0 & 31u) + l1;
-                acc |= (uint64_t)c2 << ((64u - fill) & 63u);
-                if (fill >= 32) {
-                    if (wr) out[posA] = (uint32_t)(acc >> 32);
-                    acc <<= 32;
-                    fill -= 32;
-                    posA = posB;
-                    crossed = true;
+                for (int q = 0; q < 8; ++q) {
+                    // before the pair: the lanes that completed a word read the next one
+                    const bool act = 2u * q < cnt;
+                    const bool fetch = act && crossed && nextk < N;
+                    uint32_t bf, nf;
+                    group_count<LG>(fetch, bf, nf);
+                    posB = fetch ? cons + bf : posB;
+                    nextk += fetch ? 1u : 0u;
+                    cons += nf;
+                    crossed = false;
+                    // the pair's code words (at most 32 bits) into the accumulator
+                    const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
+                    const uint32_t l1 = e1 & 31u;
+                    const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);
+                    fill += (e0 & 31u) + l1;
+                    acc |= (uint64_t)c2 << ((64u - fill) & 63u);
+                    if (fill >= 32) {
+                        put(posA, (uint32_t)(acc >> 32));
+                        acc <<= 32;
+                        fill -= 32;
+                        posA = posB;
+                        crossed = true;
+                        ++done;
+                    }
+                    if constexpr (STAGED) {
+                        if ((q & 3) == 3) {
+                            if (__ballot(over)) return true;
+                            flush(false);
+                        }
+                    }
                 }
             }
-        }
-        if (fill && wr) out[posA] = (uint32_t)(acc >> 32);
+            if (fill) put(posA, (uint32_t)(acc >> 32));
+            if constexpr (STAGED) {
+                if (__ballot(over)) return true;
+                flush(true);
+            }
+            return false;
+        };
+        if (code_task(std::true_type{})) code_task(std::false_type{});
         // header padding: the wave of the last task
         if (tk + 1 == a.ntasks) {
 #pragma unroll

@@ -101,4 +101,12 @@ __device__ inline uint32_t group_sum(uint32_t v) {
     return v;
 }
 
+// Minimum of v over the caller's group of G = 1 << LG lanes (every lane gets it).
+template <int LG>
+__device__ inline uint32_t group_min(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < (1 << LG); o <<= 1) v = min(v, (uint32_t)__shfl_xor(v, o, 64));
+    return v;
+}
+
 }  // namespace lecb

@@ -111,6 +111,26 @@ def test_encode_bit_exact_and_round_trip(name, n, chunk, gen, clamp):
     assert np.array_equal(y, x)
 
 
+def test_skewed_lanes_encode_exactly():
+    """One lane of each chunk codes 1-bit code words while the other 15 code
+    16-bit ones: the slow lane's words complete long after the others have
+    taken hundreds of read positions, more than the encoder stages per group,
+    so it codes those chunks again with direct stores.  The stream must still
+    equal the oracle's."""
+    f = np.array([max(1, (1 << 40) >> s) for s in range(256)], np.uint64)
+    ln = oracle.package_merge_lengths(f, 16)
+    long16 = np.flatnonzero(ln == 16)
+    assert ln[0] == 1 and long16.size > 100
+    chunk, nch = 4096, 6
+    x = long16[workloads.uniform_bytes(77, chunk * nch + 1000, long16.size)].astype(np.uint8)
+    blocks = x[: chunk * nch].reshape(nch, 16, 16, 16)              # chunk, block row, lane, symbol
+    blocks[:, :, 0, :] = 0                                         # lane 0: the 1-bit code word
+    got, r, _ = gpu_encode(x, ln, chunk)
+    assert int(r["status"]) == 0
+    ref, bits = oracle.encode(x, ln, oracle.canonical_codes(ln), chunk)
+    assert np.array_equal(got, ref) and int(r["payload_bits"]) == bits
+
+
 def test_long_codes_straddle_words():
     # geometric weights: code lengths up to 16, many code words cross word boundaries
     f = np.array([max(1, (1 << 30) >> s) for s in range(256)], np.uint64)
