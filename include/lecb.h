@@ -126,7 +126,7 @@ uint64_t lecb_header_bytes(uint64_t n, uint32_t chunk);
 /* Largest stream any codebook with lengths <= max_len can produce, rounded
  * up to 16 bytes: align16(header + 4 * sum over lanes of ceil(m*max_len/32))
  * for lanes of m symbols -- the size when every symbol has a max_len-bit
- * code word.  0 on bad arguments. */
+ * code word.  0 on bad arguments or n >= 2^60. */
 uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len);
 /* Workspace bytes an encode or decode of n symbols with this chunk needs. */
 uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk);

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -21,7 +22,7 @@ LIB = os.path.join(PKG, "liblecb.so")
 ARCH = "gfx950"
 
 SOURCES = ["kernels_misc.hip", "kernels_codebook.hip", "kernels_encode.hip", "kernels_decode.hip", "codebook.cpp",
-           "api.cpp", "noalloc.hip"]
+           "host.cpp", "api.cpp", "noalloc.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -38,12 +39,44 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+# The compiler's per-kernel resource report (function name, then its figures).
+RESOURCE_REPORT = ["-Rpass-analysis=kernel-resource-usage"]
+_FN = re.compile(r"remark: Function Name: (\S+)")
+_SCRATCH = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def scratch_users(report: str) -> list[tuple[str, int]]:
+    """Kernels of a resource report that use scratch (register spills or a
+    stack): (name, bytes per lane)."""
+    users, fn = [], None
+    for line in report.splitlines():
+        m = _FN.search(line)
+        if m:
+            fn = m.group(1)
+            continue
+        m = _SCRATCH.search(line)
+        if m and int(m.group(1)) > 0:
+            users.append((fn, int(m.group(1))))
+    return users
+
+
 def _compile(src: str, obj: str) -> tuple[str, int, str]:
     path = os.path.join(CSRC, src)
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + COMMON + DEVICE + lang + ["-c", path, "-o", obj]
+    hip = src.endswith(".hip")
+    lang = ["-x", "hip"] if hip else []
+    cmd = [hipcc()] + COMMON + DEVICE + lang + (RESOURCE_REPORT if hip else []) + ["-c", path, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
-    return src, p.returncode, p.stdout + p.stderr
+    out = p.stdout + p.stderr
+    rc = p.returncode
+    if rc == 0 and hip:
+        # no kernel may spill registers or use a stack: every variant keeps its
+        # state in registers and LDS (spilled variants of the 16-wave decode
+        # gave wrong results)
+        users = scratch_users(out)
+        if users:
+            rc = 1
+            out += "\nkernels using scratch memory: " + ", ".join(f"{n} ({b} bytes/lane)" for n, b in users)
+    return src, rc, "\n".join(l for l in out.splitlines() if "remark:" not in l and not l.startswith("   "))
 
 
 def build(verbose: bool = False) -> str:

@@ -33,19 +33,6 @@ int read_back_hist(const uint64_t* d_hist, int count, void* stream, const uint64
     return LECB_OK;
 }
 
-uint64_t num_chunks_checked(uint64_t n, uint32_t chunk) {
-    return valid_chunk(chunk) ? (n + chunk - 1) / chunk : 0;
-}
-
-uint64_t header_of(uint64_t n, uint32_t chunk) {
-    const uint64_t nc = num_chunks_checked(n, chunk);
-    return nc ? table_bytes(nc) + count_bytes(nc, chunk) : 0;
-}
-
-uint64_t ws_bytes_of(uint64_t n, uint32_t chunk) {
-    return ws_total_bytes(num_chunks_checked(n, chunk));
-}
-
 int build_args(const lecb_codebook* cb, CodebookArgs* a) {
     lecb_codebook canon;
     const int rc = canonical_from_lengths(cb->len, &canon);
@@ -87,10 +74,10 @@ int encode_common(const void* d_in, int mode, uint64_t n, const void* d_blob, ui
     if (!d_in || !d_out || !d_ws || !aligned16(d_in) || !aligned16(d_out) || !aligned16(d_ws))
         return LECB_ERR_INVALID_ARG;
     if (pair && (!d_out2 || !aligned16(d_out2))) return LECB_ERR_INVALID_ARG;
-    const uint64_t nc = num_chunks_checked(n, chunk);
+    const uint64_t nc = num_chunks_of(n, chunk);
     if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
-    if (out_capacity < header_of(n, chunk)) return LECB_ERR_CAPACITY;
-    if (pair && out_capacity2 < header_of(n, chunk)) return LECB_ERR_CAPACITY;
+    if (out_capacity < header_bytes_of(n, chunk)) return LECB_ERR_CAPACITY;
+    if (pair && out_capacity2 < header_bytes_of(n, chunk)) return LECB_ERR_CAPACITY;
     EncodeLaunch L{};
     L.in = d_in;
     L.in2 = d_in2;
@@ -135,14 +122,14 @@ int decode_common(int ns, int kind, const uint8_t* const* d_stream, const uint64
     if (!d_ws || !aligned16(d_ws)) return LECB_ERR_INVALID_ARG;
     if (kind != DEC_OUT_PLANES && (!merged || !aligned16(merged))) return LECB_ERR_INVALID_ARG;
     if (kind == DEC_OUT_U16_XOR && (!w0 || !aligned16(w0))) return LECB_ERR_INVALID_ARG;
-    const uint64_t hb = header_of(n, chunk);
+    const uint64_t hb = header_bytes_of(n, chunk);
     for (int k = 0; k < ns; ++k) {
         if (!d_stream[k] || !aligned16(d_stream[k])) return LECB_ERR_INVALID_ARG;
         if (kind == DEC_OUT_PLANES && (!d_out[k] || !aligned16(d_out[k]))) return LECB_ERR_INVALID_ARG;
         if (!d_sizes && (stream_bytes[k] < hb + 4 || (stream_bytes[k] - hb) % 4)) return LECB_ERR_CORRUPT;
     }
     if (ws_bytes < ws_bytes_of(n, chunk)) return LECB_ERR_WORKSPACE;
-    const uint64_t nc = num_chunks_checked(n, chunk);
+    const uint64_t nc = num_chunks_of(n, chunk);
     if (d_sizes && !aligned16(d_sizes)) return LECB_ERR_INVALID_ARG;
     DecodeLaunch L{};
     L.nstreams = ns;
@@ -202,52 +189,6 @@ static int pertensor_common(const uint16_t* d_in, const uint16_t* d_in2, uint64_
 }
 
 extern "C" {
-
-uint32_t lecb_abi_version(void) { return LECB_ABI_VERSION; }
-
-const char* lecb_status_str(int status) {
-    switch (status) {
-        case LECB_OK: return "ok";
-        case LECB_ERR_INVALID_ARG: return "invalid argument";
-        case LECB_ERR_CAPACITY: return "output capacity too small";
-        case LECB_ERR_TOO_LARGE: return "payload needs 2^32 words or more";
-        case LECB_ERR_NO_SYMBOLS: return "no codebook possible for this histogram";
-        case LECB_ERR_HIP: return "HIP runtime error";
-        case LECB_ERR_WORKSPACE: return "workspace too small";
-        case LECB_ERR_SCRATCH: return "input too large for the static scratch of the no-allocation encode";
-        case LECB_ERR_UNCODED_SYMBOL: return "input holds a byte with no code word";
-        case LECB_ERR_CORRUPT: return "corrupt stream";
-        default: return "unknown status";
-    }
-}
-
-uint64_t lecb_num_chunks(uint64_t n, uint32_t chunk) { return num_chunks_checked(n, chunk); }
-
-uint64_t lecb_header_bytes(uint64_t n, uint32_t chunk) { return header_of(n, chunk); }
-
-uint64_t lecb_encoded_bound(uint64_t n, uint32_t chunk, uint32_t max_len) {
-    if (!valid_chunk(chunk) || max_len < 1 || max_len > 16) return 0;
-    const uint64_t nc = num_chunks_checked(n, chunk);
-    if (!nc) return 0;
-    // a lane of m symbols takes at most ceil(m * max_len / 32) words; every
-    // chunk but the last has G lanes of chunk / G symbols
-    const uint64_t G = lanes_per_chunk(chunk);
-    uint64_t words = (nc - 1) * G * (((uint64_t)chunk / G * max_len + 31) / 32);
-    const uint64_t last = n - (nc - 1) * chunk;   // symbols of the last chunk
-    const uint64_t full = last / 16, rest = last % 16;
-    for (uint64_t j = 0; j < G; ++j) {
-        const uint64_t whole = full > j ? (full - j + G - 1) / G : 0;
-        const uint64_t m = whole * 16 + ((full % G) == j && rest ? rest : 0);
-        words += (m * max_len + 31) / 32;
-    }
-    return align16(header_of(n, chunk) + 4 * words);
-}
-
-uint64_t lecb_workspace_bytes(uint64_t n, uint32_t chunk) {
-    return valid_chunk(chunk) ? ws_bytes_of(n, chunk) : 0;
-}
-
-uint64_t lecb_device_codebook_bytes(void) { return sizeof(DeviceCodebook); }
 
 int lecb_workspace_init(void* d_ws, uint64_t ws_bytes, void* stream) {
     if (!d_ws || !aligned16(d_ws) || ws_bytes < sizeof(WsHeader)) return LECB_ERR_INVALID_ARG;

@@ -89,8 +89,8 @@ struct SharedOne {
 // P streams in every workgroup: the first LUT_SIZE entries of each decode
 // table (the code words of at most LUT_BITS bits, and some of the longer
 // ones); entries past them -- longer code words, rare in byte planes -- are
-// read from the device codebook in memory.  With P = 2 and 16 waves this is
-// exactly 80 KiB, so two workgroups fill a CU's LDS.
+// read from the device codebook in memory.  With P = 2 and 12 waves this is
+// 64 KiB: two workgroups per CU.
 template <int NW, int P>
 struct SharedMany {
     uint32_t ring[NW][4][ROW_WORDS];
@@ -207,9 +207,14 @@ __device__ inline v4u restore_u32(const uint32_t (&w)[4], uint32_t q) {
     return o;
 }
 
-// 64 VGPRs at most: with 16-wave workgroups two fit a CU (8 waves per SIMD).
+// Waves per SIMD the register budget is sized for: two workgroups of the
+// largest size per CU (16 waves: 8 per SIMD, 64 VGPRs; 12 waves: 6 per SIMD,
+// 85 VGPRs).  No variant may spill registers (the build rejects scratch use).
+template <int NT>
+constexpr int decode_waves_per_simd() { return NT == 768 ? 6 : 8; }
+
 template <int NT, int P, int OUT, int LG>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<NT>(), 8))) void decode_kernel(DecArgs a) {
     static_assert(P == 1 || OUT != DEC_OUT_PLANES, "plane outputs decode one stream per workgroup");
     constexpr int NW = NT / 64;
     constexpr uint32_t G = 1u << LG;
@@ -488,10 +493,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     __syncthreads();
     if (bad) atomicOr(&flag[slot], 1u);
     {
-        // bits of the lanes decoded without fault, summed per row (one stream per row)
-        uint64_t v = (run && !bad) ? bits : 0u;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+        // bits of the lanes decoded without fault, summed per row (one stream
+        // per row; a lane has at most 4096 symbols of at most 16 bits, so the
+        // sum fits 32 bits)
+        const uint32_t v = group_sum<4>((run && !bad) ? bits : 0u);
         if (i16 == 0 && v) atomicAdd(&bsum[slot], (unsigned long long)v);
     }
     __syncthreads();
@@ -593,15 +598,16 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
         e = big ? launch<1024, 1, DEC_OUT_PLANES>(a, lg, wgs, hs) : launch<256, 1, DEC_OUT_PLANES>(a, lg, wgs, hs);
     } else if (L.out_kind == DEC_OUT_U16 || L.out_kind == DEC_OUT_U16_XOR) {
         if (L.nstreams != 2 || !L.merged || (L.out_kind == DEC_OUT_U16_XOR && !L.w0)) return LECB_ERR_INVALID_ARG;
+        // (two planes need more registers per lane: 12-wave workgroups)
         const uint64_t cpt = 2 * (16 >> lg);
         const uint64_t tasks = (L.nc + cpt - 1) / cpt;
-        const bool big = tasks >= cus * 16;
-        const uint32_t nw = big ? 16 : 4;
+        const bool big = tasks >= cus * 12;
+        const uint32_t nw = big ? 12 : 4;
         const uint32_t wgs = (uint32_t)((tasks + nw - 1) / nw);
         if (L.out_kind == DEC_OUT_U16)
-            e = big ? launch<1024, 2, DEC_OUT_U16>(a, lg, wgs, hs) : launch<256, 2, DEC_OUT_U16>(a, lg, wgs, hs);
+            e = big ? launch<768, 2, DEC_OUT_U16>(a, lg, wgs, hs) : launch<256, 2, DEC_OUT_U16>(a, lg, wgs, hs);
         else
-            e = big ? launch<1024, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs)
+            e = big ? launch<768, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs)
                     : launch<256, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs);
     } else if (L.out_kind == DEC_OUT_U32) {
         if (L.nstreams != 4 || !L.merged) return LECB_ERR_INVALID_ARG;

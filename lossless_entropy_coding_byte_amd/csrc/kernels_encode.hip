@@ -153,11 +153,6 @@ __device__ inline uint64_t wave_sum_u64(uint64_t v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
-    return v;
-}
 
 __device__ inline void set_status(WsHeader* ws, int32_t code) { atomicCAS(&ws->status, 0, code); }
 

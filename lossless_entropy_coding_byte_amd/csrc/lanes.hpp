@@ -93,19 +93,51 @@ __device__ inline void group_count(bool f, uint32_t& before, uint32_t& total) {
     total = last - first;
 }
 
+// Value of lane (lane ^ O) for O < 32: ds_swizzle in its bit mode (and mask
+// 0x1F, or mask 0, xor mask O), the pattern an immediate, so no lane index
+// stays in a register.
+template <int O>
+__device__ inline uint32_t lane_xor(uint32_t v) {
+    static_assert(O > 0 && O < 32, "the swizzle works inside groups of 32 lanes");
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (O << 10));
+}
+
+// Maximum and minimum of v over the wave (wave-uniform): swizzles inside each
+// half of 32 lanes, then the two halves' results read as scalars.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, lane_xor<1>(v));
+    v = max(v, lane_xor<2>(v));
+    v = max(v, lane_xor<4>(v));
+    v = max(v, lane_xor<8>(v));
+    v = max(v, lane_xor<16>(v));
+    return max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+}
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, lane_xor<1>(v));
+    v = min(v, lane_xor<2>(v));
+    v = min(v, lane_xor<4>(v));
+    v = min(v, lane_xor<8>(v));
+    v = min(v, lane_xor<16>(v));
+    return min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+}
+
 // Sum of v over the caller's group of G = 1 << LG lanes (every lane gets it).
 template <int LG>
 __device__ inline uint32_t group_sum(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < (1 << LG); o <<= 1) v += __shfl_xor(v, o, 64);
+    if constexpr (LG >= 1) v += lane_xor<1>(v);
+    if constexpr (LG >= 2) v += lane_xor<2>(v);
+    if constexpr (LG >= 3) v += lane_xor<4>(v);
+    if constexpr (LG >= 4) v += lane_xor<8>(v);
     return v;
 }
 
 // Minimum of v over the caller's group of G = 1 << LG lanes (every lane gets it).
 template <int LG>
 __device__ inline uint32_t group_min(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < (1 << LG); o <<= 1) v = min(v, (uint32_t)__shfl_xor(v, o, 64));
+    if constexpr (LG >= 1) v = min(v, lane_xor<1>(v));
+    if constexpr (LG >= 2) v = min(v, lane_xor<2>(v));
+    if constexpr (LG >= 3) v = min(v, lane_xor<4>(v));
+    if constexpr (LG >= 4) v = min(v, lane_xor<8>(v));
     return v;
 }
 

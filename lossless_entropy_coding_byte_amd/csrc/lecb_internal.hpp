@@ -101,6 +101,16 @@ inline uint64_t ws_stream_bytes(uint64_t nc) { return (sizeof(WsHeader) + 8 * (n
 // Two more headers after the stream parts (the four streams of a four-plane decode).
 constexpr uint64_t WS_EXTRA_BYTES = 256;
 inline uint64_t ws_total_bytes(uint64_t nc) { return 2 * ws_stream_bytes(nc) + WS_EXTRA_BYTES; }
+// ceil(n / chunk) without the wrap of n + chunk - 1 near 2^64; 0 on a bad chunk.
+inline uint64_t num_chunks_of(uint64_t n, uint32_t chunk) {
+    return valid_chunk(chunk) ? n / chunk + (n % chunk != 0) : 0;
+}
+// Stream bytes before the payload (chunk table, lane word counts); 0 on a bad chunk.
+inline uint64_t header_bytes_of(uint64_t n, uint32_t chunk) {
+    const uint64_t nc = num_chunks_of(n, chunk);
+    return nc ? table_bytes(nc) + count_bytes(nc, chunk) : 0;
+}
+inline uint64_t ws_bytes_of(uint64_t n, uint32_t chunk) { return ws_total_bytes(num_chunks_of(n, chunk)); }
 // Offset of stream k's header (k < 4): the two stream parts, then the extra headers.
 inline uint64_t ws_header_offset(int k, uint64_t nc) {
     return k < 2 ? k * ws_stream_bytes(nc) : 2 * ws_stream_bytes(nc) + (k - 2) * sizeof(WsHeader);

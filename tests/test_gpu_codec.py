@@ -658,6 +658,9 @@ def test_decode_every_workgroup_size(big, chunk, n):
 
 @pytest.mark.parametrize("big", [False, True])
 def test_bf16_two_plane_decode_workgroup_sizes(big):
+    """Both planes decoded in one launch, as two byte planes and fused into
+    16-bit words (plain and snapshot delta), at the small and the big
+    workgroup size of each kernel."""
     chunk = 16384 if not big else 4096
     n = 1_000_003 if not big else _cus() * 8 * 16384 + 3
     assert _big_workgroups(n, chunk, nstreams=2) == big
@@ -686,6 +689,23 @@ def test_bf16_two_plane_decode_workgroup_sizes(big):
     r = lecb.results_to_numpy(res)
     assert int(r[0]["status"]) == 0 and int(r[1]["status"]) == 0
     assert np.array_equal(oh[:n].cpu().numpy(), hi) and np.array_equal(ol[:n].cpu().numpy(), lo)
+    del oh, ol
+    # the fused restores (both planes in every wave, 16-bit words out) pick
+    # their own workgroup size: 12 waves when every CU gets 12 of them
+    assert _big_workgroups(n, chunk, 12, planes_per_wave=2) == big
+    xd = to_dev(x.view(np.int16))
+    y = torch.empty(n, dtype=torch.int16, device=DEV)
+    rd = lecb.new_results(2, DEV)
+    lecb.lecb_decode_bf16(streams[0][0], streams[0][1], streams[1][0], streams[1][1], bh.blob, bl.blob, chunk, n,
+                          y, rd, ws)
+    assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
+    assert torch.equal(y, xd)
+    # snapshot delta: the streams are read as W0 ^ W1 with W0 drawn here
+    w0 = to_dev(np.random.default_rng(77).integers(0, 1 << 16, n, dtype=np.uint16).view(np.int16))
+    lecb.lecb_decode_bf16_delta(streams[0][0], streams[0][1], streams[1][0], streams[1][1], bh.blob, bl.blob,
+                                chunk, n, w0, y, rd, ws)
+    assert all(int(v) == 0 for v in lecb.results_to_numpy(rd)["status"])
+    assert torch.equal(y, w0 ^ xd)
 
 
 # ----------------------------------------------------------------------------- sizes on the device
