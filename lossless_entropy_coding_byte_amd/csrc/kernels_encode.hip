@@ -43,6 +43,9 @@ constexpr int ENC_THREADS = 256;                 // four independent waves
 constexpr int ENC_WAVES = ENC_THREADS / 64;
 constexpr int ENC_WAVES_PER_CU = 32;             // pack and count waves per compute unit (grid size)
 constexpr int OFF_THREADS = 1024;
+constexpr uint32_t STAGE_LANE_WORDS = 32;   // pack: staging ring words per lane of a group
+constexpr uint32_t FLUSH_PAIRS = 8;         // pack: pairs between flushes of the staging ring (a block)
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 struct StreamArgs {
     const DeviceCodebook* cb;
@@ -207,10 +210,14 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
         const uint8_t* ln = len[P == 1 ? 0 : pl.plane];
         uint32_t bits = 0, mn = 16;
         const uint32_t nb = (pl.m + BLOCK - 1) / BLOCK;
+        // the symbols of block t + 1 are loaded while block t is counted
+        uint32_t w[4] = {0, 0, 0, 0};
+        if (nb) block_symbols<MODE>(a, block_elem(a, pl, 0), min(BLOCK, pl.m), pl.plane, w);
         for (uint32_t t = 0; t < nb; ++t) {
             const uint32_t cnt = min(BLOCK, pl.m - t * BLOCK);
-            uint32_t w[4];
-            block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, w);
+            uint32_t wn[4] = {0, 0, 0, 0};
+            if (t + 1 < nb)
+                block_symbols<MODE>(a, block_elem(a, pl, t + 1), min(BLOCK, pl.m - (t + 1) * BLOCK), pl.plane, wn);
             if (cnt == BLOCK) {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
@@ -225,6 +232,8 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
                     mn = min(mn, l);
                 }
             }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = wn[k];
         }
         unc |= mn == 0;
         const uint32_t nw = (bits + 31) >> 5;
@@ -293,13 +302,16 @@ template <int MODE, int LG>
 __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
     constexpr int P = Streams<MODE>::value;
     constexpr uint32_t G = 1u << LG;
-    constexpr uint32_t RE = 16 * G;   // staging words of a group
-    __shared__ uint32_t enc[2][256];
-    __shared__ uint32_t stage[ENC_WAVES][4][256];
+    constexpr uint32_t RE = STAGE_LANE_WORDS * G;   // staging words of a group
+    __shared__ uint32_t enc[2][256];   // code | len << 16
+    __shared__ __attribute__((aligned(16))) uint32_t stage[ENC_WAVES][4][STAGE_LANE_WORDS * 16];
     const int tid = threadIdx.x;
     const uint32_t lane = tid & 63;
 #pragma unroll
-    for (int s = 0; s < P; ++s) enc[s][tid] = a.st[s].cb->enc[tid];
+    for (int s = 0; s < P; ++s) {
+        const uint32_t e = a.st[s].cb->enc[tid];
+        enc[s][tid] = (e >> 5) | ((e & 31u) << 16);
+    }
     __syncthreads();
     const uint64_t r = (uint64_t)blockIdx.x * ENC_WAVES + (tid >> 6);
     const uint64_t t0 = range_first(r, a.ntasks, a.nranges), t1 = range_first(r + 1, a.ntasks, a.nranges);
@@ -337,90 +349,125 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
         uint32_t* const out = payload + cstart;
 
         // Reads of words 0 and 1, then the pairs.  STAGED: a completed word goes
-        // to the group's staging ring in LDS, and every 4 pairs the words below
-        // the group's lowest unwritten position go out with coalesced stores (a
-        // lane writes every G-th word); a word that would land on a slot not
-        // yet stored sets `over`, and the task is then coded again with direct
-        // stores of each word (the words stored so far are the same).
+        // to the group's staging ring in LDS (slot = payload word index mod the
+        // ring size, so 4-word groups of the payload are 16-byte groups of the
+        // ring), and before every block the words below the group's lowest
+        // unwritten position, up to a 16-byte boundary of the payload, go out
+        // with 16-byte stores (a lane writes 4 consecutive words, the group's
+        // lanes neighbouring groups of 4); when the positions reserved by the
+        // next pairs could reach a slot not yet stored, the task is coded again
+        // with direct stores of each word (the words stored so far are the
+        // same).
         const bool wr = !skip && pl.valid;
         const uint32_t nblk = (wave_max_u32(pl.m) + BLOCK - 1) / BLOCK;
         uint32_t* const ring = &stage[tid >> 6][lane >> 4][((lane & 15u) >> LG) * RE];
+        const uint32_t rbase = (uint32_t)cstart;   // (mod RE: the ring slot of the chunk's word 0)
+        const uint32_t lj = lane & (G - 1);
         auto code_task = [&](auto staged_c) -> bool {
             constexpr bool STAGED = decltype(staged_c)::value;
             uint32_t b0, n0, b1, n1;
             group_count<LG>(N >= 1, b0, n0);
             group_count<LG>(N >= 2, b1, n1);
+            // posA: position of the word being filled; posB: of the one read after it
             uint32_t posA = b0, posB = n0 + b1, cons = n0 + n1;
-            uint32_t nextk = min(N, 2u), done = 0;   // words read, words written
-            bool crossed = false, over = false;
+            uint32_t done = 0;        // words completed
+            bool crossed = false;     // a word completed in the previous pair
+            // the lane's uncompleted bits: the low `fill` bits of acc
             uint64_t acc = 0;
             uint32_t fill = 0, flushed = 0;
             auto put = [&](uint32_t pos, uint32_t word) {
-                if constexpr (STAGED) {
-                    if (pos - flushed < RE) ring[pos & (RE - 1)] = word;
-                    else over = true;
-                } else {
-                    if (wr) out[pos] = word;
-                }
+                if constexpr (STAGED) ring[(rbase + pos) & (RE - 1)] = word;
+                else if (wr) out[pos] = word;
             };
-            // STAGED: store the group's words below the lowest position still to be written
-            auto flush = [&](bool all) {
-                uint32_t f = all ? cons : (done < N ? posA : cons);
-                f = group_min<LG>(f);
+            // STAGED: store the group's completed words (those below the lowest
+            // position still to be written; `all`: every word) up to the last
+            // 16-byte boundary of the payload below them (`all`: all of them);
+            // false when the next FLUSH_PAIRS pairs could overrun the ring
+            auto flush = [&](bool all) -> bool {
+                const uint32_t f = group_min<LG>(all ? cons : (done < N ? posA : cons));
+                // [flushed, a): words before the first 16-byte boundary; [a, b):
+                // whole 16-byte groups; [b, f): the rest, stored only by `all`
+                const uint32_t a = min(f, flushed + ((0u - (rbase + flushed)) & 3u));
+                const uint32_t b = a + ((f - a) & ~3u);
                 __builtin_amdgcn_wave_barrier();
-                for (uint32_t x = flushed + (lane & (G - 1)); __ballot(x < f); x += G)
-                    if (x < f && wr) out[x] = ring[x & (RE - 1)];
-                flushed = f;
+                for (uint32_t x = flushed + lj; __ballot(x < a); x += G)
+                    if (x < a && wr) out[x] = ring[(rbase + x) & (RE - 1)];
+                for (uint32_t x = a + 4 * lj; __ballot(x < b); x += 4 * G)
+                    if (x < b && wr)
+                        *reinterpret_cast<v4u*>(out + x) = *reinterpret_cast<const v4u*>(&ring[(rbase + x) & (RE - 1)]);
+                if (all)
+                    for (uint32_t x = b + lj; __ballot(x < f); x += G)
+                        if (x < f && wr) out[x] = ring[(rbase + x) & (RE - 1)];
+                flushed = all ? f : b;
                 __builtin_amdgcn_wave_barrier();
+                // the next pairs read at most one word per lane each, so their
+                // puts stay below cons + FLUSH_PAIRS * G
+                return __ballot(cons + FLUSH_PAIRS * G - flushed > RE) == 0;
             };
-            for (uint32_t t = 0; t < nblk; ++t) {
-                const uint32_t cnt = pl.m > t * BLOCK ? min(BLOCK, pl.m - t * BLOCK) : 0u;
-                uint32_t w[4] = {0, 0, 0, 0};
-                if (cnt) block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, w);
+            // One block: its code words (the wait for its symbols), the flush of
+            // the words completed so far (STAGED), pairs 0-3, `mid` (the next
+            // block's load), pairs 4-7.  Global stores and loads complete in
+            // order, so a load's wait also waits for the stores issued before
+            // it: the stores go out a whole block before the next wait, the
+            // load half a block.  False when the staging would overrun.
+            // (One body for whole and short blocks: a second, whole-block copy
+            // needs about 20 more VGPRs, which costs occupancy.)
+            auto code_block = [&](const uint32_t (&w)[4], uint32_t cnt, auto&& mid) -> bool {
                 uint32_t e[16];
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
                     const uint32_t x = e_tab[sym_of(w, k)];
-                    e[k] = (uint32_t)k < cnt ? x : 0u;
+                    e[k] = (uint32_t)k < cnt ? x : 0u;   // (past the lane's symbols: no bits)
+                }
+                if constexpr (STAGED) {
+                    if (!flush(false)) return false;
                 }
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
+                    if (q == 4) mid();
                     // before the pair: the lanes that completed a word read the next one
-                    const bool act = 2u * q < cnt;
-                    const bool fetch = act && crossed && nextk < N;
+                    // (after a lane's last symbol no word is left to read)
+                    const bool fetch = crossed && done + 1 < N;
                     uint32_t bf, nf;
                     group_count<LG>(fetch, bf, nf);
                     posB = fetch ? cons + bf : posB;
-                    nextk += fetch ? 1u : 0u;
                     cons += nf;
-                    crossed = false;
                     // the pair's code words (at most 32 bits) into the accumulator
                     const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
-                    const uint32_t l1 = e1 & 31u;
-                    const uint32_t c2 = ((e0 >> 5) << l1) | (e1 >> 5);
-                    fill += (e0 & 31u) + l1;
-                    acc |= (uint64_t)c2 << ((64u - fill) & 63u);
-                    if (fill >= 32) {
-                        put(posA, (uint32_t)(acc >> 32));
-                        acc <<= 32;
+                    const uint32_t l = (e0 >> 16) + (e1 >> 16);
+                    const uint32_t c2 = ((e0 & 0xFFFFu) << (e1 >> 16)) | (e1 & 0xFFFFu);
+                    acc = (acc << l) | c2;
+                    fill += l;
+                    crossed = fill >= 32;
+                    if (crossed) {
                         fill -= 32;
+                        put(posA, (uint32_t)(acc >> fill));
                         posA = posB;
-                        crossed = true;
                         ++done;
                     }
-                    if constexpr (STAGED) {
-                        if ((q & 3) == 3) {
-                            if (__ballot(over)) return true;
-                            flush(false);
-                        }
-                    }
                 }
+                return true;
+            };
+            // the lane's block t (symbols loaded during the block before)
+            auto load = [&](uint32_t t, uint32_t (&w)[4]) -> uint32_t {
+                const uint32_t cnt = pl.m > t * BLOCK ? min(BLOCK, pl.m - t * BLOCK) : 0u;
+                w[0] = w[1] = w[2] = w[3] = 0;
+                if (cnt) block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, w);
+                return cnt;
+            };
+            uint32_t w[4], cnt = nblk ? load(0, w) : 0u;
+            for (uint32_t t = 0; t < nblk; ++t) {
+                uint32_t wn[4] = {0, 0, 0, 0}, cn = 0;
+                if (!code_block(w, cnt, [&] {
+                        if (t + 1 < nblk) cn = load(t + 1, wn);
+                    }))
+                    return true;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[k] = wn[k];
+                cnt = cn;
             }
-            if (fill) put(posA, (uint32_t)(acc >> 32));
-            if constexpr (STAGED) {
-                if (__ballot(over)) return true;
-                flush(true);
-            }
+            if (fill) put(posA, (uint32_t)(acc << (32 - fill)));
+            if constexpr (STAGED) flush(true);
             return false;
         };
         if (code_task(std::true_type{})) code_task(std::false_type{});
