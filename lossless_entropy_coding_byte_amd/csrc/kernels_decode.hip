@@ -86,15 +86,14 @@ struct SharedOne {
     uint32_t ring[NW][4][ROW_WORDS];   // first: every row's ring is 1 KiB-aligned
     uint16_t dec[DEC_ENTRIES];
 };
-// P streams in every workgroup: the first LUT_SIZE entries of each decode
-// table (the code words of at most LUT_BITS bits, and some of the longer
-// ones); entries past them -- longer code words, rare in byte planes -- are
-// read from the device codebook in memory.  With P = 2 and 12 waves this is
-// 64 KiB: two workgroups per CU.
+// P streams in every workgroup: every stream's whole decode table.  (A
+// table entry read from memory instead would make every lookup wait for the
+// ring loads in flight: loads complete in order.)  With P = 2 and 12 waves
+// this is 72 KiB, with P = 4 and 6 waves 72 KiB: two workgroups per CU.
 template <int NW, int P>
 struct SharedMany {
     uint32_t ring[NW][4][ROW_WORDS];
-    uint16_t lut[P][LUT_SIZE];
+    uint16_t dec[P][DEC_ENTRIES];
 };
 template <int NW, int P>
 using Shared = std::conditional_t<P == 1, SharedOne<NW>, SharedMany<NW, P>>;
@@ -209,9 +208,9 @@ __device__ inline v4u restore_u32(const uint32_t (&w)[4], uint32_t q) {
 
 // Waves per SIMD the register budget is sized for: two workgroups of the
 // largest size per CU (16 waves: 8 per SIMD, 64 VGPRs; 12 waves: 6 per SIMD,
-// 85 VGPRs).  No variant may spill registers (the build rejects scratch use).
+// 85 VGPRs; 6 waves: 3 per SIMD).  No variant may spill registers (the build rejects scratch use).
 template <int NT>
-constexpr int decode_waves_per_simd() { return NT == 768 ? 6 : 8; }
+constexpr int decode_waves_per_simd() { return NT == 768 ? 6 : NT == 384 ? 3 : 8; }
 
 template <int NT, int P, int OUT, int LG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<NT>(), 8))) void decode_kernel(DecArgs a) {
@@ -261,8 +260,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const v4u* src = reinterpret_cast<const v4u*>(a.st[q].cb->dec);
-            v4u* dst = reinterpret_cast<v4u*>(&S.lut[q][0]);
-            for (int x = tid; x < LUT_SIZE * 2 / 16; x += NT) dst[x] = src[x];
+            v4u* dst = reinterpret_cast<v4u*>(&S.dec[q][0]);
+            for (int x = tid; x < DEC_ENTRIES * 2 / 16; x += NT) dst[x] = src[x];
         }
     }
     __syncthreads();   // every wave reads entries that other waves copied
@@ -346,15 +345,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     uint32_t cons = d0 + n0 + n1;               // next word the group reads, from a0
     const uint32_t w0 = N >= 1 ? ring[(slot0 + d0 + b0) & (R - 1)] : 0u;
     const uint32_t w1 = N >= 2 ? ring[(slot0 + d0 + n0 + b1) & (R - 1)] : 0u;
-    // Bit buffer: the lane's next avail = 32 - na bits, most significant first
-    // (the two-word window with its used bits shifted out).  "The first word
-    // is used up" is avail <= 32, i.e. na >= 0 as a signed value; then a word
-    // comes in below the valid bits, shifted left by na (a zero word once the
-    // lane has read all its words).  vw counts the words taken in, read or
-    // zero, so 32 * vw - avail bits are consumed.
+    // Bit buffer: the lane's next avail = 64 - u bits, most significant first
+    // (the two-word window with its used bits shifted out; u <= 63 while the
+    // stream is valid).  "The first word is used up" is avail <= 32, i.e.
+    // u >= 32; then a word comes in below the valid bits, shifted left by
+    // u - 32 = u & 31, which is also the new u (a zero word once the lane has
+    // read all its words).  vw, the words taken in (read or zero), is kept as
+    // rp = N + 31 - vw, so that "a word is left to read" (vw < N) is rp >= 32
+    // and a read is min(u, rp) >= 32, one comparison; 32 * (vw - 2) + u bits
+    // are consumed.  Bit 7 of an entry marks a window that starts no code
+    // word (its length field then is 0x90).
     uint64_t bb = ((uint64_t)w0 << 32) | w1;
-    int32_t na = -32;
-    uint32_t vw = 2;   // (the lane's next word is word vw while vw < N)
+    uint32_t u = 0;
+    int32_t rp = (int32_t)N + 29;
     uint32_t inval = 0;
 
     // ---- decode, block by block
@@ -386,38 +389,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
             if (q == 4) top_up(pa, pa_at, pa_on);
             const uint32_t s0 = t * BLOCK + 2 * q;   // the pair's first symbol in the lane
             const bool act = FULL || s0 < m;
-            const bool sh = act && na >= 0;
-            const bool fetch = sh && vw < N;
+            const bool fetch = min((int32_t)u, act ? rp : 0) >= 32;
             uint32_t bf, nf;
             group_count<LG>(fetch, bf, nf);
             const uint32_t word = ring[(slot0 + cons + bf) & (R - 1)];
-            // avail >= 1 before a pair (a pair takes at most 32 of > 32 bits): na <= 31
-            bb |= (uint64_t)(fetch ? word : 0u) << ((uint32_t)na & 63u);
-            na -= sh ? 32 : 0;
-            vw += sh ? 1u : 0u;
+            // avail >= 1 before a pair (a pair takes at most 32 of > 32 bits): u <= 63
+            const uint32_t u31 = u & 31u;
+            bb |= (uint64_t)(fetch ? word : 0u) << u31;
+            if (FULL || act) {
+                rp -= (int32_t)(u >> 5);   // (one word taken in when u >= 32)
+                u = u31;
+            }
             cons += nf;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bool use = FULL || s0 + h < m;
                 const uint32_t idx = dec_index((uint32_t)(bb >> 32), long_sub);
                 uint32_t e;
-                if constexpr (P == 1) {
-                    e = S.dec[idx];
-                } else {
-                    e = S.lut[k][idx & (LUT_SIZE - 1)];
-                    if (__ballot(use && idx >= (uint32_t)LUT_SIZE)) {
-                        // a longer code word: its entry in the codebook's table in memory
-                        if (idx >= (uint32_t)LUT_SIZE) e = ln.cb->dec[idx];
-                    }
-                }
+                if constexpr (P == 1) e = S.dec[idx];
+                else e = S.dec[k][idx];
                 if constexpr (!FULL) e = use ? e : 0u;
-                inval |= e;   // bit 7: no code word starts here
                 bb <<= (e & 63u);   // (len <= 16; bits 8.. hold the symbol)
-                na += (int32_t)(e & 0xFFu);
+                u += e & 0xFFu;
                 const int x = 2 * q + h;
                 ev[x & 3] = e;
                 if ((x & 3) == 3) w[x >> 2] = syms4(ev);
             }
+            inval |= ev[(2 * q) & 3] | ev[(2 * q + 1) & 3];   // bit 7: no code word starts here
         }
         top_up(pb, pb_at, pb_on);
     };
@@ -474,7 +472,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     // ---- the lane's end: every word read, the last one needed, zero padding
     uint32_t bits = 0;
     if (run && m) {
-        bits = 32 * vw - (uint32_t)(32 - na);
+        const uint32_t vw = (uint32_t)((int32_t)N + 31 - rp);
+        bits = 32 * (vw - 2) + u;
         if ((inval & 0x80u) || vw < N || bits > 32 * N || bits <= 32 * (N - 1)) bad = true;
         const uint32_t rest = 32 * N - bits;   // padding bits: the next ones in the buffer
         if (!bad && rest && (bb >> (64 - rest)) != 0) bad = true;
@@ -585,9 +584,9 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
     if (cus == 0) return LECB_ERR_HIP;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    // Workgroup size: 16 waves (the tables are one copy per workgroup, 8 for
-    // four planes) when the tasks give every CU such a workgroup, else 4
-    // waves, so that small inputs still spread over the CUs.
+    // Workgroup size: 16 waves (12 for two planes, 6 for four: the tables are
+    // one copy per workgroup) when the tasks give every CU such a workgroup,
+    // else 4 waves, so that small inputs still spread over the CUs.
     if (L.out_kind == DEC_OUT_PLANES) {
         const uint64_t cpt = 4 * (16 >> lg);
         const uint64_t tasks = (L.nc + cpt - 1) / cpt;
@@ -611,12 +610,13 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
                     : launch<256, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs);
     } else if (L.out_kind == DEC_OUT_U32) {
         if (L.nstreams != 4 || !L.merged) return LECB_ERR_INVALID_ARG;
+        // (four tables in LDS: 6-wave workgroups)
         const uint64_t cpt = 16 >> lg;
         const uint64_t tasks = (L.nc + cpt - 1) / cpt;
-        const bool big = tasks >= cus * 8;
-        const uint32_t nw = big ? 8 : 4;
+        const bool big = tasks >= cus * 6;
+        const uint32_t nw = big ? 6 : 4;
         const uint32_t wgs = (uint32_t)((tasks + nw - 1) / nw);
-        e = big ? launch<512, 4, DEC_OUT_U32>(a, lg, wgs, hs) : launch<256, 4, DEC_OUT_U32>(a, lg, wgs, hs);
+        e = big ? launch<384, 4, DEC_OUT_U32>(a, lg, wgs, hs) : launch<256, 4, DEC_OUT_U32>(a, lg, wgs, hs);
     } else {
         return LECB_ERR_INVALID_ARG;
     }
