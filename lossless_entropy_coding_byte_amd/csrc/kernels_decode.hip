@@ -427,15 +427,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     }
     const uint32_t nblk = (mmax + BLOCK - 1) / BLOCK, nfull = mmin / BLOCK;
     const uint64_t lane_e0 = c * a.chunk + (uint64_t)j * BLOCK;   // first element of the lane's block 0
-    for (uint32_t t = 0; t < nblk; ++t) {
-        uint32_t w[4];
-        if (t < nfull) decode_block(t, std::true_type{}, w);
-        else decode_block(t, std::false_type{}, w);
-        // the block's output: 16 symbols of block tG + j of the chunk
-        const uint32_t cnt = m > t * BLOCK ? min(BLOCK, m - t * BLOCK) : 0u;
+    // The output of block t: 16 symbols of block tG + j of the chunk (FULL:
+    // every lane's block is whole).
+    // (x0: FULL, OUT_U16_XOR: the block's 16 bytes of the other snapshot,
+    // loaded before the block's ring loads so that their wait does not drain
+    // them)
+    auto store_block = [&](uint32_t t, const uint32_t (&w)[4], auto full_c, const v4u& x0) {
+        constexpr bool FULL = decltype(full_c)::value;
+        const uint32_t cnt = FULL ? BLOCK : (m > t * BLOCK ? min(BLOCK, m - t * BLOCK) : 0u);
         const uint64_t e0 = lane_e0 + (uint64_t)(t << LG) * BLOCK;
         if constexpr (OUT == DEC_OUT_PLANES) {
-            if (t < nfull || cnt == BLOCK) {   // (every lane's block is whole below nfull)
+            if (FULL || cnt == BLOCK) {
                 v4u v;
                 v.x = w[0];
                 v.y = w[1];
@@ -451,15 +453,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
             if constexpr (OUT == DEC_OUT_U16 || OUT == DEC_OUT_U16_XOR) {
                 v4u v = restore_u16(w, k);
                 const uint64_t at = 2 * e0 + 16 * k;
-                if (cnt == BLOCK) {
-                    if constexpr (OUT == DEC_OUT_U16_XOR) v ^= *reinterpret_cast<const v4u*>(a.w0 + at);
+                if (FULL || cnt == BLOCK) {
+                    if constexpr (OUT == DEC_OUT_U16_XOR) v ^= FULL ? x0 : *reinterpret_cast<const v4u*>(a.w0 + at);
                     *reinterpret_cast<v4u*>(a.merged + at) = v;
                 }
             } else {
                 const v4u v = restore_u32(w, k);
-                if (cnt == BLOCK) *reinterpret_cast<v4u*>(a.merged + 4 * e0 + 16 * k) = v;
+                if (FULL || cnt == BLOCK) *reinterpret_cast<v4u*>(a.merged + 4 * e0 + 16 * k) = v;
             }
-            if (cnt && cnt < BLOCK) {
+            if (!FULL && cnt && cnt < BLOCK) {
                 // the tensor's last block: byte P-1-k of each element (plane k holds byte P-1-k)
                 for (uint32_t x = 0; x < cnt; ++x) {
                     const uint64_t at = (uint64_t)P * (e0 + x) + (P - 1 - k);
@@ -467,6 +469,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
                     a.merged[at] = OUT == DEC_OUT_U16_XOR ? (uint8_t)(sym ^ a.w0[at]) : sym;
                 }
             }
+        }
+    };
+    // A wave whose lanes all have only whole blocks (every wave but those of
+    // the tensor's last chunk) runs a loop of whole blocks: every lane ends
+    // each block with the same memory operations (two ring loads, one store),
+    // so the compiler's waits for a ring load count the store issued after
+    // the older load and leave it in flight.  (With the general blocks in
+    // the same loop the store could not be counted, and the wait also drained
+    // the newer ring load.)  The other waves take the general block for all
+    // their blocks: two loops, one taken, so their registers are not live at
+    // the same time.
+    if (nfull == nblk) {
+        for (uint32_t t = 0; t < nblk; ++t) {
+            uint32_t w[4];
+            v4u x0 = {0, 0, 0, 0};
+            if constexpr (OUT == DEC_OUT_U16_XOR)
+                x0 = *reinterpret_cast<const v4u*>(a.w0 + 2 * (lane_e0 + (uint64_t)(t << LG) * BLOCK) + 16 * k);
+            decode_block(t, std::true_type{}, w);
+            store_block(t, w, std::true_type{}, x0);
+        }
+    } else {
+        for (uint32_t t = 0; t < nblk; ++t) {
+            uint32_t w[4];
+            decode_block(t, std::false_type{}, w);
+            store_block(t, w, std::false_type{}, v4u{0, 0, 0, 0});
         }
     }
     // ---- the lane's end: every word read, the last one needed, zero padding
