@@ -697,12 +697,19 @@ KERNEL_SOURCES = {"encode": "kernels_encode.hip", "encode_pair": "kernels_encode
                   "histogram": "kernels_misc.hip"}
 
 
+# headers every kernel source includes (a change there changes the kernels too)
+KERNEL_HEADERS = ("lanes.hpp", "lecb_internal.hpp")
+
+
 def source_sha(label):
+    """SHA-256 over the kernel's source file and the shared headers, in that order."""
     import hashlib
 
-    path = os.path.join(ROOT, "lossless_entropy_coding_byte_amd", "csrc", KERNEL_SOURCES[label])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[label],) + KERNEL_HEADERS:
+        with open(os.path.join(ROOT, "lossless_entropy_coding_byte_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload, label):
