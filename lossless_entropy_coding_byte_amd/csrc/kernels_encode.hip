@@ -427,9 +427,12 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
                     if (q == 4) mid();
                     // before the pair: the lanes that completed a word read the next one
                     // (after a lane's last symbol no word is left to read)
-                    const bool fetch = crossed && done + 1 < N;
+                    // (the loop runs with every lane active, so the ballot of the
+                    // AND is the AND of the ballots of the two comparisons)
+                    const bool more = done + 1 < N;
+                    const bool fetch = crossed && more;
                     uint32_t bf, nf;
-                    group_count<LG>(fetch, bf, nf);
+                    group_count_mask<LG>(__builtin_amdgcn_ballot_w64(crossed) & __builtin_amdgcn_ballot_w64(more), bf, nf);
                     posB = fetch ? cons + bf : posB;
                     cons += nf;
                     // the pair's code words (at most 32 bits) into the accumulator

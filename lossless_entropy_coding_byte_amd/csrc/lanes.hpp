@@ -57,12 +57,12 @@ __device__ inline uint32_t row_bcast(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + SRC, 0xF, 0xF, false);
 }
 
-// Exclusive count of `f` over the lanes of the caller's group (G = 1 << LG
-// lanes, aligned inside a row) and the group's total.  Every lane of the wave
-// must call it (the broadcasts read neighbouring lanes).
+// Exclusive count over the lanes of the caller's group (G = 1 << LG lanes,
+// aligned inside a row) of the lanes whose bit of the wave mask `m` is set,
+// and the group's total.  Every lane of the wave must call it (the broadcasts
+// read neighbouring lanes).
 template <int LG>
-__device__ inline void group_count(bool f, uint32_t& before, uint32_t& total) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+__device__ inline void group_count_mask(uint64_t m, uint32_t& before, uint32_t& total) {
     const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     // inclusive count: p plus this lane's bit of m, taken as the carry-in
     uint32_t q;
@@ -91,6 +91,12 @@ __device__ inline void group_count(bool f, uint32_t& before, uint32_t& total) {
     }
     before = p - first;
     total = last - first;
+}
+
+// The same for a per-lane flag `f` (its ballot is the mask).
+template <int LG>
+__device__ inline void group_count(bool f, uint32_t& before, uint32_t& total) {
+    group_count_mask<LG>(__builtin_amdgcn_ballot_w64(f), before, total);
 }
 
 // Value of lane (lane ^ O) for O < 32: ds_swizzle in its bit mode (and mask
