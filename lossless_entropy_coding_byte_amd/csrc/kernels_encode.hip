@@ -366,26 +366,30 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
         const uint32_t lj = lane & (G - 1);
         auto code_task = [&](auto staged_c) -> bool {
             constexpr bool STAGED = decltype(staged_c)::value;
+            // Positions are payload word indices of the chunk plus rbase (mod
+            // 2^32), so that a position's low bits are its ring slot.
             uint32_t b0, n0, b1, n1;
             group_count<LG>(N >= 1, b0, n0);
             group_count<LG>(N >= 2, b1, n1);
-            // posA: position of the word being filled; posB: of the one read after it
-            uint32_t posA = b0, posB = n0 + b1, cons = n0 + n1;
+            // posA: position of the word being filled; posB: of the one read
+            // after it; cons: the group's next position to read
+            uint32_t posA = rbase + b0, posB = rbase + n0 + b1, cons = rbase + n0 + n1;
             uint32_t done = 0;        // words completed
-            bool crossed = false;     // a word completed in the previous pair
+            const int32_t last_word = (int32_t)N - 1;
+            uint64_t crossed = 0;     // lanes that completed a word in the previous pair
             // the lane's uncompleted bits: the low `fill` bits of acc
             uint64_t acc = 0;
-            uint32_t fill = 0, flushed = 0;
+            uint32_t fill = 0, flushed = 0;   // flushed: chunk-relative
             auto put = [&](uint32_t pos, uint32_t word) {
-                if constexpr (STAGED) ring[(rbase + pos) & (RE - 1)] = word;
-                else if (wr) out[pos] = word;
+                if constexpr (STAGED) ring[pos & (RE - 1)] = word;
+                else if (wr) out[pos - rbase] = word;
             };
             // STAGED: store the group's completed words (those below the lowest
             // position still to be written; `all`: every word) up to the last
             // 16-byte boundary of the payload below them (`all`: all of them);
             // false when the next FLUSH_PAIRS pairs could overrun the ring
             auto flush = [&](bool all) -> bool {
-                const uint32_t f = group_min<LG>(all ? cons : (done < N ? posA : cons));
+                const uint32_t f = group_min<LG>((all ? cons : (done < N ? posA : cons)) - rbase);
                 // [flushed, a): words before the first 16-byte boundary; [a, b):
                 // whole 16-byte groups; [b, f): the rest, stored only by `all`
                 const uint32_t a = min(f, flushed + ((0u - (rbase + flushed)) & 3u));
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
                 __builtin_amdgcn_wave_barrier();
                 // the next pairs read at most one word per lane each, so their
                 // puts stay below cons + FLUSH_PAIRS * G
-                return __ballot(cons + FLUSH_PAIRS * G - flushed > RE) == 0;
+                return __ballot(cons - rbase + FLUSH_PAIRS * G - flushed > RE) == 0;
             };
             // One block: its code words (the wait for its symbols), the flush of
             // the words completed so far (STAGED), pairs 0-3, `mid` (the next
@@ -416,9 +420,12 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
             auto code_block = [&](const uint32_t (&w)[4], uint32_t cnt, auto&& mid) -> bool {
                 uint32_t e[16];
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const uint32_t x = e_tab[sym_of(w, k)];
-                    e[k] = (uint32_t)k < cnt ? x : 0u;   // (past the lane's symbols: no bits)
+                for (int k = 0; k < 16; ++k) e[k] = e_tab[sym_of(w, k)];
+                // past the lane's symbols: no bits (only a lane's last block
+                // is short, so the wave mostly skips this)
+                if (__builtin_amdgcn_ballot_w64(cnt < BLOCK) != 0) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) e[k] = (uint32_t)k < cnt ? e[k] : 0u;
                 }
                 if constexpr (STAGED) {
                     if (!flush(false)) return false;
@@ -426,29 +433,30 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     if (q == 4) mid();
-                    // before the pair: the lanes that completed a word read the next one
-                    // (after a lane's last symbol no word is left to read)
-                    // (the loop runs with every lane active, so the ballot of the
-                    // AND is the AND of the ballots of the two comparisons)
-                    const bool more = done + 1 < N;
-                    const bool fetch = crossed && more;
-                    uint32_t bf, nf;
-                    group_count_mask<LG>(__builtin_amdgcn_ballot_w64(crossed) & __builtin_amdgcn_ballot_w64(more), bf, nf);
-                    posB = fetch ? cons + bf : posB;
-                    cons += nf;
+                    // before the pair: the lanes that completed a word read the
+                    // next one (after a lane's last word no word is left to
+                    // read), at the group's next positions in lane order (the
+                    // loop runs with every lane active, so ballots see the wave)
+                    const uint64_t fm = crossed & __builtin_amdgcn_ballot_w64((int32_t)done < last_word);
+                    uint32_t below, upto;
+                    group_scan_mask<LG>(fm, below, upto);
+                    const uint32_t k = cons - group_first<LG>(below);
+                    posB = __builtin_amdgcn_inverse_ballot_w64(fm) ? k + below : posB;
+                    cons = k + group_last<LG>(upto);
                     // the pair's code words (at most 32 bits) into the accumulator
                     const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
                     const uint32_t l = (e0 >> 16) + (e1 >> 16);
                     const uint32_t c2 = ((e0 & 0xFFFFu) << (e1 >> 16)) | (e1 & 0xFFFFu);
                     acc = (acc << l) | c2;
-                    fill += l;
-                    crossed = fill >= 32;
-                    if (crossed) {
-                        fill -= 32;
-                        put(posA, (uint32_t)(acc >> fill));
+                    fill += l;   // at most 31 + 32
+                    const bool cr = fill >= 32;
+                    crossed = __builtin_amdgcn_ballot_w64(cr);
+                    fill &= 31u;
+                    if (cr) {
+                        put(posA, __builtin_amdgcn_alignbit((uint32_t)(acc >> 32), (uint32_t)acc, fill));
                         posA = posB;
-                        ++done;
                     }
+                    done = plus_lane_bit(done, crossed);
                 }
                 return true;
             };

@@ -51,46 +51,70 @@ __device__ inline uint32_t lane_symbols(uint32_t m, uint32_t j) {
     return whole * BLOCK + ((full & (G - 1)) == j && rest ? rest : 0u);
 }
 
-// Value of lane `src` of the caller's row, broadcast over the row (DPP).
+// A DPP move whose every lane reads a lane of its own row (row broadcasts,
+// quad permutations).  Kept a separate move: in the form the compiler folds
+// into the VALU operation that uses it (old value 0, bound control set), the
+// folded subtract (v_subrev_u32_dpp) gave the unbroadcast operand on every
+// lane but the source lane when measured on gfx950 (the folded add was
+// right), so no folding is relied on.
+template <int CTRL>
+__device__ inline uint32_t dpp_move(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Value of lane `src` of the caller's row, broadcast over the row.
 template <int SRC>
 __device__ inline uint32_t row_bcast(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + SRC, 0xF, 0xF, false);
+    return dpp_move<0x150 + SRC>(v);
+}
+
+// v plus this lane's bit of the wave mask m (one add with carry-in).
+__device__ inline uint32_t plus_lane_bit(uint32_t v, uint64_t m) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(carry_out) : "v"(v), "s"(m));
+    (void)carry_out;
+    return r;
 }
 
 // Exclusive count over the lanes of the caller's group (G = 1 << LG lanes,
 // aligned inside a row) of the lanes whose bit of the wave mask `m` is set,
 // and the group's total.  Every lane of the wave must call it (the broadcasts
 // read neighbouring lanes).
+//
+// The parts: p, the set lanes of the wave below this lane (group_scan_mask);
+// q, p plus this lane's bit (the inclusive count); group_first(p), p of the
+// group's first lane; group_last(q), q of the group's last lane.  Then
+// before = p - group_first(p) and total = group_last(q) - group_first(p).
+template <int LG>
+__device__ inline void group_scan_mask(uint64_t m, uint32_t& p, uint32_t& q) {
+    p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    q = plus_lane_bit(p, m);
+}
+template <int LG>
+__device__ inline uint32_t group_first(uint32_t p) {
+    if constexpr (LG == 0) return p;
+    else if constexpr (LG == 1) return dpp_move<0xA0>(p);   // quad_perm [0,0,2,2]
+    else if constexpr (LG == 2) return dpp_move<0x00>(p);   // quad_perm [0,0,0,0]
+    else if constexpr (LG == 3) return (threadIdx.x & 8u) ? row_bcast<8>(p) : row_bcast<0>(p);
+    else return row_bcast<0>(p);
+}
+template <int LG>
+__device__ inline uint32_t group_last(uint32_t q) {
+    if constexpr (LG == 0) return q;
+    else if constexpr (LG == 1) return dpp_move<0xF5>(q);   // quad_perm [1,1,3,3]
+    else if constexpr (LG == 2) return dpp_move<0xFF>(q);   // quad_perm [3,3,3,3]
+    else if constexpr (LG == 3) return (threadIdx.x & 8u) ? row_bcast<15>(q) : row_bcast<7>(q);
+    else return row_bcast<15>(q);
+}
+
 template <int LG>
 __device__ inline void group_count_mask(uint64_t m, uint32_t& before, uint32_t& total) {
-    const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    // inclusive count: p plus this lane's bit of m, taken as the carry-in
-    uint32_t q;
-    uint64_t carry_out;
-    asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(q), "=s"(carry_out) : "v"(p), "s"(m));
-    (void)carry_out;
-    uint32_t first, last;
-    if constexpr (LG == 0) {
-        first = p;
-        last = q;
-    } else if constexpr (LG == 1) {
-        first = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0xA0, 0xF, 0xF, false);   // quad_perm [0,0,2,2]
-        last = (uint32_t)__builtin_amdgcn_mov_dpp((int)q, 0xF5, 0xF, 0xF, false);    // quad_perm [1,1,3,3]
-    } else if constexpr (LG == 2) {
-        first = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0x00, 0xF, 0xF, false);   // quad_perm [0,0,0,0]
-        last = (uint32_t)__builtin_amdgcn_mov_dpp((int)q, 0xFF, 0xF, 0xF, false);    // quad_perm [3,3,3,3]
-    } else if constexpr (LG == 3) {
-        const bool hi = (threadIdx.x & 8u) != 0;
-        const uint32_t f0 = row_bcast<0>(p), f8 = row_bcast<8>(p);
-        const uint32_t l7 = row_bcast<7>(q), l15 = row_bcast<15>(q);
-        first = hi ? f8 : f0;
-        last = hi ? l15 : l7;
-    } else {
-        first = row_bcast<0>(p);
-        last = row_bcast<15>(q);
-    }
+    uint32_t p, q;
+    group_scan_mask<LG>(m, p, q);
+    const uint32_t first = group_first<LG>(p);
     before = p - first;
-    total = last - first;
+    total = group_last<LG>(q) - first;
 }
 
 // The same for a per-lane flag `f` (its ballot is the mask).
