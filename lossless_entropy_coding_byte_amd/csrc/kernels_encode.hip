@@ -72,7 +72,9 @@ struct EncArgs {
     uint64_t nc;
     uint64_t ntasks;     // tasks of chunks_per_task chunks
     uint32_t cpt;        // chunks per task
-    uint32_t nranges;    // waves of the count and of the pack launch
+    uint32_t nranges;    // waves of the pack launch: range r of the tasks each
+    uint32_t nsub;       // waves of the count launch: range r is its sub-ranges rK .. rK + K - 1
+    uint32_t sub_per_range;   // K
     StreamArgs st[2];
 };
 
@@ -202,8 +204,8 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
 #pragma unroll
     for (int s = 0; s < P; ++s) len[s][tid] = (uint8_t)(a.st[s].cb->enc[tid] & 31u);
     __syncthreads();
-    const uint64_t r = (uint64_t)blockIdx.x * ENC_WAVES + (tid >> 6);
-    const uint64_t t0 = range_first(r, a.ntasks, a.nranges), t1 = range_first(r + 1, a.ntasks, a.nranges);
+    const uint64_t r = (uint64_t)blockIdx.x * ENC_WAVES + (tid >> 6);   // sub-range
+    const uint64_t t0 = range_first(r, a.ntasks, a.nsub), t1 = range_first(r + 1, a.ntasks, a.nsub);
     uint64_t words[2] = {0, 0}, bits_all[2] = {0, 0};
     bool unc = false;
     for (uint64_t tk = t0; tk < t1; ++tk) {
@@ -211,14 +213,15 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
         const uint8_t* ln = len[P == 1 ? 0 : pl.plane];
         uint32_t bits = 0, mn = 16;
         const uint32_t nb = (pl.m + BLOCK - 1) / BLOCK;
-        // the symbols of block t + 1 are loaded while block t is counted
-        uint32_t w[4] = {0, 0, 0, 0};
+        // the symbols of blocks t + 1 and t + 2 are in flight while block t is counted
+        uint32_t w[4] = {0, 0, 0, 0}, wn[4] = {0, 0, 0, 0};
         if (nb) block_symbols<MODE>(a, block_elem(a, pl, 0), min(BLOCK, pl.m), pl.plane, w);
+        if (nb > 1) block_symbols<MODE>(a, block_elem(a, pl, 1), min(BLOCK, pl.m - BLOCK), pl.plane, wn);
         for (uint32_t t = 0; t < nb; ++t) {
             const uint32_t cnt = min(BLOCK, pl.m - t * BLOCK);
-            uint32_t wn[4] = {0, 0, 0, 0};
-            if (t + 1 < nb)
-                block_symbols<MODE>(a, block_elem(a, pl, t + 1), min(BLOCK, pl.m - (t + 1) * BLOCK), pl.plane, wn);
+            uint32_t wnn[4] = {0, 0, 0, 0};
+            if (t + 2 < nb)
+                block_symbols<MODE>(a, block_elem(a, pl, t + 2), min(BLOCK, pl.m - (t + 2) * BLOCK), pl.plane, wnn);
             if (cnt == BLOCK) {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
@@ -234,7 +237,10 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
                 }
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) w[k] = wn[k];
+            for (int k = 0; k < 4; ++k) {
+                w[k] = wn[k];
+                wn[k] = wnn[k];
+            }
         }
         unc |= mn == 0;
         const uint32_t nw = (bits + 31) >> 5;
@@ -269,9 +275,9 @@ __global__ __launch_bounds__(OFF_THREADS) void offsets_kernel(EncArgs a, int ns)
     for (int s = 0; s < ns; ++s) {
         const StreamArgs& st = a.st[s];
         uint64_t run = 0;
-        for (uint32_t b = 0; b < a.nranges; b += OFF_THREADS) {
+        for (uint32_t b = 0; b < a.nsub; b += OFF_THREADS) {
             const uint32_t i = b + tid;
-            const uint64_t v = i < a.nranges ? st.range_words[i] : 0ull;
+            const uint64_t v = i < a.nsub ? st.range_words[i] : 0ull;
             uint64_t incl = v;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(OFF_THREADS) void offsets_kernel(EncArgs a, int ns)
                 before += w < wave ? part[w] : 0ull;
                 total += part[w];
             }
-            if (i < a.nranges) st.range_words[i] = run + before + incl - v;
+            if (i < a.nsub) st.range_words[i] = run + before + incl - v;
             run += total;
             __syncthreads();
         }
@@ -326,7 +332,8 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
     // a stream with a status already (a byte without a code word, too many
     // words) gets no payload
     const bool skip = __hip_atomic_load(&my_ws->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    uint64_t base = (second ? a.st[1].range_words : a.st[0].range_words)[r];   // first payload word of the range
+    // first payload word of the range: that of its first sub-range
+    uint64_t base = (second ? a.st[1].range_words : a.st[0].range_words)[r * a.sub_per_range];
     const uint32_t* e_tab = enc[second ? 1 : 0];
 
     for (uint64_t tk = t0; tk < t1; ++tk) {
@@ -540,17 +547,18 @@ hipError_t with_mode(int mode, F&& f) {
     }
 }
 
-// Workgroups of a pack kernel resident on one CU (asked once per device, mode
-// and lane count; concurrent first calls store the same value).
-uint64_t pack_workgroups_per_cu(int mode, int lg, const void* kernel) {
-    static std::atomic<int> cached[MAX_DEVICES][ENC_NUM_MODES][5];
+// Workgroups of an encode kernel resident on one CU (asked once per device,
+// kernel (0 count, 1 pack), mode and lane count; concurrent first calls store
+// the same value).
+uint64_t workgroups_per_cu(int which, int mode, int lg, const void* kernel) {
+    static std::atomic<int> cached[MAX_DEVICES][2][ENC_NUM_MODES][5];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 4;
-    int nb = cached[dev][mode][lg].load(std::memory_order_relaxed);
+    int nb = cached[dev][which][mode][lg].load(std::memory_order_relaxed);
     if (!nb) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, ENC_THREADS, 0) != hipSuccess || nb <= 0)
             nb = 4;
-        cached[dev][mode][lg].store(nb, std::memory_order_relaxed);
+        cached[dev][which][mode][lg].store(nb, std::memory_order_relaxed);
     }
     return (uint64_t)nb;
 }
@@ -599,15 +607,19 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
         st.nw_pad_to = tb + cb;
         st.res = L.st[s].res;
         st.ws = L.st[s].ws;
-        st.range_words = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);  // room for nc >= nranges values
+        st.range_words = reinterpret_cast<uint64_t*>(L.st[s].ws + 1);  // room for nc + 4 >= nsub values
     }
     // Ranges: one per wave of the pack launch, as many waves as the GPU holds
     // at once (workgroups of the pack kernel resident per CU, from its
     // registers and LDS) when there are tasks enough, never more ranges than
-    // tasks (a range is at least one task, so at most nc of them fit the
-    // workspace).  Every wave then works from the start to the end of the
-    // launch; a grid of more waves than fit ran a second round that slowed
-    // the first one's last tasks (1 GiB of int8: 1.64 -> 1.27 ms).
+    // tasks beyond the last workgroup's padding.  Every wave then works from
+    // the start to the end of the launch; a grid of more waves than fit ran a
+    // second round that slowed the first one's last tasks (1 GiB of int8:
+    // 1.64 -> 1.27 ms).  The count launch, which mostly waits for its loads,
+    // splits every range into K sub-ranges (K equal parts of a range end
+    // where the ranges end) for as many waves as the GPU holds of it, never
+    // more sub-ranges than tasks; so at most nc + 3 values go to the
+    // workspace, which holds nc + 4.
     const uint64_t cus = (uint64_t)device_cu_count();
     if (cus == 0) return LECB_ERR_HIP;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -615,13 +627,20 @@ int launch_encode(const EncodeLaunch& L, void* stream) {
         constexpr int M = decltype(m)::value;
         return with_lg(a.lg, [&](auto g) {
             constexpr int LG = decltype(g)::value;
-            const uint64_t per_cu = pack_workgroups_per_cu(M, LG, reinterpret_cast<const void*>(&pack_kernel<M, LG>));
+            const uint64_t per_cu = workgroups_per_cu(1, M, LG, reinterpret_cast<const void*>(&pack_kernel<M, LG>));
+            const uint64_t count_per_cu = workgroups_per_cu(0, M, 0, reinterpret_cast<const void*>(&count_kernel<M>));
             uint64_t waves = cus * per_cu * ENC_WAVES;
             if (waves > a.ntasks) waves = a.ntasks;
             const uint64_t nwg = (waves + ENC_WAVES - 1) / ENC_WAVES;
-            a.nranges = (uint32_t)(nwg * ENC_WAVES);   // at most ntasks + 3 <= nc + 3: the workspace has room
+            a.nranges = (uint32_t)(nwg * ENC_WAVES);
+            uint64_t k = (cus * count_per_cu * ENC_WAVES + a.nranges - 1) / a.nranges;
+            const uint64_t kmax = a.ntasks / a.nranges;
+            if (k > kmax) k = kmax;
+            if (k < 1) k = 1;
+            a.sub_per_range = (uint32_t)k;
+            a.nsub = (uint32_t)(a.nranges * k);
             const dim3 grid((uint32_t)nwg), block(ENC_THREADS);
-            hipLaunchKernelGGL(count_kernel<M>, grid, block, 0, hs, a);
+            hipLaunchKernelGGL(count_kernel<M>, dim3((uint32_t)(nwg * k)), block, 0, hs, a);
             hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(OFF_THREADS), 0, hs, a, ns);
             hipLaunchKernelGGL((pack_kernel<M, LG>), grid, block, 0, hs, a);
             return hipSuccess;
