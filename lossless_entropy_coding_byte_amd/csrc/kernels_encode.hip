@@ -445,11 +445,10 @@ __global__ __launch_bounds__(ENC_THREADS) void pack_kernel(EncArgs a) {
                     // read), at the group's next positions in lane order (the
                     // loop runs with every lane active, so ballots see the wave)
                     const uint64_t fm = crossed & __builtin_amdgcn_ballot_w64((int32_t)done < last_word);
-                    uint32_t below, upto;
-                    group_scan_mask<LG>(fm, below, upto);
-                    const uint32_t k = cons - group_first<LG>(below);
-                    posB = __builtin_amdgcn_inverse_ballot_w64(fm) ? k + below : posB;
-                    cons = k + group_last<LG>(upto);
+                    uint32_t below, total;
+                    group_count_mask<LG>(fm, below, total);
+                    posB = __builtin_amdgcn_inverse_ballot_w64(fm) ? cons + below : posB;
+                    cons += total;
                     // the pair's code words (at most 32 bits) into the accumulator
                     const uint32_t e0 = e[2 * q], e1 = e[2 * q + 1];
                     const uint32_t l = (e0 >> 16) + (e1 >> 16);

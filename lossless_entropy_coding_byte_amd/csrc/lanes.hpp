@@ -51,23 +51,6 @@ __device__ inline uint32_t lane_symbols(uint32_t m, uint32_t j) {
     return whole * BLOCK + ((full & (G - 1)) == j && rest ? rest : 0u);
 }
 
-// A DPP move whose every lane reads a lane of its own row (row broadcasts,
-// quad permutations).  Kept a separate move: in the form the compiler folds
-// into the VALU operation that uses it (old value 0, bound control set), the
-// folded subtract (v_subrev_u32_dpp) gave the unbroadcast operand on every
-// lane but the source lane when measured on gfx950 (the folded add was
-// right), so no folding is relied on.
-template <int CTRL>
-__device__ inline uint32_t dpp_move(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-
-// Value of lane `src` of the caller's row, broadcast over the row.
-template <int SRC>
-__device__ inline uint32_t row_bcast(uint32_t v) {
-    return dpp_move<0x150 + SRC>(v);
-}
-
 // v plus this lane's bit of the wave mask m (one add with carry-in).
 __device__ inline uint32_t plus_lane_bit(uint32_t v, uint64_t m) {
     uint32_t r;
@@ -79,42 +62,16 @@ __device__ inline uint32_t plus_lane_bit(uint32_t v, uint64_t m) {
 
 // Exclusive count over the lanes of the caller's group (G = 1 << LG lanes,
 // aligned inside a row) of the lanes whose bit of the wave mask `m` is set,
-// and the group's total.  Every lane of the wave must call it (the broadcasts
-// read neighbouring lanes).
-//
-// The parts: p, the set lanes of the wave below this lane (group_scan_mask);
-// q, p plus this lane's bit (the inclusive count); group_first(p), p of the
-// group's first lane; group_last(q), q of the group's last lane.  Then
-// before = p - group_first(p) and total = group_last(q) - group_first(p).
-template <int LG>
-__device__ inline void group_scan_mask(uint64_t m, uint32_t& p, uint32_t& q) {
-    p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    q = plus_lane_bit(p, m);
-}
-template <int LG>
-__device__ inline uint32_t group_first(uint32_t p) {
-    if constexpr (LG == 0) return p;
-    else if constexpr (LG == 1) return dpp_move<0xA0>(p);   // quad_perm [0,0,2,2]
-    else if constexpr (LG == 2) return dpp_move<0x00>(p);   // quad_perm [0,0,0,0]
-    else if constexpr (LG == 3) return (threadIdx.x & 8u) ? row_bcast<8>(p) : row_bcast<0>(p);
-    else return row_bcast<0>(p);
-}
-template <int LG>
-__device__ inline uint32_t group_last(uint32_t q) {
-    if constexpr (LG == 0) return q;
-    else if constexpr (LG == 1) return dpp_move<0xF5>(q);   // quad_perm [1,1,3,3]
-    else if constexpr (LG == 2) return dpp_move<0xFF>(q);   // quad_perm [3,3,3,3]
-    else if constexpr (LG == 3) return (threadIdx.x & 8u) ? row_bcast<15>(q) : row_bcast<7>(q);
-    else return row_bcast<15>(q);
-}
-
+// and the group's total: the group's bits shifted to the bottom of a word,
+// then two population counts (a caller's `x + before` folds into the count).
+// No lane reads another lane's registers.
 template <int LG>
 __device__ inline void group_count_mask(uint64_t m, uint32_t& before, uint32_t& total) {
-    uint32_t p, q;
-    group_scan_mask<LG>(m, p, q);
-    const uint32_t first = group_first<LG>(p);
-    before = p - first;
-    total = group_last<LG>(q) - first;
+    constexpr uint32_t G = 1u << LG;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t bits = (uint32_t)(m >> (lane & ~(G - 1u)));
+    before = (uint32_t)__builtin_popcount(bits & ((1u << (lane & (G - 1u))) - 1u));
+    total = (uint32_t)__builtin_popcount(bits & ((1u << G) - 1u));
 }
 
 // The same for a per-lane flag `f` (its ballot is the mask).
