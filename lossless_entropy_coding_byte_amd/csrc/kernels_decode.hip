@@ -342,7 +342,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     group_count<LG>(N >= 1, b0, n0);
     group_count<LG>(N >= 2, b1, n1);
     const uint32_t d0 = (uint32_t)(sw - a0);    // the chunk's first word, from a0
-    uint32_t cons = d0 + n0 + n1;               // next word the group reads, from a0
+    // next word the group reads, from a0, plus the ring slot of a0 (so a
+    // word's slot is the low bits of cs plus its count, one add)
+    uint32_t cs = slot0 + d0 + n0 + n1;
     const uint32_t w0 = N >= 1 ? ring[(slot0 + d0 + b0) & (R - 1)] : 0u;
     const uint32_t w1 = N >= 2 ? ring[(slot0 + d0 + n0 + b1) & (R - 1)] : 0u;
     // Bit buffer: the lane's next avail = 64 - u bits, most significant first
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
         if (pon) put4(pat, pv);
         // a load is issued every time; it is kept only when the ring has room
         // and the chunk has words there
-        pon = wr - cons <= R - 4 * G && wr < wend;
+        pon = wr + slot0 - cs <= R - 4 * G && wr < wend;
         pv = load4(wr);
         pat = wr;
         wr += pon ? 4 * G : 0u;
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
             const bool fetch = min((int32_t)u, act ? rp : 0) >= 32;
             uint32_t bf, nf;
             group_count<LG>(fetch, bf, nf);
-            const uint32_t word = ring[(slot0 + cons + bf) & (R - 1)];
+            const uint32_t word = ring[(cs + bf) & (R - 1)];
             // avail >= 1 before a pair (a pair takes at most 32 of > 32 bits): u <= 63
             const uint32_t u31 = u & 31u;
             bb |= (uint64_t)(fetch ? word : 0u) << u31;
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
                 rp -= (int32_t)(u >> 5);   // (one word taken in when u >= 32)
                 u = u31;
             }
-            cons += nf;
+            cs += nf;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bool use = FULL || s0 + h < m;
