@@ -118,13 +118,29 @@ __device__ inline uint32_t group_sum(uint32_t v) {
     return v;
 }
 
-// Minimum of v over the caller's group of G = 1 << LG lanes (every lane gets it).
+// A DPP move inside rows of 16 lanes (every lane's source is a lane of its
+// own row), kept a separate instruction: the compiler's folded form of a DPP
+// subtract was measured wrong on gfx950, so no folding is relied on.
+template <int CTRL>
+__device__ inline uint32_t dpp_row(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Minimum of v over the caller's group of G = 1 << LG lanes (every lane gets
+// it), by DPP moves (VALU, no LDS round trip): quad swaps for 2 and 4 lanes,
+// a half-row mirror before them for 8, row rotations for 16.
 template <int LG>
 __device__ inline uint32_t group_min(uint32_t v) {
-    if constexpr (LG >= 1) v = min(v, lane_xor<1>(v));
-    if constexpr (LG >= 2) v = min(v, lane_xor<2>(v));
-    if constexpr (LG >= 3) v = min(v, lane_xor<4>(v));
-    if constexpr (LG >= 4) v = min(v, lane_xor<8>(v));
+    if constexpr (LG == 4) {
+        v = min(v, dpp_row<0x128>(v));   // row_ror:8
+        v = min(v, dpp_row<0x124>(v));   // row_ror:4
+        v = min(v, dpp_row<0x122>(v));   // row_ror:2
+        v = min(v, dpp_row<0x121>(v));   // row_ror:1
+    } else {
+        if constexpr (LG == 3) v = min(v, dpp_row<0x141>(v));   // row_half_mirror
+        if constexpr (LG >= 1) v = min(v, dpp_row<0xB1>(v));    // quad_perm [1,0,3,2]
+        if constexpr (LG >= 2) v = min(v, dpp_row<0x4E>(v));    // quad_perm [2,3,0,1]
+    }
     return v;
 }
 
