@@ -430,7 +430,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     const uint32_t nblk = (mmax + BLOCK - 1) / BLOCK, nfull = mmin / BLOCK;
     const uint64_t lane_e0 = c * a.chunk + (uint64_t)j * BLOCK;   // first element of the lane's block 0
     // The output of block t: 16 symbols of block tG + j of the chunk (FULL:
-    // every lane's block is whole).
+    // every lane's block is whole).  Whole blocks go out as non-temporal
+    // stores (the decode never reads its output back; measured 2.5 % faster
+    // than plain stores on 1 GiB of int8).
     // (x0: FULL, OUT_U16_XOR: the block's 16 bytes of the other snapshot,
     // loaded before the block's ring loads so that their wait does not drain
     // them)
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
                 v.y = w[1];
                 v.z = w[2];
                 v.w = w[3];
-                *reinterpret_cast<v4u*>(ln.out + e0) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(ln.out + e0));
             } else {
                 for (uint32_t x = 0; x < cnt; ++x) ln.out[e0 + x] = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
             }
@@ -457,11 +459,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
                 const uint64_t at = 2 * e0 + 16 * k;
                 if (FULL || cnt == BLOCK) {
                     if constexpr (OUT == DEC_OUT_U16_XOR) v ^= FULL ? x0 : *reinterpret_cast<const v4u*>(a.w0 + at);
-                    *reinterpret_cast<v4u*>(a.merged + at) = v;
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(a.merged + at));
                 }
             } else {
                 const v4u v = restore_u32(w, k);
-                if (FULL || cnt == BLOCK) *reinterpret_cast<v4u*>(a.merged + 4 * e0 + 16 * k) = v;
+                if (FULL || cnt == BLOCK) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(a.merged + 4 * e0 + 16 * k));
             }
             if (!FULL && cnt && cnt < BLOCK) {
                 // the tensor's last block: byte P-1-k of each element (plane k holds byte P-1-k)
