@@ -155,6 +155,40 @@ def test_config_int8_acts():
         _fixed_mode("int8_acts", x, hist, pool)
 
 
+@pytest.mark.timeout(600)
+def test_encode_uneven_ranges_whole_stream():
+    """An int8 input of 2^27 + 12345 symbols at chunk 4096: 8193 tasks, more
+    than twice the pack launch's waves on a 256-CU GPU, so the count launch
+    splits every pack range into sub-ranges, and 8193 tasks over a power of
+    two of ranges make the ranges (and sub-ranges) of unequal length.  The
+    whole stream equals the oracle's; decode restores the input."""
+    n, chunk = (1 << 27) + 12345, 4096
+    x = workloads.q8(np.random.default_rng([7, 41]).normal(0, 20.0, n))
+    _say(f"uneven ranges: n={n} chunk={chunk}")
+    hist = oracle.histogram(x)
+    ln = oracle.package_merge_lengths(oracle.codebook_frequencies([hist], 1), 16)
+    with oracle_jobs.pool() as pool:
+        job = pool.apply_async(oracle_jobs.encode, ((x, ln, chunk),))
+        dcb = lecb.DeviceCodebook.upload(lecb.lecb_codebook_from_lengths(ln), DEV)
+        xd = torch.from_numpy(x).to(DEV)
+        out = torch.empty(lecb.lecb_encoded_bound(n, chunk), dtype=torch.uint8, device=DEV)
+        res = lecb.new_results(1, DEV)
+        ws = lecb.new_workspace(n, chunk, DEV)
+        lecb.lecb_encode(xd, n, dcb.blob, chunk, out, res, ws)
+        r = lecb.results_to_numpy(res)[0]
+        assert int(r["status"]) == 0
+        y = torch.empty(n, dtype=torch.uint8, device=DEV)
+        rd = lecb.new_results(1, DEV)
+        lecb.lecb_decode(out, int(r["bytes"]), dcb.blob, chunk, n, y, rd, ws)
+        assert int(lecb.results_to_numpy(rd)[0]["status"]) == 0
+        assert torch.equal(y, xd)
+        got = _host(out, int(r["bytes"]))
+        ref, bits = job.get()
+    assert int(r["payload_bits"]) == bits
+    assert np.array_equal(got, ref), "uneven ranges: stream differs from the oracle's"
+    _say(f"uneven ranges: whole stream ({got.size} bytes) equals the oracle's")
+
+
 def test_config_int4_packed():
     """4-bit weights two per byte, coded as packed pairs with a fixed codebook
     from warm-up batches; the pair code of the tensor is never longer than the
