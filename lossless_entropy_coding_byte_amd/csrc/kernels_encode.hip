@@ -11,17 +11,18 @@
 //
 // One hardware lane codes one lane of the format (lane geometry: lanes.hpp).
 // A wave's task is 4 rows of 16 lanes, i.e. 4/P row groups of 16/G chunks.
-// The waves of a launch split the tasks into contiguous ranges, the same
-// ranges in the count and the pack launch:
+// The pack launch's waves split the tasks into contiguous ranges; the count
+// launch, with more waves, splits every range into K equal sub-ranges (they
+// end where the ranges end):
 //   1. count: every lane sums the code lengths of its symbols, stores its
 //      word count nw = ceil(bits / 32) in the stream, and every wave stores
-//      the words of its range (per stream) in the workspace;
-//   2. offsets: one workgroup turns the ranges' words into their first
+//      the words of its sub-range (per stream) in the workspace;
+//   2. offsets: one workgroup turns the sub-ranges' words into their first
 //      payload words (exclusive scan) and checks the total against the
 //      capacity;
 //   3. pack: every wave walks its range task by task.  A chunk's first word
-//      is the range's first word plus the words of the range's earlier
-//      chunks; the chunk's end goes to the table.  Every lane then runs the
+//      is the range's first word (its first sub-range's) plus the words of
+//      the range's earlier chunks; the chunk's end goes to the table.  Every lane then runs the
 //      decoder's read order in lock step with its group: before each pair
 //      of symbols, the lanes that completed a word in the previous pair get
 //      the next read positions of the chunk (a count over the group's lanes),
@@ -194,7 +195,7 @@ __device__ inline uint64_t block_elem(const EncArgs& a, const Place& pl, uint32_
     return pl.c * a.chunk + ((uint64_t)(t << a.lg) + pl.j) * BLOCK;
 }
 
-// Launch 1: word counts of every lane, words of every range.
+// Launch 1: word counts of every lane, words of every sub-range.
 template <int MODE>
 __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
     constexpr int P = Streams<MODE>::value;
