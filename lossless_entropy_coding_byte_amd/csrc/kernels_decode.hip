@@ -42,6 +42,8 @@
 // checked; a violation sets status CORRUPT.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "lanes.hpp"
@@ -73,7 +75,9 @@ struct DecArgs {
     uint32_t chunk;
     uint64_t n;
     uint64_t nc;
-    uint32_t wg_per_group;     // OUT_PLANES: workgroups of one stream; stream = blockIdx.x / wg_per_group
+    uint32_t wg_per_group;     // workgroup tasks (NW tasks each) of one stream (OUT_PLANES) or of the call
+    uint32_t wg_stride;        // workgroups launched per stream (OUT_PLANES) or in all; each loops over
+                               // its workgroup tasks bid, bid + wg_stride, ...  (stream = blockIdx.x / wg_stride)
     uint32_t nstreams;
     uint8_t* merged;           // OUT_U16, OUT_U16_XOR, OUT_U32: the restored elements
     const uint8_t* w0;         // OUT_U16_XOR: the other snapshot (element i ^ restored i is written)
@@ -85,6 +89,8 @@ template <int NW>
 struct SharedOne {
     uint32_t ring[NW][4][ROW_WORDS];   // first: every row's ring is 1 KiB-aligned
     uint16_t dec[DEC_ENTRIES];
+    unsigned long long bsum[1];        // payload bits of the lanes decoded without fault
+    uint32_t flag[1];                  // bit 0: a fault was found
 };
 // P streams in every workgroup: every stream's whole decode table.  (A
 // table entry read from memory instead would make every lookup wait for the
@@ -94,6 +100,8 @@ template <int NW, int P>
 struct SharedMany {
     uint32_t ring[NW][4][ROW_WORDS];
     uint16_t dec[P][DEC_ENTRIES];
+    unsigned long long bsum[P];
+    uint32_t flag[P];
 };
 template <int NW, int P>
 using Shared = std::conditional_t<P == 1, SharedOne<NW>, SharedMany<NW, P>>;
@@ -206,6 +214,15 @@ __device__ inline v4u restore_u32(const uint32_t (&w)[4], uint32_t q) {
     return o;
 }
 
+// The lane's index in its wave, from an asm statement that the compiler
+// cannot move or merge: a value derived from it is computed where it is used
+// instead of being kept in a register through a loop.
+__device__ inline uint32_t lane_index_fresh() {
+    uint32_t lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    return lane;
+}
+
 // Waves per SIMD the register budget is sized for: two workgroups of the
 // largest size per CU (16 waves: 8 per SIMD, 64 VGPRs; 12 waves: 6 per SIMD,
 // 85 VGPRs; 6 waves: 3 per SIMD).  No variant may spill registers (the build rejects scratch use).
@@ -220,17 +237,60 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     constexpr uint32_t R = 16 * G;                    // ring words of a group
     __shared__ __attribute__((aligned(16))) Shared<NW, P> S;
     const int tid = threadIdx.x;
-    const uint32_t lane = tid & 63u, wave = tid >> 6;
-    const uint32_t row = lane >> 4, i16 = lane & 15u;
-
-    // ---- which stream, task, chunk and lane this hardware lane decodes
-    const uint32_t sidx = P == 1 ? blockIdx.x / a.wg_per_group : 0u;     // P == 1: stream of the workgroup
-    const uint32_t bid = P == 1 ? blockIdx.x - sidx * a.wg_per_group : blockIdx.x;
-    const uint32_t k = P == 1 ? sidx : row % P;                           // this lane's stream
-    const uint64_t task = (uint64_t)bid * NW + wave;
     constexpr uint32_t CPT = (4 / P) * (16u >> LG);
-    const uint64_t c = task * CPT + (row / P) * (16u >> LG) + (i16 >> LG);
+    constexpr int NS = P == 1 ? 1 : P;  // streams in this workgroup
+    // P == 1: the workgroup's stream and its first workgroup task
+    const uint32_t sidx = P == 1 ? blockIdx.x / a.wg_stride : 0u;
+    const uint32_t bid0 = P == 1 ? blockIdx.x - sidx * a.wg_stride : blockIdx.x;
+
+    // ---- tables
+    if constexpr (P == 1) {
+        const v4u* src = reinterpret_cast<const v4u*>(a.st[sidx].cb->dec);
+        v4u* dst = reinterpret_cast<v4u*>(S.dec);
+        for (int x = tid; x < DEC_ENTRIES * 2 / 16; x += NT) dst[x] = src[x];
+    } else {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const v4u* src = reinterpret_cast<const v4u*>(a.st[q].cb->dec);
+            v4u* dst = reinterpret_cast<v4u*>(&S.dec[q][0]);
+            for (int x = tid; x < DEC_ENTRIES * 2 / 16; x += NT) dst[x] = src[x];
+        }
+    }
+    if (tid < NS) {
+        S.flag[tid] = 0u;
+        S.bsum[tid] = 0ull;
+    }
+    __syncthreads();   // every wave reads entries that other waves copied
+
+    // padding bytes of the header are part of the format (checked by the
+    // first workgroup of each stream, spread over that stream's lanes)
+    if (bid0 == 0) {
+        const uint32_t lane = tid & 63u, wave = tid >> 6, row = lane >> 4;
+        const uint32_t k = P == 1 ? sidx : row % P;
+        const Lane ln = lane_stream<P>(a, k, 0);
+        bool pad_bad = false;
+        const uint32_t lane_in = wave * (64 / P) + (row / P) * 16 + (lane & 15u);
+        for (uint64_t b = ln.table_pad_from + lane_in; b < ln.table_pad_to; b += NT / P) pad_bad |= ln.stream[b] != 0;
+        for (uint64_t b = ln.nw_pad_from + lane_in; b < ln.nw_pad_to; b += NT / P) pad_bad |= ln.stream[b] != 0;
+        if (pad_bad) atomicOr(&S.flag[P == 1 ? 0u : k], 1u);
+    }
+
+    // ---- the workgroup's tasks, one after the other (every wave of the
+    // workgroup runs the same number; lanes past the last chunk decode
+    // nothing)
+    const uint32_t wave = __builtin_amdgcn_readfirstlane((uint32_t)tid >> 6);
+    for (uint32_t bid = bid0; bid < a.wg_per_group; bid += a.wg_stride) {
+    // The lane's geometry and stream are worked out again for every task:
+    // the lane index comes from an asm statement the compiler cannot move
+    // out of the loop, so nothing derived from it stays in a register from
+    // one task to the next.
+    const uint32_t lane = lane_index_fresh();
+    const uint32_t row = lane >> 4, i16 = lane & 15u;
+    const uint32_t k = P == 1 ? sidx : row % P;   // this lane's stream
+    const uint32_t slot = P == 1 ? 0u : k;
     const uint32_t j = i16 & (G - 1);
+    const uint64_t task = (uint64_t)bid * NW + wave;
+    const uint64_t c = task * CPT + (row / P) * (16u >> LG) + (i16 >> LG);
     // stream sizes: given, or read from the encoder's results (this lane's
     // stream picked by conditional moves, not by an index into an array)
     uint64_t my_words = 0;
@@ -251,20 +311,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
         my_size_bad = mine ? sb : my_size_bad;
     }
     const Lane ln = lane_stream<P>(a, k, my_words);
-    // ---- tables
-    if constexpr (P == 1) {
-        const v4u* src = reinterpret_cast<const v4u*>(a.st[sidx].cb->dec);
-        v4u* dst = reinterpret_cast<v4u*>(S.dec);
-        for (int x = tid; x < DEC_ENTRIES * 2 / 16; x += NT) dst[x] = src[x];
-    } else {
-#pragma unroll
-        for (int q = 0; q < P; ++q) {
-            const v4u* src = reinterpret_cast<const v4u*>(a.st[q].cb->dec);
-            v4u* dst = reinterpret_cast<v4u*>(&S.dec[q][0]);
-            for (int x = tid; x < DEC_ENTRIES * 2 / 16; x += NT) dst[x] = src[x];
-        }
-    }
-    __syncthreads();   // every wave reads entries that other waves copied
     const uint32_t long_sub = ln.cb->long_sub;
 
     // ---- the chunk and its structure
@@ -289,14 +335,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
         m = 0;
         N = 0;
         sw = 0;   // a chunk that is not decoded reads payload word 0 onwards (always in the buffer)
-    }
-
-    // padding bytes of the header are part of the format (checked by the
-    // first workgroup of each stream, spread over that stream's lanes)
-    if (bid == 0) {
-        const uint32_t lane_in = wave * (64 / P) + (row / P) * 16 + i16;
-        for (uint64_t b = ln.table_pad_from + lane_in; b < ln.table_pad_to; b += NT / P) bad |= ln.stream[b] != 0;
-        for (uint64_t b = ln.nw_pad_from + lane_in; b < ln.nw_pad_to; b += NT / P) bad |= ln.stream[b] != 0;
     }
 
     // ---- the group's ring: words of the chunk's payload, slot = word & (R - 1).
@@ -510,35 +548,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
         if (!bad && rest && (bb >> (64 - rest)) != 0) bad = true;
     }
 
-    // ---- status, accounting, exit
-    constexpr int NS = P == 1 ? 1 : P;  // streams in this workgroup
-    const uint32_t slot = P == 1 ? 0u : k;
-    __syncthreads();  // the rings are free again: per-stream flags and bit sums
-    uint32_t* const flag = &S.ring[0][0][0];                                                    // [NS]
-    unsigned long long* const bsum = reinterpret_cast<unsigned long long*>(&S.ring[0][1][0]);  // [NS]
-    if (tid < NS) {
-        flag[tid] = 0u;
-        bsum[tid] = 0ull;
-    }
-    __syncthreads();
-    if (bad) atomicOr(&flag[slot], 1u);
+    // ---- the task's status and bits, per stream of the workgroup
+    if (bad) atomicOr(&S.flag[slot], 1u);
     {
         // bits of the lanes decoded without fault, summed per row (one stream
         // per row; a lane has at most 4096 symbols of at most 16 bits, so the
         // sum fits 32 bits)
         const uint32_t v = group_sum<4>((run && !bad) ? bits : 0u);
-        if (i16 == 0 && v) atomicAdd(&bsum[slot], (unsigned long long)v);
+        if (i16 == 0 && v) atomicAdd(&S.bsum[slot], (unsigned long long)v);
     }
+    }   // the workgroup's tasks
+
+    // ---- status, accounting, exit
     __syncthreads();
+    const uint32_t tid_end = wave * 64 + lane_index_fresh();
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
-        if (tid == q) {
+        if (tid_end == (uint32_t)q) {
             const DecStream& d = a.st[P == 1 ? sidx : (uint32_t)q];
-            if (bsum[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&d.ws->bits), bsum[q]);
-            if (flag[q]) atomicCAS(&d.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
+            if (S.bsum[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&d.ws->bits), S.bsum[q]);
+            if (S.flag[q]) atomicCAS(&d.ws->status, 0, (int32_t)LECB_ERR_CORRUPT);
         }
     }
-    if (tid == 0) {
+    if (tid_end == 0) {
         __threadfence();
         WsHeader* ws0 = a.st[0].ws;
         const uint32_t done = __hip_atomic_fetch_add(&ws0->exit_count, 1u, __ATOMIC_ACQ_REL,
@@ -567,14 +599,54 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
 }
 
 template <int NT, int P, int OUT>
-hipError_t launch(const DecArgs& a, uint32_t lg, uint32_t wgs, hipStream_t hs) {
+const void* kernel_of(uint32_t lg) {
+    switch (lg) {
+        case 0: return reinterpret_cast<const void*>(&decode_kernel<NT, P, OUT, 0>);
+        case 1: return reinterpret_cast<const void*>(&decode_kernel<NT, P, OUT, 1>);
+        case 2: return reinterpret_cast<const void*>(&decode_kernel<NT, P, OUT, 2>);
+        case 3: return reinterpret_cast<const void*>(&decode_kernel<NT, P, OUT, 3>);
+        case 4: return reinterpret_cast<const void*>(&decode_kernel<NT, P, OUT, 4>);
+        default: return nullptr;
+    }
+}
+
+// Workgroups of one decode kernel resident on a CU (asked once per device and
+// kernel; concurrent first calls store the same value).
+constexpr int DEC_VARIANTS = 8;
+template <int NT, int P, int OUT>
+uint64_t resident_per_cu(int variant, uint32_t lg) {
+    static std::atomic<int> cached[MAX_DEVICES][DEC_VARIANTS][5];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 1;
+    int nb = cached[dev][variant][lg].load(std::memory_order_relaxed);
+    if (!nb) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel_of<NT, P, OUT>(lg), NT, 0) != hipSuccess || nb <= 0)
+            nb = 1;
+        cached[dev][variant][lg].store(nb, std::memory_order_relaxed);
+    }
+    return (uint64_t)nb;
+}
+
+// Launch with wg_tasks workgroup tasks per stream (OUT_PLANES: one stream per
+// workgroup, `groups` streams) or in all (groups = 1): as many workgroups as
+// the CUs hold at once (never more than the tasks), each looping over its
+// tasks.
+template <int NT, int P, int OUT>
+hipError_t launch(DecArgs& a, int variant, uint32_t lg, uint64_t wg_tasks, uint32_t groups, uint64_t cus,
+                  hipStream_t hs) {
+    if (lg > 4) return hipErrorInvalidValue;
+    if (wg_tasks == 0 || wg_tasks > 0xFFFFFFFFull) return hipErrorInvalidValue;
+    const uint64_t resident = cus * resident_per_cu<NT, P, OUT>(variant, lg);
+    const uint64_t per_group = std::max<uint64_t>(1, resident / groups);
+    a.wg_per_group = (uint32_t)wg_tasks;
+    a.wg_stride = (uint32_t)std::min<uint64_t>(wg_tasks, per_group);
+    const uint32_t wgs = a.wg_stride * groups;
     switch (lg) {
         case 0: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 0>), dim3(wgs), dim3(NT), 0, hs, a); break;
         case 1: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 1>), dim3(wgs), dim3(NT), 0, hs, a); break;
         case 2: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 2>), dim3(wgs), dim3(NT), 0, hs, a); break;
         case 3: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 3>), dim3(wgs), dim3(NT), 0, hs, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 4>), dim3(wgs), dim3(NT), 0, hs, a); break;
-        default: return hipErrorInvalidValue;
+        default: hipLaunchKernelGGL((decode_kernel<NT, P, OUT, 4>), dim3(wgs), dim3(NT), 0, hs, a); break;
     }
     return hipSuccess;
 }
@@ -622,32 +694,35 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
         const uint64_t cpt = 4 * (16 >> lg);
         const uint64_t tasks = (L.nc + cpt - 1) / cpt;
         const bool big = tasks * (uint64_t)L.nstreams >= cus * 16;
-        const uint32_t nw = big ? 16 : 4;
-        a.wg_per_group = (uint32_t)((tasks + nw - 1) / nw);
-        const uint32_t wgs = a.wg_per_group * (uint32_t)L.nstreams;
-        e = big ? launch<1024, 1, DEC_OUT_PLANES>(a, lg, wgs, hs) : launch<256, 1, DEC_OUT_PLANES>(a, lg, wgs, hs);
+        const uint64_t nw = big ? 16 : 4;
+        const uint64_t wg_tasks = (tasks + nw - 1) / nw;
+        const uint32_t ns = (uint32_t)L.nstreams;
+        e = big ? launch<1024, 1, DEC_OUT_PLANES>(a, 0, lg, wg_tasks, ns, cus, hs)
+                : launch<256, 1, DEC_OUT_PLANES>(a, 1, lg, wg_tasks, ns, cus, hs);
     } else if (L.out_kind == DEC_OUT_U16 || L.out_kind == DEC_OUT_U16_XOR) {
         if (L.nstreams != 2 || !L.merged || (L.out_kind == DEC_OUT_U16_XOR && !L.w0)) return LECB_ERR_INVALID_ARG;
         // (two planes need more registers per lane: 12-wave workgroups)
         const uint64_t cpt = 2 * (16 >> lg);
         const uint64_t tasks = (L.nc + cpt - 1) / cpt;
         const bool big = tasks >= cus * 12;
-        const uint32_t nw = big ? 12 : 4;
-        const uint32_t wgs = (uint32_t)((tasks + nw - 1) / nw);
+        const uint64_t nw = big ? 12 : 4;
+        const uint64_t wg_tasks = (tasks + nw - 1) / nw;
         if (L.out_kind == DEC_OUT_U16)
-            e = big ? launch<768, 2, DEC_OUT_U16>(a, lg, wgs, hs) : launch<256, 2, DEC_OUT_U16>(a, lg, wgs, hs);
+            e = big ? launch<768, 2, DEC_OUT_U16>(a, 2, lg, wg_tasks, 1, cus, hs)
+                    : launch<256, 2, DEC_OUT_U16>(a, 3, lg, wg_tasks, 1, cus, hs);
         else
-            e = big ? launch<768, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs)
-                    : launch<256, 2, DEC_OUT_U16_XOR>(a, lg, wgs, hs);
+            e = big ? launch<768, 2, DEC_OUT_U16_XOR>(a, 4, lg, wg_tasks, 1, cus, hs)
+                    : launch<256, 2, DEC_OUT_U16_XOR>(a, 5, lg, wg_tasks, 1, cus, hs);
     } else if (L.out_kind == DEC_OUT_U32) {
         if (L.nstreams != 4 || !L.merged) return LECB_ERR_INVALID_ARG;
         // (four tables in LDS: 6-wave workgroups)
         const uint64_t cpt = 16 >> lg;
         const uint64_t tasks = (L.nc + cpt - 1) / cpt;
         const bool big = tasks >= cus * 6;
-        const uint32_t nw = big ? 6 : 4;
-        const uint32_t wgs = (uint32_t)((tasks + nw - 1) / nw);
-        e = big ? launch<384, 4, DEC_OUT_U32>(a, lg, wgs, hs) : launch<256, 4, DEC_OUT_U32>(a, lg, wgs, hs);
+        const uint64_t nw = big ? 6 : 4;
+        const uint64_t wg_tasks = (tasks + nw - 1) / nw;
+        e = big ? launch<384, 4, DEC_OUT_U32>(a, 6, lg, wg_tasks, 1, cus, hs)
+                : launch<256, 4, DEC_OUT_U32>(a, 7, lg, wg_tasks, 1, cus, hs);
     } else {
         return LECB_ERR_INVALID_ARG;
     }
