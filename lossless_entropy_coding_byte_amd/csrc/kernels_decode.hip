@@ -279,6 +279,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     // workgroup runs the same number; lanes past the last chunk decode
     // nothing)
     const uint32_t wave = __builtin_amdgcn_readfirstlane((uint32_t)tid >> 6);
+    // Stream sizes (given, or read from the encoder's results) and the
+    // codebooks' long-window offsets, once per workgroup: values common to
+    // the workgroup, held in scalar registers.
+    uint64_t s_words[NS];
+    bool s_bad[NS];
+    uint32_t s_long_sub[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        const uint32_t si = P == 1 ? sidx : (uint32_t)q;
+        const DecStream& d = a.st[si];
+        uint64_t w = d.payload_words;
+        bool sb = false;
+        if (a.sizes) {
+            const uint64_t b = a.sizes[si].bytes;
+            const uint64_t bytes = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                                   __builtin_amdgcn_readfirstlane((uint32_t)b);
+            const int32_t status = __builtin_amdgcn_readfirstlane(a.sizes[si].status);
+            sb = status != 0 || bytes < d.header_bytes + 4 || ((bytes - d.header_bytes) & 3) != 0;
+            w = sb ? 0 : (bytes - d.header_bytes) / 4;
+        }
+        s_words[q] = w;
+        s_bad[q] = sb;
+        s_long_sub[q] = __builtin_amdgcn_readfirstlane(d.cb->long_sub);
+    }
     for (uint32_t bid = bid0; bid < a.wg_per_group; bid += a.wg_stride) {
     // The lane's geometry and stream are worked out again for every task:
     // the lane index comes from an asm statement the compiler cannot move
@@ -291,27 +315,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     const uint32_t j = i16 & (G - 1);
     const uint64_t task = (uint64_t)bid * NW + wave;
     const uint64_t c = task * CPT + (row / P) * (16u >> LG) + (i16 >> LG);
-    // stream sizes: given, or read from the encoder's results (this lane's
-    // stream picked by conditional moves, not by an index into an array)
+    // this lane's stream's size and codebook field, picked by conditional
+    // moves, not by an index into an array
     uint64_t my_words = 0;
     bool my_size_bad = false;
+    uint32_t long_sub = 0;
 #pragma unroll
-    for (int q = 0; q < (P == 1 ? 1 : P); ++q) {
-        const uint32_t s = P == 1 ? sidx : (uint32_t)q;
-        const DecStream& d = a.st[s];
-        uint64_t w = d.payload_words;
-        bool sb = false;
-        if (a.sizes) {
-            const uint64_t bytes = a.sizes[s].bytes;
-            sb = a.sizes[s].status != 0 || bytes < d.header_bytes + 4 || ((bytes - d.header_bytes) & 3) != 0;
-            w = sb ? 0 : (bytes - d.header_bytes) / 4;
-        }
+    for (int q = 0; q < NS; ++q) {
         const bool mine = P == 1 || (uint32_t)q == k;
-        my_words = mine ? w : my_words;
-        my_size_bad = mine ? sb : my_size_bad;
+        my_words = mine ? s_words[q] : my_words;
+        my_size_bad = mine ? s_bad[q] : my_size_bad;
+        long_sub = mine ? s_long_sub[q] : long_sub;
     }
     const Lane ln = lane_stream<P>(a, k, my_words);
-    const uint32_t long_sub = ln.cb->long_sub;
 
     // ---- the chunk and its structure
     const bool valid = c < a.nc;
@@ -466,7 +482,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
         mmin = min(mmin, (uint32_t)__shfl_xor(mmin, o, 64));
     }
     const uint32_t nblk = (mmax + BLOCK - 1) / BLOCK, nfull = mmin / BLOCK;
-    const uint64_t lane_e0 = c * a.chunk + (uint64_t)j * BLOCK;   // first element of the lane's block 0
+    // Output addresses: the task's first element (common to the wave, so the
+    // bases below are scalar) plus the lane's 32-bit offset from it (a task
+    // spans at most 4 * 65536 elements).
+    const uint64_t task_e0 = task * CPT * (uint64_t)a.chunk;
+    const uint32_t lane_e0 = ((row / P) * (16u >> LG) + (i16 >> LG)) * a.chunk + j * BLOCK;  // lane's block 0
+    uint8_t* const out_t = P == 1 ? ln.out + task_e0 : nullptr;   // OUT_PLANES
+    uint8_t* const merged_t = a.merged + (uint64_t)P * task_e0;    // OUT_U16, OUT_U16_XOR, OUT_U32
+    const uint8_t* const w0_t = a.w0 + 2 * task_e0;                // OUT_U16_XOR
     // The output of block t: 16 symbols of block tG + j of the chunk (FULL:
     // every lane's block is whole).  Whole blocks go out as non-temporal
     // stores (the decode never reads its output back; measured 2.5 % faster
@@ -477,7 +500,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
     auto store_block = [&](uint32_t t, const uint32_t (&w)[4], auto full_c, const v4u& x0) {
         constexpr bool FULL = decltype(full_c)::value;
         const uint32_t cnt = FULL ? BLOCK : (m > t * BLOCK ? min(BLOCK, m - t * BLOCK) : 0u);
-        const uint64_t e0 = lane_e0 + (uint64_t)(t << LG) * BLOCK;
+        const uint32_t e0 = lane_e0 + (t << LG) * BLOCK;
         if constexpr (OUT == DEC_OUT_PLANES) {
             if (FULL || cnt == BLOCK) {
                 v4u v;
@@ -485,30 +508,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
                 v.y = w[1];
                 v.z = w[2];
                 v.w = w[3];
-                __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(ln.out + e0));
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(out_t + e0));
             } else {
-                for (uint32_t x = 0; x < cnt; ++x) ln.out[e0 + x] = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
+                for (uint32_t x = 0; x < cnt; ++x) out_t[e0 + x] = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
             }
         } else {
             // every lane takes part in the exchanges; the lanes of one element
             // group have the same cnt
             if constexpr (OUT == DEC_OUT_U16 || OUT == DEC_OUT_U16_XOR) {
                 v4u v = restore_u16(w, k);
-                const uint64_t at = 2 * e0 + 16 * k;
+                const uint32_t at = 2 * e0 + 16 * k;
                 if (FULL || cnt == BLOCK) {
-                    if constexpr (OUT == DEC_OUT_U16_XOR) v ^= FULL ? x0 : *reinterpret_cast<const v4u*>(a.w0 + at);
-                    __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(a.merged + at));
+                    if constexpr (OUT == DEC_OUT_U16_XOR) v ^= FULL ? x0 : *reinterpret_cast<const v4u*>(w0_t + at);
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(merged_t + at));
                 }
             } else {
                 const v4u v = restore_u32(w, k);
-                if (FULL || cnt == BLOCK) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(a.merged + 4 * e0 + 16 * k));
+                if (FULL || cnt == BLOCK) __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(merged_t + 4 * e0 + 16 * k));
             }
             if (!FULL && cnt && cnt < BLOCK) {
                 // the tensor's last block: byte P-1-k of each element (plane k holds byte P-1-k)
                 for (uint32_t x = 0; x < cnt; ++x) {
-                    const uint64_t at = (uint64_t)P * (e0 + x) + (P - 1 - k);
+                    const uint32_t at = P * (e0 + x) + (P - 1 - k);
                     const uint8_t sym = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
-                    a.merged[at] = OUT == DEC_OUT_U16_XOR ? (uint8_t)(sym ^ a.w0[at]) : sym;
+                    merged_t[at] = OUT == DEC_OUT_U16_XOR ? (uint8_t)(sym ^ w0_t[at]) : sym;
                 }
             }
         }
@@ -527,7 +550,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves
             uint32_t w[4];
             v4u x0 = {0, 0, 0, 0};
             if constexpr (OUT == DEC_OUT_U16_XOR)
-                x0 = *reinterpret_cast<const v4u*>(a.w0 + 2 * (lane_e0 + (uint64_t)(t << LG) * BLOCK) + 16 * k);
+                x0 = *reinterpret_cast<const v4u*>(w0_t + 2 * (lane_e0 + (t << LG) * BLOCK) + 16 * k);
             decode_block(t, std::true_type{}, w);
             store_block(t, w, std::true_type{}, x0);
         }
