@@ -243,7 +243,7 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
                 const bool low = MODE == ENC_PLANE_LO || (MODE == ENC_PAIR && pl.plane == 1);
                 const uint32_t sel = low ? 0x06040200u : 0x07050301u;
                 auto step = [&](uint32_t t, const uint4 (&cur)[2], uint4 (&ahead)[2]) {
-                    load_raw(t + 1 < nfw ? t + 1 : 0u, ahead);
+                    load_raw(t + 1 < nfw ? t + 1 : nfw - 1, ahead);
                         // the plane's bytes of two elements: bytes 0 and 2 (low
                     // plane) or 1 and 3 (high plane) of each word, by one permute
                     uint32_t w[4];
@@ -268,13 +268,14 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
         } else if (FAST && nfw) {
             // three buffers, block x in buf[x % 3] (a rotation by copies would
             // make every copy wait for the load it copies); every step issues
-            // its load (past the whole blocks it reads block 0 again), so the
-            // waits count exactly the loads issued after the one they wait for
+            // its load (past the whole blocks it reads the last one again,
+            // still in the caches), so the waits count exactly the loads
+            // issued after the one they wait for
             uint32_t b0[4], b1[4], b2[4];
             block_symbols<MODE>(a, block_elem(a, pl, 0), BLOCK, pl.plane, b0);
             block_symbols<MODE>(a, block_elem(a, pl, nfw > 1 ? 1u : 0u), BLOCK, pl.plane, b1);
             auto step = [&](uint32_t t, const uint32_t (&cur)[4], uint32_t (&ahead)[4]) {
-                block_symbols<MODE>(a, block_elem(a, pl, t + 2 < nfw ? t + 2 : 0u), BLOCK, pl.plane, ahead);
+                block_symbols<MODE>(a, block_elem(a, pl, t + 2 < nfw ? t + 2 : nfw - 1), BLOCK, pl.plane, ahead);
                 const bool on = t < nfw;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
