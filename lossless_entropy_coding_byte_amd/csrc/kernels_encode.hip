@@ -222,7 +222,7 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
         // count of 1 GiB of int8 took ~6 % longer.)
         // (modes with four 16-byte loads per block pick their bytes from all
         // four at once, so a load in flight would need 16 more registers per
-        // block: those count every block in the loop below)
+        // block: those keep the loop over every block at the end)
         constexpr bool FAST = MODE == ENC_BYTES || MODE == ENC_PAIR || MODE == ENC_PLANE_LO || MODE == ENC_PLANE_HI;
         const uint32_t nfw = FAST ? wave_min_u32(pl.m) / BLOCK : 0u;
         if constexpr (MODE == ENC_PAIR || MODE == ENC_PLANE_LO || MODE == ENC_PLANE_HI) {
@@ -291,15 +291,48 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
                 step(t + 2, b2, b1);
             }
         }
-        // the rest of the lane's blocks (the tensor's last chunk), one by one
-        for (uint32_t t = nfw; t < nb; ++t) {
-            const uint32_t cnt = min(BLOCK, pl.m - t * BLOCK);
-            uint32_t wt[4];
-            block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, wt);
-            for (uint32_t k = 0; k < cnt; ++k) {
-                const uint32_t l = ln[sym_of(wt, (int)k)];
-                bits += l;
-                mn = min(mn, l);
+        if constexpr (FAST) {
+            // the rest of the lane's blocks (the tensor's last chunk), one by one
+            for (uint32_t t = nfw; t < nb; ++t) {
+                const uint32_t cnt = min(BLOCK, pl.m - t * BLOCK);
+                uint32_t wt[4];
+                block_symbols<MODE>(a, block_elem(a, pl, t), cnt, pl.plane, wt);
+                for (uint32_t k = 0; k < cnt; ++k) {
+                    const uint32_t l = ln[sym_of(wt, (int)k)];
+                    bits += l;
+                    mn = min(mn, l);
+                }
+            }
+        } else {
+            // every block, the loads of blocks t + 1 and t + 2 issued ahead
+            uint32_t w[4] = {0, 0, 0, 0}, wn[4] = {0, 0, 0, 0};
+            if (nb) block_symbols<MODE>(a, block_elem(a, pl, 0), min(BLOCK, pl.m), pl.plane, w);
+            if (nb > 1) block_symbols<MODE>(a, block_elem(a, pl, 1), min(BLOCK, pl.m - BLOCK), pl.plane, wn);
+            for (uint32_t t = 0; t < nb; ++t) {
+                const uint32_t cnt = min(BLOCK, pl.m - t * BLOCK);
+                uint32_t wnn[4] = {0, 0, 0, 0};
+                if (t + 2 < nb)
+                    block_symbols<MODE>(a, block_elem(a, pl, t + 2), min(BLOCK, pl.m - (t + 2) * BLOCK), pl.plane,
+                                        wnn);
+                if (cnt == BLOCK) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) {
+                        const uint32_t l = ln[sym_of(w, k)];
+                        bits += l;
+                        mn = min(mn, l);
+                    }
+                } else {
+                    for (uint32_t k = 0; k < cnt; ++k) {
+                        const uint32_t l = ln[sym_of(w, (int)k)];
+                        bits += l;
+                        mn = min(mn, l);
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    w[k] = wn[k];
+                    wn[k] = wnn[k];
+                }
             }
         }
         unc |= mn == 0;
