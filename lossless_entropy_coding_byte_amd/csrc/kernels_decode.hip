@@ -225,11 +225,11 @@ __device__ inline uint32_t lane_index_fresh() {
 
 // Waves per SIMD the register budget is sized for: two workgroups of the
 // largest size per CU (16 waves: 8 per SIMD, 64 VGPRs; 12 waves: 6 per SIMD,
-// 85 VGPRs; 6 waves: 3 per SIMD), or one 16-wave workgroup of two planes
-// (4 per SIMD, 128 VGPRs).  No variant may spill registers (the build
+// 85 VGPRs; 6 waves: 3 per SIMD), or one 16-wave workgroup of two or four
+// planes (4 per SIMD, 128 VGPRs).  No variant may spill registers (the build
 // rejects scratch use).
 template <int NT>
-constexpr int decode_waves_per_simd(int p) { return NT == 768 ? 6 : NT == 384 ? 3 : (NT == 1024 && p == 2) ? 4 : 8; }
+constexpr int decode_waves_per_simd(int p) { return NT == 768 ? 6 : NT == 384 ? 3 : (NT == 1024 && p > 1) ? 4 : 8; }
 
 template <int NT, int P, int OUT, int LG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<NT>(P), 8))) void decode_kernel(DecArgs a) {
@@ -637,7 +637,7 @@ const void* kernel_of(uint32_t lg) {
 
 // Workgroups of one decode kernel resident on a CU (asked once per device and
 // kernel; concurrent first calls store the same value).
-constexpr int DEC_VARIANTS = 10;
+constexpr int DEC_VARIANTS = 11;
 template <int NT, int P, int OUT>
 uint64_t resident_per_cu(int variant, uint32_t lg) {
     static std::atomic<int> cached[MAX_DEVICES][DEC_VARIANTS][5];
@@ -745,14 +745,17 @@ int launch_decode(const DecodeLaunch& L, void* stream) {
                           : launch<256, 2, DEC_OUT_U16_XOR>(a, 5, lg, wg_tasks, 1, cus, hs);
     } else if (L.out_kind == DEC_OUT_U32) {
         if (L.nstreams != 4 || !L.merged) return LECB_ERR_INVALID_ARG;
-        // (four tables in LDS: 6-wave workgroups)
+        // (four tables in LDS: 6-wave workgroups; one 16-wave workgroup per CU
+        // when that holds every task)
         const uint64_t cpt = 16 >> lg;
         const uint64_t tasks = (L.nc + cpt - 1) / cpt;
         const bool big = tasks >= cus * 6;
-        const uint64_t nw = big ? 6 : 4;
+        const bool one_round = big && tasks <= cus * 16;
+        const uint64_t nw = one_round ? 16 : big ? 6 : 4;
         const uint64_t wg_tasks = (tasks + nw - 1) / nw;
-        e = big ? launch<384, 4, DEC_OUT_U32>(a, 6, lg, wg_tasks, 1, cus, hs)
-                : launch<256, 4, DEC_OUT_U32>(a, 7, lg, wg_tasks, 1, cus, hs);
+        e = one_round ? launch<1024, 4, DEC_OUT_U32>(a, 10, lg, wg_tasks, 1, cus, hs)
+            : big     ? launch<384, 4, DEC_OUT_U32>(a, 6, lg, wg_tasks, 1, cus, hs)
+                      : launch<256, 4, DEC_OUT_U32>(a, 7, lg, wg_tasks, 1, cus, hs);
     } else {
         return LECB_ERR_INVALID_ARG;
     }
