@@ -7,7 +7,8 @@
 // lanes of the format.
 //
 // One hardware lane runs one lane of the format (lane geometry: lanes.hpp);
-// a wave decodes one task, 4 rows of 16 lanes:
+// a wave decodes one task at a time, 4 rows of 16 lanes (the grid is as many
+// workgroups as the CUs hold, each looping over its tasks):
 //   * P = 1, OUT_PLANES: the rows hold lanes of one stream, one byte per
 //     symbol written to that stream's output (a stream's tasks run in
 //     workgroups of their own);
