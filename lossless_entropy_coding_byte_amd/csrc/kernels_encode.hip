@@ -266,29 +266,32 @@ __global__ __launch_bounds__(ENC_THREADS) void count_kernel(EncArgs a) {
                 }
             }
         } else if (FAST && nfw) {
-            // three buffers, block x in buf[x % 3] (a rotation by copies would
-            // make every copy wait for the load it copies); every step issues
-            // its load (past the whole blocks it reads the last one again,
-            // still in the caches), so the waits count exactly the loads
-            // issued after the one they wait for
-            uint32_t b0[4], b1[4], b2[4];
-            block_symbols<MODE>(a, block_elem(a, pl, 0), BLOCK, pl.plane, b0);
-            block_symbols<MODE>(a, block_elem(a, pl, nfw > 1 ? 1u : 0u), BLOCK, pl.plane, b1);
-            auto step = [&](uint32_t t, const uint32_t (&cur)[4], uint32_t (&ahead)[4]) {
-                block_symbols<MODE>(a, block_elem(a, pl, t + 2 < nfw ? t + 2 : nfw - 1), BLOCK, pl.plane, ahead);
-                const bool on = t < nfw;
+            // Four buffers, block x in buf[x % 4]: step t loads block t and
+            // counts block t - 3, so three blocks' loads are in flight and the
+            // waits count them exactly (`vmcnt(3)`).  Every load is issued in
+            // the loop (past the whole blocks it reads the last one again,
+            // still in the caches): loads before the loop, or a rotation of
+            // the buffers by copies, made the compiler wait for all loads at
+            // the loop head or at every copy.  (Encode of 1 GiB of int8, one
+            // box: 1190 -> 1169 us against two blocks ahead with the first
+            // loads before the loop.)
+            uint32_t b0[4] = {0, 0, 0, 0}, b1[4] = {0, 0, 0, 0}, b2[4] = {0, 0, 0, 0}, b3[4] = {0, 0, 0, 0};
+            auto step = [&](uint32_t t, uint32_t (&ld)[4], const uint32_t (&cur)[4]) {
+                block_symbols<MODE>(a, block_elem(a, pl, t < nfw ? t : nfw - 1), BLOCK, pl.plane, ld);
+                const bool on = t >= 3 && t - 3 < nfw;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
                     const uint32_t l = ln[sym_of(cur, k)];
                     bits += on ? l : 0u;
                     mn = on ? min(mn, l) : mn;
                 }
-                __builtin_amdgcn_sched_barrier(0);   // one load per block, not all three at once
+                __builtin_amdgcn_sched_barrier(0);   // one load per block, not all at once
             };
-            for (uint32_t t = 0; t < nfw; t += 3) {
-                step(t, b0, b2);
-                step(t + 1, b1, b0);
-                step(t + 2, b2, b1);
+            for (uint32_t t = 0; t < nfw + 3; t += 4) {
+                step(t, b0, b1);
+                step(t + 1, b1, b2);
+                step(t + 2, b2, b3);
+                step(t + 3, b3, b0);
             }
         }
         if constexpr (FAST) {
